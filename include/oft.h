@@ -1,0 +1,213 @@
+/*
+ * oft.h -- C ABI of liboft: the OFT-adapted linear layer over a frozen
+ * low-precision base, and its MoE (grouped, active-expert) form, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method (sources are the Orbit pages):
+ *   - Sphere AI Lab's Orbit release news (chooseai.io), section "Technical
+ *     principles": the base stays frozen at deployment precision (INT4/FP8)
+ *     and every gradient goes through a small BF16 OFT adapter;
+ *   - same page, "Five design features of the adapter-first architecture"
+ *     and "Architectural advantages of OFT over LoRA": each sub-projection of
+ *     a fused tensor (Q/K/V, gate/up) gets its own orthogonal rotation;
+ *   - same page, "Dedicated optimisation for low-precision MoE models", and
+ *     the Synced article on Orbit, section "Technical details": only the
+ *     router-selected experts are dequantised, in fixed-size batches, before
+ *     a grouped GEMM; the backward never computes a base-weight gradient.
+ *   The pages print no formula.  This library implements: each output
+ *   channel block j (b consecutive channels; segments are multiples of b)
+ *   has R_j = (I + Q_j)(I - Q_j)^-1 with Q_j skew-symmetric, and
+ *   y = rot_R(x . dequant(W0)^T), i.e. Y[:, blk j] = Z[:, blk j] . R_j^T
+ *   with Z = x . dequant(W0)^T.  Training produces dX and dQ only.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a caller-owned DEVICE pointer, 16-byte
+ *     aligned, row-major and contiguous.  Descriptors (structs passed by
+ *     pointer) are HOST memory, read only during the call.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     A call validates its arguments on the host, enqueues kernels on
+ *     `stream` and returns; it never synchronises and never allocates.
+ *     Scratch memory is the caller's workspace `ws` of `ws_bytes` bytes,
+ *     sized by the matching *_workspace_bytes query.
+ *   - Return value: OFT_OK or a negative oft_status.  On every error except
+ *     OFT_EHIP nothing has been enqueued and no output was touched.
+ *     OFT_EHIP means a launch failed; oft_last_hip_error() returns the
+ *     hipError_t (thread-local).  Faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Results are deterministic: no floating-point atomics; every reduction
+ *     runs in a fixed order.  Calls are re-entrant; calls on different
+ *     streams may overlap only if they share no output or workspace.
+ *   - Encodings: bf16 / fp16 tensors are uint16_t bit patterns; fp8 is OCP
+ *     e4m3fn (bias 7, max 448, no infinities).  INT4 weights are uint8
+ *     [rows, cols/2]: element c of a row sits in byte c/2, low nibble for
+ *     even c, two's complement in [-8, 7]; INT4 scales are fp16
+ *     [rows, cols/g] (group of g consecutive in-features).  FP8 weights are
+ *     uint8 [rows, cols] with fp32 scales [rows] (one per output channel).
+ *   - Adapter parameters q: bf16 [nblk, b(b-1)/2], the strict upper triangle
+ *     of each Q_j in row-major order (0,1),(0,2),...,(0,b-1),(1,2),...;
+ *     entry p of pair (i,l) sets Q[i][l] = p and Q[l][i] = -p.  Block j
+ *     covers output channels [j*b, (j+1)*b).
+ *   - Rotation operand R_ops: bf16 [nblk, 2, b, b]; [j][0] is R_j and [j][1]
+ *     is R_j^T (both row-major).  R_f32: fp32 [nblk, b, b], R_j row-major.
+ */
+#ifndef OFT_H_
+#define OFT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OFT_ABI_VERSION 1
+
+typedef enum {
+  OFT_OK = 0,
+  OFT_EINVAL = -1,      /* null required pointer, bad size, misaligned pointer */
+  OFT_ESHAPE = -2,      /* shape constraint violated (see each call)           */
+  OFT_EDTYPE = -3,      /* unknown dtype / format enum                          */
+  OFT_EUNSUPPORTED = -4,/* valid but not implemented (b, g, k, segments)        */
+  OFT_EWORKSPACE = -5,  /* workspace smaller than the query returned            */
+  OFT_EHIP = -6         /* a HIP launch failed; see oft_last_hip_error()        */
+} oft_status;
+
+enum { OFT_DT_BF16 = 0, OFT_DT_F32 = 1 };
+enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1 };
+enum { OFT_PASS_FWD = 0, OFT_PASS_BWD = 1 };
+
+#define OFT_MAX_SEGMENTS 8
+
+/* Dense OFT linear layer: x [M, K] -> y [M, N], N = sum(seg).
+ * Constraints: M >= 0 (M == 0 is a no-op); K >= 64 and K % 64 == 0;
+ * b in {16, 32}; 1 <= n_seg <= 8, every seg[s] > 0 and seg[s] % b == 0,
+ * N % 32 == 0; INT4: g in {32, 64, 128} and K % g == 0. */
+typedef struct {
+  int32_t M, K, N;
+  int32_t x_dtype; /* OFT_DT_BF16 | OFT_DT_F32; y and dx use the same dtype */
+  int32_t w_fmt;   /* OFT_W_INT4 | OFT_W_FP8_E4M3                          */
+  int32_t g;       /* INT4 group size along K (ignored for FP8)            */
+  int32_t b;       /* OFT block size                                       */
+  int32_t n_seg;
+  int32_t seg[OFT_MAX_SEGMENTS];
+} oft_linear_desc;
+
+/* MoE layer: T tokens, E experts, top-k routing, hidden H, expert
+ * intermediate I.  Per expert e: gate/up weight [2I, H] (gate rows [0, I),
+ * up rows [I, 2I)) with its own adapter of 2I/b blocks (gate blocks first),
+ * down weight [H, I] without adapter; all INT4 with group g.
+ * Constraints: T >= 0; 1 <= k <= 16; k <= E <= 1024; H % 64 == 0;
+ * I % 64 == 0; b in {16, 32}; I % b == 0; g in {32, 64, 128}; H % g == 0;
+ * I % g == 0; chunk >= 1; renorm in {0, 1}. */
+typedef struct {
+  int32_t T, E, k, H, I, g, b;
+  int32_t chunk;  /* active experts per chunk (scheduling unit)            */
+  int32_t renorm; /* 0: combine weights = softmax over all E at the chosen
+                     experts; 1: renormalised over the k chosen             */
+} oft_moe_desc;
+
+/* Routing tables: device pointers, caller-allocated, written by the
+ * forward (oft_moe_route / oft_moe_grouped_fwd) and read by the backward.
+ * P = T*k routed (token, slot) pairs, pair id t*k + j. */
+typedef struct {
+  int32_t* topk_idx;        /* [T, k] expert of slot j, descending logit, ties -> lower id */
+  float* topk_w;            /* [T, k] combine weights                            */
+  int32_t* counts;          /* [E]    pairs per expert                           */
+  int32_t* offsets;         /* [E+1]  exclusive scan of counts                   */
+  int32_t* perm;            /* [P]    pos -> pair id, ordered by (expert, token)  */
+  int32_t* inv_perm;        /* [P]    pair id -> pos                             */
+  int32_t* active;          /* [E]    active expert ids ascending, then -1        */
+  int32_t* n_active;        /* [1]                                               */
+  int32_t* chunk_of_expert; /* [E]    active rank / chunk, -1 when inactive      */
+} oft_moe_routing;
+
+/* ---- helpers ------------------------------------------------------------ */
+int32_t oft_abi_version(void);
+const char* oft_status_str(int32_t status); /* static string, never NULL */
+int32_t oft_last_hip_error(void);           /* hipError_t of the last OFT_EHIP */
+
+/* ---- Cayley map (adapter -> rotation) ------------------------------------
+ * Per block: A = I - Q_j, R_j = (I + Q_j) A^-1 = 2 A^-1 - I, by Gauss-Jordan
+ * elimination without pivoting in fp32 (the symmetric part of A is I, so the
+ * pivots stay >= 1).
+ * q_bf16 [nblk, b(b-1)/2] -> R_f32 [nblk, b, b] and, when R_ops is not NULL,
+ * the bf16 operand pack [nblk, 2, b, b] (R, R^T; round to nearest even).
+ * nblk == 0 is a no-op.  Errors: OFT_EINVAL (null, nblk < 0),
+ * OFT_EUNSUPPORTED (b not in {16, 32}). */
+int32_t cayley_build(const uint16_t* q_bf16, int32_t nblk, int32_t b, float* R_f32,
+                     uint16_t* R_ops_or_null, void* stream);
+
+/* ---- dequantisation hook (what the matrix cores consume) ------------------
+ * INT4: out[r][c] = bf16_RNE(q[r][c] * s[r][c / g]) (the product is exact in
+ * fp32, so this is one rounding).  FP8: out[r][c] = e4m3fn(code) exactly;
+ * the per-row scale is NOT applied (the GEMMs apply it in fp32 outside the
+ * K loop).  codes: INT4 [rows, cols/2] / FP8 [rows, cols]; scales: fp16
+ * [rows, cols/g] / ignored for FP8 (may be NULL); out_bf16 [rows, cols].
+ * Constraints: rows, cols >= 0, cols % 8 == 0; INT4: g in {32, 64, 128},
+ * cols % g == 0. */
+int32_t oft_dequant(int32_t w_fmt, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
+                    const void* scales, uint16_t* out_bf16, void* stream);
+
+/* ---- dense layer ----------------------------------------------------------
+ * Workspace query for `pass` (OFT_PASS_FWD / OFT_PASS_BWD); writes *bytes. */
+int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_t* bytes);
+
+/* Forward: y = rot_R(x . dequant(W0)^T).
+ * x [M, K] (x_dtype), w_codes / w_scales (w_fmt layout, N rows, K cols),
+ * R_ops from cayley_build, y [M, N] (x_dtype).  The dequantised tile never
+ * leaves LDS; bf16 matrix-core products accumulate in fp32; the FP8 row
+ * scale multiplies the fp32 accumulator; the block rotation runs in the
+ * epilogue on bf16 operands with fp32 accumulation. */
+int32_t oft_linear_fwd(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
+                       const void* w_scales, const uint16_t* R_ops, void* y, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Backward of <dy, y>: dx = rot_R^T(dy) . dequant(W0) and dq (fp32, packed
+ * like q).  dy [M, N] bf16; y_saved [M, N] (x_dtype) is the forward output
+ * (dq uses Z = y R recomputed from it); R_f32 / R_ops from cayley_build.
+ * dx_or_null [M, K] (x_dtype) and dq_or_null [nblk, b(b-1)/2] may each be
+ * NULL to skip that gradient.  No gradient of the frozen base is formed. */
+int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void* y_saved,
+                       const uint8_t* w_codes, const void* w_scales, const float* R_f32,
+                       const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ---- MoE layer ------------------------------------------------------------ */
+int32_t oft_moe_workspace_bytes(const oft_moe_desc* d, int32_t pass, size_t* bytes);
+
+/* Routing only: top-k of fp32 logits [T, E] (descending, ties to the lower
+ * expert id), softmax combine weights, per-expert counts, exclusive-scan
+ * offsets, the stable (expert, token) permutation and its inverse, the
+ * active-expert list and chunk table.  All on the device, no host sync. */
+int32_t oft_moe_route(const oft_moe_desc* d, const float* logits, const oft_moe_routing* rt,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Forward: routing (as oft_moe_route), then for the active experts, chunk by
+ * chunk, the gate/up dequant grouped GEMM over the gathered token rows with
+ * the per-expert split rotation in its epilogue -> h_saved [P, 2I] bf16 in
+ * permuted order; SwiGLU; the down dequant grouped GEMM; and the combine
+ * y[t] = sum_j w[t,j] O[inv_perm[t*k+j]] (fixed order over j) -> y [T, H].
+ * x [T, H] bf16; wgu_codes [E, 2I, H/2], wgu_scales fp16 [E, 2I, H/g];
+ * wd_codes [E, H, I/2], wd_scales fp16 [E, H, I/g]; R_ops [E, 2I/b, 2, b, b]. */
+int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const float* logits,
+                            const uint8_t* wgu_codes, const uint16_t* wgu_scales,
+                            const uint8_t* wd_codes, const uint16_t* wd_scales,
+                            const uint16_t* R_ops, const oft_moe_routing* rt,
+                            uint16_t* h_saved, uint16_t* y, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Backward of <dy, y> with the routing fixed: dx [T, H] bf16 through the
+ * experts, dq fp32 [E, 2I/b, b(b-1)/2] (zero for inactive experts) and
+ * dw fp32 [T, k] = <dy[t], W_d,e . act>.  Any of the three may be NULL.
+ * Reads rt and h_saved from the forward; re-dequantises the weights. */
+int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft_moe_routing* rt,
+                            const uint16_t* h_saved, const uint8_t* wgu_codes,
+                            const uint16_t* wgu_scales, const uint8_t* wd_codes,
+                            const uint16_t* wd_scales, const float* R_f32,
+                            const uint16_t* R_ops, uint16_t* dx_or_null, float* dq_or_null,
+                            float* dw_or_null, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OFT_H_ */

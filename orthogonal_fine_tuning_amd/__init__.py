@@ -1,0 +1,125 @@
+"""OFT dequant-GEMM for AMD Instinct MI355X (gfx950): Python binding.
+
+Every function here marshals torch tensors (device memory) into the C ABI of
+liboft.so (include/oft.h) and calls it on the current torch stream.  All
+arithmetic runs in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+from . import _lib
+from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_FP8_E4M3,
+                   OFT_W_INT4, OftError, oft_linear_desc, oft_moe_desc, oft_moe_routing)
+
+__all__ = [
+    "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
+    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_bwd", "oft_moe_workspace_bytes",
+    "oft_moe_route", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
+    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_PASS_FWD", "OFT_PASS_BWD",
+]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(int(stream))
+    import torch
+
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def abi_version() -> int:
+    return _lib.load().oft_abi_version()
+
+
+def linear_desc(M, K, segs, b, x_dtype=OFT_DT_BF16, w_fmt=OFT_W_INT4, g=0) -> oft_linear_desc:
+    d = oft_linear_desc()
+    d.M, d.K, d.N = int(M), int(K), int(sum(segs))
+    d.x_dtype, d.w_fmt, d.g, d.b = int(x_dtype), int(w_fmt), int(g), int(b)
+    d.n_seg = len(segs)
+    for i, s in enumerate(segs):
+        d.seg[i] = int(s)
+    return d
+
+
+def moe_desc(T, E, k, H, I, g, b, chunk, renorm=0) -> oft_moe_desc:
+    d = oft_moe_desc()
+    d.T, d.E, d.k, d.H, d.I, d.g, d.b, d.chunk, d.renorm = (int(v) for v in
+                                                            (T, E, k, H, I, g, b, chunk, renorm))
+    return d
+
+
+def moe_routing(topk_idx, topk_w, counts, offsets, perm, inv_perm, active, n_active,
+                chunk_of_expert) -> oft_moe_routing:
+    rt = oft_moe_routing()
+    for name, t in (("topk_idx", topk_idx), ("topk_w", topk_w), ("counts", counts),
+                    ("offsets", offsets), ("perm", perm), ("inv_perm", inv_perm),
+                    ("active", active), ("n_active", n_active),
+                    ("chunk_of_expert", chunk_of_expert)):
+        setattr(rt, name, t.data_ptr())
+    return rt
+
+
+def cayley_build(q, nblk, b, R_f32, R_ops=None, stream=None):
+    _lib.check(_lib.load().cayley_build(_ptr(q), nblk, b, _ptr(R_f32), _ptr(R_ops),
+                                        _stream(stream)), "cayley_build")
+
+
+def oft_dequant(w_fmt, rows, cols, g, codes, scales, out, stream=None):
+    _lib.check(_lib.load().oft_dequant(w_fmt, rows, cols, g, _ptr(codes), _ptr(scales), _ptr(out),
+                                       _stream(stream)), "oft_dequant")
+
+
+def oft_linear_workspace_bytes(desc, pass_) -> int:
+    n = C.c_size_t(0)
+    _lib.check(_lib.load().oft_linear_workspace_bytes(C.byref(desc), pass_, C.byref(n)),
+               "oft_linear_workspace_bytes")
+    return n.value
+
+
+def oft_linear_fwd(desc, x, w_codes, w_scales, R_ops, y, ws=None, ws_bytes=0, stream=None):
+    _lib.check(_lib.load().oft_linear_fwd(C.byref(desc), _ptr(x), _ptr(w_codes), _ptr(w_scales),
+                                          _ptr(R_ops), _ptr(y), _ptr(ws), ws_bytes,
+                                          _stream(stream)), "oft_linear_fwd")
+
+
+def oft_linear_bwd(desc, dy, y_saved, w_codes, w_scales, R_f32, R_ops, dx=None, dq=None, ws=None,
+                   ws_bytes=0, stream=None):
+    _lib.check(_lib.load().oft_linear_bwd(C.byref(desc), _ptr(dy), _ptr(y_saved), _ptr(w_codes),
+                                          _ptr(w_scales), _ptr(R_f32), _ptr(R_ops), _ptr(dx),
+                                          _ptr(dq), _ptr(ws), ws_bytes, _stream(stream)),
+               "oft_linear_bwd")
+
+
+def oft_moe_workspace_bytes(desc, pass_) -> int:
+    n = C.c_size_t(0)
+    _lib.check(_lib.load().oft_moe_workspace_bytes(C.byref(desc), pass_, C.byref(n)),
+               "oft_moe_workspace_bytes")
+    return n.value
+
+
+def oft_moe_route(desc, logits, rt, ws, ws_bytes, stream=None):
+    _lib.check(_lib.load().oft_moe_route(C.byref(desc), _ptr(logits), C.byref(rt), _ptr(ws),
+                                         ws_bytes, _stream(stream)), "oft_moe_route")
+
+
+def oft_moe_grouped_fwd(desc, x, logits, wgu_codes, wgu_scales, wd_codes, wd_scales, R_ops, rt,
+                        h_saved, y, ws, ws_bytes, stream=None):
+    _lib.check(_lib.load().oft_moe_grouped_fwd(
+        C.byref(desc), _ptr(x), _ptr(logits), _ptr(wgu_codes), _ptr(wgu_scales), _ptr(wd_codes),
+        _ptr(wd_scales), _ptr(R_ops), C.byref(rt), _ptr(h_saved), _ptr(y), _ptr(ws), ws_bytes,
+        _stream(stream)), "oft_moe_grouped_fwd")
+
+
+def oft_moe_grouped_bwd(desc, dy, rt, h_saved, wgu_codes, wgu_scales, wd_codes, wd_scales, R_f32,
+                        R_ops, dx=None, dq=None, dw=None, ws=None, ws_bytes=0, stream=None):
+    _lib.check(_lib.load().oft_moe_grouped_bwd(
+        C.byref(desc), _ptr(dy), C.byref(rt), _ptr(h_saved), _ptr(wgu_codes), _ptr(wgu_scales),
+        _ptr(wd_codes), _ptr(wd_scales), _ptr(R_f32), _ptr(R_ops), _ptr(dx), _ptr(dq), _ptr(dw),
+        _ptr(ws), ws_bytes, _stream(stream)), "oft_moe_grouped_bwd")

@@ -1,0 +1,170 @@
+// extern "C" entry points of liboft (declared in include/oft.h).
+//
+// Every call validates its arguments on the host first; only then does it
+// touch the HIP runtime.  On a validation error nothing is enqueued and no
+// output is written.
+#include <hip/hip_runtime.h>
+
+#include "oft.h"
+#include "oft_launch.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return OFT_OK;
+  g_last_hip = static_cast<int>(e);
+  return OFT_EHIP;
+}
+
+bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
+
+int32_t validate_linear(const oft_linear_desc* d) {
+  if (d == nullptr) return OFT_EINVAL;
+  if (d->M < 0 || d->K <= 0 || d->N <= 0) return OFT_EINVAL;
+  if (d->M > (1 << 24) || d->K > (1 << 20) || d->N > (1 << 20)) return OFT_EUNSUPPORTED;
+  if (d->x_dtype != OFT_DT_BF16 && d->x_dtype != OFT_DT_F32) return OFT_EDTYPE;
+  if (d->w_fmt != OFT_W_INT4 && d->w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
+  if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;
+  if (d->n_seg < 1 || d->n_seg > OFT_MAX_SEGMENTS) return OFT_EUNSUPPORTED;
+  long long sum = 0;
+  for (int s = 0; s < d->n_seg; ++s) {
+    if (d->seg[s] <= 0 || d->seg[s] % d->b != 0) return OFT_ESHAPE;
+    sum += d->seg[s];
+  }
+  if (sum != d->N) return OFT_ESHAPE;
+  if (d->N % 32 != 0 || d->K % 64 != 0) return OFT_ESHAPE;
+  if (d->w_fmt == OFT_W_INT4) {
+    if (!group_ok(d->g)) return OFT_EUNSUPPORTED;
+    if (d->K % d->g != 0) return OFT_ESHAPE;
+  }
+  return OFT_OK;
+}
+
+oft::DenseArgs dense_args(const oft_linear_desc* d) {
+  oft::DenseArgs a;
+  a.M = d->M;
+  a.K = d->K;
+  a.N = d->N;
+  a.g = d->w_fmt == OFT_W_INT4 ? d->g : 0;
+  a.b = d->b;
+  a.xf32 = d->x_dtype == OFT_DT_F32;
+  a.fp8 = d->w_fmt == OFT_W_FP8_E4M3;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oft_abi_version(void) { return OFT_ABI_VERSION; }
+
+const char* oft_status_str(int32_t s) {
+  switch (s) {
+    case OFT_OK: return "OFT_OK: success";
+    case OFT_EINVAL: return "OFT_EINVAL: null or misaligned pointer, or bad size";
+    case OFT_ESHAPE: return "OFT_ESHAPE: shape constraint violated";
+    case OFT_EDTYPE: return "OFT_EDTYPE: unknown dtype or weight format";
+    case OFT_EUNSUPPORTED: return "OFT_EUNSUPPORTED: configuration not implemented";
+    case OFT_EWORKSPACE: return "OFT_EWORKSPACE: workspace too small";
+    case OFT_EHIP: return "OFT_EHIP: HIP launch failed (see oft_last_hip_error)";
+    default: return "unknown oft status";
+  }
+}
+
+int32_t oft_last_hip_error(void) { return g_last_hip; }
+
+int32_t cayley_build(const uint16_t* q_bf16, int32_t nblk, int32_t b, float* R_f32,
+                     uint16_t* R_ops_or_null, void* stream) {
+  if (nblk < 0) return OFT_EINVAL;
+  if (b != 16 && b != 32) return OFT_EUNSUPPORTED;
+  if (nblk == 0) return OFT_OK;
+  if (q_bf16 == nullptr || !ptr_ok(R_f32) || !opt_ok(R_ops_or_null)) return OFT_EINVAL;
+  return hip_status(oft::launch_cayley(q_bf16, nblk, b, R_f32, R_ops_or_null,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int32_t oft_dequant(int32_t w_fmt, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
+                    const void* scales, uint16_t* out_bf16, void* stream) {
+  if (w_fmt != OFT_W_INT4 && w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
+  if (rows < 0 || cols < 0) return OFT_EINVAL;
+  if (cols % 8 != 0) return OFT_ESHAPE;
+  if (w_fmt == OFT_W_INT4) {
+    if (!group_ok(g)) return OFT_EUNSUPPORTED;
+    if (cols % g != 0) return OFT_ESHAPE;
+  }
+  if ((long long)rows * cols == 0) return OFT_OK;
+  if (!ptr_ok(codes) || !ptr_ok(out_bf16)) return OFT_EINVAL;
+  if (w_fmt == OFT_W_INT4 && !ptr_ok(scales)) return OFT_EINVAL;
+  return hip_status(oft::launch_dequant(w_fmt, rows, cols, g, codes, scales, out_bf16,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_t* bytes) {
+  if (bytes == nullptr) return OFT_EINVAL;
+  const int32_t v = validate_linear(d);
+  if (v != OFT_OK) return v;
+  if (pass == OFT_PASS_FWD) {
+    *bytes = 0;
+  } else if (pass == OFT_PASS_BWD) {
+    *bytes = oft::plan_dq(d->M, d->N).part_bytes;
+  } else {
+    return OFT_EINVAL;
+  }
+  return OFT_OK;
+}
+
+int32_t oft_linear_fwd(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
+                       const void* w_scales, const uint16_t* R_ops, void* y, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const int32_t v = validate_linear(d);
+  if (v != OFT_OK) return v;
+  if (d->M == 0) return OFT_OK;
+  if (!ptr_ok(x) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(R_ops) || !ptr_ok(y))
+    return OFT_EINVAL;
+  return hip_status(oft::launch_linear_fwd(dense_args(d), x, w_codes, w_scales, R_ops, y,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void* y_saved,
+                       const uint8_t* w_codes, const void* w_scales, const float* R_f32,
+                       const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,
+                       size_t ws_bytes, void* stream) {
+  const int32_t v = validate_linear(d);
+  if (v != OFT_OK) return v;
+  if (!opt_ok(dx_or_null) || !opt_ok(dq_or_null)) return OFT_EINVAL;
+  const bool want_dx = dx_or_null != nullptr && d->M > 0;
+  const bool want_dq = dq_or_null != nullptr;
+  const oft::DqPlan plan = oft::plan_dq(d->M, d->N);
+  if (want_dx) {
+    if (!ptr_ok(dy) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(R_ops)) return OFT_EINVAL;
+  }
+  if (want_dq) {
+    if (!ptr_ok(R_f32)) return OFT_EINVAL;
+    if (d->M > 0) {
+      if (!ptr_ok(dy) || !ptr_ok(y_saved)) return OFT_EINVAL;
+      if (!ptr_ok(ws)) return OFT_EINVAL;
+      if (ws_bytes < plan.part_bytes) return OFT_EWORKSPACE;
+    }
+  }
+  const oft::DenseArgs a = dense_args(d);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (want_dq) {
+    const int32_t s = hip_status(oft::launch_linear_dq(a, plan, dy, y_saved, R_f32, dq_or_null,
+                                                       static_cast<float*>(ws), st));
+    if (s != OFT_OK) return s;
+  }
+  if (want_dx) {
+    return hip_status(oft::launch_linear_bwd_dx(a, dy, w_codes, w_scales, R_ops, dx_or_null, st));
+  }
+  return OFT_OK;
+}
+
+}  // extern "C"

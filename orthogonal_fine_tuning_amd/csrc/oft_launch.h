@@ -1,0 +1,44 @@
+// Internal launchers (host side).  Arguments are validated by the C-ABI
+// layer (abi.cpp) before any of these is called; each returns the
+// hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oft {
+
+hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
+                         hipStream_t st);
+
+hipError_t launch_dequant(int fmt, int rows, int cols, int g, const uint8_t* codes,
+                          const void* scales, uint16_t* out, hipStream_t st);
+
+// Dense layer.  xf32: x / y / dx are fp32 (else bf16); fp8: FP8 weights
+// (else INT4 with group g).
+struct DenseArgs {
+  int M, K, N, g, b;
+  bool xf32, fp8;
+};
+
+hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
+                             const uint16_t* Rops, void* y, hipStream_t st);
+
+// Split of the M reduction used by dq (deterministic partials).
+struct DqPlan {
+  int nsplit;          // number of M slices
+  int rows_per_split;  // multiple of 64
+  int ng32;            // N / 32 column groups
+  size_t part_bytes;   // fp32 partial sums, nsplit * ng32 * 32 * 32 * 4
+};
+DqPlan plan_dq(int M, int N);
+
+hipError_t launch_linear_bwd_dx(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc,
+                                const void* ws, const uint16_t* Rops, void* dx, hipStream_t st);
+
+hipError_t launch_linear_dq(const DenseArgs& a, const DqPlan& p, const uint16_t* dy,
+                            const void* y, const float* Rf, float* dq, float* part,
+                            hipStream_t st);
+
+}  // namespace oft

@@ -1,0 +1,164 @@
+"""GPU parity of the dense OFT linear path against the fp64 oracle.
+
+Tolerances: outputs and gradients max|a - ref| / max|ref| <= 2e-2 (bf16
+matrix-core arithmetic); fp32 R orthogonality <= 1e-3; dequantised weights
+bit-exact.
+"""
+import numpy as np
+import pytest
+
+from oft_inputs import CONFIGS, DenseConfig, make_dense
+from oracle import codec, dense as odense
+from tests.helpers import bf16_to_f64, dev, err, host
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+SMALL = {
+    "tiny_qkv": CONFIGS["tiny_qkv"],
+    # several tiles in every dimension, ragged M / N / n-step / K tile
+    "fp8_b32_ragged": DenseConfig("fp8_b32_ragged", M=300, K=512, segs=(256, 64, 96), b=32,
+                                  x_dtype="bf16", w_fmt="fp8"),
+    "int4_g64_ragged_k": DenseConfig("int4_g64_ragged_k", M=520, K=576, segs=(320, 320), b=32,
+                                     x_dtype="bf16", w_fmt="int4", g=64),
+    "int4_g128_b16": DenseConfig("int4_g128_b16", M=257, K=384, segs=(160, 96), b=16,
+                                 x_dtype="bf16", w_fmt="int4", g=128, q_std=0.05),
+    "fp8_b16_f32x": DenseConfig("fp8_b16_f32x", M=70, K=128, segs=(48, 16, 32), b=16,
+                                x_dtype="f32", w_fmt="fp8"),
+    "int4_g32_f32x_b32": DenseConfig("int4_g32_f32x_b32", M=33, K=256, segs=(64, 32), b=32,
+                                     x_dtype="f32", w_fmt="int4", g=32),
+    "decode_m1": DenseConfig("decode_m1", M=1, K=256, segs=(128, 128), b=32, x_dtype="bf16",
+                             w_fmt="int4", g=128),
+}
+
+
+def _run_gpu(inp, want_bwd=True):
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = inp["cfg"]
+    xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
+    wf = oft.OFT_W_FP8_E4M3 if cfg.w_fmt == "fp8" else oft.OFT_W_INT4
+    d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
+    tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
+    q = dev(inp["p"])
+    Rf = torch.empty((cfg.nblk, cfg.b, cfg.b), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((cfg.nblk, 2, cfg.b, cfg.b), dtype=torch.int16, device="cuda")
+    oft.cayley_build(q, cfg.nblk, cfg.b, Rf, Rops)
+    x, wc, ws = dev(inp["x"]), dev(inp["w_codes"]), dev(inp["w_scales"])
+    y = torch.empty((cfg.M, cfg.N), dtype=tdt, device="cuda")
+    oft.oft_linear_fwd(d, x, wc, ws, Rops, y)
+    out = {"Rf": Rf, "Rops": Rops, "y": y}
+    if want_bwd:
+        dy = dev(inp["dy"])
+        dx = torch.empty((cfg.M, cfg.K), dtype=tdt, device="cuda")
+        dq = torch.empty((cfg.nblk, cfg.npair), dtype=torch.float32, device="cuda")
+        nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
+        work = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb)
+        out.update(dx=dx, dq=dq)
+    torch.cuda.synchronize()
+    return out
+
+
+def _to64(t, cfg):
+    a = host(t)
+    return a.astype(np.float64) if cfg.x_dtype == "f32" else bf16_to_f64(a)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dense_parity_small(name):
+    cfg = SMALL[name]
+    print(f"[dense parity] {name} M={cfg.M} K={cfg.K} N={cfg.N} b={cfg.b} {cfg.w_fmt}", flush=True)
+    inp = make_dense(cfg, seed=0)
+    ref = odense.run(inp)
+    out = _run_gpu(inp)
+    R = host(out["Rf"]).astype(np.float64)
+    orth = np.abs(np.swapaxes(R, 1, 2) @ R - np.eye(cfg.b)).max()
+    assert orth <= 1e-3, orth
+    assert err(R, ref["R"]) <= 1e-5
+    e_y = err(_to64(out["y"], cfg), ref["y"])
+    e_dx = err(_to64(out["dx"], cfg), ref["dx"])
+    e_dq = err(host(out["dq"]), ref["dp"])
+    print(f"  err y={e_y:.2e} dx={e_dx:.2e} dq={e_dq:.2e} orth={orth:.1e}", flush=True)
+    assert e_y <= TOL and e_dx <= TOL and e_dq <= TOL
+
+
+def test_cayley_ops_pack_is_bf16_of_f32():
+    import torch
+
+    cfg = SMALL["fp8_b32_ragged"]
+    out = _run_gpu(make_dense(cfg, seed=1), want_bwd=False)
+    R = host(out["Rf"])
+    ops = host(out["Rops"], np.uint16)
+    want = codec.f32_to_bf16_bits(R)
+    assert np.array_equal(ops[:, 0], want)
+    assert np.array_equal(ops[:, 1], np.swapaxes(want, 1, 2))
+
+
+@pytest.mark.parametrize("fmt,g", [("int4", 32), ("int4", 64), ("int4", 128), ("fp8", 0)])
+def test_dequant_bit_exact(fmt, g):
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    rows, cols = 96, 512
+    cfg = DenseConfig("dq", M=1, K=cols, segs=(rows,), b=32, x_dtype="bf16", w_fmt=fmt, g=g)
+    inp = make_dense(cfg, seed=3, with_dy=False)
+    if fmt == "fp8":  # every e4m3fn code except NaN, in every row
+        codes = np.tile(np.arange(256, dtype=np.uint8), (rows, cols // 256))
+        codes[(codes & 0x7F) == 0x7F] = 0
+        inp["w_codes"] = codes
+        ref = codec.f32_to_bf16_bits(odense.dequant_fp8_codes(codes).astype(np.float32))
+    else:
+        ref = codec.f32_to_bf16_bits(odense.dequant_int4(inp["w_codes"], inp["w_scales"], g)
+                                     .astype(np.float32))
+    out = torch.empty((rows, cols), dtype=torch.int16, device="cuda")
+    wf = oft.OFT_W_FP8_E4M3 if fmt == "fp8" else oft.OFT_W_INT4
+    oft.oft_dequant(wf, rows, cols, g, dev(inp["w_codes"]), dev(inp["w_scales"]), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out, np.uint16), ref)
+
+
+def test_q_zero_gives_plain_dequant_gemm():
+    """Q = 0: R = I exactly, so y equals the un-rotated dequant GEMM (to bf16)."""
+    cfg = SMALL["int4_g64_ragged_k"]
+    inp = make_dense(cfg, seed=2)
+    inp["p"] = np.zeros_like(inp["p"])
+    out = _run_gpu(inp)
+    R = host(out["Rf"])
+    assert np.array_equal(R, np.broadcast_to(np.eye(cfg.b, dtype=np.float32), R.shape))
+    W = odense.dequant(inp)
+    ref = odense.x_f64(inp) @ W.T
+    assert err(_to64(out["y"], cfg), ref) <= TOL
+    # dq at Q = 0 follows the closed form 2 (G_il - G_li); compared to the oracle
+    assert err(host(out["dq"]), odense.run(inp)["dp"]) <= TOL
+
+
+def test_m_zero_is_noop_and_dq_zero():
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = SMALL["fp8_b32_ragged"].with_(M=0)
+    d = oft.linear_desc(0, cfg.K, cfg.segs, cfg.b, oft.OFT_DT_BF16, oft.OFT_W_FP8_E4M3, 0)
+    inp = make_dense(cfg.with_(M=1), seed=0)
+    q = dev(inp["p"])
+    Rf = torch.empty((cfg.nblk, 32, 32), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((cfg.nblk, 2, 32, 32), dtype=torch.int16, device="cuda")
+    oft.cayley_build(q, cfg.nblk, 32, Rf, Rops)
+    dq = torch.full((cfg.nblk, cfg.npair), 7.0, dtype=torch.float32, device="cuda")
+    nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
+    work = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    wc, ws = dev(inp["w_codes"]), dev(inp["w_scales"])
+    oft.oft_linear_fwd(d, None, wc, ws, Rops, None)
+    oft.oft_linear_bwd(d, None, None, wc, ws, Rf, Rops, None, dq, work, nb)
+    torch.cuda.synchronize()
+    assert np.all(host(dq) == 0.0)
+
+
+def test_deterministic_bitwise():
+    cfg = SMALL["fp8_b32_ragged"]
+    inp = make_dense(cfg, seed=4)
+    a = _run_gpu(inp)
+    b = _run_gpu(inp)
+    for k in ("y", "dx", "dq"):
+        assert np.array_equal(host(a[k]), host(b[k])), k
