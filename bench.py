@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the OFT dequant-GEMM hot path on one MI355X.
+
+One step = one pass of the whole dense path over one batch: Cayley build of
+the adapter rotations, the forward (dequant GEMM + split-projection rotation
+epilogue) and the backward (dX with the rotation prologue, and dQ).  The
+default workload is the fused Q/K/V projection of a 4B-shaped model: 4096
+tokens, hidden 2560, out 6144 = 4096 + 1024 + 1024, FP8 e4m3 weights with
+per-channel scales, OFT blocks of 32.  Inputs are seeded synthetic data,
+resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0).  ``value`` is algorithmic TFLOP/s of the
+whole step (fwd 2MNK + 2MNb, bwd 2MNK + 4MNb; the Cayley build is timed but
+its flops are not counted).  ``roofline`` reports the forward GEMM kernel:
+algorithmic flops per launch over its mean duration from HIP events
+recorded on the launch stream inside the timed region.  ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "OFT dequant-GEMM fwd+bwd TFLOP/s and HBM GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qkv_4b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="token rows of the oracle sample for cpu_baseline")
+    return ap.parse_args()
+
+
+def dense_flops(cfg):
+    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
+    fwd = 2 * M * N * K + 2 * M * N * b
+    bwd = 2 * M * N * K + 4 * M * N * b
+    return fwd, bwd
+
+
+def dense_bytes(cfg):
+    """Algorithmic HBM bytes: what the method must read and write once."""
+    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
+    xb = 4 if cfg.x_dtype == "f32" else 2
+    if cfg.w_fmt == "int4":
+        wbytes = N * K // 2 + N * (K // cfg.g) * 2
+    else:
+        wbytes = N * K + N * 4
+    nblk = N // b
+    rops = nblk * 2 * b * b * 2
+    rf = nblk * b * b * 4
+    npair = b * (b - 1) // 2
+    fwd = wbytes + M * K * xb + M * N * xb + rops
+    bwd = wbytes + M * N * 2 + M * N * xb + M * K * xb + rops + rf + nblk * npair * 4
+    return fwd, bwd
+
+
+def kernel_source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, sha):
+    """HBM traffic per launch from committed rocprofv3 counter runs, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, rows):
+    import numpy as np
+    from oracle import dense as odense
+
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        cores = os.cpu_count() or 1
+    ms = min(rows, cfg.M)
+    sub = dict(inp)
+    sub["cfg"] = cfg.with_(M=ms)
+    sub["x"] = inp["x"][:ms]
+    sub["dy"] = inp["dy"][:ms]
+    t0 = time.perf_counter()
+    odense.run(sub)
+    dt = time.perf_counter() - t0
+    f, b = dense_flops(sub["cfg"])
+    return {"value": (f + b) / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{cfg.name}: first {ms} of {cfg.M} token rows, dequant + Cayley + fwd + "
+                      f"bwd (dX, dQ) in fp64 numpy, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note only)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import orthogonal_fine_tuning_amd as oft
+    from oft_inputs import CONFIGS, make_dense
+
+    cfg = CONFIGS[args.config]
+    if not hasattr(cfg, "segs"):
+        raise SystemExit(f"{args.config} is not a dense configuration")
+    inp = make_dense(cfg, seed=0)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
+    wf = oft.OFT_W_FP8_E4M3 if cfg.w_fmt == "fp8" else oft.OFT_W_INT4
+    d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
+    tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
+    q, x = dev(inp["p"]), dev(inp["x"])
+    wc, ws = dev(inp["w_codes"]), dev(inp["w_scales"])
+    dy = dev(inp["dy"])
+    Rf = torch.empty((cfg.nblk, cfg.b, cfg.b), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((cfg.nblk, 2, cfg.b, cfg.b), dtype=torch.int16, device="cuda")
+    y = torch.empty((cfg.M, cfg.N), dtype=tdt, device="cuda")
+    dx = torch.empty((cfg.M, cfg.K), dtype=tdt, device="cuda")
+    dq = torch.empty((cfg.nblk, cfg.npair), dtype=torch.float32, device="cuda")
+    nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
+    work = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        oft.cayley_build(q, cfg.nblk, cfg.b, Rf, Rops, stream=sp)
+        if ev is not None:
+            ev[1].record(stream)
+        oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp)
+        if ev is not None:
+            ev[2].record(stream)
+        oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_cay = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    ms_per_step = wall / args.steps * 1e3
+    f_fwd, f_bwd = dense_flops(cfg)
+    by_fwd, by_bwd = dense_bytes(cfg)
+    value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
+
+    fwd_src = ["orthogonal_fine_tuning_amd/csrc/linear_fwd.hip",
+               "orthogonal_fine_tuning_amd/csrc/oft_device.h"]
+    sha = kernel_source_sha(fwd_src)
+    achieved = f_fwd / t_fwd / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(f"linear_fwd_kernel:{cfg.name}", sha),
+            "kernel": "linear_fwd_kernel", "kernel_us": round(t_fwd * 1e6, 2),
+            "source_sha": sha}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.M, "in_features": cfg.K,
+                   "out_features": cfg.N, "segments": list(cfg.segs), "oft_block": cfg.b,
+                   "weights": cfg.w_fmt + (f"_g{cfg.g}" if cfg.w_fmt == "int4" else "_e4m3"),
+                   "x_dtype": cfg.x_dtype, "parallelism": "single_gpu"},
+        "roofline": roof,
+        "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
+                      "bwd": round(t_bwd * 1e6, 2)},
+        "phase_rates": {
+            "fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
+            "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
+            "step_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,7 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboft.so")
+LIB_PATH = os.environ.get("OFT_LIBRARY") or os.path.join(_HERE, "liboft.so")
 
 OFT_OK, OFT_EINVAL, OFT_ESHAPE, OFT_EDTYPE, OFT_EUNSUPPORTED, OFT_EWORKSPACE, OFT_EHIP = (
     0, -1, -2, -3, -4, -5, -6)

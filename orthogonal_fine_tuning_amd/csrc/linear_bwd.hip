@@ -25,34 +25,46 @@
 namespace oft {
 namespace {
 
-constexpr int BM = 256;   // tokens per tile
 constexpr int BKO = 128;  // output in-features per tile
 constexpr int BNS = 64;   // channels per contraction step
 constexpr int LDN = BNS + 8;
 
-template <bool XF32, bool FP8, int B>
+// WsT row k keeps channel n at column n ^ wsw(k): rows 8..15 of every 16
+// swap their two 32-channel halves, so the transposed 8-byte stores of a
+// half-wave (4 rows x 64 bytes) spread over all banks, while 16-byte operand
+// reads stay contiguous.
+__device__ __forceinline__ int wsw(int k) { return ((k >> 3) & 1) << 5; }
+
+template <bool XF32, bool FP8, int B, int BM>
 __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
     const uint16_t* __restrict__ dy, const uint8_t* __restrict__ wc, const void* __restrict__ wsv,
     const uint16_t* __restrict__ Rops, void* __restrict__ dxv, int M, int K, int N, int g) {
   __shared__ __attribute__((aligned(16))) uint16_t WsT[BKO * LDN];  // [k][n]
   __shared__ __attribute__((aligned(16))) uint16_t dZs[BM * LDN];   // [m][n]
+  static_assert(BM == 128 || BM == 256, "tile");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int k0 = blockIdx.x * BKO, m0 = blockIdx.y * BM;
   const int wk = wave >> 1, wm = wave & 1;
+  constexpr int TM = BM / 64;   // 32-token tiles per wave
+  constexpr int PM = BM / 128;  // 32-token tiles each wave rotates in the prologue
 
-  // W tile: thread owns rows n0 + 4*rg + q (q < 4), in-features k0 + 8*kg + e (e < 8)
-  const int kg = tid & 15, rg = tid >> 4;
+  // W tile: thread owns rows n0 + 4*rg + q (q < 4), in-features k0 + 8*kg + e
+  // (e < 8).  A wave covers 4 kg x 16 rg, so each transposed LDS write of a
+  // wave fills 4 whole 128-byte rows (no bank conflicts); lanes 4j..4j+3
+  // read 16 contiguous bytes of one row.
+  const int kg = (tid & 3) + 4 * (tid >> 6), rg = (tid >> 2) & 15;
   const bool k_ok = (k0 + 8 * kg) < K;
   uint32_t wr32[4];  // INT4: 8 nibbles per row
   uint2 wr64[4];     // FP8: 8 bytes per row
   float wsc[4];
 
-  // prologue operands: this wave rotates token tiles mt = 2*wave + i (i < 2)
-  uint4 dyf[2][2][2];  // [i][32-channel group][t]
+  // prologue operands: this wave rotates token tiles mt = PM*wave + i (i < PM)
+  uint4 dyf[PM][2][2];  // [i][32-channel group][t]
   uint4 rtf[2][2];     // [32-channel group][t]
+  float4 scf[2][4];    // FP8 channel scales of the step, C-layout order
 
   auto prefetch = [&](int n0) {
 #pragma unroll
@@ -87,9 +99,18 @@ __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
           }
         }
         rtf[grp][t] = v;
+        if constexpr (FP8) {
+          if (t == 0) {
+            const float* s = static_cast<const float*>(wsv);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int m = m0 + (2 * wave + i) * 32 + l32;
+            for (int q = 0; q < 4; ++q)
+              scf[grp][q] = gok ? *reinterpret_cast<const float4*>(s + nb + 8 * q + 4 * g2)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < PM; ++i) {
+          const int m = m0 + (PM * wave + i) * 32 + l32;
           dyf[i][grp][t] = (gok && m < M)
                                ? *reinterpret_cast<const uint4*>(dy + (size_t)m * N + nb + 16 * t + 8 * g2)
                                : zero4();
@@ -98,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
     }
   };
 
-  auto stage = [&](int n0) {
+  auto stage = [&]() {
     // W tile -> LDS, transposed: WsT[k][n]
     uint16_t v[4][8];
 #pragma unroll
@@ -119,27 +140,24 @@ __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
       uint2 p;
       p.x = (uint32_t)v[0][e] | ((uint32_t)v[1][e] << 16);
       p.y = (uint32_t)v[2][e] | ((uint32_t)v[3][e] << 16);
-      *reinterpret_cast<uint2*>(&WsT[(8 * kg + e) * LDN + 4 * rg]) = p;
+      const int k = 8 * kg + e;
+      *reinterpret_cast<uint2*>(&WsT[k * LDN + ((4 * rg) ^ wsw(k))]) = p;
     }
     // prologue: dZ^T = R^T dY^T per 32-channel group, into dZs[m][n]
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
-      const int nb = n0 + 32 * grp;
       float sc[16];
       if constexpr (FP8) {
-        const float* s = static_cast<const float*>(wsv);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (nb < N) f = *reinterpret_cast<const float4*>(s + nb + 8 * q + 4 * g2);
-          sc[4 * q] = f.x;
-          sc[4 * q + 1] = f.y;
-          sc[4 * q + 2] = f.z;
-          sc[4 * q + 3] = f.w;
+          sc[4 * q] = scf[grp][q].x;
+          sc[4 * q + 1] = scf[grp][q].y;
+          sc[4 * q + 2] = scf[grp][q].z;
+          sc[4 * q + 3] = scf[grp][q].w;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < PM; ++i) {
         f32x16 o;
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[r] = 0.0f;
@@ -149,43 +167,57 @@ __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[r] *= sc[r];
         }
-        const int ml = (2 * wave + i) * 32 + l32;
+        const int ml = (PM * wave + i) * 32 + l32;
+        // Lane (m, g2) holds channels 8q + 4g2 + 0..3 in registers 4q..4q+3.
+        // Swapping one 4-channel run with lane m + 32(1 - g2) leaves lane g2
+        // with channels 16h + 8g2 + 0..7 of the pair q = 2h, 2h + 1.
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          *reinterpret_cast<uint2*>(&dZs[ml * LDN + 32 * grp + 8 * q + 4 * g2]) =
-              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+        for (int h = 0; h < 2; ++h) {
+          const uint2 p0 = make_uint2(pack_bf16x2(o[8 * h], o[8 * h + 1]),
+                                      pack_bf16x2(o[8 * h + 2], o[8 * h + 3]));
+          const uint2 p1 = make_uint2(pack_bf16x2(o[8 * h + 4], o[8 * h + 5]),
+                                      pack_bf16x2(o[8 * h + 6], o[8 * h + 7]));
+          const uint2 snd = g2 ? p0 : p1;
+          uint2 rcv;
+          rcv.x = (uint32_t)__shfl_xor((int)snd.x, 32);
+          rcv.y = (uint32_t)__shfl_xor((int)snd.y, 32);
+          const uint4 v = g2 ? make_uint4(rcv.x, rcv.y, p1.x, p1.y) : make_uint4(p0.x, p0.y, rcv.x, rcv.y);
+          *reinterpret_cast<uint4*>(&dZs[ml * LDN + 32 * grp + 16 * h + 8 * g2]) = v;
         }
       }
     }
   };
 
-  f32x16 acc[2][4];
+  f32x16 acc[2][TM];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < TM; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
   prefetch(0);
   for (int n0 = 0; n0 < N; n0 += BNS) {
     __syncthreads();
-    stage(n0);
+    stage();
     __syncthreads();
     if (n0 + BNS < N) prefetch(n0 + BNS);
 #pragma unroll
     for (int kk = 0; kk < BNS / 16; ++kk) {
-      bf16x8 a[2], b[4];
+      bf16x8 a[2], b[TM];
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk)
-        a[tk] = *reinterpret_cast<const bf16x8*>(&WsT[(wk * 64 + tk * 32 + l32) * LDN + kk * 16 + 8 * g2]);
+      {
+        const int k = wk * 64 + tk * 32 + l32;
+        a[tk] = *reinterpret_cast<const bf16x8*>(&WsT[k * LDN + ((kk * 16 + 8 * g2) ^ wsw(k))]);
+      }
 #pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-        b[tm] = *reinterpret_cast<const bf16x8*>(&dZs[(wm * 128 + tm * 32 + l32) * LDN + kk * 16 + 8 * g2]);
+      for (int tm = 0; tm < TM; ++tm)
+        b[tm] = *reinterpret_cast<const bf16x8*>(&dZs[(wm * (BM / 2) + tm * 32 + l32) * LDN + kk * 16 + 8 * g2]);
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
+        for (int tm = 0; tm < TM; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
     }
   }
 
@@ -194,8 +226,8 @@ __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
     const int kb = k0 + wk * 64 + tk * 32;
     if (kb >= K) continue;
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-      const int m = m0 + wm * 128 + tm * 32 + l32;
+    for (int tm = 0; tm < TM; ++tm) {
+      const int m = m0 + wm * (BM / 2) + tm * 32 + l32;
       if (m >= M) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -215,6 +247,11 @@ __global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
 
 // ---------------------------------------------------------------- dq stage 1
 constexpr int LDM = 64 + 8;
+
+// dYT / YT row n keeps token m at column m ^ msw(n) (16-token groups XORed by
+// bits 3..4 of n): the transposed 4-byte stores of a wave hit every bank
+// twice at most, 16-byte operand reads stay contiguous.
+__device__ __forceinline__ int msw(int n) { return ((n >> 3) & 3) << 4; }
 
 template <bool YF32>
 __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restrict__ dy,
@@ -274,16 +311,19 @@ __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restr
         const int sh = 16 * (e & 1);
         const uint32_t pd = ((d0[e >> 1] >> sh) & 0xFFFFu) | (((d1[e >> 1] >> sh) & 0xFFFFu) << 16);
         const uint32_t py = ((y0[e >> 1] >> sh) & 0xFFFFu) | (((y1[e >> 1] >> sh) & 0xFFFFu) << 16);
-        *reinterpret_cast<uint32_t*>(&dYT[(8 * c + e) * LDM + 2 * rp]) = pd;
-        *reinterpret_cast<uint32_t*>(&YT[(8 * c + e) * LDM + 2 * rp]) = py;
+        const int n = 8 * c + e;
+        *reinterpret_cast<uint32_t*>(&dYT[n * LDM + ((2 * rp) ^ msw(n))]) = pd;
+        *reinterpret_cast<uint32_t*>(&YT[n * LDM + ((2 * rp) ^ msw(n))]) = py;
       }
     }
     __syncthreads();
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
       const int kk = 2 * kh + kq;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&dYT[(32 * grp + l32) * LDM + 16 * kk + 8 * g2]);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&YT[(32 * grp + l32) * LDM + 16 * kk + 8 * g2]);
+      const int n = 32 * grp + l32;
+      const int mo = (16 * kk + 8 * g2) ^ msw(n);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&dYT[n * LDM + mo]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&YT[n * LDM + mo]);
       acc = mfma32(a, b, acc);
     }
   }
@@ -308,15 +348,18 @@ __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------- dq stage 2
+// Per block: S = sum of the slice partials (fixed order); with
+// R (R^T + I) = I + R the Cayley gradient is
+//   Gq = (R^T + I) S (I + R) / 2,  dp_il = Gq_il - Gq_li.
 template <int B>
-__global__ __launch_bounds__(64) void dq_final_kernel(const float* __restrict__ part, int nsplit,
-                                                      int ng32, const float* __restrict__ Rf,
-                                                      float* __restrict__ dq) {
+__global__ __launch_bounds__(256) void dq_final_kernel(const float* __restrict__ part, int nsplit,
+                                                       int ng32, const float* __restrict__ Rf,
+                                                       float* __restrict__ dq) {
   __shared__ float S[B][B + 1], Rm[B][B + 1], T1[B][B + 1];
   const int j = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int g32 = (j * B) / 32, off = (j * B) % 32;
-  for (int e = lane; e < B * B; e += 64) {
+  for (int e = tid; e < B * B; e += 256) {
     const int r = e / B, c = e % B;
     float s = 0.0f;
     for (int sp = 0; sp < nsplit; ++sp)
@@ -325,32 +368,24 @@ __global__ __launch_bounds__(64) void dq_final_kernel(const float* __restrict__ 
     Rm[r][c] = Rf[(size_t)j * B * B + e];
   }
   __syncthreads();
-  // G = S R
-  for (int e = lane; e < B * B; e += 64) {
+  for (int e = tid; e < B * B; e += 256) {  // T1 = S (I + R)
     const int r = e / B, c = e % B;
-    float s = 0.0f;
+    float s = S[r][c];
+#pragma unroll 8
     for (int i = 0; i < B; ++i) s += S[r][i] * Rm[i][c];
     T1[r][c] = s;
   }
   __syncthreads();
-  // S <- (R^T + I) G
-  for (int e = lane; e < B * B; e += 64) {
+  for (int e = tid; e < B * B; e += 256) {  // S = (R^T + I) T1 / 2
     const int r = e / B, c = e % B;
     float s = T1[r][c];
+#pragma unroll 8
     for (int i = 0; i < B; ++i) s += Rm[i][r] * T1[i][c];
-    S[r][c] = s;
-  }
-  __syncthreads();
-  // T1 <- S (R^T + I) / 2
-  for (int e = lane; e < B * B; e += 64) {
-    const int r = e / B, c = e % B;
-    float s = S[r][c];
-    for (int i = 0; i < B; ++i) s += S[r][i] * Rm[c][i];
-    T1[r][c] = 0.5f * s;
+    S[r][c] = 0.5f * s;
   }
   __syncthreads();
   constexpr int NP = B * (B - 1) / 2;
-  for (int pidx = lane; pidx < NP; pidx += 64) {
+  for (int pidx = tid; pidx < NP; pidx += 256) {
     // invert the row-major upper-triangle index
     int i = 0, rem = pidx;
     while (rem >= B - 1 - i) {
@@ -358,16 +393,20 @@ __global__ __launch_bounds__(64) void dq_final_kernel(const float* __restrict__ 
       ++i;
     }
     const int l = i + 1 + rem;
-    dq[(size_t)j * NP + pidx] = T1[i][l] - T1[l][i];
+    dq[(size_t)j * NP + pidx] = S[i][l] - S[l][i];
   }
 }
 
 template <bool XF32, bool FP8, int B>
 hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc, const void* ws,
                        const uint16_t* Rops, void* dx, hipStream_t st) {
+#ifndef OFT_DX_BM
+#define OFT_DX_BM 128
+#endif
+  constexpr int BM = OFT_DX_BM;
   dim3 grid((a.K + BKO - 1) / BKO, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL((linear_bwd_dx_kernel<XF32, FP8, B>), grid, dim3(256), 0, st, dy, wc, ws, Rops,
-                     dx, a.M, a.K, a.N, a.g);
+  hipLaunchKernelGGL((linear_bwd_dx_kernel<XF32, FP8, B, BM>), grid, dim3(256), 0, st, dy, wc, ws,
+                     Rops, dx, a.M, a.K, a.N, a.g);
   return hipGetLastError();
 }
 
@@ -424,9 +463,9 @@ hipError_t launch_linear_dq(const DenseArgs& a, const DqPlan& p, const uint16_t*
   }
   const int nblk = a.N / a.b;
   if (a.b == 32)
-    hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(64), 0, st, part, p.nsplit, p.ng32, Rf, dq);
+    hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
   else
-    hipLaunchKernelGGL(dq_final_kernel<16>, dim3(nblk), dim3(64), 0, st, part, p.nsplit, p.ng32, Rf, dq);
+    hipLaunchKernelGGL(dq_final_kernel<16>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
   return hipGetLastError();
 }
 
