@@ -36,6 +36,7 @@ __all__ = [
     "CONFIGS",
     "make_dense",
     "make_moe",
+    "make_moe_logits",
     "to_bf16_bits",
     "to_fp16_bits",
 ]
@@ -224,3 +225,15 @@ def make_moe(cfg: MoEConfig, seed: int = 0, with_dy: bool = True) -> dict:
     if with_dy:
         out["dy"] = to_bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
     return out
+
+
+def make_moe_logits(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """The router logits of ``make_moe(cfg, seed)`` without drawing the weights
+    (same stream: x first, then logits, then the optional bias)."""
+    rng = np.random.default_rng(seed)
+    rng.standard_normal((cfg.T, cfg.H), dtype=np.float32)
+    logits = rng.standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    if cfg.bias_std > 0:
+        bias = rng.normal(0.0, cfg.bias_std, size=cfg.E).astype(np.float32)
+        logits = (logits + bias[None, :]).astype(np.float32)
+    return logits

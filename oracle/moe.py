@@ -160,10 +160,33 @@ def forward(inp: dict, rt: dict | None = None, experts=None, threads: int = 1,
     return y, Hsave, rt
 
 
+def expert_backward(inp: dict, e: int, pairs, X, dy, wflat, P=None):
+    """Backward of one expert over the given routed pairs (flat ids t*k + j).
+
+    Returns (dw [n], dp [2I/b, b(b-1)/2], dXp [n, H]); dp covers only the
+    given pairs (all of the expert's pairs give its full gradient).
+    """
+    cfg = inp["cfg"]
+    k, I, b = cfg.k, cfg.I, cfg.b
+    pairs = np.asarray(pairs, dtype=np.int64)
+    t = pairs // k
+    Wgu, Wd, R = expert_weights(inp, e, P)
+    Z, Hh, act, _ = expert_forward(X[t], Wgu, Wd, R, I)
+    dA_u = dy[t] @ Wd  # d act before the combine weight
+    dw = np.sum(dA_u * act, axis=1)
+    dA = wflat[pairs][:, None] * dA_u
+    hg, hu = Hh[:, :I], Hh[:, I:]
+    sg = 1.0 / (1.0 + np.exp(-hg))
+    dH = np.concatenate([dA * hu * sg * (1.0 + hg * (1.0 - sg)), dA * hg * sg], axis=1)
+    dp = cayley_grad(R, rotation_grad(dH, Z, b))
+    dXp = rotate_adjoint(dH, R) @ Wgu
+    return dw, dp, dXp
+
+
 def backward(inp: dict, rt: dict, experts=None, threads: int = 1, X=None, P=None):
     """Returns (dX [T,H], dp [E, 2I/b, b(b-1)/2], dw [T,k])."""
     cfg = inp["cfg"]
-    T, k, H, I, b = cfg.T, cfg.k, cfg.H, cfg.I, cfg.b
+    T, k, H = cfg.T, cfg.k, cfg.H
     if X is None:
         X = bf16_bits_to_f64(inp["x"])
     dy = bf16_bits_to_f64(inp["dy"])
@@ -174,20 +197,9 @@ def backward(inp: dict, rt: dict, experts=None, threads: int = 1, X=None, P=None
         order = [e for e in order if e in keep]
 
     def one(e):
-        lo, hi = rt["offsets"][e], rt["offsets"][e + 1]
-        pairs = rt["perm"][lo:hi]
-        t = pairs // k
-        Wgu, Wd, R = expert_weights(inp, e, P)
-        Z, Hh, act, _ = expert_forward(X[t], Wgu, Wd, R, I)
-        dA_u = dy[t] @ Wd  # d act before the combine weight
-        dw = np.sum(dA_u * act, axis=1)
-        dA = wflat[pairs][:, None] * dA_u
-        hg, hu = Hh[:, :I], Hh[:, I:]
-        sg = 1.0 / (1.0 + np.exp(-hg))
-        dH = np.concatenate([dA * hu * sg * (1.0 + hg * (1.0 - sg)), dA * hg * sg], axis=1)
-        dp = cayley_grad(R, rotation_grad(dH, Z, b))
-        dXp = rotate_adjoint(dH, R) @ Wgu
-        return e, pairs, dw, dp, dXp
+        pairs = rt["perm"][rt["offsets"][e]:rt["offsets"][e + 1]]
+        dwe, dpe, dXp = expert_backward(inp, e, pairs, X, dy, wflat, P)
+        return e, pairs, dwe, dpe, dXp
 
     dX = np.zeros((T, H))
     dp_all = np.zeros((cfg.E, cfg.nblk_e, cfg.npair))

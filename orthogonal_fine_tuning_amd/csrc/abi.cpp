@@ -60,6 +60,10 @@ oft::DenseArgs dense_args(const oft_linear_desc* d) {
 
 }  // namespace
 
+namespace oft {
+void set_last_hip_error(int e) { g_last_hip = e; }
+}  // namespace oft
+
 extern "C" {
 
 int32_t oft_abi_version(void) { return OFT_ABI_VERSION; }

@@ -1,0 +1,354 @@
+// Generic backward-type dequant GEMM:  C^T[k][m] = sum_n W[n][k] B'[m][n]
+// where the contraction runs over the weight's rows n and B' is built from
+// bf16 source rows by a prologue:
+//   PRO_ROT  : B'_blk = src_blk R_j (computed as R_j^T src^T on the matrix
+//              cores; FP8 also multiplies channel n by s_n), rounded to bf16;
+//   PRO_NONE : B' = src.
+// The weight tile [64 n x 128 k] is dequantised in registers and stored
+// transposed (n contiguous) to LDS.  Rows are dense tokens or grouped expert
+// positions exactly as in gemm_nt.h (kslots > 0 gathers src row
+// perm[pos] / kslots).
+// Epilogues:
+//   EPI_STORE      : store C rows (bf16 or fp32);
+//   EPI_SWIGLU_BWD : C = d act (before the combine weight) for the down
+//                    projection; with h = (gate, up) from the saved
+//                    activations and w the pair's combine weight:
+//                      dw partial  = sum_k C * silu(gate) * up (this k tile),
+//                      d gate      = w C up sig (1 + gate (1 - sig)),
+//                      d up        = w C silu(gate),
+//                    written to dH rows (gate half at k, up half at I + k).
+#pragma once
+
+#include "oft_device.h"
+
+namespace oft {
+
+enum : int { PRO_ROT = 0, PRO_NONE = 1 };
+enum : int { EPI_STORE = 0, EPI_SWIGLU_BWD = 1 };
+
+struct NnArgs {
+  const uint16_t* src;
+  long lds;
+  const uint8_t* wc;
+  const void* ws;
+  long wc_e, ws_e;
+  const uint16_t* rops;
+  long rops_e;
+  void* out;
+  long ldo;
+  int M, K, N, g;  // K: output columns (weight columns), N: contraction (weight rows)
+  const int* tiles;
+  const int* ntiles;
+  const int* offsets;
+  const int* perm;
+  int kslots;
+  // EPI_SWIGLU_BWD
+  const uint16_t* hsave;  // [P, 2I]
+  long ldh;
+  const float* topk_w;    // [P] by pair id
+  float* dw_part;         // [K / 128][P] by position
+  long P;
+};
+
+namespace nn {
+constexpr int BKO = 128;  // output columns per tile
+constexpr int BNS = 64;   // contraction step
+constexpr int LDN = BNS + 8;
+// Row k keeps channel n at column n ^ wsw(k): rows 8..15 of every 16 swap
+// their two 32-channel halves, so the transposed 8-byte stores of a
+// half-wave spread over all banks; 16-byte operand reads stay contiguous.
+__device__ __forceinline__ int wsw(int k) { return ((k >> 3) & 1) << 5; }
+}  // namespace nn
+
+template <int BM, bool OUTF32, bool FP8, int B, int PRO, int EPI, bool GROUPED>
+__global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
+  using namespace nn;
+  static_assert(BM == 128 || BM == 256, "tile");
+  constexpr int TM = BM / 64;   // 32-token tiles per wave (main product)
+  constexpr int PM = BM / 128;  // 32-token tiles each wave prepares in the prologue
+  __shared__ __attribute__((aligned(16))) uint16_t WsT[BKO * LDN];  // [k][n]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BM * LDN];    // [m][n]
+  __shared__ float dwred[EPI == EPI_SWIGLU_BWD ? 2 * BM : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int wk = wave >> 1, wm = wave & 1;
+  const int K = p.K, N = p.N;
+  const int k0 = blockIdx.x * BKO;
+
+  int e = 0, pos0, nrows;
+  if constexpr (GROUPED) {
+    const int t = blockIdx.y;
+    if (t >= *p.ntiles) return;
+    e = p.tiles[2 * t];
+    const int r0 = p.tiles[2 * t + 1];
+    pos0 = p.offsets[e] + r0;
+    nrows = min(BM, p.offsets[e + 1] - pos0);
+  } else {
+    pos0 = blockIdx.y * BM;
+    nrows = min(BM, p.M - pos0);
+  }
+  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
+  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  const float* ws_f = static_cast<const float*>(p.ws);
+  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
+
+  // W tile: thread owns rows n0 + 4*rg + q (q < 4), columns k0 + 8*kg + c (c < 8).
+  const int kg = (tid & 3) + 4 * (tid >> 6), rg = (tid >> 2) & 15;
+  const bool k_ok = (k0 + 8 * kg) < K;
+  uint32_t wr32[4];
+  uint2 wr64[4];
+  float wsc[4];
+
+  // source rows this wave feeds to the prologue
+  long srow[PM];
+#pragma unroll
+  for (int i = 0; i < PM; ++i) {
+    const int ml = (PM * wave + i) * 32 + l32;
+    long r = -1;
+    if (ml < nrows) {
+      r = pos0 + ml;
+      if constexpr (GROUPED) {
+        if (p.kslots > 0) r = p.perm[pos0 + ml] / p.kslots;
+      }
+    }
+    srow[i] = r;
+  }
+  uint4 sf[PM][2][2];  // [i][32-channel group][t] source operand fragments
+  uint4 rtf[2][2];     // [32-channel group][t] R^T operand fragments
+  float4 scf[2][4];    // FP8 channel scales, accumulator order
+
+  auto prefetch = [&](int n0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = n0 + 4 * rg + q;
+      const bool ok = k_ok && n < N;
+      if constexpr (FP8) {
+        wr64[q] = ok ? *reinterpret_cast<const uint2*>(wc + (size_t)n * K + k0 + 8 * kg) : make_uint2(0u, 0u);
+      } else {
+        wr32[q] = ok ? *reinterpret_cast<const uint32_t*>(wc + (size_t)n * (K / 2) + (k0 + 8 * kg) / 2) : 0u;
+        wsc[q] = ok ? fp16_to_f32(ws_h[(size_t)n * (K / p.g) + (k0 + 8 * kg) / p.g]) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      const int nb = n0 + 32 * grp;
+      const bool gok = nb < N;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if constexpr (PRO == PRO_ROT) {
+          uint4 v = zero4();
+          if (gok) {
+            if constexpr (B == 32) {
+              v = *reinterpret_cast<const uint4*>(rops + (size_t)(nb / 32) * 2048 + 1024 + l32 * 32 + 16 * t + 8 * g2);
+            } else {
+              if ((l32 >> 4) == t)
+                v = *reinterpret_cast<const uint4*>(rops + (size_t)(nb / 16 + t) * 512 + 256 + (l32 & 15) * 16 + 8 * g2);
+            }
+          }
+          rtf[grp][t] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < PM; ++i)
+          sf[i][grp][t] = (gok && srow[i] >= 0)
+                              ? *reinterpret_cast<const uint4*>(p.src + srow[i] * p.lds + nb + 16 * t + 8 * g2)
+                              : zero4();
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          scf[grp][q] = gok ? *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+
+  auto stage = [&]() {
+    // W tile -> LDS, transposed
+    uint32_t d[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint4 v;
+      if constexpr (FP8) {
+        const uint2 lo = dq_fp8x4(wr64[q].x), hi = dq_fp8x4(wr64[q].y);
+        v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        v = dq_int4x8(wr32[q], wsc[q]);
+      }
+      d[q][0] = v.x;
+      d[q][1] = v.y;
+      d[q][2] = v.z;
+      d[q][3] = v.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // element c of rows q = 0..3: low half for even c, high half for odd c
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      uint2 pk;
+      pk.x = __builtin_amdgcn_perm(d[1][c >> 1], d[0][c >> 1], sel);
+      pk.y = __builtin_amdgcn_perm(d[3][c >> 1], d[2][c >> 1], sel);
+      const int k = 8 * kg + c;
+      *reinterpret_cast<uint2*>(&WsT[k * LDN + ((4 * rg) ^ wsw(k))]) = pk;
+    }
+    // prologue -> Bs[m][n]
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+      for (int i = 0; i < PM; ++i) {
+        const int ml = (PM * wave + i) * 32 + l32;
+        if constexpr (PRO == PRO_NONE) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            *reinterpret_cast<uint4*>(&Bs[ml * LDN + 32 * grp + 16 * t + 8 * g2]) = sf[i][grp][t];
+        } else {
+          f32x16 o;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+          o = mfma32(as_bf16x8(rtf[grp][0]), as_bf16x8(sf[i][grp][0]), o);
+          o = mfma32(as_bf16x8(rtf[grp][1]), as_bf16x8(sf[i][grp][1]), o);
+          if constexpr (FP8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              o[4 * q] *= scf[grp][q].x;
+              o[4 * q + 1] *= scf[grp][q].y;
+              o[4 * q + 2] *= scf[grp][q].z;
+              o[4 * q + 3] *= scf[grp][q].w;
+            }
+          }
+          // Lane (m, g2) holds channels 8q + 4g2 + 0..3 in registers 4q..4q+3.
+          // Swapping one 4-channel run with lane m + 32(1 - g2) leaves lane g2
+          // with channels 16h + 8g2 + 0..7 of the pair q = 2h, 2h + 1.
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint2 p0 = make_uint2(pack_bf16x2(o[8 * h], o[8 * h + 1]), pack_bf16x2(o[8 * h + 2], o[8 * h + 3]));
+            const uint2 p1 = make_uint2(pack_bf16x2(o[8 * h + 4], o[8 * h + 5]), pack_bf16x2(o[8 * h + 6], o[8 * h + 7]));
+            const uint2 snd = g2 ? p0 : p1;
+            uint2 rcv;
+            rcv.x = (uint32_t)__shfl_xor((int)snd.x, 32);
+            rcv.y = (uint32_t)__shfl_xor((int)snd.y, 32);
+            const uint4 v = g2 ? make_uint4(rcv.x, rcv.y, p1.x, p1.y) : make_uint4(p0.x, p0.y, rcv.x, rcv.y);
+            *reinterpret_cast<uint4*>(&Bs[ml * LDN + 32 * grp + 16 * h + 8 * g2]) = v;
+          }
+        }
+      }
+    }
+  };
+
+  f32x16 acc[2][TM];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  prefetch(0);
+  for (int n0 = 0; n0 < N; n0 += BNS) {
+    __syncthreads();
+    stage();
+    __syncthreads();
+    if (n0 + BNS < N) prefetch(n0 + BNS);
+#pragma unroll
+    for (int kk = 0; kk < BNS / 16; ++kk) {
+      bf16x8 a[2], b[TM];
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        const int k = wk * 64 + tk * 32 + l32;
+        a[tk] = *reinterpret_cast<const bf16x8*>(&WsT[k * LDN + ((kk * 16 + 8 * g2) ^ wsw(k))]);
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        b[tm] = *reinterpret_cast<const bf16x8*>(&Bs[(wm * (BM / 2) + tm * 32 + l32) * LDN + kk * 16 + 8 * g2]);
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
+    }
+  }
+
+  // ------------------------------------------------------------ epilogue
+  if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+    for (int tk = 0; tk < 2; ++tk) {
+      const int kb = k0 + wk * 64 + tk * 32;
+      if (kb >= K) continue;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int ml = wm * (BM / 2) + tm * 32 + l32;
+        if (ml >= nrows) continue;
+        const long orow = (long)(pos0 + ml);
+        const f32x16& o = acc[tk][tm];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const size_t off = (size_t)orow * p.ldo + kb + 8 * q + 4 * g2;
+          if constexpr (OUTF32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) =
+                make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
+                make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+          }
+        }
+      }
+    }
+  } else {
+    // SwiGLU backward; out = dH [P, 2I] with ldo, K = I
+    float dwp[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) dwp[tm] = 0.0f;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int ml = wm * (BM / 2) + tm * 32 + l32;
+      const bool m_ok = ml < nrows;
+      const long pos = (long)(pos0 + ml);
+      const float wgt = m_ok ? p.topk_w[p.perm[pos]] : 0.0f;
+#pragma unroll
+      for (int tk = 0; tk < 2; ++tk) {
+        const int kb = k0 + wk * 64 + tk * 32;
+        if (kb >= K || !m_ok) continue;
+        const f32x16& o = acc[tk][tm];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = kb + 8 * q + 4 * g2;
+          const uint2 hg = *reinterpret_cast<const uint2*>(p.hsave + pos * p.ldh + col);
+          const uint2 hu = *reinterpret_cast<const uint2*>(p.hsave + pos * p.ldh + K + col);
+          const uint32_t gw[2] = {hg.x, hg.y}, uw[2] = {hu.x, hu.y};
+          float dg[4], du[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float gv = bf16_to_f32((uint16_t)(gw[s >> 1] >> (16 * (s & 1))));
+            const float uv = bf16_to_f32((uint16_t)(uw[s >> 1] >> (16 * (s & 1))));
+            const float sg = 1.0f / (1.0f + __expf(-gv));
+            const float silu = gv * sg;
+            const float da_u = o[4 * q + s];
+            dwp[tm] += da_u * silu * uv;
+            const float da = wgt * da_u;
+            dg[s] = da * uv * sg * (1.0f + gv * (1.0f - sg));
+            du[s] = da * silu;
+          }
+          uint16_t* dh = static_cast<uint16_t*>(p.out) + pos * p.ldo;
+          *reinterpret_cast<uint2*>(dh + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(dh + K + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        }
+      }
+    }
+    // per-position partial over this k tile: lanes g2 = 0/1, then waves wk = 0/1
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) dwp[tm] += __shfl_xor(dwp[tm], 32);
+    if (wk == 1 && g2 == 0) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) dwred[wm * (BM / 2) + tm * 32 + l32] = dwp[tm];
+    }
+    __syncthreads();
+    if (wk == 0 && g2 == 0) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int ml = wm * (BM / 2) + tm * 32 + l32;
+        if (ml < nrows) p.dw_part[(size_t)blockIdx.x * p.P + pos0 + ml] = dwp[tm] + dwred[ml];
+      }
+    }
+  }
+}
+
+}  // namespace oft

@@ -7,243 +7,19 @@
 //   dQ: S_j = dY_blk^T Y_blk, G_j = S_j R_j (= dY_blk^T Z_blk, Z = Y R),
 //       dL/dQ_j = (R_j^T + I) G_j (R_j^T + I) / 2, packed dp_il = Gq_il - Gq_li.
 //
-// dX kernel: one workgroup computes a 128 (k) x 256 (tokens) tile of dX^T.
-// Each contraction step covers 64 output channels n:
-//   * prologue: dZ^T = R_j^T dY^T for the step's blocks on the matrix cores,
-//     dY read straight from HBM in B-operand layout; FP8 multiplies by s_n;
-//     rounded to bf16 into LDS;
-//   * the W tile [64 n x 128 k] is loaded packed, dequantised in registers
-//     and stored transposed (k-major, n contiguous) to LDS;
-//   * main MFMAs dX^T += W^T dZ^T.
+// dX: one launch of gemm_nn_kernel (gemm_nn.h) with the rotation prologue:
+// each contraction step of 64 channels first forms dZ^T = R_j^T dY^T on the
+// matrix cores (FP8 also multiplies by s_n), then dX^T += W^T dZ^T with the
+// dequantised weight tile stored transposed in LDS.
 // dQ: stage 1 transposes 64 x 64 tiles of dY and Y through LDS and forms the
 // b x b cross products S on the matrix cores, one fp32 partial per M slice;
 // stage 2 reduces the slices in a fixed order and applies the Cayley
 // gradient in fp32 with R_f32.
-#include "oft_device.h"
+#include "gemm_nn.h"
 #include "oft_launch.h"
 
 namespace oft {
 namespace {
-
-constexpr int BKO = 128;  // output in-features per tile
-constexpr int BNS = 64;   // channels per contraction step
-constexpr int LDN = BNS + 8;
-
-// WsT row k keeps channel n at column n ^ wsw(k): rows 8..15 of every 16
-// swap their two 32-channel halves, so the transposed 8-byte stores of a
-// half-wave (4 rows x 64 bytes) spread over all banks, while 16-byte operand
-// reads stay contiguous.
-__device__ __forceinline__ int wsw(int k) { return ((k >> 3) & 1) << 5; }
-
-template <bool XF32, bool FP8, int B, int BM>
-__global__ __launch_bounds__(256, 2) void linear_bwd_dx_kernel(
-    const uint16_t* __restrict__ dy, const uint8_t* __restrict__ wc, const void* __restrict__ wsv,
-    const uint16_t* __restrict__ Rops, void* __restrict__ dxv, int M, int K, int N, int g) {
-  __shared__ __attribute__((aligned(16))) uint16_t WsT[BKO * LDN];  // [k][n]
-  __shared__ __attribute__((aligned(16))) uint16_t dZs[BM * LDN];   // [m][n]
-  static_assert(BM == 128 || BM == 256, "tile");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g2 = lane >> 5;
-  const int k0 = blockIdx.x * BKO, m0 = blockIdx.y * BM;
-  const int wk = wave >> 1, wm = wave & 1;
-  constexpr int TM = BM / 64;   // 32-token tiles per wave
-  constexpr int PM = BM / 128;  // 32-token tiles each wave rotates in the prologue
-
-  // W tile: thread owns rows n0 + 4*rg + q (q < 4), in-features k0 + 8*kg + e
-  // (e < 8).  A wave covers 4 kg x 16 rg, so each transposed LDS write of a
-  // wave fills 4 whole 128-byte rows (no bank conflicts); lanes 4j..4j+3
-  // read 16 contiguous bytes of one row.
-  const int kg = (tid & 3) + 4 * (tid >> 6), rg = (tid >> 2) & 15;
-  const bool k_ok = (k0 + 8 * kg) < K;
-  uint32_t wr32[4];  // INT4: 8 nibbles per row
-  uint2 wr64[4];     // FP8: 8 bytes per row
-  float wsc[4];
-
-  // prologue operands: this wave rotates token tiles mt = PM*wave + i (i < PM)
-  uint4 dyf[PM][2][2];  // [i][32-channel group][t]
-  uint4 rtf[2][2];     // [32-channel group][t]
-  float4 scf[2][4];    // FP8 channel scales of the step, C-layout order
-
-  auto prefetch = [&](int n0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 4 * rg + q;
-      const bool ok = k_ok && n < N;
-      if constexpr (FP8) {
-        wr64[q] = ok ? *reinterpret_cast<const uint2*>(wc + (size_t)n * K + k0 + 8 * kg)
-                     : make_uint2(0u, 0u);
-      } else {
-        wr32[q] = ok ? *reinterpret_cast<const uint32_t*>(wc + (size_t)n * (K / 2) + (k0 + 8 * kg) / 2)
-                     : 0u;
-        const uint16_t* s = static_cast<const uint16_t*>(wsv);
-        wsc[q] = ok ? fp16_to_f32(s[(size_t)n * (K / g) + (k0 + 8 * kg) / g]) : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      const int nb = n0 + 32 * grp;
-      const bool gok = nb < N;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint4 v = zero4();
-        if (gok) {
-          if constexpr (B == 32) {
-            v = *reinterpret_cast<const uint4*>(Rops + (size_t)(nb / 32) * 2048 + 1024 + l32 * 32 +
-                                                16 * t + 8 * g2);
-          } else {
-            if ((l32 >> 4) == t)
-              v = *reinterpret_cast<const uint4*>(Rops + (size_t)(nb / 16 + t) * 512 + 256 +
-                                                  (l32 & 15) * 16 + 8 * g2);
-          }
-        }
-        rtf[grp][t] = v;
-        if constexpr (FP8) {
-          if (t == 0) {
-            const float* s = static_cast<const float*>(wsv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              scf[grp][q] = gok ? *reinterpret_cast<const float4*>(s + nb + 8 * q + 4 * g2)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < PM; ++i) {
-          const int m = m0 + (PM * wave + i) * 32 + l32;
-          dyf[i][grp][t] = (gok && m < M)
-                               ? *reinterpret_cast<const uint4*>(dy + (size_t)m * N + nb + 16 * t + 8 * g2)
-                               : zero4();
-        }
-      }
-    }
-  };
-
-  auto stage = [&]() {
-    // W tile -> LDS, transposed: WsT[k][n]
-    uint16_t v[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 d;
-      if constexpr (FP8) {
-        const uint2 lo = dq_fp8x4(wr64[q].x), hi = dq_fp8x4(wr64[q].y);
-        d = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else {
-        d = dq_int4x8(wr32[q], wsc[q]);
-      }
-      const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[q][e] = (uint16_t)(dw[e >> 1] >> (16 * (e & 1)));
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint2 p;
-      p.x = (uint32_t)v[0][e] | ((uint32_t)v[1][e] << 16);
-      p.y = (uint32_t)v[2][e] | ((uint32_t)v[3][e] << 16);
-      const int k = 8 * kg + e;
-      *reinterpret_cast<uint2*>(&WsT[k * LDN + ((4 * rg) ^ wsw(k))]) = p;
-    }
-    // prologue: dZ^T = R^T dY^T per 32-channel group, into dZs[m][n]
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      float sc[16];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sc[4 * q] = scf[grp][q].x;
-          sc[4 * q + 1] = scf[grp][q].y;
-          sc[4 * q + 2] = scf[grp][q].z;
-          sc[4 * q + 3] = scf[grp][q].w;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < PM; ++i) {
-        f32x16 o;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-        o = mfma32(as_bf16x8(rtf[grp][0]), as_bf16x8(dyf[i][grp][0]), o);
-        o = mfma32(as_bf16x8(rtf[grp][1]), as_bf16x8(dyf[i][grp][1]), o);
-        if constexpr (FP8) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[r] *= sc[r];
-        }
-        const int ml = (PM * wave + i) * 32 + l32;
-        // Lane (m, g2) holds channels 8q + 4g2 + 0..3 in registers 4q..4q+3.
-        // Swapping one 4-channel run with lane m + 32(1 - g2) leaves lane g2
-        // with channels 16h + 8g2 + 0..7 of the pair q = 2h, 2h + 1.
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint2 p0 = make_uint2(pack_bf16x2(o[8 * h], o[8 * h + 1]),
-                                      pack_bf16x2(o[8 * h + 2], o[8 * h + 3]));
-          const uint2 p1 = make_uint2(pack_bf16x2(o[8 * h + 4], o[8 * h + 5]),
-                                      pack_bf16x2(o[8 * h + 6], o[8 * h + 7]));
-          const uint2 snd = g2 ? p0 : p1;
-          uint2 rcv;
-          rcv.x = (uint32_t)__shfl_xor((int)snd.x, 32);
-          rcv.y = (uint32_t)__shfl_xor((int)snd.y, 32);
-          const uint4 v = g2 ? make_uint4(rcv.x, rcv.y, p1.x, p1.y) : make_uint4(p0.x, p0.y, rcv.x, rcv.y);
-          *reinterpret_cast<uint4*>(&dZs[ml * LDN + 32 * grp + 16 * h + 8 * g2]) = v;
-        }
-      }
-    }
-  };
-
-  f32x16 acc[2][TM];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < TM; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-  prefetch(0);
-  for (int n0 = 0; n0 < N; n0 += BNS) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (n0 + BNS < N) prefetch(n0 + BNS);
-#pragma unroll
-    for (int kk = 0; kk < BNS / 16; ++kk) {
-      bf16x8 a[2], b[TM];
-#pragma unroll
-      for (int tk = 0; tk < 2; ++tk)
-      {
-        const int k = wk * 64 + tk * 32 + l32;
-        a[tk] = *reinterpret_cast<const bf16x8*>(&WsT[k * LDN + ((kk * 16 + 8 * g2) ^ wsw(k))]);
-      }
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-        b[tm] = *reinterpret_cast<const bf16x8*>(&dZs[(wm * (BM / 2) + tm * 32 + l32) * LDN + kk * 16 + 8 * g2]);
-#pragma unroll
-      for (int tk = 0; tk < 2; ++tk)
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
-    }
-  }
-
-#pragma unroll
-  for (int tk = 0; tk < 2; ++tk) {
-    const int kb = k0 + wk * 64 + tk * 32;
-    if (kb >= K) continue;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int m = m0 + wm * (BM / 2) + tm * 32 + l32;
-      if (m >= M) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const size_t off = (size_t)m * K + kb + 8 * q + 4 * g2;
-        const f32x16& o = acc[tk][tm];
-        if constexpr (XF32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(dxv) + off) =
-              make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dxv) + off) =
-              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
-        }
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------- dq stage 1
 constexpr int LDM = 64 + 8;
@@ -404,9 +180,21 @@ hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc
 #define OFT_DX_BM 128
 #endif
   constexpr int BM = OFT_DX_BM;
-  dim3 grid((a.K + BKO - 1) / BKO, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL((linear_bwd_dx_kernel<XF32, FP8, B, BM>), grid, dim3(256), 0, st, dy, wc, ws,
-                     Rops, dx, a.M, a.K, a.N, a.g);
+  NnArgs p{};
+  p.src = dy;
+  p.lds = a.N;
+  p.wc = wc;
+  p.ws = ws;
+  p.rops = Rops;
+  p.out = dx;
+  p.ldo = a.K;
+  p.M = a.M;
+  p.K = a.K;
+  p.N = a.N;
+  p.g = a.g;
+  dim3 grid((a.K + nn::BKO - 1) / nn::BKO, (a.M + BM - 1) / BM);
+  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8, B, PRO_ROT, EPI_STORE, false>), grid, dim3(256), 0,
+                     st, p);
   return hipGetLastError();
 }
 

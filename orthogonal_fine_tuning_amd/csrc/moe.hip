@@ -1,0 +1,607 @@
+// MoE layer with OFT on the split gate/up projection.
+//
+// Orbit pages: the Synced article, section "Technical details", and the
+// chooseai.io release news, section "Dedicated optimisation for low-precision
+// MoE models": the router-selected experts are grouped dynamically into
+// fixed-size batches, dequantised only temporarily and run as a grouped GEMM,
+// so the transient high-precision weight memory stays bounded.  Here the
+// dequantised weight never leaves LDS (zero transient weight memory); the
+// chunk table of active experts orders the grouped work list.
+//
+// Routing (all on the device, no host synchronisation):
+//   topk    : one wave per token; k rounds of a wave arg-max over the fp32
+//             logits (larger value, then lower expert id), softmax over all E
+//             by a butterfly reduction;
+//   count   : per 64-token tile, a 64-bit LDS mask per expert marking the
+//             tile's tokens that selected it (integer OR, order-free);
+//   scan    : counts = popcounts summed over tiles, exclusive scans over
+//             experts and over tiles by wavefront scans, active list, chunk
+//             table, grouped-GEMM work list;
+//   permute : rank of a token inside its tile and expert = popcount of the
+//             mask bits below its lane, so positions are stable (expert, then
+//             token).
+#include "gemm_nn.h"
+#include "gemm_nt.h"
+#include "oft_moe.h"
+
+namespace oft {
+namespace {
+
+constexpr int MOE_BM = 128;  // rows (expert positions) per grouped tile
+
+// ---------------------------------------------------------------- wave scans
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// exclusive scan of v over a block of 1024 threads; also returns the total
+__device__ int block_excl_scan(int v, int* total, int* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int wt = lane < 16 ? sh[lane] : 0;
+    const int ws = wave_incl_scan(wt);
+    if (lane < 16) sh[16 + lane] = ws - wt;
+    if (lane == 15) sh[32] = ws;
+  }
+  __syncthreads();
+  const int r = sh[16 + w] + inc - v;
+  *total = sh[32];
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------- top-k
+__global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E,
+                                                       int k, int renorm, int* __restrict__ idx,
+                                                       float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  constexpr int MAXV = 16;  // E <= 1024
+  float v[MAXV];
+  const int nv = (E + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    const float x = (i < nv && e < E) ? row[e] : -INFINITY;
+    v[i] = x != x ? -INFINITY : x;  // NaN ranks as -inf: every slot finds a candidate
+  }
+  uint32_t taken = 0;
+  float mx = 0.0f, sel_sum = 0.0f;
+  float sel_v[16];
+  int sel_e[16];
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const int e = lane + 64 * i;
+      if (i < nv && e < E && !((taken >> i) & 1u)) {
+        if (v[i] > bv || (v[i] == bv && e < be)) {
+          bv = v[i];
+          be = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    sel_v[j] = bv;
+    sel_e[j] = be;
+    if (j == 0) mx = bv;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    if (i < nv && e < E) s += __expf(v[i] - mx);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  for (int j = 0; j < k; ++j) sel_sum += __expf(sel_v[j] - mx);
+  const float den = renorm ? sel_sum : s;
+  if (lane < k) {
+    float myv = 0.0f;
+    int mye = 0;
+    for (int j = 0; j < k; ++j)
+      if (j == lane) {
+        myv = sel_v[j];
+        mye = sel_e[j];
+      }
+    idx[(size_t)t * k + lane] = mye;
+    wout[(size_t)t * k + lane] = __expf(myv - mx) / den;
+  }
+}
+
+// ---------------------------------------------------------------- count
+__global__ __launch_bounds__(64) void moe_count_kernel(const int* __restrict__ idx, int T, int E, int k,
+                                                       unsigned long long* __restrict__ gmask) {
+  extern __shared__ unsigned long long smask[];
+  const int lane = threadIdx.x;
+  const int tile = blockIdx.x;
+  for (int e = lane; e < E; e += 64) smask[e] = 0ull;
+  __syncthreads();
+  const int t = tile * 64 + lane;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) atomicOr(&smask[idx[(size_t)t * k + j]], 1ull << lane);
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) gmask[(size_t)tile * E + e] = smask[e];
+}
+
+// ---------------------------------------------------------------- scan
+__device__ void write_work_list(int cnt_e, int e, int E, int bm, int* list, int* ntiles, int* sh) {
+  const int nt_e = e < E ? (cnt_e + bm - 1) / bm : 0;
+  int total;
+  const int start = block_excl_scan(nt_e, &total, sh);
+  for (int i = 0; i < nt_e; ++i) {
+    list[2 * (start + i)] = e;
+    list[2 * (start + i) + 1] = i * bm;
+  }
+  if (threadIdx.x == 0) *ntiles = total;
+}
+
+__global__ __launch_bounds__(1024) void moe_scan_kernel(const unsigned long long* __restrict__ gmask,
+                                                        int ntile64, int E, int chunk, MoeRoutingDev rt,
+                                                        int* __restrict__ tile_off, int* __restrict__ list,
+                                                        int* __restrict__ ntiles) {
+  __shared__ int sh[40];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E)
+    for (int tl = 0; tl < ntile64; ++tl) cnt += __popcll(gmask[(size_t)tl * E + e]);
+  int total;
+  const int off = block_excl_scan(cnt, &total, sh);
+  if (e < E) {
+    rt.counts[e] = cnt;
+    rt.offsets[e] = off;
+    int run = off;
+    for (int tl = 0; tl < ntile64; ++tl) {
+      tile_off[(size_t)tl * E + e] = run;
+      run += __popcll(gmask[(size_t)tl * E + e]);
+    }
+  }
+  if (e == 0) rt.offsets[E] = total;
+  int nact;
+  const int rank = block_excl_scan((e < E && cnt > 0) ? 1 : 0, &nact, sh);
+  if (e < E) {
+    rt.chunk_of_expert[e] = cnt > 0 ? rank / chunk : -1;
+    if (cnt > 0) rt.active[rank] = e;
+    if (e >= nact) rt.active[e] = -1;
+  }
+  if (e == 0) *rt.n_active = nact;
+  write_work_list(e < E ? cnt : 0, e, E, MOE_BM, list, ntiles, sh);
+}
+
+__global__ __launch_bounds__(1024) void moe_worklist_kernel(const int* __restrict__ counts, int E,
+                                                            int* __restrict__ list, int* __restrict__ ntiles) {
+  __shared__ int sh[40];
+  const int e = threadIdx.x;
+  write_work_list(e < E ? counts[e] : 0, e, E, MOE_BM, list, ntiles, sh);
+}
+
+// ---------------------------------------------------------------- permute
+__global__ __launch_bounds__(64) void moe_permute_kernel(const int* __restrict__ idx, int T, int E, int k,
+                                                         const unsigned long long* __restrict__ gmask,
+                                                         const int* __restrict__ tile_off,
+                                                         int* __restrict__ perm, int* __restrict__ inv_perm) {
+  const int lane = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int t = tile * 64 + lane;
+  if (t >= T) return;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[(size_t)t * k + j];
+    const int rank = __popcll(gmask[(size_t)tile * E + e] & below);
+    const int pos = tile_off[(size_t)tile * E + e] + rank;
+    perm[pos] = t * k + j;
+    inv_perm[t * k + j] = pos;
+  }
+}
+
+// ---------------------------------------------------------------- combine
+// y[t] = sum_j w[t, j] * O[inv_perm[t*k + j]], fixed order over j
+__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ O, int H, int k,
+                                                          const int* __restrict__ inv_perm,
+                                                          const float* __restrict__ w, size_t n8,
+                                                          uint16_t* __restrict__ y) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int per = H / 8;
+  const size_t t = i / per;
+  const int c = (int)(i % per) * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[t * k + j];
+    const uint4 v = *reinterpret_cast<const uint4*>(O + (size_t)inv_perm[t * k + j] * H + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += wj * bf16_to_f32((uint16_t)(u[q >> 1] >> (16 * (q & 1))));
+  }
+  *reinterpret_cast<uint4*>(y + t * H + c) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+}
+
+// dX[t] = sum_j dXp[inv_perm[t*k + j]], fixed order over j
+__global__ __launch_bounds__(256) void moe_unpermute_sum_kernel(const uint16_t* __restrict__ dXp, int H, int k,
+                                                                const int* __restrict__ inv_perm, size_t n8,
+                                                                uint16_t* __restrict__ dx) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int per = H / 8;
+  const size_t t = i / per;
+  const int c = (int)(i % per) * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const uint4 v = *reinterpret_cast<const uint4*>(dXp + (size_t)inv_perm[t * k + j] * H + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += bf16_to_f32((uint16_t)(u[q >> 1] >> (16 * (q & 1))));
+  }
+  *reinterpret_cast<uint4*>(dx + t * H + c) = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+}
+
+// dw[p] = sum over k tiles of dw_part[kt][inv_perm[p]], fixed order
+__global__ __launch_bounds__(256) void moe_dw_reduce_kernel(const float* __restrict__ part, int nkt, long P,
+                                                            const int* __restrict__ inv_perm, float* __restrict__ dw) {
+  const long p = (long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= P) return;
+  const int pos = inv_perm[p];
+  float s = 0.0f;
+  for (int kt = 0; kt < nkt; ++kt) s += part[(size_t)kt * P + pos];
+  dw[p] = s;
+}
+
+// ---------------------------------------------------------------- dq per expert
+// One workgroup per (64 gate/up channels, expert): S = dH_blk^T H_blk over the
+// expert's rows (64-row steps through swizzled LDS transposes, MFMA), then the
+// Cayley gradient per block in fp32: Gq = (R^T + I) S (I + R) / 2,
+// dp_il = Gq_il - Gq_li.  Inactive experts get zeros.
+constexpr int LDM = 64 + 8;
+__device__ __forceinline__ int msw(int n) { return ((n >> 3) & 3) << 4; }
+
+template <int B>
+__global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict__ dH, const uint16_t* __restrict__ Hs,
+                                                     int ld, const int* __restrict__ offsets,
+                                                     const float* __restrict__ Rf, int nblk_e,
+                                                     float* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) uint16_t dYT[64 * LDM];
+  __shared__ __attribute__((aligned(16))) uint16_t YT[64 * LDM];
+  __shared__ float red[2][64][17];
+  __shared__ float S[2][32][33];
+  __shared__ float Rm[2][32][33];
+  __shared__ float T1[2][32][33];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int n0 = blockIdx.x * 64;
+  const int e = blockIdx.y;
+  const int m_lo = offsets[e], m_hi = offsets[e + 1];
+  const int grp = wave & 1, kh = wave >> 1;
+  const int c = tid & 7, rp = tid >> 3;
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int ms = m_lo; ms < m_hi; ms += 64) {
+    uint4 d[2], y[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = ms + 2 * rp + h;
+      const bool ok = m < m_hi;
+      d[h] = ok ? *reinterpret_cast<const uint4*>(dH + (size_t)m * ld + n0 + 8 * c) : zero4();
+      y[h] = ok ? *reinterpret_cast<const uint4*>(Hs + (size_t)m * ld + n0 + 8 * c) : zero4();
+    }
+    __syncthreads();
+    {
+      const uint32_t d0[4] = {d[0].x, d[0].y, d[0].z, d[0].w}, d1[4] = {d[1].x, d[1].y, d[1].z, d[1].w};
+      const uint32_t y0[4] = {y[0].x, y[0].y, y[0].z, y[0].w}, y1[4] = {y[1].x, y[1].y, y[1].z, y[1].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+        const int n = 8 * c + q;
+        *reinterpret_cast<uint32_t*>(&dYT[n * LDM + ((2 * rp) ^ msw(n))]) =
+            __builtin_amdgcn_perm(d1[q >> 1], d0[q >> 1], sel);
+        *reinterpret_cast<uint32_t*>(&YT[n * LDM + ((2 * rp) ^ msw(n))]) =
+            __builtin_amdgcn_perm(y1[q >> 1], y0[q >> 1], sel);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      const int kk = 2 * kh + kq;
+      const int n = 32 * grp + l32;
+      const int mo = (16 * kk + 8 * g2) ^ msw(n);
+      acc = mfma32(*reinterpret_cast<const bf16x8*>(&dYT[n * LDM + mo]),
+                   *reinterpret_cast<const bf16x8*>(&YT[n * LDM + mo]), acc);
+    }
+  }
+  if (kh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[grp][lane][r] = acc[r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[grp][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = acc[r] + red[grp][lane][r];
+  }
+  // R blocks of this 64-channel group
+  for (int i = tid; i < 2048; i += 256) {
+    const int gq = i >> 10, r = (i >> 5) & 31, cc = i & 31;
+    float v = 0.0f;
+    if (B == 32) {
+      v = Rf[((size_t)e * nblk_e + n0 / 32 + gq) * 1024 + r * 32 + cc];
+    } else if ((r >> 4) == (cc >> 4)) {
+      const int blk = n0 / 16 + 2 * gq + (r >> 4);
+      v = Rf[((size_t)e * nblk_e + blk) * 256 + (r & 15) * 16 + (cc & 15)];
+    }
+    Rm[gq][r][cc] = v;
+  }
+  __syncthreads();
+  // T1 = S (I + R), block-diagonal R (b = 16 keeps only the diagonal blocks)
+  for (int i = tid; i < 2048; i += 256) {
+    const int gq = i >> 10, r = (i >> 5) & 31, cc = i & 31;
+    const int lo = B == 32 ? 0 : (cc & 16), hi = lo + B;
+    float s = S[gq][r][cc];
+    for (int q = lo; q < hi; ++q) s += S[gq][r][q] * Rm[gq][q][cc];
+    T1[gq][r][cc] = s;
+  }
+  __syncthreads();
+  for (int i = tid; i < 2048; i += 256) {
+    const int gq = i >> 10, r = (i >> 5) & 31, cc = i & 31;
+    const int lo = B == 32 ? 0 : (r & 16), hi = lo + B;
+    float s = T1[gq][r][cc];
+    for (int q = lo; q < hi; ++q) s += Rm[gq][q][r] * T1[gq][q][cc];
+    S[gq][r][cc] = 0.5f * s;
+  }
+  __syncthreads();
+  constexpr int NP = B * (B - 1) / 2;
+  constexpr int BPG = 32 / B;  // blocks per 32-channel group
+  for (int i = tid; i < 2 * BPG * NP; i += 256) {
+    const int bl = i / NP, pidx = i % NP;
+    const int gq = bl / BPG, sub = bl % BPG;
+    int a = 0, rem = pidx;
+    while (rem >= B - 1 - a) {
+      rem -= B - 1 - a;
+      ++a;
+    }
+    const int l = a + 1 + rem;
+    const int blk = n0 / B + bl;
+    const int o = sub * B;
+    dq[((size_t)e * nblk_e + blk) * NP + pidx] = S[gq][o + a][o + l] - S[gq][o + l][o + a];
+  }
+}
+
+hipError_t last() { return hipGetLastError(); }
+
+}  // namespace
+
+MoeWs moe_ws_layout(const MoeDims& d, int pass) {
+  MoeWs w{};
+  const long P = (long)d.T * d.k;
+  const int nt64 = (d.T + 63) / 64;
+  const long max_tiles = (P + MOE_BM - 1) / MOE_BM + d.E;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.list = take(2 * max_tiles * sizeof(int));
+  w.ntiles = take(sizeof(int));
+  w.max_tiles = max_tiles;
+  if (pass == 0) {
+    w.gmask = take((size_t)nt64 * d.E * 8);
+    w.tile_off = take((size_t)nt64 * d.E * 4);
+    w.act = take((size_t)P * d.I * 2);
+    w.O = take((size_t)P * d.H * 2);
+  } else {
+    w.dH = take((size_t)P * 2 * d.I * 2);
+    w.dw_part = take((size_t)((d.I + 127) / 128) * P * 4);
+    w.dXp = take((size_t)P * d.H * 2);
+  }
+  w.bytes = off;
+  return w;
+}
+
+hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRoutingDev& rt, char* ws,
+                            const MoeWs& L, hipStream_t st) {
+  const int nt64 = (d.T + 63) / 64;
+  int* list = reinterpret_cast<int*>(ws + L.list);
+  int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
+  if (d.T > 0) {
+    hipLaunchKernelGGL(moe_topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, st, logits, d.T, d.E, d.k, d.renorm,
+                       rt.topk_idx, rt.topk_w);
+    hipLaunchKernelGGL(moe_count_kernel, dim3(nt64), dim3(64), (size_t)d.E * 8, st, rt.topk_idx, d.T, d.E, d.k,
+                       reinterpret_cast<unsigned long long*>(ws + L.gmask));
+  }
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st,
+                     reinterpret_cast<const unsigned long long*>(ws + L.gmask), nt64, d.E, d.chunk, rt,
+                     reinterpret_cast<int*>(ws + L.tile_off), list, ntiles);
+  if (d.T > 0)
+    hipLaunchKernelGGL(moe_permute_kernel, dim3(nt64), dim3(64), 0, st, rt.topk_idx, d.T, d.E, d.k,
+                       reinterpret_cast<const unsigned long long*>(ws + L.gmask),
+                       reinterpret_cast<const int*>(ws + L.tile_off), rt.perm, rt.inv_perm);
+  return last();
+}
+
+template <int B>
+static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const MoeRoutingDev& rt, char* ws,
+                                const MoeWs& L, hipStream_t st) {
+  const long P = (long)d.T * d.k;
+  int* list = reinterpret_cast<int*>(ws + L.list);
+  int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+  uint16_t* O = reinterpret_cast<uint16_t*>(ws + L.O);
+  const int nblk_e = 2 * d.I / B;
+  {
+    NtArgs p{};
+    p.a = q.x;
+    p.lda = d.H;
+    p.wc = q.wgu_codes;
+    p.ws = q.wgu_scales;
+    p.wc_e = (long)2 * d.I * d.H / 2;
+    p.ws_e = (long)2 * d.I * (d.H / d.g);
+    p.rops = q.R_ops;
+    p.rops_e = (long)nblk_e * 2 * B * B;
+    p.out = q.h_saved;
+    p.ldo = 2 * d.I;
+    p.act = act;
+    p.ldact = d.I;
+    p.M = 0;
+    p.K = d.H;
+    p.N = 2 * d.I;
+    p.g = d.g;
+    p.half_n = d.I;
+    p.tiles = list;
+    p.ntiles = ntiles;
+    p.offsets = rt.offsets;
+    p.perm = rt.perm;
+    p.kslots = d.k;
+    dim3 grid(d.I / 64, (unsigned)L.max_tiles);
+    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false>), grid, dim3(256), 0,
+                       st, p);
+  }
+  {
+    NtArgs p{};
+    p.a = act;
+    p.lda = d.I;
+    p.wc = q.wd_codes;
+    p.ws = q.wd_scales;
+    p.wc_e = (long)d.H * d.I / 2;
+    p.ws_e = (long)d.H * (d.I / d.g);
+    p.rops = q.R_ops;
+    p.rops_e = 0;
+    p.out = O;
+    p.ldo = d.H;
+    p.M = 0;
+    p.K = d.I;
+    p.N = d.H;
+    p.g = d.g;
+    p.tiles = list;
+    p.ntiles = ntiles;
+    p.offsets = rt.offsets;
+    p.perm = rt.perm;
+    p.kslots = 0;
+    dim3 grid((d.H + nt::BN - 1) / nt::BN, (unsigned)L.max_tiles);
+    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false>), grid, dim3(256), 0, st,
+                       p);
+  }
+  const size_t n8 = (size_t)d.T * d.H / 8;
+  if (n8 > 0)
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, O, d.H, d.k,
+                       rt.inv_perm, rt.topk_w, n8, q.y);
+  (void)P;
+  return last();
+}
+
+hipError_t launch_moe_fwd(const MoeDims& d, const float* logits, const MoeFwdPtrs& q, const MoeRoutingDev& rt,
+                          char* ws, const MoeWs& L, hipStream_t st) {
+  hipError_t err = launch_moe_route(d, logits, rt, ws, L, st);
+  if (err != hipSuccess) return err;
+  if (d.T == 0) return hipSuccess;
+  return d.b == 32 ? moe_fwd_gemms<32>(d, q, rt, ws, L, st) : moe_fwd_gemms<16>(d, q, rt, ws, L, st);
+}
+
+template <int B>
+static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
+                            const MoeWs& L, hipStream_t st) {
+  const long P = (long)d.T * d.k;
+  int* list = reinterpret_cast<int*>(ws + L.list);
+  int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
+  uint16_t* dH = reinterpret_cast<uint16_t*>(ws + L.dH);
+  float* dw_part = reinterpret_cast<float*>(ws + L.dw_part);
+  uint16_t* dXp = reinterpret_cast<uint16_t*>(ws + L.dXp);
+  const int nblk_e = 2 * d.I / B;
+  hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, list, ntiles);
+  if (d.T > 0) {
+    NnArgs p{};
+    p.src = q.dy;
+    p.lds = d.H;
+    p.wc = q.wd_codes;
+    p.ws = q.wd_scales;
+    p.wc_e = (long)d.H * d.I / 2;
+    p.ws_e = (long)d.H * (d.I / d.g);
+    p.rops = q.R_ops;
+    p.out = dH;
+    p.ldo = 2 * d.I;
+    p.M = 0;
+    p.K = d.I;
+    p.N = d.H;
+    p.g = d.g;
+    p.tiles = list;
+    p.ntiles = ntiles;
+    p.offsets = rt.offsets;
+    p.perm = rt.perm;
+    p.kslots = d.k;
+    p.hsave = q.h_saved;
+    p.ldh = 2 * d.I;
+    p.topk_w = rt.topk_w;
+    p.dw_part = dw_part;
+    p.P = P;
+    dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
+    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_SWIGLU_BWD, true>), grid, dim3(256),
+                       0, st, p);
+    if (q.dw)
+      hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part,
+                         (d.I + 127) / 128, P, rt.inv_perm, q.dw);
+  }
+  if (q.dq)
+    hipLaunchKernelGGL(moe_dq_kernel<B>, dim3(2 * d.I / 64, d.E), dim3(256), 0, st, dH, q.h_saved, 2 * d.I,
+                       rt.offsets, q.R_f32, nblk_e, q.dq);
+  if (q.dx && d.T > 0) {
+    NnArgs p{};
+    p.src = dH;
+    p.lds = 2 * d.I;
+    p.wc = q.wgu_codes;
+    p.ws = q.wgu_scales;
+    p.wc_e = (long)2 * d.I * d.H / 2;
+    p.ws_e = (long)2 * d.I * (d.H / d.g);
+    p.rops = q.R_ops;
+    p.rops_e = (long)nblk_e * 2 * B * B;
+    p.out = dXp;
+    p.ldo = d.H;
+    p.M = 0;
+    p.K = d.H;
+    p.N = 2 * d.I;
+    p.g = d.g;
+    p.tiles = list;
+    p.ntiles = ntiles;
+    p.offsets = rt.offsets;
+    p.perm = rt.perm;
+    p.kslots = 0;
+    dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
+    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_ROT, EPI_STORE, true>), grid, dim3(256), 0, st,
+                       p);
+    const size_t n8 = (size_t)d.T * d.H / 8;
+    hipLaunchKernelGGL(moe_unpermute_sum_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dXp, d.H,
+                       d.k, rt.inv_perm, n8, q.dx);
+  }
+  return last();
+}
+
+hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
+                          const MoeWs& L, hipStream_t st) {
+  return d.b == 32 ? moe_bwd_t<32>(d, q, rt, ws, L, st) : moe_bwd_t<16>(d, q, rt, ws, L, st);
+}
+
+}  // namespace oft

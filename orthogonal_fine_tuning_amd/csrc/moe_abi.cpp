@@ -1,19 +1,78 @@
-// MoE entry points (temporary: not implemented yet).
+// extern "C" MoE entry points of liboft (declared in include/oft.h).
+// Arguments are validated on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 
 #include "oft.h"
+#include "oft_launch.h"
+#include "oft_moe.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+bool opt_ok(const void* p) { return p == nullptr || aligned16(p); }
+
+int32_t validate_moe(const oft_moe_desc* d) {
+  if (d == nullptr) return OFT_EINVAL;
+  if (d->T < 0 || d->E <= 0 || d->k <= 0 || d->H <= 0 || d->I <= 0 || d->chunk < 1) return OFT_EINVAL;
+  if (d->k > 16 || d->E > 1024 || d->k > d->E) return OFT_EUNSUPPORTED;
+  if ((long long)d->T * d->k > (1LL << 30) || d->H > (1 << 16) || d->I > (1 << 16)) return OFT_EUNSUPPORTED;
+  if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;
+  if (d->g != 32 && d->g != 64 && d->g != 128) return OFT_EUNSUPPORTED;
+  if (d->renorm != 0 && d->renorm != 1) return OFT_EINVAL;
+  if (d->H % 64 != 0 || d->I % 64 != 0 || d->I % d->b != 0) return OFT_ESHAPE;
+  if (d->H % d->g != 0 || d->I % d->g != 0) return OFT_ESHAPE;
+  return OFT_OK;
+}
+
+oft::MoeDims dims(const oft_moe_desc* d) {
+  return oft::MoeDims{d->T, d->E, d->k, d->H, d->I, d->g, d->b, d->chunk, d->renorm};
+}
+
+int32_t routing_ok(const oft_moe_routing* rt) {
+  if (rt == nullptr) return OFT_EINVAL;
+  const void* ptrs[] = {rt->topk_idx, rt->topk_w, rt->counts, rt->offsets, rt->perm,
+                        rt->inv_perm, rt->active, rt->n_active, rt->chunk_of_expert};
+  for (const void* p : ptrs)
+    if (!ptr_ok(p)) return OFT_EINVAL;
+  return OFT_OK;
+}
+
+oft::MoeRoutingDev routing_dev(const oft_moe_routing* rt) {
+  return oft::MoeRoutingDev{rt->topk_idx, rt->topk_w, rt->counts, rt->offsets, rt->perm,
+                            rt->inv_perm, rt->active, rt->n_active, rt->chunk_of_expert};
+}
+
+int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return OFT_OK;
+  oft::set_last_hip_error(static_cast<int>(e));
+  return OFT_EHIP;
+}
+
+}  // namespace
 
 extern "C" {
 
 int32_t oft_moe_workspace_bytes(const oft_moe_desc* d, int32_t pass, size_t* bytes) {
-  (void)d; (void)pass; (void)bytes;
-  return OFT_EUNSUPPORTED;
+  if (bytes == nullptr) return OFT_EINVAL;
+  const int32_t v = validate_moe(d);
+  if (v != OFT_OK) return v;
+  if (pass != OFT_PASS_FWD && pass != OFT_PASS_BWD) return OFT_EINVAL;
+  *bytes = oft::moe_ws_layout(dims(d), pass).bytes;
+  return OFT_OK;
 }
 
-int32_t oft_moe_route(const oft_moe_desc* d, const float* logits, const oft_moe_routing* rt,
-                      void* ws, size_t ws_bytes, void* stream) {
-  (void)d; (void)logits; (void)rt; (void)ws; (void)ws_bytes; (void)stream;
-  return OFT_EUNSUPPORTED;
+int32_t oft_moe_route(const oft_moe_desc* d, const float* logits, const oft_moe_routing* rt, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int32_t v = validate_moe(d);
+  if (v != OFT_OK) return v;
+  if ((v = routing_ok(rt)) != OFT_OK) return v;
+  if (d->T > 0 && !ptr_ok(logits)) return OFT_EINVAL;
+  const oft::MoeWs L = oft::moe_ws_layout(dims(d), OFT_PASS_FWD);
+  if (!ptr_ok(ws)) return OFT_EINVAL;
+  if (ws_bytes < L.bytes) return OFT_EWORKSPACE;
+  return hip_status(oft::launch_moe_route(dims(d), logits, routing_dev(rt), static_cast<char*>(ws), L,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const float* logits,
@@ -22,10 +81,20 @@ int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const floa
                             const uint16_t* R_ops, const oft_moe_routing* rt,
                             uint16_t* h_saved, uint16_t* y, void* ws, size_t ws_bytes,
                             void* stream) {
-  (void)d; (void)x; (void)logits; (void)wgu_codes; (void)wgu_scales; (void)wd_codes;
-  (void)wd_scales; (void)R_ops; (void)rt; (void)h_saved; (void)y; (void)ws; (void)ws_bytes;
-  (void)stream;
-  return OFT_EUNSUPPORTED;
+  int32_t v = validate_moe(d);
+  if (v != OFT_OK) return v;
+  if ((v = routing_ok(rt)) != OFT_OK) return v;
+  if (d->T > 0) {
+    const void* req[] = {x, logits, wgu_codes, wgu_scales, wd_codes, wd_scales, R_ops, h_saved, y};
+    for (const void* p : req)
+      if (!ptr_ok(p)) return OFT_EINVAL;
+  }
+  const oft::MoeWs L = oft::moe_ws_layout(dims(d), OFT_PASS_FWD);
+  if (!ptr_ok(ws)) return OFT_EINVAL;
+  if (ws_bytes < L.bytes) return OFT_EWORKSPACE;
+  const oft::MoeFwdPtrs q{x, wgu_codes, wgu_scales, wd_codes, wd_scales, R_ops, h_saved, y};
+  return hip_status(oft::launch_moe_fwd(dims(d), logits, q, routing_dev(rt), static_cast<char*>(ws), L,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft_moe_routing* rt,
@@ -34,10 +103,25 @@ int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft
                             const uint16_t* wd_scales, const float* R_f32,
                             const uint16_t* R_ops, uint16_t* dx_or_null, float* dq_or_null,
                             float* dw_or_null, void* ws, size_t ws_bytes, void* stream) {
-  (void)d; (void)dy; (void)rt; (void)h_saved; (void)wgu_codes; (void)wgu_scales; (void)wd_codes;
-  (void)wd_scales; (void)R_f32; (void)R_ops; (void)dx_or_null; (void)dq_or_null;
-  (void)dw_or_null; (void)ws; (void)ws_bytes; (void)stream;
-  return OFT_EUNSUPPORTED;
+  int32_t v = validate_moe(d);
+  if (v != OFT_OK) return v;
+  if ((v = routing_ok(rt)) != OFT_OK) return v;
+  if (!opt_ok(dx_or_null) || !opt_ok(dq_or_null) || !opt_ok(dw_or_null)) return OFT_EINVAL;
+  if (dq_or_null != nullptr && !ptr_ok(R_f32)) return OFT_EINVAL;
+  if (dx_or_null != nullptr && !ptr_ok(R_ops)) return OFT_EINVAL;
+  if (d->T > 0) {
+    const void* req[] = {dy, h_saved, wd_codes, wd_scales};
+    for (const void* p : req)
+      if (!ptr_ok(p)) return OFT_EINVAL;
+    if (dx_or_null != nullptr && (!ptr_ok(wgu_codes) || !ptr_ok(wgu_scales))) return OFT_EINVAL;
+  }
+  const oft::MoeWs L = oft::moe_ws_layout(dims(d), OFT_PASS_BWD);
+  if (!ptr_ok(ws)) return OFT_EINVAL;
+  if (ws_bytes < L.bytes) return OFT_EWORKSPACE;
+  const oft::MoeBwdPtrs q{dy, h_saved, wgu_codes, wgu_scales, wd_codes, wd_scales, R_f32, R_ops,
+                          dx_or_null, dq_or_null, dw_or_null};
+  return hip_status(oft::launch_moe_bwd(dims(d), q, routing_dev(rt), static_cast<char*>(ws), L,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -9,6 +9,9 @@
 
 namespace oft {
 
+// thread-local hipError_t reported by oft_last_hip_error()
+void set_last_hip_error(int e);
+
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st);
 

@@ -1,0 +1,140 @@
+"""CPU checks of the C ABI: symbols, validation errors, workspace queries.
+
+No compute call is made: every call here fails validation (or is a pure
+host query) before the library touches the HIP runtime.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import orthogonal_fine_tuning_amd as oft
+from orthogonal_fine_tuning_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "oft.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.oft_abi_version() == 1
+    for s in range(-6, 1):
+        assert lib.oft_status_str(s)
+    assert b"unknown" in lib.oft_status_str(-99)
+
+
+def _desc(**kw):
+    base = dict(M=64, K=256, segs=(128, 128, 128), b=16, x_dtype=oft.OFT_DT_F32, w_fmt=oft.OFT_W_INT4, g=32)
+    base.update(kw)
+    return oft.linear_desc(base["M"], base["K"], base["segs"], base["b"], base["x_dtype"], base["w_fmt"],
+                           base["g"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=8), _lib.OFT_EUNSUPPORTED),
+    (dict(g=16), _lib.OFT_EUNSUPPORTED),
+    (dict(K=96), _lib.OFT_ESHAPE),                 # K % 64
+    (dict(K=320, g=128), _lib.OFT_ESHAPE),         # K % g
+    (dict(segs=(120, 136, 128)), _lib.OFT_ESHAPE),  # segment % b
+    (dict(segs=(16, 16, 16)), _lib.OFT_ESHAPE),    # N % 32
+    (dict(x_dtype=7), _lib.OFT_EDTYPE),
+    (dict(w_fmt=9), _lib.OFT_EDTYPE),
+    (dict(M=-1), _lib.OFT_EINVAL),
+])
+def test_linear_validation(kw, code):
+    d = _desc(**kw)
+    n = C.c_size_t(0)
+    assert _lib.load().oft_linear_workspace_bytes(C.byref(d), 1, C.byref(n)) == code
+
+
+def test_linear_segment_sum_mismatch():
+    d = _desc()
+    d.N = 512
+    n = C.c_size_t(0)
+    assert _lib.load().oft_linear_workspace_bytes(C.byref(d), 1, C.byref(n)) == _lib.OFT_ESHAPE
+
+
+def test_linear_null_and_misaligned_pointers_rejected():
+    d = _desc()
+    lib = _lib.load()
+    assert lib.oft_linear_fwd(C.byref(d), None, None, None, None, None, None, 0, None) == _lib.OFT_EINVAL
+    bad = C.c_void_p(0x1008)  # not 16-byte aligned
+    ok = C.c_void_p(0x1000)
+    assert lib.oft_linear_fwd(C.byref(d), bad, ok, ok, ok, ok, None, 0, None) == _lib.OFT_EINVAL
+    # dq requested with a too-small workspace
+    nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
+    st = lib.oft_linear_bwd(C.byref(d), ok, ok, ok, ok, ok, ok, None, ok, ok, nb - 1, None)
+    assert st == _lib.OFT_EWORKSPACE
+
+
+def test_linear_workspace_query():
+    d = _desc()
+    assert oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_FWD) == 0
+    assert oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD) >= (384 // 32) * 1024 * 4
+    with pytest.raises(oft.OftError):
+        oft.oft_linear_workspace_bytes(d, 5)
+
+
+def test_cayley_and_dequant_validation():
+    lib = _lib.load()
+    ok = C.c_void_p(0x1000)
+    assert lib.cayley_build(ok, 4, 24, ok, None, None) == _lib.OFT_EUNSUPPORTED
+    assert lib.cayley_build(ok, -1, 32, ok, None, None) == _lib.OFT_EINVAL
+    assert lib.cayley_build(None, 0, 32, None, None, None) == _lib.OFT_OK  # empty no-op
+    assert lib.oft_dequant(3, 4, 64, 32, ok, ok, ok, None) == _lib.OFT_EDTYPE
+    assert lib.oft_dequant(0, 4, 60, 32, ok, ok, ok, None) == _lib.OFT_ESHAPE
+    assert lib.oft_dequant(0, 4, 64, 48, ok, ok, ok, None) == _lib.OFT_EUNSUPPORTED
+    assert lib.oft_dequant(0, 4, 64, 32, ok, None, ok, None) == _lib.OFT_EINVAL
+    assert lib.oft_dequant(1, 0, 64, 0, None, None, None, None) == _lib.OFT_OK
+
+
+def _moe(**kw):
+    base = dict(T=128, E=16, k=4, H=256, I=128, g=32, b=32, chunk=4, renorm=0)
+    base.update(kw)
+    return oft.moe_desc(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=17), _lib.OFT_EUNSUPPORTED),
+    (dict(E=2048), _lib.OFT_EUNSUPPORTED),
+    (dict(k=20, E=16), _lib.OFT_EUNSUPPORTED),
+    (dict(b=64), _lib.OFT_EUNSUPPORTED),
+    (dict(g=8), _lib.OFT_EUNSUPPORTED),
+    (dict(H=200), _lib.OFT_ESHAPE),
+    (dict(I=96), _lib.OFT_ESHAPE),
+    (dict(chunk=0), _lib.OFT_EINVAL),
+    (dict(renorm=2), _lib.OFT_EINVAL),
+    (dict(T=-3), _lib.OFT_EINVAL),
+])
+def test_moe_validation(kw, code):
+    d = _moe(**kw)
+    n = C.c_size_t(0)
+    assert _lib.load().oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == code
+
+
+def test_moe_workspace_and_routing_checks():
+    d = _moe()
+    fwd = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
+    bwd = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_BWD)
+    P = 128 * 4
+    assert fwd >= P * 128 * 2 + P * 256 * 2  # act + down output
+    assert bwd >= P * 256 * 2 + P * 256 * 2  # dH + dX per pair
+    lib = _lib.load()
+    rt = _lib.oft_moe_routing()  # all NULL
+    ok = C.c_void_p(0x1000)
+    assert lib.oft_moe_route(C.byref(d), ok, C.byref(rt), ok, fwd, None) == _lib.OFT_EINVAL

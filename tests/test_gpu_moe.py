@@ -1,0 +1,246 @@
+"""GPU parity of the MoE path (routing, grouped fwd, bwd) against the oracle.
+
+Routing tables must match bit for bit; outputs and gradients to
+max|a - ref| / max|ref| <= 2e-2; combine weights to 1e-5 relative.
+Full-size configurations are checked on sampled tokens (y, dX, dw) and
+sampled experts (dQ), which the oracle computes one by one.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+from oft_inputs import CONFIGS, MoEConfig, make_moe, make_moe_logits
+from oracle import codec, moe as omoe
+from tests.helpers import bf16_to_f64, dev, err, host
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+SMALL = {
+    # ragged against 64-token count tiles and 128-row GEMM tiles
+    "moe_small_b32": MoEConfig("moe_small_b32", T=300, E=16, k=4, H=256, I=128, g=32, chunk=3, b=32,
+                               q_std=0.05),
+    "moe_small_b16_g64": MoEConfig("moe_small_b16_g64", T=200, E=12, k=3, H=192, I=192, g=64, chunk=5,
+                                   b=16, q_std=0.05),
+    "moe_small_g128": MoEConfig("moe_small_g128", T=77, E=8, k=2, H=384, I=256, g=128, chunk=2, b=32,
+                                bias_std=0.5),
+}
+
+
+def _routing_tensors(T, E, k):
+    import torch
+
+    P = T * k
+    z = lambda *s, dt=torch.int32: torch.full(s, -7, dtype=dt, device="cuda")  # noqa: E731
+    return dict(topk_idx=z(max(T, 1), k), topk_w=z(max(T, 1), k, dt=torch.float32), counts=z(E),
+                offsets=z(E + 1), perm=z(max(P, 1)), inv_perm=z(max(P, 1)), active=z(E), n_active=z(4),
+                chunk_of_expert=z(E))
+
+
+def _run_route(cfg, logits, renorm=0):
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    d = oft.moe_desc(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.g, cfg.b, cfg.chunk, renorm)
+    rtt = _routing_tensors(cfg.T, cfg.E, cfg.k)
+    rt = oft.moe_routing(**rtt)
+    nb = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    oft.oft_moe_route(d, dev(logits), rt, ws, nb)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in rtt.items()}
+
+
+def _check_routing(cfg, logits, got, renorm=False):
+    idx, w = omoe.route(logits, cfg.k, renorm=renorm)
+    g = omoe.group(idx, cfg.E, cfg.chunk)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    assert np.array_equal(got["topk_idx"][:T], idx)
+    assert np.abs(got["topk_w"][:T] - w).max() <= 1e-5 * max(1e-30, np.abs(w).max())
+    assert np.array_equal(got["counts"], g["counts"])
+    assert np.array_equal(got["offsets"], g["offsets"])
+    assert np.array_equal(got["perm"][:T * k], g["perm"])
+    assert np.array_equal(got["inv_perm"][:T * k], g["inv_perm"])
+    assert got["n_active"][0] == g["n_active"]
+    assert np.array_equal(got["active"][:g["n_active"]], g["active"])
+    assert np.all(got["active"][g["n_active"]:] == -1)
+    assert np.array_equal(got["chunk_of_expert"], g["chunk_of_expert"])
+
+
+@pytest.mark.parametrize("name", ["moe_30b_a3b", "moe_1t_train", "moe_1t_decode"])
+def test_routing_bit_exact_config_logits(name):
+    cfg = CONFIGS[name]
+    print(f"[moe routing] {name} T={cfg.T} E={cfg.E} k={cfg.k}", flush=True)
+    logits = make_moe_logits(cfg, seed=0)
+    _check_routing(cfg, logits, _run_route(cfg, logits))
+
+
+def test_routing_ties_and_renorm():
+    cfg = MoEConfig("ties", T=1000, E=96, k=8, H=64, I=64, g=32, chunk=7, b=32)
+    rng = np.random.default_rng(9)
+    logits = rng.integers(-3, 4, size=(cfg.T, cfg.E)).astype(np.float32)  # massive ties
+    logits[5, :] = 0.0
+    logits[:, 40] -= 100.0  # expert 40 never chosen
+    got = _run_route(cfg, logits)
+    _check_routing(cfg, logits, got)
+    assert got["topk_idx"][5].tolist() == list(range(8))
+    got = _run_route(cfg, logits, renorm=1)
+    _check_routing(cfg, logits, got, renorm=True)
+
+
+def _run_moe(inp, want_bwd=True):
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = inp["cfg"]
+    T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
+    P = T * k
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0)
+    rtt = _routing_tensors(T, E, k)
+    rt = oft.moe_routing(**rtt)
+    nblk = E * cfg.nblk_e
+    Rf = torch.empty((E, cfg.nblk_e, b, b), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((E, cfg.nblk_e, 2, b, b), dtype=torch.int16, device="cuda")
+    oft.cayley_build(dev(inp["p"]), nblk, b, Rf, Rops)
+    W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
+    hs = torch.empty((max(P, 1), 2 * I), dtype=torch.int16, device="cuda")
+    y = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
+    nbf = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
+    wsf = torch.empty(nbf, dtype=torch.uint8, device="cuda")
+    x = dev(inp["x"]) if T > 0 else torch.empty((1, H), dtype=torch.int16, device="cuda")
+    lg = dev(inp["logits"]) if T > 0 else torch.empty((1, E), dtype=torch.float32, device="cuda")
+    oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rops,
+                            rt, hs, y, wsf, nbf)
+    out = {"rt": rtt, "hs": hs, "y": y}
+    if want_bwd:
+        dy = dev(inp["dy"]) if T > 0 else torch.empty((1, H), dtype=torch.int16, device="cuda")
+        dx = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
+        dq = torch.full((E, cfg.nblk_e, cfg.npair), 3.0, dtype=torch.float32, device="cuda")
+        dw = torch.empty((max(T, 1), k), dtype=torch.float32, device="cuda")
+        nbb = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_BWD)
+        wsb = torch.empty(nbb, dtype=torch.uint8, device="cuda")
+        oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"],
+                                Rf, Rops, dx, dq, dw, wsb, nbb)
+        out.update(dx=dx, dq=dq, dw=dw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_moe_parity_small(name):
+    cfg = SMALL[name]
+    print(f"[moe parity] {name}", flush=True)
+    inp = make_moe(cfg, seed=0)
+    # one inactive expert and one hot expert spanning several 128-row tiles
+    inp["logits"] = inp["logits"].copy()
+    inp["logits"][:, 1] -= 100.0
+    inp["logits"][:, 2] += 3.0
+    y_ref, H_ref, rt = omoe.forward(inp)
+    dX_ref, dp_ref, dw_ref = omoe.backward(inp, rt)
+    out = _run_moe(inp)
+    got_rt = {k: host(v) for k, v in out["rt"].items()}
+    _check_routing(cfg, inp["logits"], got_rt)
+    assert rt["counts"][1] == 0
+    if cfg.T > 128:  # the hot expert spans several 128-row tiles
+        assert rt["counts"][2] > 128
+    P = cfg.T * cfg.k
+    e_y = err(bf16_to_f64(host(out["y"])), y_ref)
+    e_h = err(bf16_to_f64(host(out["hs"])[:P]), H_ref)
+    e_dx = err(bf16_to_f64(host(out["dx"])), dX_ref)
+    e_dq = err(host(out["dq"]), dp_ref)
+    e_dw = err(host(out["dw"]), dw_ref)
+    print(f"  err y={e_y:.2e} h={e_h:.2e} dx={e_dx:.2e} dq={e_dq:.2e} dw={e_dw:.2e}", flush=True)
+    assert max(e_y, e_h, e_dx, e_dq, e_dw) <= TOL
+    assert np.all(host(out["dq"])[1] == 0.0)  # inactive expert
+
+
+def test_moe_deterministic():
+    cfg = SMALL["moe_small_b32"]
+    inp = make_moe(cfg, seed=5)
+    a, b = _run_moe(inp), _run_moe(inp)
+    for key in ("y", "hs", "dx", "dq", "dw"):
+        assert np.array_equal(host(a[key]), host(b[key])), key
+
+
+def test_moe_zero_tokens():
+    cfg = SMALL["moe_small_b32"].with_(T=0)
+    inp = make_moe(cfg.with_(T=1), seed=1)
+    inp["cfg"] = cfg
+    out = _run_moe(inp)
+    assert np.all(host(out["dq"]) == 0.0)
+    assert np.all(host(out["rt"]["counts"]) == 0)
+    assert host(out["rt"]["n_active"])[0] == 0
+
+
+# ------------------------------------------------------------ full size, sampled
+def _sampled_reference(inp, tokens, experts, threads=16):
+    cfg = inp["cfg"]
+    k = cfg.k
+    idx, w = omoe.route(inp["logits"], k)
+    rt = omoe.group(idx, cfg.E, cfg.chunk)
+    X = codec.bf16_bits_to_f64(inp["x"])
+    dy = codec.bf16_bits_to_f64(inp["dy"])
+    wflat = w.reshape(-1)
+    need = sorted(set(int(idx[t, j]) for t in tokens for j in range(k)) | set(experts))
+
+    def one(e):
+        pairs_all = rt["perm"][rt["offsets"][e]:rt["offsets"][e + 1]]
+        sel = [p for p in pairs_all if p // k in set(tokens)]
+        Wgu, Wd, R = omoe.expert_weights(inp, e)
+        res = {}
+        if sel:
+            sel = np.asarray(sel)
+            _, _, _, O = omoe.expert_forward(X[sel // k], Wgu, Wd, R, cfg.I)
+            dwe, _, dXp = omoe.expert_backward(inp, e, sel, X, dy, wflat)
+            res["tok"] = (sel, O, dwe, dXp)
+        if e in experts:
+            res["dp"] = omoe.expert_backward(inp, e, pairs_all, X, dy, wflat)[1] if len(pairs_all) else \
+                np.zeros((cfg.nblk_e, cfg.npair))
+        return e, res
+
+    with ThreadPoolExecutor(threads) as ex:
+        results = dict(ex.map(one, need))
+    y = {t: np.zeros(cfg.H) for t in tokens}
+    dx = {t: np.zeros(cfg.H) for t in tokens}
+    dw = {}
+    for e, res in results.items():
+        if "tok" in res:
+            sel, O, dwe, dXp = res["tok"]
+            for r, p in enumerate(sel):
+                t = int(p // k)
+                y[t] += wflat[p] * O[r]
+                dx[t] += dXp[r]
+                dw[int(p)] = dwe[r]
+    dp = {e: results[e]["dp"] for e in experts}
+    return rt, y, dx, dw, dp
+
+
+@pytest.mark.parametrize("name", ["moe_30b_a3b", "moe_1t_train", "moe_1t_decode"])
+def test_moe_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    print(f"[moe full size] {name}: generating inputs", flush=True)
+    inp = make_moe(cfg, seed=0)
+    print(f"[moe full size] {name}: GPU fwd+bwd", flush=True)
+    out = _run_moe(inp)
+    counts = host(out["rt"]["counts"])
+    order = np.argsort(-counts, kind="stable")
+    experts = [int(order[0]), int(order[len(order) // 2])]
+    inactive = np.nonzero(counts == 0)[0]
+    tokens = [0, cfg.T // 3, cfg.T - 1]
+    print(f"[moe full size] {name}: oracle on tokens {tokens}, experts {experts}", flush=True)
+    rt, y, dx, dw, dp = _sampled_reference(inp, tokens, experts)
+    assert np.array_equal(counts, rt["counts"])
+    gy = bf16_to_f64(host(out["y"]))
+    gdx = bf16_to_f64(host(out["dx"]))
+    gdw = host(out["dw"]).reshape(-1)
+    gdq = host(out["dq"])
+    e_y = err(np.stack([gy[t] for t in tokens]), np.stack([y[t] for t in tokens]))
+    e_dx = err(np.stack([gdx[t] for t in tokens]), np.stack([dx[t] for t in tokens]))
+    ps = sorted(dw)
+    e_dw = err(gdw[ps], np.array([dw[p] for p in ps]))
+    e_dq = max(err(gdq[e], dp[e]) for e in experts)
+    print(f"  err y={e_y:.2e} dx={e_dx:.2e} dw={e_dw:.2e} dq={e_dq:.2e} inactive={len(inactive)}", flush=True)
+    assert max(e_y, e_dx, e_dw, e_dq) <= TOL
+    for e in inactive[:8]:
+        assert np.all(gdq[e] == 0.0)
