@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="token rows of the oracle sample for cpu_baseline")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (a reference "
+                         "for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -116,6 +119,146 @@ def cpu_baseline(cfg, inp, rows):
                       f"bwd (dX, dQ) in fp64 numpy, {dt:.2f} s"}
 
 
+def moe_flops(cfg):
+    P, H, I, b = cfg.T * cfg.k, cfg.H, cfg.I, cfg.b
+    gemm = 2 * P * H * 2 * I + 2 * P * I * H
+    return gemm + 2 * P * 2 * I * b, gemm + 4 * P * 2 * I * b
+
+
+def moe_bytes(cfg, n_active):
+    P, T, E, H, I, g, b = cfg.T * cfg.k, cfg.T, cfg.E, cfg.H, cfg.I, cfg.g, cfg.b
+    w_e = 2 * I * H // 2 + 2 * I * (H // g) * 2 + H * I // 2 + H * (I // g) * 2
+    nblk = 2 * I // b
+    rops = nblk * 2 * b * b * 2
+    fwd = n_active * (w_e + rops) + T * H * 2 + T * E * 4 + P * 2 * I * 2 + T * H * 2 + P * 16
+    bwd = (n_active * (w_e + rops + nblk * b * b * 4) + T * H * 2 + P * 2 * I * 2 + T * H * 2
+           + E * nblk * (b * (b - 1) // 2) * 4 + P * 4 + P * 16)
+    return fwd, bwd
+
+
+def run_moe(cfg, args):
+    import numpy as np
+    import torch
+
+    import orthogonal_fine_tuning_amd as oft
+    from oft_inputs import make_moe
+
+    inp = make_moe(cfg, seed=0)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
+    P = T * k
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    rtt = dict(topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+               counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32), perm=torch.empty(P, **i32),
+               inv_perm=torch.empty(P, **i32), active=torch.empty(E, **i32), n_active=torch.empty(4, **i32),
+               chunk_of_expert=torch.empty(E, **i32))
+    rt = oft.moe_routing(**rtt)
+    nblk = E * cfg.nblk_e
+    q = dev(inp["p"])
+    Rf = torch.empty((E, cfg.nblk_e, b, b), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((E, cfg.nblk_e, 2, b, b), dtype=torch.int16, device="cuda")
+    W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
+    x, lg, dy = dev(inp["x"]), dev(inp["logits"]), dev(inp["dy"])
+    hs = torch.empty((P, 2 * I), dtype=torch.int16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    dx = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    dq = torch.empty((E, cfg.nblk_e, cfg.npair), dtype=torch.float32, device="cuda")
+    dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    nbf = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
+    nbb = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_BWD)
+    wsf = torch.empty(nbf, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(nbb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        oft.cayley_build(q, nblk, b, Rf, Rops, stream=sp)
+        if ev is not None:
+            ev[1].record(stream)
+        oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rops, rt,
+                                hs, y, wsf, nbf, stream=sp)
+        if ev is not None:
+            ev[2].record(stream)
+        oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rf,
+                                Rops, dx, dq, dw, wsb, nbb, stream=sp)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_active = int(rtt["n_active"][0].item())
+    t_cay = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    f_fwd, f_bwd = moe_flops(cfg)
+    by_fwd, by_bwd = moe_bytes(cfg, n_active)
+    value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
+    achieved = (f_fwd + f_bwd) / (t_fwd + t_bwd) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "experts": E, "top_k": k, "hidden": H,
+                   "expert_intermediate": I, "weights": f"int4_g{cfg.g}", "oft_block": b, "chunk": cfg.chunk,
+                   "active_experts": n_active, "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma" if (f_fwd + f_bwd) / (by_fwd + by_bwd) > 312.5 else "hbm",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe fwd+bwd calls", "kernel_us": round((t_fwd + t_bwd) * 1e6, 2)},
+        "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
+                      "bwd": round(t_bwd * 1e6, 2)},
+        "phase_rates": {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
+                        "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
+                        "hbm_frac": round((by_fwd + by_bwd) / (t_fwd + t_bwd) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = moe_cpu_baseline(cfg, inp)
+    return out
+
+
+def moe_cpu_baseline(cfg, inp, n_experts=4):
+    from oracle import moe as omoe
+
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    idx, w = omoe.route(inp["logits"], cfg.k)
+    rt = omoe.group(idx, cfg.E, cfg.chunk)
+    rt.update(idx=idx, w=w)
+    experts = [int(e) for e in rt["active"][:n_experts]]
+    t0 = time.perf_counter()
+    omoe.forward(inp, rt, experts=experts)
+    omoe.backward(inp, rt, experts=experts)
+    dt = time.perf_counter() - t0
+    rows = int(sum(rt["counts"][e] for e in experts))
+    H, I, b = cfg.H, cfg.I, cfg.b
+    gemm = 2 * rows * H * 2 * I + 2 * rows * I * H
+    fl = 2 * gemm + 6 * rows * 2 * I * b
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{cfg.name}: experts {experts} ({rows} routed rows), dequant + Cayley + fwd + bwd "
+                      f"in fp64 numpy, {dt:.2f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -129,9 +272,17 @@ def main():
     import orthogonal_fine_tuning_amd as oft
     from oft_inputs import CONFIGS, make_dense
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = CONFIGS[args.config]
     if not hasattr(cfg, "segs"):
-        raise SystemExit(f"{args.config} is not a dense configuration")
+        print(json.dumps(run_moe(cfg, args)))
+        return
     inp = make_dense(cfg, seed=0)
 
     def dev(a):

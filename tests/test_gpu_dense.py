@@ -162,3 +162,34 @@ def test_deterministic_bitwise():
     b = _run_gpu(inp)
     for k in ("y", "dx", "dq"):
         assert np.array_equal(host(a[k]), host(b[k])), k
+
+
+@pytest.mark.parametrize("name", ["qkv_4b", "gateup_4b_train", "gateup_4b_decode"])
+def test_dense_full_size_sampled(name):
+    """Full workload shapes in the launch configuration the benchmark times;
+    the oracle checks sampled token rows of y and dX and sampled adapter
+    blocks of dQ (each block's reduction runs over every token)."""
+    cfg = CONFIGS[name]
+    print(f"[dense full size] {name}: M={cfg.M} K={cfg.K} N={cfg.N}", flush=True)
+    inp = make_dense(cfg, seed=0)
+    out = _run_gpu(inp)
+    W = odense.dequant(inp)
+    R = odense.cayley(inp["p"], cfg.b)
+    x = odense.x_f64(inp)
+    dY = codec.bf16_bits_to_f64(inp["dy"])
+    rows = sorted({0, 1, cfg.M // 3, cfg.M // 2 + 7, cfg.M - 1})
+    y_ref = odense.forward(x[rows], W, R)
+    dx_ref, _ = odense.backward(x[rows], W, R, dY[rows])
+    e_y = err(_to64(out["y"], cfg)[rows], y_ref)
+    e_dx = err(_to64(out["dx"], cfg)[rows], dx_ref)
+    blocks = sorted({0, 1, cfg.nblk // 2, cfg.nblk - 1})
+    gdq = host(out["dq"])
+    e_dq = 0.0
+    for j in blocks:
+        sl = slice(j * cfg.b, (j + 1) * cfg.b)
+        _, dp = odense.backward(x, W[sl], R[j:j + 1], dY[:, sl])
+        e_dq = max(e_dq, err(gdq[j], dp[0]))
+    R32 = host(out["Rf"]).astype(np.float64)
+    orth = np.abs(np.swapaxes(R32, 1, 2) @ R32 - np.eye(cfg.b)).max()
+    print(f"  err y={e_y:.2e} dx={e_dx:.2e} dq={e_dq:.2e} orth={orth:.1e}", flush=True)
+    assert max(e_y, e_dx, e_dq) <= TOL and orth <= 1e-3
