@@ -116,7 +116,7 @@ int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_
   if (pass == OFT_PASS_FWD) {
     *bytes = 0;
   } else if (pass == OFT_PASS_BWD) {
-    *bytes = oft::plan_dq(d->M, d->N).part_bytes;
+    *bytes = oft::plan_bwd(d->M, d->K, d->N).bytes;
   } else {
     return OFT_EINVAL;
   }
@@ -146,29 +146,22 @@ int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void*
   if (!opt_ok(dx_or_null) || !opt_ok(dq_or_null)) return OFT_EINVAL;
   const bool want_dx = dx_or_null != nullptr && d->M > 0;
   const bool want_dq = dq_or_null != nullptr;
-  const oft::DqPlan plan = oft::plan_dq(d->M, d->N);
+  const oft::DqPlan plan = oft::plan_bwd(d->M, d->K, d->N);
   if (want_dx) {
     if (!ptr_ok(dy) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(R_ops)) return OFT_EINVAL;
   }
   if (want_dq) {
     if (!ptr_ok(R_f32)) return OFT_EINVAL;
-    if (d->M > 0) {
-      if (!ptr_ok(dy) || !ptr_ok(y_saved)) return OFT_EINVAL;
-      if (!ptr_ok(ws)) return OFT_EINVAL;
-      if (ws_bytes < plan.part_bytes) return OFT_EWORKSPACE;
-    }
+    if (d->M > 0 && (!ptr_ok(dy) || !ptr_ok(y_saved))) return OFT_EINVAL;
   }
-  const oft::DenseArgs a = dense_args(d);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (want_dq) {
-    const int32_t s = hip_status(oft::launch_linear_dq(a, plan, dy, y_saved, R_f32, dq_or_null,
-                                                       static_cast<float*>(ws), st));
-    if (s != OFT_OK) return s;
+  if (want_dx || (want_dq && d->M > 0)) {
+    if (!ptr_ok(ws)) return OFT_EINVAL;
+    if (ws_bytes < plan.bytes) return OFT_EWORKSPACE;
   }
-  if (want_dx) {
-    return hip_status(oft::launch_linear_bwd_dx(a, dy, w_codes, w_scales, R_ops, dx_or_null, st));
-  }
-  return OFT_OK;
+  if (!want_dx && !want_dq) return OFT_OK;
+  return hip_status(oft::launch_linear_bwd(dense_args(d), plan, dy, y_saved, w_codes, w_scales, R_f32,
+                                           R_ops, want_dx ? dx_or_null : nullptr, dq_or_null,
+                                           static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

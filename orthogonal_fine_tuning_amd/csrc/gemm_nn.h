@@ -4,10 +4,16 @@
 //   PRO_ROT  : B'_blk = src_blk R_j (computed as R_j^T src^T on the matrix
 //              cores; FP8 also multiplies channel n by s_n), rounded to bf16;
 //   PRO_NONE : B' = src.
-// The weight tile [64 n x 128 k] is dequantised in registers and stored
-// transposed (n contiguous) to LDS.  Rows are dense tokens or grouped expert
-// positions exactly as in gemm_nt.h (kslots > 0 gathers src row
-// perm[pos] / kslots).
+// The weight tile [64 n x 128 k] is dequantised in registers and stored to
+// LDS in its natural layout (k contiguous, 16-byte stores); the matrix-core
+// operand, which must run along the contraction n, is read with the gfx950
+// LDS transpose load (ds_read_b64_tr_b16: within each 16-lane group, lane i
+// receives element i % 4 of the 8-byte chunks loaded by lanes 4e + i / 4,
+// e = 0..3; pointing lane r at row n0 + r / 4, column k0 + 4 (r % 4) gives
+// lane i the four values W[n0 .. n0+3][k0 + i]).  Two LDS buffers, registers
+// one step ahead, one barrier per step as in gemm_nt.h.  Rows are dense
+// tokens or grouped expert positions exactly as in gemm_nt.h (kslots > 0
+// gathers src row perm[pos] / kslots).
 // Epilogues:
 //   EPI_STORE      : store C rows (bf16 or fp32);
 //   EPI_SWIGLU_BWD : C = d act (before the combine weight) for the down
@@ -51,23 +57,28 @@ struct NnArgs {
 };
 
 namespace nn {
-constexpr int BKO = 128;  // output columns per tile
-constexpr int BNS = 64;   // contraction step
-constexpr int LDN = BNS + 8;
-// Row k keeps channel n at column n ^ wsw(k): rows 8..15 of every 16 swap
-// their two 32-channel halves, so the transposed 8-byte stores of a
-// half-wave spread over all banks; 16-byte operand reads stay contiguous.
-__device__ __forceinline__ int wsw(int k) { return ((k >> 3) & 1) << 5; }
+constexpr int BKO = 128;       // output columns per tile
+constexpr int BNS = 64;        // contraction step
+constexpr int LDN = BNS + 8;   // B' rows (n contiguous)
+constexpr int LDW = BKO + 16;  // weight rows (k contiguous); 288-byte stride puts
+                               // the 4 rows of a transpose load on disjoint banks
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  return __builtin_bit_cast(uint2, v);
+}
 }  // namespace nn
 
 template <int BM, bool OUTF32, bool FP8, int B, int PRO, int EPI, bool GROUPED>
-__global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
+__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nn_kernel(NnArgs p) {
   using namespace nn;
   static_assert(BM == 128 || BM == 256, "tile");
   constexpr int TM = BM / 64;   // 32-token tiles per wave (main product)
   constexpr int PM = BM / 128;  // 32-token tiles each wave prepares in the prologue
-  __shared__ __attribute__((aligned(16))) uint16_t WsT[BKO * LDN];  // [k][n]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BM * LDN];    // [m][n]
+  constexpr int WSZ = BNS * LDW;        // weight tile [n][k]
+  constexpr int STAGE = WSZ + BM * LDN;  // + B' tile [m][n]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
   __shared__ float dwred[EPI == EPI_SWIGLU_BWD ? 2 * BM : 1];
 
   const int tid = threadIdx.x;
@@ -94,12 +105,11 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
   const float* ws_f = static_cast<const float*>(p.ws);
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
 
-  // W tile: thread owns rows n0 + 4*rg + q (q < 4), columns k0 + 8*kg + c (c < 8).
-  const int kg = (tid & 3) + 4 * (tid >> 6), rg = (tid >> 2) & 15;
-  const bool k_ok = (k0 + 8 * kg) < K;
-  uint32_t wr32[4];
-  uint2 wr64[4];
-  float wsc[4];
+  // W tile: thread owns row n0 + wrow, columns k0 + 32*wq + 0..31
+  const int wrow = tid >> 2, wq = tid & 3;
+  const bool k_ok = (k0 + 32 * wq) < K;
+  uint4 wr[FP8 ? 2 : 1];
+  float wsc = 0.0f;
 
   // source rows this wave feeds to the prologue
   long srow[PM];
@@ -120,15 +130,16 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
   float4 scf[2][4];    // FP8 channel scales, accumulator order
 
   auto prefetch = [&](int n0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + 4 * rg + q;
+    {
+      const int n = n0 + wrow;
       const bool ok = k_ok && n < N;
       if constexpr (FP8) {
-        wr64[q] = ok ? *reinterpret_cast<const uint2*>(wc + (size_t)n * K + k0 + 8 * kg) : make_uint2(0u, 0u);
+        const uint8_t* src = wc + (size_t)n * K + k0 + 32 * wq;
+        wr[0] = ok ? *reinterpret_cast<const uint4*>(src) : zero4();
+        wr[1] = ok ? *reinterpret_cast<const uint4*>(src + 16) : zero4();
       } else {
-        wr32[q] = ok ? *reinterpret_cast<const uint32_t*>(wc + (size_t)n * (K / 2) + (k0 + 8 * kg) / 2) : 0u;
-        wsc[q] = ok ? fp16_to_f32(ws_h[(size_t)n * (K / p.g) + (k0 + 8 * kg) / p.g]) : 0.0f;
+        wr[0] = ok ? *reinterpret_cast<const uint4*>(wc + (size_t)n * (K / 2) + (k0 + 32 * wq) / 2) : zero4();
+        wsc = ok ? fp16_to_f32(ws_h[(size_t)n * (K / p.g) + (k0 + 32 * wq) / p.g]) : 0.0f;
       }
     }
 #pragma unroll
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
                               ? *reinterpret_cast<const uint4*>(p.src + srow[i] * p.lds + nb + 16 * t + 8 * g2)
                               : zero4();
       }
-      if constexpr (FP8) {
+      if constexpr (FP8 && PRO == PRO_ROT) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           scf[grp][q] = gok ? *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2)
@@ -164,32 +175,23 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
     }
   };
 
-  auto stage = [&]() {
-    // W tile -> LDS, transposed
-    uint32_t d[4][4];
+  auto stage = [&](int buf) {
+    uint16_t* Ws = smem + buf * STAGE;
+    uint16_t* Bs = Ws + WSZ;
+    // W tile -> LDS, natural layout
+    uint4* dst = reinterpret_cast<uint4*>(&Ws[wrow * LDW + 32 * wq]);
+    if constexpr (FP8) {
+      const uint32_t wv[8] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w, wr[1].x, wr[1].y, wr[1].z, wr[1].w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 v;
-      if constexpr (FP8) {
-        const uint2 lo = dq_fp8x4(wr64[q].x), hi = dq_fp8x4(wr64[q].y);
-        v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      } else {
-        v = dq_int4x8(wr32[q], wsc[q]);
+      for (int q = 0; q < 4; ++q) {
+        const uint2 lo = dq_fp8x4(wv[2 * q]), hi = dq_fp8x4(wv[2 * q + 1]);
+        dst[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
-      d[q][0] = v.x;
-      d[q][1] = v.y;
-      d[q][2] = v.z;
-      d[q][3] = v.w;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // element c of rows q = 0..3: low half for even c, high half for odd c
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      uint2 pk;
-      pk.x = __builtin_amdgcn_perm(d[1][c >> 1], d[0][c >> 1], sel);
-      pk.y = __builtin_amdgcn_perm(d[3][c >> 1], d[2][c >> 1], sel);
-      const int k = 8 * kg + c;
-      *reinterpret_cast<uint2*>(&WsT[k * LDN + ((4 * rg) ^ wsw(k))]) = pk;
+    } else {
+      dst[0] = dq_int4x8(wr[0].x, wsc);
+      dst[1] = dq_int4x8(wr[0].y, wsc);
+      dst[2] = dq_int4x8(wr[0].z, wsc);
+      dst[3] = dq_int4x8(wr[0].w, wsc);
     }
     // prologue -> Bs[m][n]
 #pragma unroll
@@ -243,19 +245,21 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  prefetch(0);
-  for (int n0 = 0; n0 < N; n0 += BNS) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (n0 + BNS < N) prefetch(n0 + BNS);
+  // A operand (W^T rows k, contraction n) through the LDS transpose load
+  const int G = lane >> 4, li = lane & 15;
+  auto compute = [&](int buf) {
+    const uint16_t* Ws = smem + buf * STAGE;
+    const uint16_t* Bs = Ws + WSZ;
 #pragma unroll
     for (int kk = 0; kk < BNS / 16; ++kk) {
       bf16x8 a[2], b[TM];
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk) {
-        const int k = wk * 64 + tk * 32 + l32;
-        a[tk] = *reinterpret_cast<const bf16x8*>(&WsT[k * LDN + ((kk * 16 + 8 * g2) ^ wsw(k))]);
+        const int kcol = wk * 64 + tk * 32 + 16 * (G & 1) + 4 * (li & 3);
+        const int nrow = kk * 16 + 8 * (G >> 1) + (li >> 2);
+        const uint2 lo = ds_read_tr16(&Ws[nrow * LDW + kcol]);
+        const uint2 hi = ds_read_tr16(&Ws[(nrow + 4) * LDW + kcol]);
+        a[tk] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
@@ -265,6 +269,18 @@ __global__ __launch_bounds__(256, 2) void gemm_nn_kernel(NnArgs p) {
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
     }
+  };
+
+  const int ns = (N + BNS - 1) / BNS;
+  prefetch(0);
+  stage(0);
+  if (ns > 1) prefetch(BNS);
+  __syncthreads();
+  for (int s = 0; s < ns; ++s) {
+    compute(s & 1);
+    if (s + 1 < ns) stage((s + 1) & 1);
+    if (s + 2 < ns) prefetch((s + 2) * BNS);
+    __syncthreads();
   }
 
   // ------------------------------------------------------------ epilogue

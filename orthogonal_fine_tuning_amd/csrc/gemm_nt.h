@@ -53,13 +53,20 @@ constexpr int BK = 64;
 constexpr int LDK = BK + 8;
 }  // namespace nt
 
-template <int BM, bool AF32, bool FP8, int B, int EPI, bool GROUPED, bool OUTF32>
-__global__ __launch_bounds__(256, 2) void gemm_nt_kernel(NtArgs p) {
+// Pipeline (NBUF = 2): two LDS buffers, registers one step ahead, one
+// barrier per K step: while the matrix cores run step s from one buffer, the
+// same waves dequantise step s + 1 (already in registers) into the other
+// buffer and issue the global loads of step s + 2.  NBUF = 1: one buffer, two
+// barriers per step; the smaller LDS footprint lets two workgroups share a
+// CU and overlap each other's dequantisation with their matrix-core work.
+template <int BM, bool AF32, bool FP8, int B, int EPI, bool GROUPED, bool OUTF32, int NBUF = 2>
+__global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt_kernel(NtArgs p) {
   using namespace nt;
   static_assert(BM == 128 || BM == 256, "tile");
+  static_assert(NBUF == 1 || NBUF == 2, "buffers");
   constexpr int TM = BM / 64;  // 32-token tiles per wave
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[BN * LDK];
+  constexpr int STAGE = (BM + BN) * LDK;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -142,7 +149,9 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(NtArgs p) {
     }
   };
 
-  auto store_tiles = [&]() {
+  auto store_tiles = [&](int buf) {
+    uint16_t* Xs = smem + buf * STAGE;
+    uint16_t* Ws = Xs + BM * LDK;
     if constexpr (AF32) {
       const int c = tid & 15;
 #pragma unroll
@@ -184,12 +193,9 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(NtArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  load_tiles(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    store_tiles();
-    __syncthreads();
-    if (k0 + BK < K) load_tiles(k0 + BK);
+  auto compute = [&](int buf) {
+    const uint16_t* Xs = smem + buf * STAGE;
+    const uint16_t* Ws = Xs + BM * LDK;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 a[2], b[TM];
@@ -204,6 +210,30 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(NtArgs p) {
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma32(a[tn], b[tm], acc[tn][tm]);
     }
+  };
+
+  const int nk = K / BK;
+  if constexpr (NBUF == 2) {
+    load_tiles(0);
+    store_tiles(0);
+    if (nk > 1) load_tiles(BK);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+      compute(s & 1);
+      if (s + 1 < nk) store_tiles((s + 1) & 1);
+      if (s + 2 < nk) load_tiles((s + 2) * BK);
+      __syncthreads();
+    }
+  } else {
+    load_tiles(0);
+    for (int s = 0; s < nk; ++s) {
+      if (s > 0) __syncthreads();
+      store_tiles(0);
+      __syncthreads();
+      if (s + 1 < nk) load_tiles((s + 1) * BK);
+      compute(0);
+    }
+    __syncthreads();
   }
 
   // ------------------------------------------------------------ epilogue
@@ -295,9 +325,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(NtArgs p) {
   if constexpr (EPI == EPI_ROT_SWIGLU) {
     // up waves (wn = 1) hand their bf16 outputs to the gate waves (wn = 0)
     // holding the same (token, channel) slots; the tiles are free now.
-    static_assert(2 * 2 * TM * 64 * 8 * 4 <= BM * LDK * 2, "exchange buffer");
-    uint32_t* xb = reinterpret_cast<uint32_t*>(Xs);
-    __syncthreads();
+    static_assert(2 * 2 * TM * 64 * 8 * 4 <= NBUF * STAGE * 2, "exchange buffer");
+    uint32_t* xb = reinterpret_cast<uint32_t*>(smem);
     if (wn == 1) {
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn)

@@ -7,10 +7,12 @@
 //   dQ: S_j = dY_blk^T Y_blk, G_j = S_j R_j (= dY_blk^T Z_blk, Z = Y R),
 //       dL/dQ_j = (R_j^T + I) G_j (R_j^T + I) / 2, packed dp_il = Gq_il - Gq_li.
 //
-// dX: one launch of gemm_nn_kernel (gemm_nn.h) with the rotation prologue:
-// each contraction step of 64 channels first forms dZ^T = R_j^T dY^T on the
-// matrix cores (FP8 also multiplies by s_n), then dX^T += W^T dZ^T with the
-// dequantised weight tile stored transposed in LDS.
+// dX = dZ' . W with dZ' = (dY_blk R_j) * s_n (FP8 channel scale): the
+// rotation is a prologue of the dX GEMM.  For narrow layers (dX at most two
+// 128-column tiles wide) it runs inside gemm_nn_kernel (PRO_ROT); for wider
+// layers it would be recomputed once per column tile, so it runs once per dY
+// tile inside the dQ pass below (which reads dY anyway) and gemm_nn_kernel
+// consumes the rotated bf16 tile (PRO_NONE).
 // dQ: stage 1 transposes 64 x 64 tiles of dY and Y through LDS and forms the
 // b x b cross products S on the matrix cores, one fp32 partial per M slice;
 // stage 2 reduces the slices in a fixed order and applies the Cayley
@@ -29,11 +31,18 @@ constexpr int LDM = 64 + 8;
 // twice at most, 16-byte operand reads stay contiguous.
 __device__ __forceinline__ int msw(int n) { return ((n >> 3) & 3) << 4; }
 
-template <bool YF32>
+// Besides the partial cross products, when dz != nullptr the kernel writes
+// the rotated upstream gradient dz = (dY_blk R_j) * s (s: FP8 channel scale,
+// else 1) in bf16: the rotation runs on the matrix cores once per dY tile
+// (dZ^T = R_j^T dY^T, accumulator rows are channels), for the dX GEMM.
+template <bool YF32, bool FP8, int B>
 __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restrict__ dy,
                                                          const void* __restrict__ yv,
                                                          float* __restrict__ part, int M, int N,
-                                                         int rows_per_split, int ng32) {
+                                                         int rows_per_split, int ng32,
+                                                         const uint16_t* __restrict__ Rops,
+                                                         const float* __restrict__ fp8_scale,
+                                                         uint16_t* __restrict__ dz) {
   __shared__ __attribute__((aligned(16))) uint16_t dYT[64 * LDM];  // [n][m]
   __shared__ __attribute__((aligned(16))) uint16_t YT[64 * LDM];   // [n][m]
   __shared__ float red[2][64][17];
@@ -54,7 +63,59 @@ __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restr
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
+  // rotation operands of this wave: 32-channel group rg = wave & 1, token
+  // half rh = wave >> 1 of each 64-token step
+  const int rg = wave & 1, rh = wave >> 1;
+  const int nbr = n0 + 32 * rg;
+  const bool rot = dz != nullptr && nbr < N;
+  uint4 rtf[2] = {zero4(), zero4()};
+  float sc[16];
+  if (rot) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (B == 32) {
+        rtf[t] = *reinterpret_cast<const uint4*>(Rops + (size_t)(nbr / 32) * 2048 + 1024 + l32 * 32 + 16 * t + 8 * g2);
+      } else {
+        if ((l32 >> 4) == t)
+          rtf[t] = *reinterpret_cast<const uint4*>(Rops + (size_t)(nbr / 16 + t) * 512 + 256 + (l32 & 15) * 16 + 8 * g2);
+      }
+    }
+    if constexpr (FP8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(fp8_scale + nbr + 8 * q + 4 * g2);
+        sc[4 * q] = v.x;
+        sc[4 * q + 1] = v.y;
+        sc[4 * q + 2] = v.z;
+        sc[4 * q + 3] = v.w;
+      }
+    }
+  }
+
   for (int ms = m_lo; ms < m_hi; ms += 64) {
+    if (rot) {
+      const int m = ms + 32 * rh + l32;
+      const bool mok = m < m_hi;
+      uint4 f[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        f[t] = mok ? *reinterpret_cast<const uint4*>(dy + (size_t)m * N + nbr + 16 * t + 8 * g2) : zero4();
+      f32x16 o;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+      o = mfma32(as_bf16x8(rtf[0]), as_bf16x8(f[0]), o);
+      o = mfma32(as_bf16x8(rtf[1]), as_bf16x8(f[1]), o);
+      if constexpr (FP8) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] *= sc[r];
+      }
+      if (mok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(dz + (size_t)m * N + nbr + 8 * q + 4 * g2) =
+              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+      }
+    }
     uint4 d[2], y[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -173,15 +234,12 @@ __global__ __launch_bounds__(256) void dq_final_kernel(const float* __restrict__
   }
 }
 
-template <bool XF32, bool FP8, int B>
-hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc, const void* ws,
+template <bool XF32, bool FP8, int B, int PRO>
+hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* src, const uint8_t* wc, const void* ws,
                        const uint16_t* Rops, void* dx, hipStream_t st) {
-#ifndef OFT_DX_BM
-#define OFT_DX_BM 128
-#endif
-  constexpr int BM = OFT_DX_BM;
+  constexpr int BM = 128;
   NnArgs p{};
-  p.src = dy;
+  p.src = src;
   p.lds = a.N;
   p.wc = wc;
   p.ws = ws;
@@ -193,14 +251,13 @@ hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc
   p.N = a.N;
   p.g = a.g;
   dim3 grid((a.K + nn::BKO - 1) / nn::BKO, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8, B, PRO_ROT, EPI_STORE, false>), grid, dim3(256), 0,
-                     st, p);
+  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8, B, PRO, EPI_STORE, false>), grid, dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-DqPlan plan_dq(int M, int N) {
+DqPlan plan_bwd(int M, int K, int N) {
   DqPlan p;
   p.ng32 = N / 32;
   const int ng64 = (N + 63) / 64;
@@ -218,43 +275,59 @@ DqPlan plan_dq(int M, int N) {
     p.nsplit = (msteps + steps_per - 1) / steps_per;
   }
   p.part_bytes = (size_t)(p.nsplit > 0 ? p.nsplit : 1) * p.ng32 * 1024 * sizeof(float);
+  // Wide layers rotate dY once in the dQ pass; narrow ones (at most two
+  // 128-column tiles of dX) keep the rotation in the dX GEMM prologue.
+  p.prerotate = K > 2 * nn::BKO;
+  p.dz_off = (p.part_bytes + 255) / 256 * 256;
+  p.bytes = p.dz_off + (p.prerotate ? (size_t)M * N * 2 : 0);
   return p;
 }
 
-hipError_t launch_linear_bwd_dx(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc,
-                                const void* ws, const uint16_t* Rops, void* dx, hipStream_t st) {
-  if (a.M == 0) return hipSuccess;
-#define OFT_DX_CASE(XF, F8, BB) \
-  if (a.xf32 == XF && a.fp8 == F8 && a.b == BB) return launch_dx_t<XF, F8, BB>(a, dy, wc, ws, Rops, dx, st);
-  OFT_DX_CASE(false, false, 32)
-  OFT_DX_CASE(false, false, 16)
-  OFT_DX_CASE(false, true, 32)
-  OFT_DX_CASE(false, true, 16)
-  OFT_DX_CASE(true, false, 32)
-  OFT_DX_CASE(true, false, 16)
-  OFT_DX_CASE(true, true, 32)
-  OFT_DX_CASE(true, true, 16)
-#undef OFT_DX_CASE
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_linear_dq(const DenseArgs& a, const DqPlan& p, const uint16_t* dy, const void* y,
-                            const float* Rf, float* dq, float* part, hipStream_t st) {
-  if (p.nsplit > 0) {
+hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t* dy, const void* y,
+                             const uint8_t* wc, const void* ws, const float* Rf, const uint16_t* Rops,
+                             void* dx, float* dq, char* work, hipStream_t st) {
+  float* part = reinterpret_cast<float*>(work);
+  uint16_t* dz = (dx != nullptr && p.prerotate && a.M > 0) ? reinterpret_cast<uint16_t*>(work + p.dz_off) : nullptr;
+  if ((dq != nullptr || dz != nullptr) && p.nsplit > 0) {
     dim3 grid((a.N + 63) / 64, p.nsplit);
-    if (a.xf32)
-      hipLaunchKernelGGL(dq_partial_kernel<true>, grid, dim3(256), 0, st, dy, y, part, a.M, a.N,
-                         p.rows_per_split, p.ng32);
-    else
-      hipLaunchKernelGGL(dq_partial_kernel<false>, grid, dim3(256), 0, st, dy, y, part, a.M, a.N,
-                         p.rows_per_split, p.ng32);
+    const float* s8 = a.fp8 ? static_cast<const float*>(ws) : nullptr;
+#define OFT_DQP(YF, F8, BB)                                                                               \
+  if (a.xf32 == YF && a.fp8 == F8 && a.b == BB)                                                           \
+    hipLaunchKernelGGL((dq_partial_kernel<YF, F8, BB>), grid, dim3(256), 0, st, dy, y, part, a.M, a.N,    \
+                       p.rows_per_split, p.ng32, Rops, s8, dz);
+    OFT_DQP(false, false, 32)
+    OFT_DQP(false, false, 16)
+    OFT_DQP(false, true, 32)
+    OFT_DQP(false, true, 16)
+    OFT_DQP(true, false, 32)
+    OFT_DQP(true, false, 16)
+    OFT_DQP(true, true, 32)
+    OFT_DQP(true, true, 16)
+#undef OFT_DQP
   }
-  const int nblk = a.N / a.b;
-  if (a.b == 32)
-    hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
-  else
-    hipLaunchKernelGGL(dq_final_kernel<16>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
-  return hipGetLastError();
+  if (dq != nullptr) {
+    const int nblk = a.N / a.b;
+    if (a.b == 32)
+      hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
+    else
+      hipLaunchKernelGGL(dq_final_kernel<16>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || dx == nullptr || a.M == 0) return err;
+#define OFT_DX(XF, F8, BB)                                                                              \
+  if (a.xf32 == XF && a.fp8 == F8 && a.b == BB)                                                         \
+    return dz != nullptr ? launch_dx_t<XF, F8, BB, PRO_NONE>(a, dz, wc, ws, Rops, dx, st)               \
+                         : launch_dx_t<XF, F8, BB, PRO_ROT>(a, dy, wc, ws, Rops, dx, st);
+  OFT_DX(false, false, 32)
+  OFT_DX(false, false, 16)
+  OFT_DX(false, true, 32)
+  OFT_DX(false, true, 16)
+  OFT_DX(true, false, 32)
+  OFT_DX(true, false, 16)
+  OFT_DX(true, true, 32)
+  OFT_DX(true, true, 16)
+#undef OFT_DX
+  return hipErrorInvalidValue;
 }
 
 }  // namespace oft

@@ -15,7 +15,14 @@
 namespace oft {
 namespace {
 
-constexpr int FWD_BM = 256;
+#ifndef OFT_FWD_BM
+#define OFT_FWD_BM 256
+#endif
+#ifndef OFT_FWD_NBUF
+#define OFT_FWD_NBUF 1
+#endif
+constexpr int FWD_BM = OFT_FWD_BM;
+constexpr int FWD_NBUF = OFT_FWD_NBUF;
 
 template <bool XF32, bool FP8, int B>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
@@ -33,7 +40,7 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
   p.N = a.N;
   p.g = a.g;
   dim3 grid((a.N + nt::BN - 1) / nt::BN, (a.M + FWD_BM - 1) / FWD_BM);
-  hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, FP8, B, EPI_ROT, false, XF32>), grid, dim3(256), 0,
+  hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, FP8, B, EPI_ROT, false, XF32, FWD_NBUF>), grid, dim3(256), 0,
                      st, p);
   return hipGetLastError();
 }

@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) void moe_dw_reduce_kernel(const float* __restr
 // One workgroup per (64 gate/up channels, expert): S = dH_blk^T H_blk over the
 // expert's rows (64-row steps through swizzled LDS transposes, MFMA), then the
 // Cayley gradient per block in fp32: Gq = (R^T + I) S (I + R) / 2,
-// dp_il = Gq_il - Gq_li.  Inactive experts get zeros.
+// dp_il = Gq_il - Gq_li.  Inactive experts get zeros.  When dz != nullptr
+// the same pass writes dz = dH_blk R_j (bf16, MFMA), the rotated operand of
+// the gate/up dX GEMM, once per dH tile.
 constexpr int LDM = 64 + 8;
 __device__ __forceinline__ int msw(int n) { return ((n >> 3) & 3) << 4; }
 
@@ -282,7 +284,8 @@ template <int B>
 __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict__ dH, const uint16_t* __restrict__ Hs,
                                                      int ld, const int* __restrict__ offsets,
                                                      const float* __restrict__ Rf, int nblk_e,
-                                                     float* __restrict__ dq) {
+                                                     float* __restrict__ dq, const uint16_t* __restrict__ Rops,
+                                                     uint16_t* __restrict__ dz) {
   __shared__ __attribute__((aligned(16))) uint16_t dYT[64 * LDM];
   __shared__ __attribute__((aligned(16))) uint16_t YT[64 * LDM];
   __shared__ float red[2][64][17];
@@ -302,7 +305,41 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  const int rg = wave & 1, rh = wave >> 1;
+  const int nbr = n0 + 32 * rg;
+  uint4 rtf[2] = {zero4(), zero4()};
+  if (dz != nullptr) {
+    const uint16_t* re = Rops + (size_t)e * nblk_e * 2 * B * B;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (B == 32) {
+        rtf[t] = *reinterpret_cast<const uint4*>(re + (size_t)(nbr / 32) * 2048 + 1024 + l32 * 32 + 16 * t + 8 * g2);
+      } else {
+        if ((l32 >> 4) == t)
+          rtf[t] = *reinterpret_cast<const uint4*>(re + (size_t)(nbr / 16 + t) * 512 + 256 + (l32 & 15) * 16 + 8 * g2);
+      }
+    }
+  }
   for (int ms = m_lo; ms < m_hi; ms += 64) {
+    if (dz != nullptr) {
+      const int m = ms + 32 * rh + l32;
+      const bool mok = m < m_hi;
+      uint4 f[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        f[t] = mok ? *reinterpret_cast<const uint4*>(dH + (size_t)m * ld + nbr + 16 * t + 8 * g2) : zero4();
+      f32x16 o;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+      o = mfma32(as_bf16x8(rtf[0]), as_bf16x8(f[0]), o);
+      o = mfma32(as_bf16x8(rtf[1]), as_bf16x8(f[1]), o);
+      if (mok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(dz + (size_t)m * ld + nbr + 8 * q + 4 * g2) =
+              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+      }
+    }
     uint4 d[2], y[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -335,6 +372,7 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
                    *reinterpret_cast<const bf16x8*>(&YT[n * LDM + mo]), acc);
     }
   }
+  if (dq == nullptr) return;
   if (kh == 1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[grp][lane][r] = acc[r];
@@ -418,6 +456,7 @@ MoeWs moe_ws_layout(const MoeDims& d, int pass) {
     w.dH = take((size_t)P * 2 * d.I * 2);
     w.dw_part = take((size_t)((d.I + 127) / 128) * P * 4);
     w.dXp = take((size_t)P * d.H * 2);
+    w.dz = take((size_t)P * 2 * d.I * 2);
   }
   w.bytes = off;
   return w;
@@ -565,12 +604,13 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
       hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part,
                          (d.I + 127) / 128, P, rt.inv_perm, q.dw);
   }
-  if (q.dq)
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
+  if (q.dq || (q.dx && d.T > 0))
     hipLaunchKernelGGL(moe_dq_kernel<B>, dim3(2 * d.I / 64, d.E), dim3(256), 0, st, dH, q.h_saved, 2 * d.I,
-                       rt.offsets, q.R_f32, nblk_e, q.dq);
+                       rt.offsets, q.R_f32, nblk_e, q.dq, q.R_ops, (q.dx && d.T > 0) ? dz : nullptr);
   if (q.dx && d.T > 0) {
     NnArgs p{};
-    p.src = dH;
+    p.src = dz;
     p.lds = 2 * d.I;
     p.wc = q.wgu_codes;
     p.ws = q.wgu_scales;
@@ -590,8 +630,8 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.perm = rt.perm;
     p.kslots = 0;
     dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_ROT, EPI_STORE, true>), grid, dim3(256), 0, st,
-                       p);
+    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_STORE, true>), grid, dim3(256), 0,
+                       st, p);
     const size_t n8 = (size_t)d.T * d.H / 8;
     hipLaunchKernelGGL(moe_unpermute_sum_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dXp, d.H,
                        d.k, rt.inv_perm, n8, q.dx);

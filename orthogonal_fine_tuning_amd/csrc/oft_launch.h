@@ -28,20 +28,21 @@ struct DenseArgs {
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                              const uint16_t* Rops, void* y, hipStream_t st);
 
-// Split of the M reduction used by dq (deterministic partials).
+// Backward plan: split of the M reduction used by dq (deterministic
+// partials) and the workspace layout.
 struct DqPlan {
   int nsplit;          // number of M slices
   int rows_per_split;  // multiple of 64
   int ng32;            // N / 32 column groups
   size_t part_bytes;   // fp32 partial sums, nsplit * ng32 * 32 * 32 * 4
+  bool prerotate;      // dX reads a rotated copy of dY made by the dq pass
+  size_t dz_off;       // workspace offset of that copy (bf16 [M, N])
+  size_t bytes;        // total workspace
 };
-DqPlan plan_dq(int M, int N);
+DqPlan plan_bwd(int M, int K, int N);
 
-hipError_t launch_linear_bwd_dx(const DenseArgs& a, const uint16_t* dy, const uint8_t* wc,
-                                const void* ws, const uint16_t* Rops, void* dx, hipStream_t st);
-
-hipError_t launch_linear_dq(const DenseArgs& a, const DqPlan& p, const uint16_t* dy,
-                            const void* y, const float* Rf, float* dq, float* part,
-                            hipStream_t st);
+hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t* dy, const void* y,
+                             const uint8_t* wc, const void* ws, const float* Rf, const uint16_t* Rops,
+                             void* dx, float* dq, char* work, hipStream_t st);
 
 }  // namespace oft

@@ -27,7 +27,7 @@ struct MoeRoutingDev {
 
 // byte offsets of the scratch buffers inside the caller's workspace
 struct MoeWs {
-  size_t list, ntiles, gmask, tile_off, act, O, dH, dw_part, dXp;
+  size_t list, ntiles, gmask, tile_off, act, O, dH, dw_part, dXp, dz;
   long max_tiles;
   size_t bytes;
 };
