@@ -5,18 +5,108 @@
 // sub-projection's rotation orthogonal; this library builds each b x b block
 // as R = (I + Q)(I - Q)^-1 = 2 (I - Q)^-1 - I from the skew-symmetric Q.
 //
-// Layout of the solve: one block per 2b lanes (b = 32: one block per wave,
-// b = 16: two blocks per wave).  Lane c owns column c of the augmented
-// matrix [A | I], A = I - Q, in registers; Gauss-Jordan elimination runs b
-// pivot steps, broadcasting the pivot column through LDS.  No pivot search
-// is needed: the symmetric part of A is I, so every pivot is >= 1.
+// Layout of the solve.  Few blocks (cayley_kernel): one workgroup of 4
+// waves per block, to spread each solve over 4 SIMDs; lane c of each wave
+// owns column c of the augmented matrix [A | I] (2b <= 64 columns) for the
+// b/4 rows of its wave's quarter, in registers.  Each of the b
+// Gauss-Jordan pivot steps publishes the pivot row and pivot column through
+// LDS (ping-pong slots, one barrier per step) and every lane updates its
+// rows.  No pivot search is needed: the symmetric part of A is I, so every
+// pivot is >= 1.
 #include "oft_device.h"
 #include "oft_launch.h"
 
 namespace oft {
 
 template <int B>
-__global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__ q, int nblk,
+__global__ __launch_bounds__(256) void cayley_kernel(const uint16_t* __restrict__ q, int nblk,
+                                                     float* __restrict__ Rf,
+                                                     uint16_t* __restrict__ Rops) {
+  constexpr int NT = 256;
+  constexpr int RQ = B / 4;  // rows per wave
+  constexpr int NP = B * (B - 1) / 2;
+  __shared__ float qs[NP];
+  __shared__ float prow[2][2 * B];  // pivot row (2b columns)
+  __shared__ float pcol[2][B];      // pivot column (b rows)
+  __shared__ float Rt[B][B + 1];    // result, for coalesced stores
+
+  const int blk = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int c = tid & 63;   // column of [A | I]
+  const int w = tid >> 6;   // row quarter
+  const bool colv = c < 2 * B;
+  for (int i = tid; i < NP; i += NT) qs[i] = bf16_to_f32(q[(size_t)blk * NP + i]);
+  __syncthreads();
+
+  float col[RQ];
+#pragma unroll
+  for (int u = 0; u < RQ; ++u) {
+    const int i = w * RQ + u;
+    float v = 0.0f;
+    if (c < B) {
+      float qic = 0.0f;
+      if (i < c) qic = qs[i * B - i * (i + 1) / 2 + (c - i - 1)];
+      if (i > c) qic = -qs[c * B - c * (c + 1) / 2 + (i - c - 1)];
+      v = (i == c ? 1.0f : 0.0f) - qic;
+    } else if (colv) {
+      v = (i == c - B) ? 1.0f : 0.0f;
+    }
+    col[u] = v;
+  }
+
+  for (int s = 0; s < B; ++s) {
+    const int sl = s & 1;
+    const int ws = s / RQ, us = s % RQ;
+    // publish the pivot row (owned by wave ws) and the pivot column (lane s)
+    if (w == ws && colv) {
+      float v = 0.0f;
+#pragma unroll
+      for (int u = 0; u < RQ; ++u)
+        if (u == us) v = col[u];
+      prow[sl][c] = v;
+    }
+    if (c == s) {
+#pragma unroll
+      for (int u = 0; u < RQ; ++u) pcol[sl][w * RQ + u] = col[u];
+    }
+    __syncthreads();
+    if (colv) {
+      const float ps = prow[sl][c] / prow[sl][s];  // new pivot-row entry of this column
+#pragma unroll
+      for (int u = 0; u < RQ; ++u) {
+        const int i = w * RQ + u;
+        col[u] = (i == s) ? ps : col[u] - pcol[sl][i] * ps;
+      }
+    }
+  }
+
+  // lanes b..2b-1 hold A^-1; R = 2 A^-1 - I
+  if (c >= B && colv) {
+    const int j = c - B;
+#pragma unroll
+    for (int u = 0; u < RQ; ++u) {
+      const int i = w * RQ + u;
+      Rt[i][j] = 2.0f * col[u] - (i == j ? 1.0f : 0.0f);
+    }
+  }
+  __syncthreads();
+  float* Rb = Rf + (size_t)blk * B * B;
+  uint16_t* R0 = Rops ? Rops + (size_t)blk * 2 * B * B : nullptr;
+  for (int e = tid; e < B * B; e += NT) {
+    const int i = e / B, j = e % B;
+    const float v = Rt[i][j];
+    Rb[e] = v;
+    if (R0) {
+      R0[e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);                   // R[i][j]
+      R0[B * B + j * B + i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);   // R^T[j][i]
+    }
+  }
+}
+
+// Many blocks: one wave solves 64 / (2b) blocks, lane c owning the whole
+// column c of [A | I] in registers, the pivot column broadcast through LDS.
+template <int B>
+__global__ __launch_bounds__(64) void cayley_wave_kernel(const uint16_t* __restrict__ q, int nblk,
                                                     float* __restrict__ Rf,
                                                     uint16_t* __restrict__ Rops) {
   constexpr int LANES = 2 * B;
@@ -110,11 +200,16 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint2* __restric
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st) {
   if (nblk == 0) return hipSuccess;
-  if (b == 32) {
-    hipLaunchKernelGGL(cayley_kernel<32>, dim3(nblk), dim3(64), 0, st, q, nblk, Rf, Rops);
+  if (nblk < 2048) {
+    if (b == 32)
+      hipLaunchKernelGGL(cayley_kernel<32>, dim3(nblk), dim3(256), 0, st, q, nblk, Rf, Rops);
+    else
+      hipLaunchKernelGGL(cayley_kernel<16>, dim3(nblk), dim3(256), 0, st, q, nblk, Rf, Rops);
   } else {
-    hipLaunchKernelGGL(cayley_kernel<16>, dim3((nblk + 1) / 2), dim3(64), 0, st, q, nblk, Rf,
-                       Rops);
+    if (b == 32)
+      hipLaunchKernelGGL(cayley_wave_kernel<32>, dim3(nblk), dim3(64), 0, st, q, nblk, Rf, Rops);
+    else
+      hipLaunchKernelGGL(cayley_wave_kernel<16>, dim3((nblk + 1) / 2), dim3(64), 0, st, q, nblk, Rf, Rops);
   }
   return hipGetLastError();
 }

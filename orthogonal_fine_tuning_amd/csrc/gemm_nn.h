@@ -54,6 +54,11 @@ struct NnArgs {
   const float* topk_w;    // [P] by pair id
   float* dw_part;         // [K / 128][P] by position
   long P;
+  // contraction split (few-token layers): workgroup z covers weight rows
+  // [z * nsplit_len, (z + 1) * nsplit_len) and stores fp32 partials to
+  // part[z][M][K]; nsplit_len == 0 means no split
+  int nsplit_len;
+  float* part;
 };
 
 namespace nn {
@@ -70,15 +75,16 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
 }
 }  // namespace nn
 
-template <int BM, bool OUTF32, bool FP8, int B, int PRO, int EPI, bool GROUPED>
-__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nn_kernel(NnArgs p) {
+template <int BM, bool OUTF32, bool FP8, int B, int PRO, int EPI, bool GROUPED, int NBUF = 2>
+__global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn_kernel(NnArgs p) {
   using namespace nn;
   static_assert(BM == 128 || BM == 256, "tile");
   constexpr int TM = BM / 64;   // 32-token tiles per wave (main product)
   constexpr int PM = BM / 128;  // 32-token tiles each wave prepares in the prologue
   constexpr int WSZ = BNS * LDW;        // weight tile [n][k]
   constexpr int STAGE = WSZ + BM * LDN;  // + B' tile [m][n]
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  static_assert(NBUF == 1 || NBUF == 2, "buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[NBUF * STAGE];
   __shared__ float dwred[EPI == EPI_SWIGLU_BWD ? 2 * BM : 1];
 
   const int tid = threadIdx.x;
@@ -271,15 +277,31 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nn_kernel(NnArgs 
     }
   };
 
-  const int ns = (N + BNS - 1) / BNS;
-  prefetch(0);
-  stage(0);
-  if (ns > 1) prefetch(BNS);
-  __syncthreads();
-  for (int s = 0; s < ns; ++s) {
-    compute(s & 1);
-    if (s + 1 < ns) stage((s + 1) & 1);
-    if (s + 2 < ns) prefetch((s + 2) * BNS);
+  const int nbeg = p.nsplit_len > 0 ? blockIdx.z * p.nsplit_len : 0;
+  const int nend = p.nsplit_len > 0 ? min(N, nbeg + p.nsplit_len) : N;
+  const int ns = (nend - nbeg + BNS - 1) / BNS;
+  if constexpr (NBUF == 2) {
+    if (ns > 0) {
+      prefetch(nbeg);
+      stage(0);
+      if (ns > 1) prefetch(nbeg + BNS);
+    }
+    __syncthreads();
+    for (int s = 0; s < ns; ++s) {
+      compute(s & 1);
+      if (s + 1 < ns) stage((s + 1) & 1);
+      if (s + 2 < ns) prefetch(nbeg + (s + 2) * BNS);
+      __syncthreads();
+    }
+  } else {
+    if (ns > 0) prefetch(nbeg);
+    for (int s = 0; s < ns; ++s) {
+      if (s > 0) __syncthreads();
+      stage(0);
+      __syncthreads();
+      if (s + 1 < ns) prefetch(nbeg + (s + 1) * BNS);
+      compute(0);
+    }
     __syncthreads();
   }
 
@@ -298,7 +320,10 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_nn_kernel(NnArgs 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const size_t off = (size_t)orow * p.ldo + kb + 8 * q + 4 * g2;
-          if constexpr (OUTF32) {
+          if (p.nsplit_len > 0) {
+            *reinterpret_cast<float4*>(p.part + (size_t)blockIdx.z * p.M * p.ldo + off) =
+                make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+          } else if constexpr (OUTF32) {
             *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) =
                 make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
           } else {

@@ -198,9 +198,14 @@ __global__ __launch_bounds__(256) void dq_final_kernel(const float* __restrict__
   const int g32 = (j * B) / 32, off = (j * B) % 32;
   for (int e = tid; e < B * B; e += 256) {
     const int r = e / B, c = e % B;
+    // all slice loads in flight first (nsplit <= 16), then a fixed-order sum
+    float v[16];
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp)
+      v[sp] = sp < nsplit ? part[((size_t)sp * ng32 + g32) * 1024 + (off + r) * 32 + off + c] : 0.0f;
     float s = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp)
-      s += part[((size_t)sp * ng32 + g32) * 1024 + (off + r) * 32 + off + c];
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) s += v[sp];
     S[r][c] = s;
     Rm[r][c] = Rf[(size_t)j * B * B + e];
   }
@@ -234,10 +239,38 @@ __global__ __launch_bounds__(256) void dq_final_kernel(const float* __restrict__
   }
 }
 
+// dx[m][k] = sum_z part[z][m][k] in a fixed order (contraction split)
+template <bool XF32>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int nsplit, size_t n4,
+                                                           void* __restrict__ dx) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 s = reinterpret_cast<const float4*>(part)[i];
+  for (int z = 1; z < nsplit; ++z) {
+    const float4 v = reinterpret_cast<const float4*>(part)[(size_t)z * n4 + i];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  if constexpr (XF32) {
+    reinterpret_cast<float4*>(dx)[i] = s;
+  } else {
+    reinterpret_cast<uint2*>(dx)[i] = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+  }
+}
+
+#ifndef OFT_DX_BM
+#define OFT_DX_BM 128
+#endif
+#ifndef OFT_DX_NBUF
+#define OFT_DX_NBUF 1
+#endif
 template <bool XF32, bool FP8, int B, int PRO>
-hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* src, const uint8_t* wc, const void* ws,
-                       const uint16_t* Rops, void* dx, hipStream_t st) {
-  constexpr int BM = 128;
+hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src, const uint8_t* wc,
+                       const void* ws, const uint16_t* Rops, void* dx, char* work, hipStream_t st) {
+  constexpr int BM = OFT_DX_BM;
+  constexpr int NB = OFT_DX_NBUF;
   NnArgs p{};
   p.src = src;
   p.lds = a.N;
@@ -250,8 +283,17 @@ hipError_t launch_dx_t(const DenseArgs& a, const uint16_t* src, const uint8_t* w
   p.K = a.K;
   p.N = a.N;
   p.g = a.g;
-  dim3 grid((a.K + nn::BKO - 1) / nn::BKO, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8, B, PRO, EPI_STORE, false>), grid, dim3(256), 0, st, p);
+  dim3 grid((a.K + nn::BKO - 1) / nn::BKO, (a.M + BM - 1) / BM, pl.nsplit_n > 1 ? pl.nsplit_n : 1);
+  if (pl.nsplit_n > 1) {
+    p.nsplit_len = pl.nsplit_len;
+    p.part = reinterpret_cast<float*>(work + pl.npart_off);
+  }
+  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
+  if (pl.nsplit_n > 1) {
+    const size_t n4 = (size_t)a.M * a.K / 4;
+    hipLaunchKernelGGL(split_reduce_kernel<XF32>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, p.part,
+                       pl.nsplit_n, n4, dx);
+  }
   return hipGetLastError();
 }
 
@@ -279,7 +321,27 @@ DqPlan plan_bwd(int M, int K, int N) {
   // 128-column tiles of dX) keep the rotation in the dX GEMM prologue.
   p.prerotate = K > 2 * nn::BKO;
   p.dz_off = (p.part_bytes + 255) / 256 * 256;
-  p.bytes = p.dz_off + (p.prerotate ? (size_t)M * N * 2 : 0);
+  size_t end = p.dz_off + (p.prerotate ? (size_t)M * N * 2 : 0);
+  // Few tokens: the dX GEMM has (K / 128) x 1 tiles only; split its
+  // contraction so that about 512 workgroups stream the weight, each
+  // writing an fp32 partial reduced afterwards in a fixed order.
+  p.nsplit_n = 1;
+  p.nsplit_len = 0;
+  p.npart_off = 0;
+  const int ktiles = (K + nn::BKO - 1) / nn::BKO;
+  if (M > 0 && M <= 128 && p.prerotate) {
+    int want = (512 + ktiles - 1) / ktiles;
+    const int nsteps = (N + nn::BNS - 1) / nn::BNS;
+    if (want > nsteps) want = nsteps;
+    if (want > 1) {
+      const int steps_per = (nsteps + want - 1) / want;
+      p.nsplit_len = steps_per * nn::BNS;
+      p.nsplit_n = (N + p.nsplit_len - 1) / p.nsplit_len;
+      p.npart_off = (end + 255) / 256 * 256;
+      end = p.npart_off + (size_t)p.nsplit_n * M * K * 4;
+    }
+  }
+  p.bytes = end;
   return p;
 }
 
@@ -316,8 +378,8 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
   if (err != hipSuccess || dx == nullptr || a.M == 0) return err;
 #define OFT_DX(XF, F8, BB)                                                                              \
   if (a.xf32 == XF && a.fp8 == F8 && a.b == BB)                                                         \
-    return dz != nullptr ? launch_dx_t<XF, F8, BB, PRO_NONE>(a, dz, wc, ws, Rops, dx, st)               \
-                         : launch_dx_t<XF, F8, BB, PRO_ROT>(a, dy, wc, ws, Rops, dx, st);
+    return dz != nullptr ? launch_dx_t<XF, F8, BB, PRO_NONE>(a, p, dz, wc, ws, Rops, dx, work, st)     \
+                         : launch_dx_t<XF, F8, BB, PRO_ROT>(a, p, dy, wc, ws, Rops, dx, work, st);
   OFT_DX(false, false, 32)
   OFT_DX(false, false, 16)
   OFT_DX(false, true, 32)

@@ -5,11 +5,13 @@
 // independent rotation per sub-projection, applied by custom split-projection
 // kernels ("Five design features of the adapter-first architecture").
 //
-// One launch of gemm_nt_kernel (gemm_nt.h) with the rotation epilogue: a
-// 32-channel accumulator group is exactly one b = 32 block (or two b = 16
-// blocks), and blocks never straddle projection segments, so every segment
-// gets its own rotation with no extra pass over HBM.
+// One launch of gemm_nt_kernel (gemm_nt.h) with the rotation epilogue, or of
+// gemm_nt_skinny_kernel (gemm_skinny.h) for decode batches of at most 64
+// tokens: a 32-channel accumulator group is exactly one b = 32 block (or two
+// b = 16 blocks), and blocks never straddle projection segments, so every
+// segment gets its own rotation with no extra pass over HBM.
 #include "gemm_nt.h"
+#include "gemm_skinny.h"
 #include "oft_launch.h"
 
 namespace oft {
@@ -27,6 +29,30 @@ constexpr int FWD_NBUF = OFT_FWD_NBUF;
 template <bool XF32, bool FP8, int B>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                         const uint16_t* Rops, void* y, hipStream_t st) {
+  if (a.M <= 64 && a.K % 256 == 0) {  // few tokens: weight-streaming kernel
+    NtArgs p{};
+    p.a = x;
+    p.lda = a.K;
+    p.wc = wc;
+    p.ws = ws;
+    p.rops = Rops;
+    p.out = y;
+    p.ldo = a.N;
+    p.M = a.M;
+    p.K = a.K;
+    p.N = a.N;
+    p.g = a.g;
+#ifndef OFT_SKINNY_TN
+#define OFT_SKINNY_TN 2
+#endif
+    constexpr int TN = OFT_SKINNY_TN;
+    if (a.N % (32 * TN) == 0) {
+      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, TN>), dim3(a.N / (32 * TN), 1), dim3(256), 0, st, p);
+    } else {
+      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, 1>), dim3(a.N / 32, 1), dim3(256), 0, st, p);
+    }
+    return hipGetLastError();
+  }
   NtArgs p{};
   p.a = x;
   p.lda = a.K;

@@ -28,6 +28,10 @@ namespace oft {
 namespace {
 
 constexpr int MOE_BM = 128;  // rows (expert positions) per grouped tile
+#ifndef OFT_MOE_NBUF
+#define OFT_MOE_NBUF 1
+#endif
+constexpr int MOE_NBUF = OFT_MOE_NBUF;  // LDS buffers of the grouped GEMMs
 
 // ---------------------------------------------------------------- wave scans
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -40,14 +44,17 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// exclusive scan of v over a block of 1024 threads; also returns the total
+// exclusive scan of v over the workgroup (blockDim.x a multiple of 64, at
+// most 1024): wavefront inclusive scans, then a scan of the wave totals by
+// wave 0; also returns the total.  sh needs 33 ints.
 __device__ int block_excl_scan(int v, int* total, int* sh) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = blockDim.x >> 6;
   const int inc = wave_incl_scan(v);
   if (lane == 63) sh[w] = inc;
   __syncthreads();
   if (w == 0) {
-    const int wt = lane < 16 ? sh[lane] : 0;
+    const int wt = lane < nw ? sh[lane] : 0;
     const int ws = wave_incl_scan(wt);
     if (lane < 16) sh[16 + lane] = ws - wt;
     if (lane == 15) sh[32] = ws;
@@ -158,26 +165,35 @@ __device__ void write_work_list(int cnt_e, int e, int E, int bm, int* list, int*
   if (threadIdx.x == 0) *ntiles = total;
 }
 
-__global__ __launch_bounds__(1024) void moe_scan_kernel(const unsigned long long* __restrict__ gmask,
-                                                        int ntile64, int E, int chunk, MoeRoutingDev rt,
-                                                        int* __restrict__ tile_off, int* __restrict__ list,
-                                                        int* __restrict__ ntiles) {
+// per expert (one workgroup each): counts over the 64-token tiles and the
+// exclusive scan over tiles, relative to the expert's first position
+__global__ __launch_bounds__(256) void moe_tilescan_kernel(const unsigned long long* __restrict__ gmask,
+                                                           int ntile64, int E, int* __restrict__ tile_rel,
+                                                           int* __restrict__ counts) {
+  __shared__ int sh[40];
+  const int e = blockIdx.x;
+  int carry = 0;
+  for (int t0 = 0; t0 < ntile64; t0 += 256) {
+    const int t = t0 + threadIdx.x;
+    const int c = t < ntile64 ? __popcll(gmask[(size_t)t * E + e]) : 0;
+    int tot;
+    const int ex = block_excl_scan(c, &tot, sh);
+    if (t < ntile64) tile_rel[(size_t)t * E + e] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// one workgroup: offsets (scan over experts), active list, chunk table and
+// the grouped-GEMM work list
+__global__ __launch_bounds__(1024) void moe_scan_kernel(int E, int chunk, MoeRoutingDev rt,
+                                                        int* __restrict__ list, int* __restrict__ ntiles) {
   __shared__ int sh[40];
   const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E)
-    for (int tl = 0; tl < ntile64; ++tl) cnt += __popcll(gmask[(size_t)tl * E + e]);
+  const int cnt = e < E ? rt.counts[e] : 0;
   int total;
   const int off = block_excl_scan(cnt, &total, sh);
-  if (e < E) {
-    rt.counts[e] = cnt;
-    rt.offsets[e] = off;
-    int run = off;
-    for (int tl = 0; tl < ntile64; ++tl) {
-      tile_off[(size_t)tl * E + e] = run;
-      run += __popcll(gmask[(size_t)tl * E + e]);
-    }
-  }
+  if (e < E) rt.offsets[e] = off;
   if (e == 0) rt.offsets[E] = total;
   int nact;
   const int rank = block_excl_scan((e < E && cnt > 0) ? 1 : 0, &nact, sh);
@@ -200,7 +216,8 @@ __global__ __launch_bounds__(1024) void moe_worklist_kernel(const int* __restric
 // ---------------------------------------------------------------- permute
 __global__ __launch_bounds__(64) void moe_permute_kernel(const int* __restrict__ idx, int T, int E, int k,
                                                          const unsigned long long* __restrict__ gmask,
-                                                         const int* __restrict__ tile_off,
+                                                         const int* __restrict__ tile_rel,
+                                                         const int* __restrict__ offsets,
                                                          int* __restrict__ perm, int* __restrict__ inv_perm) {
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(64) void moe_permute_kernel(const int* __restrict__
   for (int j = 0; j < k; ++j) {
     const int e = idx[(size_t)t * k + j];
     const int rank = __popcll(gmask[(size_t)tile * E + e] & below);
-    const int pos = tile_off[(size_t)tile * E + e] + rank;
+    const int pos = offsets[e] + tile_rel[(size_t)tile * E + e] + rank;
     perm[pos] = t * k + j;
     inv_perm[t * k + j] = pos;
   }
@@ -473,13 +490,15 @@ hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRout
     hipLaunchKernelGGL(moe_count_kernel, dim3(nt64), dim3(64), (size_t)d.E * 8, st, rt.topk_idx, d.T, d.E, d.k,
                        reinterpret_cast<unsigned long long*>(ws + L.gmask));
   }
-  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st,
-                     reinterpret_cast<const unsigned long long*>(ws + L.gmask), nt64, d.E, d.chunk, rt,
-                     reinterpret_cast<int*>(ws + L.tile_off), list, ntiles);
+  // (with no tokens the tile loop is empty and every count is written as 0)
+  hipLaunchKernelGGL(moe_tilescan_kernel, dim3(d.E), dim3(256), 0, st,
+                     reinterpret_cast<const unsigned long long*>(ws + L.gmask), nt64, d.E,
+                     reinterpret_cast<int*>(ws + L.tile_off), rt.counts);
+  hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(1024), 0, st, d.E, d.chunk, rt, list, ntiles);
   if (d.T > 0)
     hipLaunchKernelGGL(moe_permute_kernel, dim3(nt64), dim3(64), 0, st, rt.topk_idx, d.T, d.E, d.k,
                        reinterpret_cast<const unsigned long long*>(ws + L.gmask),
-                       reinterpret_cast<const int*>(ws + L.tile_off), rt.perm, rt.inv_perm);
+                       reinterpret_cast<const int*>(ws + L.tile_off), rt.offsets, rt.perm, rt.inv_perm);
   return last();
 }
 
@@ -517,7 +536,7 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.perm = rt.perm;
     p.kslots = d.k;
     dim3 grid(d.I / 64, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false, MOE_NBUF>), grid, dim3(256), 0,
                        st, p);
   }
   {
@@ -542,7 +561,7 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.perm = rt.perm;
     p.kslots = 0;
     dim3 grid((d.H + nt::BN - 1) / nt::BN, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false, MOE_NBUF>), grid, dim3(256), 0, st,
                        p);
   }
   const size_t n8 = (size_t)d.T * d.H / 8;
@@ -598,7 +617,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.dw_part = dw_part;
     p.P = P;
     dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_SWIGLU_BWD, true>), grid, dim3(256),
+    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>), grid, dim3(256),
                        0, st, p);
     if (q.dw)
       hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part,
@@ -630,7 +649,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.perm = rt.perm;
     p.kslots = 0;
     dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_STORE, true>), grid, dim3(256), 0,
+    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid, dim3(256), 0,
                        st, p);
     const size_t n8 = (size_t)d.T * d.H / 8;
     hipLaunchKernelGGL(moe_unpermute_sum_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dXp, d.H,

@@ -37,6 +37,9 @@ struct DqPlan {
   size_t part_bytes;   // fp32 partial sums, nsplit * ng32 * 32 * 32 * 4
   bool prerotate;      // dX reads a rotated copy of dY made by the dq pass
   size_t dz_off;       // workspace offset of that copy (bf16 [M, N])
+  int nsplit_n;        // contraction splits of the dX GEMM (1 = none)
+  int nsplit_len;      // weight rows per split
+  size_t npart_off;    // workspace offset of the fp32 dX partials
   size_t bytes;        // total workspace
 };
 DqPlan plan_bwd(int M, int K, int N);

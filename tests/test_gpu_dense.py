@@ -29,6 +29,11 @@ SMALL = {
                                      x_dtype="f32", w_fmt="int4", g=32),
     "decode_m1": DenseConfig("decode_m1", M=1, K=256, segs=(128, 128), b=32, x_dtype="bf16",
                              w_fmt="int4", g=128),
+    # few tokens, wide layer: weight-streaming forward, split-contraction dX
+    "decode_split": DenseConfig("decode_split", M=100, K=512, segs=(256, 192), b=32, x_dtype="bf16",
+                                w_fmt="int4", g=128),
+    "decode_split_fp8_b16": DenseConfig("decode_split_fp8_b16", M=37, K=768, segs=(64, 96), b=16,
+                                        x_dtype="bf16", w_fmt="fp8"),
 }
 
 
@@ -193,3 +198,26 @@ def test_dense_full_size_sampled(name):
     orth = np.abs(np.swapaxes(R32, 1, 2) @ R32 - np.eye(cfg.b)).max()
     print(f"  err y={e_y:.2e} dx={e_dx:.2e} dq={e_dq:.2e} orth={orth:.1e}", flush=True)
     assert max(e_y, e_dx, e_dq) <= TOL and orth <= 1e-3
+
+
+@pytest.mark.parametrize("b", [32, 16])
+def test_cayley_many_blocks(b):
+    """Enough blocks for the one-wave-per-block variant of the solve."""
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+    from oft_inputs import to_bf16_bits
+
+    nblk = 3000
+    rng = np.random.default_rng(b)
+    p = to_bf16_bits(rng.normal(0.0, 0.3, size=(nblk, b * (b - 1) // 2)).astype(np.float32))
+    Rf = torch.empty((nblk, b, b), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((nblk, 2, b, b), dtype=torch.int16, device="cuda")
+    oft.cayley_build(dev(p), nblk, b, Rf, Rops)
+    torch.cuda.synchronize()
+    R = host(Rf).astype(np.float64)
+    ref = odense.cayley(p, b)
+    assert err(R, ref) <= 1e-5
+    assert np.abs(np.swapaxes(R, 1, 2) @ R - np.eye(b)).max() <= 1e-3
+    ops = host(Rops, np.uint16)
+    assert np.array_equal(ops[:, 0], codec.f32_to_bf16_bits(host(Rf)))
+    assert np.array_equal(ops[:, 1], np.swapaxes(ops[:, 0], 1, 2))
