@@ -74,6 +74,7 @@ def dense_bytes(cfg):
 
 FWD_KERNEL_SOURCES = ["orthogonal_fine_tuning_amd/csrc/linear_fwd.hip",
                       "orthogonal_fine_tuning_amd/csrc/gemm_nt.h",
+                      "orthogonal_fine_tuning_amd/csrc/gemm_nt_dma.h",
                       "orthogonal_fine_tuning_amd/csrc/gemm_skinny.h",
                       "orthogonal_fine_tuning_amd/csrc/oft_device.h"]
 
@@ -82,6 +83,8 @@ def fwd_kernel_name(cfg):
     """The kernel oft_linear_fwd launches for this shape (one launch per call)."""
     if cfg.M <= 64 and cfg.K % 256 == 0:
         return "gemm_nt_skinny_kernel"
+    if cfg.x_dtype == "bf16":
+        return "gemm_nt_dma_kernel"
     return "gemm_nt_kernel"
 
 
@@ -363,7 +366,7 @@ def main():
     achieved = f_fwd / t_fwd / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(f"gemm_nt_kernel:{cfg.name}", sha),
+            "traffic": load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha),
             "kernel": fwd_kernel_name(cfg), "kernel_us": round(t_fwd * 1e6, 2),
             "source_sha": sha}
 

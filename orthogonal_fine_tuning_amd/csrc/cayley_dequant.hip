@@ -184,8 +184,7 @@ __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __res
   const int per_row = cols / 8;
   const size_t r = idx / per_row;
   const int c = (int)(idx % per_row) * 8;
-  const float s = fp16_to_f32(scales[r * (size_t)(cols / g) + c / g]);
-  out[idx] = dq_int4x8(codes[idx], s);
+  out[idx] = dq_int4x8(codes[idx], i4scale(scales[r * (size_t)(cols / g) + c / g]));
 }
 
 __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint2* __restrict__ codes,

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
   const int wrow = tid >> 2, wq = tid & 3;
   const bool k_ok = (k0 + 32 * wq) < K;
   uint4 wr[FP8 ? 2 : 1];
-  float wsc = 0.0f;
+  uint16_t wsb = 0;  // INT4: fp16 scale bits of the prefetched weight row
 
   // source rows this wave feeds to the prologue
   long srow[PM];
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
         wr[1] = ok ? *reinterpret_cast<const uint4*>(src + 16) : zero4();
       } else {
         wr[0] = ok ? *reinterpret_cast<const uint4*>(wc + (size_t)n * (K / 2) + (k0 + 32 * wq) / 2) : zero4();
-        wsc = ok ? fp16_to_f32(ws_h[(size_t)n * (K / p.g) + (k0 + 32 * wq) / p.g]) : 0.0f;
+        wsb = ok ? ws_h[(size_t)n * (K / p.g) + (k0 + 32 * wq) / p.g] : (uint16_t)0;
       }
     }
 #pragma unroll
@@ -194,6 +194,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
         dst[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     } else {
+      const I4Scale wsc = i4scale(wsb);
       dst[0] = dq_int4x8(wr[0].x, wsc);
       dst[1] = dq_int4x8(wr[0].y, wsc);
       dst[2] = dq_int4x8(wr[0].z, wsc);

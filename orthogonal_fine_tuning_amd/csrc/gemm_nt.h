@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
     xrow[i] = r < nrows ? a_row(r) : -1;
   }
   uint4 wr[FP8 ? 2 : 1];
-  float wsc = 0.0f;
+  uint16_t wsb = 0;  // INT4: fp16 scale bits of the prefetched weight row
   const int w_row = tid >> 1, w_half = tid & 1;
   const int wchan = w_chan(w_row);
   const bool w_ok = wchan < p.N;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
     } else {
       const uint8_t* src = wc + n * (K / 2) + k0 / 2 + 16 * w_half;
       wr[0] = w_ok ? *reinterpret_cast<const uint4*>(src) : zero4();
-      wsc = w_ok ? fp16_to_f32(ws_h[n * (K / p.g) + (k0 + 32 * w_half) / p.g]) : 0.0f;
+      wsb = w_ok ? ws_h[n * (K / p.g) + (k0 + 32 * w_half) / p.g] : (uint16_t)0;
     }
   };
 
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
         dst[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     } else {
+      const I4Scale wsc = i4scale(wsb);
       dst[0] = dq_int4x8(wr[0].x, wsc);
       dst[1] = dq_int4x8(wr[0].y, wsc);
       dst[2] = dq_int4x8(wr[0].z, wsc);

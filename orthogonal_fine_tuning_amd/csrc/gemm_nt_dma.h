@@ -1,0 +1,299 @@
+// Forward dequant GEMM with asynchronous global -> LDS copies (dense, bf16 x):
+//   C^T[n][m] = sum_k W[n][k] x[m][k],  then the rotation epilogue of gemm_nt.h.
+//
+// Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 256 or 128), K
+// steps of 64.  Wave (wn, wm) = (wave % 4, wave / 4) owns channels
+// 64 wn + [0, 64) and tokens wm BM / 2 + [0, BM / 2).
+//
+// Everything the main loop reads from HBM travels by global_load_lds (16 or
+// 4 bytes per lane; lane l of an instruction writes LDS bytes [s l, s l + s)
+// after the wave-uniform base in M0), through a ring of three LDS stages:
+//   activations : BM rows x 128 bytes (one full cache line per row);
+//   weight codes: 256 rows x 64 bytes (FP8) or x 32 bytes plus one 4-byte
+//                 word per row holding its fp16 group scale(s) (INT4).
+// Each wave copies an eighth of both.  The copies for step s + 2 are issued
+// right after the barrier of step s, so each has two steps of matrix-core
+// work to land; no registers hold data in flight.  The kernel counts its
+// copies itself (vmcnt): they are assembly, so the compiler neither waits
+// for them before unrelated LDS reads nor miscounts its own loads around
+// them, and the loop issues no other global loads.  One barrier per step:
+// it publishes step s and retires the reads of step s - 1, whose stage the
+// copies of step s + 2 then overwrite.
+//
+// Weights are dequantised by the waves that multiply them, from the LDS
+// codes straight into matrix-core operands (FP8: exact conversion, its
+// per-channel scale applied in the fp32 epilogue; INT4: bf16(q s) with the
+// group scale, the same values as the dequant hook).
+//
+// Contraction order: in MFMA kk (0..3) of a step, lane group g2 takes the
+// in-features 32 g2 + 8 kk + p (p = 0..7) for both operands, so a lane's
+// weight codes for the whole step are contiguous (32 FP8 or 16 INT4 bytes)
+// and each activation operand is one 16-byte read.
+//
+// LDS layouts: 16-byte chunk c of a row r sits at chunk c ^ h(r), chosen so
+// that the 16-byte operand reads of any 8 consecutive rows hit 8 distinct
+// slots of a 128-byte bank window and those of any 16 rows 16 distinct slots
+// of a 256-byte window: h = (r ^ ((r >> 3) & 1)) & 7 for activation rows (8
+// chunks), ((r >> 1) ^ (r >> 3)) & 3 for FP8 code rows (4 chunks) and
+// ((r >> 2) ^ (r >> 3)) & 1 for INT4 code rows (2 chunks).
+#pragma once
+
+#include "gemm_nt.h"
+
+namespace oft {
+
+namespace ntd {
+constexpr int BN = 256;  // channels per workgroup
+constexpr int BK = 64;   // in-features per step
+constexpr int NST = 3;   // ring depth
+constexpr int NTHR = 512;
+template <int BM> constexpr int X_BYTES = BM * BK * 2;
+template <bool FP8> constexpr int W_BYTES = FP8 ? BN * BK : BN * BK / 2 + BN * 4;
+__device__ __forceinline__ int swz_x(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+__device__ __forceinline__ int swz_w8(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_w4(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+// 16 (or 4) bytes per lane from base + voff to LDS byte address lds + 16 l (4 l)
+__device__ __forceinline__ void copy16(uint32_t lds, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4(uint32_t lds, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+// wait until at most N copies of this wave are in flight, then a workgroup
+// barrier that also retires this wave's LDS reads
+template <int N>
+__device__ __forceinline__ void wait_copies_barrier() {
+  static_assert(N == 0 || N == 4 || N == 6, "copies per step");
+  if constexpr (N == 0)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4)
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+}  // namespace ntd
+
+template <bool FP8, int B, int BM>
+__global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
+  using namespace ntd;
+  static_assert(BM == 128 || BM == 256, "tile");
+  constexpr int TM = BM / 64;  // 32-token tiles per wave
+  constexpr int XB = X_BYTES<BM>;
+  constexpr int WB = W_BYTES<FP8>;
+  constexpr int XI = BM / 64;  // activation copies per wave and step (8 rows each)
+  constexpr int V = XI + 2;    // copies per wave and step
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NST * XB];
+  __shared__ __attribute__((aligned(16))) uint8_t wsm[NST * WB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, wm = wave >> 2;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int K = p.K;
+  const int n0 = blockIdx.x * BN;
+  const int pos0 = blockIdx.y * BM;
+  const int nrows = min(BM, p.M - pos0);
+  const int nk = K / BK;
+  const int kg = FP8 ? 1 : K / p.g;  // INT4 scales per row
+  const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;  // INT4: log2(64 / g)
+
+  // ---- copy sources: per-lane 32-bit offsets from wave-uniform bases
+  const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
+  uint32_t xoff[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = (BM / 8) * wave + 8 * i + (lane >> 3);
+    const int rr = r < nrows ? r : 0;  // rows past the end copy row 0; never stored
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + 16 * ((lane & 7) ^ swz_x(r)));
+  }
+  const uint32_t x_lds = lds_addr(xs) + (uint32_t)((BM / 8) * wave * 128);
+
+  // rows past N copy the workgroup's first row (their outputs are never stored)
+  auto crow = [&](int rw) { return n0 + rw < p.N ? rw : 0; };
+  const uint8_t* wbase = p.wc + (FP8 ? (size_t)n0 * K : (size_t)n0 * (K / 2));
+  uint32_t woff[2] = {0u, 0u};
+  uint32_t sbase = 0;  // INT4: index of the copy row's first scale
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rw = 32 * wave + 16 * i + (lane >> 2);
+      woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 3) ^ swz_w8(rw)));
+    }
+  } else {
+    const int rw = 32 * wave + (lane >> 1);
+    woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
+    sbase = (uint32_t)((n0 + crow(32 * wave + l32)) * kg);
+  }
+  const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(FP8 ? 32 * wave * 64 : 32 * wave * 32);
+  const uint32_t s_lds = lds_addr(wsm) + (uint32_t)(BN * BK / 2 + 32 * wave * 4);
+  // first scale of step s: (64 s) / g
+  auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
+
+  auto issue = [&](int s) {
+    const int st = s % NST;
+    const uint8_t* xb = xbase + (size_t)s * BK * 2;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) copy16(x_lds + st * XB + i * 1024, xb, xoff[i]);
+    if constexpr (FP8) {
+      const uint8_t* wb = wbase + (size_t)s * BK;
+      copy16(w_lds + st * WB, wb, woff[0]);
+      copy16(w_lds + st * WB + 1024, wb, woff[1]);
+    } else {
+      copy16(w_lds + st * WB, wbase + (size_t)s * (BK / 2), woff[0]);
+      // lanes 0..31: the 4-byte word holding the step's scale(s) of row 32 wave + lane
+      if (lane < 32) copy4(s_lds + st * WB, p.ws, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
+    }
+  };
+
+  // ---- operand reads
+  uint32_t xrd[TM];  // activation row r = wm BM / 2 + 32 tm + l32
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) xrd[tm] = (uint32_t)((wm * (BM / 2) + 32 * tm + l32) * 128);
+  const int xsw = swz_x(l32);  // h depends on bits 0..3 of the row only: the same for every tm, wm
+  uint32_t wrd[2][2];
+  uint32_t srd[2] = {0u, 0u};  // INT4: scale index of the operand row at k = 0
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) {
+    const int rw = 64 * wn + 32 * tn + l32;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wrd[tn][j] = (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
+    } else {
+      wrd[tn][0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
+      wrd[tn][1] = 0u;
+      srd[tn] = (uint32_t)((n0 + crow(rw)) * kg);
+    }
+  }
+
+  f32x16 acc[2][TM];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  auto compute = [&](int s) {
+    const int st = s % NST;
+    const uint8_t* X = xs + st * XB;
+    const uint8_t* W = wsm + st * WB;
+    uint32_t cw[2][8];  // this lane's codes for the step (INT4: words 0..3)
+    I4Scale sc[2];
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+      if constexpr (FP8) {
+        const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[tn][0]);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[tn][1]);
+        cw[tn][0] = c0.x; cw[tn][1] = c0.y; cw[tn][2] = c0.z; cw[tn][3] = c0.w;
+        cw[tn][4] = c1.x; cw[tn][5] = c1.y; cw[tn][6] = c1.z; cw[tn][7] = c1.w;
+      } else {
+        const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[tn][0]);
+        cw[tn][0] = c0.x; cw[tn][1] = c0.y; cw[tn][2] = c0.z; cw[tn][3] = c0.w;
+        const int rw = 64 * wn + 32 * tn + l32;
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(W + BN * BK / 2 + rw * 4);
+        // this lane's in-features 64 s + 32 g2 .. + 31 lie in group (64 s + 32 g2) / g
+        const uint32_t idx = srd[tn] + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
+        sc[tn] = i4scale((uint16_t)(word >> (16 * (idx & 1))));
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a[2], b[TM];
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        if constexpr (FP8) {
+          const uint2 lo = dq_fp8x4(cw[tn][2 * kk]), hi = dq_fp8x4(cw[tn][2 * kk + 1]);
+          a[tn] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        } else {
+          a[tn] = as_bf16x8(dq_int4x8(cw[tn][kk], sc[tn]));
+        }
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        b[tm] = *reinterpret_cast<const bf16x8*>(X + xrd[tm] + 16 * ((4 * g2 + kk) ^ xsw));
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma32(a[tn], b[tm], acc[tn][tm]);
+    }
+  };
+
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int s = 0; s < nk; ++s) {
+    if (s + 1 < nk) wait_copies_barrier<V>(); else wait_copies_barrier<0>();
+    if (s + 2 < nk) issue(s + 2);
+    compute(s);
+  }
+
+  // ------------------------------------------------------------ epilogue (rotation)
+  const float* ws_f = static_cast<const float*>(p.ws);
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) {
+    const int nb = n0 + 64 * wn + 32 * tn;
+    if (nb >= p.N) continue;
+    float fs[16];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
+        fs[4 * q] = v.x;
+        fs[4 * q + 1] = v.y;
+        fs[4 * q + 2] = v.z;
+        fs[4 * q + 3] = v.w;
+      }
+    }
+    bf16x8 ra[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+      if constexpr (B == 32) {
+        const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
+        lo = *reinterpret_cast<const uint2*>(Rj);
+        hi = *reinterpret_cast<const uint2*>(Rj + 8);
+      } else {
+        if ((l32 >> 4) == t) {
+          const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+          lo = *reinterpret_cast<const uint2*>(Rj);
+          hi = *reinterpret_cast<const uint2*>(Rj + 8);
+        }
+      }
+      ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      f32x16 z = acc[tn][tm];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] *= fs[r];
+      }
+      bf16x8 zb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
+                                     pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
+      f32x16 o;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+      o = mfma32(ra[0], zb[0], o);
+      o = mfma32(ra[1], zb[1], o);
+      const int ml = wm * (BM / 2) + 32 * tm + l32;
+      if (ml >= nrows) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
+            make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+      }
+    }
+  }
+}
+
+}  // namespace oft

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
 
   struct Chunk {
     uint4 w[TN][FP8 ? 2 : 1];
-    float s[TN];
+    uint16_t s[TN];  // INT4: fp16 scale bits
     uint4 x[2][4][AF32 ? 2 : 1];
   };
   auto load = [&](Chunk& ch, int kc) {
@@ -59,10 +59,10 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
         const uint8_t* src = p.wc + n * K + kk;
         ch.w[tn][0] = *reinterpret_cast<const uint4*>(src);
         ch.w[tn][1] = *reinterpret_cast<const uint4*>(src + 16);
-        ch.s[tn] = 1.0f;
+        ch.s[tn] = 0;
       } else {
         ch.w[tn][0] = *reinterpret_cast<const uint4*>(p.wc + n * (K / 2) + kk / 2);
-        ch.s[tn] = fp16_to_f32(ws_h[n * (K / p.g) + kk / p.g]);
+        ch.s[tn] = ws_h[n * (K / p.g) + kk / p.g];
       }
     }
 #pragma unroll
@@ -101,10 +101,11 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
           a[tn][j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
       } else {
-        a[tn][0] = as_bf16x8(dq_int4x8(ch.w[tn][0].x, ch.s[tn]));
-        a[tn][1] = as_bf16x8(dq_int4x8(ch.w[tn][0].y, ch.s[tn]));
-        a[tn][2] = as_bf16x8(dq_int4x8(ch.w[tn][0].z, ch.s[tn]));
-        a[tn][3] = as_bf16x8(dq_int4x8(ch.w[tn][0].w, ch.s[tn]));
+        const I4Scale sc = i4scale(ch.s[tn]);
+        a[tn][0] = as_bf16x8(dq_int4x8(ch.w[tn][0].x, sc));
+        a[tn][1] = as_bf16x8(dq_int4x8(ch.w[tn][0].y, sc));
+        a[tn][2] = as_bf16x8(dq_int4x8(ch.w[tn][0].z, sc));
+        a[tn][3] = as_bf16x8(dq_int4x8(ch.w[tn][0].w, sc));
       }
     }
 #pragma unroll

@@ -5,12 +5,15 @@
 // independent rotation per sub-projection, applied by custom split-projection
 // kernels ("Five design features of the adapter-first architecture").
 //
-// One launch of gemm_nt_kernel (gemm_nt.h) with the rotation epilogue, or of
-// gemm_nt_skinny_kernel (gemm_skinny.h) for decode batches of at most 64
-// tokens: a 32-channel accumulator group is exactly one b = 32 block (or two
-// b = 16 blocks), and blocks never straddle projection segments, so every
-// segment gets its own rotation with no extra pass over HBM.
+// One launch with the rotation epilogue: gemm_nt_dma_kernel (gemm_nt_dma.h)
+// for bf16 activations, gemm_nt_kernel (gemm_nt.h) for fp32 ones (converted
+// to bf16 on the way into LDS), gemm_nt_skinny_kernel (gemm_skinny.h) for
+// decode batches of at most 64 tokens.  A 32-channel accumulator group is
+// exactly one b = 32 block (or two b = 16 blocks), and blocks never straddle
+// projection segments, so every segment gets its own rotation with no extra
+// pass over HBM.
 #include "gemm_nt.h"
+#include "gemm_nt_dma.h"
 #include "gemm_skinny.h"
 #include "oft_launch.h"
 
@@ -23,8 +26,24 @@ namespace {
 #ifndef OFT_FWD_NBUF
 #define OFT_FWD_NBUF 1
 #endif
+#ifndef OFT_FWD_DMA
+#define OFT_FWD_DMA 1
+#endif
 constexpr int FWD_BM = OFT_FWD_BM;
 constexpr int FWD_NBUF = OFT_FWD_NBUF;
+
+// compute units of the current device (queried once per device)
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 template <bool XF32, bool FP8, int B>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
@@ -65,6 +84,22 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
   p.K = a.K;
   p.N = a.N;
   p.g = a.g;
+  if constexpr (!XF32 && OFT_FWD_DMA) {
+    if (a.K % ntd::BK == 0) {
+      // 256-token tiles (less traffic per flop) unless they leave the CUs'
+      // last round of workgroups mostly idle and 128-token tiles do not
+      const int nt = (a.N + ntd::BN - 1) / ntd::BN;
+      const long t256 = (long)nt * ((a.M + 255) / 256), t128 = (long)nt * ((a.M + 127) / 128);
+      const int cus = num_cus();
+      auto fill = [&](long t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
+      const bool big = OFT_FWD_DMA == 2 || (OFT_FWD_DMA != 3 && (fill(t256) >= 0.9 || fill(t256) >= fill(t128)));
+      if (big)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<FP8, B, 256>), dim3(nt, (a.M + 255) / 256), dim3(ntd::NTHR), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<FP8, B, 128>), dim3(nt, (a.M + 127) / 128), dim3(ntd::NTHR), 0, st, p);
+      return hipGetLastError();
+    }
+  }
   dim3 grid((a.N + nt::BN - 1) / nt::BN, (a.M + FWD_BM - 1) / FWD_BM);
   hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, FP8, B, EPI_ROT, false, XF32, FWD_NBUF>), grid, dim3(256), 0,
                      st, p);

@@ -44,14 +44,32 @@ __device__ __forceinline__ float fp16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// 8 INT4 nibbles (low nibble first) times one scale -> 8 bf16 (as uint4).
-// Each product q*s is exact in fp32; the conversion rounds once (RNE).
-__device__ __forceinline__ uint4 dq_int4x8(uint32_t w, float s) {
+// INT4 group scale in the two forms the dequantisation uses: the fp16 value
+// itself and -1032 s in fp32 (exact: 11 x 8 significant bits).
+struct I4Scale {
+  _Float16 s;
+  float m;
+};
+__device__ __forceinline__ I4Scale i4scale(uint16_t bits) {
+  const _Float16 s = __builtin_bit_cast(_Float16, bits);
+  return I4Scale{s, -1032.0f * (float)s};
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 8 INT4 nibbles (low nibble first, two's complement) times one scale -> 8
+// bf16 (as uint4), each bf16(q s) rounded once to nearest even.  Nibble n
+// becomes the fp16 value 1024 + (n ^ 8) (exponent 10, so the nibble lands in
+// the low mantissa bits: one AND/XOR per two nibbles), and one mixed
+// fp16 x fp16 + fp32 FMA gives (1024 + (n ^ 8)) s - 1032 s = q s exactly.
+__device__ __forceinline__ uint4 dq_int4x8(uint32_t w, I4Scale sc) {
+  const float s = (float)sc.s;
   float f[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q = (int)(w << (28 - 4 * e)) >> 28;  // sign-extended nibble e
-    f[e] = (float)q * s;
+  for (int j = 0; j < 4; ++j) {
+    const f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * j)) & 0x000F000Fu) ^ 0x64086408u);
+    f[j] = __builtin_fmaf((float)h[0], s, sc.m);      // nibble j
+    f[j + 4] = __builtin_fmaf((float)h[1], s, sc.m);  // nibble j + 4
   }
   uint4 r;
   r.x = pack_bf16x2(f[0], f[1]);
@@ -68,20 +86,6 @@ __device__ __forceinline__ uint2 dq_fp8x4(uint32_t w) {
   uint2 r;
   r.x = __builtin_bit_cast(uint32_t, lo);
   r.y = __builtin_bit_cast(uint32_t, hi);
-  return r;
-}
-
-// 4 nibbles (low first) of the low 16 bits of w times s -> 4 bf16 (uint2)
-__device__ __forceinline__ uint2 dq_int4x4(uint32_t w, float s) {
-  float f[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int q = (int)(w << (28 - 4 * e)) >> 28;
-    f[e] = (float)q * s;
-  }
-  uint2 r;
-  r.x = pack_bf16x2(f[0], f[1]);
-  r.y = pack_bf16x2(f[2], f[3]);
   return r;
 }
 

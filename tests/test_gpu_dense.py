@@ -27,6 +27,10 @@ SMALL = {
                                 x_dtype="f32", w_fmt="fp8"),
     "int4_g32_f32x_b32": DenseConfig("int4_g32_f32x_b32", M=33, K=256, segs=(64, 32), b=32,
                                      x_dtype="f32", w_fmt="int4", g=32),
+    "fp8_b16_bf16x": DenseConfig("fp8_b16_bf16x", M=200, K=320, segs=(96, 64, 32), b=16,
+                                 x_dtype="bf16", w_fmt="fp8"),
+    "int4_g32_bf16x": DenseConfig("int4_g32_bf16x", M=129, K=192, segs=(288,), b=32,
+                                  x_dtype="bf16", w_fmt="int4", g=32),
     "decode_m1": DenseConfig("decode_m1", M=1, K=256, segs=(128, 128), b=32, x_dtype="bf16",
                              w_fmt="int4", g=128),
     # few tokens, wide layer: weight-streaming forward, split-contraction dX
