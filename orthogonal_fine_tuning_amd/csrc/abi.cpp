@@ -116,7 +116,7 @@ int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_
   if (pass == OFT_PASS_FWD) {
     *bytes = 0;
   } else if (pass == OFT_PASS_BWD) {
-    *bytes = oft::plan_bwd(d->M, d->K, d->N).bytes;
+    *bytes = oft::plan_bwd(d->M, d->K, d->N, d->w_fmt == OFT_W_FP8_E4M3).bytes;
   } else {
     return OFT_EINVAL;
   }
@@ -146,7 +146,7 @@ int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void*
   if (!opt_ok(dx_or_null) || !opt_ok(dq_or_null)) return OFT_EINVAL;
   const bool want_dx = dx_or_null != nullptr && d->M > 0;
   const bool want_dq = dq_or_null != nullptr;
-  const oft::DqPlan plan = oft::plan_bwd(d->M, d->K, d->N);
+  const oft::DqPlan plan = oft::plan_bwd(d->M, d->K, d->N, d->w_fmt == OFT_W_FP8_E4M3);
   if (want_dx) {
     if (!ptr_ok(dy) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(R_ops)) return OFT_EINVAL;
   }

@@ -1,7 +1,11 @@
-// Forward dequant GEMM with asynchronous global -> LDS copies (dense, bf16 x):
-//   C^T[n][m] = sum_k W[n][k] x[m][k],  then the rotation epilogue of gemm_nt.h.
+// Dense dequant GEMM with asynchronous global -> LDS copies (bf16 x):
+//   C^T[n][m] = sum_k W[n][k] x[m][k]
+// with W as FP8 or INT4 codes (the forward, EPI_ROT: the rotation epilogue
+// of gemm_nt.h) or as bf16 (EPI_PLAIN: plain store; the backward's dX runs
+// here with W = the transposed, dequantised weight and x = the rotated
+// upstream gradient).
 //
-// Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 256 or 128), K
+// Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 128, 192, 256), K
 // steps of 64.  Wave (wn, wm) = (wave % 4, wave / 4) owns channels
 // 64 wn + [0, 64) and tokens wm BM / 2 + [0, BM / 2).
 //
@@ -9,8 +13,9 @@
 // 4 bytes per lane; lane l of an instruction writes LDS bytes [s l, s l + s)
 // after the wave-uniform base in M0), through a ring of three LDS stages:
 //   activations : BM rows x 128 bytes (one full cache line per row);
-//   weight codes: 256 rows x 64 bytes (FP8) or x 32 bytes plus one 4-byte
-//                 word per row holding its fp16 group scale(s) (INT4).
+//   weights     : 256 rows x 64 bytes (FP8) or x 32 bytes plus one 4-byte
+//                 word per row holding its fp16 group scale(s) (INT4), or
+//                 x 128 bytes (bf16, laid out like the activations).
 // Each wave copies an eighth of both.  The copies for step s + 2 are issued
 // right after the barrier of step s, so each has two steps of matrix-core
 // work to land; no registers hold data in flight.  The kernel counts its
@@ -34,13 +39,15 @@
 // that the 16-byte operand reads of any 8 consecutive rows hit 8 distinct
 // slots of a 128-byte bank window and those of any 16 rows 16 distinct slots
 // of a 256-byte window: h = (r ^ ((r >> 3) & 1)) & 7 for activation rows (8
-// chunks), ((r >> 1) ^ (r >> 3)) & 3 for FP8 code rows (4 chunks) and
-// ((r >> 2) ^ (r >> 3)) & 1 for INT4 code rows (2 chunks).
+// chunks; bf16 weight rows too), ((r >> 1) ^ (r >> 3)) & 3 for FP8 code
+// rows (4 chunks) and ((r >> 2) ^ (r >> 3)) & 1 for INT4 code rows (2).
 #pragma once
 
 #include "gemm_nt.h"
 
 namespace oft {
+
+enum : int { WF_INT4 = 0, WF_FP8 = 1, WF_BF16 = 2 };
 
 namespace ntd {
 constexpr int BN = 256;  // channels per workgroup
@@ -48,7 +55,7 @@ constexpr int BK = 64;   // in-features per step
 constexpr int NST = 3;   // ring depth
 constexpr int NTHR = 512;
 template <int BM> constexpr int X_BYTES = BM * BK * 2;
-template <bool FP8> constexpr int W_BYTES = FP8 ? BN * BK : BN * BK / 2 + BN * 4;
+template <int WF> constexpr int W_BYTES = WF == WF_BF16 ? BN * BK * 2 : WF == WF_FP8 ? BN * BK : BN * BK / 2 + BN * 4;
 __device__ __forceinline__ int swz_x(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 __device__ __forceinline__ int swz_w8(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz_w4(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
@@ -66,28 +73,37 @@ __device__ __forceinline__ void copy4(uint32_t lds, const void* base, uint32_t v
 // barrier that also retires this wave's LDS reads
 template <int N>
 __device__ __forceinline__ void wait_copies_barrier() {
-  static_assert(N == 0 || N == 4 || N == 6, "copies per step");
+  static_assert(N == 0 || N == 4 || N == 5 || N == 6 || N == 8, "copies per step");
   if constexpr (N == 0)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 5)
+    asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 4)
     asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else
+  else if constexpr (N == 6)
     asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 }  // namespace ntd
 
-template <bool FP8, int B, int BM>
+template <int WF, int B, int BM, int EPI, bool OUTF32>
 __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   using namespace ntd;
-  static_assert(BM == 128 || BM == 256, "tile");
+  static_assert(BM == 128 || BM == 192 || BM == 256, "tile");
+  static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN, "epilogue");
+  constexpr bool FP8 = WF == WF_FP8;
+  constexpr bool W16 = WF == WF_BF16;
   constexpr int TM = BM / 64;  // 32-token tiles per wave
   constexpr int XB = X_BYTES<BM>;
-  constexpr int WB = W_BYTES<FP8>;
-  constexpr int XI = BM / 64;  // activation copies per wave and step (8 rows each)
-  constexpr int V = XI + 2;    // copies per wave and step
+  constexpr int WB = W_BYTES<WF>;
+  constexpr int XI = BM / 64;        // activation copies per wave and step (8 rows each)
+  constexpr int WI = W16 ? 4 : 2;    // weight copies per wave and step
+  constexpr int V = XI + WI;         // copies per wave and step
   __shared__ __attribute__((aligned(16))) uint8_t xs[NST * XB];
   __shared__ __attribute__((aligned(16))) uint8_t wsm[NST * WB];
 
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   const int pos0 = blockIdx.y * BM;
   const int nrows = min(BM, p.M - pos0);
   const int nk = K / BK;
-  const int kg = FP8 ? 1 : K / p.g;  // INT4 scales per row
+  const int kg = WF == WF_INT4 ? K / p.g : 1;  // INT4 scales per row
   const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;  // INT4: log2(64 / g)
 
   // ---- copy sources: per-lane 32-bit offsets from wave-uniform bases
@@ -117,10 +133,16 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 
   // rows past N copy the workgroup's first row (their outputs are never stored)
   auto crow = [&](int rw) { return n0 + rw < p.N ? rw : 0; };
-  const uint8_t* wbase = p.wc + (FP8 ? (size_t)n0 * K : (size_t)n0 * (K / 2));
-  uint32_t woff[2] = {0u, 0u};
+  const uint8_t* wbase = p.wc + (W16 ? (size_t)n0 * K * 2 : FP8 ? (size_t)n0 * K : (size_t)n0 * (K / 2));
+  uint32_t woff[4] = {0u, 0u, 0u, 0u};
   uint32_t sbase = 0;  // INT4: index of the copy row's first scale
-  if constexpr (FP8) {
+  if constexpr (W16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rw = 32 * wave + 8 * i + (lane >> 3);
+      woff[i] = (uint32_t)(crow(rw) * K * 2 + 16 * ((lane & 7) ^ swz_x(rw)));
+    }
+  } else if constexpr (FP8) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int rw = 32 * wave + 16 * i + (lane >> 2);
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
     sbase = (uint32_t)((n0 + crow(32 * wave + l32)) * kg);
   }
-  const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(FP8 ? 32 * wave * 64 : 32 * wave * 32);
+  const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(32 * wave * (W16 ? 128 : FP8 ? 64 : 32));
   const uint32_t s_lds = lds_addr(wsm) + (uint32_t)(BN * BK / 2 + 32 * wave * 4);
   // first scale of step s: (64 s) / g
   auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
@@ -141,7 +163,11 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     const uint8_t* xb = xbase + (size_t)s * BK * 2;
 #pragma unroll
     for (int i = 0; i < XI; ++i) copy16(x_lds + st * XB + i * 1024, xb, xoff[i]);
-    if constexpr (FP8) {
+    if constexpr (W16) {
+      const uint8_t* wb = wbase + (size_t)s * BK * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) copy16(w_lds + st * WB + i * 1024, wb, woff[i]);
+    } else if constexpr (FP8) {
       const uint8_t* wb = wbase + (size_t)s * BK;
       copy16(w_lds + st * WB, wb, woff[0]);
       copy16(w_lds + st * WB + 1024, wb, woff[1]);
@@ -162,7 +188,10 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
     const int rw = 64 * wn + 32 * tn + l32;
-    if constexpr (FP8) {
+    if constexpr (W16) {
+      wrd[tn][0] = (uint32_t)(rw * 128);
+      wrd[tn][1] = 0u;
+    } else if constexpr (FP8) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) wrd[tn][j] = (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
     } else {
@@ -188,7 +217,9 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     I4Scale sc[2];
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
-      if constexpr (FP8) {
+      if constexpr (W16) {
+        // bf16 weight rows are read per MFMA below, like the activations
+      } else if constexpr (FP8) {
         const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[tn][0]);
         const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[tn][1]);
         cw[tn][0] = c0.x; cw[tn][1] = c0.y; cw[tn][2] = c0.z; cw[tn][3] = c0.w;
@@ -208,7 +239,9 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       bf16x8 a[2], b[TM];
 #pragma unroll
       for (int tn = 0; tn < 2; ++tn) {
-        if constexpr (FP8) {
+        if constexpr (W16) {
+          a[tn] = *reinterpret_cast<const bf16x8*>(W + wrd[tn][0] + 16 * ((4 * g2 + kk) ^ xsw));
+        } else if constexpr (FP8) {
           const uint2 lo = dq_fp8x4(cw[tn][2 * kk]), hi = dq_fp8x4(cw[tn][2 * kk + 1]);
           a[tn] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         } else {
@@ -233,14 +266,17 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     compute(s);
   }
 
-  // ------------------------------------------------------------ epilogue (rotation)
+  // ------------------------------------------------------------ epilogue
+  // EPI_ROT: FP8 channel scale, bf16, Y^T_blk = R_j Z^T_blk on the matrix
+  // cores (accumulator registers reused as the B operand), store.
+  // EPI_PLAIN: store the accumulators (bf16 or fp32).
   const float* ws_f = static_cast<const float*>(p.ws);
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
     const int nb = n0 + 64 * wn + 32 * tn;
     if (nb >= p.N) continue;
     float fs[16];
-    if constexpr (FP8) {
+    if constexpr (EPI == EPI_ROT && FP8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
@@ -251,46 +287,57 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       }
     }
     bf16x8 ra[2];
+    if constexpr (EPI == EPI_ROT) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-      if constexpr (B == 32) {
-        const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
-        lo = *reinterpret_cast<const uint2*>(Rj);
-        hi = *reinterpret_cast<const uint2*>(Rj + 8);
-      } else {
-        if ((l32 >> 4) == t) {
-          const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+      for (int t = 0; t < 2; ++t) {
+        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+        if constexpr (B == 32) {
+          const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
           lo = *reinterpret_cast<const uint2*>(Rj);
           hi = *reinterpret_cast<const uint2*>(Rj + 8);
+        } else {
+          if ((l32 >> 4) == t) {
+            const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+            lo = *reinterpret_cast<const uint2*>(Rj);
+            hi = *reinterpret_cast<const uint2*>(Rj + 8);
+          }
         }
+        ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
-      ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      f32x16 z = acc[tn][tm];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] *= fs[r];
-      }
-      bf16x8 zb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
-                                     pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
       f32x16 o;
+      if constexpr (EPI == EPI_ROT) {
+        f32x16 z = acc[tn][tm];
+        if constexpr (FP8) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-      o = mfma32(ra[0], zb[0], o);
-      o = mfma32(ra[1], zb[1], o);
+          for (int r = 0; r < 16; ++r) z[r] *= fs[r];
+        }
+        bf16x8 zb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
+                                       pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+        o = mfma32(ra[0], zb[0], o);
+        o = mfma32(ra[1], zb[1], o);
+      } else {
+        o = acc[tn][tm];
+      }
       const int ml = wm * (BM / 2) + 32 * tm + l32;
       if (ml >= nrows) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
-            make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+        if constexpr (OUTF32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) =
+              make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
+              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+        }
       }
     }
   }

@@ -11,13 +11,21 @@
 // rotation is a prologue of the dX GEMM.  For narrow layers (dX at most two
 // 128-column tiles wide) it runs inside gemm_nn_kernel (PRO_ROT); for wider
 // layers it would be recomputed once per column tile, so it runs once per dY
-// tile inside the dQ pass below (which reads dY anyway) and gemm_nn_kernel
-// consumes the rotated bf16 tile (PRO_NONE).
+// tile inside the dQ pass below (which reads dY anyway) and the dX GEMM
+// consumes the rotated bf16 tile.  The dX GEMM contracts over the weight's
+// rows, against its storage order; for wide layers with many tokens the
+// weight is first rewritten transposed into the workspace (FP8: the codes,
+// whose channel scale is already folded into dZ'; INT4: the dequantised bf16
+// values, since its group scale varies along the contraction), a pass over
+// the weight bytes only, and dX runs on gemm_nt_dma_kernel (gemm_nt_dma.h)
+// with a plain epilogue.  Otherwise gemm_nn_kernel reads the weight rows
+// directly and transposes tiles through LDS.
 // dQ: stage 1 transposes 64 x 64 tiles of dY and Y through LDS and forms the
 // b x b cross products S on the matrix cores, one fp32 partial per M slice;
 // stage 2 reduces the slices in a fixed order and applies the Cayley
 // gradient in fp32 with R_f32.
 #include "gemm_nn.h"
+#include "gemm_nt_dma.h"
 #include "oft_launch.h"
 
 namespace oft {
@@ -297,9 +305,111 @@ hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------- transposed weight
+// FP8 codes [N][K] -> [K][N], 64 x 64 tiles: rows go through LDS as 4-byte
+// words, each thread transposes a 4 x 4 byte block in registers.
+__global__ __launch_bounds__(256) void transpose_fp8_kernel(const uint8_t* __restrict__ in,
+                                                            uint8_t* __restrict__ out, int N, int K) {
+  __shared__ uint32_t t[64][17];
+  const int tid = threadIdx.x;
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  {
+    const int n = tid >> 2, q = tid & 3;
+    const uint4 v = *reinterpret_cast<const uint4*>(in + (size_t)(n0 + n) * K + k0 + 16 * q);
+    t[n][4 * q] = v.x;
+    t[n][4 * q + 1] = v.y;
+    t[n][4 * q + 2] = v.z;
+    t[n][4 * q + 3] = v.w;
+  }
+  __syncthreads();
+  const int bn = tid & 15, bk = tid >> 4;  // 4 x 4 block: n 4bn.., k 4bk..
+  const uint32_t w0 = t[4 * bn][bk], w1 = t[4 * bn + 1][bk], w2 = t[4 * bn + 2][bk], w3 = t[4 * bn + 3][bk];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t o = ((w0 >> (8 * j)) & 0xFFu) | (((w1 >> (8 * j)) & 0xFFu) << 8) |
+                       (((w2 >> (8 * j)) & 0xFFu) << 16) | (((w3 >> (8 * j)) & 0xFFu) << 24);
+    *reinterpret_cast<uint32_t*>(out + (size_t)(k0 + 4 * bk + j) * N + n0 + 4 * bn) = o;
+  }
+}
+
+// INT4 codes [N][K/2] + fp16 scales [N][K/g] -> bf16 [K][N] holding the
+// dequant hook's values bf16(q s); 64 x 64 tiles, natural layout in LDS,
+// each thread then pairs two rows n into 4-byte output words.
+__global__ __launch_bounds__(256) void transpose_dequant_int4_kernel(const uint8_t* __restrict__ codes,
+                                                                     const uint16_t* __restrict__ scales,
+                                                                     uint16_t* __restrict__ out, int N, int K,
+                                                                     int g) {
+  constexpr int LD = 64 + 8;  // bf16 per LDS row
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * LD];
+  const int tid = threadIdx.x;
+  const int k0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  {
+    const int n = tid >> 2, q = tid & 3;  // in-features k0 + 16q .. + 15 (one scale group: g >= 32)
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + (size_t)(n0 + n) * (K / 2) + (k0 + 16 * q) / 2);
+    const I4Scale sc = i4scale(scales[(size_t)(n0 + n) * (K / g) + (k0 + 16 * q) / g]);
+    uint4* dst = reinterpret_cast<uint4*>(&t[n * LD + 16 * q]);
+    dst[0] = dq_int4x8(c.x, sc);
+    dst[1] = dq_int4x8(c.y, sc);
+  }
+  __syncthreads();
+  const int np = tid & 31, kq = tid >> 5;  // rows n 2np, 2np + 1; in-features 8kq .. 8kq + 7
+  const uint4 r0 = *reinterpret_cast<const uint4*>(&t[(2 * np) * LD + 8 * kq]);
+  const uint4 r1 = *reinterpret_cast<const uint4*>(&t[(2 * np + 1) * LD + 8 * kq]);
+  const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w}, b[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const size_t base = (size_t)(k0 + 8 * kq + 2 * j) * N + n0 + 2 * np;
+    *reinterpret_cast<uint32_t*>(out + base) = (a[j] & 0xFFFFu) | (b[j] << 16);
+    *reinterpret_cast<uint32_t*>(out + base + N) = (a[j] >> 16) | (b[j] & 0xFFFF0000u);
+  }
+}
+
+// dX = dZ' . W through the transposed weight (plan.wt)
+template <bool XF32, bool FP8>
+hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz, const uint8_t* wc,
+                        const void* ws, void* dx, char* work, hipStream_t st) {
+  uint8_t* wt = reinterpret_cast<uint8_t*>(work + pl.wt_off);
+  const dim3 tgrid(a.K / 64, a.N / 64);
+  if constexpr (FP8)
+    hipLaunchKernelGGL(transpose_fp8_kernel, tgrid, dim3(256), 0, st, wc, wt, a.N, a.K);
+  else
+    hipLaunchKernelGGL(transpose_dequant_int4_kernel, tgrid, dim3(256), 0, st, wc,
+                       static_cast<const uint16_t*>(ws), reinterpret_cast<uint16_t*>(wt), a.N, a.K, a.g);
+  NtArgs p{};
+  p.a = dz;
+  p.lda = a.N;
+  p.wc = wt;
+  p.ws = nullptr;
+  p.rops = nullptr;
+  p.out = dx;
+  p.ldo = a.K;
+  p.M = a.M;
+  p.K = a.N;  // contraction: the layer's output channels
+  p.N = a.K;  // output columns: the layer's input features
+  p.g = 64;
+  const int ntl = (a.K + ntd::BN - 1) / ntd::BN;
+  if constexpr (FP8) {
+    const int bm = pick_token_tile(ntl, a.M, num_cus(), 256);
+    if (bm == 256)
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 256, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 255) / 256),
+                         dim3(ntd::NTHR), 0, st, p);
+    else if (bm == 192)
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 192, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 191) / 192),
+                         dim3(ntd::NTHR), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 128, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 127) / 128),
+                         dim3(ntd::NTHR), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, 32, 128, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 127) / 128),
+                       dim3(ntd::NTHR), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-DqPlan plan_bwd(int M, int K, int N) {
+DqPlan plan_bwd(int M, int K, int N, bool fp8) {
   DqPlan p;
   p.ng32 = N / 32;
   const int ng64 = (N + 63) / 64;
@@ -341,6 +451,13 @@ DqPlan plan_bwd(int M, int K, int N) {
       end = p.npart_off + (size_t)p.nsplit_n * M * K * 4;
     }
   }
+  // Wide layer, many tokens: transposed weight for gemm_nt_dma_kernel
+  p.wt = M > 0 && p.prerotate && p.nsplit_n == 1 && N % 64 == 0;
+  p.wt_off = 0;
+  if (p.wt) {
+    p.wt_off = (end + 255) / 256 * 256;
+    end = p.wt_off + (size_t)K * N * (fp8 ? 1 : 2);
+  }
   p.bytes = end;
   return p;
 }
@@ -376,6 +493,12 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || dx == nullptr || a.M == 0) return err;
+  if (dz != nullptr && p.wt) {
+    if (a.xf32) return a.fp8 ? launch_dx_wt<true, true>(a, p, dz, wc, ws, dx, work, st)
+                             : launch_dx_wt<true, false>(a, p, dz, wc, ws, dx, work, st);
+    return a.fp8 ? launch_dx_wt<false, true>(a, p, dz, wc, ws, dx, work, st)
+                 : launch_dx_wt<false, false>(a, p, dz, wc, ws, dx, work, st);
+  }
 #define OFT_DX(XF, F8, BB)                                                                              \
   if (a.xf32 == XF && a.fp8 == F8 && a.b == BB)                                                         \
     return dz != nullptr ? launch_dx_t<XF, F8, BB, PRO_NONE>(a, p, dz, wc, ws, Rops, dx, work, st)     \

@@ -32,19 +32,6 @@ namespace {
 constexpr int FWD_BM = OFT_FWD_BM;
 constexpr int FWD_NBUF = OFT_FWD_NBUF;
 
-// compute units of the current device (queried once per device)
-int num_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <bool XF32, bool FP8, int B>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                         const uint16_t* Rops, void* y, hipStream_t st) {
@@ -86,17 +73,18 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
   p.g = a.g;
   if constexpr (!XF32 && OFT_FWD_DMA) {
     if (a.K % ntd::BK == 0) {
-      // 256-token tiles (less traffic per flop) unless they leave the CUs'
-      // last round of workgroups mostly idle and 128-token tiles do not
       const int nt = (a.N + ntd::BN - 1) / ntd::BN;
-      const long t256 = (long)nt * ((a.M + 255) / 256), t128 = (long)nt * ((a.M + 127) / 128);
-      const int cus = num_cus();
-      auto fill = [&](long t) { return (double)t / (double)(((t + cus - 1) / cus) * cus); };
-      const bool big = OFT_FWD_DMA == 2 || (OFT_FWD_DMA != 3 && (fill(t256) >= 0.9 || fill(t256) >= fill(t128)));
-      if (big)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<FP8, B, 256>), dim3(nt, (a.M + 255) / 256), dim3(ntd::NTHR), 0, st, p);
+      const int bm = OFT_FWD_DMA >= 128 ? OFT_FWD_DMA : pick_token_tile(nt, a.M, num_cus(), 256);
+      constexpr int WF = FP8 ? WF_FP8 : WF_INT4;
+      if (bm == 256)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI_ROT, false>), dim3(nt, (a.M + 255) / 256),
+                           dim3(ntd::NTHR), 0, st, p);
+      else if (bm == 192)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 192, EPI_ROT, false>), dim3(nt, (a.M + 191) / 192),
+                           dim3(ntd::NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<FP8, B, 128>), dim3(nt, (a.M + 127) / 128), dim3(ntd::NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI_ROT, false>), dim3(nt, (a.M + 127) / 128),
+                           dim3(ntd::NTHR), 0, st, p);
       return hipGetLastError();
     }
   }
@@ -107,6 +95,18 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
 }
 
 }  // namespace
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                              const uint16_t* Rops, void* y, hipStream_t st) {

@@ -12,6 +12,30 @@ namespace oft {
 // thread-local hipError_t reported by oft_last_hip_error()
 void set_last_hip_error(int e);
 
+// compute units of the current device (queried once per device)
+int num_cus();
+// Token tile of gemm_nt_dma_kernel (one workgroup per CU): the candidate
+// with the least estimated time, rounds of workgroups x tile rows / per-tile
+// efficiency (measured relative to 256-token tiles: 0.95 at 192 and 0.88 at
+// 128 tokens).  max_bm limits the choice (bf16 weights: 128).
+inline int pick_token_tile(long col_tiles, long M, int cus, int max_bm) {
+  const int cand[3] = {256, 192, 128};
+  const double eff[3] = {1.0, 0.95, 0.88};
+  int best = 128;
+  double best_cost = 0.0;
+  for (int i = 0; i < 3; ++i) {
+    if (cand[i] > max_bm) continue;
+    const long tiles = col_tiles * ((M + cand[i] - 1) / cand[i]);
+    const long rounds = (tiles + cus - 1) / cus;
+    const double cost = (double)rounds * cand[i] / eff[i];
+    if (best_cost == 0.0 || cost < best_cost) {
+      best = cand[i];
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st);
 
@@ -40,9 +64,11 @@ struct DqPlan {
   int nsplit_n;        // contraction splits of the dX GEMM (1 = none)
   int nsplit_len;      // weight rows per split
   size_t npart_off;    // workspace offset of the fp32 dX partials
+  bool wt;             // dX runs on a transposed copy of the weight
+  size_t wt_off;       // its workspace offset ([K, N]: FP8 codes or bf16)
   size_t bytes;        // total workspace
 };
-DqPlan plan_bwd(int M, int K, int N);
+DqPlan plan_bwd(int M, int K, int N, bool fp8);
 
 hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t* dy, const void* y,
                              const uint8_t* wc, const void* ws, const float* Rf, const uint16_t* Rops,

@@ -31,6 +31,11 @@ SMALL = {
                                  x_dtype="bf16", w_fmt="fp8"),
     "int4_g32_bf16x": DenseConfig("int4_g32_bf16x", M=129, K=192, segs=(288,), b=32,
                                   x_dtype="bf16", w_fmt="int4", g=32),
+    # wide layers, many tokens: dX through the transposed weight, fp32 dX
+    "fp8_f32x_wide": DenseConfig("fp8_f32x_wide", M=150, K=320, segs=(64, 64), b=32,
+                                 x_dtype="f32", w_fmt="fp8"),
+    "int4_f32x_wide": DenseConfig("int4_f32x_wide", M=140, K=384, segs=(96, 96), b=16,
+                                  x_dtype="f32", w_fmt="int4", g=64),
     "decode_m1": DenseConfig("decode_m1", M=1, K=256, segs=(128, 128), b=32, x_dtype="bf16",
                              w_fmt="int4", g=128),
     # few tokens, wide layer: weight-streaming forward, split-contraction dX
