@@ -85,6 +85,8 @@ __device__ __forceinline__ void wait_copies_barrier() {
   else
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// workgroup barrier after this wave's LDS accesses have completed
+__device__ __forceinline__ void lds_barrier_plain() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

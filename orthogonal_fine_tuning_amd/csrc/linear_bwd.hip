@@ -192,6 +192,226 @@ __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------- dq stage 1, bf16 Y
+// The same partial cross products (and rotated copy dz) for bf16 Y, shaped
+// for bandwidth: the 64-token x 64-channel tiles of dY and Y travel by
+// asynchronous global -> LDS copies (gemm_nt_dma.h) through three LDS
+// stages, two steps ahead, in their natural layout; the cross products read
+// both operands along the tokens with the LDS transpose load, the rotation
+// reads dY rows directly.  The rotated tile is staged in LDS (two buffers)
+// and stored one step later as whole 128-byte rows.  Tile row m keeps
+// 16-byte chunk c at c ^ f(m),
+// f(m) = rot((m >> 1) & 7) (3-bit rotate right): 16 consecutive rows read
+// at one chunk fill 16 distinct 16-byte bank slots, and the 4 rows of a
+// transpose load use 4 disjoint 32-byte slots.
+__device__ __forceinline__ int dqsw(int m) {
+  const int x = (m >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+
+template <bool FP8, int B>
+__global__ __launch_bounds__(256, 2) void dq_dma_kernel(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y,
+                                                        float* __restrict__ part, int M, int N, int rows_per_split,
+                                                        int ng32, const uint16_t* __restrict__ Rops,
+                                                        const float* __restrict__ fp8_scale,
+                                                        uint16_t* __restrict__ dz) {
+  using namespace ntd;
+  constexpr int ST = 64 * 128;  // bytes per tile
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[3][2][ST];  // [stage][dY, Y][m][n]
+  __shared__ __attribute__((aligned(16))) uint8_t zt[2][ST];        // rotated tiles, [m][n]
+  __shared__ float red[2][64][17];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int n0 = blockIdx.x * 64;
+  const int split = blockIdx.y;
+  const int m_lo = split * rows_per_split;
+  const int m_hi = min(M, m_lo + rows_per_split);
+  const int nsteps = (m_hi - m_lo + 63) / 64;
+  const bool want_dq = part != nullptr;
+
+  // copies: wave w moves tile rows 16w .. 16w + 15 of dY and of Y (two
+  // instructions each, 8 rows x 128 bytes); rows past m_hi copy the tile's
+  // first row and columns past N column chunk 0 (neither is used)
+  uint32_t off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wave + 8 * i + (lane >> 3);
+    const int lc = (lane & 7) ^ dqsw(r);
+    const int col = n0 + 8 * lc < N ? n0 + 8 * lc : 0;
+    off[i] = (uint32_t)((r * N + col) * 2);
+  }
+  const uint32_t t_lds = lds_addr(&tiles[0][0][0]) + (uint32_t)(16 * wave * 128);
+  auto issue = [&](int s) {
+    const int st = s % 3;
+    const int m = m_lo + 64 * s;
+    const int rows_ok = min(64, m_hi - m);
+    uint32_t o[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * wave + 8 * i + (lane >> 3);
+      o[i] = r < rows_ok ? off[i] : off[i] - (uint32_t)(r * N * 2);  // same column, tile row 0
+    }
+    const uint16_t* dyb = dy + (size_t)m * N;
+    const uint16_t* yb = y + (size_t)m * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      copy16(t_lds + st * 2 * ST + i * 1024, dyb, o[i]);
+      copy16(t_lds + st * 2 * ST + ST + i * 1024, yb, o[i]);
+    }
+  };
+
+  // rotation of wave (rg, rh): channels n0 + 32 rg, tokens 32 rh of each step
+  const int rg = wave & 1, rh = wave >> 1;
+  const int nbr = n0 + 32 * rg;
+  const bool rot = dz != nullptr && nbr < N;
+  bf16x8 rtf[2];
+  float sc[16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    uint4 v = zero4();
+    if (rot) {
+      if constexpr (B == 32) {
+        v = *reinterpret_cast<const uint4*>(Rops + (size_t)(nbr / 32) * 2048 + 1024 + l32 * 32 + 16 * t + 8 * g2);
+      } else {
+        if ((l32 >> 4) == t)
+          v = *reinterpret_cast<const uint4*>(Rops + (size_t)(nbr / 16 + t) * 512 + 256 + (l32 & 15) * 16 + 8 * g2);
+      }
+    }
+    rtf[t] = as_bf16x8(v);
+  }
+  if constexpr (FP8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rot) v = *reinterpret_cast<const float4*>(fp8_scale + nbr + 8 * q + 4 * g2);
+      sc[4 * q] = v.x;
+      sc[4 * q + 1] = v.y;
+      sc[4 * q + 2] = v.z;
+      sc[4 * q + 3] = v.w;
+    }
+  }
+
+  // the rotation operands are in registers before any copy is in flight (a
+  // wait the compiler knows about, so it adds none for them in the loop)
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+
+  // cross products of wave (grp, kh): channels n0 + 32 grp, token blocks
+  // kk = 2 kh, 2 kh + 1 (16 tokens each) of every step
+  const int grp = wave & 1, kh = wave >> 1;
+  const bool gok = n0 + 32 * grp < N;
+  const int G = lane >> 4, li = lane & 15;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+  // rows 16 wave .. 16 wave + 15 of the staged rotated tile of step s -> dz
+  auto store_z = [&](int s) {
+    const int m = m_lo + 64 * s;
+    const int rows_ok = min(64, m_hi - m);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * wave + 8 * i + (lane >> 3);
+      const int c = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(&zt[s & 1][r * 128 + 16 * (c ^ dqsw(r))]);
+      if (r < rows_ok && n0 + 8 * c < N) *reinterpret_cast<uint4*>(dz + (size_t)(m + r) * N + n0 + 8 * c) = v;
+    }
+  };
+
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int s = 0; s < nsteps; ++s) {
+    if (s + 1 < nsteps) wait_copies_barrier<4>(); else wait_copies_barrier<0>();
+    const int st = s % 3;
+    const uint8_t* T = &tiles[st][0][0];
+    const int rows_ok = min(64, m_hi - (m_lo + 64 * s));  // valid tokens of this step
+    if (dz != nullptr && s > 0) store_z(s - 1);
+    if (rot) {
+      // dZ^T = R^T dY^T: B operand = dY row (token 32 rh + l32), channels
+      // nbr + 16 t + 8 g2 .. + 7; the result (channels 32 rg + 8 q + 4 g2
+      // .. + 3 of that token) goes to the staging tile
+      const int r = 32 * rh + l32;
+      f32x16 o;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) o[q] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int lc = (32 * rg + 16 * t + 8 * g2) / 8;
+        const bf16x8 f = *reinterpret_cast<const bf16x8*>(T + r * 128 + 16 * (lc ^ dqsw(r)));
+        o = mfma32(rtf[t], f, o);
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) o[q] *= sc[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint2*>(&zt[s & 1][r * 128 + 16 * ((4 * rg + q) ^ dqsw(r)) + 8 * g2]) =
+            make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+    }
+    // the dz stores above precede these copies: at the next barrier the 4
+    // copies of step s + 2, if any, are the youngest of this wave's loads
+    // and stores, and everything older (the copies of step s + 1) must land
+    if (s + 2 < nsteps) issue(s + 2);
+    if (want_dq && gok) {
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int kk = 2 * kh + kq;
+        // lane (li, G): tile rows 16 kk + 8 (G >> 1) + li / 4 (+ 4), channel
+        // 32 grp + 16 (G & 1) + 4 (li & 3): it receives channel + li's four
+        // tokens, i.e. operand row l32, items 8 g2 .. 8 g2 + 7
+        const int col = 32 * grp + 16 * (G & 1) + 4 * (li & 3);
+        const int r0 = 16 * kk + 8 * (G >> 1) + (li >> 2);
+        uint2 d[2], yv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = r0 + 4 * h;
+          const int boff = r * 128 + 16 * ((col / 8) ^ dqsw(r)) + 2 * (col % 8);
+          d[h] = nn::ds_read_tr16(reinterpret_cast<const uint16_t*>(T + boff));
+          yv[h] = nn::ds_read_tr16(reinterpret_cast<const uint16_t*>(T + ST + boff));
+        }
+        uint4 a = make_uint4(d[0].x, d[0].y, d[1].x, d[1].y);
+        const uint4 b = make_uint4(yv[0].x, yv[0].y, yv[1].x, yv[1].y);
+        if (16 * kk + 16 > rows_ok) {
+          // ragged last step: this lane's tokens 16 kk + 8 g2 + p past the slice end contribute 0
+          const int base = 16 * kk + 8 * g2;
+          uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+          for (int pp = 0; pp < 8; ++pp)
+            if (base + pp >= rows_ok) w[pp >> 1] &= (pp & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          a = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        acc = mfma32(as_bf16x8(a), as_bf16x8(b), acc);
+      }
+    }
+  }
+  if (dz != nullptr) {
+    lds_barrier_plain();
+    store_z(nsteps - 1);
+  }
+  if (!want_dq) return;
+
+  // fixed-order reduction of the two token halves, then one partial per slice
+  if (kh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[grp][lane][r] = acc[r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const int g32 = n0 / 32 + grp;
+    if (g32 < ng32) {
+      float* dst = part + ((size_t)split * ng32 + g32) * 1024;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r / 4) * 8 + 4 * g2 + (r % 4);
+        dst[row * 32 + l32] = acc[r] + red[grp][lane][r];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dq stage 2
 // Per block: S = sum of the slice partials (fixed order); with
 // R (R^T + I) = I + R the Cayley gradient is
@@ -414,15 +634,26 @@ DqPlan plan_bwd(int M, int K, int N, bool fp8) {
   p.ng32 = N / 32;
   const int ng64 = (N + 63) / 64;
   const int msteps = (M + 63) / 64;
-  int want = ng64 > 0 ? (1024 + ng64 - 1) / ng64 : 1;
-  if (want < 1) want = 1;
-  if (want > 16) want = 16;
-  if (want > msteps) want = msteps;
+  // M slices of the dq pass: fewest (rounds of workgroups x 64-token steps
+  // per workgroup), two workgroups per CU, at most 16 slices
+  const long slots = 2L * num_cus();
+  int best = 1;
+  long best_cost = -1;
+  for (int ns = 1; ns <= 16 && ns <= msteps; ++ns) {
+    const long steps_per = (msteps + ns - 1) / ns;
+    const long used = (msteps + steps_per - 1) / steps_per;  // slices actually needed
+    const long rounds = ((long)ng64 * used + slots - 1) / slots;
+    const long cost = rounds * steps_per;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = ns;
+    }
+  }
   if (msteps == 0) {
     p.nsplit = 0;
     p.rows_per_split = 64;
   } else {
-    const int steps_per = (msteps + want - 1) / want;
+    const int steps_per = (msteps + best - 1) / best;
     p.rows_per_split = steps_per * 64;
     p.nsplit = (msteps + steps_per - 1) / steps_per;
   }
@@ -470,18 +701,24 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
   if ((dq != nullptr || dz != nullptr) && p.nsplit > 0) {
     dim3 grid((a.N + 63) / 64, p.nsplit);
     const float* s8 = a.fp8 ? static_cast<const float*>(ws) : nullptr;
-#define OFT_DQP(YF, F8, BB)                                                                               \
-  if (a.xf32 == YF && a.fp8 == F8 && a.b == BB)                                                           \
-    hipLaunchKernelGGL((dq_partial_kernel<YF, F8, BB>), grid, dim3(256), 0, st, dy, y, part, a.M, a.N,    \
+    float* dq_part = dq != nullptr ? part : nullptr;
+#define OFT_DQD(F8, BB)                                                                                   \
+  if (!a.xf32 && a.fp8 == F8 && a.b == BB)                                                                \
+    hipLaunchKernelGGL((dq_dma_kernel<F8, BB>), grid, dim3(256), 0, st, dy, static_cast<const uint16_t*>(y), \
+                       dq_part, a.M, a.N, p.rows_per_split, p.ng32, Rops, s8, dz);
+    OFT_DQD(false, 32)
+    OFT_DQD(false, 16)
+    OFT_DQD(true, 32)
+    OFT_DQD(true, 16)
+#undef OFT_DQD
+#define OFT_DQP(F8, BB)                                                                                   \
+  if (a.xf32 && a.fp8 == F8 && a.b == BB)                                                                 \
+    hipLaunchKernelGGL((dq_partial_kernel<true, F8, BB>), grid, dim3(256), 0, st, dy, y, part, a.M, a.N,  \
                        p.rows_per_split, p.ng32, Rops, s8, dz);
-    OFT_DQP(false, false, 32)
-    OFT_DQP(false, false, 16)
-    OFT_DQP(false, true, 32)
-    OFT_DQP(false, true, 16)
-    OFT_DQP(true, false, 32)
-    OFT_DQP(true, false, 16)
-    OFT_DQP(true, true, 32)
-    OFT_DQP(true, true, 16)
+    OFT_DQP(false, 32)
+    OFT_DQP(false, 16)
+    OFT_DQP(true, 32)
+    OFT_DQP(true, 16)
 #undef OFT_DQP
   }
   if (dq != nullptr) {

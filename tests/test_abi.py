@@ -90,6 +90,24 @@ def test_linear_workspace_query():
         oft.oft_linear_workspace_bytes(d, 5)
 
 
+@pytest.mark.parametrize("w_fmt,g", [(oft.OFT_W_FP8_E4M3, 0), (oft.OFT_W_INT4, 64)])
+@pytest.mark.parametrize("M", [0, 1, 63, 64, 128, 129, 300, 4096])
+@pytest.mark.parametrize("K,segs", [(128, (96, 32)), (256, (64,)), (320, (64, 64)), (2560, (4096, 1024, 1024)),
+                                    (576, (320, 320)), (512, (256, 64, 96))])
+def test_linear_bwd_workspace_covers_its_parts(w_fmt, g, M, K, segs):
+    """Host-only backward planning over edge shapes (M = 0 included): the
+    query succeeds and covers the dq partials, the rotated copy of dY for
+    wide layers and, for wide layers with many tokens, the transposed weight."""
+    N = sum(segs)
+    d = oft.linear_desc(M, K, segs, 32, oft.OFT_DT_BF16, w_fmt, g)
+    nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
+    assert nb >= (N // 32) * 1024 * 4  # at least one slice of dq partials
+    if K > 256 and M > 0:
+        assert nb >= M * N * 2  # rotated dY
+    if K > 256 and M > 128 and N % 64 == 0:
+        assert nb >= M * N * 2 + K * N * (1 if w_fmt == oft.OFT_W_FP8_E4M3 else 2)
+
+
 def test_cayley_and_dequant_validation():
     lib = _lib.load()
     ok = C.c_void_p(0x1000)
