@@ -81,10 +81,10 @@ FWD_KERNEL_SOURCES = ["orthogonal_fine_tuning_amd/csrc/linear_fwd.hip",
 
 def fwd_kernel_name(cfg):
     """The kernel oft_linear_fwd launches for this shape (one launch per call)."""
+    if cfg.x_dtype == "bf16":
+        return "gemm_nt_dec_kernel" if cfg.M <= 64 else "gemm_nt_dma_kernel"
     if cfg.M <= 64 and cfg.K % 256 == 0:
         return "gemm_nt_skinny_kernel"
-    if cfg.x_dtype == "bf16":
-        return "gemm_nt_dma_kernel"
     return "gemm_nt_kernel"
 
 

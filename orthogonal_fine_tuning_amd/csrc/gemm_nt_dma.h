@@ -85,6 +85,16 @@ __device__ __forceinline__ void wait_copies_barrier() {
   else
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// runtime count (one of 0, 4, 8, 12, 16)
+__device__ __forceinline__ void wait_copies_barrier_n(int n) {
+  switch (n) {
+    case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
 // workgroup barrier after this wave's LDS accesses have completed
 __device__ __forceinline__ void lds_barrier_plain() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -341,6 +351,236 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
               make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
         }
       }
+    }
+  }
+}
+
+
+// Few tokens (M <= 64): the layer is a weight stream.  Workgroup: 8 waves,
+// 128 channels x 64 tokens; wave (wn, kh) = (wave % 4, wave / 4) owns
+// channels 32 wn + [0, 32), all 64 tokens, and the in-features of every
+// other 64-wide step: a ring stage holds a 128-wide step, kh picks its half,
+// so two waves share each SIMD and the two halves' partial sums are added
+// in LDS at the end (fixed order).  Same copies, layouts, contraction order
+// and epilogue as above; four stages, copies issued three 128-wide steps
+// ahead (about 75 KB in flight per workgroup).
+namespace ntd {
+constexpr int DEC_BN = 128, DEC_NST = 4, DEC_NTHR = 512;
+template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK / 2 + DEC_BN * 4;
+}  // namespace ntd
+
+template <bool FP8, int B>
+__global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p) {
+  using namespace ntd;
+  constexpr int BMD = 64, TM = 2, NST = DEC_NST;
+  constexpr int XH = BMD * BK * 2;      // 8 KB: one 64-wide half of a step
+  constexpr int WH = DEC_W_HALF<FP8>;   // weight bytes of one half
+  constexpr int SB = 2 * XH + 2 * WH;   // stage bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, kh = wave >> 2;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int K = p.K;
+  const int n0 = blockIdx.x * DEC_BN;
+  const int pos0 = blockIdx.y * BMD;
+  const int nrows = min(BMD, p.M - pos0);
+  const int nk = K / BK;          // 64-wide steps
+  const int nk2 = (nk + 1) / 2;   // 128-wide steps
+  const int kg = FP8 ? 1 : K / p.g;
+  const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;
+
+  // copies of wave (wn, kh), for half kh of each step (a missing last half
+  // re-copies the first half: same count, never read):
+  //   activations rows 16 wn .. 16 wn + 15 (two instructions),
+  //   weight rows 32 wn .. 32 wn + 31 (FP8: two instructions; INT4: one,
+  //   plus the rows' scale words on lanes 0..31)
+  const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
+  uint32_t xoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wn + 8 * i + (lane >> 3);
+    const int rr = r < nrows ? r : 0;
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + 16 * ((lane & 7) ^ swz_x(r)));
+  }
+  auto crow = [&](int rw) { return n0 + rw < p.N ? rw : 0; };
+  const uint8_t* wbase = p.wc + (FP8 ? (size_t)n0 * K : (size_t)n0 * (K / 2));
+  uint32_t woff[2] = {0u, 0u};
+  uint32_t sbase = 0;
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rw = 32 * wn + 16 * i + (lane >> 2);
+      woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 3) ^ swz_w8(rw)));
+    }
+  } else {
+    const int rw = 32 * wn + (lane >> 1);
+    woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
+    sbase = (uint32_t)((n0 + crow(32 * wn + l32)) * kg);
+  }
+  const uint32_t base_lds = lds_addr(smem);
+  const uint32_t x_lds = base_lds + (uint32_t)(kh * XH + 16 * wn * 128);
+  const uint32_t w_lds = base_lds + (uint32_t)(2 * XH + kh * WH + 32 * wn * (FP8 ? 64 : 32));
+  const uint32_t s_lds = base_lds + (uint32_t)(2 * XH + kh * WH + DEC_BN * BK / 2 + 32 * wn * 4);
+  auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
+
+  auto issue = [&](int s2) {  // 128-wide step s2, this wave's half
+    const int st = s2 % NST;
+    int s = 2 * s2 + kh;
+    if (s >= nk) s = 2 * s2;
+    const uint8_t* xb = xbase + (size_t)s * BK * 2;
+    copy16(x_lds + st * SB, xb, xoff[0]);
+    copy16(x_lds + st * SB + 1024, xb, xoff[1]);
+    if constexpr (FP8) {
+      const uint8_t* wb = wbase + (size_t)s * BK;
+      copy16(w_lds + st * SB, wb, woff[0]);
+      copy16(w_lds + st * SB + 1024, wb, woff[1]);
+    } else {
+      copy16(w_lds + st * SB, wbase + (size_t)s * (BK / 2), woff[0]);
+      if (lane < 32) copy4(s_lds + st * SB, p.ws, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
+    }
+  };
+
+  const int rw = 32 * wn + l32;  // this lane's operand row
+  const int xsw = swz_x(l32);
+  uint32_t wrd[2];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wrd[j] = (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
+  } else {
+    wrd[0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
+    wrd[1] = 0u;
+  }
+  const uint32_t srd = FP8 ? 0u : (uint32_t)((n0 + crow(rw)) * kg);
+
+  f32x16 acc[TM];
+#pragma unroll
+  for (int b = 0; b < TM; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+
+  auto compute = [&](int s2) {
+    const int s = 2 * s2 + kh;
+    if (s >= nk) return;
+    const int st = s2 % NST;
+    const uint8_t* X = smem + st * SB + kh * XH;
+    const uint8_t* W = smem + st * SB + 2 * XH + kh * WH;
+    uint32_t cw[8];
+    I4Scale sc;
+    if constexpr (FP8) {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[1]);
+      cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
+      cw[4] = c1.x; cw[5] = c1.y; cw[6] = c1.z; cw[7] = c1.w;
+    } else {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
+      cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(W + DEC_BN * BK / 2 + rw * 4);
+      const uint32_t idx = srd + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
+      sc = i4scale((uint16_t)(word >> (16 * (idx & 1))));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a;
+      if constexpr (FP8) {
+        const uint2 lo = dq_fp8x4(cw[2 * kk]), hi = dq_fp8x4(cw[2 * kk + 1]);
+        a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      } else {
+        a = as_bf16x8(dq_int4x8(cw[kk], sc));
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(X + (32 * tm + l32) * 128 + 16 * ((4 * g2 + kk) ^ xsw));
+        acc[tm] = mfma32(a, b, acc[tm]);
+      }
+    }
+  };
+
+  const int pre = nk2 < NST - 1 ? nk2 : NST - 1;
+  for (int s2 = 0; s2 < pre; ++s2) issue(s2);
+  for (int s2 = 0; s2 < nk2; ++s2) {
+    // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight (4 per step)
+    const int ahead = min(NST - 2, nk2 - 1 - s2);
+    wait_copies_barrier_n(4 * ahead);
+    if (s2 + NST - 1 < nk2) issue(s2 + NST - 1);
+    compute(s2);
+  }
+
+  // the two halves' partial sums: kh = 1 hands over through LDS (the ring
+  // is free once every wave has passed the barrier below)
+  lds_barrier_plain();
+  float* red = reinterpret_cast<float*>(smem);
+  if (kh == 1) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((wn * TM + tm) * 16 + r) * 64 + lane] = acc[tm][r];
+  }
+  lds_barrier_plain();
+  if (kh == 1) return;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tm][r] += red[((wn * TM + tm) * 16 + r) * 64 + lane];
+
+  // epilogue: FP8 channel scale, bf16, rotation, store
+  const int nb = n0 + 32 * wn;
+  if (nb >= p.N) return;
+  const float* ws_f = static_cast<const float*>(p.ws);
+  float fs[16];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
+      fs[4 * q] = v.x;
+      fs[4 * q + 1] = v.y;
+      fs[4 * q + 2] = v.z;
+      fs[4 * q + 3] = v.w;
+    }
+  }
+  bf16x8 ra[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+    if constexpr (B == 32) {
+      const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
+      lo = *reinterpret_cast<const uint2*>(Rj);
+      hi = *reinterpret_cast<const uint2*>(Rj + 8);
+    } else {
+      if ((l32 >> 4) == t) {
+        const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+        lo = *reinterpret_cast<const uint2*>(Rj);
+        hi = *reinterpret_cast<const uint2*>(Rj + 8);
+      }
+    }
+    ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    f32x16 z = acc[tm];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] *= fs[r];
+    }
+    bf16x8 zb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
+                                   pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
+    f32x16 o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+    o = mfma32(ra[0], zb[0], o);
+    o = mfma32(ra[1], zb[1], o);
+    const int ml = 32 * tm + l32;
+    if (ml >= nrows) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
+          make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
     }
   }
 }

@@ -35,7 +35,26 @@ constexpr int FWD_NBUF = OFT_FWD_NBUF;
 template <bool XF32, bool FP8, int B>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                         const uint16_t* Rops, void* y, hipStream_t st) {
-  if (a.M <= 64 && a.K % 256 == 0) {  // few tokens: weight-streaming kernel
+  if constexpr (!XF32) {
+    if (a.M <= 64) {  // few tokens: weight stream through the deep copy ring
+      NtArgs p{};
+      p.a = x;
+      p.lda = a.K;
+      p.wc = wc;
+      p.ws = ws;
+      p.rops = Rops;
+      p.out = y;
+      p.ldo = a.N;
+      p.M = a.M;
+      p.K = a.K;
+      p.N = a.N;
+      p.g = a.g;
+      hipLaunchKernelGGL((gemm_nt_dec_kernel<FP8, B>), dim3((a.N + ntd::DEC_BN - 1) / ntd::DEC_BN, 1),
+                         dim3(ntd::DEC_NTHR), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if (a.M <= 64 && a.K % 256 == 0) {  // few tokens, fp32 activations: weight-streaming kernel
     NtArgs p{};
     p.a = x;
     p.lda = a.K;
