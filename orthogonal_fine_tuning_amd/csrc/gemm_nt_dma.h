@@ -5,6 +5,15 @@
 // here with W = the transposed, dequantised weight and x = the rotated
 // upstream gradient).
 //
+// Grouped (MoE experts): tile y is entry y of a device work list (expert e,
+// row0) as in gemm_nt.h; its rows are expert-sorted positions, activation
+// rows are gathered (row perm[pos] / kslots) by per-lane 64-bit copy
+// addresses, and the weight, scale and rotation pointers advance by expert.
+// EPI_ROT_SWIGLU: the 256-channel tile is 128 gate channels [c, c + 128) and
+// the matching 128 up channels [I + c, I + c + 128); both are rotated and
+// stored, then act = silu(gate) * up, the up waves handing their bf16
+// outputs to the gate waves through LDS.
+//
 // Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 128, 192, 256), K
 // steps of 64.  Wave (wn, wm) = (wave % 4, wave / 4) owns channels
 // 64 wn + [0, 64) and tokens wm BM / 2 + [0, BM / 2).
@@ -65,6 +74,9 @@ __device__ __forceinline__ void copy16(uint32_t lds, const void* base, uint32_t 
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
                : "memory", "m0");
 }
+__device__ __forceinline__ void copy16v(uint32_t lds, const void* addr) {  // per-lane 64-bit address
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr) : "memory", "m0");
+}
 __device__ __forceinline__ void copy4(uint32_t lds, const void* base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
                : "memory", "m0");
@@ -102,14 +114,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 }  // namespace ntd
 
-template <int WF, int B, int BM, int EPI, bool OUTF32>
+template <int WF, int B, int BM, int EPI, bool OUTF32, bool GROUPED = false>
 __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   using namespace ntd;
   static_assert(BM == 128 || BM == 192 || BM == 256, "tile");
   static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN, "epilogue");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  static_assert(EPI != EPI_ROT_SWIGLU || BM == 128, "exchange buffer sized for 128-token tiles");
   constexpr bool FP8 = WF == WF_FP8;
   constexpr bool W16 = WF == WF_BF16;
+  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   constexpr int TM = BM / 64;  // 32-token tiles per wave
   constexpr int XB = X_BYTES<BM>;
   constexpr int WB = W_BYTES<WF>;
@@ -125,27 +139,58 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   const int wn = wave & 3, wm = wave >> 2;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
-  const int n0 = blockIdx.x * BN;
-  const int pos0 = blockIdx.y * BM;
-  const int nrows = min(BM, p.M - pos0);
+
+  // ---- tile: rows (tokens / expert positions) and weight rows (channels)
+  int e = 0, pos0, nrows;
+  if constexpr (GROUPED) {
+    const int t = blockIdx.y;
+    if (t >= *p.ntiles) return;
+    e = p.tiles[2 * t];
+    pos0 = p.offsets[e] + p.tiles[2 * t + 1];
+    nrows = min(BM, p.offsets[e + 1] - pos0);
+  } else {
+    pos0 = blockIdx.y * BM;
+    nrows = min(BM, p.M - pos0);
+  }
+  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
+  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
+  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  // channel of local weight row rw (0..255), or -1 past the layer's channels
+  const int cbase = SWI ? blockIdx.x * (BN / 2) : blockIdx.x * BN;
+  auto chan = [&](int rw) -> int {
+    if constexpr (SWI) {
+      const int c = cbase + (rw & (BN / 2 - 1));
+      return c < p.half_n ? (rw < BN / 2 ? c : p.half_n + c) : -1;
+    } else {
+      return cbase + rw < p.N ? cbase + rw : -1;
+    }
+  };
+  // copy source row: invalid rows copy the workgroup's first row (never stored)
+  auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
   const int nk = K / BK;
   const int kg = WF == WF_INT4 ? K / p.g : 1;  // INT4 scales per row
   const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;  // INT4: log2(64 / g)
 
-  // ---- copy sources: per-lane 32-bit offsets from wave-uniform bases
+  // ---- copy sources: activations (dense: per-lane 32-bit offsets from the
+  // tile's first row; grouped: per-lane 64-bit addresses of gathered rows)
   const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
   uint32_t xoff[XI];
+  const uint8_t* xptr[GROUPED ? XI : 1];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int r = (BM / 8) * wave + 8 * i + (lane >> 3);
     const int rr = r < nrows ? r : 0;  // rows past the end copy row 0; never stored
-    xoff[i] = (uint32_t)(rr * p.lda * 2 + 16 * ((lane & 7) ^ swz_x(r)));
+    const int chunk = 16 * ((lane & 7) ^ swz_x(r));
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + chunk);
+    if constexpr (GROUPED) {
+      const long src = p.kslots > 0 ? (long)(p.perm[pos0 + rr] / p.kslots) : (long)(pos0 + rr);
+      xptr[i] = static_cast<const uint8_t*>(p.a) + src * p.lda * 2 + chunk;
+    }
   }
   const uint32_t x_lds = lds_addr(xs) + (uint32_t)((BM / 8) * wave * 128);
 
-  // rows past N copy the workgroup's first row (their outputs are never stored)
-  auto crow = [&](int rw) { return n0 + rw < p.N ? rw : 0; };
-  const uint8_t* wbase = p.wc + (W16 ? (size_t)n0 * K * 2 : FP8 ? (size_t)n0 * K : (size_t)n0 * (K / 2));
+  // weights: per-lane 32-bit offsets from the row of channel cbase
+  const uint8_t* wbase = wc + (W16 ? (size_t)cbase * K * 2 : FP8 ? (size_t)cbase * K : (size_t)cbase * (K / 2));
   uint32_t woff[4] = {0u, 0u, 0u, 0u};
   uint32_t sbase = 0;  // INT4: index of the copy row's first scale
   if constexpr (W16) {
@@ -163,7 +208,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   } else {
     const int rw = 32 * wave + (lane >> 1);
     woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
-    sbase = (uint32_t)((n0 + crow(32 * wave + l32)) * kg);
+    sbase = (uint32_t)((cbase + crow(32 * wave + l32)) * kg);
   }
   const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(32 * wave * (W16 ? 128 : FP8 ? 64 : 32));
   const uint32_t s_lds = lds_addr(wsm) + (uint32_t)(BN * BK / 2 + 32 * wave * 4);
@@ -174,7 +219,12 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     const int st = s % NST;
     const uint8_t* xb = xbase + (size_t)s * BK * 2;
 #pragma unroll
-    for (int i = 0; i < XI; ++i) copy16(x_lds + st * XB + i * 1024, xb, xoff[i]);
+    for (int i = 0; i < XI; ++i) {
+      if constexpr (GROUPED)
+        copy16v(x_lds + st * XB + i * 1024, xptr[i] + (size_t)s * BK * 2);
+      else
+        copy16(x_lds + st * XB + i * 1024, xb, xoff[i]);
+    }
     if constexpr (W16) {
       const uint8_t* wb = wbase + (size_t)s * BK * 2;
 #pragma unroll
@@ -186,7 +236,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     } else {
       copy16(w_lds + st * WB, wbase + (size_t)s * (BK / 2), woff[0]);
       // lanes 0..31: the 4-byte word holding the step's scale(s) of row 32 wave + lane
-      if (lane < 32) copy4(s_lds + st * WB, p.ws, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
+      if (lane < 32) copy4(s_lds + st * WB, ws_h, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
     }
   };
 
@@ -209,7 +259,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     } else {
       wrd[tn][0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
       wrd[tn][1] = 0u;
-      srd[tn] = (uint32_t)((n0 + crow(rw)) * kg);
+      srd[tn] = (uint32_t)((cbase + crow(rw)) * kg);
     }
   }
 
@@ -279,19 +329,21 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   }
 
   // ------------------------------------------------------------ epilogue
-  // EPI_ROT: FP8 channel scale, bf16, Y^T_blk = R_j Z^T_blk on the matrix
-  // cores (accumulator registers reused as the B operand), store.
-  // EPI_PLAIN: store the accumulators (bf16 or fp32).
+  // EPI_ROT / EPI_ROT_SWIGLU: FP8 channel scale, bf16, Y^T_blk = R_j Z^T_blk
+  // on the matrix cores (accumulator registers reused as the B operand),
+  // store.  EPI_PLAIN: store the accumulators (bf16 or fp32).
   const float* ws_f = static_cast<const float*>(p.ws);
+  uint32_t swg[SWI ? 2 : 1][SWI ? TM : 1][8];  // EPI_ROT_SWIGLU: this lane's bf16 outputs
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
-    const int nb = n0 + 64 * wn + 32 * tn;
-    if (nb >= p.N) continue;
+    const int nb = chan(64 * wn + 32 * tn);  // first channel of this 32-channel group
+    const bool n_ok = nb >= 0;
     float fs[16];
-    if constexpr (EPI == EPI_ROT && FP8) {
+    if constexpr (EPI != EPI_PLAIN && FP8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (n_ok) v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
         fs[4 * q] = v.x;
         fs[4 * q + 1] = v.y;
         fs[4 * q + 2] = v.z;
@@ -299,19 +351,21 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       }
     }
     bf16x8 ra[2];
-    if constexpr (EPI == EPI_ROT) {
+    if constexpr (EPI != EPI_PLAIN) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-        if constexpr (B == 32) {
-          const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
-          lo = *reinterpret_cast<const uint2*>(Rj);
-          hi = *reinterpret_cast<const uint2*>(Rj + 8);
-        } else {
-          if ((l32 >> 4) == t) {
-            const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+        if (n_ok) {
+          if constexpr (B == 32) {
+            const uint16_t* Rj = rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
             lo = *reinterpret_cast<const uint2*>(Rj);
             hi = *reinterpret_cast<const uint2*>(Rj + 8);
+          } else {
+            if ((l32 >> 4) == t) {
+              const uint16_t* Rj = rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+              lo = *reinterpret_cast<const uint2*>(Rj);
+              hi = *reinterpret_cast<const uint2*>(Rj + 8);
+            }
           }
         }
         ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -320,7 +374,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       f32x16 o;
-      if constexpr (EPI == EPI_ROT) {
+      if constexpr (EPI != EPI_PLAIN) {
         f32x16 z = acc[tn][tm];
         if constexpr (FP8) {
 #pragma unroll
@@ -339,22 +393,76 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
         o = acc[tn][tm];
       }
       const int ml = wm * (BM / 2) + 32 * tm + l32;
-      if (ml >= nrows) continue;
+      const bool m_ok = n_ok && ml < nrows;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
-        if constexpr (OUTF32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) =
-              make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
-              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+        const uint32_t lo = pack_bf16x2(o[4 * q], o[4 * q + 1]);
+        const uint32_t hi = pack_bf16x2(o[4 * q + 2], o[4 * q + 3]);
+        if constexpr (SWI) {
+          swg[tn][tm][2 * q] = lo;
+          swg[tn][tm][2 * q + 1] = hi;
+        }
+        if (m_ok) {
+          const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
+          if constexpr (OUTF32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) =
+                make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) = make_uint2(lo, hi);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (SWI) {
+    // up waves (wn = 2, 3) hand their bf16 outputs to the gate waves (wn =
+    // 0, 1) holding the same (token, channel) slots; the ring is free once
+    // every wave has passed the barrier
+    static_assert(2 * 2 * 2 * TM * 8 * 64 * 4 <= NST * XB, "exchange buffer");
+    uint32_t* xb = reinterpret_cast<uint32_t*>(xs);
+    const int wg = wn & 1;
+    lds_barrier_plain();
+    if (wn >= 2) {
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) xb[((((wg * 2 + wm) * 2 + tn) * TM + tm) * 8 + v) * 64 + lane] = swg[tn][tm][v];
+    }
+    lds_barrier_plain();
+    if (wn < 2) {
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        const int cb = chan(64 * wn + 32 * tn);  // gate channel = act column
+        if (cb < 0) continue;
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const int ml = wm * (BM / 2) + 32 * tm + l32;
+          if (ml >= nrows) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float av[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint32_t gw = swg[tn][tm][2 * q + h];
+              const uint32_t uw = xb[((((wg * 2 + wm) * 2 + tn) * TM + tm) * 8 + 2 * q + h) * 64 + lane];
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const float gv = bf16_to_f32((uint16_t)(gw >> (16 * u)));
+                const float uv = bf16_to_f32((uint16_t)(uw >> (16 * u)));
+                av[2 * h + u] = gv / (1.0f + __expf(-gv)) * uv;
+              }
+            }
+            *reinterpret_cast<uint2*>(p.act + (size_t)(pos0 + ml) * p.ldact + cb + 8 * q + 4 * g2) =
+                make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+          }
         }
       }
     }
   }
 }
-
 
 // Few tokens (M <= 64): the layer is a weight stream.  Workgroup: 8 waves,
 // 128 channels x 64 tokens; wave (wn, kh) = (wave % 4, wave / 4) owns

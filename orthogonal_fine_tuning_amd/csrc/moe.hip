@@ -22,6 +22,7 @@
 //             token).
 #include "gemm_nn.h"
 #include "gemm_nt.h"
+#include "gemm_nt_dma.h"
 #include "oft_moe.h"
 
 namespace oft {
@@ -32,6 +33,9 @@ constexpr int MOE_BM = 128;  // rows (expert positions) per grouped tile
 #define OFT_MOE_NBUF 1
 #endif
 constexpr int MOE_NBUF = OFT_MOE_NBUF;  // LDS buffers of the grouped GEMMs
+#ifndef OFT_MOE_DMA
+#define OFT_MOE_DMA 1
+#endif
 
 // ---------------------------------------------------------------- wave scans
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -511,6 +515,9 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + L.O);
   const int nblk_e = 2 * d.I / B;
+  // copy-ring kernels when experts average at least 64 rows; with fewer the
+  // 128-row tiles are mostly empty and the register-prefetch kernels win
+  const bool dma = OFT_MOE_DMA && (long)d.T * d.k >= 64L * d.E;
   {
     NtArgs p{};
     p.a = q.x;
@@ -535,9 +542,15 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.offsets = rt.offsets;
     p.perm = rt.perm;
     p.kslots = d.k;
-    dim3 grid(d.I / 64, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false, MOE_NBUF>), grid, dim3(256), 0,
-                       st, p);
+    if (dma) {
+      dim3 grid((d.I + ntd::BN / 2 - 1) / (ntd::BN / 2), (unsigned)L.max_tiles);
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid, dim3(ntd::NTHR),
+                         0, st, p);
+    } else {
+      dim3 grid(d.I / 64, (unsigned)L.max_tiles);
+      hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false, MOE_NBUF>), grid,
+                         dim3(256), 0, st, p);
+    }
   }
   {
     NtArgs p{};
@@ -560,9 +573,15 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.offsets = rt.offsets;
     p.perm = rt.perm;
     p.kslots = 0;
-    dim3 grid((d.H + nt::BN - 1) / nt::BN, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false, MOE_NBUF>), grid, dim3(256), 0, st,
-                       p);
+    if (dma) {
+      dim3 grid((d.H + ntd::BN - 1) / ntd::BN, (unsigned)L.max_tiles);
+      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, 32, MOE_BM, EPI_PLAIN, false, true>), grid, dim3(ntd::NTHR), 0,
+                         st, p);
+    } else {
+      dim3 grid((d.H + nt::BN - 1) / nt::BN, (unsigned)L.max_tiles);
+      hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false, MOE_NBUF>), grid, dim3(256),
+                         0, st, p);
+    }
   }
   const size_t n8 = (size_t)d.T * d.H / 8;
   if (n8 > 0)

@@ -25,6 +25,12 @@ SMALL = {
                                    b=16, q_std=0.05),
     "moe_small_g128": MoEConfig("moe_small_g128", T=77, E=8, k=2, H=384, I=256, g=128, chunk=2, b=32,
                                 bias_std=0.5),
+    # at least 64 rows per expert on average (the copy-ring grouped GEMMs);
+    # I = 192 leaves a half-filled 128-channel gate/up tile
+    "moe_dense_b16_g64": MoEConfig("moe_dense_b16_g64", T=256, E=4, k=2, H=192, I=192, g=64, chunk=2,
+                                   b=16, q_std=0.05),
+    "moe_dense_g128": MoEConfig("moe_dense_g128", T=300, E=4, k=2, H=384, I=256, g=128, chunk=3, b=32,
+                                bias_std=0.5),
 }
 
 
