@@ -470,16 +470,19 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 // other 64-wide step: a ring stage holds a 128-wide step, kh picks its half,
 // so two waves share each SIMD and the two halves' partial sums are added
 // in LDS at the end (fixed order).  Same copies, layouts, contraction order
-// and epilogue as above; four stages, copies issued three 128-wide steps
-// ahead (about 75 KB in flight per workgroup).
+// and epilogues as above (grouped: tiles of at most 64 expert positions;
+// EPI_ROT_SWIGLU: 64 gate + 64 up channels per tile); four stages, copies
+// issued three 128-wide steps ahead (about 75 KB in flight per workgroup).
 namespace ntd {
 constexpr int DEC_BN = 128, DEC_NST = 4, DEC_NTHR = 512;
 template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK / 2 + DEC_BN * 4;
 }  // namespace ntd
 
-template <bool FP8, int B>
+template <bool FP8, int B, int EPI = EPI_ROT, bool GROUPED = false>
 __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p) {
   using namespace ntd;
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   constexpr int BMD = 64, TM = 2, NST = DEC_NST;
   constexpr int XH = BMD * BK * 2;      // 8 KB: one 64-wide half of a step
   constexpr int WH = DEC_W_HALF<FP8>;   // weight bytes of one half
@@ -492,9 +495,31 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
   const int wn = wave & 3, kh = wave >> 2;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
-  const int n0 = blockIdx.x * DEC_BN;
-  const int pos0 = blockIdx.y * BMD;
-  const int nrows = min(BMD, p.M - pos0);
+  int e = 0, pos0, nrows;
+  if constexpr (GROUPED) {
+    const int t = blockIdx.y;
+    if (t >= *p.ntiles) return;
+    e = p.tiles[2 * t];
+    pos0 = p.offsets[e] + p.tiles[2 * t + 1];
+    nrows = min(BMD, p.offsets[e + 1] - pos0);
+  } else {
+    pos0 = blockIdx.y * BMD;
+    nrows = min(BMD, p.M - pos0);
+  }
+  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
+  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
+  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  // channel of local weight row rw (0..127), or -1 past the layer's channels
+  const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
+  auto chan = [&](int rw) -> int {
+    if constexpr (SWI) {
+      const int c = cbase + (rw & (DEC_BN / 2 - 1));
+      return c < p.half_n ? (rw < DEC_BN / 2 ? c : p.half_n + c) : -1;
+    } else {
+      return cbase + rw < p.N ? cbase + rw : -1;
+    }
+  };
+  auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
   const int nk = K / BK;          // 64-wide steps
   const int nk2 = (nk + 1) / 2;   // 128-wide steps
   const int kg = FP8 ? 1 : K / p.g;
@@ -507,14 +532,19 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
   //   plus the rows' scale words on lanes 0..31)
   const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
   uint32_t xoff[2];
+  const uint8_t* xptr[GROUPED ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 16 * wn + 8 * i + (lane >> 3);
     const int rr = r < nrows ? r : 0;
-    xoff[i] = (uint32_t)(rr * p.lda * 2 + 16 * ((lane & 7) ^ swz_x(r)));
+    const int chunk = 16 * ((lane & 7) ^ swz_x(r));
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + chunk);
+    if constexpr (GROUPED) {
+      const long src = p.kslots > 0 ? (long)(p.perm[pos0 + rr] / p.kslots) : (long)(pos0 + rr);
+      xptr[i] = static_cast<const uint8_t*>(p.a) + src * p.lda * 2 + chunk;
+    }
   }
-  auto crow = [&](int rw) { return n0 + rw < p.N ? rw : 0; };
-  const uint8_t* wbase = p.wc + (FP8 ? (size_t)n0 * K : (size_t)n0 * (K / 2));
+  const uint8_t* wbase = wc + (FP8 ? (size_t)cbase * K : (size_t)cbase * (K / 2));
   uint32_t woff[2] = {0u, 0u};
   uint32_t sbase = 0;
   if constexpr (FP8) {
@@ -526,7 +556,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
   } else {
     const int rw = 32 * wn + (lane >> 1);
     woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
-    sbase = (uint32_t)((n0 + crow(32 * wn + l32)) * kg);
+    sbase = (uint32_t)((cbase + crow(32 * wn + l32)) * kg);
   }
   const uint32_t base_lds = lds_addr(smem);
   const uint32_t x_lds = base_lds + (uint32_t)(kh * XH + 16 * wn * 128);
@@ -539,15 +569,20 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
     int s = 2 * s2 + kh;
     if (s >= nk) s = 2 * s2;
     const uint8_t* xb = xbase + (size_t)s * BK * 2;
-    copy16(x_lds + st * SB, xb, xoff[0]);
-    copy16(x_lds + st * SB + 1024, xb, xoff[1]);
+    if constexpr (GROUPED) {
+      copy16v(x_lds + st * SB, xptr[0] + (size_t)s * BK * 2);
+      copy16v(x_lds + st * SB + 1024, xptr[1] + (size_t)s * BK * 2);
+    } else {
+      copy16(x_lds + st * SB, xb, xoff[0]);
+      copy16(x_lds + st * SB + 1024, xb, xoff[1]);
+    }
     if constexpr (FP8) {
       const uint8_t* wb = wbase + (size_t)s * BK;
       copy16(w_lds + st * SB, wb, woff[0]);
       copy16(w_lds + st * SB + 1024, wb, woff[1]);
     } else {
       copy16(w_lds + st * SB, wbase + (size_t)s * (BK / 2), woff[0]);
-      if (lane < 32) copy4(s_lds + st * SB, p.ws, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
+      if (lane < 32) copy4(s_lds + st * SB, ws_h, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
     }
   };
 
@@ -561,7 +596,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
     wrd[0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
     wrd[1] = 0u;
   }
-  const uint32_t srd = FP8 ? 0u : (uint32_t)((n0 + crow(rw)) * kg);
+  const uint32_t srd = FP8 ? 0u : (uint32_t)((cbase + crow(rw)) * kg);
 
   f32x16 acc[TM];
 #pragma unroll
@@ -627,68 +662,122 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
       for (int r = 0; r < 16; ++r) red[((wn * TM + tm) * 16 + r) * 64 + lane] = acc[tm][r];
   }
   lds_barrier_plain();
-  if (kh == 1) return;
+  if (kh == 0) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[tm][r] += red[((wn * TM + tm) * 16 + r) * 64 + lane];
-
-  // epilogue: FP8 channel scale, bf16, rotation, store
-  const int nb = n0 + 32 * wn;
-  if (nb >= p.N) return;
-  const float* ws_f = static_cast<const float*>(p.ws);
-  float fs[16];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
-      fs[4 * q] = v.x;
-      fs[4 * q + 1] = v.y;
-      fs[4 * q + 2] = v.z;
-      fs[4 * q + 3] = v.w;
-    }
+      for (int r = 0; r < 16; ++r) acc[tm][r] += red[((wn * TM + tm) * 16 + r) * 64 + lane];
   }
-  bf16x8 ra[2];
+
+  // epilogue (kh = 0 waves): FP8 channel scale, bf16, rotation (EPI_ROT*), store
+  const int nb = chan(32 * wn);
+  const float* ws_f = static_cast<const float*>(p.ws);
+  uint32_t swg[SWI ? TM : 1][8];
+  if (kh == 0 && nb >= 0) {
+    float fs[16];
+    if constexpr (EPI != EPI_PLAIN && FP8) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-    if constexpr (B == 32) {
-      const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
-      lo = *reinterpret_cast<const uint2*>(Rj);
-      hi = *reinterpret_cast<const uint2*>(Rj + 8);
-    } else {
-      if ((l32 >> 4) == t) {
-        const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
-        lo = *reinterpret_cast<const uint2*>(Rj);
-        hi = *reinterpret_cast<const uint2*>(Rj + 8);
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(ws_f + nb + 8 * q + 4 * g2);
+        fs[4 * q] = v.x;
+        fs[4 * q + 1] = v.y;
+        fs[4 * q + 2] = v.z;
+        fs[4 * q + 3] = v.w;
       }
     }
-    ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-  }
+    bf16x8 ra[2];
+    if constexpr (EPI != EPI_PLAIN) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    f32x16 z = acc[tm];
-    if constexpr (FP8) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) z[r] *= fs[r];
+      for (int t = 0; t < 2; ++t) {
+        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+        if constexpr (B == 32) {
+          const uint16_t* Rj = rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
+          lo = *reinterpret_cast<const uint2*>(Rj);
+          hi = *reinterpret_cast<const uint2*>(Rj + 8);
+        } else {
+          if ((l32 >> 4) == t) {
+            const uint16_t* Rj = rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+            lo = *reinterpret_cast<const uint2*>(Rj);
+            hi = *reinterpret_cast<const uint2*>(Rj + 8);
+          }
+        }
+        ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
     }
-    bf16x8 zb[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
-                                   pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
-    f32x16 o;
+    for (int tm = 0; tm < TM; ++tm) {
+      f32x16 o;
+      if constexpr (EPI != EPI_PLAIN) {
+        f32x16 z = acc[tm];
+        if constexpr (FP8) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-    o = mfma32(ra[0], zb[0], o);
-    o = mfma32(ra[1], zb[1], o);
-    const int ml = 32 * tm + l32;
-    if (ml >= nrows) continue;
+          for (int r = 0; r < 16; ++r) z[r] *= fs[r];
+        }
+        bf16x8 zb[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
-          make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+        for (int t = 0; t < 2; ++t)
+          zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
+                                       pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+        o = mfma32(ra[0], zb[0], o);
+        o = mfma32(ra[1], zb[1], o);
+      } else {
+        o = acc[tm];
+      }
+      const int ml = 32 * tm + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = pack_bf16x2(o[4 * q], o[4 * q + 1]);
+        const uint32_t hi = pack_bf16x2(o[4 * q + 2], o[4 * q + 3]);
+        if constexpr (SWI) {
+          swg[tm][2 * q] = lo;
+          swg[tm][2 * q + 1] = hi;
+        }
+        if (ml < nrows) {
+          const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  if constexpr (SWI) {
+    // up waves (wn = 2, 3) hand their bf16 outputs to the gate waves (wn =
+    // 0, 1), in LDS past the partial-sum area; every wave takes the barrier
+    constexpr int RED = 4 * TM * 16 * 64;  // floats of the partial-sum area
+    uint32_t* xb = reinterpret_cast<uint32_t*>(smem) + RED;
+    static_assert((RED + 2 * TM * 8 * 64) * 4 <= NST * SB, "exchange buffer");
+    const int wg = wn & 1;
+    if (kh == 0 && wn >= 2 && nb >= 0) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) xb[((wg * TM + tm) * 8 + v) * 64 + lane] = swg[tm][v];
+    }
+    lds_barrier_plain();
+    if (kh == 0 && wn < 2 && nb >= 0) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int ml = 32 * tm + l32;
+        if (ml >= nrows) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float av[4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t gw = swg[tm][2 * q + h];
+            const uint32_t uw = xb[((wg * TM + tm) * 8 + 2 * q + h) * 64 + lane];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const float gv = bf16_to_f32((uint16_t)(gw >> (16 * u)));
+              const float uv = bf16_to_f32((uint16_t)(uw >> (16 * u)));
+              av[2 * h + u] = gv / (1.0f + __expf(-gv)) * uv;
+            }
+          }
+          *reinterpret_cast<uint2*>(p.act + (size_t)(pos0 + ml) * p.ldact + nb + 8 * q + 4 * g2) =
+              make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+        }
+      }
     }
   }
 }

@@ -210,11 +210,11 @@ __global__ __launch_bounds__(1024) void moe_scan_kernel(int E, int chunk, MoeRou
   write_work_list(e < E ? cnt : 0, e, E, MOE_BM, list, ntiles, sh);
 }
 
-__global__ __launch_bounds__(1024) void moe_worklist_kernel(const int* __restrict__ counts, int E,
+__global__ __launch_bounds__(1024) void moe_worklist_kernel(const int* __restrict__ counts, int E, int bm,
                                                             int* __restrict__ list, int* __restrict__ ntiles) {
   __shared__ int sh[40];
   const int e = threadIdx.x;
-  write_work_list(e < E ? counts[e] : 0, e, E, MOE_BM, list, ntiles, sh);
+  write_work_list(e < E ? counts[e] : 0, e, E, bm, list, ntiles, sh);
 }
 
 // ---------------------------------------------------------------- permute
@@ -469,6 +469,9 @@ MoeWs moe_ws_layout(const MoeDims& d, int pass) {
   w.ntiles = take(sizeof(int));
   w.max_tiles = max_tiles;
   if (pass == 0) {
+    w.max_tiles64 = (P + 63) / 64 + d.E;
+    w.list64 = take(2 * w.max_tiles64 * sizeof(int));
+    w.ntiles64 = take(sizeof(int));
     w.gmask = take((size_t)nt64 * d.E * 8);
     w.tile_off = take((size_t)nt64 * d.E * 4);
     w.act = take((size_t)P * d.I * 2);
@@ -515,9 +518,13 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + L.O);
   const int nblk_e = 2 * d.I / B;
-  // copy-ring kernels when experts average at least 64 rows; with fewer the
-  // 128-row tiles are mostly empty and the register-prefetch kernels win
+  // experts averaging at least 64 rows: copy-ring kernels on 128-row tiles;
+  // fewer (decode): the weight-streaming copy-ring kernel on 64-row tiles
   const bool dma = OFT_MOE_DMA && (long)d.T * d.k >= 64L * d.E;
+  const bool dec = OFT_MOE_DMA && !dma;
+  int* list64 = reinterpret_cast<int*>(ws + L.list64);
+  int* ntiles64 = reinterpret_cast<int*>(ws + L.ntiles64);
+  if (dec) hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, 64, list64, ntiles64);
   {
     NtArgs p{};
     p.a = q.x;
@@ -546,6 +553,11 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       dim3 grid((d.I + ntd::BN / 2 - 1) / (ntd::BN / 2), (unsigned)L.max_tiles);
       hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid, dim3(ntd::NTHR),
                          0, st, p);
+    } else if (dec) {
+      p.tiles = list64;
+      p.ntiles = ntiles64;
+      dim3 grid((d.I + ntd::DEC_BN / 2 - 1) / (ntd::DEC_BN / 2), (unsigned)L.max_tiles64);
+      hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     } else {
       dim3 grid(d.I / 64, (unsigned)L.max_tiles);
       hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false, MOE_NBUF>), grid,
@@ -577,6 +589,11 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       dim3 grid((d.H + ntd::BN - 1) / ntd::BN, (unsigned)L.max_tiles);
       hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, 32, MOE_BM, EPI_PLAIN, false, true>), grid, dim3(ntd::NTHR), 0,
                          st, p);
+    } else if (dec) {
+      p.tiles = list64;
+      p.ntiles = ntiles64;
+      dim3 grid((d.H + ntd::DEC_BN - 1) / ntd::DEC_BN, (unsigned)L.max_tiles64);
+      hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     } else {
       dim3 grid((d.H + nt::BN - 1) / nt::BN, (unsigned)L.max_tiles);
       hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false, MOE_NBUF>), grid, dim3(256),
@@ -609,7 +626,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
   float* dw_part = reinterpret_cast<float*>(ws + L.dw_part);
   uint16_t* dXp = reinterpret_cast<uint16_t*>(ws + L.dXp);
   const int nblk_e = 2 * d.I / B;
-  hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, list, ntiles);
+  hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, MOE_BM, list, ntiles);
   if (d.T > 0) {
     NnArgs p{};
     p.src = q.dy;

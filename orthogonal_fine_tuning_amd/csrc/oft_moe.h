@@ -28,7 +28,8 @@ struct MoeRoutingDev {
 // byte offsets of the scratch buffers inside the caller's workspace
 struct MoeWs {
   size_t list, ntiles, gmask, tile_off, act, O, dH, dw_part, dXp, dz;
-  long max_tiles;
+  size_t list64, ntiles64;  // forward: work list of 64-row tiles (few rows per expert)
+  long max_tiles, max_tiles64;
   size_t bytes;
 };
 MoeWs moe_ws_layout(const MoeDims& d, int pass);
