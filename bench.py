@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qkv_4b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-ref", action="store_true",
+                    help="MoE: skip the dense-bf16-weight reference run of the same grouped kernels")
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
                     help="token rows of the oracle sample for cpu_baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -220,11 +222,14 @@ def run_moe(cfg, args):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    mem0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    transient = torch.cuda.max_memory_allocated() - mem0  # the library allocates nothing
     n_active = int(rtt["n_active"][0].item())
     t_cay = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
@@ -250,9 +255,69 @@ def run_moe(cfg, args):
                         "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
                         "hbm_frac": round((by_fwd + by_bwd) / (t_fwd + t_bwd) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    out["transient_bytes"] = int(transient)
+    if not args.no_dense_ref:
+        del W
+        out["dense_bf16_reference"] = moe_dense_reference(cfg, inp, args, dict(
+            x=x, lg=lg, dy=dy, rt=rt, Rf=Rf, Rops=Rops, hs=hs, y=y, dx=dx, dq=dq, dw=dw), t_fwd + t_bwd)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = moe_cpu_baseline(cfg, inp)
     return out
+
+
+def moe_dense_reference(cfg, inp, args, bufs, t_ours):
+    """The same grouped kernels with every expert's weights dequantised to
+    bf16 in HBM beforehand (not timed): the dense-weight reference of the
+    fwd + bwd calls.  Same routing, inputs, outputs and step count."""
+    import numpy as np
+    import torch
+
+    import orthogonal_fine_tuning_amd as oft
+
+    T, E, k, H, I, b, g = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b, cfg.g
+    d16 = oft.moe_desc(T, E, k, H, I, g, b, cfg.chunk, 0, w_fmt=oft.OFT_W_BF16)
+    wgu = torch.empty((E, 2 * I, H), dtype=torch.int16, device="cuda")
+    wd = torch.empty((E, H, I), dtype=torch.int16, device="cuda")
+    for name, rows, cols, out in (("wgu", E * 2 * I, H, wgu), ("wd", E * H, I, wd)):
+        codes = torch.from_numpy(np.ascontiguousarray(inp[f"{name}_codes"])).to("cuda")
+        scales = torch.from_numpy(np.ascontiguousarray(inp[f"{name}_scales"]).view(np.int16)).to("cuda")
+        oft.oft_dequant(oft.OFT_W_INT4, rows, cols, g, codes, scales, out)
+        del codes, scales
+    nbf = oft.oft_moe_workspace_bytes(d16, oft.OFT_PASS_FWD)
+    nbb = oft.oft_moe_workspace_bytes(d16, oft.OFT_PASS_BWD)
+    wsf = torch.empty(nbf, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(nbb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    B = bufs
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        oft.oft_moe_grouped_fwd(d16, B["x"], B["lg"], wgu, None, wd, None, B["Rops"], B["rt"], B["hs"], B["y"],
+                                wsf, nbf, stream=sp)
+        if ev is not None:
+            ev[1].record(stream)
+        oft.oft_moe_grouped_bwd(d16, B["dy"], B["rt"], B["hs"], wgu, None, wd, None, B["Rf"], B["Rops"], B["dx"],
+                                B["dq"], B["dw"], wsb, nbb, stream=sp)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    del wgu, wd, wsf, wsb
+    torch.cuda.empty_cache()
+    return {"fwd_us": round(t_fwd * 1e6, 2), "bwd_us": round(t_bwd * 1e6, 2),
+            "weights_bytes": int(E * 3 * I * H * 2),
+            "ratio": round(t_ours / (t_fwd + t_bwd), 4),
+            "note": "fwd+bwd time of the INT4 path over that of the same kernels on bf16 weights"}
 
 
 def moe_cpu_baseline(cfg, inp, n_experts=4):

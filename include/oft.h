@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 1
+#define OFT_ABI_VERSION 2
 
 typedef enum {
   OFT_OK = 0,
@@ -73,7 +73,10 @@ typedef enum {
 } oft_status;
 
 enum { OFT_DT_BF16 = 0, OFT_DT_F32 = 1 };
-enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1 };
+/* OFT_W_BF16: weights already dequantised to bf16 (MoE calls only; the
+ * dense-weight reference that the grouped dequant GEMMs are measured
+ * against: same kernels, no scales, two bytes per weight in HBM). */
+enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1, OFT_W_BF16 = 2 };
 enum { OFT_PASS_FWD = 0, OFT_PASS_BWD = 1 };
 
 #define OFT_MAX_SEGMENTS 8
@@ -95,15 +98,20 @@ typedef struct {
 /* MoE layer: T tokens, E experts, top-k routing, hidden H, expert
  * intermediate I.  Per expert e: gate/up weight [2I, H] (gate rows [0, I),
  * up rows [I, 2I)) with its own adapter of 2I/b blocks (gate blocks first),
- * down weight [H, I] without adapter; all INT4 with group g.
+ * down weight [H, I] without adapter; INT4 with group g (w_fmt =
+ * OFT_W_INT4, zero) or, as a measurement reference, bf16 (OFT_W_BF16: the
+ * code arrays hold bf16 weights [E, 2I, H] and [E, H, I], the scale
+ * pointers are ignored and may be NULL, g is not checked).
  * Constraints: T >= 0; 1 <= k <= 16; k <= E <= 1024; H % 64 == 0;
- * I % 64 == 0; b in {16, 32}; I % b == 0; g in {32, 64, 128}; H % g == 0;
- * I % g == 0; chunk >= 1; renorm in {0, 1}. */
+ * I % 64 == 0; b in {16, 32}; I % b == 0; INT4: g in {32, 64, 128},
+ * H % g == 0, I % g == 0; chunk >= 1; renorm in {0, 1}; w_fmt one of the
+ * two formats above (else OFT_EDTYPE). */
 typedef struct {
   int32_t T, E, k, H, I, g, b;
   int32_t chunk;  /* active experts per chunk (scheduling unit)            */
   int32_t renorm; /* 0: combine weights = softmax over all E at the chosen
                      experts; 1: renormalised over the k chosen             */
+  int32_t w_fmt;  /* OFT_W_INT4 (0) or OFT_W_BF16                          */
 } oft_moe_desc;
 
 /* Routing tables: device pointers, caller-allocated, written by the
@@ -188,7 +196,8 @@ int32_t oft_moe_route(const oft_moe_desc* d, const float* logits, const oft_moe_
  * permuted order; SwiGLU; the down dequant grouped GEMM; and the combine
  * y[t] = sum_j w[t,j] O[inv_perm[t*k+j]] (fixed order over j) -> y [T, H].
  * x [T, H] bf16; wgu_codes [E, 2I, H/2], wgu_scales fp16 [E, 2I, H/g];
- * wd_codes [E, H, I/2], wd_scales fp16 [E, H, I/g]; R_ops [E, 2I/b, 2, b, b]. */
+ * wd_codes [E, H, I/2], wd_scales fp16 [E, H, I/g] (OFT_W_BF16: bf16
+ * weights in the code arrays, see oft_moe_desc); R_ops [E, 2I/b, 2, b, b]. */
 int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const float* logits,
                             const uint8_t* wgu_codes, const uint16_t* wgu_scales,
                             const uint8_t* wd_codes, const uint16_t* wd_scales,

@@ -9,14 +9,16 @@ from __future__ import annotations
 import ctypes as C
 
 from . import _lib
-from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_FP8_E4M3,
-                   OFT_W_INT4, OftError, oft_linear_desc, oft_moe_desc, oft_moe_routing)
+from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF16,
+                   OFT_W_FP8_E4M3, OFT_W_INT4, OftError, oft_linear_desc, oft_moe_desc,
+                   oft_moe_routing)
 
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
     "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_bwd", "oft_moe_workspace_bytes",
     "oft_moe_route", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
-    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_PASS_FWD", "OFT_PASS_BWD",
+    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_PASS_FWD",
+    "OFT_PASS_BWD",
 ]
 
 
@@ -48,10 +50,10 @@ def linear_desc(M, K, segs, b, x_dtype=OFT_DT_BF16, w_fmt=OFT_W_INT4, g=0) -> of
     return d
 
 
-def moe_desc(T, E, k, H, I, g, b, chunk, renorm=0) -> oft_moe_desc:
+def moe_desc(T, E, k, H, I, g, b, chunk, renorm=0, w_fmt=OFT_W_INT4) -> oft_moe_desc:
     d = oft_moe_desc()
-    d.T, d.E, d.k, d.H, d.I, d.g, d.b, d.chunk, d.renorm = (int(v) for v in
-                                                            (T, E, k, H, I, g, b, chunk, renorm))
+    d.T, d.E, d.k, d.H, d.I, d.g, d.b, d.chunk, d.renorm, d.w_fmt = (
+        int(v) for v in (T, E, k, H, I, g, b, chunk, renorm, w_fmt))
     return d
 
 

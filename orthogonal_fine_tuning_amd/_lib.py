@@ -14,7 +14,7 @@ LIB_PATH = os.environ.get("OFT_LIBRARY") or os.path.join(_HERE, "liboft.so")
 OFT_OK, OFT_EINVAL, OFT_ESHAPE, OFT_EDTYPE, OFT_EUNSUPPORTED, OFT_EWORKSPACE, OFT_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
 OFT_DT_BF16, OFT_DT_F32 = 0, 1
-OFT_W_INT4, OFT_W_FP8_E4M3 = 0, 1
+OFT_W_INT4, OFT_W_FP8_E4M3, OFT_W_BF16 = 0, 1, 2
 OFT_PASS_FWD, OFT_PASS_BWD = 0, 1
 OFT_MAX_SEGMENTS = 8
 
@@ -28,7 +28,7 @@ class oft_linear_desc(C.Structure):
 class oft_moe_desc(C.Structure):
     _fields_ = [("T", C.c_int32), ("E", C.c_int32), ("k", C.c_int32), ("H", C.c_int32),
                 ("I", C.c_int32), ("g", C.c_int32), ("b", C.c_int32), ("chunk", C.c_int32),
-                ("renorm", C.c_int32)]
+                ("renorm", C.c_int32), ("w_fmt", C.c_int32)]
 
 
 class oft_moe_routing(C.Structure):

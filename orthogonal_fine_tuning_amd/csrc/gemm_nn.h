@@ -4,8 +4,8 @@
 //   PRO_ROT  : B'_blk = src_blk R_j (computed as R_j^T src^T on the matrix
 //              cores; FP8 also multiplies channel n by s_n), rounded to bf16;
 //   PRO_NONE : B' = src.
-// The weight tile [64 n x 128 k] is dequantised in registers and stored to
-// LDS in its natural layout (k contiguous, 16-byte stores); the matrix-core
+// The weight tile [64 n x 128 k] (INT4 or FP8 codes, or bf16 values) is
+// dequantised in registers and stored to LDS in its natural layout (k contiguous, 16-byte stores); the matrix-core
 // operand, which must run along the contraction n, is read with the gfx950
 // LDS transpose load (ds_read_b64_tr_b16: within each 16-lane group, lane i
 // receives element i % 4 of the 8-byte chunks loaded by lanes 4e + i / 4,
@@ -75,10 +75,12 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
 }
 }  // namespace nn
 
-template <int BM, bool OUTF32, bool FP8, int B, int PRO, int EPI, bool GROUPED, int NBUF = 2>
+template <int BM, bool OUTF32, int WF, int B, int PRO, int EPI, bool GROUPED, int NBUF = 2>
 __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn_kernel(NnArgs p) {
   using namespace nn;
   static_assert(BM == 128 || BM == 256, "tile");
+  constexpr bool FP8 = WF == WF_FP8;
+  constexpr bool W16 = WF == WF_BF16;  // bf16 weights: plain copies into the tile
   constexpr int TM = BM / 64;   // 32-token tiles per wave (main product)
   constexpr int PM = BM / 128;  // 32-token tiles each wave prepares in the prologue
   constexpr int WSZ = BNS * LDW;        // weight tile [n][k]
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
   // W tile: thread owns row n0 + wrow, columns k0 + 32*wq + 0..31
   const int wrow = tid >> 2, wq = tid & 3;
   const bool k_ok = (k0 + 32 * wq) < K;
-  uint4 wr[FP8 ? 2 : 1];
+  uint4 wr[W16 ? 4 : FP8 ? 2 : 1];
   uint16_t wsb = 0;  // INT4: fp16 scale bits of the prefetched weight row
 
   // source rows this wave feeds to the prologue
@@ -139,7 +141,11 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
     {
       const int n = n0 + wrow;
       const bool ok = k_ok && n < N;
-      if constexpr (FP8) {
+      if constexpr (W16) {
+        const uint8_t* src = wc + ((size_t)n * K + k0 + 32 * wq) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[i] = ok ? *reinterpret_cast<const uint4*>(src + 16 * i) : zero4();
+      } else if constexpr (FP8) {
         const uint8_t* src = wc + (size_t)n * K + k0 + 32 * wq;
         wr[0] = ok ? *reinterpret_cast<const uint4*>(src) : zero4();
         wr[1] = ok ? *reinterpret_cast<const uint4*>(src + 16) : zero4();
@@ -186,7 +192,10 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
     uint16_t* Bs = Ws + WSZ;
     // W tile -> LDS, natural layout
     uint4* dst = reinterpret_cast<uint4*>(&Ws[wrow * LDW + 32 * wq]);
-    if constexpr (FP8) {
+    if constexpr (W16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = wr[i];
+    } else if constexpr (FP8) {
       const uint32_t wv[8] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w, wr[1].x, wr[1].y, wr[1].z, wr[1].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

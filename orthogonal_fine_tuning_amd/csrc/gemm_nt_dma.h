@@ -56,8 +56,6 @@
 
 namespace oft {
 
-enum : int { WF_INT4 = 0, WF_FP8 = 1, WF_BF16 = 2 };
-
 namespace ntd {
 constexpr int BN = 256;  // channels per workgroup
 constexpr int BK = 64;   // in-features per step

@@ -516,7 +516,7 @@ hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src
     p.nsplit_len = pl.nsplit_len;
     p.part = reinterpret_cast<float*>(work + pl.npart_off);
   }
-  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8 ? WF_FP8 : WF_INT4, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
   if (pl.nsplit_n > 1) {
     const size_t n4 = (size_t)a.M * a.K / 4;
     hipLaunchKernelGGL(split_reduce_kernel<XF32>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, p.part,

@@ -520,8 +520,11 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
   const int nblk_e = 2 * d.I / B;
   // experts averaging at least 64 rows: copy-ring kernels on 128-row tiles;
   // fewer (decode): the weight-streaming copy-ring kernel on 64-row tiles
-  const bool dma = OFT_MOE_DMA && (long)d.T * d.k >= 64L * d.E;
+  // (bf16 reference weights: the 128-row copy-ring kernel at every size)
+  const bool w16 = d.wf == WF_BF16;
+  const bool dma = w16 || (OFT_MOE_DMA && (long)d.T * d.k >= 64L * d.E);
   const bool dec = OFT_MOE_DMA && !dma;
+  const long wb2 = w16 ? 4 : 1;  // bytes per two weights
   int* list64 = reinterpret_cast<int*>(ws + L.list64);
   int* ntiles64 = reinterpret_cast<int*>(ws + L.ntiles64);
   if (dec) hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, 64, list64, ntiles64);
@@ -531,8 +534,8 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.lda = d.H;
     p.wc = q.wgu_codes;
     p.ws = q.wgu_scales;
-    p.wc_e = (long)2 * d.I * d.H / 2;
-    p.ws_e = (long)2 * d.I * (d.H / d.g);
+    p.wc_e = (long)2 * d.I * d.H / 2 * wb2;
+    p.ws_e = w16 ? 0 : (long)2 * d.I * (d.H / d.g);
     p.rops = q.R_ops;
     p.rops_e = (long)nblk_e * 2 * B * B;
     p.out = q.h_saved;
@@ -551,8 +554,12 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.kslots = d.k;
     if (dma) {
       dim3 grid((d.I + ntd::BN / 2 - 1) / (ntd::BN / 2), (unsigned)L.max_tiles);
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid, dim3(ntd::NTHR),
-                         0, st, p);
+      if (w16)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
+                           dim3(ntd::NTHR), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
+                           dim3(ntd::NTHR), 0, st, p);
     } else if (dec) {
       p.tiles = list64;
       p.ntiles = ntiles64;
@@ -570,8 +577,8 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.lda = d.I;
     p.wc = q.wd_codes;
     p.ws = q.wd_scales;
-    p.wc_e = (long)d.H * d.I / 2;
-    p.ws_e = (long)d.H * (d.I / d.g);
+    p.wc_e = (long)d.H * d.I / 2 * wb2;
+    p.ws_e = w16 ? 0 : (long)d.H * (d.I / d.g);
     p.rops = q.R_ops;
     p.rops_e = 0;
     p.out = O;
@@ -587,8 +594,12 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.kslots = 0;
     if (dma) {
       dim3 grid((d.H + ntd::BN - 1) / ntd::BN, (unsigned)L.max_tiles);
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, 32, MOE_BM, EPI_PLAIN, false, true>), grid, dim3(ntd::NTHR), 0,
-                         st, p);
+      if (w16)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
+                           dim3(ntd::NTHR), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
+                           dim3(ntd::NTHR), 0, st, p);
     } else if (dec) {
       p.tiles = list64;
       p.ntiles = ntiles64;
@@ -626,6 +637,8 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
   float* dw_part = reinterpret_cast<float*>(ws + L.dw_part);
   uint16_t* dXp = reinterpret_cast<uint16_t*>(ws + L.dXp);
   const int nblk_e = 2 * d.I / B;
+  const bool w16 = d.wf == WF_BF16;
+  const long wb2 = w16 ? 4 : 1;  // bytes per two weights
   hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, MOE_BM, list, ntiles);
   if (d.T > 0) {
     NnArgs p{};
@@ -633,8 +646,8 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.lds = d.H;
     p.wc = q.wd_codes;
     p.ws = q.wd_scales;
-    p.wc_e = (long)d.H * d.I / 2;
-    p.ws_e = (long)d.H * (d.I / d.g);
+    p.wc_e = (long)d.H * d.I / 2 * wb2;
+    p.ws_e = w16 ? 0 : (long)d.H * (d.I / d.g);
     p.rops = q.R_ops;
     p.out = dH;
     p.ldo = 2 * d.I;
@@ -653,8 +666,12 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.dw_part = dw_part;
     p.P = P;
     dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>), grid, dim3(256),
-                       0, st, p);
+    if (w16)
+      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>), grid,
+                         dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_INT4, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>), grid,
+                         dim3(256), 0, st, p);
     if (q.dw)
       hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part,
                          (d.I + 127) / 128, P, rt.inv_perm, q.dw);
@@ -669,8 +686,8 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.lds = 2 * d.I;
     p.wc = q.wgu_codes;
     p.ws = q.wgu_scales;
-    p.wc_e = (long)2 * d.I * d.H / 2;
-    p.ws_e = (long)2 * d.I * (d.H / d.g);
+    p.wc_e = (long)2 * d.I * d.H / 2 * wb2;
+    p.ws_e = w16 ? 0 : (long)2 * d.I * (d.H / d.g);
     p.rops = q.R_ops;
     p.rops_e = (long)nblk_e * 2 * B * B;
     p.out = dXp;
@@ -685,8 +702,12 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.perm = rt.perm;
     p.kslots = 0;
     dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, false, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid, dim3(256), 0,
-                       st, p);
+    if (w16)
+      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
+                         dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_INT4, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
+                         dim3(256), 0, st, p);
     const size_t n8 = (size_t)d.T * d.H / 8;
     hipLaunchKernelGGL(moe_unpermute_sum_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dXp, d.H,
                        d.k, rt.inv_perm, n8, q.dx);

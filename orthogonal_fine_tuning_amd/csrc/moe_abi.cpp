@@ -18,16 +18,23 @@ int32_t validate_moe(const oft_moe_desc* d) {
   if (d->k > 16 || d->E > 1024 || d->k > d->E) return OFT_EUNSUPPORTED;
   if ((long long)d->T * d->k > (1LL << 30) || d->H > (1 << 16) || d->I > (1 << 16)) return OFT_EUNSUPPORTED;
   if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;
-  if (d->g != 32 && d->g != 64 && d->g != 128) return OFT_EUNSUPPORTED;
+  if (d->w_fmt != OFT_W_INT4 && d->w_fmt != OFT_W_BF16) return OFT_EDTYPE;
+  const bool int4 = d->w_fmt == OFT_W_INT4;
+  if (int4 && d->g != 32 && d->g != 64 && d->g != 128) return OFT_EUNSUPPORTED;
   if (d->renorm != 0 && d->renorm != 1) return OFT_EINVAL;
   if (d->H % 64 != 0 || d->I % 64 != 0 || d->I % d->b != 0) return OFT_ESHAPE;
-  if (d->H % d->g != 0 || d->I % d->g != 0) return OFT_ESHAPE;
+  if (int4 && (d->H % d->g != 0 || d->I % d->g != 0)) return OFT_ESHAPE;
   return OFT_OK;
 }
 
 oft::MoeDims dims(const oft_moe_desc* d) {
-  return oft::MoeDims{d->T, d->E, d->k, d->H, d->I, d->g, d->b, d->chunk, d->renorm};
+  const bool int4 = d->w_fmt == OFT_W_INT4;
+  return oft::MoeDims{d->T, d->E, d->k, d->H, d->I, int4 ? d->g : 64, d->b, d->chunk, d->renorm,
+                      int4 ? oft::WF_INT4 : oft::WF_BF16};
 }
+
+// scales are required for INT4 weights only
+bool scales_ok(const oft_moe_desc* d, const void* p) { return d->w_fmt != OFT_W_INT4 || ptr_ok(p); }
 
 int32_t routing_ok(const oft_moe_routing* rt) {
   if (rt == nullptr) return OFT_EINVAL;
@@ -85,9 +92,10 @@ int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const floa
   if (v != OFT_OK) return v;
   if ((v = routing_ok(rt)) != OFT_OK) return v;
   if (d->T > 0) {
-    const void* req[] = {x, logits, wgu_codes, wgu_scales, wd_codes, wd_scales, R_ops, h_saved, y};
+    const void* req[] = {x, logits, wgu_codes, wd_codes, R_ops, h_saved, y};
     for (const void* p : req)
       if (!ptr_ok(p)) return OFT_EINVAL;
+    if (!scales_ok(d, wgu_scales) || !scales_ok(d, wd_scales)) return OFT_EINVAL;
   }
   const oft::MoeWs L = oft::moe_ws_layout(dims(d), OFT_PASS_FWD);
   if (!ptr_ok(ws)) return OFT_EINVAL;
@@ -110,10 +118,11 @@ int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft
   if (dq_or_null != nullptr && !ptr_ok(R_f32)) return OFT_EINVAL;
   if (dx_or_null != nullptr && !ptr_ok(R_ops)) return OFT_EINVAL;
   if (d->T > 0) {
-    const void* req[] = {dy, h_saved, wd_codes, wd_scales};
+    const void* req[] = {dy, h_saved, wd_codes};
     for (const void* p : req)
       if (!ptr_ok(p)) return OFT_EINVAL;
-    if (dx_or_null != nullptr && (!ptr_ok(wgu_codes) || !ptr_ok(wgu_scales))) return OFT_EINVAL;
+    if (!scales_ok(d, wd_scales)) return OFT_EINVAL;
+    if (dx_or_null != nullptr && (!ptr_ok(wgu_codes) || !scales_ok(d, wgu_scales))) return OFT_EINVAL;
   }
   const oft::MoeWs L = oft::moe_ws_layout(dims(d), OFT_PASS_BWD);
   if (!ptr_ok(ws)) return OFT_EINVAL;

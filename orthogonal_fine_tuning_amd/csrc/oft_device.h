@@ -15,6 +15,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "oft_formats.h"
 
 namespace oft {
 

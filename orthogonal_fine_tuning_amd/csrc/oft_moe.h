@@ -5,11 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include "oft_formats.h"
 
 namespace oft {
 
 struct MoeDims {
   int T, E, k, H, I, g, b, chunk, renorm;
+  int wf;  // WF_INT4 or WF_BF16 (dequantised reference weights)
 };
 
 // device pointers of the routing tables (mirrors oft_moe_routing)

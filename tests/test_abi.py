@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.oft_abi_version() == 1
+    assert lib.oft_abi_version() == 2
     for s in range(-6, 1):
         assert lib.oft_status_str(s)
     assert b"unknown" in lib.oft_status_str(-99)
@@ -138,6 +138,10 @@ def _moe(**kw):
     (dict(chunk=0), _lib.OFT_EINVAL),
     (dict(renorm=2), _lib.OFT_EINVAL),
     (dict(T=-3), _lib.OFT_EINVAL),
+    (dict(w_fmt=1), _lib.OFT_EDTYPE),  # FP8 experts are not a MoE format
+    (dict(w_fmt=7), _lib.OFT_EDTYPE),
+    (dict(w_fmt=2, g=0), _lib.OFT_OK),  # bf16 reference weights: no group
+    (dict(w_fmt=2, g=0, I=96), _lib.OFT_ESHAPE),
 ])
 def test_moe_validation(kw, code):
     d = _moe(**kw)
@@ -156,3 +160,21 @@ def test_moe_workspace_and_routing_checks():
     rt = _lib.oft_moe_routing()  # all NULL
     ok = C.c_void_p(0x1000)
     assert lib.oft_moe_route(C.byref(d), ok, C.byref(rt), ok, fwd, None) == _lib.OFT_EINVAL
+
+
+def test_moe_bf16_weights_need_no_scales():
+    # bf16 reference weights: NULL scale pointers pass validation, which then
+    # stops at the routing tables (all NULL here), before anything is enqueued
+    lib = _lib.load()
+    ok = C.c_void_p(0x1000)
+    rt = _lib.oft_moe_routing()
+    for w_fmt, code in ((oft.OFT_W_BF16, _lib.OFT_EINVAL), (oft.OFT_W_INT4, _lib.OFT_EINVAL)):
+        d = _moe(w_fmt=w_fmt)
+        assert lib.oft_moe_grouped_fwd(C.byref(d), ok, ok, ok, None, ok, None, ok, C.byref(rt), ok,
+                                       ok, ok, 1 << 30, None) == code
+    full = _lib.oft_moe_routing(*([0x1000] * 9))
+    ws = oft.oft_moe_workspace_bytes(_moe(), oft.OFT_PASS_FWD)
+    # INT4 without scales: rejected; bf16 without scales would launch, so only
+    # the rejection is exercised here
+    assert lib.oft_moe_grouped_fwd(C.byref(_moe()), ok, ok, ok, None, ok, None, ok, C.byref(full),
+                                   ok, ok, ok, ws, None) == _lib.OFT_EINVAL

@@ -95,21 +95,39 @@ def test_routing_ties_and_renorm():
     _check_routing(cfg, logits, got, renorm=True)
 
 
-def _run_moe(inp, want_bwd=True):
+def _bf16_weights(inp):
+    """The experts' weights dequantised to bf16 on the GPU (oft_dequant)."""
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = inp["cfg"]
+    E, H, I, g = cfg.E, cfg.H, cfg.I, cfg.g
+    wgu = torch.empty((E, 2 * I, H), dtype=torch.int16, device="cuda")
+    wd = torch.empty((E, H, I), dtype=torch.int16, device="cuda")
+    oft.oft_dequant(oft.OFT_W_INT4, E * 2 * I, H, g, dev(inp["wgu_codes"]), dev(inp["wgu_scales"]), wgu)
+    oft.oft_dequant(oft.OFT_W_INT4, E * H, I, g, dev(inp["wd_codes"]), dev(inp["wd_scales"]), wd)
+    return {"wgu_codes": wgu, "wgu_scales": None, "wd_codes": wd, "wd_scales": None}
+
+
+def _run_moe(inp, want_bwd=True, bf16_weights=False):
     import torch
     import orthogonal_fine_tuning_amd as oft
 
     cfg = inp["cfg"]
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
     P = T * k
-    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0)
+    w_fmt = oft.OFT_W_BF16 if bf16_weights else oft.OFT_W_INT4
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=w_fmt)
     rtt = _routing_tensors(T, E, k)
     rt = oft.moe_routing(**rtt)
     nblk = E * cfg.nblk_e
     Rf = torch.empty((E, cfg.nblk_e, b, b), dtype=torch.float32, device="cuda")
     Rops = torch.empty((E, cfg.nblk_e, 2, b, b), dtype=torch.int16, device="cuda")
     oft.cayley_build(dev(inp["p"]), nblk, b, Rf, Rops)
-    W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
+    if bf16_weights:
+        W = _bf16_weights(inp)
+    else:
+        W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
     hs = torch.empty((max(P, 1), 2 * I), dtype=torch.int16, device="cuda")
     y = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
     nbf = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
@@ -159,6 +177,33 @@ def test_moe_parity_small(name):
     print(f"  err y={e_y:.2e} h={e_h:.2e} dx={e_dx:.2e} dq={e_dq:.2e} dw={e_dw:.2e}", flush=True)
     assert max(e_y, e_h, e_dx, e_dq, e_dw) <= TOL
     assert np.all(host(out["dq"])[1] == 0.0)  # inactive expert
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_moe_bf16_weights_small(name):
+    """Dequantised bf16 weights (the dense reference the grouped dequant GEMMs
+    are measured against) through the same entry points: the oracle's result;
+    where both formats run the 128-row copy-ring kernels (at least 64 rows per
+    expert on average) the contraction order is the same, so every output
+    equals the INT4 run's bit for bit."""
+    cfg = SMALL[name]
+    print(f"[moe bf16 weights] {name}", flush=True)
+    inp = make_moe(cfg, seed=3)
+    y_ref, H_ref, rt = omoe.forward(inp)
+    dX_ref, dp_ref, dw_ref = omoe.backward(inp, rt)
+    out = _run_moe(inp, bf16_weights=True)
+    P = cfg.T * cfg.k
+    e_y = err(bf16_to_f64(host(out["y"])), y_ref)
+    e_h = err(bf16_to_f64(host(out["hs"])[:P]), H_ref)
+    e_dx = err(bf16_to_f64(host(out["dx"])), dX_ref)
+    e_dq = err(host(out["dq"]), dp_ref)
+    e_dw = err(host(out["dw"]), dw_ref)
+    print(f"  err y={e_y:.2e} h={e_h:.2e} dx={e_dx:.2e} dq={e_dq:.2e} dw={e_dw:.2e}", flush=True)
+    assert max(e_y, e_h, e_dx, e_dq, e_dw) <= TOL
+    if P >= 64 * cfg.E:
+        ref = _run_moe(inp)
+        for key in ("y", "hs", "dx", "dq", "dw"):
+            assert np.array_equal(host(out[key]), host(ref[key])), key
 
 
 def test_moe_deterministic():
