@@ -81,7 +81,8 @@ FWD_KERNEL_SOURCES = ["orthogonal_fine_tuning_amd/csrc/linear_fwd.hip",
                       "orthogonal_fine_tuning_amd/csrc/gemm_nt.h",
                       "orthogonal_fine_tuning_amd/csrc/gemm_nt_dma.h",
                       "orthogonal_fine_tuning_amd/csrc/gemm_skinny.h",
-                      "orthogonal_fine_tuning_amd/csrc/oft_device.h"]
+                      "orthogonal_fine_tuning_amd/csrc/oft_device.h",
+                      "orthogonal_fine_tuning_amd/csrc/oft_formats.h"]
 
 
 def fwd_kernel_name(cfg):

@@ -25,6 +25,8 @@
 //                    written to dH rows (gate half at k, up half at I + k).
 #pragma once
 
+#include <type_traits>
+
 #include "oft_device.h"
 
 namespace oft {
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
   __shared__ float dwred[EPI == EPI_SWIGLU_BWD ? 2 * BM : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g2 = lane >> 5;
   const int wk = wave >> 1, wm = wave & 1;
   const int K = p.K, N = p.N;
@@ -263,7 +265,11 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
 
   // A operand (W^T rows k, contraction n) through the LDS transpose load
   const int G = lane >> 4, li = lane & 15;
-  auto compute = [&](int buf) {
+  // TMV (a std::integral_constant): this wave's 32-row tiles that hold rows
+  // (grouped tiles past an expert's last row skip the rest)
+  auto compute = [&](int buf, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    if constexpr (TMV == 0) return;
     const uint16_t* Ws = smem + buf * STAGE;
     const uint16_t* Bs = Ws + WSZ;
 #pragma unroll
@@ -278,41 +284,56 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
         a[tk] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TMV; ++tm)
         b[tm] = *reinterpret_cast<const bf16x8*>(&Bs[(wm * (BM / 2) + tm * 32 + l32) * LDN + kk * 16 + 8 * g2]);
 #pragma unroll
       for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
+        for (int tm = 0; tm < TMV; ++tm) acc[tk][tm] = mfma32(a[tk], b[tm], acc[tk][tm]);
     }
   };
 
   const int nbeg = p.nsplit_len > 0 ? blockIdx.z * p.nsplit_len : 0;
   const int nend = p.nsplit_len > 0 ? min(N, nbeg + p.nsplit_len) : N;
   const int ns = (nend - nbeg + BNS - 1) / BNS;
-  if constexpr (NBUF == 2) {
-    if (ns > 0) {
-      prefetch(nbeg);
-      stage(0);
-      if (ns > 1) prefetch(nbeg + BNS);
-    }
-    __syncthreads();
-    for (int s = 0; s < ns; ++s) {
-      compute(s & 1);
-      if (s + 1 < ns) stage((s + 1) & 1);
-      if (s + 2 < ns) prefetch(nbeg + (s + 2) * BNS);
+  // every wave stages its share and takes every barrier, whatever its TMV
+  auto run = [&](auto tmv_c) {
+    if constexpr (NBUF == 2) {
+      if (ns > 0) {
+        prefetch(nbeg);
+        stage(0);
+        if (ns > 1) prefetch(nbeg + BNS);
+      }
+      __syncthreads();
+      for (int s = 0; s < ns; ++s) {
+        compute(s & 1, tmv_c);
+        if (s + 1 < ns) stage((s + 1) & 1);
+        if (s + 2 < ns) prefetch(nbeg + (s + 2) * BNS);
+        __syncthreads();
+      }
+    } else {
+      if (ns > 0) prefetch(nbeg);
+      for (int s = 0; s < ns; ++s) {
+        if (s > 0) __syncthreads();
+        stage(0);
+        __syncthreads();
+        if (s + 1 < ns) prefetch(nbeg + (s + 1) * BNS);
+        compute(0, tmv_c);
+      }
       __syncthreads();
     }
+  };
+  if constexpr (GROUPED) {
+    static_assert(TM == 2, "grouped tiles: 128 rows");
+    const int rows_w = nrows - wm * (BM / 2);  // rows of this wave's 64 (uniform)
+    if (rows_w > 32)
+      run(std::integral_constant<int, 2>{});
+    else if (rows_w > 0)
+      run(std::integral_constant<int, 1>{});
+    else
+      run(std::integral_constant<int, 0>{});
   } else {
-    if (ns > 0) prefetch(nbeg);
-    for (int s = 0; s < ns; ++s) {
-      if (s > 0) __syncthreads();
-      stage(0);
-      __syncthreads();
-      if (s + 1 < ns) prefetch(nbeg + (s + 1) * BNS);
-      compute(0);
-    }
-    __syncthreads();
+    run(std::integral_constant<int, TM>{});
   }
 
   // ------------------------------------------------------------ epilogue

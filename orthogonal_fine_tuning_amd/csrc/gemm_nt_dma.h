@@ -15,8 +15,12 @@
 // outputs to the gate waves through LDS.
 //
 // Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 128, 192, 256), K
-// steps of 64.  Wave (wn, wm) = (wave % 4, wave / 4) owns channels
-// 64 wn + [0, 64) and tokens wm BM / 2 + [0, BM / 2).
+// steps of 64.  FP8 and bf16 weights: wave (wn, wm) = (wave % 4, wave / 4)
+// owns channels 64 wn + [0, 64) and tokens wm BM / 2 + [0, BM / 2).  INT4
+// weights on 128-token tiles: wave wn owns channels 32 wn + [0, 32) and every
+// token, so each code row is dequantised by one wave only (with the 4 x 2
+// layout both token halves dequantised it, and on 128-token tiles the
+// dequant, not the matrix cores, set the pace).
 //
 // Everything the main loop reads from HBM travels by global_load_lds (16 or
 // 4 bytes per lane; lane l of an instruction writes LDS bytes [s l, s l + s)
@@ -26,8 +30,9 @@
 //                 word per row holding its fp16 group scale(s) (INT4), or
 //                 x 128 bytes (bf16, laid out like the activations).
 // Each wave copies an eighth of both.  The copies for step s + 2 are issued
-// right after the barrier of step s, so each has two steps of matrix-core
-// work to land; no registers hold data in flight.  The kernel counts its
+// during step s, right after its first group of matrix-core instructions,
+// so each has two steps of matrix-core work to land; no registers hold data
+// in flight.  The kernel counts its
 // copies itself (vmcnt): they are assembly, so the compiler neither waits
 // for them before unrelated LDS reads nor miscounts its own loads around
 // them, and the loop issues no other global loads.  One barrier per step:
@@ -44,13 +49,16 @@
 // weight codes for the whole step are contiguous (32 FP8 or 16 INT4 bytes)
 // and each activation operand is one 16-byte read.
 //
-// LDS layouts: 16-byte chunk c of a row r sits at chunk c ^ h(r), chosen so
-// that the 16-byte operand reads of any 8 consecutive rows hit 8 distinct
-// slots of a 128-byte bank window and those of any 16 rows 16 distinct slots
-// of a 256-byte window: h = (r ^ ((r >> 3) & 1)) & 7 for activation rows (8
-// chunks; bf16 weight rows too), ((r >> 1) ^ (r >> 3)) & 3 for FP8 code
-// rows (4 chunks) and ((r >> 2) ^ (r >> 3)) & 1 for INT4 code rows (2).
+// LDS layouts: 16-byte chunk c of a row r sits at chunk c ^ h(r), with
+// h = (r ^ ((r >> 3) & 1)) & 7 for activation rows (8 chunks; bf16 weight
+// rows too), (r >> 2) & 3 for FP8 code rows (4 chunks) and
+// ((r >> 2) ^ (r >> 3)) & 1 for INT4 code rows (2).  Each was measured free
+// of bank conflicts for the operand reads on gfx950 (bank-conflict counter
+// and read rate of a probe kernel, against contiguous reads); the earlier
+// FP8 choice ((r >> 1) ^ (r >> 3)) & 3 ran at half rate.
 #pragma once
+
+#include <type_traits>
 
 #include "gemm_nt.h"
 
@@ -64,7 +72,7 @@ constexpr int NTHR = 512;
 template <int BM> constexpr int X_BYTES = BM * BK * 2;
 template <int WF> constexpr int W_BYTES = WF == WF_BF16 ? BN * BK * 2 : WF == WF_FP8 ? BN * BK : BN * BK / 2 + BN * 4;
 __device__ __forceinline__ int swz_x(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
-__device__ __forceinline__ int swz_w8(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_w8(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_w4(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 // 16 (or 4) bytes per lane from base + voff to LDS byte address lds + 16 l (4 l)
@@ -95,13 +103,15 @@ __device__ __forceinline__ void wait_copies_barrier() {
   else
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// runtime count (one of 0, 4, 8, 12, 16)
+// runtime count (one of 0, 2, 4, 6, 8, 12, 16; anything else waits for all)
 __device__ __forceinline__ void wait_copies_barrier_n(int n) {
   switch (n) {
     case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
 }
@@ -122,7 +132,14 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   constexpr bool FP8 = WF == WF_FP8;
   constexpr bool W16 = WF == WF_BF16;
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
-  constexpr int TM = BM / 64;  // 32-token tiles per wave
+  // wave layout: INT4 weights on 128-token tiles, 8 waves x 32 channels over
+  // every token of the tile (each code row is dequantised by one wave only);
+  // otherwise 4 x 2 waves of 64 channels x BM / 2 tokens (with 256 tokens
+  // the matrix work per dequantised operand is already large enough)
+  constexpr bool W8 = WF == WF_INT4 && BM == 128;
+  constexpr int TN = W8 ? 1 : 2;              // 32-channel tiles per wave
+  constexpr int TM = W8 ? BM / 32 : BM / 64;  // 32-token tiles per wave
+  constexpr int NWN = W8 ? 8 : 4;             // waves along the channels
   constexpr int XB = X_BYTES<BM>;
   constexpr int WB = W_BYTES<WF>;
   constexpr int XI = BM / 64;        // activation copies per wave and step (8 rows each)
@@ -134,7 +151,9 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 3, wm = wave >> 2;
+  const int wn = W8 ? wave : (wave & 3), wm = W8 ? 0 : (wave >> 2);
+  const int cw0 = W8 ? 32 * wn : 64 * wn;  // this wave's first weight row of the tile
+  const int rw0 = W8 ? 0 : wm * (BM / 2);  // and first token row
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
 
@@ -239,15 +258,15 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   };
 
   // ---- operand reads
-  uint32_t xrd[TM];  // activation row r = wm BM / 2 + 32 tm + l32
+  uint32_t xrd[TM];  // activation row r = rw0 + 32 tm + l32
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) xrd[tm] = (uint32_t)((wm * (BM / 2) + 32 * tm + l32) * 128);
+  for (int tm = 0; tm < TM; ++tm) xrd[tm] = (uint32_t)((rw0 + 32 * tm + l32) * 128);
   const int xsw = swz_x(l32);  // h depends on bits 0..3 of the row only: the same for every tm, wm
   uint32_t wrd[2][2];
   uint32_t srd[2] = {0u, 0u};  // INT4: scale index of the operand row at k = 0
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn) {
-    const int rw = 64 * wn + 32 * tn + l32;
+  for (int tn = 0; tn < TN; ++tn) {
+    const int rw = cw0 + 32 * tn + l32;
     if constexpr (W16) {
       wrd[tn][0] = (uint32_t)(rw * 128);
       wrd[tn][1] = 0u;
@@ -261,22 +280,31 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     }
   }
 
-  f32x16 acc[2][TM];
+  f32x16 acc[TN][TM];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TN; ++a)
 #pragma unroll
     for (int b = 0; b < TM; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  auto compute = [&](int s) {
+  // iss: issue the copies of step s + 2 once the first matrix-core group of
+  // step s is queued, so that a stalled copy issue overlaps matrix work.
+  // TMV (a std::integral_constant): this wave's 32-token tiles that hold
+  // rows; the others are skipped (grouped tiles past an expert's last row).
+  auto compute = [&](int s, bool iss, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
     const int st = s % NST;
     const uint8_t* X = xs + st * XB;
     const uint8_t* W = wsm + st * WB;
-    uint32_t cw[2][8];  // this lane's codes for the step (INT4: words 0..3)
-    I4Scale sc[2];
+    if constexpr (TMV == 0) {
+      if (iss) issue(s + 2);
+      return;
+    }
+    uint32_t cw[TN][8];  // this lane's codes for the step (INT4: words 0..3)
+    I4Scale sc[TN];
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
+    for (int tn = 0; tn < TN; ++tn) {
       if constexpr (W16) {
         // bf16 weight rows are read per MFMA below, like the activations
       } else if constexpr (FP8) {
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       } else {
         const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[tn][0]);
         cw[tn][0] = c0.x; cw[tn][1] = c0.y; cw[tn][2] = c0.z; cw[tn][3] = c0.w;
-        const int rw = 64 * wn + 32 * tn + l32;
+        const int rw = cw0 + 32 * tn + l32;
         const uint32_t word = *reinterpret_cast<const uint32_t*>(W + BN * BK / 2 + rw * 4);
         // this lane's in-features 64 s + 32 g2 .. + 31 lie in group (64 s + 32 g2) / g
         const uint32_t idx = srd[tn] + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
@@ -296,9 +324,9 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[2], b[TM];
+      bf16x8 a[TN], b[TM];
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
+      for (int tn = 0; tn < TN; ++tn) {
         if constexpr (W16) {
           a[tn] = *reinterpret_cast<const bf16x8*>(W + wrd[tn][0] + 16 * ((4 * g2 + kk) ^ xsw));
         } else if constexpr (FP8) {
@@ -309,21 +337,47 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
         }
       }
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TMV; ++tm)
         b[tm] = *reinterpret_cast<const bf16x8*>(X + xrd[tm] + 16 * ((4 * g2 + kk) ^ xsw));
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) acc[tn][tm] = mfma32(a[tn], b[tm], acc[tn][tm]);
+        for (int tm = 0; tm < TMV; ++tm) acc[tn][tm] = mfma32(a[tn], b[tm], acc[tn][tm]);
+      if (kk == 0 && iss) issue(s + 2);
     }
   };
 
-  issue(0);
-  if (nk > 1) issue(1);
-  for (int s = 0; s < nk; ++s) {
-    if (s + 1 < nk) wait_copies_barrier<V>(); else wait_copies_barrier<0>();
-    if (s + 2 < nk) issue(s + 2);
-    compute(s);
+  // every wave runs the same copies and barriers, whatever its TMV
+  auto run = [&](auto tmv_c) {
+    issue(0);
+    if (nk > 1) issue(1);
+    for (int s = 0; s < nk; ++s) {
+      if (s + 1 < nk) wait_copies_barrier<V>(); else wait_copies_barrier<0>();
+      compute(s, s + 2 < nk, tmv_c);
+    }
+  };
+  if constexpr (GROUPED) {
+    static_assert(BM == 128, "grouped tiles: 128 rows");
+    const int rows_w = nrows - rw0;  // rows of this wave's tokens (uniform)
+    if constexpr (TM == 4) {
+      if (rows_w > 96)
+        run(std::integral_constant<int, 4>{});
+      else if (rows_w > 64)
+        run(std::integral_constant<int, 3>{});
+      else if (rows_w > 32)
+        run(std::integral_constant<int, 2>{});
+      else
+        run(std::integral_constant<int, 1>{});
+    } else {
+      if (rows_w > 32)
+        run(std::integral_constant<int, 2>{});
+      else if (rows_w > 0)
+        run(std::integral_constant<int, 1>{});
+      else
+        run(std::integral_constant<int, 0>{});
+    }
+  } else {
+    run(std::integral_constant<int, TM>{});
   }
 
   // ------------------------------------------------------------ epilogue
@@ -331,10 +385,10 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   // on the matrix cores (accumulator registers reused as the B operand),
   // store.  EPI_PLAIN: store the accumulators (bf16 or fp32).
   const float* ws_f = static_cast<const float*>(p.ws);
-  uint32_t swg[SWI ? 2 : 1][SWI ? TM : 1][8];  // EPI_ROT_SWIGLU: this lane's bf16 outputs
+  uint32_t swg[SWI ? TN : 1][SWI ? TM : 1][8];  // EPI_ROT_SWIGLU: this lane's bf16 outputs
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn) {
-    const int nb = chan(64 * wn + 32 * tn);  // first channel of this 32-channel group
+  for (int tn = 0; tn < TN; ++tn) {
+    const int nb = chan(cw0 + 32 * tn);  // first channel of this 32-channel group
     const bool n_ok = nb >= 0;
     float fs[16];
     if constexpr (EPI != EPI_PLAIN && FP8) {
@@ -390,7 +444,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       } else {
         o = acc[tn][tm];
       }
-      const int ml = wm * (BM / 2) + 32 * tm + l32;
+      const int ml = rw0 + 32 * tm + l32;
       const bool m_ok = n_ok && ml < nrows;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -414,30 +468,30 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   }
 
   if constexpr (SWI) {
-    // up waves (wn = 2, 3) hand their bf16 outputs to the gate waves (wn =
-    // 0, 1) holding the same (token, channel) slots; the ring is free once
-    // every wave has passed the barrier
-    static_assert(2 * 2 * 2 * TM * 8 * 64 * 4 <= NST * XB, "exchange buffer");
+    // up waves (the upper half of wn) hand their bf16 outputs to the gate
+    // waves (wn - NWN / 2) holding the same (token, channel) slots; the ring
+    // is free once every wave has passed the barrier
+    static_assert(4 * TN * TM * 8 * 64 * 4 <= NST * XB, "exchange buffer");
     uint32_t* xb = reinterpret_cast<uint32_t*>(xs);
-    const int wg = wn & 1;
+    const int pid = W8 ? (wn % (NWN / 2)) : (wn % (NWN / 2)) * 2 + wm;  // pair slot 0..3
     lds_barrier_plain();
-    if (wn >= 2) {
+    if (wn >= NWN / 2) {
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-          for (int v = 0; v < 8; ++v) xb[((((wg * 2 + wm) * 2 + tn) * TM + tm) * 8 + v) * 64 + lane] = swg[tn][tm][v];
+          for (int v = 0; v < 8; ++v) xb[(((pid * TN + tn) * TM + tm) * 8 + v) * 64 + lane] = swg[tn][tm][v];
     }
     lds_barrier_plain();
-    if (wn < 2) {
+    if (wn < NWN / 2) {
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) {
-        const int cb = chan(64 * wn + 32 * tn);  // gate channel = act column
+      for (int tn = 0; tn < TN; ++tn) {
+        const int cb = chan(cw0 + 32 * tn);  // gate channel = act column
         if (cb < 0) continue;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const int ml = wm * (BM / 2) + 32 * tm + l32;
+          const int ml = rw0 + 32 * tm + l32;
           if (ml >= nrows) continue;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -445,7 +499,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const uint32_t gw = swg[tn][tm][2 * q + h];
-              const uint32_t uw = xb[((((wg * 2 + wm) * 2 + tn) * TM + tm) * 8 + 2 * q + h) * 64 + lane];
+              const uint32_t uw = xb[(((pid * TN + tn) * TM + tm) * 8 + 2 * q + h) * 64 + lane];
 #pragma unroll
               for (int u = 0; u < 2; ++u) {
                 const float gv = bf16_to_f32((uint16_t)(gw >> (16 * u)));
@@ -602,7 +656,10 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
 
-  auto compute = [&](int s2) {
+  // TMV (a std::integral_constant): 32-token tiles that hold rows (1 when
+  // the tile has at most 32 rows: the other tile is skipped)
+  auto compute = [&](int s2, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
     const int s = 2 * s2 + kh;
     if (s >= nk) return;
     const int st = s2 % NST;
@@ -632,22 +689,28 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
         a = as_bf16x8(dq_int4x8(cw[kk], sc));
       }
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
+      for (int tm = 0; tm < TMV; ++tm) {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(X + (32 * tm + l32) * 128 + 16 * ((4 * g2 + kk) ^ xsw));
         acc[tm] = mfma32(a, b, acc[tm]);
       }
     }
   };
 
-  const int pre = nk2 < NST - 1 ? nk2 : NST - 1;
-  for (int s2 = 0; s2 < pre; ++s2) issue(s2);
-  for (int s2 = 0; s2 < nk2; ++s2) {
-    // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight (4 per step)
-    const int ahead = min(NST - 2, nk2 - 1 - s2);
-    wait_copies_barrier_n(4 * ahead);
-    if (s2 + NST - 1 < nk2) issue(s2 + NST - 1);
-    compute(s2);
-  }
+  auto run = [&](auto tmv_c) {
+    const int pre = nk2 < NST - 1 ? nk2 : NST - 1;
+    for (int s2 = 0; s2 < pre; ++s2) issue(s2);
+    for (int s2 = 0; s2 < nk2; ++s2) {
+      // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight (4 per step)
+      const int ahead = min(NST - 2, nk2 - 1 - s2);
+      wait_copies_barrier_n(4 * ahead);
+      if (s2 + NST - 1 < nk2) issue(s2 + NST - 1);
+      compute(s2, tmv_c);
+    }
+  };
+  if (nrows > 32)
+    run(std::integral_constant<int, 2>{});
+  else
+    run(std::integral_constant<int, 1>{});
 
   // the two halves' partial sums: kh = 1 hands over through LDS (the ring
   // is free once every wave has passed the barrier below)

@@ -21,6 +21,7 @@
 //             mask bits below its lane, so positions are stable (expert, then
 //             token).
 #include "gemm_nn.h"
+#include "gemm_nn_dma.h"
 #include "gemm_nt.h"
 #include "gemm_nt_dma.h"
 #include "oft_moe.h"
@@ -665,16 +666,29 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.topk_w = rt.topk_w;
     p.dw_part = dw_part;
     p.P = P;
-    dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    if (w16)
-      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>), grid,
-                         dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_INT4, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>), grid,
-                         dim3(256), 0, st, p);
+    // experts averaging at least 64 rows: the copy-ring NN kernel (faster
+    // there; with fewer rows the two-workgroups-per-CU kernel is)
+    int nkt;  // column tiles = partial sums of dw per position
+    if ((long)d.T * d.k >= 64L * d.E) {
+      dim3 grid((d.I + nnd::BKO - 1) / nnd::BKO, (unsigned)L.max_tiles);
+      if (w16)
+        hipLaunchKernelGGL((gemm_nn_dma_kernel<WF_BF16, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nn_dma_kernel<WF_INT4, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
+      nkt = (d.I + nnd::BKO - 1) / nnd::BKO;
+    } else {
+      dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
+      if (w16)
+        hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>),
+                           grid, dim3(256), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_INT4, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>),
+                           grid, dim3(256), 0, st, p);
+      nkt = (d.I + nn::BKO - 1) / nn::BKO;
+    }
     if (q.dw)
-      hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part,
-                         (d.I + 127) / 128, P, rt.inv_perm, q.dw);
+      hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part, nkt, P,
+                         rt.inv_perm, q.dw);
   }
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
   if (q.dq || (q.dx && d.T > 0))
