@@ -322,9 +322,8 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
         sc[tn] = i4scale((uint16_t)(word >> (16 * (idx & 1))));
       }
     }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a[TN], b[TM];
+    // operands of MFMA group kk: weights (dequantised or read) and tokens
+    auto make_a = [&](int kk, bf16x8* a) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         if constexpr (W16) {
@@ -336,14 +335,27 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
           a[tn] = as_bf16x8(dq_int4x8(cw[tn][kk], sc[tn]));
         }
       }
+    };
+    auto load_b = [&](int kk, bf16x8* b) {
 #pragma unroll
       for (int tm = 0; tm < TMV; ++tm)
         b[tm] = *reinterpret_cast<const bf16x8*>(X + xrd[tm] + 16 * ((4 * g2 + kk) ^ xsw));
+    };
+    // one group ahead: the token reads and the dequant of group kk + 1 are
+    // issued around the matrix instructions of group kk
+    bf16x8 aq[2][TN], bq[2][TMV];
+    load_b(0, bq[0]);
+    make_a(0, aq[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk & 1;
+      if (kk + 1 < 4) load_b(kk + 1, bq[c ^ 1]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-        for (int tm = 0; tm < TMV; ++tm) acc[tn][tm] = mfma32(a[tn], b[tm], acc[tn][tm]);
+        for (int tm = 0; tm < TMV; ++tm) acc[tn][tm] = mfma32(aq[c][tn], bq[c][tm], acc[tn][tm]);
       if (kk == 0 && iss) issue(s + 2);
+      if (kk + 1 < 4) make_a(kk + 1, aq[c ^ 1]);
     }
   };
 
