@@ -17,7 +17,11 @@ launch stream around a burst of back-to-back forward launches right after
 the timed steps (``phases_us`` comes from events around each phase of every
 timed step and also counts the idle time an event boundary adds).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.
+workload.  MoE workloads also report ``transient_bytes`` (peak device memory
+allocated during the timed calls beyond what existed before them) and
+``dense_bf16_reference``: the same fwd + bwd calls on every expert's weights
+dequantised to bf16 beforehand (``--no-dense-ref`` skips it), with the ratio
+of the INT4 path's time to it.
 """
 from __future__ import annotations
 
