@@ -5,7 +5,8 @@
 //              cores; FP8 also multiplies channel n by s_n), rounded to bf16;
 //   PRO_NONE : B' = src.
 // The weight tile [64 n x 128 k] (INT4 or FP8 codes, or bf16 values) is
-// dequantised in registers and stored to LDS in its natural layout (k contiguous, 16-byte stores); the matrix-core
+// dequantised in registers and stored to LDS with k contiguous (16-byte
+// stores; 256-byte rows, chunk c of row n at c ^ 4 (n % 4)); the matrix-core
 // operand, which must run along the contraction n, is read with the gfx950
 // LDS transpose load (ds_read_b64_tr_b16: within each 16-lane group, lane i
 // receives element i % 4 of the 8-byte chunks loaded by lanes 4e + i / 4,
@@ -67,8 +68,8 @@ namespace nn {
 constexpr int BKO = 128;       // output columns per tile
 constexpr int BNS = 64;        // contraction step
 constexpr int LDN = BNS + 8;   // B' rows (n contiguous)
-constexpr int LDW = BKO + 16;  // weight rows (k contiguous); 288-byte stride puts
-                               // the 4 rows of a transpose load on disjoint banks
+constexpr int LDW = BKO;       // weight rows (k contiguous), 256 bytes; 16-byte chunk
+                               // c of row n stored at c ^ 4 (n % 4)
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 __device__ __forceinline__ uint2 ds_read_tr16(const uint16_t* p) {
@@ -192,24 +193,42 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
   auto stage = [&](int buf) {
     uint16_t* Ws = smem + buf * STAGE;
     uint16_t* Bs = Ws + WSZ;
-    // W tile -> LDS, natural layout
-    uint4* dst = reinterpret_cast<uint4*>(&Ws[wrow * LDW + 32 * wq]);
+    // W tile -> LDS: this thread's chunks 4 wq + u (u = 0..3) of row wrow,
+    // chunk c stored at c ^ 4 (wrow % 4); the i-th store writes u = (i + wq)
+    // % 4 (the order measured free of bank conflicts; the plain order ran
+    // at less than half the write rate)
+    uint16_t* wrow_p = Ws + wrow * LDW;
+    const int wx = 4 * (wrow & 3);
+    auto put = [&](int i, uint4 v) {
+      const int c = (4 * wq + ((i + wq) & 3)) ^ wx;
+      *reinterpret_cast<uint4*>(wrow_p + 8 * c) = v;
+    };
+    // rotate four per-lane units by wq: out[i] = in[(i + wq) % 4]
+    auto rot4 = [&](auto* v) {
+      auto t1 = v[0];
+      if (wq & 1) { t1 = v[0]; v[0] = v[1]; v[1] = v[2]; v[2] = v[3]; v[3] = t1; }
+      if (wq & 2) { t1 = v[0]; v[0] = v[2]; v[2] = t1; t1 = v[1]; v[1] = v[3]; v[3] = t1; }
+    };
     if constexpr (W16) {
+      uint4 v[4] = {wr[0], wr[1], wr[2], wr[3]};
+      rot4(v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = wr[i];
+      for (int i = 0; i < 4; ++i) put(i, v[i]);
     } else if constexpr (FP8) {
-      const uint32_t wv[8] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w, wr[1].x, wr[1].y, wr[1].z, wr[1].w};
+      uint2 v[4] = {make_uint2(wr[0].x, wr[0].y), make_uint2(wr[0].z, wr[0].w), make_uint2(wr[1].x, wr[1].y),
+                    make_uint2(wr[1].z, wr[1].w)};
+      rot4(v);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint2 lo = dq_fp8x4(wv[2 * q]), hi = dq_fp8x4(wv[2 * q + 1]);
-        dst[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      for (int i = 0; i < 4; ++i) {
+        const uint2 lo = dq_fp8x4(v[i].x), hi = dq_fp8x4(v[i].y);
+        put(i, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     } else {
       const I4Scale wsc = i4scale(wsb);
-      dst[0] = dq_int4x8(wr[0].x, wsc);
-      dst[1] = dq_int4x8(wr[0].y, wsc);
-      dst[2] = dq_int4x8(wr[0].z, wsc);
-      dst[3] = dq_int4x8(wr[0].w, wsc);
+      uint32_t v[4] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w};
+      rot4(v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) put(i, dq_int4x8(v[i], wsc));
     }
     // prologue -> Bs[m][n]
 #pragma unroll
@@ -279,8 +298,9 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
       for (int tk = 0; tk < 2; ++tk) {
         const int kcol = wk * 64 + tk * 32 + 16 * (G & 1) + 4 * (li & 3);
         const int nrow = kk * 16 + 8 * (G >> 1) + (li >> 2);
-        const uint2 lo = ds_read_tr16(&Ws[nrow * LDW + kcol]);
-        const uint2 hi = ds_read_tr16(&Ws[(nrow + 4) * LDW + kcol]);
+        const int off = nrow * LDW + 8 * ((kcol >> 3) ^ (4 * (nrow & 3))) + (kcol & 7);
+        const uint2 lo = ds_read_tr16(&Ws[off]);
+        const uint2 hi = ds_read_tr16(&Ws[off + 4 * LDW]);
         a[tk] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
 #pragma unroll
