@@ -535,19 +535,23 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 // so two waves share each SIMD and the two halves' partial sums are added
 // in LDS at the end (fixed order).  Same copies, layouts, contraction order
 // and epilogues as above (grouped: tiles of at most 64 expert positions;
-// EPI_ROT_SWIGLU: 64 gate + 64 up channels per tile); four stages, copies
-// issued three 128-wide steps ahead (about 75 KB in flight per workgroup).
+// EPI_ROT_SWIGLU: 64 gate + 64 up channels per tile).  FP8: four stages,
+// copies issued three 128-wide steps ahead; INT4: three stages (75 KB), two
+// workgroups per CU, so that four waves per SIMD hide each other's waits.
+// A tile of at most 32 rows skips the second token tile: its matrix work,
+// and the activation copies of the waves whose rows all lie past row 31.
 namespace ntd {
 constexpr int DEC_BN = 128, DEC_NST = 4, DEC_NTHR = 512;
 template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK / 2 + DEC_BN * 4;
 }  // namespace ntd
 
 template <bool FP8, int B, int EPI = EPI_ROT, bool GROUPED = false>
-__global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p) {
+__global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel(NtArgs p) {
   using namespace ntd;
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
-  constexpr int BMD = 64, TM = 2, NST = DEC_NST;
+  // INT4: three stages (75 KB), two workgroups per CU; FP8: four stages
+  constexpr int BMD = 64, TM = 2, NST = FP8 ? DEC_NST : DEC_NST - 1;
   constexpr int XH = BMD * BK * 2;      // 8 KB: one 64-wide half of a step
   constexpr int WH = DEC_W_HALF<FP8>;   // weight bytes of one half
   constexpr int SB = 2 * XH + 2 * WH;   // stage bytes
@@ -628,17 +632,21 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
   const uint32_t s_lds = base_lds + (uint32_t)(2 * XH + kh * WH + DEC_BN * BK / 2 + 32 * wn * 4);
   auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
 
-  auto issue = [&](int s2) {  // 128-wide step s2, this wave's half
+  // xc: this wave copies its activation rows (waves whose rows are all past
+  // a tile of at most 32 rows skip them; their copy count per step is 2)
+  auto issue = [&](int s2, bool xc) {  // 128-wide step s2, this wave's half
     const int st = s2 % NST;
     int s = 2 * s2 + kh;
     if (s >= nk) s = 2 * s2;
     const uint8_t* xb = xbase + (size_t)s * BK * 2;
-    if constexpr (GROUPED) {
-      copy16v(x_lds + st * SB, xptr[0] + (size_t)s * BK * 2);
-      copy16v(x_lds + st * SB + 1024, xptr[1] + (size_t)s * BK * 2);
-    } else {
-      copy16(x_lds + st * SB, xb, xoff[0]);
-      copy16(x_lds + st * SB + 1024, xb, xoff[1]);
+    if (xc) {
+      if constexpr (GROUPED) {
+        copy16v(x_lds + st * SB, xptr[0] + (size_t)s * BK * 2);
+        copy16v(x_lds + st * SB + 1024, xptr[1] + (size_t)s * BK * 2);
+      } else {
+        copy16(x_lds + st * SB, xb, xoff[0]);
+        copy16(x_lds + st * SB + 1024, xb, xoff[1]);
+      }
     }
     if constexpr (FP8) {
       const uint8_t* wb = wbase + (size_t)s * BK;
@@ -709,13 +717,16 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, 1) void gemm_nt_dec_kernel(NtArgs p)
   };
 
   auto run = [&](auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    const bool xc = TMV == 2 || wn < 2;  // uniform
+    const int per = xc ? 4 : 2;          // copies per step of this wave
     const int pre = nk2 < NST - 1 ? nk2 : NST - 1;
-    for (int s2 = 0; s2 < pre; ++s2) issue(s2);
+    for (int s2 = 0; s2 < pre; ++s2) issue(s2, xc);
     for (int s2 = 0; s2 < nk2; ++s2) {
-      // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight (4 per step)
+      // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight
       const int ahead = min(NST - 2, nk2 - 1 - s2);
-      wait_copies_barrier_n(4 * ahead);
-      if (s2 + NST - 1 < nk2) issue(s2 + NST - 1);
+      wait_copies_barrier_n(per * ahead);
+      if (s2 + NST - 1 < nk2) issue(s2 + NST - 1, xc);
       compute(s2, tmv_c);
     }
   };
