@@ -342,14 +342,30 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
       }
     }
   }
+  // registers one 64-row step ahead: the dz operand rows (f) and the dH / H
+  // rows of the cross product (d, y)
+  uint4 f[2], d[2], y[2];
+  auto load = [&](int ms) {
+    if (dz != nullptr) {
+      const int m = ms + 32 * rh + l32;
+      const bool mok = m < m_hi;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        f[t] = mok ? *reinterpret_cast<const uint4*>(dH + (size_t)m * ld + nbr + 16 * t + 8 * g2) : zero4();
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = ms + 2 * rp + h;
+      const bool ok = m < m_hi;
+      d[h] = ok ? *reinterpret_cast<const uint4*>(dH + (size_t)m * ld + n0 + 8 * c) : zero4();
+      y[h] = ok ? *reinterpret_cast<const uint4*>(Hs + (size_t)m * ld + n0 + 8 * c) : zero4();
+    }
+  };
+  if (m_lo < m_hi) load(m_lo);
   for (int ms = m_lo; ms < m_hi; ms += 64) {
     if (dz != nullptr) {
       const int m = ms + 32 * rh + l32;
       const bool mok = m < m_hi;
-      uint4 f[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        f[t] = mok ? *reinterpret_cast<const uint4*>(dH + (size_t)m * ld + nbr + 16 * t + 8 * g2) : zero4();
       f32x16 o;
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[r] = 0.0f;
@@ -362,18 +378,11 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
               make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
       }
     }
-    uint4 d[2], y[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = ms + 2 * rp + h;
-      const bool ok = m < m_hi;
-      d[h] = ok ? *reinterpret_cast<const uint4*>(dH + (size_t)m * ld + n0 + 8 * c) : zero4();
-      y[h] = ok ? *reinterpret_cast<const uint4*>(Hs + (size_t)m * ld + n0 + 8 * c) : zero4();
-    }
     __syncthreads();
     {
       const uint32_t d0[4] = {d[0].x, d[0].y, d[0].z, d[0].w}, d1[4] = {d[1].x, d[1].y, d[1].z, d[1].w};
       const uint32_t y0[4] = {y[0].x, y[0].y, y[0].z, y[0].w}, y1[4] = {y[1].x, y[1].y, y[1].z, y[1].w};
+      if (ms + 64 < m_hi) load(ms + 64);  // in flight during the transposes and MFMAs below
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
