@@ -34,9 +34,6 @@ constexpr int MOE_BM = 128;  // rows (expert positions) per grouped tile
 #define OFT_MOE_NBUF 1
 #endif
 constexpr int MOE_NBUF = OFT_MOE_NBUF;  // LDS buffers of the grouped GEMMs
-#ifndef OFT_MOE_DMA
-#define OFT_MOE_DMA 1
-#endif
 
 // ---------------------------------------------------------------- wave scans
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -532,8 +529,8 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
   // fewer (decode): the weight-streaming copy-ring kernel on 64-row tiles
   // (bf16 reference weights: the 128-row copy-ring kernel at every size)
   const bool w16 = d.wf == WF_BF16;
-  const bool dma = w16 || (OFT_MOE_DMA && (long)d.T * d.k >= 64L * d.E);
-  const bool dec = OFT_MOE_DMA && !dma;
+  const bool dma = w16 || (long)d.T * d.k >= 64L * d.E;
+  const bool dec = !dma;
   const long wb2 = w16 ? 4 : 1;  // bytes per two weights
   int* list64 = reinterpret_cast<int*>(ws + L.list64);
   int* ntiles64 = reinterpret_cast<int*>(ws + L.ntiles64);
@@ -570,15 +567,11 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
-    } else if (dec) {
+    } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.I + ntd::DEC_BN / 2 - 1) / (ntd::DEC_BN / 2), (unsigned)L.max_tiles64);
       hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-    } else {
-      dim3 grid(d.I / 64, (unsigned)L.max_tiles);
-      hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_ROT_SWIGLU, true, false, MOE_NBUF>), grid,
-                         dim3(256), 0, st, p);
     }
   }
   {
@@ -610,15 +603,11 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
-    } else if (dec) {
+    } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.H + ntd::DEC_BN - 1) / ntd::DEC_BN, (unsigned)L.max_tiles64);
       hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-    } else {
-      dim3 grid((d.H + nt::BN - 1) / nt::BN, (unsigned)L.max_tiles);
-      hipLaunchKernelGGL((gemm_nt_kernel<MOE_BM, false, false, B, EPI_PLAIN, true, false, MOE_NBUF>), grid, dim3(256),
-                         0, st, p);
     }
   }
   const size_t n8 = (size_t)d.T * d.H / 8;
