@@ -122,9 +122,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 }  // namespace ntd
 
-template <int WF, int B, int BM, int EPI, bool OUTF32, bool GROUPED = false>
+template <int WF, int B, int BM, int EPI, bool OUTF32, bool GROUPED = false, int KB = 64>
 __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   using namespace ntd;
+  static_assert(KB == 64 || (KB == 128 && WF == WF_FP8 && BM <= 192 && !GROUPED), "128-wide K steps: FP8, <= 192 tokens");
   static_assert(BM == 128 || BM == 192 || BM == 256, "tile");
   static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
@@ -140,13 +141,21 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   constexpr int TN = W8 ? 1 : 2;              // 32-channel tiles per wave
   constexpr int TM = W8 ? BM / 32 : BM / 64;  // 32-token tiles per wave
   constexpr int NWN = W8 ? 8 : 4;             // waves along the channels
-  constexpr int XB = X_BYTES<BM>;
-  constexpr int WB = W_BYTES<WF>;
-  constexpr int XI = BM / 64;        // activation copies per wave and step (8 rows each)
-  constexpr int WI = W16 ? 4 : 2;    // weight copies per wave and step
-  constexpr int V = XI + WI;         // copies per wave and step
-  __shared__ __attribute__((aligned(16))) uint8_t xs[NST * XB];
-  __shared__ __attribute__((aligned(16))) uint8_t wsm[NST * WB];
+  // K steps of KB in-features: 64 (three stages, copies two steps ahead) or
+  // 128 (FP8 on 128- or 192-token tiles: two stages of 64 or 80 KB, copies
+  // one step ahead, half the barriers)
+  constexpr int NSTK = KB == 128 ? 2 : NST;
+  constexpr int LA = NSTK - 1;               // copy lookahead in steps
+  constexpr int XROW = KB * 2;               // activation row bytes per step
+  constexpr int XB = BM * XROW;
+  constexpr int WB = KB == 128 ? BN * KB : W_BYTES<WF>;
+  constexpr int XI = XB / 8 / 1024;          // activation copies per wave and step
+  constexpr int WI = W16 ? 4 : FP8 ? KB / 32 : 2;  // weight copies per wave and step
+  constexpr int V = XI + WI;                 // copies per wave and step
+  constexpr int NKK = KB / 16;               // MFMA groups per step
+  static_assert(NSTK * (XB + WB) <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NSTK * XB];
+  __shared__ __attribute__((aligned(16))) uint8_t wsm[NSTK * WB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   };
   // copy source row: invalid rows copy the workgroup's first row (never stored)
   auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
-  const int nk = K / BK;
+  const int nk = K / KB;
   const int kg = WF == WF_INT4 ? K / p.g : 1;  // INT4 scales per row
   const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;  // INT4: log2(64 / g)
 
@@ -195,16 +204,17 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   const uint8_t* xptr[GROUPED ? XI : 1];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
-    const int r = (BM / 8) * wave + 8 * i + (lane >> 3);
+    // one copy = 1 KB: 8 rows of 128 bytes (KB = 64) or 4 rows of 256 bytes
+    const int r = KB == 128 ? (BM / 8) * wave + 4 * i + (lane >> 4) : (BM / 8) * wave + 8 * i + (lane >> 3);
     const int rr = r < nrows ? r : 0;  // rows past the end copy row 0; never stored
-    const int chunk = 16 * ((lane & 7) ^ swz_x(r));
+    const int chunk = KB == 128 ? 16 * ((lane & 15) ^ (r & 15)) : 16 * ((lane & 7) ^ swz_x(r));
     xoff[i] = (uint32_t)(rr * p.lda * 2 + chunk);
     if constexpr (GROUPED) {
       const long src = p.kslots > 0 ? (long)(p.perm[pos0 + rr] / p.kslots) : (long)(pos0 + rr);
       xptr[i] = static_cast<const uint8_t*>(p.a) + src * p.lda * 2 + chunk;
     }
   }
-  const uint32_t x_lds = lds_addr(xs) + (uint32_t)((BM / 8) * wave * 128);
+  const uint32_t x_lds = lds_addr(xs) + (uint32_t)((BM / 8) * wave * XROW);
 
   // weights: per-lane 32-bit offsets from the row of channel cbase
   const uint8_t* wbase = wc + (W16 ? (size_t)cbase * K * 2 : FP8 ? (size_t)cbase * K : (size_t)cbase * (K / 2));
@@ -218,27 +228,32 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     }
   } else if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rw = 32 * wave + 16 * i + (lane >> 2);
-      woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 3) ^ swz_w8(rw)));
+    for (int i = 0; i < WI; ++i) {
+      if constexpr (KB == 128) {  // 128-byte rows, chunk c at c ^ ((r >> 1) & 7)
+        const int rw = 32 * wave + 8 * i + (lane >> 3);
+        woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 7) ^ ((rw >> 1) & 7)));
+      } else {
+        const int rw = 32 * wave + 16 * i + (lane >> 2);
+        woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 3) ^ swz_w8(rw)));
+      }
     }
   } else {
     const int rw = 32 * wave + (lane >> 1);
     woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
     sbase = (uint32_t)((cbase + crow(32 * wave + l32)) * kg);
   }
-  const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(32 * wave * (W16 ? 128 : FP8 ? 64 : 32));
+  const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(32 * wave * (W16 ? 128 : FP8 ? KB : 32));
   const uint32_t s_lds = lds_addr(wsm) + (uint32_t)(BN * BK / 2 + 32 * wave * 4);
   // first scale of step s: (64 s) / g
   auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
 
   auto issue = [&](int s) {
-    const int st = s % NST;
-    const uint8_t* xb = xbase + (size_t)s * BK * 2;
+    const int st = s % NSTK;
+    const uint8_t* xb = xbase + (size_t)s * XROW;
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       if constexpr (GROUPED)
-        copy16v(x_lds + st * XB + i * 1024, xptr[i] + (size_t)s * BK * 2);
+        copy16v(x_lds + st * XB + i * 1024, xptr[i] + (size_t)s * XROW);
       else
         copy16(x_lds + st * XB + i * 1024, xb, xoff[i]);
     }
@@ -247,9 +262,9 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) copy16(w_lds + st * WB + i * 1024, wb, woff[i]);
     } else if constexpr (FP8) {
-      const uint8_t* wb = wbase + (size_t)s * BK;
-      copy16(w_lds + st * WB, wb, woff[0]);
-      copy16(w_lds + st * WB + 1024, wb, woff[1]);
+      const uint8_t* wb = wbase + (size_t)s * KB;
+#pragma unroll
+      for (int i = 0; i < WI; ++i) copy16(w_lds + st * WB + i * 1024, wb, woff[i]);
     } else {
       copy16(w_lds + st * WB, wbase + (size_t)s * (BK / 2), woff[0]);
       // lanes 0..31: the 4-byte word holding the step's scale(s) of row 32 wave + lane
@@ -260,9 +275,11 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   // ---- operand reads
   uint32_t xrd[TM];  // activation row r = rw0 + 32 tm + l32
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) xrd[tm] = (uint32_t)((rw0 + 32 * tm + l32) * 128);
-  const int xsw = swz_x(l32);  // h depends on bits 0..3 of the row only: the same for every tm, wm
-  uint32_t wrd[2][2];
+  for (int tm = 0; tm < TM; ++tm) xrd[tm] = (uint32_t)((rw0 + 32 * tm + l32) * XROW);
+  // the swizzle depends on bits 0..3 of the row only: the same for every tm, wm
+  const int xsw = KB == 128 ? (l32 & 15) : swz_x(l32);
+  const int xg = KB == 128 ? 8 * g2 : 4 * g2;  // first chunk of this lane group's in-features
+  uint32_t wrd[2][4];
   uint32_t srd[2] = {0u, 0u};  // INT4: scale index of the operand row at k = 0
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
@@ -272,7 +289,9 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       wrd[tn][1] = 0u;
     } else if constexpr (FP8) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) wrd[tn][j] = (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
+      for (int j = 0; j < KB / 32; ++j)
+        wrd[tn][j] = KB == 128 ? (uint32_t)(rw * 128 + 16 * ((4 * g2 + j) ^ ((rw >> 1) & 7)))
+                               : (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
     } else {
       wrd[tn][0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
       wrd[tn][1] = 0u;
@@ -294,24 +313,25 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   // rows; the others are skipped (grouped tiles past an expert's last row).
   auto compute = [&](int s, bool iss, auto tmv_c) {
     constexpr int TMV = decltype(tmv_c)::value;
-    const int st = s % NST;
+    const int st = s % NSTK;
     const uint8_t* X = xs + st * XB;
     const uint8_t* W = wsm + st * WB;
     if constexpr (TMV == 0) {
-      if (iss) issue(s + 2);
+      if (iss) issue(s + LA);
       return;
     }
-    uint32_t cw[TN][8];  // this lane's codes for the step (INT4: words 0..3)
+    uint32_t cw[TN][KB / 4];  // this lane's codes for the step (INT4: words 0..3)
     I4Scale sc[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       if constexpr (W16) {
         // bf16 weight rows are read per MFMA below, like the activations
       } else if constexpr (FP8) {
-        const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[tn][0]);
-        const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[tn][1]);
-        cw[tn][0] = c0.x; cw[tn][1] = c0.y; cw[tn][2] = c0.z; cw[tn][3] = c0.w;
-        cw[tn][4] = c1.x; cw[tn][5] = c1.y; cw[tn][6] = c1.z; cw[tn][7] = c1.w;
+#pragma unroll
+        for (int j = 0; j < KB / 32; ++j) {
+          const uint4 c = *reinterpret_cast<const uint4*>(W + wrd[tn][j]);
+          cw[tn][4 * j] = c.x; cw[tn][4 * j + 1] = c.y; cw[tn][4 * j + 2] = c.z; cw[tn][4 * j + 3] = c.w;
+        }
       } else {
         const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[tn][0]);
         cw[tn][0] = c0.x; cw[tn][1] = c0.y; cw[tn][2] = c0.z; cw[tn][3] = c0.w;
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         if constexpr (W16) {
-          a[tn] = *reinterpret_cast<const bf16x8*>(W + wrd[tn][0] + 16 * ((4 * g2 + kk) ^ xsw));
+          a[tn] = *reinterpret_cast<const bf16x8*>(W + wrd[tn][0] + 16 * ((xg + kk) ^ xsw));
         } else if constexpr (FP8) {
           const uint2 lo = dq_fp8x4(cw[tn][2 * kk]), hi = dq_fp8x4(cw[tn][2 * kk + 1]);
           a[tn] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -339,7 +359,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     auto load_b = [&](int kk, bf16x8* b) {
 #pragma unroll
       for (int tm = 0; tm < TMV; ++tm)
-        b[tm] = *reinterpret_cast<const bf16x8*>(X + xrd[tm] + 16 * ((4 * g2 + kk) ^ xsw));
+        b[tm] = *reinterpret_cast<const bf16x8*>(X + xrd[tm] + 16 * ((xg + kk) ^ xsw));
     };
     // one group ahead: the token reads and the dequant of group kk + 1 are
     // issued around the matrix instructions of group kk
@@ -347,25 +367,30 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     load_b(0, bq[0]);
     make_a(0, aq[0]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
       const int c = kk & 1;
-      if (kk + 1 < 4) load_b(kk + 1, bq[c ^ 1]);
+      if (kk + 1 < NKK) load_b(kk + 1, bq[c ^ 1]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int tm = 0; tm < TMV; ++tm) acc[tn][tm] = mfma32(aq[c][tn], bq[c][tm], acc[tn][tm]);
-      if (kk == 0 && iss) issue(s + 2);
-      if (kk + 1 < 4) make_a(kk + 1, aq[c ^ 1]);
+      if (kk == 0 && iss) issue(s + LA);
+      if (kk + 1 < NKK) make_a(kk + 1, aq[c ^ 1]);
     }
   };
 
   // every wave runs the same copies and barriers, whatever its TMV
   auto run = [&](auto tmv_c) {
     issue(0);
-    if (nk > 1) issue(1);
+    if (LA > 1 && nk > 1) issue(1);
     for (int s = 0; s < nk; ++s) {
-      if (s + 1 < nk) wait_copies_barrier<V>(); else wait_copies_barrier<0>();
-      compute(s, s + 2 < nk, tmv_c);
+      // copies of steps s + 1 .. s + LA - 1 may stay in flight
+      if constexpr (LA > 1) {
+        if (s + 1 < nk) wait_copies_barrier<V>(); else wait_copies_barrier<0>();
+      } else {
+        wait_copies_barrier<0>();
+      }
+      compute(s, s + LA < nk, tmv_c);
     }
   };
   if constexpr (GROUPED) {
@@ -483,7 +508,7 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
     // up waves (the upper half of wn) hand their bf16 outputs to the gate
     // waves (wn - NWN / 2) holding the same (token, channel) slots; the ring
     // is free once every wave has passed the barrier
-    static_assert(4 * TN * TM * 8 * 64 * 4 <= NST * XB, "exchange buffer");
+    static_assert(4 * TN * TM * 8 * 64 * 4 <= NSTK * XB, "exchange buffer");
     uint32_t* xb = reinterpret_cast<uint32_t*>(xs);
     const int pid = W8 ? (wn % (NWN / 2)) : (wn % (NWN / 2)) * 2 + wm;  // pair slot 0..3
     lds_barrier_plain();

@@ -98,9 +98,15 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       if (bm == 256)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI_ROT, false>), dim3(nt, (a.M + 255) / 256),
                            dim3(ntd::NTHR), 0, st, p);
+      else if (bm == 192 && FP8 && a.K % 128 == 0)  // FP8: 128-wide K steps
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, B, 192, EPI_ROT, false, false, 128>),
+                           dim3(nt, (a.M + 191) / 192), dim3(ntd::NTHR), 0, st, p);
       else if (bm == 192)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 192, EPI_ROT, false>), dim3(nt, (a.M + 191) / 192),
                            dim3(ntd::NTHR), 0, st, p);
+      else if (FP8 && a.K % 128 == 0)
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, B, 128, EPI_ROT, false, false, 128>),
+                           dim3(nt, (a.M + 127) / 128), dim3(ntd::NTHR), 0, st, p);
       else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI_ROT, false>), dim3(nt, (a.M + 127) / 128),
                            dim3(ntd::NTHR), 0, st, p);

@@ -178,12 +178,17 @@ def test_deterministic_bitwise():
         assert np.array_equal(host(a[k]), host(b[k])), k
 
 
-@pytest.mark.parametrize("name", ["qkv_4b", "gateup_4b_train", "gateup_4b_decode"])
+# the QKV layer at 3072 tokens: the forward picks 192-token tiles (128-wide
+# K steps at that tile size) and dX 128-token tiles
+FULL_EXTRA = {"qkv_3072": CONFIGS["qkv_4b"].with_(name="qkv_3072", M=3072)}
+
+
+@pytest.mark.parametrize("name", ["qkv_4b", "gateup_4b_train", "gateup_4b_decode", "qkv_3072"])
 def test_dense_full_size_sampled(name):
     """Full workload shapes in the launch configuration the benchmark times;
     the oracle checks sampled token rows of y and dX and sampled adapter
     blocks of dQ (each block's reduction runs over every token)."""
-    cfg = CONFIGS[name]
+    cfg = FULL_EXTRA[name] if name in FULL_EXTRA else CONFIGS[name]
     print(f"[dense full size] {name}: M={cfg.M} K={cfg.K} N={cfg.N}", flush=True)
     inp = make_dense(cfg, seed=0)
     out = _run_gpu(inp)
