@@ -247,29 +247,31 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
   // first scale of step s: (64 s) / g
   auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
 
-  auto issue = [&](int s) {
+  // copy c (0 .. V - 1) of step s: activations first, then weights
+  auto copy_one = [&](int s, int c) {
     const int st = s % NSTK;
-    const uint8_t* xb = xbase + (size_t)s * XROW;
-#pragma unroll
-    for (int i = 0; i < XI; ++i) {
+    if (c < XI) {
       if constexpr (GROUPED)
-        copy16v(x_lds + st * XB + i * 1024, xptr[i] + (size_t)s * XROW);
+        copy16v(x_lds + st * XB + c * 1024, xptr[c] + (size_t)s * XROW);
       else
-        copy16(x_lds + st * XB + i * 1024, xb, xoff[i]);
+        copy16(x_lds + st * XB + c * 1024, xbase + (size_t)s * XROW, xoff[c]);
+      return;
     }
+    const int i = c - XI;
     if constexpr (W16) {
-      const uint8_t* wb = wbase + (size_t)s * BK * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) copy16(w_lds + st * WB + i * 1024, wb, woff[i]);
+      copy16(w_lds + st * WB + i * 1024, wbase + (size_t)s * BK * 2, woff[i]);
     } else if constexpr (FP8) {
-      const uint8_t* wb = wbase + (size_t)s * KB;
-#pragma unroll
-      for (int i = 0; i < WI; ++i) copy16(w_lds + st * WB + i * 1024, wb, woff[i]);
-    } else {
+      copy16(w_lds + st * WB + i * 1024, wbase + (size_t)s * KB, woff[i]);
+    } else if (i == 0) {
       copy16(w_lds + st * WB, wbase + (size_t)s * (BK / 2), woff[0]);
+    } else {
       // lanes 0..31: the 4-byte word holding the step's scale(s) of row 32 wave + lane
       if (lane < 32) copy4(s_lds + st * WB, ws_h, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
     }
+  };
+  auto issue = [&](int s) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) copy_one(s, c);
   };
 
   // ---- operand reads
@@ -374,7 +376,15 @@ __global__ __launch_bounds__(ntd::NTHR, 1) void gemm_nt_dma_kernel(NtArgs p) {
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int tm = 0; tm < TMV; ++tm) acc[tn][tm] = mfma32(aq[c][tn], bq[c][tm], acc[tn][tm]);
-      if (kk == 0 && iss) issue(s + LA);
+      // the copies of step s + LA: bf16 weights and INT4 on 128-token tiles
+      // spread them over the step's groups, the others issue them after the
+      // first group (each measured faster that way)
+      if (iss) {
+        constexpr bool SPREAD = W16 || W8;
+#pragma unroll
+        for (int cc = 0; cc < V; ++cc)
+          if (SPREAD ? (cc * NKK / V == kk) : kk == 0) copy_one(s + LA, cc);
+      }
       if (kk + 1 < NKK) make_a(kk + 1, aq[c ^ 1]);
     }
   };
