@@ -620,9 +620,6 @@ hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz
     else if (bm == 192)
       hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 192, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 191) / 192),
                          dim3(ntd::NTHR), 0, st, p);
-    else if (a.N % 128 == 0)
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 128, EPI_PLAIN, XF32, false, 128>),
-                         dim3(ntl, (a.M + 127) / 128), dim3(ntd::NTHR), 0, st, p);
     else
       hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 128, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 127) / 128),
                          dim3(ntd::NTHR), 0, st, p);

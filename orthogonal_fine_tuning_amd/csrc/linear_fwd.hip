@@ -104,9 +104,6 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       else if (bm == 192)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 192, EPI_ROT, false>), dim3(nt, (a.M + 191) / 192),
                            dim3(ntd::NTHR), 0, st, p);
-      else if (FP8 && a.K % 128 == 0)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, B, 128, EPI_ROT, false, false, 128>),
-                           dim3(nt, (a.M + 127) / 128), dim3(ntd::NTHR), 0, st, p);
       else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI_ROT, false>), dim3(nt, (a.M + 127) / 128),
                            dim3(ntd::NTHR), 0, st, p);
