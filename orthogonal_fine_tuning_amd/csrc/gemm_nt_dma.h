@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }  // namespace ntd
 
 template <int WF, int B, int BM, int EPI, bool OUTF32, bool GROUPED = false, int KB = 64>
-__global__ __launch_bounds__(ntd::NTHR, (WF == WF_FP8 && BM == 128 && KB == 64 && !GROUPED) ? 2 : 1) void gemm_nt_dma_kernel(
+__global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64) ? 2 : 1) void gemm_nt_dma_kernel(
     NtArgs p) {
   using namespace ntd;
   static_assert(KB == 64 || (KB == 128 && WF == WF_FP8 && BM <= 192 && !GROUPED), "128-wide K steps: FP8, <= 192 tokens");
@@ -144,11 +144,11 @@ __global__ __launch_bounds__(ntd::NTHR, (WF == WF_FP8 && BM == 128 && KB == 64 &
   constexpr int NWN = W8 ? 8 : 4;             // waves along the channels
   // K steps of KB in-features: 64 (three stages, copies two steps ahead) or
   // 128 (FP8 on 192-token tiles: two stages of 80 KB, copies one step ahead,
-  // half the barriers).  FP8 on 128-token tiles: 64-wide steps on two
-  // stages (64 KB), so that two workgroups share a CU and their barriers
-  // do not stall each other (measured faster than one workgroup with
-  // 128-wide steps)
-  constexpr bool TWO = WF == WF_FP8 && BM == 128 && KB == 64 && !GROUPED;
+  // half the barriers).  128-token tiles run two workgroups per CU, so that
+  // one's barrier waits are covered by the other's matrix work: INT4 fits
+  // with three stages (77 KB), FP8 with two stages of 64-wide steps (64 KB;
+  // measured faster than one workgroup with 128-wide steps)
+  constexpr bool TWO = WF == WF_FP8 && BM == 128 && KB == 64;
   constexpr int NSTK = (KB == 128 || TWO) ? 2 : NST;
   constexpr int LA = NSTK - 1;               // copy lookahead in steps
   constexpr int XROW = KB * 2;               // activation row bytes per step

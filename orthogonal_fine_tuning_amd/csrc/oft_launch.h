@@ -14,20 +14,25 @@ void set_last_hip_error(int e);
 
 // compute units of the current device (queried once per device)
 int num_cus();
-// Token tile of gemm_nt_dma_kernel (one workgroup per CU): the candidate
-// with the least estimated time, rounds of workgroups x tile rows / per-tile
-// efficiency (measured relative to 256-token tiles: 0.95 at 192 and 0.88 at
-// 128 tokens).  max_bm limits the choice (bf16 weights: 128).
+// Token tile of gemm_nt_dma_kernel: the candidate with the least estimated
+// time, rounds of workgroups x tile rows x workgroups per CU / per-tile
+// efficiency.  256- and 192-token tiles run one workgroup per CU, 128-token
+// tiles two (FP8 and INT4 weights; measured rates relative to one 256-token
+// tile per CU: 0.95 at 192 tokens, 1.02 for two 128-token tiles).  max_bm
+// limits the choice (bf16 weights: 128, one workgroup per CU at 0.88).
 inline int pick_token_tile(long col_tiles, long M, int cus, int max_bm) {
   const int cand[3] = {256, 192, 128};
-  const double eff[3] = {1.0, 0.95, 0.88};
+  const bool w16 = max_bm < 192;
+  const int per_cu[3] = {1, 1, w16 ? 1 : 2};
+  const double eff[3] = {1.0, 0.95, w16 ? 0.88 : 1.02};
   int best = 128;
   double best_cost = 0.0;
   for (int i = 0; i < 3; ++i) {
     if (cand[i] > max_bm) continue;
     const long tiles = col_tiles * ((M + cand[i] - 1) / cand[i]);
-    const long rounds = (tiles + cus - 1) / cus;
-    const double cost = (double)rounds * cand[i] / eff[i];
+    const long slots = (long)cus * per_cu[i];
+    const long rounds = (tiles + slots - 1) / slots;
+    const double cost = (double)rounds * cand[i] * per_cu[i] / eff[i];
     if (best_cost == 0.0 || cost < best_cost) {
       best = cand[i];
       best_cost = cost;
