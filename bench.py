@@ -21,7 +21,9 @@ workload.  MoE workloads also report ``transient_bytes`` (peak device memory
 allocated during the timed calls beyond what existed before them) and
 ``dense_bf16_reference``: the same fwd + bwd calls on every expert's weights
 dequantised to bf16 beforehand (``--no-dense-ref`` skips it), with the ratio
-of the INT4 path's time to it.
+of the INT4 path's time to it.  ``phases_cold_us`` times fwd and bwd again,
+each right after evicting the last-level cache, so that the weights stream
+from HBM.
 """
 from __future__ import annotations
 
@@ -149,6 +151,35 @@ def cpu_baseline(cfg, inp, rows):
                       f"in fp64 numpy, {reps} repetitions in {dt:.1f} s"}
 
 
+def cold_phases(fwd, bwd, reps=5):
+    """fwd and bwd timed separately (HIP events on the current stream), each
+    right after writing 512 MiB of device memory, twice the 256 MB
+    last-level cache (MALL), so that the weights come from HBM.  Medians in
+    seconds."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    tf, tb = [], []
+    for i in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        flush.fill_(i & 255)
+        ev[0].record(stream)
+        fwd()
+        ev[1].record(stream)
+        flush.fill_((i + 1) & 255)
+        ev[2].record(stream)
+        bwd()
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        tf.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        tb.append(ev[2].elapsed_time(ev[3]) * 1e-3)
+    del flush
+    torch.cuda.empty_cache()
+    return float(np.median(tf)), float(np.median(tb))
+
+
 def moe_flops(cfg):
     P, H, I, b = cfg.T * cfg.k, cfg.H, cfg.I, cfg.b
     gemm = 2 * P * H * 2 * I + 2 * P * I * H
@@ -261,6 +292,14 @@ def run_moe(cfg, args):
                         "hbm_frac": round((by_fwd + by_bwd) / (t_fwd + t_bwd) / 1e9 / PEAK_HBM_GBS, 4)},
     }
     out["transient_bytes"] = int(transient)
+    cf, cb = cold_phases(
+        lambda: oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"],
+                                        Rops, rt, hs, y, wsf, nbf, stream=sp),
+        lambda: oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"],
+                                        W["wd_scales"], Rf, Rops, dx, dq, dw, wsb, nbb, stream=sp))
+    out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
+                             "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
+                             "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
     if not args.no_dense_ref:
         del W
         out["dense_bf16_reference"] = moe_dense_reference(cfg, inp, args, dict(
@@ -474,6 +513,11 @@ def main():
             "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
             "step_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4)},
     }
+    cf, cb = cold_phases(lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp),
+                         lambda: oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp))
+    out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
+                             "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
+                             "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
     print(json.dumps(out))
