@@ -192,6 +192,73 @@ __global__ __launch_bounds__(256) void dq_partial_kernel(const uint16_t* __restr
   }
 }
 
+// Cayley gradient of a group of G = 1024 / B^2 consecutive blocks (one for
+// B = 32, four for B = 16), the formula of dq stage 2 below.  Each of the 256
+// threads owns four adjacent outputs of one block row, so every global load
+// of the group is in flight at once; load_s(g, r, c) returns S[r][c .. c + 3]
+// of block g.  lds holds 3 G B (B + 4) floats; nb <= G blocks are valid.
+template <int B, class LoadS>
+__device__ __forceinline__ void cayley_grad_group(float* lds, const float* __restrict__ Rg,
+                                                  float* __restrict__ dqg, int nb, int tid, LoadS load_s) {
+  constexpr int G = 1024 / (B * B), P = B + 4, BQ = B / 4, BS = B * P;
+  constexpr int NP = B * (B - 1) / 2;
+  const int g = tid / (B * BQ), r = (tid / BQ) % B, c = 4 * (tid % BQ);
+  const bool ok = g < nb;
+  float* S = lds + g * BS;               // S, later Gq
+  float* Rm = lds + G * BS + g * BS;     // R
+  float* T1 = lds + 2 * G * BS + g * BS;  // S (I + R)
+  float4 rv = make_float4(0.f, 0.f, 0.f, 0.f), sv = rv;
+  if (ok) {
+    rv = *reinterpret_cast<const float4*>(Rg + (size_t)g * B * B + r * B + c);
+    sv = load_s(g, r, c);
+  }
+  *reinterpret_cast<float4*>(Rm + r * P + c) = rv;
+  *reinterpret_cast<float4*>(S + r * P + c) = sv;
+  __syncthreads();
+  float4 t = sv;  // T1 = S + S R
+#pragma unroll
+  for (int i = 0; i < B; i += 4) {
+    const float4 sr = *reinterpret_cast<const float4*>(S + r * P + i);
+    const float sk[4] = {sr.x, sr.y, sr.z, sr.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 rr = *reinterpret_cast<const float4*>(Rm + (i + j) * P + c);
+      t.x += sk[j] * rr.x;
+      t.y += sk[j] * rr.y;
+      t.z += sk[j] * rr.z;
+      t.w += sk[j] * rr.w;
+    }
+  }
+  *reinterpret_cast<float4*>(T1 + r * P + c) = t;
+  __syncthreads();
+  float4 q = t;  // Gq = (T1 + R^T T1) / 2
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    const float ri = Rm[i * P + r];
+    const float4 tt = *reinterpret_cast<const float4*>(T1 + i * P + c);
+    q.x += ri * tt.x;
+    q.y += ri * tt.y;
+    q.z += ri * tt.z;
+    q.w += ri * tt.w;
+  }
+  // S is no longer read (its last reads precede the barrier above)
+  *reinterpret_cast<float4*>(S + r * P + c) = make_float4(0.5f * q.x, 0.5f * q.y, 0.5f * q.z, 0.5f * q.w);
+  __syncthreads();
+  for (int e = tid; e < G * NP; e += 256) {
+    const int gb = e / NP;
+    if (gb >= nb) break;
+    // invert the row-major upper-triangle index
+    int i = 0, rem = e - gb * NP;
+    while (rem >= B - 1 - i) {
+      rem -= B - 1 - i;
+      ++i;
+    }
+    const int l = i + 1 + rem;
+    const float* Q = lds + gb * BS;
+    dqg[e] = Q[i * P + l] - Q[l * P + i];
+  }
+}
+
 // ---------------------------------------------------------------- dq stage 1, bf16 Y
 // The same partial cross products (and rotated copy dz) for bf16 Y, shaped
 // for bandwidth: the 64-token x 64-channel tiles of dY and Y travel by
@@ -214,7 +281,8 @@ __global__ __launch_bounds__(256, 2) void dq_dma_kernel(const uint16_t* __restri
                                                         float* __restrict__ part, int M, int N, int rows_per_split,
                                                         int ng32, const uint16_t* __restrict__ Rops,
                                                         const float* __restrict__ fp8_scale,
-                                                        uint16_t* __restrict__ dz) {
+                                                        uint16_t* __restrict__ dz, const float* __restrict__ Rf,
+                                                        float* __restrict__ dq) {
   using namespace ntd;
   constexpr int ST = 64 * 128;  // bytes per tile
   __shared__ __attribute__((aligned(16))) uint8_t tiles[3][2][ST];  // [stage][dY, Y][m][n]
@@ -399,16 +467,42 @@ __global__ __launch_bounds__(256, 2) void dq_dma_kernel(const uint16_t* __restri
     for (int r = 0; r < 16; ++r) red[grp][lane][r] = acc[r];
   }
   __syncthreads();
-  if (kh == 0) {
-    const int g32 = n0 / 32 + grp;
-    if (g32 < ng32) {
-      float* dst = part + ((size_t)split * ng32 + g32) * 1024;
+  if (dq == nullptr) {
+    if (kh == 0) {
+      const int g32 = n0 / 32 + grp;
+      if (g32 < ng32) {
+        float* dst = part + ((size_t)split * ng32 + g32) * 1024;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (r / 4) * 8 + 4 * g2 + (r % 4);
-        dst[row * 32 + l32] = acc[r] + red[grp][lane][r];
+        for (int r = 0; r < 16; ++r) {
+          const int row = (r / 4) * 8 + 4 * g2 + (r % 4);
+          dst[row * 32 + l32] = acc[r] + red[grp][lane][r];
+        }
       }
     }
+    return;
+  }
+  // one slice (few tokens): the workgroup holds the whole S of its 64
+  // channels and finishes their blocks itself (the tiles are free now)
+  float(*Sg)[32][33] = reinterpret_cast<float(*)[32][33]>(&tiles[0][0][0]);
+  if (kh == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Sg[grp][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = acc[r] + red[grp][lane][r];
+  }
+  __syncthreads();
+  constexpr int GB = 1024 / (B * B), NP = B * (B - 1) / 2;
+  float* scratch = reinterpret_cast<float*>(&tiles[1][0][0]);  // 32 KB free past Sg
+  const int nblk = N / B;
+#pragma unroll
+  for (int q = 0; q < 64 / (GB * B); ++q) {
+    const int j0 = n0 / B + q * GB;  // first block of the group
+    if (j0 >= nblk) break;          // uniform
+    cayley_grad_group<B>(scratch, Rf + (size_t)j0 * B * B, dq + (size_t)j0 * NP, min(GB, nblk - j0), tid,
+                         [&](int g, int r, int c) {
+                           const int ch = (q * GB + g) * B;  // first channel of the block in the tile
+                           const float* row = &Sg[ch / 32][ch % 32 + r][ch % 32 + c];
+                           return make_float4(row[0], row[1], row[2], row[3]);
+                         });
+    __syncthreads();
   }
 }
 
@@ -417,54 +511,32 @@ __global__ __launch_bounds__(256, 2) void dq_dma_kernel(const uint16_t* __restri
 // R (R^T + I) = I + R the Cayley gradient is
 //   Gq = (R^T + I) S (I + R) / 2,  dp_il = Gq_il - Gq_li.
 template <int B>
-__global__ __launch_bounds__(256) void dq_final_kernel(const float* __restrict__ part, int nsplit,
-                                                       int ng32, const float* __restrict__ Rf,
+__global__ __launch_bounds__(256) void dq_final_kernel(const float* __restrict__ part, int nsplit, int ng32,
+                                                       int nblk, const float* __restrict__ Rf,
                                                        float* __restrict__ dq) {
-  __shared__ float S[B][B + 1], Rm[B][B + 1], T1[B][B + 1];
-  const int j = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int g32 = (j * B) / 32, off = (j * B) % 32;
-  for (int e = tid; e < B * B; e += 256) {
-    const int r = e / B, c = e % B;
-    // all slice loads in flight first (nsplit <= 16), then a fixed-order sum
-    float v[16];
+  constexpr int G = 1024 / (B * B);
+  __shared__ __attribute__((aligned(16))) float lds[3 * G * B * (B + 4)];
+  const int j0 = blockIdx.x * G;
+  cayley_grad_group<B>(lds, Rf + (size_t)j0 * B * B, dq + (size_t)j0 * (B * (B - 1) / 2), min(G, nblk - j0),
+                       threadIdx.x, [&](int g, int r, int c) {
+                         const int j = j0 + g, g32 = (j * B) / 32, off = (j * B) % 32;
+                         const float* src = part + (size_t)g32 * 1024 + (off + r) * 32 + off + c;
+                         // every slice load in flight first (nsplit <= 16), then a fixed-order sum
+                         float4 v[16];
 #pragma unroll
-    for (int sp = 0; sp < 16; ++sp)
-      v[sp] = sp < nsplit ? part[((size_t)sp * ng32 + g32) * 1024 + (off + r) * 32 + off + c] : 0.0f;
-    float s = 0.0f;
+                         for (int sp = 0; sp < 16; ++sp)
+                           v[sp] = sp < nsplit ? *reinterpret_cast<const float4*>(src + (size_t)sp * ng32 * 1024)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int sp = 0; sp < 16; ++sp) s += v[sp];
-    S[r][c] = s;
-    Rm[r][c] = Rf[(size_t)j * B * B + e];
-  }
-  __syncthreads();
-  for (int e = tid; e < B * B; e += 256) {  // T1 = S (I + R)
-    const int r = e / B, c = e % B;
-    float s = S[r][c];
-#pragma unroll 8
-    for (int i = 0; i < B; ++i) s += S[r][i] * Rm[i][c];
-    T1[r][c] = s;
-  }
-  __syncthreads();
-  for (int e = tid; e < B * B; e += 256) {  // S = (R^T + I) T1 / 2
-    const int r = e / B, c = e % B;
-    float s = T1[r][c];
-#pragma unroll 8
-    for (int i = 0; i < B; ++i) s += Rm[i][r] * T1[i][c];
-    S[r][c] = 0.5f * s;
-  }
-  __syncthreads();
-  constexpr int NP = B * (B - 1) / 2;
-  for (int pidx = tid; pidx < NP; pidx += 256) {
-    // invert the row-major upper-triangle index
-    int i = 0, rem = pidx;
-    while (rem >= B - 1 - i) {
-      rem -= B - 1 - i;
-      ++i;
-    }
-    const int l = i + 1 + rem;
-    dq[(size_t)j * NP + pidx] = S[i][l] - S[l][i];
-  }
+                         for (int sp = 0; sp < 16; ++sp) {
+                           s.x += v[sp].x;
+                           s.y += v[sp].y;
+                           s.z += v[sp].z;
+                           s.w += v[sp].w;
+                         }
+                         return s;
+                       });
 }
 
 // dx[m][k] = sum_z part[z][m][k] in a fixed order (contraction split)
@@ -705,10 +777,12 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
     dim3 grid((a.N + 63) / 64, p.nsplit);
     const float* s8 = a.fp8 ? static_cast<const float*>(ws) : nullptr;
     float* dq_part = dq != nullptr ? part : nullptr;
+    // one slice: the dq pass finishes the blocks itself (no dq_final launch)
+    float* dq_fused = (dq != nullptr && p.nsplit == 1) ? dq : nullptr;
 #define OFT_DQD(F8, BB)                                                                                   \
   if (!a.xf32 && a.fp8 == F8 && a.b == BB)                                                                \
     hipLaunchKernelGGL((dq_dma_kernel<F8, BB>), grid, dim3(256), 0, st, dy, static_cast<const uint16_t*>(y), \
-                       dq_part, a.M, a.N, p.rows_per_split, p.ng32, Rops, s8, dz);
+                       dq_part, a.M, a.N, p.rows_per_split, p.ng32, Rops, s8, dz, Rf, dq_fused);
     OFT_DQD(false, 32)
     OFT_DQD(false, 16)
     OFT_DQD(true, 32)
@@ -724,12 +798,14 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
     OFT_DQP(true, 16)
 #undef OFT_DQP
   }
-  if (dq != nullptr) {
+  const bool fused = dq != nullptr && p.nsplit == 1 && !a.xf32;
+  if (dq != nullptr && !fused) {
     const int nblk = a.N / a.b;
     if (a.b == 32)
-      hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
+      hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, nblk, Rf, dq);
     else
-      hipLaunchKernelGGL(dq_final_kernel<16>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, Rf, dq);
+      hipLaunchKernelGGL(dq_final_kernel<16>, dim3((nblk + 3) / 4), dim3(256), 0, st, part, p.nsplit, p.ng32,
+                         nblk, Rf, dq);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || dx == nullptr || a.M == 0) return err;
