@@ -5,172 +5,165 @@
 // sub-projection's rotation orthogonal; this library builds each b x b block
 // as R = (I + Q)(I - Q)^-1 = 2 (I - Q)^-1 - I from the skew-symmetric Q.
 //
-// Layout of the solve.  Few blocks (cayley_kernel): one workgroup of 4
-// waves per block, to spread each solve over 4 SIMDs; lane c of each wave
-// owns column c of the augmented matrix [A | I] (2b <= 64 columns) for the
-// b/4 rows of its wave's quarter, in registers.  Each of the b
-// Gauss-Jordan pivot steps publishes the pivot row and pivot column through
-// LDS (ping-pong slots, one barrier per step) and every lane updates its
-// rows.  No pivot search is needed: the symmetric part of A is I, so every
-// pivot is >= 1.
+// Layout of the solve: in-place Gauss-Jordan on A = I - Q with row
+// ownership.  Lane r of a b-lane group holds row r of A in registers, so a
+// wave solves 64 / b blocks at once and a block needs b, not 2b, lanes (the
+// in-place form keeps the growing inverse in the columns already
+// eliminated).  Each pivot step publishes the pivot row through LDS and
+// every lane applies one fused multiply-add per element.  No pivot search is
+// needed: the symmetric part of A is I, so every pivot is >= 1.
+#include <utility>
+
 #include "oft_device.h"
 #include "oft_launch.h"
 
 namespace oft {
 
-template <int B>
-__global__ __launch_bounds__(256) void cayley_kernel(const uint16_t* __restrict__ q, int nblk,
-                                                     float* __restrict__ Rf,
-                                                     uint16_t* __restrict__ Rops) {
-  constexpr int NT = 256;
-  constexpr int RQ = B / 4;  // rows per wave
-  constexpr int NP = B * (B - 1) / 2;
-  __shared__ float qs[NP];
-  __shared__ float prow[2][2 * B];  // pivot row (2b columns)
-  __shared__ float pcol[2][B];      // pivot column (b rows)
-  __shared__ float Rt[B][B + 1];    // result, for coalesced stores
-
-  const int blk = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int c = tid & 63;   // column of [A | I]
-  const int w = tid >> 6;   // row quarter
-  const bool colv = c < 2 * B;
-  for (int i = tid; i < NP; i += NT) qs[i] = bf16_to_f32(q[(size_t)blk * NP + i]);
-  __syncthreads();
-
-  float col[RQ];
-#pragma unroll
-  for (int u = 0; u < RQ; ++u) {
-    const int i = w * RQ + u;
-    float v = 0.0f;
-    if (c < B) {
-      float qic = 0.0f;
-      if (i < c) qic = qs[i * B - i * (i + 1) / 2 + (c - i - 1)];
-      if (i > c) qic = -qs[c * B - c * (c + 1) / 2 + (i - c - 1)];
-      v = (i == c ? 1.0f : 0.0f) - qic;
-    } else if (colv) {
-      v = (i == c - B) ? 1.0f : 0.0f;
-    }
-    col[u] = v;
-  }
-
-  for (int s = 0; s < B; ++s) {
-    const int sl = s & 1;
-    const int ws = s / RQ, us = s % RQ;
-    // publish the pivot row (owned by wave ws) and the pivot column (lane s)
-    if (w == ws && colv) {
-      float v = 0.0f;
-#pragma unroll
-      for (int u = 0; u < RQ; ++u)
-        if (u == us) v = col[u];
-      prow[sl][c] = v;
-    }
-    if (c == s) {
-#pragma unroll
-      for (int u = 0; u < RQ; ++u) pcol[sl][w * RQ + u] = col[u];
-    }
-    __syncthreads();
-    if (colv) {
-      const float ps = prow[sl][c] / prow[sl][s];  // new pivot-row entry of this column
-#pragma unroll
-      for (int u = 0; u < RQ; ++u) {
-        const int i = w * RQ + u;
-        col[u] = (i == s) ? ps : col[u] - pcol[sl][i] * ps;
-      }
-    }
-  }
-
-  // lanes b..2b-1 hold A^-1; R = 2 A^-1 - I
-  if (c >= B && colv) {
-    const int j = c - B;
-#pragma unroll
-    for (int u = 0; u < RQ; ++u) {
-      const int i = w * RQ + u;
-      Rt[i][j] = 2.0f * col[u] - (i == j ? 1.0f : 0.0f);
-    }
-  }
-  __syncthreads();
-  float* Rb = Rf + (size_t)blk * B * B;
-  uint16_t* R0 = Rops ? Rops + (size_t)blk * 2 * B * B : nullptr;
-  for (int e = tid; e < B * B; e += NT) {
-    const int i = e / B, j = e % B;
-    const float v = Rt[i][j];
-    Rb[e] = v;
-    if (R0) {
-      R0[e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);                   // R[i][j]
-      R0[B * B + j * B + i] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);   // R^T[j][i]
-    }
-  }
+// LDS hand-off among the lanes of one wave (the workgroup is one wave): a
+// wavefront-scope release / acquire pair.  The LDS of a wave executes its
+// operations in issue order, so this orders the accesses for the compiler
+// without waiting for the writes to complete.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Many blocks: one wave solves 64 / (2b) blocks, lane c owning the whole
-// column c of [A | I] in registers, the pivot column broadcast through LDS.
+// f(integral_constant<int, S>) for S in order
+template <class F, int... S>
+__device__ __forceinline__ void for_each_index(F& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+
 template <int B>
-__global__ __launch_bounds__(64) void cayley_wave_kernel(const uint16_t* __restrict__ q, int nblk,
-                                                    float* __restrict__ Rf,
-                                                    uint16_t* __restrict__ Rops) {
-  constexpr int LANES = 2 * B;
-  constexpr int PER_WAVE = 64 / LANES;
-  __shared__ float pivcol[PER_WAVE][B];
+__global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__ q, int nblk,
+                                                    float* __restrict__ Rf, uint16_t* __restrict__ Rops) {
+  constexpr int PER = 64 / B;  // blocks per wave
+  constexpr int NP = B * (B - 1) / 2;
+  constexpr int TP = B + 2;  // row pitch (bf16) of the transpose tile
+  // the parameters of the wave's blocks, later the bf16 transpose of R
+  constexpr int STAGE = PER * NP * 4 > PER * B * TP * 2 ? PER * NP * 4 : PER * B * TP * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[STAGE];
+  __shared__ __attribute__((aligned(16))) float prow[PER][B];  // pivot row
+
   const int lane = threadIdx.x;
-  const int sub = lane / LANES;
-  const int c = lane % LANES;
-  const int blk = blockIdx.x * PER_WAVE + sub;
-  const bool valid = blk < nblk;
-  const uint16_t* qb = q + (size_t)(valid ? blk : 0) * (B * (B - 1) / 2);
+  const int sub = lane / B, r = lane % B;
+  const int blk0 = blockIdx.x * PER;
+  const int nv = min(PER, nblk - blk0);  // blocks of this wave
+  const int blk = blk0 + sub;
 
-  float col[B];
+  // parameters: PER consecutive blocks are PER * NP contiguous bf16; every
+  // load of the wave is in flight before the first is used
+  float* qs = reinterpret_cast<float*>(stage);
+  const uint16_t* qw = q + (size_t)blk0 * NP;
+  const int nq = nv * NP;
+  static_assert(NP % 8 == 0, "whole 16-byte chunks per block");
+  if ((reinterpret_cast<uintptr_t>(q) & 15) == 0) {  // then so is every wave's span
+    constexpr int NV = (PER * NP / 8 + 63) / 64;
+    uint4 v[NV];
 #pragma unroll
-  for (int i = 0; i < B; ++i) {
-    float v;
-    if (c < B) {
-      // A[i][c] = delta - Q[i][c]; Q[i][c] = p(i,c) above, -p(c,i) below
-      float qic = 0.0f;
-      if (valid && i < c) qic = bf16_to_f32(qb[i * B - i * (i + 1) / 2 + (c - i - 1)]);
-      if (valid && i > c) qic = -bf16_to_f32(qb[c * B - c * (c + 1) / 2 + (i - c - 1)]);
-      v = (i == c ? 1.0f : 0.0f) - qic;
-    } else {
-      v = (i == c - B) ? 1.0f : 0.0f;
+    for (int k = 0; k < NV; ++k) {
+      const int idx = lane + 64 * k;
+      v[k] = reinterpret_cast<const uint4*>(qw)[min(idx, nq / 8 - 1)];  // clamped: no branch
     }
-    col[i] = v;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int idx = lane + 64 * k;
+      if (8 * idx < nq) {
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          qs[8 * idx + 2 * t] = __uint_as_float(w[t] << 16);
+          qs[8 * idx + 2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+        }
+      }
+    }
+  } else {
+    constexpr int NV = (PER * NP + 63) / 64;
+    uint16_t v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = qw[min(lane + 64 * k, nq - 1)];  // clamped: no branch
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      if (lane + 64 * k < nq) qs[lane + 64 * k] = bf16_to_f32(v[k]);
   }
+  __syncthreads();
 
+  // A[r][c] = delta_rc - Q[r][c], Q[r][c] = p(r, c) above the diagonal and
+  // -p(c, r) below (row-major upper-triangle order of p)
+  float a[B];
+  const float* qb = qs + sub * NP;
 #pragma unroll
-  for (int s = 0; s < B; ++s) {
-    if (c == s) {
-#pragma unroll
-      for (int i = 0; i < B; ++i) pivcol[sub][i] = col[i];
-    }
-    __syncthreads();
-    const float ps = col[s] / pivcol[sub][s];
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      if (i != s) col[i] -= pivcol[sub][i] * ps;
-    }
-    col[s] = ps;
-    __syncthreads();
+  for (int c = 0; c < B; ++c) {
+    const int lo = c < r ? c : r, hi = c < r ? r : c;
+    const float v = (c == r || sub >= nv) ? 0.0f : qb[lo * B - lo * (lo + 1) / 2 + (hi - lo - 1)];
+    a[c] = c == r ? 1.0f : (c > r ? -v : v);
   }
+  __syncthreads();  // stage is reused for the transpose at the end
 
-  if (!valid || c < B) return;
-  const int j = c - B;  // this lane holds column j of A^-1
-  float* Rb = Rf + (size_t)blk * B * B;
+  // one pivot step; the step index is a compile-time constant so that every
+  // a[] access stays a register
+  auto step = [&](auto sc) {
+    constexpr int s = decltype(sc)::value;
+    if (r == s) {
 #pragma unroll
-  for (int i = 0; i < B; ++i) Rb[i * B + j] = 2.0f * col[i] - (i == j ? 1.0f : 0.0f);
-  if (Rops != nullptr) {
-    uint16_t* R0 = Rops + (size_t)blk * 2 * B * B;  // R, row-major
-    uint16_t* R1 = R0 + B * B;                      // R^T, row-major
-    uint32_t packed[B / 2];
-#pragma unroll
-    for (int i = 0; i < B; i += 2) {
-      packed[i / 2] = pack_bf16x2(2.0f * col[i] - (i == j ? 1.0f : 0.0f),
-                                  2.0f * col[i + 1] - (i + 1 == j ? 1.0f : 0.0f));
+      for (int j = 0; j < B; j += 4)
+        *reinterpret_cast<float4*>(&prow[sub][j]) = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
     }
+    wave_sync();
+    float pr[B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) R0[i * B + j] = (uint16_t)(packed[i / 2] >> (16 * (i & 1)));
-    uint4* dst = reinterpret_cast<uint4*>(R1 + j * B);  // row j of R^T = column j of R
+    for (int j = 0; j < B; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(&prow[sub][j]);
+      pr[j] = v.x;
+      pr[j + 1] = v.y;
+      pr[j + 2] = v.z;
+      pr[j + 3] = v.w;
+    }
+    // 1 / pivot: hardware reciprocal and one Newton step
+    const float piv = pr[s];
+    float rp = __builtin_amdgcn_rcpf(piv);
+    rp = fmaf(rp, fmaf(-piv, rp, 1.0f), rp);
+    // pivot row: a_sj / p; other rows: a_rj - (a_rs / p) a_sj; column s of
+    // the inverse: 1 / p on the pivot row, -a_rs / p elsewhere
+    const float f = a[s];
+    const float g = r == s ? 1.0f - rp : f * rp;
 #pragma unroll
-    for (int v = 0; v < B / 8; ++v)
-      dst[v] = make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+    for (int j = 0; j < B; ++j)
+      if (j != s) a[j] = fmaf(-g, pr[j], a[j]);
+    a[s] = r == s ? rp : -g;
+    wave_sync();
+  };
+  for_each_index(step, std::make_integer_sequence<int, B>{});
+
+  // lane r holds row r of A^-1; R = 2 A^-1 - I
+#pragma unroll
+  for (int j = 0; j < B; ++j) a[j] = 2.0f * a[j] - (j == r ? 1.0f : 0.0f);
+  if (sub < nv) {
+    float4* dst = reinterpret_cast<float4*>(Rf + (size_t)blk * B * B + r * B);
+#pragma unroll
+    for (int j = 0; j < B; j += 4) dst[j / 4] = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
+  }
+  if (Rops == nullptr) return;
+  uint32_t pk[B / 2];
+#pragma unroll
+  for (int j = 0; j < B; j += 2) pk[j / 2] = pack_bf16x2(a[j], a[j + 1]);
+  // R^T through LDS: row r of R in, column r of R (row r of R^T) out
+  uint16_t* tt = reinterpret_cast<uint16_t*>(stage) + sub * B * TP;
+#pragma unroll
+  for (int j = 0; j < B; j += 2) *reinterpret_cast<uint32_t*>(tt + r * TP + j) = pk[j / 2];
+  __syncthreads();
+  uint32_t pt[B / 2];
+#pragma unroll
+  for (int j = 0; j < B; j += 2) pt[j / 2] = (uint32_t)tt[j * TP + r] | ((uint32_t)tt[(j + 1) * TP + r] << 16);
+  if (sub < nv) {
+    uint4* r0 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + r * B);  // R, row r
+    uint4* r1 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + B * B + r * B);  // R^T, row r
+#pragma unroll
+    for (int v = 0; v < B / 8; ++v) {
+      r0[v] = make_uint4(pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]);
+      r1[v] = make_uint4(pt[4 * v], pt[4 * v + 1], pt[4 * v + 2], pt[4 * v + 3]);
+    }
   }
 }
 
@@ -199,17 +192,10 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint2* __restric
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st) {
   if (nblk == 0) return hipSuccess;
-  if (nblk < 2048) {
-    if (b == 32)
-      hipLaunchKernelGGL(cayley_kernel<32>, dim3(nblk), dim3(256), 0, st, q, nblk, Rf, Rops);
-    else
-      hipLaunchKernelGGL(cayley_kernel<16>, dim3(nblk), dim3(256), 0, st, q, nblk, Rf, Rops);
-  } else {
-    if (b == 32)
-      hipLaunchKernelGGL(cayley_wave_kernel<32>, dim3(nblk), dim3(64), 0, st, q, nblk, Rf, Rops);
-    else
-      hipLaunchKernelGGL(cayley_wave_kernel<16>, dim3((nblk + 1) / 2), dim3(64), 0, st, q, nblk, Rf, Rops);
-  }
+  if (b == 32)
+    hipLaunchKernelGGL(cayley_kernel<32>, dim3((nblk + 1) / 2), dim3(64), 0, st, q, nblk, Rf, Rops);
+  else
+    hipLaunchKernelGGL(cayley_kernel<16>, dim3((nblk + 3) / 4), dim3(64), 0, st, q, nblk, Rf, Rops);
   return hipGetLastError();
 }
 

@@ -216,12 +216,12 @@ def test_dense_full_size_sampled(name):
 
 @pytest.mark.parametrize("b", [32, 16])
 def test_cayley_many_blocks(b):
-    """Enough blocks for the one-wave-per-block variant of the solve."""
+    """Many blocks, the last wave holding fewer than 64 / b of them."""
     import torch
     import orthogonal_fine_tuning_amd as oft
     from oft_inputs import to_bf16_bits
 
-    nblk = 3000
+    nblk = 3001
     rng = np.random.default_rng(b)
     p = to_bf16_bits(rng.normal(0.0, 0.3, size=(nblk, b * (b - 1) // 2)).astype(np.float32))
     Rf = torch.empty((nblk, b, b), dtype=torch.float32, device="cuda")
