@@ -108,9 +108,12 @@ __device__ __forceinline__ void wait_copies_barrier_n(int n) {
   switch (n) {
     case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
@@ -568,215 +571,18 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   }
 }
 
-// Few tokens (M <= 64): the layer is a weight stream.  Workgroup: 8 waves,
-// 128 channels x 64 tokens; wave (wn, kh) = (wave % 4, wave / 4) owns
-// channels 32 wn + [0, 32), all 64 tokens, and the in-features of every
-// other 64-wide step: a ring stage holds a 128-wide step, kh picks its half,
-// so two waves share each SIMD and the two halves' partial sums are added
-// in LDS at the end (fixed order).  Same copies, layouts, contraction order
-// and epilogues as above (grouped: tiles of at most 64 expert positions;
-// EPI_ROT_SWIGLU: 64 gate + 64 up channels per tile).  FP8: four stages,
-// copies issued three 128-wide steps ahead; INT4: three stages (75 KB), two
-// workgroups per CU, so that four waves per SIMD hide each other's waits.
-// A tile of at most 32 rows skips the second token tile: its matrix work,
-// and the activation copies of the waves whose rows all lie past row 31.
-namespace ntd {
-constexpr int DEC_BN = 128, DEC_NST = 4, DEC_NTHR = 512;
-template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK / 2 + DEC_BN * 4;
-}  // namespace ntd
-
-template <bool FP8, int B, int EPI = EPI_ROT, bool GROUPED = false>
-__global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel(NtArgs p) {
+// Decode kernels' finish: the kh = 1 waves hand their partial sums to the
+// kh = 0 waves through LDS (fixed order), which then run the epilogue: FP8
+// channel scale, bf16, rotation (EPI_ROT*), store; EPI_ROT_SWIGLU passes the
+// up outputs to the gate waves through LDS.  smem: SMEM bytes, free once
+// every wave has passed the first barrier.  nb: first channel of the wave's
+// 32 (-1 past the layer).
+template <bool FP8, int B, int EPI, int TM, int SMEM>
+__device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], uint8_t* smem, int wn, int kh,
+                                           int lane, int nb, int nrows, int pos0, const uint16_t* rops) {
   using namespace ntd;
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
-  // INT4: three stages (75 KB), two workgroups per CU; FP8: four stages
-  constexpr int BMD = 64, TM = 2, NST = FP8 ? DEC_NST : DEC_NST - 1;
-  constexpr int XH = BMD * BK * 2;      // 8 KB: one 64-wide half of a step
-  constexpr int WH = DEC_W_HALF<FP8>;   // weight bytes of one half
-  constexpr int SB = 2 * XH + 2 * WH;   // stage bytes
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * SB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 3, kh = wave >> 2;
   const int l32 = lane & 31, g2 = lane >> 5;
-  const int K = p.K;
-  int e = 0, pos0, nrows;
-  if constexpr (GROUPED) {
-    const int t = blockIdx.y;
-    if (t >= *p.ntiles) return;
-    e = p.tiles[2 * t];
-    pos0 = p.offsets[e] + p.tiles[2 * t + 1];
-    nrows = min(BMD, p.offsets[e + 1] - pos0);
-  } else {
-    pos0 = blockIdx.y * BMD;
-    nrows = min(BMD, p.M - pos0);
-  }
-  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
-  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
-  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
-  // channel of local weight row rw (0..127), or -1 past the layer's channels
-  const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
-  auto chan = [&](int rw) -> int {
-    if constexpr (SWI) {
-      const int c = cbase + (rw & (DEC_BN / 2 - 1));
-      return c < p.half_n ? (rw < DEC_BN / 2 ? c : p.half_n + c) : -1;
-    } else {
-      return cbase + rw < p.N ? cbase + rw : -1;
-    }
-  };
-  auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
-  const int nk = K / BK;          // 64-wide steps
-  const int nk2 = (nk + 1) / 2;   // 128-wide steps
-  const int kg = FP8 ? 1 : K / p.g;
-  const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;
-
-  // copies of wave (wn, kh), for half kh of each step (a missing last half
-  // re-copies the first half: same count, never read):
-  //   activations rows 16 wn .. 16 wn + 15 (two instructions),
-  //   weight rows 32 wn .. 32 wn + 31 (FP8: two instructions; INT4: one,
-  //   plus the rows' scale words on lanes 0..31)
-  const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
-  uint32_t xoff[2];
-  const uint8_t* xptr[GROUPED ? 2 : 1];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * wn + 8 * i + (lane >> 3);
-    const int rr = r < nrows ? r : 0;
-    const int chunk = 16 * ((lane & 7) ^ swz_x(r));
-    xoff[i] = (uint32_t)(rr * p.lda * 2 + chunk);
-    if constexpr (GROUPED) {
-      const long src = p.kslots > 0 ? (long)(p.perm[pos0 + rr] / p.kslots) : (long)(pos0 + rr);
-      xptr[i] = static_cast<const uint8_t*>(p.a) + src * p.lda * 2 + chunk;
-    }
-  }
-  const uint8_t* wbase = wc + (FP8 ? (size_t)cbase * K : (size_t)cbase * (K / 2));
-  uint32_t woff[2] = {0u, 0u};
-  uint32_t sbase = 0;
-  if constexpr (FP8) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int rw = 32 * wn + 16 * i + (lane >> 2);
-      woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 3) ^ swz_w8(rw)));
-    }
-  } else {
-    const int rw = 32 * wn + (lane >> 1);
-    woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
-    sbase = (uint32_t)((cbase + crow(32 * wn + l32)) * kg);
-  }
-  const uint32_t base_lds = lds_addr(smem);
-  const uint32_t x_lds = base_lds + (uint32_t)(kh * XH + 16 * wn * 128);
-  const uint32_t w_lds = base_lds + (uint32_t)(2 * XH + kh * WH + 32 * wn * (FP8 ? 64 : 32));
-  const uint32_t s_lds = base_lds + (uint32_t)(2 * XH + kh * WH + DEC_BN * BK / 2 + 32 * wn * 4);
-  auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
-
-  // xc: this wave copies its activation rows (waves whose rows are all past
-  // a tile of at most 32 rows skip them; their copy count per step is 2)
-  auto issue = [&](int s2, bool xc) {  // 128-wide step s2, this wave's half
-    const int st = s2 % NST;
-    int s = 2 * s2 + kh;
-    if (s >= nk) s = 2 * s2;
-    const uint8_t* xb = xbase + (size_t)s * BK * 2;
-    if (xc) {
-      if constexpr (GROUPED) {
-        copy16v(x_lds + st * SB, xptr[0] + (size_t)s * BK * 2);
-        copy16v(x_lds + st * SB + 1024, xptr[1] + (size_t)s * BK * 2);
-      } else {
-        copy16(x_lds + st * SB, xb, xoff[0]);
-        copy16(x_lds + st * SB + 1024, xb, xoff[1]);
-      }
-    }
-    if constexpr (FP8) {
-      const uint8_t* wb = wbase + (size_t)s * BK;
-      copy16(w_lds + st * SB, wb, woff[0]);
-      copy16(w_lds + st * SB + 1024, wb, woff[1]);
-    } else {
-      copy16(w_lds + st * SB, wbase + (size_t)s * (BK / 2), woff[0]);
-      if (lane < 32) copy4(s_lds + st * SB, ws_h, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
-    }
-  };
-
-  const int rw = 32 * wn + l32;  // this lane's operand row
-  const int xsw = swz_x(l32);
-  uint32_t wrd[2];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) wrd[j] = (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
-  } else {
-    wrd[0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
-    wrd[1] = 0u;
-  }
-  const uint32_t srd = FP8 ? 0u : (uint32_t)((cbase + crow(rw)) * kg);
-
-  f32x16 acc[TM];
-#pragma unroll
-  for (int b = 0; b < TM; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
-
-  // TMV (a std::integral_constant): 32-token tiles that hold rows (1 when
-  // the tile has at most 32 rows: the other tile is skipped)
-  auto compute = [&](int s2, auto tmv_c) {
-    constexpr int TMV = decltype(tmv_c)::value;
-    const int s = 2 * s2 + kh;
-    if (s >= nk) return;
-    const int st = s2 % NST;
-    const uint8_t* X = smem + st * SB + kh * XH;
-    const uint8_t* W = smem + st * SB + 2 * XH + kh * WH;
-    uint32_t cw[8];
-    I4Scale sc;
-    if constexpr (FP8) {
-      const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
-      const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[1]);
-      cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
-      cw[4] = c1.x; cw[5] = c1.y; cw[6] = c1.z; cw[7] = c1.w;
-    } else {
-      const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
-      cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
-      const uint32_t word = *reinterpret_cast<const uint32_t*>(W + DEC_BN * BK / 2 + rw * 4);
-      const uint32_t idx = srd + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
-      sc = i4scale((uint16_t)(word >> (16 * (idx & 1))));
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 a;
-      if constexpr (FP8) {
-        const uint2 lo = dq_fp8x4(cw[2 * kk]), hi = dq_fp8x4(cw[2 * kk + 1]);
-        a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-      } else {
-        a = as_bf16x8(dq_int4x8(cw[kk], sc));
-      }
-#pragma unroll
-      for (int tm = 0; tm < TMV; ++tm) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(X + (32 * tm + l32) * 128 + 16 * ((4 * g2 + kk) ^ xsw));
-        acc[tm] = mfma32(a, b, acc[tm]);
-      }
-    }
-  };
-
-  auto run = [&](auto tmv_c) {
-    constexpr int TMV = decltype(tmv_c)::value;
-    const bool xc = TMV == 2 || wn < 2;  // uniform
-    const int per = xc ? 4 : 2;          // copies per step of this wave
-    const int pre = nk2 < NST - 1 ? nk2 : NST - 1;
-    for (int s2 = 0; s2 < pre; ++s2) issue(s2, xc);
-    for (int s2 = 0; s2 < nk2; ++s2) {
-      // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight
-      const int ahead = min(NST - 2, nk2 - 1 - s2);
-      wait_copies_barrier_n(per * ahead);
-      if (s2 + NST - 1 < nk2) issue(s2 + NST - 1, xc);
-      compute(s2, tmv_c);
-    }
-  };
-  if (nrows > 32)
-    run(std::integral_constant<int, 2>{});
-  else
-    run(std::integral_constant<int, 1>{});
-
-  // the two halves' partial sums: kh = 1 hands over through LDS (the ring
-  // is free once every wave has passed the barrier below)
   lds_barrier_plain();
   float* red = reinterpret_cast<float*>(smem);
   if (kh == 1) {
@@ -794,7 +600,6 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
   }
 
   // epilogue (kh = 0 waves): FP8 channel scale, bf16, rotation (EPI_ROT*), store
-  const int nb = chan(32 * wn);
   const float* ws_f = static_cast<const float*>(p.ws);
   uint32_t swg[SWI ? TM : 1][8];
   if (kh == 0 && nb >= 0) {
@@ -870,7 +675,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
     // 0, 1), in LDS past the partial-sum area; every wave takes the barrier
     constexpr int RED = 4 * TM * 16 * 64;  // floats of the partial-sum area
     uint32_t* xb = reinterpret_cast<uint32_t*>(smem) + RED;
-    static_assert((RED + 2 * TM * 8 * 64) * 4 <= NST * SB, "exchange buffer");
+    static_assert((RED + 2 * TM * 8 * 64) * 4 <= SMEM, "exchange buffer");
     const int wg = wn & 1;
     if (kh == 0 && wn >= 2 && nb >= 0) {
 #pragma unroll
@@ -904,6 +709,410 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
       }
     }
   }
+}
+
+// Few tokens (M <= 64): the layer is a weight stream.  Workgroup: 8 waves,
+// 128 channels x 64 tokens; wave (wn, kh) = (wave % 4, wave / 4) owns
+// channels 32 wn + [0, 32), all 64 tokens, and the in-features of every
+// other 64-wide step: a ring stage holds a 128-wide step, kh picks its half,
+// so two waves share each SIMD and the two halves' partial sums are added
+// in LDS at the end (fixed order).  Same copies, layouts, contraction order
+// and epilogues as above (grouped: tiles of at most 64 expert positions;
+// EPI_ROT_SWIGLU: 64 gate + 64 up channels per tile).  FP8: four stages,
+// copies issued three 128-wide steps ahead; INT4: three stages (75 KB), two
+// workgroups per CU, so that four waves per SIMD hide each other's waits.
+// A tile of at most 32 rows skips the second token tile: its matrix work,
+// and the activation copies of the waves whose rows all lie past row 31.
+// BMD = 16 (INT4, grouped; experts of a few rows each): 16-row activation
+// tiles (8 KB less per stage), so five stages (65 KB) fit, four 128-wide
+// weight steps in flight per workgroup; the matrix cores see the 16 rows
+// twice (token columns 16..31 are dropped).
+namespace ntd {
+constexpr int DEC_BN = 128, DEC_NST = 4, DEC_NTHR = 512;
+template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK / 2 + DEC_BN * 4;
+}  // namespace ntd
+
+template <bool FP8, int B, int EPI = EPI_ROT, bool GROUPED = false, int BMD = 64>
+__global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel(NtArgs p) {
+  using namespace ntd;
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  static_assert(BMD == 64 || (BMD == 16 && !FP8 && GROUPED), "16-row tiles: grouped INT4");
+  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
+  // INT4: three stages (75 KB; 16-row tiles: five, 65 KB), two workgroups
+  // per CU; FP8: four stages
+  #ifndef OFT_DEC16_NST
+#define OFT_DEC16_NST 5
+#endif
+  constexpr int TM = BMD == 64 ? 2 : 1, NST = FP8 ? DEC_NST : (BMD == 16 ? OFT_DEC16_NST : DEC_NST - 1);
+  constexpr int XI = BMD == 64 ? 2 : 1;  // activation copies per step of a copying wave
+  constexpr int XH = BMD * BK * 2;      // 8 KB (2 KB): one 64-wide half of a step
+  constexpr int WH = DEC_W_HALF<FP8>;   // weight bytes of one half
+  constexpr int SB = 2 * XH + 2 * WH;   // stage bytes
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, kh = wave >> 2;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int K = p.K;
+  int e = 0, pos0, nrows;
+  if constexpr (GROUPED) {
+    const int t = blockIdx.y;
+    if (t >= *p.ntiles) return;
+    e = p.tiles[2 * t];
+    pos0 = p.offsets[e] + p.tiles[2 * t + 1];
+    nrows = min(BMD, p.offsets[e + 1] - pos0);
+  } else {
+    pos0 = blockIdx.y * BMD;
+    nrows = min(BMD, p.M - pos0);
+  }
+  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
+  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
+  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  // channel of local weight row rw (0..127), or -1 past the layer's channels
+  const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
+  auto chan = [&](int rw) -> int {
+    if constexpr (SWI) {
+      const int c = cbase + (rw & (DEC_BN / 2 - 1));
+      return c < p.half_n ? (rw < DEC_BN / 2 ? c : p.half_n + c) : -1;
+    } else {
+      return cbase + rw < p.N ? cbase + rw : -1;
+    }
+  };
+  auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
+  const int nk = K / BK;          // 64-wide steps
+  const int nk2 = (nk + 1) / 2;   // 128-wide steps
+  const int kg = FP8 ? 1 : K / p.g;
+  const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;
+
+  // copies of wave (wn, kh), for half kh of each step (a missing last half
+  // re-copies the first half: same count, never read):
+  //   activations rows 16 wn .. 16 wn + 15 (two instructions; 16-row
+  //   tiles: rows 8 wn .. 8 wn + 7 on waves wn < 2, one instruction),
+  //   weight rows 32 wn .. 32 wn + 31 (FP8: two instructions; INT4: one,
+  //   plus the rows' scale words on lanes 0..31)
+  const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
+  uint32_t xoff[XI];
+  const uint8_t* xptr[GROUPED ? XI : 1];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = (BMD == 64 ? 16 * wn + 8 * i : 8 * (wn & 1)) + (lane >> 3);
+    const int rr = r < nrows ? r : 0;
+    const int chunk = 16 * ((lane & 7) ^ swz_x(r));
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + chunk);
+    if constexpr (GROUPED) {
+      const long src = p.kslots > 0 ? (long)(p.perm[pos0 + rr] / p.kslots) : (long)(pos0 + rr);
+      xptr[i] = static_cast<const uint8_t*>(p.a) + src * p.lda * 2 + chunk;
+    }
+  }
+  const uint8_t* wbase = wc + (FP8 ? (size_t)cbase * K : (size_t)cbase * (K / 2));
+  uint32_t woff[2] = {0u, 0u};
+  uint32_t sbase = 0;
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rw = 32 * wn + 16 * i + (lane >> 2);
+      woff[i] = (uint32_t)(crow(rw) * K + 16 * ((lane & 3) ^ swz_w8(rw)));
+    }
+  } else {
+    const int rw = 32 * wn + (lane >> 1);
+    woff[0] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 1) ^ swz_w4(rw)));
+    sbase = (uint32_t)((cbase + crow(32 * wn + l32)) * kg);
+  }
+  const uint32_t base_lds = lds_addr(smem);
+  const uint32_t x_lds = base_lds + (uint32_t)(kh * XH + (BMD == 64 ? 16 * wn : 8 * (wn & 1)) * 128);
+  const uint32_t w_lds = base_lds + (uint32_t)(2 * XH + kh * WH + 32 * wn * (FP8 ? 64 : 32));
+  const uint32_t s_lds = base_lds + (uint32_t)(2 * XH + kh * WH + DEC_BN * BK / 2 + 32 * wn * 4);
+  auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };
+
+  // xc: this wave copies its activation rows (waves whose rows are all past
+  // a tile of at most 32 rows skip them; their copy count per step is 2)
+  auto issue = [&](int s2, bool xc) {  // 128-wide step s2, this wave's half
+    const int st = s2 % NST;
+    int s = 2 * s2 + kh;
+    if (s >= nk) s = 2 * s2;
+    const uint8_t* xb = xbase + (size_t)s * BK * 2;
+    if (xc) {
+#pragma unroll
+      for (int i = 0; i < XI; ++i) {
+        if constexpr (GROUPED)
+          copy16v(x_lds + st * SB + 1024 * i, xptr[i] + (size_t)s * BK * 2);
+        else
+          copy16(x_lds + st * SB + 1024 * i, xb, xoff[i]);
+      }
+    }
+    if constexpr (FP8) {
+      const uint8_t* wb = wbase + (size_t)s * BK;
+      copy16(w_lds + st * SB, wb, woff[0]);
+      copy16(w_lds + st * SB + 1024, wb, woff[1]);
+    } else {
+      copy16(w_lds + st * SB, wbase + (size_t)s * (BK / 2), woff[0]);
+      if (lane < 32) copy4(s_lds + st * SB, ws_h, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
+    }
+  };
+
+  const int rw = 32 * wn + l32;  // this lane's operand row
+  const int xsw = swz_x(l32);
+  uint32_t wrd[2];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wrd[j] = (uint32_t)(rw * 64 + 16 * ((2 * g2 + j) ^ swz_w8(rw)));
+  } else {
+    wrd[0] = (uint32_t)(rw * 32 + 16 * (g2 ^ swz_w4(rw)));
+    wrd[1] = 0u;
+  }
+  const uint32_t srd = FP8 ? 0u : (uint32_t)((cbase + crow(rw)) * kg);
+
+  f32x16 acc[TM];
+#pragma unroll
+  for (int b = 0; b < TM; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+
+  // TMV (a std::integral_constant): 32-token tiles that hold rows (1 when
+  // the tile has at most 32 rows: the other tile is skipped)
+  auto compute = [&](int s2, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    const int s = 2 * s2 + kh;
+    if (s >= nk) return;
+    const int st = s2 % NST;
+    const uint8_t* X = smem + st * SB + kh * XH;
+    const uint8_t* W = smem + st * SB + 2 * XH + kh * WH;
+    uint32_t cw[8];
+    I4Scale sc;
+    if constexpr (FP8) {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[1]);
+      cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
+      cw[4] = c1.x; cw[5] = c1.y; cw[6] = c1.z; cw[7] = c1.w;
+    } else {
+      const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
+      cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(W + DEC_BN * BK / 2 + rw * 4);
+      const uint32_t idx = srd + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
+      sc = i4scale((uint16_t)(word >> (16 * (idx & 1))));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a;
+      if constexpr (FP8) {
+        const uint2 lo = dq_fp8x4(cw[2 * kk]), hi = dq_fp8x4(cw[2 * kk + 1]);
+        a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      } else {
+        a = as_bf16x8(dq_int4x8(cw[kk], sc));
+      }
+#pragma unroll
+      for (int tm = 0; tm < TMV; ++tm) {
+        const int xr = BMD == 64 ? 32 * tm + l32 : (l32 & 15);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(X + xr * 128 + 16 * ((4 * g2 + kk) ^ xsw));
+        acc[tm] = mfma32(a, b, acc[tm]);
+      }
+    }
+  };
+
+  auto run = [&](auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    const bool xc = BMD == 64 ? (TMV == 2 || wn < 2) : wn < 2;  // uniform
+    const int per = (xc ? XI : 0) + 2;                          // copies per step of this wave
+    const int pre = nk2 < NST - 1 ? nk2 : NST - 1;
+    for (int s2 = 0; s2 < pre; ++s2) issue(s2, xc);
+    for (int s2 = 0; s2 < nk2; ++s2) {
+      // copies of steps s2 + 1 .. s2 + NST - 2 may stay in flight
+      const int ahead = min(NST - 2, nk2 - 1 - s2);
+      wait_copies_barrier_n(per * ahead);
+      if (s2 + NST - 1 < nk2) issue(s2 + NST - 1, xc);
+      compute(s2, tmv_c);
+    }
+  };
+  if (BMD == 64 && nrows > 32)
+    run(std::integral_constant<int, TM>{});
+  else
+    run(std::integral_constant<int, 1>{});
+
+  dec_finish<FP8, B, EPI, TM, NST * SB>(p, acc, smem, wn, kh, lane, chan(32 * wn), nrows, pos0, rops);
+}
+
+// INT4 weight stream on 256-wide K steps (K % 256 == 0): every weight copy
+// reads whole 128-byte lines (8 rows x 128 B per instruction), and a stage
+// costs one barrier.  Workgroup: 8 waves, 128 channels x BMD tokens (16 or
+// 64); wave (wn, kh) multiplies channels 32 wn + [0, 32) with in-features
+// [128 kh, 128 kh + 128) of every step, the halves' partial sums are added
+// at the end (dec_finish).  Stage (three, copies two steps ahead):
+//   weights      128 rows x 128 B, chunk c of row r at c ^ ((r >> 1) & 7)
+//   scales       128 rows x 512/g B
+//   activations  BMD rows x 512 B, chunk c of row r at c ^ (r & 15)
+// (16 consecutive rows read at one chunk hit 16 distinct 16-byte bank
+// slots in both layouts).  16-row tiles: 78 KB, two workgroups per CU.
+namespace ntd {
+constexpr int D4_NST = 3;
+}  // namespace ntd
+
+template <int B, int EPI, bool GROUPED, int BMD>
+__global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4_kernel(NtArgs p) {
+  using namespace ntd;
+  static_assert(BMD == 16 || BMD == 64, "tile rows");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
+  constexpr int TM = BMD == 64 ? 2 : 1, NST = D4_NST;
+  constexpr int WBY = 128 * 128, SBY = 128 * 16, XBY = BMD * 512, SB = WBY + SBY + XBY;
+  constexpr int XI = BMD / 16;  // activation copies per wave per step (2 rows x 512 B each)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, kh = wave >> 2;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int K = p.K;
+  int e = 0, pos0, nrows;
+  if constexpr (GROUPED) {
+    const int t = blockIdx.y;
+    if (t >= *p.ntiles) return;
+    e = p.tiles[2 * t];
+    pos0 = p.offsets[e] + p.tiles[2 * t + 1];
+    nrows = min(BMD, p.offsets[e + 1] - pos0);
+  } else {
+    pos0 = blockIdx.y * BMD;
+    nrows = min(BMD, p.M - pos0);
+  }
+  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
+  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
+  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
+  auto chan = [&](int rw) -> int {
+    if constexpr (SWI) {
+      const int c = cbase + (rw & (DEC_BN / 2 - 1));
+      return c < p.half_n ? (rw < DEC_BN / 2 ? c : p.half_n + c) : -1;
+    } else {
+      return cbase + rw < p.N ? cbase + rw : -1;
+    }
+  };
+  auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
+  const int nks = K / 256;
+  const int kg = K / p.g;
+  const int sg = 512 / p.g;  // scale bytes per row and step: 16, 8 or 4
+  // scale copy instructions per step: g = 64 takes four (two dwords a row)
+  const int nsw = p.g == 64 ? 4 : 2;
+
+  // copies of wave w per step:
+  //   weights rows 16 w + 8 i + lane / 8 (i = 0, 1), chunk lane % 8;
+  //   activations rows 2 (XI w + i) + lane / 32, chunk lane % 32;
+  //   scales (waves w < nsw): g = 32 16 B of row 64 w + lane; g = 64 dword
+  //   64 w + lane (row / 2, half % 2); g = 128 the dword of row 64 w + lane.
+  const uint8_t* wbase = wc + (size_t)cbase * (K / 2);
+  uint32_t woff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rw = 16 * wave + 8 * i + (lane >> 3);
+    woff[i] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 7) ^ ((rw >> 1) & 7)));
+  }
+  uint32_t soff = 0;
+  {
+    const int j = 64 * wave + lane;
+    const int row = p.g == 64 ? (j >> 1) : j;
+    const int sub = p.g == 64 ? 4 * (j & 1) : 0;
+    soff = (uint32_t)((cbase + crow(row & 127)) * kg * 2 + sub);
+  }
+  uint32_t xoff[XI];
+  const uint8_t* xptr[GROUPED ? XI : 1];
+  const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = 2 * (XI * wave + i) + (lane >> 5);
+    const int rr = r < nrows ? r : 0;
+    const int chunk = 16 * ((lane & 31) ^ (r & 15));
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + chunk);
+    if constexpr (GROUPED) {
+      const long src = p.kslots > 0 ? (long)(p.perm[pos0 + rr] / p.kslots) : (long)(pos0 + rr);
+      xptr[i] = static_cast<const uint8_t*>(p.a) + src * p.lda * 2 + chunk;
+    }
+  }
+  const uint32_t base_lds = lds_addr(smem);
+  const uint32_t w_lds = base_lds + (uint32_t)(16 * wave * 128);
+  const uint32_t s_lds = base_lds + (uint32_t)(WBY + (p.g == 64 ? 4 * 64 * wave : (p.g == 32 ? 16 : 4) * 64 * wave));
+  const uint32_t x_lds = base_lds + (uint32_t)(WBY + SBY + 2 * XI * wave * 512);
+  const bool scopy = wave < nsw;
+  const int per = 2 + XI + (scopy ? 1 : 0);  // copies per step of this wave
+
+  auto issue = [&](int s) {
+    const int st = s % NST;
+    const uint32_t so = (uint32_t)(st * SB);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy16(w_lds + so + 1024 * i, wbase + (size_t)s * 128, woff[i]);
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      if constexpr (GROUPED)
+        copy16v(x_lds + so + 1024 * i, xptr[i] + (size_t)s * 512);
+      else
+        copy16(x_lds + so + 1024 * i, xbase + (size_t)s * 512, xoff[i]);
+    }
+    if (scopy) {
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(ws_h) + (size_t)s * sg;
+      if (p.g == 32)
+        copy16(s_lds + so, sb, soff);
+      else
+        copy4(s_lds + so, sb, soff);
+    }
+  };
+
+  const int rw = 32 * wn + l32;  // this lane's operand row
+  const int wsw = (rw >> 1) & 7;
+  f32x16 acc[TM];
+#pragma unroll
+  for (int b = 0; b < TM; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+
+  auto compute = [&](int s, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    const uint8_t* W = smem + (s % NST) * SB;
+    const uint8_t* S = W + WBY;
+    const uint8_t* X = S + SBY;
+    const int c0 = 4 * kh + 2 * g2;  // this lane's two 16-byte chunks: in-features 32 c0 .. 32 c0 + 63
+    const uint4 v0 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * (c0 ^ wsw));
+    const uint4 v1 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * ((c0 + 1) ^ wsw));
+    const uint32_t cw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    I4Scale sc[2];
+    if (p.g == 32) {
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(S + rw * 16 + 2 * c0);
+      sc[0] = i4scale((uint16_t)word);
+      sc[1] = i4scale((uint16_t)(word >> 16));
+    } else {
+      const int gi = p.g == 64 ? c0 / 2 : kh;
+      sc[0] = i4scale(*reinterpret_cast<const uint16_t*>(S + rw * sg + 2 * gi));
+      sc[1] = sc[0];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 a = as_bf16x8(dq_int4x8(cw[kk], sc[kk >> 2]));
+#pragma unroll
+      for (int tm = 0; tm < TMV; ++tm) {
+        const int xr = BMD == 64 ? 32 * tm + l32 : (l32 & 15);
+        const bf16x8 b =
+            *reinterpret_cast<const bf16x8*>(X + xr * 512 + 16 * ((16 * kh + 8 * g2 + kk) ^ (xr & 15)));
+        acc[tm] = mfma32(a, b, acc[tm]);
+      }
+    }
+  };
+
+  auto run = [&](auto tmv_c) {
+    const int pre = nks < NST - 1 ? nks : NST - 1;
+    for (int s = 0; s < pre; ++s) issue(s);
+    for (int s = 0; s < nks; ++s) {
+      // copies of steps s + 1 .. s + NST - 2 may stay in flight
+      const int ahead = min(NST - 2, nks - 1 - s);
+      wait_copies_barrier_n(per * ahead);
+      if (s + NST - 1 < nks) issue(s + NST - 1);
+      compute(s, tmv_c);
+    }
+  };
+  if (BMD == 64 && nrows > 32)
+    run(std::integral_constant<int, TM>{});
+  else
+    run(std::integral_constant<int, 1>{});
+
+  dec_finish<false, B, EPI, TM, NST * SB>(p, acc, smem, wn, kh, lane, chan(32 * wn), nrows, pos0, rops);
 }
 
 }  // namespace oft

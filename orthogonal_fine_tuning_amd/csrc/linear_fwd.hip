@@ -49,8 +49,11 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       p.K = a.K;
       p.N = a.N;
       p.g = a.g;
-      hipLaunchKernelGGL((gemm_nt_dec_kernel<FP8, B>), dim3((a.N + ntd::DEC_BN - 1) / ntd::DEC_BN, 1),
-                         dim3(ntd::DEC_NTHR), 0, st, p);
+      const dim3 grid((a.N + ntd::DEC_BN - 1) / ntd::DEC_BN, 1);
+      if (!FP8 && a.K % 256 == 0)  // INT4: whole-line weight copies on 256-wide steps
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT, false, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<FP8, B>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       return hipGetLastError();
     }
   }

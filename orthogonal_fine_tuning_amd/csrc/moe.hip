@@ -476,7 +476,7 @@ MoeWs moe_ws_layout(const MoeDims& d, int pass) {
   w.ntiles = take(sizeof(int));
   w.max_tiles = max_tiles;
   if (pass == 0) {
-    w.max_tiles64 = (P + 63) / 64 + d.E;
+    w.max_tiles64 = (P + 15) / 16 + d.E;  // tiles of 16 or 64 rows
     w.list64 = take(2 * w.max_tiles64 * sizeof(int));
     w.ntiles64 = take(sizeof(int));
     w.gmask = take((size_t)nt64 * d.E * 8);
@@ -526,15 +526,19 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
   uint16_t* O = reinterpret_cast<uint16_t*>(ws + L.O);
   const int nblk_e = 2 * d.I / B;
   // experts averaging at least 64 rows: copy-ring kernels on 128-row tiles;
-  // fewer (decode): the weight-streaming copy-ring kernel on 64-row tiles
+  // fewer (decode): the weight-streaming copy-ring kernel on 64-row tiles,
+  // or on 16-row tiles (deeper weight ring) when they average at most 8
   // (bf16 reference weights: the 128-row copy-ring kernel at every size)
   const bool w16 = d.wf == WF_BF16;
   const bool dma = w16 || (long)d.T * d.k >= 64L * d.E;
   const bool dec = !dma;
+  const bool dec16 = dec && (long)d.T * d.k <= 8L * d.E;
   const long wb2 = w16 ? 4 : 1;  // bytes per two weights
   int* list64 = reinterpret_cast<int*>(ws + L.list64);
   int* ntiles64 = reinterpret_cast<int*>(ws + L.ntiles64);
-  if (dec) hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, 64, list64, ntiles64);
+  if (dec)
+    hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, dec16 ? 16 : 64, list64,
+                       ntiles64);
   {
     NtArgs p{};
     p.a = q.x;
@@ -571,7 +575,15 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.I + ntd::DEC_BN / 2 - 1) / (ntd::DEC_BN / 2), (unsigned)L.max_tiles64);
-      hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      if (d.H % 256 == 0 && dec16)  // whole-line weight copies on 256-wide steps
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      else if (d.H % 256 == 0)
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      else if (dec16)
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
+                           st, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     }
   }
   {
@@ -607,7 +619,14 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.H + ntd::DEC_BN - 1) / ntd::DEC_BN, (unsigned)L.max_tiles64);
-      hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      if (d.I % 256 == 0 && dec16)
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      else if (d.I % 256 == 0)
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      else if (dec16)
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     }
   }
   const size_t n8 = (size_t)d.T * d.H / 8;

@@ -43,6 +43,12 @@ SMALL = {
                                 w_fmt="int4", g=128),
     "decode_split_fp8_b16": DenseConfig("decode_split_fp8_b16", M=37, K=768, segs=(64, 96), b=16,
                                         x_dtype="bf16", w_fmt="fp8"),
+    # few tokens, INT4, K % 256 == 0: weight stream on 256-wide steps (two
+    # token tiles, ragged last channel tile; one token tile)
+    "decode_int4_g32": DenseConfig("decode_int4_g32", M=48, K=512, segs=(160, 128), b=32, x_dtype="bf16",
+                                   w_fmt="int4", g=32),
+    "decode_int4_g64_b16": DenseConfig("decode_int4_g64_b16", M=20, K=768, segs=(96, 64), b=16,
+                                       x_dtype="bf16", w_fmt="int4", g=64),
 }
 
 

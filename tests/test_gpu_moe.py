@@ -31,6 +31,19 @@ SMALL = {
                                    b=16, q_std=0.05),
     "moe_dense_g128": MoEConfig("moe_dense_g128", T=300, E=4, k=2, H=384, I=256, g=128, chunk=3, b=32,
                                 bias_std=0.5),
+    # at most 8 rows per expert on average (16-row weight-streaming tiles);
+    # the hot expert spans several of them.  H, I multiples of 256 take the
+    # 256-wide-step kernels (and I = 128 the 64-wide-step one for the down
+    # projection)
+    "moe_decode16_b32": MoEConfig("moe_decode16_b32", T=40, E=32, k=4, H=512, I=256, g=32, chunk=3, b=32,
+                                  q_std=0.05),
+    "moe_decode16_b16_g64": MoEConfig("moe_decode16_b16_g64", T=24, E=16, k=3, H=256, I=256, g=64, chunk=5,
+                                      b=16, q_std=0.05),
+    "moe_decode16_i128": MoEConfig("moe_decode16_i128", T=40, E=32, k=4, H=256, I=128, g=32, chunk=3, b=32,
+                                   q_std=0.05),
+    # 9 to 63 rows per expert on average: 64-row weight-streaming tiles
+    "moe_dec64_g128": MoEConfig("moe_dec64_g128", T=100, E=16, k=4, H=256, I=256, g=128, chunk=4, b=32,
+                                q_std=0.05),
 }
 
 
