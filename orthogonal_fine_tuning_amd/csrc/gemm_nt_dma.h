@@ -740,10 +740,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   // INT4: three stages (75 KB; 16-row tiles: five, 65 KB), two workgroups
   // per CU; FP8: four stages
-  #ifndef OFT_DEC16_NST
-#define OFT_DEC16_NST 5
-#endif
-  constexpr int TM = BMD == 64 ? 2 : 1, NST = FP8 ? DEC_NST : (BMD == 16 ? OFT_DEC16_NST : DEC_NST - 1);
+    constexpr int TM = BMD == 64 ? 2 : 1, NST = FP8 ? DEC_NST : (BMD == 16 ? 5 : DEC_NST - 1);
   constexpr int XI = BMD == 64 ? 2 : 1;  // activation copies per step of a copying wave
   constexpr int XH = BMD * BK * 2;      // 8 KB (2 KB): one 64-wide half of a step
   constexpr int WH = DEC_W_HALF<FP8>;   // weight bytes of one half

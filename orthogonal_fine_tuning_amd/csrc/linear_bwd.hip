@@ -560,17 +560,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   }
 }
 
-#ifndef OFT_DX_BM
-#define OFT_DX_BM 128
-#endif
-#ifndef OFT_DX_NBUF
-#define OFT_DX_NBUF 1
-#endif
 template <bool XF32, bool FP8, int B, int PRO>
 hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src, const uint8_t* wc,
                        const void* ws, const uint16_t* Rops, void* dx, char* work, hipStream_t st) {
-  constexpr int BM = OFT_DX_BM;
-  constexpr int NB = OFT_DX_NBUF;
+  constexpr int BM = 128;
+  constexpr int NB = 1;
   NnArgs p{};
   p.src = src;
   p.lds = a.N;

@@ -20,17 +20,8 @@
 namespace oft {
 namespace {
 
-#ifndef OFT_FWD_BM
-#define OFT_FWD_BM 256
-#endif
-#ifndef OFT_FWD_NBUF
-#define OFT_FWD_NBUF 1
-#endif
-#ifndef OFT_FWD_DMA
-#define OFT_FWD_DMA 1
-#endif
-constexpr int FWD_BM = OFT_FWD_BM;
-constexpr int FWD_NBUF = OFT_FWD_NBUF;
+constexpr int FWD_BM = 256;
+constexpr int FWD_NBUF = 1;
 
 template <bool XF32, bool FP8, int B>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
@@ -70,10 +61,7 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
     p.K = a.K;
     p.N = a.N;
     p.g = a.g;
-#ifndef OFT_SKINNY_TN
-#define OFT_SKINNY_TN 2
-#endif
-    constexpr int TN = OFT_SKINNY_TN;
+    constexpr int TN = 2;
     if (a.N % (32 * TN) == 0) {
       hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, TN>), dim3(a.N / (32 * TN), 1), dim3(256), 0, st, p);
     } else {
@@ -93,10 +81,10 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
   p.K = a.K;
   p.N = a.N;
   p.g = a.g;
-  if constexpr (!XF32 && OFT_FWD_DMA) {
+  if constexpr (!XF32) {
     if (a.K % ntd::BK == 0) {
       const int nt = (a.N + ntd::BN - 1) / ntd::BN;
-      const int bm = OFT_FWD_DMA >= 128 ? OFT_FWD_DMA : pick_token_tile(nt, a.M, num_cus(), 256);
+      const int bm = pick_token_tile(nt, a.M, num_cus(), 256);
       constexpr int WF = FP8 ? WF_FP8 : WF_INT4;
       if (bm == 256)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI_ROT, false>), dim3(nt, (a.M + 255) / 256),

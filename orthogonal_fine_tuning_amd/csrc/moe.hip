@@ -30,10 +30,7 @@ namespace oft {
 namespace {
 
 constexpr int MOE_BM = 128;  // rows (expert positions) per grouped tile
-#ifndef OFT_MOE_NBUF
-#define OFT_MOE_NBUF 1
-#endif
-constexpr int MOE_NBUF = OFT_MOE_NBUF;  // LDS buffers of the grouped GEMMs
+constexpr int MOE_NBUF = 1;  // LDS buffers of the grouped GEMMs
 
 // ---------------------------------------------------------------- wave scans
 __device__ __forceinline__ int wave_incl_scan(int v) {
