@@ -103,20 +103,16 @@ __device__ __forceinline__ void wait_copies_barrier() {
   else
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// runtime count (one of 0, 2, 4, 6, 8, 12, 16; anything else waits for all)
+// runtime count 0 .. 16 (a larger count waits for all)
 __device__ __forceinline__ void wait_copies_barrier_n(int n) {
+#define OFT_WCB(N) \
+  case N: asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
   switch (n) {
-    case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 12: asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    OFT_WCB(16) OFT_WCB(15) OFT_WCB(14) OFT_WCB(13) OFT_WCB(12) OFT_WCB(11) OFT_WCB(10) OFT_WCB(9)
+    OFT_WCB(8) OFT_WCB(7) OFT_WCB(6) OFT_WCB(5) OFT_WCB(4) OFT_WCB(3) OFT_WCB(2) OFT_WCB(1)
     default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
+#undef OFT_WCB
 }
 // workgroup barrier after this wave's LDS accesses have completed
 __device__ __forceinline__ void lds_barrier_plain() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
