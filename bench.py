@@ -12,9 +12,11 @@ resident in HBM before timing starts.
 Prints ONE JSON line (rank 0).  ``value`` is algorithmic TFLOP/s of the
 whole step (fwd 2MNK + 2MNb, bwd 2MNK + 4MNb; the Cayley build is timed but
 its flops are not counted).  ``roofline`` reports the forward GEMM kernel:
-algorithmic flops per launch over its mean duration, from HIP events on the
-launch stream around a burst of back-to-back forward launches right after
-the timed steps (``phases_us`` comes from events around each phase of every
+algorithmic flops per launch over its mean duration against the bf16
+matrix peak, or, for shapes below the ridge point (312.5 flop per byte:
+the weight streams of few-token layers), algorithmic bytes per launch
+against HBM; the duration comes from HIP events on the launch stream
+around a burst of back-to-back forward launches right after the timed steps (``phases_us`` comes from events around each phase of every
 timed step and also counts the idle time an event boundary adds).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.  MoE workloads also report ``transient_bytes`` (peak device memory
@@ -40,6 +42,20 @@ sys.path.insert(0, ROOT)
 METRIC = "OFT dequant-GEMM fwd+bwd TFLOP/s and HBM GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte where the two meet (312.5)
+
+
+def roofline_object(mfma_bound, flops, nbytes, seconds, kernel, traffic):
+    """Above the ridge point: algorithmic TFLOP/s against the bf16 matrix
+    peak; below it (the weight streams of few-token shapes): algorithmic
+    GB/s against HBM."""
+    if mfma_bound:
+        achieved, peak, unit = flops / seconds / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s"
+    return {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel,
+            "kernel_us": round(seconds * 1e6, 2), "algorithmic_flops": int(flops), "algorithmic_bytes": int(nbytes)}
 
 
 def parse():
@@ -94,7 +110,9 @@ FWD_KERNEL_SOURCES = ["orthogonal_fine_tuning_amd/csrc/linear_fwd.hip",
 def fwd_kernel_name(cfg):
     """The kernel oft_linear_fwd launches for this shape (one launch per call)."""
     if cfg.x_dtype == "bf16":
-        return "gemm_nt_dec_kernel" if cfg.M <= 64 else "gemm_nt_dma_kernel"
+        if cfg.M <= 64:
+            return "gemm_nt_dec4_kernel" if cfg.w_fmt == "int4" and cfg.K % 256 == 0 else "gemm_nt_dec_kernel"
+        return "gemm_nt_dma_kernel"
     if cfg.M <= 64 and cfg.K % 256 == 0:
         return "gemm_nt_skinny_kernel"
     return "gemm_nt_kernel"
@@ -273,7 +291,6 @@ def run_moe(cfg, args):
     f_fwd, f_bwd = moe_flops(cfg)
     by_fwd, by_bwd = moe_bytes(cfg, n_active)
     value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
-    achieved = (f_fwd + f_bwd) / (t_fwd + t_bwd) / 1e12
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
@@ -281,10 +298,8 @@ def run_moe(cfg, args):
         "config": {"workload": cfg.name, "tokens": T, "experts": E, "top_k": k, "hidden": H,
                    "expert_intermediate": I, "weights": f"int4_g{cfg.g}", "oft_block": b, "chunk": cfg.chunk,
                    "active_experts": n_active, "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma" if (f_fwd + f_bwd) / (by_fwd + by_bwd) > 312.5 else "hbm",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "moe fwd+bwd calls", "kernel_us": round((t_fwd + t_bwd) * 1e6, 2)},
+        "roofline": roofline_object((f_fwd + f_bwd) / (by_fwd + by_bwd) > RIDGE, f_fwd + f_bwd, by_fwd + by_bwd,
+                                    t_fwd + t_bwd, kernel="moe fwd+bwd calls", traffic=None),
         "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
                       "bwd": round(t_bwd * 1e6, 2)},
         "phase_rates": {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
@@ -488,13 +503,10 @@ def main():
 
     fwd_src = FWD_KERNEL_SOURCES
     sha = kernel_source_sha(fwd_src)
-    achieved = f_fwd / t_kernel / 1e12
-    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha),
-            "kernel": fwd_kernel_name(cfg), "kernel_us": round(t_kernel * 1e6, 2),
-            "kernel_timing": f"HIP events around {burst} back-to-back launches after the timed steps",
-            "source_sha": sha}
+    roof = roofline_object(f_fwd / by_fwd > RIDGE, f_fwd, by_fwd, t_kernel, kernel=fwd_kernel_name(cfg),
+                           traffic=load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha))
+    roof["kernel_timing"] = f"HIP events around {burst} back-to-back launches after the timed steps"
+    roof["source_sha"] = sha
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
