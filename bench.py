@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="MoE: skip the dense-bf16-weight reference run of the same grouped kernels")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip phases_cold_us (keeps a profiler's kernel averages to the timed steps)")
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
                     help="token rows of the oracle sample for cpu_baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -307,14 +309,15 @@ def run_moe(cfg, args):
                         "hbm_frac": round((by_fwd + by_bwd) / (t_fwd + t_bwd) / 1e9 / PEAK_HBM_GBS, 4)},
     }
     out["transient_bytes"] = int(transient)
-    cf, cb = cold_phases(
-        lambda: oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"],
-                                        Rops, rt, hs, y, wsf, nbf, stream=sp),
-        lambda: oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"],
-                                        W["wd_scales"], Rf, Rops, dx, dq, dw, wsb, nbb, stream=sp))
-    out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
-                             "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
-                             "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
+    if not args.no_cold:
+        cf, cb = cold_phases(
+            lambda: oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"],
+                                            Rops, rt, hs, y, wsf, nbf, stream=sp),
+            lambda: oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"],
+                                            W["wd_scales"], Rf, Rops, dx, dq, dw, wsb, nbb, stream=sp))
+        out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
+                                 "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
+                                 "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
     if not args.no_dense_ref:
         del W
         out["dense_bf16_reference"] = moe_dense_reference(cfg, inp, args, dict(
@@ -525,11 +528,12 @@ def main():
             "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
             "step_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4)},
     }
-    cf, cb = cold_phases(lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp),
-                         lambda: oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp))
-    out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
-                             "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
-                             "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
+    if not args.no_cold:
+        cf, cb = cold_phases(lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp),
+                             lambda: oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp))
+        out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
+                                 "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
+                                 "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
     print(json.dumps(out))
