@@ -289,8 +289,8 @@ __global__ __launch_bounds__(256) void moe_dw_reduce_kernel(const float* __restr
 // ---------------------------------------------------------------- dq per expert
 // One workgroup per (64 gate/up channels, expert): S = dH_blk^T H_blk over the
 // expert's rows (64-row steps through swizzled LDS transposes, MFMA), then the
-// Cayley gradient per block in fp32: Gq = (R^T + I) S (I + R) / 2,
-// dp_il = Gq_il - Gq_li.  Inactive experts get zeros.  When dz != nullptr
+// Cayley gradient per block in fp32 (cayley_grad_group): Gq = (R^T + I) S
+// (I + R) / 2, dp_il = Gq_il - Gq_li.  Inactive experts get zeros (S = 0).  When dz != nullptr
 // the same pass writes dz = dH_blk R_j (bf16, MFMA), the rotated operand of
 // the gate/up dX GEMM, once per dH tile.
 constexpr int LDM = 64 + 8;
@@ -306,8 +306,8 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) uint16_t YT[64 * LDM];
   __shared__ float red[2][64][17];
   __shared__ float S[2][32][33];
-  __shared__ float Rm[2][32][33];
-  __shared__ float T1[2][32][33];
+  // scratch of the Cayley gradient: 3 G B (B + 4) floats, G = 1024 / B^2
+  __shared__ __attribute__((aligned(16))) float scr[3 * (1024 / (B * B)) * B * (B + 4)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -407,50 +407,20 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[grp][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = acc[r] + red[grp][lane][r];
   }
-  // R blocks of this 64-channel group
-  for (int i = tid; i < 2048; i += 256) {
-    const int gq = i >> 10, r = (i >> 5) & 31, cc = i & 31;
-    float v = 0.0f;
-    if (B == 32) {
-      v = Rf[((size_t)e * nblk_e + n0 / 32 + gq) * 1024 + r * 32 + cc];
-    } else if ((r >> 4) == (cc >> 4)) {
-      const int blk = n0 / 16 + 2 * gq + (r >> 4);
-      v = Rf[((size_t)e * nblk_e + blk) * 256 + (r & 15) * 16 + (cc & 15)];
-    }
-    Rm[gq][r][cc] = v;
-  }
   __syncthreads();
-  // T1 = S (I + R), block-diagonal R (b = 16 keeps only the diagonal blocks)
-  for (int i = tid; i < 2048; i += 256) {
-    const int gq = i >> 10, r = (i >> 5) & 31, cc = i & 31;
-    const int lo = B == 32 ? 0 : (cc & 16), hi = lo + B;
-    float s = S[gq][r][cc];
-    for (int q = lo; q < hi; ++q) s += S[gq][r][q] * Rm[gq][q][cc];
-    T1[gq][r][cc] = s;
-  }
-  __syncthreads();
-  for (int i = tid; i < 2048; i += 256) {
-    const int gq = i >> 10, r = (i >> 5) & 31, cc = i & 31;
-    const int lo = B == 32 ? 0 : (r & 16), hi = lo + B;
-    float s = T1[gq][r][cc];
-    for (int q = lo; q < hi; ++q) s += Rm[gq][q][r] * T1[gq][q][cc];
-    S[gq][r][cc] = 0.5f * s;
-  }
-  __syncthreads();
-  constexpr int NP = B * (B - 1) / 2;
-  constexpr int BPG = 32 / B;  // blocks per 32-channel group
-  for (int i = tid; i < 2 * BPG * NP; i += 256) {
-    const int bl = i / NP, pidx = i % NP;
-    const int gq = bl / BPG, sub = bl % BPG;
-    int a = 0, rem = pidx;
-    while (rem >= B - 1 - a) {
-      rem -= B - 1 - a;
-      ++a;
-    }
-    const int l = a + 1 + rem;
-    const int blk = n0 / B + bl;
-    const int o = sub * B;
-    dq[((size_t)e * nblk_e + blk) * NP + pidx] = S[gq][o + a][o + l] - S[gq][o + l][o + a];
+  // the blocks of the 64 channels, G at a time
+  constexpr int GB = 1024 / (B * B), NP = B * (B - 1) / 2;
+#pragma unroll
+  for (int q = 0; q < 64 / (GB * B); ++q) {
+    const int j0 = n0 / B + q * GB;  // first block (within the expert) of the group
+    if (j0 >= nblk_e) break;         // uniform
+    const size_t jb = (size_t)e * nblk_e + j0;
+    cayley_grad_group<B>(scr, Rf + jb * B * B, dq + jb * NP, min(GB, nblk_e - j0), tid, [&](int g, int r, int cc) {
+      const int ch = (q * GB + g) * B;  // first channel of the block in the 64
+      const float* row = &S[ch / 32][ch % 32 + r][ch % 32 + cc];
+      return make_float4(row[0], row[1], row[2], row[3]);
+    });
+    __syncthreads();
   }
 }
 

@@ -94,4 +94,72 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_b
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Cayley gradient of a group of G = 1024 / B^2 consecutive blocks (one for
+// B = 32, four for B = 16): Gq = (R^T + I) S (I + R) / 2, dp_il = Gq_il -
+// Gq_li (packed upper triangle, row-major).  Each of the 256
+// threads owns four adjacent outputs of one block row, so every global load
+// of the group is in flight at once; load_s(g, r, c) returns S[r][c .. c + 3]
+// of block g.  lds holds 3 G B (B + 4) floats; nb <= G blocks are valid.
+template <int B, class LoadS>
+__device__ __forceinline__ void cayley_grad_group(float* lds, const float* __restrict__ Rg,
+                                                  float* __restrict__ dqg, int nb, int tid, LoadS load_s) {
+  constexpr int G = 1024 / (B * B), P = B + 4, BQ = B / 4, BS = B * P;
+  constexpr int NP = B * (B - 1) / 2;
+  const int g = tid / (B * BQ), r = (tid / BQ) % B, c = 4 * (tid % BQ);
+  const bool ok = g < nb;
+  float* S = lds + g * BS;               // S, later Gq
+  float* Rm = lds + G * BS + g * BS;     // R
+  float* T1 = lds + 2 * G * BS + g * BS;  // S (I + R)
+  float4 rv = make_float4(0.f, 0.f, 0.f, 0.f), sv = rv;
+  if (ok) {
+    rv = *reinterpret_cast<const float4*>(Rg + (size_t)g * B * B + r * B + c);
+    sv = load_s(g, r, c);
+  }
+  *reinterpret_cast<float4*>(Rm + r * P + c) = rv;
+  *reinterpret_cast<float4*>(S + r * P + c) = sv;
+  __syncthreads();
+  float4 t = sv;  // T1 = S + S R
+#pragma unroll
+  for (int i = 0; i < B; i += 4) {
+    const float4 sr = *reinterpret_cast<const float4*>(S + r * P + i);
+    const float sk[4] = {sr.x, sr.y, sr.z, sr.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 rr = *reinterpret_cast<const float4*>(Rm + (i + j) * P + c);
+      t.x += sk[j] * rr.x;
+      t.y += sk[j] * rr.y;
+      t.z += sk[j] * rr.z;
+      t.w += sk[j] * rr.w;
+    }
+  }
+  *reinterpret_cast<float4*>(T1 + r * P + c) = t;
+  __syncthreads();
+  float4 q = t;  // Gq = (T1 + R^T T1) / 2
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    const float ri = Rm[i * P + r];
+    const float4 tt = *reinterpret_cast<const float4*>(T1 + i * P + c);
+    q.x += ri * tt.x;
+    q.y += ri * tt.y;
+    q.z += ri * tt.z;
+    q.w += ri * tt.w;
+  }
+  // S is no longer read (its last reads precede the barrier above)
+  *reinterpret_cast<float4*>(S + r * P + c) = make_float4(0.5f * q.x, 0.5f * q.y, 0.5f * q.z, 0.5f * q.w);
+  __syncthreads();
+  for (int e = tid; e < G * NP; e += 256) {
+    const int gb = e / NP;
+    if (gb >= nb) break;
+    // invert the row-major upper-triangle index
+    int i = 0, rem = e - gb * NP;
+    while (rem >= B - 1 - i) {
+      rem -= B - 1 - i;
+      ++i;
+    }
+    const int l = i + 1 + rem;
+    const float* Q = lds + gb * BS;
+    dqg[e] = Q[i * P + l] - Q[l * P + i];
+  }
+}
+
 }  // namespace oft
