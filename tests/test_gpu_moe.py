@@ -41,6 +41,8 @@ SMALL = {
                                       b=16, q_std=0.05),
     "moe_decode16_i128": MoEConfig("moe_decode16_i128", T=40, E=32, k=4, H=256, I=128, g=32, chunk=3, b=32,
                                    q_std=0.05),
+    "moe_decode16_g128": MoEConfig("moe_decode16_g128", T=30, E=32, k=2, H=256, I=256, g=128, chunk=4, b=32,
+                                   q_std=0.05, bias_std=0.5),
     # 9 to 63 rows per expert on average: 64-row weight-streaming tiles
     "moe_dec64_g128": MoEConfig("moe_dec64_g128", T=100, E=16, k=4, H=256, I=256, g=128, chunk=4, b=32,
                                 q_std=0.05),
