@@ -23,9 +23,11 @@ workload.  MoE workloads also report ``transient_bytes`` (peak device memory
 allocated during the timed calls beyond what existed before them) and
 ``dense_bf16_reference``: the same fwd + bwd calls on every expert's weights
 dequantised to bf16 beforehand (``--no-dense-ref`` skips it), with the ratio
-of the INT4 path's time to it.  ``phases_cold_us`` times fwd and bwd again,
-each right after evicting the last-level cache, so that the weights stream
-from HBM.
+of the INT4 path's time to it.  Dense workloads also report
+``reference_policy_fwd``: the frozen base alone (``oft_linear_fwd_base``, the
+KL reference), timed the same way as ``roofline``.  ``phases_cold_us`` times
+fwd and bwd again, each right after evicting the last-level cache, so that
+the weights stream from HBM.
 """
 from __future__ import annotations
 
@@ -500,6 +502,14 @@ def main():
     eb[1].record(stream)
     torch.cuda.synchronize()
     t_kernel = eb[0].elapsed_time(eb[1]) * 1e-3 / burst
+    # the reference-policy forward (frozen base alone, oft_linear_fwd_base),
+    # timed the same way
+    eb[0].record(stream)
+    for _ in range(burst):
+        oft.oft_linear_fwd_base(d, x, wc, ws, y, stream=sp)
+    eb[1].record(stream)
+    torch.cuda.synchronize()
+    t_base = eb[0].elapsed_time(eb[1]) * 1e-3 / burst
     f_fwd, f_bwd = dense_flops(cfg)
     by_fwd, by_bwd = dense_bytes(cfg)
     value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
@@ -510,6 +520,10 @@ def main():
                            traffic=load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha))
     roof["kernel_timing"] = f"HIP events around {burst} back-to-back launches after the timed steps"
     roof["source_sha"] = sha
+    f_base = 2 * cfg.M * cfg.N * cfg.K
+    by_base = by_fwd - cfg.nblk * 2 * cfg.b * cfg.b * 2  # no rotation operands
+    base_roof = roofline_object(f_base / by_base > RIDGE, f_base, by_base, t_base, kernel=fwd_kernel_name(cfg),
+                                traffic=None)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -521,6 +535,7 @@ def main():
                    "weights": cfg.w_fmt + (f"_g{cfg.g}" if cfg.w_fmt == "int4" else "_e4m3"),
                    "x_dtype": cfg.x_dtype, "parallelism": "single_gpu"},
         "roofline": roof,
+        "reference_policy_fwd": base_roof,
         "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
                       "bwd": round(t_bwd * 1e6, 2)},
         "phase_rates": {

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 2
+#define OFT_ABI_VERSION 3
 
 typedef enum {
   OFT_OK = 0,
@@ -169,6 +169,19 @@ int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_
 int32_t oft_linear_fwd(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
                        const void* w_scales, const uint16_t* R_ops, void* y, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* Reference-policy forward: y = x . dequant(W0)^T, the frozen base alone
+ * (R = I).  The pages' section "Five design features of the adapter-first
+ * architecture" takes the KL reference from the frozen base without the
+ * adapter, so no copy of the actor is kept; this is that layer, run by the
+ * forward kernels with the rotation epilogue left out.  bf16 y is
+ * bit-identical to oft_linear_fwd with Q = 0 (whose R is exactly I); fp32 y
+ * is Z itself, which the adapted path rounds to bf16 for the rotation.
+ * Arguments as in
+ * oft_linear_fwd, without R_ops; the block size b is validated but plays no
+ * part.  Workspace: none (ws may be NULL).  Errors as oft_linear_fwd. */
+int32_t oft_linear_fwd_base(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
+                            const void* w_scales, void* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of <dy, y>: dx = rot_R^T(dy) . dequant(W0) and dq (fp32, packed
  * like q).  dy [M, N] bf16; y_saved [M, N] (x_dtype) is the forward output

@@ -140,6 +140,13 @@ def forward(x: np.ndarray, W: np.ndarray, R: np.ndarray) -> np.ndarray:
     return rotate(x @ W.T, R)
 
 
+def base_forward(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """The frozen base alone, y = x W^T: the KL reference of [P2] "Five
+    design features" (the reference policy is the base without the adapter,
+    so no copy of the actor is kept)."""
+    return x @ W.T
+
+
 def backward(x: np.ndarray, W: np.ndarray, R: np.ndarray, dY: np.ndarray):
     """Gradients of <dY, y> w.r.t. x and the packed adapter parameters.
 

@@ -15,8 +15,8 @@ from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF
 
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
-    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_bwd", "oft_moe_workspace_bytes",
-    "oft_moe_route", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
+    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd",
+    "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
     "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_PASS_FWD",
     "OFT_PASS_BWD",
 ]
@@ -89,6 +89,12 @@ def oft_linear_fwd(desc, x, w_codes, w_scales, R_ops, y, ws=None, ws_bytes=0, st
     _lib.check(_lib.load().oft_linear_fwd(C.byref(desc), _ptr(x), _ptr(w_codes), _ptr(w_scales),
                                           _ptr(R_ops), _ptr(y), _ptr(ws), ws_bytes,
                                           _stream(stream)), "oft_linear_fwd")
+
+
+def oft_linear_fwd_base(desc, x, w_codes, w_scales, y, ws=None, ws_bytes=0, stream=None):
+    _lib.check(_lib.load().oft_linear_fwd_base(C.byref(desc), _ptr(x), _ptr(w_codes), _ptr(w_scales),
+                                               _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+               "oft_linear_fwd_base")
 
 
 def oft_linear_bwd(desc, dy, y_saved, w_codes, w_scales, R_f32, R_ops, dx=None, dq=None, ws=None,

@@ -137,6 +137,18 @@ int32_t oft_linear_fwd(const oft_linear_desc* d, const void* x, const uint8_t* w
                                            static_cast<hipStream_t>(stream)));
 }
 
+int32_t oft_linear_fwd_base(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
+                            const void* w_scales, void* y, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const int32_t v = validate_linear(d);
+  if (v != OFT_OK) return v;
+  if (d->M == 0) return OFT_OK;
+  if (!ptr_ok(x) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(y)) return OFT_EINVAL;
+  return hip_status(oft::launch_linear_fwd_base(dense_args(d), x, w_codes, w_scales, y,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void* y_saved,
                        const uint8_t* w_codes, const void* w_scales, const float* R_f32,
                        const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,

@@ -17,14 +17,17 @@
 //   EPI_ROT_SWIGLU : channel tile = 64 gate channels [c, c+64) and the
 //                    matching 64 up channels [I+c, I+c+64); both are rotated
 //                    and stored, then act = silu(gate) * up (from the bf16
-//                    values just stored) is written as well.
+//                    values just stored) is written as well;
+//   EPI_BASE       : FP8 scale, store rows (the frozen base alone, R = I).
 #pragma once
 
 #include "oft_device.h"
 
 namespace oft {
 
-enum : int { EPI_ROT = 0, EPI_PLAIN = 1, EPI_ROT_SWIGLU = 2 };
+enum : int { EPI_ROT = 0, EPI_PLAIN = 1, EPI_ROT_SWIGLU = 2, EPI_BASE = 3 };
+// epilogues that apply the block rotation
+constexpr bool epi_rotates(int epi) { return epi == EPI_ROT || epi == EPI_ROT_SWIGLU; }
 
 struct NtArgs {
   const void* a;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
       }
     }
     bf16x8 ra[2];
-    if constexpr (EPI != EPI_PLAIN) {
+    if constexpr (epi_rotates(EPI)) {
       // A operand: R rows j = l32; items follow the accumulator row order
       // i(t, p) = 16t + 8(p/4) + 4g2 + p%4.
 #pragma unroll
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
         for (int r = 0; r < 16; ++r) z[r] *= sc[r];
       }
       f32x16 o;
-      if constexpr (EPI != EPI_PLAIN) {
+      if constexpr (epi_rotates(EPI)) {
         bf16x8 zb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)

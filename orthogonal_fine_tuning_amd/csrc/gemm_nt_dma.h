@@ -128,7 +128,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   static_assert(KB == 64 || (KB == 128 && WF == WF_FP8 && BM <= 192 && !GROUPED), "128-wide K steps: FP8, <= 192 tokens");
   static_assert(BM == 128 || BM == 192 || BM == 256, "tile");
   static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
   static_assert(EPI != EPI_ROT_SWIGLU || BM == 128, "exchange buffer sized for 128-token tiles");
   constexpr bool FP8 = WF == WF_FP8;
   constexpr bool W16 = WF == WF_BF16;
@@ -434,7 +434,8 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   // ------------------------------------------------------------ epilogue
   // EPI_ROT / EPI_ROT_SWIGLU: FP8 channel scale, bf16, Y^T_blk = R_j Z^T_blk
   // on the matrix cores (accumulator registers reused as the B operand),
-  // store.  EPI_PLAIN: store the accumulators (bf16 or fp32).
+  // store.  EPI_PLAIN: store the accumulators (bf16 or fp32).  EPI_BASE:
+  // FP8 channel scale, store (no rotation).
   const float* ws_f = static_cast<const float*>(p.ws);
   uint32_t swg[SWI ? TN : 1][SWI ? TM : 1][8];  // EPI_ROT_SWIGLU: this lane's bf16 outputs
 #pragma unroll
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
       }
     }
     bf16x8 ra[2];
-    if constexpr (EPI != EPI_PLAIN) {
+    if constexpr (epi_rotates(EPI)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       f32x16 o;
-      if constexpr (EPI != EPI_PLAIN) {
+      if constexpr (epi_rotates(EPI)) {
         f32x16 z = acc[tn][tm];
         if constexpr (FP8) {
 #pragma unroll
@@ -494,6 +495,10 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
         o = mfma32(ra[1], zb[1], o);
       } else {
         o = acc[tn][tm];
+        if constexpr (EPI == EPI_BASE && FP8) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[r] *= fs[r];
+        }
       }
       const int ml = rw0 + 32 * tm + l32;
       const bool m_ok = n_ok && ml < nrows;
@@ -611,7 +616,7 @@ __device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], u
       }
     }
     bf16x8 ra[2];
-    if constexpr (EPI != EPI_PLAIN) {
+    if constexpr (epi_rotates(EPI)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
@@ -632,7 +637,7 @@ __device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], u
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       f32x16 o;
-      if constexpr (EPI != EPI_PLAIN) {
+      if constexpr (epi_rotates(EPI)) {
         f32x16 z = acc[tm];
         if constexpr (FP8) {
 #pragma unroll
@@ -649,6 +654,10 @@ __device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], u
         o = mfma32(ra[1], zb[1], o);
       } else {
         o = acc[tm];
+        if constexpr (EPI == EPI_BASE && FP8) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[r] *= fs[r];
+        }
       }
       const int ml = 32 * tm + l32;
 #pragma unroll
@@ -731,7 +740,7 @@ template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK /
 template <bool FP8, int B, int EPI = EPI_ROT, bool GROUPED = false, int BMD = 64>
 __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel(NtArgs p) {
   using namespace ntd;
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
   static_assert(BMD == 64 || (BMD == 16 && !FP8 && GROUPED), "16-row tiles: grouped INT4");
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   // INT4: three stages (75 KB; 16-row tiles: five, 65 KB), two workgroups
@@ -945,7 +954,7 @@ template <int B, int EPI, bool GROUPED, int BMD>
 __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4_kernel(NtArgs p) {
   using namespace ntd;
   static_assert(BMD == 16 || BMD == 64, "tile rows");
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU, "epilogue");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   constexpr int TM = BMD == 64 ? 2 : 1, NST = D4_NST;
   constexpr int WBY = 128 * 128, SBY = 128 * 16, XBY = BMD * 512, SB = WBY + SBY + XBY;

@@ -13,15 +13,17 @@
 // k = c + 32 g2 + 8 j + p (p = item 0..7), and the token operand uses the
 // same labels.  The 4 partial accumulators are summed through LDS in a fixed
 // order, then wave 0 applies the FP8 scale, rounds to bf16, rotates
-// (Y^T_blk = R_j Z^T_blk on the matrix cores) and stores.
+// (Y^T_blk = R_j Z^T_blk on the matrix cores; EPI_BASE: no rotation) and
+// stores.
 #pragma once
 
 #include "gemm_nt.h"
 
 namespace oft {
 
-template <bool AF32, bool FP8, int B, bool OUTF32, int TN = 1>
+template <bool AF32, bool FP8, int B, bool OUTF32, int TN = 1, int EPI = EPI_ROT>
 __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
+  static_assert(EPI == EPI_ROT || EPI == EPI_BASE, "epilogue");
   __shared__ float red[3][TN][2][16][64];
 
   const int tid = threadIdx.x;
@@ -174,21 +176,23 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
       }
     }
     bf16x8 ra[2];
+    if constexpr (EPI == EPI_ROT) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-      if constexpr (B == 32) {
-        const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
-        lo = *reinterpret_cast<const uint2*>(Rj);
-        hi = *reinterpret_cast<const uint2*>(Rj + 8);
-      } else {
-        if ((l32 >> 4) == t) {
-          const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+      for (int t = 0; t < 2; ++t) {
+        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+        if constexpr (B == 32) {
+          const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
           lo = *reinterpret_cast<const uint2*>(Rj);
           hi = *reinterpret_cast<const uint2*>(Rj + 8);
+        } else {
+          if ((l32 >> 4) == t) {
+            const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+            lo = *reinterpret_cast<const uint2*>(Rj);
+            hi = *reinterpret_cast<const uint2*>(Rj + 8);
+          }
         }
+        ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
-      ra[t] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm) {
@@ -197,16 +201,19 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) z[r] *= sc[r];
       }
-      bf16x8 zb[2];
+      f32x16 o = z;
+      if constexpr (EPI == EPI_ROT) {
+        bf16x8 zb[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
-                                     pack_bf16x2(z[8 * t + 4], z[8 * t + 5]), pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
-      f32x16 o;
+        for (int t = 0; t < 2; ++t)
+          zb[t] = as_bf16x8(make_uint4(pack_bf16x2(z[8 * t], z[8 * t + 1]), pack_bf16x2(z[8 * t + 2], z[8 * t + 3]),
+                                       pack_bf16x2(z[8 * t + 4], z[8 * t + 5]),
+                                       pack_bf16x2(z[8 * t + 6], z[8 * t + 7])));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-      o = mfma32(ra[0], zb[0], o);
-      o = mfma32(ra[1], zb[1], o);
+        for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+        o = mfma32(ra[0], zb[0], o);
+        o = mfma32(ra[1], zb[1], o);
+      }
       const int ml = tm * 32 + l32;
       if (ml >= nrows) continue;
 #pragma unroll

@@ -23,7 +23,8 @@ namespace {
 constexpr int FWD_BM = 256;
 constexpr int FWD_NBUF = 1;
 
-template <bool XF32, bool FP8, int B>
+// EPI: EPI_ROT (the adapted layer) or EPI_BASE (the frozen base alone)
+template <bool XF32, bool FP8, int B, int EPI = EPI_ROT>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                         const uint16_t* Rops, void* y, hipStream_t st) {
   if constexpr (!XF32) {
@@ -42,9 +43,9 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       p.g = a.g;
       const dim3 grid((a.N + ntd::DEC_BN - 1) / ntd::DEC_BN, 1);
       if (!FP8 && a.K % 256 == 0)  // INT4: whole-line weight copies on 256-wide steps
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT, false, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI, false, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<FP8, B>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<FP8, B, EPI>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       return hipGetLastError();
     }
   }
@@ -63,9 +64,11 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
     p.g = a.g;
     constexpr int TN = 2;
     if (a.N % (32 * TN) == 0) {
-      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, TN>), dim3(a.N / (32 * TN), 1), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, TN, EPI>), dim3(a.N / (32 * TN), 1), dim3(256),
+                         0, st, p);
     } else {
-      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, 1>), dim3(a.N / 32, 1), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, 1, EPI>), dim3(a.N / 32, 1), dim3(256), 0, st,
+                         p);
     }
     return hipGetLastError();
   }
@@ -87,22 +90,22 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       const int bm = pick_token_tile(nt, a.M, num_cus(), 256);
       constexpr int WF = FP8 ? WF_FP8 : WF_INT4;
       if (bm == 256)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI_ROT, false>), dim3(nt, (a.M + 255) / 256),
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI, false>), dim3(nt, (a.M + 255) / 256),
                            dim3(ntd::NTHR), 0, st, p);
       else if (bm == 192 && FP8 && a.K % 128 == 0)  // FP8: 128-wide K steps
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, B, 192, EPI_ROT, false, false, 128>),
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, B, 192, EPI, false, false, 128>),
                            dim3(nt, (a.M + 191) / 192), dim3(ntd::NTHR), 0, st, p);
       else if (bm == 192)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 192, EPI_ROT, false>), dim3(nt, (a.M + 191) / 192),
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 192, EPI, false>), dim3(nt, (a.M + 191) / 192),
                            dim3(ntd::NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI_ROT, false>), dim3(nt, (a.M + 127) / 128),
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI, false>), dim3(nt, (a.M + 127) / 128),
                            dim3(ntd::NTHR), 0, st, p);
       return hipGetLastError();
     }
   }
   dim3 grid((a.N + nt::BN - 1) / nt::BN, (a.M + FWD_BM - 1) / FWD_BM);
-  hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, FP8, B, EPI_ROT, false, XF32, FWD_NBUF>), grid, dim3(256), 0,
+  hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, FP8, B, EPI, false, XF32, FWD_NBUF>), grid, dim3(256), 0,
                      st, p);
   return hipGetLastError();
 }
@@ -136,6 +139,17 @@ hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* w
   OFT_FWD_CASE(true, true, 16)
 #undef OFT_FWD_CASE
   return hipErrorInvalidValue;
+}
+
+// The frozen base alone (R = I): y = x . dequant(W0)^T, the same kernels with
+// the rotation epilogue left out (the block size plays no part)
+hipError_t launch_linear_fwd_base(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws, void* y,
+                                  hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  if (a.xf32) return a.fp8 ? launch_fwd_t<true, true, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st)
+                           : launch_fwd_t<true, false, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st);
+  return a.fp8 ? launch_fwd_t<false, true, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st)
+               : launch_fwd_t<false, false, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st);
 }
 
 }  // namespace oft

@@ -56,6 +56,9 @@ struct DenseArgs {
 
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                              const uint16_t* Rops, void* y, hipStream_t st);
+// the frozen base alone: y = x . dequant(W0)^T
+hipError_t launch_linear_fwd_base(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws, void* y,
+                                  hipStream_t st);
 
 // Backward plan: split of the M reduction used by dq (deterministic
 // partials) and the workspace layout.

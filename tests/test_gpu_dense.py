@@ -81,6 +81,52 @@ def _run_gpu(inp, want_bwd=True):
     return out
 
 
+def _run_base(inp):
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = inp["cfg"]
+    xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
+    wf = oft.OFT_W_FP8_E4M3 if cfg.w_fmt == "fp8" else oft.OFT_W_INT4
+    d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
+    tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
+    y = torch.full((cfg.M, cfg.N), -7, dtype=tdt, device="cuda")
+    oft.oft_linear_fwd_base(d, dev(inp["x"]), dev(inp["w_codes"]), dev(inp["w_scales"]), y)
+    torch.cuda.synchronize()
+    return y
+
+
+# one case per forward kernel: copy-ring FP8 and INT4 (bf16 x), register-
+# prefetch FP8 and INT4 (fp32 x), skinny (fp32 x, few tokens), INT4 decode
+# on 256-wide steps (one and two token tiles), FP8 decode
+BASE_CASES = ["fp8_b32_ragged", "int4_g64_ragged_k", "fp8_b16_f32x", "int4_f32x_wide", "int4_g32_f32x_b32",
+              "decode_int4_g32", "decode_m1", "decode_split_fp8_b16"]
+
+
+@pytest.mark.parametrize("name", BASE_CASES)
+def test_base_forward_parity_and_q_zero_identity(name):
+    """Reference-policy forward (frozen base, R = I) against the oracle, and
+    bit-identical to the adapted forward with Q = 0 (whose R is exactly I);
+    with fp32 outputs the adapted path rounds Z to bf16 for the rotation, so
+    it equals the base output rounded to bf16."""
+    cfg = SMALL[name]
+    print(f"[base fwd] {name} M={cfg.M} K={cfg.K} N={cfg.N} {cfg.w_fmt} x {cfg.x_dtype}", flush=True)
+    inp = make_dense(cfg, seed=0)
+    y_ref = odense.base_forward(odense.x_f64(inp), odense.dequant(inp))
+    yb = _run_base(inp)
+    e = err(_to64(yb, cfg), y_ref)
+    print(f"  err y_base={e:.2e}", flush=True)
+    assert e <= TOL
+    inp0 = dict(inp)
+    inp0["p"] = np.zeros_like(inp["p"])
+    y0 = host(_run_gpu(inp0, want_bwd=False)["y"])
+    if cfg.x_dtype == "f32":
+        rounded = codec.bf16_bits_to_f64(codec.f32_to_bf16_bits(host(yb))).astype(np.float32)
+        assert np.array_equal(y0, rounded)
+    else:
+        assert np.array_equal(y0, host(yb))
+
+
 def _to64(t, cfg):
     a = host(t)
     return a.astype(np.float64) if cfg.x_dtype == "f32" else bf16_to_f64(a)

@@ -101,6 +101,19 @@ def test_fp8_q_zero_reproduces_base_output_exactly():
     assert np.array_equal(dense.forward(x, W, R), x @ W.T)
 
 
+def test_base_forward_is_the_q_zero_layer():
+    """The reference-policy layer (frozen base alone) is the adapted layer at
+    Q = 0 exactly, and differs from it once the adapter has moved."""
+    for cfg, inp in (_tiny_inputs(),
+                     (lambda c: (c, make_dense(c, seed=5)))(CONFIGS["qkv_4b"].with_(M=32, K=128, segs=(64, 32, 32)))):
+        W = dense.dequant(inp)
+        x = dense.x_f64(inp)
+        yb = dense.base_forward(x, W)
+        assert np.array_equal(yb, dense.forward(x, W, dense.cayley(np.zeros_like(inp["p"]), cfg.b)))
+        y = dense.forward(x, W, dense.cayley(inp["p"], cfg.b))
+        assert np.abs(y - yb).max() > 1e-3 * np.abs(yb).max()
+
+
 def test_forward_preserves_block_norms_and_is_linear():
     cfg, inp = _tiny_inputs()
     W = dense.dequant(inp)
