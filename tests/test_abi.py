@@ -76,6 +76,11 @@ def test_linear_null_and_misaligned_pointers_rejected():
     bad = C.c_void_p(0x1008)  # not 16-byte aligned
     ok = C.c_void_p(0x1000)
     assert lib.oft_linear_fwd(C.byref(d), bad, ok, ok, ok, ok, None, 0, None) == _lib.OFT_EINVAL
+    # the reference-policy forward validates the same way (no R operand)
+    assert lib.oft_linear_fwd_base(C.byref(d), None, ok, ok, ok, None, 0, None) == _lib.OFT_EINVAL
+    assert lib.oft_linear_fwd_base(C.byref(d), ok, ok, bad, ok, None, 0, None) == _lib.OFT_EINVAL
+    assert lib.oft_linear_fwd_base(C.byref(_desc(b=8)), ok, ok, ok, ok, None, 0, None) == _lib.OFT_EUNSUPPORTED
+    assert lib.oft_linear_fwd_base(C.byref(_desc(M=0)), None, None, None, None, None, 0, None) == _lib.OFT_OK
     # dq requested with a too-small workspace
     nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
     st = lib.oft_linear_bwd(C.byref(d), ok, ok, ok, ok, ok, ok, None, ok, ok, nb - 1, None)
