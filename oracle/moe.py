@@ -63,6 +63,37 @@ def route(logits: np.ndarray, k: int, renorm: bool = False):
     return idx, w
 
 
+def router_backward(logits: np.ndarray, idx: np.ndarray, dw: np.ndarray, renorm: bool = False) -> np.ndarray:
+    """Gradient of the loss with respect to the router logits, given its
+    gradient dw[t, j] with respect to the combine weights w[t, j] of route()
+    (the selection idx is held fixed: top-k is piecewise constant).
+
+    Without renormalisation w_j = p[idx_j] with p = softmax over all E, and
+    dp_i / dl_e = p_i (delta_ie - p_e), so
+        dl_e = p_e (g_e - S),  g_e = dw_j where idx_j = e (else 0),
+                               S = sum_j dw_j w_j.
+    With renormalisation w is the softmax of the selected logits alone (the
+    full denominator cancels), so only selected experts move:
+        dl_{idx_m} = w_m (dw_m - S), 0 elsewhere.
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    _, w = route(logits, idx.shape[1], renorm=renorm)
+    dw = np.asarray(dw, dtype=np.float64)
+    S = (dw * w).sum(axis=1, keepdims=True)
+    rows = np.arange(T)[:, None]
+    out = np.zeros((T, E))
+    if renorm:
+        out[rows, idx] = w * (dw - S)
+    else:
+        p = np.exp(L - L.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        g = np.zeros((T, E))
+        g[rows, idx] = dw
+        out = p * (g - S)
+    return out
+
+
 def group(idx: np.ndarray, E: int, chunk: int) -> dict:
     """Histogram, offsets, stable permutation, active list and chunk table."""
     T, k = idx.shape

@@ -147,3 +147,46 @@ def test_routing_on_config_logits(name):
     assert np.array_equal(idx, np.argsort(-L, axis=1, kind="stable")[:, :cfg.k])
     rt = moe.group(idx, cfg.E, cfg.chunk)
     assert rt["counts"].sum() == cfg.P
+
+
+def _router_case(seed, T=24, E=12, k=3):
+    """Distinct logits on a 1/64 grid, so that a step of 2^-10 is exact in
+    fp32 and never changes the top-k selection."""
+    rng = np.random.default_rng(seed)
+    L = np.stack([rng.permutation(np.arange(-E, E)[:E]) for _ in range(T)]).astype(np.float64) * (5.0 / 64)
+    L = L.astype(np.float32)
+    dw = rng.standard_normal((T, k))
+    return L, dw
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_router_backward_central_difference(renorm):
+    L, dw = _router_case(11)
+    T, E = L.shape
+    k = dw.shape[1]
+    idx, _ = moe.route(L, k, renorm=renorm)
+    g = moe.router_backward(L, idx, dw, renorm=renorm)
+    h = 2.0 ** -10
+    fd = np.zeros_like(g)
+    for e in range(E):
+        Lp, Lm = L.copy(), L.copy()
+        Lp[:, e] += np.float32(h)
+        Lm[:, e] -= np.float32(h)
+        ip, wp = moe.route(Lp, k, renorm=renorm)
+        im, wm = moe.route(Lm, k, renorm=renorm)
+        assert np.array_equal(ip, idx) and np.array_equal(im, idx)
+        fd[:, e] = ((dw * wp).sum(axis=1) - (dw * wm).sum(axis=1)) / (2 * h)
+    assert np.abs(g - fd).max() <= 1e-5 * np.abs(g).max()
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_router_backward_rows_sum_to_zero(renorm):
+    # adding a constant to every logit of a token changes no weight
+    L, dw = _router_case(12, T=40, E=16, k=4)
+    idx, _ = moe.route(L, 4, renorm=renorm)
+    g = moe.router_backward(L, idx, dw, renorm=renorm)
+    assert np.abs(g.sum(axis=1)).max() <= 1e-12 * np.abs(g).max()
+    if renorm:  # only the selected logits enter the renormalised weights
+        mask = np.ones_like(g, dtype=bool)
+        mask[np.arange(g.shape[0])[:, None], idx] = False
+        assert np.all(g[mask] == 0.0)
