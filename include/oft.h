@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 3
+#define OFT_ABI_VERSION 4
 
 typedef enum {
   OFT_OK = 0,
@@ -228,6 +228,21 @@ int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft
                             const uint16_t* wd_scales, const float* R_f32,
                             const uint16_t* R_ops, uint16_t* dx_or_null, float* dq_or_null,
                             float* dw_or_null, void* ws, size_t ws_bytes, void* stream);
+
+/* Router backward: d_logits fp32 [T, E] from dw fp32 [T, k] (the gradient of
+ * the combine weights, as oft_moe_grouped_bwd writes it) through the softmax
+ * of the router-selected experts (the pages' section "Dedicated optimisation
+ * for low-precision MoE models" routes every token to the experts its router
+ * selects).  The selection topk_idx [T, k] (int32, from oft_moe_route) is
+ * held fixed: top-k is piecewise constant in the logits.  renorm = 0:
+ * dl_e = p_e (g_e - S) for every expert, p the softmax of the row, g_e the
+ * dw of e if selected (else 0), S = sum_j dw_j w_j; renorm = 1: the selected
+ * experts get w_m (dw_m - S), the others 0.  p and w are recomputed from
+ * logits [T, E] exactly as oft_moe_route computes them; a NaN logit gets no
+ * gradient.  Errors: as oft_moe_route (descriptor), OFT_EINVAL (a NULL or
+ * misaligned pointer when T > 0).  T == 0 is a no-op. */
+int32_t oft_moe_router_bwd(const oft_moe_desc* d, const float* logits, const int32_t* topk_idx,
+                           const float* dw, float* d_logits, void* stream);
 
 #ifdef __cplusplus
 }

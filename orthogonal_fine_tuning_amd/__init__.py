@@ -16,7 +16,7 @@ from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
     "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd",
-    "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
+    "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
     "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_PASS_FWD",
     "OFT_PASS_BWD",
 ]
@@ -115,6 +115,11 @@ def oft_moe_workspace_bytes(desc, pass_) -> int:
 def oft_moe_route(desc, logits, rt, ws, ws_bytes, stream=None):
     _lib.check(_lib.load().oft_moe_route(C.byref(desc), _ptr(logits), C.byref(rt), _ptr(ws),
                                          ws_bytes, _stream(stream)), "oft_moe_route")
+
+
+def oft_moe_router_bwd(desc, logits, topk_idx, dw, d_logits, stream=None):
+    _lib.check(_lib.load().oft_moe_router_bwd(C.byref(desc), _ptr(logits), _ptr(topk_idx), _ptr(dw),
+                                              _ptr(d_logits), _stream(stream)), "oft_moe_router_bwd")
 
 
 def oft_moe_grouped_fwd(desc, x, logits, wgu_codes, wgu_scales, wd_codes, wd_scales, R_ops, rt,

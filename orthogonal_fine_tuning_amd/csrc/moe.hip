@@ -136,6 +136,84 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
   }
 }
 
+// Router backward: d_logits[t, e] from dw[t, j], the gradient of the combine
+// weights, through the softmax and the fixed top-k selection idx[t, j].
+// Without renormalisation dl_e = p_e (g_e - S) for every expert (p the
+// softmax of the row, g_e = dw_j where idx_j = e, else 0, S = sum_j dw_j
+// w_j); renormalised, w is the softmax of the selected logits alone, so
+// dl_{idx_m} = w_m (dw_m - S) and the other experts get 0.  p and w are
+// recomputed from the logits with the arithmetic of moe_topk_kernel (a NaN
+// logit ranks as -inf there and gets no gradient here).  One wave per token.
+__global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                             int renorm, const int* __restrict__ idx,
+                                                             const float* __restrict__ dw,
+                                                             float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  constexpr int MAXV = 16;  // E <= 1024
+  float v[MAXV];
+  const int nv = (E + 63) / 64;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    const float x = (i < nv && e < E) ? row[e] : -INFINITY;
+    v[i] = x != x ? -INFINITY : x;
+    mx = fmaxf(mx, v[i]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    if (i < nv && e < E) s += __expf(v[i] - mx);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  // the selected experts on lanes 0 .. k - 1
+  int ej = -1;
+  float dj = 0.0f, xj = 0.0f;
+  if (lane < k) {
+    ej = idx[(size_t)t * k + lane];
+    dj = dw[(size_t)t * k + lane];
+    const float x = row[ej < 0 ? 0 : (ej < E ? ej : E - 1)];  // an index out of range reads in bounds, matches none
+    xj = __expf((x != x ? -INFINITY : x) - mx);
+  }
+  float sel = xj;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sel += __shfl_xor(sel, off);
+  const float wj = xj / (renorm ? sel : s);
+  float S = dj * wj;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+  // gradient and weight of the selected experts this lane owns
+  float g[MAXV], ws[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) g[i] = ws[i] = 0.0f;
+  for (int m = 0; m < k; ++m) {
+    const int em = __shfl(ej, m);
+    const float dm = __shfl(dj, m), wm = __shfl(wj, m);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (em == lane + 64 * i) {
+        g[i] = dm;
+        ws[i] = wm;
+      }
+  }
+  float* out = dl + (size_t)t * E;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + 64 * i;
+    if (i < nv && e < E) {
+      const float q = renorm ? ws[i] : __expf(v[i] - mx) / s;
+      out[e] = q * (g[i] - S);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- count
 __global__ __launch_bounds__(64) void moe_count_kernel(const int* __restrict__ idx, int T, int E, int k,
                                                        unsigned long long* __restrict__ gmask) {
@@ -716,6 +794,14 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
 hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                           const MoeWs& L, hipStream_t st) {
   return d.b == 32 ? moe_bwd_t<32>(d, q, rt, ws, L, st) : moe_bwd_t<16>(d, q, rt, ws, L, st);
+}
+
+hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,
+                                 float* d_logits, hipStream_t st) {
+  if (d.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_router_bwd_kernel, dim3((d.T + 3) / 4), dim3(256), 0, st, logits, d.T, d.E, d.k, d.renorm,
+                     topk_idx, dw, d_logits);
+  return hipGetLastError();
 }
 
 }  // namespace oft

@@ -82,6 +82,16 @@ int32_t oft_moe_route(const oft_moe_desc* d, const float* logits, const oft_moe_
                                           static_cast<hipStream_t>(stream)));
 }
 
+int32_t oft_moe_router_bwd(const oft_moe_desc* d, const float* logits, const int32_t* topk_idx,
+                           const float* dw, float* d_logits, void* stream) {
+  const int32_t v = validate_moe(d);
+  if (v != OFT_OK) return v;
+  if (d->T == 0) return OFT_OK;
+  if (!ptr_ok(logits) || !ptr_ok(topk_idx) || !ptr_ok(dw) || !ptr_ok(d_logits)) return OFT_EINVAL;
+  return hip_status(oft::launch_moe_router_bwd(dims(d), logits, topk_idx, dw, d_logits,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const float* logits,
                             const uint8_t* wgu_codes, const uint16_t* wgu_scales,
                             const uint8_t* wd_codes, const uint16_t* wd_scales,

@@ -67,5 +67,8 @@ hipError_t launch_moe_fwd(const MoeDims& d, const float* logits, const MoeFwdPtr
                           const MoeRoutingDev& rt, char* ws, const MoeWs& L, hipStream_t st);
 hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                           const MoeWs& L, hipStream_t st);
+// d_logits [T, E] from dw [T, k] through the softmax and the top-k selection
+hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,
+                                 float* d_logits, hipStream_t st);
 
 }  // namespace oft

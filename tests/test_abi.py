@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.oft_abi_version() == 3
+    assert lib.oft_abi_version() == 4
     for s in range(-6, 1):
         assert lib.oft_status_str(s)
     assert b"unknown" in lib.oft_status_str(-99)
@@ -152,6 +152,17 @@ def test_moe_validation(kw, code):
     d = _moe(**kw)
     n = C.c_size_t(0)
     assert _lib.load().oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == code
+
+
+def test_moe_router_bwd_validation():
+    lib = _lib.load()
+    ok = C.c_void_p(0x1000)
+    bad = C.c_void_p(0x1004)
+    d = _moe()
+    assert lib.oft_moe_router_bwd(C.byref(d), ok, ok, ok, None, None) == _lib.OFT_EINVAL
+    assert lib.oft_moe_router_bwd(C.byref(d), ok, bad, ok, ok, None) == _lib.OFT_EINVAL
+    assert lib.oft_moe_router_bwd(C.byref(_moe(k=17)), ok, ok, ok, ok, None) == _lib.OFT_EUNSUPPORTED
+    assert lib.oft_moe_router_bwd(C.byref(_moe(T=0)), None, None, None, None, None) == _lib.OFT_OK
 
 
 def test_moe_workspace_and_routing_checks():

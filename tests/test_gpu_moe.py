@@ -97,6 +97,34 @@ def test_routing_bit_exact_config_logits(name):
     _check_routing(cfg, logits, _run_route(cfg, logits))
 
 
+@pytest.mark.parametrize("name,renorm", [("moe_small_b32", 0), ("moe_small_g128", 1), ("moe_decode16_b32", 1),
+                                         ("moe_30b_a3b", 0), ("moe_1t_decode", 1), ("moe_1t_train", 0)])
+def test_router_backward(name, renorm):
+    """d_logits through the softmax top-k, the selection from the GPU routing
+    (bit-exact against the oracle's) and a seeded dw, against the oracle."""
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = SMALL[name] if name in SMALL else CONFIGS[name]
+    print(f"[router bwd] {name} T={cfg.T} E={cfg.E} k={cfg.k} renorm={renorm}", flush=True)
+    logits = make_moe_logits(cfg, seed=0)
+    got = _run_route(cfg, logits, renorm=renorm)
+    idx = got["topk_idx"][:cfg.T]
+    dw = np.random.default_rng(7).standard_normal((cfg.T, cfg.k)).astype(np.float32)
+    d = oft.moe_desc(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.g, cfg.b, cfg.chunk, renorm)
+    dl = torch.full((cfg.T, cfg.E), -7.0, dtype=torch.float32, device="cuda")
+    oft.oft_moe_router_bwd(d, dev(logits), dev(idx), dev(dw), dl)
+    torch.cuda.synchronize()
+    ref = omoe.router_backward(logits, idx, dw, renorm=bool(renorm))
+    e = err(host(dl), ref)
+    print(f"  err d_logits={e:.2e}", flush=True)
+    assert e <= 1e-5
+    if renorm:  # only the selected experts get a gradient
+        mask = np.ones((cfg.T, cfg.E), dtype=bool)
+        mask[np.arange(cfg.T)[:, None], idx] = False
+        assert np.all(host(dl)[mask] == 0.0)
+
+
 def test_routing_ties_and_renorm():
     cfg = MoEConfig("ties", T=1000, E=96, k=8, H=64, I=64, g=32, chunk=7, b=32)
     rng = np.random.default_rng(9)
