@@ -16,7 +16,9 @@ algorithmic flops per launch over its mean duration against the bf16
 matrix peak, or, for shapes below the ridge point (312.5 flop per byte:
 the weight streams of few-token layers), algorithmic bytes per launch
 against HBM; the duration comes from HIP events on the launch stream
-around a burst of back-to-back forward launches right after the timed steps (``phases_us`` comes from events around each phase of every
+around a burst of back-to-back forward launches right after the timed
+steps, queued behind a short GPU spin so that the host's cost per call
+leaves no gaps (``phases_us`` comes from events around each phase of every
 timed step and also counts the idle time an event boundary adds).
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.  MoE workloads also report ``transient_bytes`` (peak device memory
@@ -25,7 +27,9 @@ allocated during the timed calls beyond what existed before them) and
 dequantised to bf16 beforehand (``--no-dense-ref`` skips it), with the ratio
 of the INT4 path's time to it.  Dense workloads also report
 ``reference_policy_fwd``: the frozen base alone (``oft_linear_fwd_base``, the
-KL reference), timed the same way as ``roofline``.  ``phases_cold_us`` times
+KL reference), timed the same way as ``roofline``; MoE workloads report
+``router_bwd`` (``oft_moe_router_bwd``: d_logits from the combine-weight
+gradient, outside the step) the same way.  ``phases_cold_us`` times
 fwd and bwd again, each right after evicting the last-level cache, so that
 the weights stream from HBM.
 """
@@ -58,6 +62,25 @@ def roofline_object(mfma_bound, flops, nbytes, seconds, kernel, traffic):
     return {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel,
             "kernel_us": round(seconds * 1e6, 2), "algorithmic_flops": int(flops), "algorithmic_bytes": int(nbytes)}
+
+
+def burst_seconds(stream, launch, n=10):
+    """Mean duration of one of n back-to-back launches: HIP events on the
+    launch stream around the burst.  A short GPU spin is queued first, so
+    every launch is already in the queue when the first event fires and the
+    host's cost per call adds no idle time between the kernels."""
+    import torch
+
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(2_000_000)  # a bounded spin of one thread: about a millisecond
+    eb[0].record(stream)
+    for _ in range(n):
+        launch()
+    eb[1].record(stream)
+    torch.cuda.synchronize()
+    return eb[0].elapsed_time(eb[1]) * 1e-3 / n
 
 
 def parse():
@@ -289,6 +312,16 @@ def run_moe(cfg, args):
     wall = time.perf_counter() - t0
     transient = torch.cuda.max_memory_allocated() - mem0  # the library allocates nothing
     n_active = int(rtt["n_active"][0].item())
+    # the router backward (d_logits from dw through the softmax top-k), not
+    # part of the step: a burst of launches on the step's routing and dw
+    dl = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    burst = 10
+    t_rb = burst_seconds(stream, lambda: oft.oft_moe_router_bwd(d, lg, rtt["topk_idx"], dw, dl, stream=sp), burst)
+    by_rb = 2 * T * E * 4 + 2 * T * k * 4  # logits in, d_logits out, idx and dw in
+    rb_roof = roofline_object(False, 0, by_rb, t_rb, kernel="moe_router_bwd_kernel", traffic=None)
+    rb_roof["kernel_timing"] = (f"HIP events around {burst} back-to-back launches queued behind a spin, "
+                                "after the timed steps")
+    del dl
     t_cay = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
     t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
@@ -304,6 +337,7 @@ def run_moe(cfg, args):
                    "active_experts": n_active, "parallelism": "single_gpu"},
         "roofline": roofline_object((f_fwd + f_bwd) / (by_fwd + by_bwd) > RIDGE, f_fwd + f_bwd, by_fwd + by_bwd,
                                     t_fwd + t_bwd, kernel="moe fwd+bwd calls", traffic=None),
+        "router_bwd": rb_roof,
         "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
                       "bwd": round(t_bwd * 1e6, 2)},
         "phase_rates": {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
@@ -491,25 +525,15 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     # Roofline kernel time: one event pair on the same stream around a burst
-    # of back-to-back forward launches (one kernel each).  The per-phase
+    # of back-to-back forward launches (one kernel each), queued behind a
+    # spin.  The per-phase
     # events above also count the idle time an event boundary adds on each
     # side of the launch it brackets (about 6 us here).
     burst = 10
-    eb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    eb[0].record(stream)
-    for _ in range(burst):
-        oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp)
-    eb[1].record(stream)
-    torch.cuda.synchronize()
-    t_kernel = eb[0].elapsed_time(eb[1]) * 1e-3 / burst
+    t_kernel = burst_seconds(stream, lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp), burst)
     # the reference-policy forward (frozen base alone, oft_linear_fwd_base),
     # timed the same way
-    eb[0].record(stream)
-    for _ in range(burst):
-        oft.oft_linear_fwd_base(d, x, wc, ws, y, stream=sp)
-    eb[1].record(stream)
-    torch.cuda.synchronize()
-    t_base = eb[0].elapsed_time(eb[1]) * 1e-3 / burst
+    t_base = burst_seconds(stream, lambda: oft.oft_linear_fwd_base(d, x, wc, ws, y, stream=sp), burst)
     f_fwd, f_bwd = dense_flops(cfg)
     by_fwd, by_bwd = dense_bytes(cfg)
     value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
@@ -518,7 +542,7 @@ def main():
     sha = kernel_source_sha(fwd_src)
     roof = roofline_object(f_fwd / by_fwd > RIDGE, f_fwd, by_fwd, t_kernel, kernel=fwd_kernel_name(cfg),
                            traffic=load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha))
-    roof["kernel_timing"] = f"HIP events around {burst} back-to-back launches after the timed steps"
+    roof["kernel_timing"] = f"HIP events around {burst} back-to-back launches queued behind a spin, after the timed steps"
     roof["source_sha"] = sha
     f_base = 2 * cfg.M * cfg.N * cfg.K
     by_base = by_fwd - cfg.nblk * 2 * cfg.b * cfg.b * 2  # no rotation operands

@@ -239,7 +239,7 @@ int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft
  * dw of e if selected (else 0), S = sum_j dw_j w_j; renorm = 1: the selected
  * experts get w_m (dw_m - S), the others 0.  p and w are recomputed from
  * logits [T, E] exactly as oft_moe_route computes them; a NaN logit gets no
- * gradient.  Errors: as oft_moe_route (descriptor), OFT_EINVAL (a NULL or
+ * gradient and an index outside [0, E) selects nothing.  Errors: as oft_moe_route (descriptor), OFT_EINVAL (a NULL or
  * misaligned pointer when T > 0).  T == 0 is a no-op. */
 int32_t oft_moe_router_bwd(const oft_moe_desc* d, const float* logits, const int32_t* topk_idx,
                            const float* dw, float* d_logits, void* stream);

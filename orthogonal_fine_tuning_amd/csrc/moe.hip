@@ -144,6 +144,7 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
 // dl_{idx_m} = w_m (dw_m - S) and the other experts get 0.  p and w are
 // recomputed from the logits with the arithmetic of moe_topk_kernel (a NaN
 // logit ranks as -inf there and gets no gradient here).  One wave per token.
+template <int NV>  // NV * 64 >= E: logits per lane
 __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                              int renorm, const int* __restrict__ idx,
                                                              const float* __restrict__ dw,
@@ -152,63 +153,74 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  constexpr int MAXV = 16;  // E <= 1024
-  float v[MAXV];
-  const int nv = (E + 63) / 64;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + 64 * i;
-    const float x = (i < nv && e < E) ? row[e] : -INFINITY;
-    v[i] = x != x ? -INFINITY : x;
-    mx = fmaxf(mx, v[i]);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + 64 * i;
-    if (i < nv && e < E) s += __expf(v[i] - mx);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  // the selected experts on lanes 0 .. k - 1
+  // one round trip: the row, the selection and its dw are all in flight
+  // before the first is used; the selected logits are read from the row's
+  // registers, not loaded again
   int ej = -1;
-  float dj = 0.0f, xj = 0.0f;
+  float dj = 0.0f;
   if (lane < k) {
     ej = idx[(size_t)t * k + lane];
     dj = dw[(size_t)t * k + lane];
-    const float x = row[ej < 0 ? 0 : (ej < E ? ej : E - 1)];  // an index out of range reads in bounds, matches none
-    xj = __expf((x != x ? -INFINITY : x) - mx);
   }
-  float sel = xj;
+  float v[NV];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sel += __shfl_xor(sel, off);
-  const float wj = xj / (renorm ? sel : s);
-  float S = dj * wj;
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    const float x = e < E ? row[e] : -INFINITY;
+    v[i] = x != x ? -INFINITY : x;
+  }
+  float mx = v[0];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
-  // gradient and weight of the selected experts this lane owns
-  float g[MAXV], ws[MAXV];
+  for (int i = 1; i < NV; ++i) mx = fmaxf(mx, v[i]);
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) g[i] = ws[i] = 0.0f;
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float p[NV], s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    p[i] = lane + 64 * i < E ? __expf(v[i] - mx) : 0.0f;
+    s += p[i];
+  }
+  // dw of the selected experts this lane owns (0 elsewhere); an index
+  // outside [0, E) matches no expert
+  float g[NV];
+  bool in[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    g[i] = 0.0f;
+    in[i] = false;
+  }
   for (int m = 0; m < k; ++m) {
-    const int em = __shfl(ej, m);
-    const float dm = __shfl(dj, m), wm = __shfl(wj, m);
+    const int em = __builtin_amdgcn_readlane(ej, m);
+    const float dm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dj), m));
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i)
+    for (int i = 0; i < NV; ++i)
       if (em == lane + 64 * i) {
         g[i] = dm;
-        ws[i] = wm;
+        in[i] = true;
       }
   }
+  // selected mass and sum_j dw_j p_j, reduced together with the row sum
+  float sel = 0.0f, gp = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    sel += in[i] ? p[i] : 0.0f;
+    gp = fmaf(g[i], p[i], gp);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    s += __shfl_xor(s, off);
+    sel += __shfl_xor(sel, off);
+    gp += __shfl_xor(gp, off);
+  }
+  // w = p / den over the experts that carry weight; S = sum_j dw_j w_j
+  const float den = renorm ? sel : s;
+  const float S = gp / den;
   float* out = dl + (size_t)t * E;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
-    if (i < nv && e < E) {
-      const float q = renorm ? ws[i] : __expf(v[i] - mx) / s;
+    if (e < E) {
+      const float q = (renorm && !in[i]) ? 0.0f : p[i] / den;
       out[e] = q * (g[i] - S);
     }
   }
@@ -799,8 +811,23 @@ hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutin
 hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,
                                  float* d_logits, hipStream_t st) {
   if (d.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_router_bwd_kernel, dim3((d.T + 3) / 4), dim3(256), 0, st, logits, d.T, d.E, d.k, d.renorm,
-                     topk_idx, dw, d_logits);
+  const dim3 grid((d.T + 3) / 4), block(256);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, st, logits, d.T, d.E, d.k, d.renorm, topk_idx, dw, d_logits);
+  };
+  const int nv = (d.E + 63) / 64;  // E <= 1024
+  if (nv <= 1)
+    go(moe_router_bwd_kernel<1>);
+  else if (nv <= 2)
+    go(moe_router_bwd_kernel<2>);
+  else if (nv <= 4)
+    go(moe_router_bwd_kernel<4>);
+  else if (nv <= 6)
+    go(moe_router_bwd_kernel<6>);
+  else if (nv <= 8)
+    go(moe_router_bwd_kernel<8>);
+  else
+    go(moe_router_bwd_kernel<16>);
   return hipGetLastError();
 }
 
