@@ -14,6 +14,9 @@ Encodings (the library's documented layouts):
     when ``k`` is odd; a nibble is a two's-complement integer in [-8, 7];
   * INT4 scales are fp16 ``[N, K/g]`` (one per row and group of ``g``
     consecutive in-features); FP8 scales are fp32 ``[N]``;
+  * FP4 weights use the INT4 layout with OCP MX E2M1 codes in the nibbles;
+    their scale slots are ``uint16`` ``[N, K/g]`` holding an E8M0 exponent
+    code in the low byte;
   * adapter parameters are bf16 ``[nblk, b(b-1)/2]``: the strict upper
     triangle of each skew-symmetric block, row-major.
 
@@ -72,8 +75,8 @@ class DenseConfig:
     segs: tuple
     b: int
     x_dtype: str  # "f32" | "bf16"
-    w_fmt: str  # "int4" | "fp8"
-    g: int = 0  # INT4 group along the in-dim (0 for fp8)
+    w_fmt: str  # "int4" | "fp8" | "fp4"
+    g: int = 0  # INT4 / FP4 group along the in-dim (0 for fp8)
     q_std: float = 0.02
     scale_lo: float = 0.01
     scale_hi: float = 0.05
@@ -109,6 +112,7 @@ class MoEConfig:
     bias_std: float = 0.0  # per-expert logit skew (0 = none)
     scale_lo: float = 0.01
     scale_hi: float = 0.05
+    w_fmt: str = "int4"  # "int4" | "fp4"
 
     @property
     def P(self) -> int:
@@ -158,10 +162,19 @@ def _int4_bytes(rng: np.random.Generator, n: int) -> np.ndarray:
     return np.frombuffer(rng.bytes(n), dtype=np.uint8).copy()
 
 
+def _scale_slots(rng: np.random.Generator, w_fmt: str, lo: float, hi: float, shape) -> np.ndarray:
+    """INT4: fp16 scales uniform in [lo, hi].  FP4: E8M0 exponent codes
+    uniform over those of the powers of two nearest lo and hi."""
+    if w_fmt == "int4":
+        return to_fp16_bits(rng.uniform(lo, hi, size=shape))
+    c_lo, c_hi = 127 + int(np.round(np.log2(lo))), 127 + int(np.round(np.log2(hi)))
+    return rng.integers(c_lo, c_hi + 1, size=shape).astype(np.uint16)
+
+
 def make_dense(cfg: DenseConfig, seed: int = 0, with_dy: bool = True) -> dict:
     """Draw one dense OFT-linear problem.
 
-    Draw order: x, weight (INT4 codes | FP8 source values), weight scales,
+    Draw order: x, weight (INT4 / FP4 codes | FP8 source values), weight scales,
     adapter parameters (segment by segment, block by block), dY.
     """
     rng = np.random.default_rng(seed)
@@ -169,11 +182,10 @@ def make_dense(cfg: DenseConfig, seed: int = 0, with_dy: bool = True) -> dict:
     out = {"cfg": cfg}
     xf = rng.standard_normal((M, K), dtype=np.float32)
     out["x"] = xf if cfg.x_dtype == "f32" else to_bf16_bits(xf)
-    if cfg.w_fmt == "int4":
+    if cfg.w_fmt in ("int4", "fp4"):
         assert K % cfg.g == 0 and K % 2 == 0
         out["w_codes"] = _int4_bytes(rng, N * K // 2).reshape(N, K // 2)
-        s = rng.uniform(cfg.scale_lo, cfg.scale_hi, size=(N, K // cfg.g))
-        out["w_scales"] = to_fp16_bits(s)
+        out["w_scales"] = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (N, K // cfg.g))
     elif cfg.w_fmt == "fp8":
         w = rng.standard_normal((N, K), dtype=np.float32)
         s = (np.abs(w).max(axis=1) / np.float32(448.0)).astype(np.float32)
@@ -212,13 +224,13 @@ def make_moe(cfg: MoEConfig, seed: int = 0, with_dy: bool = True) -> dict:
         wgu[e] = _int4_bytes(rng, 2 * I * H // 2).reshape(2 * I, H // 2)
     sgu = np.empty((E, 2 * I, H // g), dtype=np.uint16)
     for e in range(E):
-        sgu[e] = to_fp16_bits(rng.uniform(cfg.scale_lo, cfg.scale_hi, size=(2 * I, H // g)))
+        sgu[e] = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (2 * I, H // g))
     wd = np.empty((E, H, I // 2), dtype=np.uint8)
     for e in range(E):
         wd[e] = _int4_bytes(rng, H * I // 2).reshape(H, I // 2)
     sd = np.empty((E, H, I // g), dtype=np.uint16)
     for e in range(E):
-        sd[e] = to_fp16_bits(rng.uniform(cfg.scale_lo, cfg.scale_hi, size=(H, I // g)))
+        sd[e] = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (H, I // g))
     out.update(wgu_codes=wgu, wgu_scales=sgu, wd_codes=wd, wd_scales=sd)
     p = rng.normal(0.0, cfg.q_std, size=(E, cfg.nblk_e, cfg.npair)).astype(np.float32)
     out["p"] = to_bf16_bits(p)

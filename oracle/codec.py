@@ -9,6 +9,11 @@ Test infrastructure only (see the package header).
 * e4m3fn: the OCP 8-bit float "E4M3" (1 sign, 4 exponent bits with bias 7,
   3 fraction bits; exponent 0 is subnormal; S.1111.111 is NaN; no infinity;
   largest finite 448).
+* e2m1: the OCP Microscaling (MX) 4-bit float element "E2M1" (1 sign, 2
+  exponent bits with bias 1, 1 fraction bit; exponent 0 is subnormal, value
+  fraction / 2; no infinity or NaN; largest 6).
+* e8m0: the OCP MX scale "E8M0" (8 exponent bits with bias 127, no sign, no
+  fraction; 0xFF is NaN), the value 2^(code - 127).
 """
 from __future__ import annotations
 
@@ -49,3 +54,18 @@ def e4m3fn_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     val = np.where(e == 0, f * 2.0 ** -9, (8.0 + f) * np.exp2(e - 10.0))
     val = np.where((e == 15) & (f == 7), np.nan, val)
     return sign * val
+
+
+def e2m1_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Low nibble of each value, decoded as OCP MX E2M1."""
+    u = np.asarray(bits, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where(u >> 3, -1.0, 1.0)
+    e = (u >> 1) & 0x3
+    f = (u & 0x1).astype(np.float64)
+    val = np.where(e == 0, f * 0.5, (2.0 + f) * np.exp2(e - 2.0))
+    return sign * val
+
+
+def e8m0_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    u = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    return np.where(u == 0xFF, np.nan, np.exp2(u - 127.0))

@@ -14,6 +14,11 @@ Conventions (this library's readings; the pages print no formula):
     single rounding.
   * FP8: e4m3fn codes decode exactly; the per-row fp32 scale multiplies the
     row.  The oracle uses the exact product code * scale.
+  * FP4 (the pages name an FP4 base but not its encoding; read as OCP MX):
+    E2M1 codes in the INT4 nibble layout, and per group of g an E8M0
+    exponent code in the low byte of a 16-bit slot (high byte ignored).  The
+    dequantised weight is bf16_RNE(e2m1 * 2^(c - 127)): exact unless it
+    overflows.
   * Adapter block j covers output channels [j*b, (j+1)*b) (segments are
     multiples of b and follow one another, so no block straddles two
     segments).  Q_j[i, l] = p, Q_j[l, i] = -p for the packed entry p of the
@@ -24,7 +29,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codec import bf16_bits_to_f64, e4m3fn_bits_to_f64, f32_to_bf16_bits, fp16_bits_to_f64
+from .codec import (bf16_bits_to_f64, e2m1_bits_to_f64, e4m3fn_bits_to_f64, e8m0_bits_to_f64, f32_to_bf16_bits,
+                    fp16_bits_to_f64)
 
 
 # ---------------------------------------------------------------- dequant
@@ -46,6 +52,37 @@ def dequant_int4(codes: np.ndarray, scale_bits: np.ndarray, g: int) -> np.ndarra
     return bf16_bits_to_f64(f32_to_bf16_bits(prod.astype(np.float32)))
 
 
+def unpack_fp4(codes: np.ndarray) -> np.ndarray:
+    """[rows, K/2] bytes -> [rows, K] E2M1 codes 0..15 (low nibble = even k)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    c = np.empty((rows, 2 * half), dtype=np.uint8)
+    c[:, 0::2] = codes & 0x0F
+    c[:, 1::2] = codes >> 4
+    return c
+
+
+def dequant_fp4(codes: np.ndarray, scale_slots: np.ndarray, g: int) -> np.ndarray:
+    """W[n, k] = bf16_RNE(e2m1(c[n, k]) * 2^(e[n, k // g] - 127)) as fp64,
+    e the low byte of the 16-bit scale slot."""
+    v = e2m1_bits_to_f64(unpack_fp4(codes))
+    s = e8m0_bits_to_f64((np.asarray(scale_slots, dtype=np.uint16) & 0xFF).astype(np.uint8))
+    prod = v * np.repeat(s, g, axis=1)  # exact in fp64: 2 significant bits
+    with np.errstate(over="ignore"):  # 6 * 2^127 overflows binary32, as it overflows bf16
+        return bf16_bits_to_f64(f32_to_bf16_bits(prod.astype(np.float32)))
+
+
+def dequant_fmt(w_fmt: str, codes: np.ndarray, scales: np.ndarray, g: int) -> np.ndarray:
+    """The dequantised base weight of one matrix in any of the formats."""
+    if w_fmt == "int4":
+        return dequant_int4(codes, scales, g)
+    if w_fmt == "fp4":
+        return dequant_fp4(codes, scales, g)
+    if w_fmt == "fp8":
+        return dequant_fp8(codes, scales)
+    raise ValueError(w_fmt)
+
+
 def dequant_fp8_codes(codes: np.ndarray) -> np.ndarray:
     """Exact e4m3fn values of the codes (the per-row scale is NOT applied)."""
     return e4m3fn_bits_to_f64(codes)
@@ -58,9 +95,7 @@ def dequant_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 def dequant(inp: dict) -> np.ndarray:
     cfg = inp["cfg"]
-    if cfg.w_fmt == "int4":
-        return dequant_int4(inp["w_codes"], inp["w_scales"], cfg.g)
-    return dequant_fp8(inp["w_codes"], inp["w_scales"])
+    return dequant_fmt(cfg.w_fmt, inp["w_codes"], inp["w_scales"], cfg.g)
 
 
 # ---------------------------------------------------------------- Cayley

@@ -36,7 +36,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from .codec import bf16_bits_to_f64
-from .dense import cayley, cayley_grad, cayley_params, dequant_int4, rotate, rotate_adjoint, rotation_grad
+from .dense import cayley, cayley_grad, cayley_params, dequant_fmt, rotate, rotate_adjoint, rotation_grad
 
 
 # ---------------------------------------------------------------- routing
@@ -131,8 +131,8 @@ def expert_weights(inp: dict, e: int, P=None):
     [E, 2I/b, b(b-1)/2] (used by finite-difference checks).
     """
     cfg = inp["cfg"]
-    Wgu = dequant_int4(inp["wgu_codes"][e], inp["wgu_scales"][e], cfg.g)
-    Wd = dequant_int4(inp["wd_codes"][e], inp["wd_scales"][e], cfg.g)
+    Wgu = dequant_fmt(cfg.w_fmt, inp["wgu_codes"][e], inp["wgu_scales"][e], cfg.g)
+    Wd = dequant_fmt(cfg.w_fmt, inp["wd_codes"][e], inp["wd_scales"][e], cfg.g)
     R = cayley(inp["p"][e], cfg.b) if P is None else cayley_params(P[e], cfg.b)
     return Wgu, Wd, R
 
