@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 4
+#define OFT_ABI_VERSION 5
 
 typedef enum {
   OFT_OK = 0,
@@ -76,7 +76,16 @@ enum { OFT_DT_BF16 = 0, OFT_DT_F32 = 1 };
 /* OFT_W_BF16: weights already dequantised to bf16 (MoE calls only; the
  * dense-weight reference that the grouped dequant GEMMs are measured
  * against: same kernels, no scales, two bytes per weight in HBM). */
-enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1, OFT_W_BF16 = 2 };
+/* OFT_W_FP4_E2M1: an FP4 base (the pages' "Architectural advantages of OFT
+ * over LoRA" section names one) in the OCP Microscaling form: E2M1 codes
+ * (1 sign, 2 exponent bits with bias 1, 1 fraction bit; 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6 and their negatives), two per byte, low nibble first, exactly as
+ * INT4 codes; one scale slot per group of g codes along K, also as INT4, but
+ * each 16-bit slot holds an E8M0 exponent code c in its low byte (the high
+ * byte is ignored): w = e2m1(code) * 2^(c - 127).  g = 32 is the OCP MXFP4
+ * block; its one-byte scales are widened to 16 bits.  c = 255 (NaN in the
+ * OCP format) is not supported: its results are unspecified. */
+enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1, OFT_W_BF16 = 2, OFT_W_FP4_E2M1 = 3 };
 enum { OFT_PASS_FWD = 0, OFT_PASS_BWD = 1 };
 
 #define OFT_MAX_SEGMENTS 8
@@ -84,12 +93,12 @@ enum { OFT_PASS_FWD = 0, OFT_PASS_BWD = 1 };
 /* Dense OFT linear layer: x [M, K] -> y [M, N], N = sum(seg).
  * Constraints: M >= 0 (M == 0 is a no-op); K >= 64 and K % 64 == 0;
  * b in {16, 32}; 1 <= n_seg <= 8, every seg[s] > 0 and seg[s] % b == 0,
- * N % 32 == 0; INT4: g in {32, 64, 128} and K % g == 0. */
+ * N % 32 == 0; INT4 and FP4: g in {32, 64, 128} and K % g == 0. */
 typedef struct {
   int32_t M, K, N;
   int32_t x_dtype; /* OFT_DT_BF16 | OFT_DT_F32; y and dx use the same dtype */
-  int32_t w_fmt;   /* OFT_W_INT4 | OFT_W_FP8_E4M3                          */
-  int32_t g;       /* INT4 group size along K (ignored for FP8)            */
+  int32_t w_fmt;   /* OFT_W_INT4 | OFT_W_FP8_E4M3 | OFT_W_FP4_E2M1         */
+  int32_t g;       /* INT4 / FP4 group size along K (ignored for FP8)      */
   int32_t b;       /* OFT block size                                       */
   int32_t n_seg;
   int32_t seg[OFT_MAX_SEGMENTS];
@@ -99,19 +108,21 @@ typedef struct {
  * intermediate I.  Per expert e: gate/up weight [2I, H] (gate rows [0, I),
  * up rows [I, 2I)) with its own adapter of 2I/b blocks (gate blocks first),
  * down weight [H, I] without adapter; INT4 with group g (w_fmt =
- * OFT_W_INT4, zero) or, as a measurement reference, bf16 (OFT_W_BF16: the
+ * OFT_W_INT4, zero), FP4 with group g (OFT_W_FP4_E2M1, the same layout with
+ * E8M0 exponents in the scale slots) or, as a measurement reference, bf16
+ * (OFT_W_BF16: the
  * code arrays hold bf16 weights [E, 2I, H] and [E, H, I], the scale
  * pointers are ignored and may be NULL, g is not checked).
  * Constraints: T >= 0; 1 <= k <= 16; k <= E <= 1024; H % 64 == 0;
- * I % 64 == 0; b in {16, 32}; I % b == 0; INT4: g in {32, 64, 128},
- * H % g == 0, I % g == 0; chunk >= 1; renorm in {0, 1}; w_fmt one of the
- * two formats above (else OFT_EDTYPE). */
+ * I % 64 == 0; b in {16, 32}; I % b == 0; INT4 and FP4: g in {32, 64,
+ * 128}, H % g == 0, I % g == 0; chunk >= 1; renorm in {0, 1}; w_fmt one of
+ * the three formats above (else OFT_EDTYPE). */
 typedef struct {
   int32_t T, E, k, H, I, g, b;
   int32_t chunk;  /* active experts per chunk (scheduling unit)            */
   int32_t renorm; /* 0: combine weights = softmax over all E at the chosen
                      experts; 1: renormalised over the k chosen             */
-  int32_t w_fmt;  /* OFT_W_INT4 (0) or OFT_W_BF16                          */
+  int32_t w_fmt;  /* OFT_W_INT4 (0), OFT_W_FP4_E2M1 or OFT_W_BF16         */
 } oft_moe_desc;
 
 /* Routing tables: device pointers, caller-allocated, written by the
@@ -147,12 +158,14 @@ int32_t cayley_build(const uint16_t* q_bf16, int32_t nblk, int32_t b, float* R_f
 
 /* ---- dequantisation hook (what the matrix cores consume) ------------------
  * INT4: out[r][c] = bf16_RNE(q[r][c] * s[r][c / g]) (the product is exact in
- * fp32, so this is one rounding).  FP8: out[r][c] = e4m3fn(code) exactly;
+ * fp32, so this is one rounding).  FP4: out[r][c] = bf16_RNE(e2m1(code) *
+ * 2^(c_e - 127)) with c_e the exponent code of the group (exact short of
+ * overflow).  FP8: out[r][c] = e4m3fn(code) exactly;
  * the per-row scale is NOT applied (the GEMMs apply it in fp32 outside the
- * K loop).  codes: INT4 [rows, cols/2] / FP8 [rows, cols]; scales: fp16
- * [rows, cols/g] / ignored for FP8 (may be NULL); out_bf16 [rows, cols].
- * Constraints: rows, cols >= 0, cols % 8 == 0; INT4: g in {32, 64, 128},
- * cols % g == 0. */
+ * K loop).  codes: INT4 / FP4 [rows, cols/2] / FP8 [rows, cols]; scales:
+ * 16-bit [rows, cols/g] (INT4 fp16, FP4 exponent codes) / ignored for FP8
+ * (may be NULL); out_bf16 [rows, cols].  Constraints: rows, cols >= 0,
+ * cols % 8 == 0; INT4 and FP4: g in {32, 64, 128}, cols % g == 0. */
 int32_t oft_dequant(int32_t w_fmt, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
                     const void* scales, uint16_t* out_bf16, void* stream);
 

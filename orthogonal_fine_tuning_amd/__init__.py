@@ -10,14 +10,14 @@ import ctypes as C
 
 from . import _lib
 from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF16,
-                   OFT_W_FP8_E4M3, OFT_W_INT4, OftError, oft_linear_desc, oft_moe_desc,
+                   OFT_W_FP4_E2M1, OFT_W_FP8_E4M3, OFT_W_INT4, OftError, oft_linear_desc, oft_moe_desc,
                    oft_moe_routing)
 
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
     "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd",
     "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
-    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_PASS_FWD",
+    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_W_FP4_E2M1", "OFT_PASS_FWD",
     "OFT_PASS_BWD",
 ]
 

@@ -14,7 +14,7 @@ LIB_PATH = os.environ.get("OFT_LIBRARY") or os.path.join(_HERE, "liboft.so")
 OFT_OK, OFT_EINVAL, OFT_ESHAPE, OFT_EDTYPE, OFT_EUNSUPPORTED, OFT_EWORKSPACE, OFT_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
 OFT_DT_BF16, OFT_DT_F32 = 0, 1
-OFT_W_INT4, OFT_W_FP8_E4M3, OFT_W_BF16 = 0, 1, 2
+OFT_W_INT4, OFT_W_FP8_E4M3, OFT_W_BF16, OFT_W_FP4_E2M1 = 0, 1, 2, 3
 OFT_PASS_FWD, OFT_PASS_BWD = 0, 1
 OFT_MAX_SEGMENTS = 8
 

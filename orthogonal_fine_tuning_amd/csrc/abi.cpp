@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "oft.h"
+#include "oft_formats.h"
 #include "oft_launch.h"
 
 namespace {
@@ -24,12 +25,19 @@ int32_t hip_status(hipError_t e) {
 
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
 
+static_assert(oft::WF_INT4 == OFT_W_INT4 && oft::WF_FP8 == OFT_W_FP8_E4M3 && oft::WF_BF16 == OFT_W_BF16 &&
+                  oft::WF_FP4 == OFT_W_FP4_E2M1,
+              "kernel weight formats are numbered as the ABI's");
+
+// the 4-bit formats: codes two per byte plus a 16-bit scale per group of g
+bool w4(int f) { return f == OFT_W_INT4 || f == OFT_W_FP4_E2M1; }
+
 int32_t validate_linear(const oft_linear_desc* d) {
   if (d == nullptr) return OFT_EINVAL;
   if (d->M < 0 || d->K <= 0 || d->N <= 0) return OFT_EINVAL;
   if (d->M > (1 << 24) || d->K > (1 << 20) || d->N > (1 << 20)) return OFT_EUNSUPPORTED;
   if (d->x_dtype != OFT_DT_BF16 && d->x_dtype != OFT_DT_F32) return OFT_EDTYPE;
-  if (d->w_fmt != OFT_W_INT4 && d->w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
+  if (!w4(d->w_fmt) && d->w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
   if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;
   if (d->n_seg < 1 || d->n_seg > OFT_MAX_SEGMENTS) return OFT_EUNSUPPORTED;
   long long sum = 0;
@@ -39,7 +47,7 @@ int32_t validate_linear(const oft_linear_desc* d) {
   }
   if (sum != d->N) return OFT_ESHAPE;
   if (d->N % 32 != 0 || d->K % 64 != 0) return OFT_ESHAPE;
-  if (d->w_fmt == OFT_W_INT4) {
+  if (w4(d->w_fmt)) {
     if (!group_ok(d->g)) return OFT_EUNSUPPORTED;
     if (d->K % d->g != 0) return OFT_ESHAPE;
   }
@@ -51,10 +59,11 @@ oft::DenseArgs dense_args(const oft_linear_desc* d) {
   a.M = d->M;
   a.K = d->K;
   a.N = d->N;
-  a.g = d->w_fmt == OFT_W_INT4 ? d->g : 0;
+  a.g = w4(d->w_fmt) ? d->g : 0;
   a.b = d->b;
   a.xf32 = d->x_dtype == OFT_DT_F32;
   a.fp8 = d->w_fmt == OFT_W_FP8_E4M3;
+  a.wf = d->w_fmt == OFT_W_INT4 ? oft::WF_INT4 : a.fp8 ? oft::WF_FP8 : oft::WF_FP4;
   return a;
 }
 
@@ -95,16 +104,16 @@ int32_t cayley_build(const uint16_t* q_bf16, int32_t nblk, int32_t b, float* R_f
 
 int32_t oft_dequant(int32_t w_fmt, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
                     const void* scales, uint16_t* out_bf16, void* stream) {
-  if (w_fmt != OFT_W_INT4 && w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
+  if (!w4(w_fmt) && w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
   if (rows < 0 || cols < 0) return OFT_EINVAL;
   if (cols % 8 != 0) return OFT_ESHAPE;
-  if (w_fmt == OFT_W_INT4) {
+  if (w4(w_fmt)) {
     if (!group_ok(g)) return OFT_EUNSUPPORTED;
     if (cols % g != 0) return OFT_ESHAPE;
   }
   if ((long long)rows * cols == 0) return OFT_OK;
   if (!ptr_ok(codes) || !ptr_ok(out_bf16)) return OFT_EINVAL;
-  if (w_fmt == OFT_W_INT4 && !ptr_ok(scales)) return OFT_EINVAL;
+  if (w4(w_fmt) && !ptr_ok(scales)) return OFT_EINVAL;
   return hip_status(oft::launch_dequant(w_fmt, rows, cols, g, codes, scales, out_bf16,
                                         static_cast<hipStream_t>(stream)));
 }

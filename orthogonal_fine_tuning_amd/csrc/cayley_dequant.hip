@@ -168,16 +168,17 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
 }
 
 // ---- dequant hook: exactly the bf16 values the matrix cores consume -------
-__global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ codes,
-                                                           const uint16_t* __restrict__ scales,
-                                                           uint4* __restrict__ out, size_t n8,
-                                                           int cols, int g) {
+template <int WF>  // a 4-bit format
+__global__ __launch_bounds__(256) void dequant_w4_kernel(const uint32_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales,
+                                                         uint4* __restrict__ out, size_t n8,
+                                                         int cols, int g) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n8) return;
   const int per_row = cols / 8;
   const size_t r = idx / per_row;
   const int c = (int)(idx % per_row) * 8;
-  out[idx] = dq_int4x8(codes[idx], i4scale(scales[r * (size_t)(cols / g) + c / g]));
+  out[idx] = W4<WF>::dq(codes[idx], W4<WF>::scale(scales[r * (size_t)(cols / g) + c / g]));
 }
 
 __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint2* __restrict__ codes,
@@ -204,11 +205,10 @@ hipError_t launch_dequant(int fmt, int rows, int cols, int g, const uint8_t* cod
   const size_t n8 = (size_t)rows * cols / 8;
   if (n8 == 0) return hipSuccess;
   const unsigned grid = (unsigned)((n8 + 255) / 256);
-  if (fmt == 0) {
-    hipLaunchKernelGGL(dequant_int4_kernel, dim3(grid), dim3(256), 0, st,
-                       reinterpret_cast<const uint32_t*>(codes),
-                       static_cast<const uint16_t*>(scales), reinterpret_cast<uint4*>(out), n8,
-                       cols, g);
+  if (wf_4bit(fmt)) {
+    hipLaunchKernelGGL(fmt == WF_FP4 ? dequant_w4_kernel<WF_FP4> : dequant_w4_kernel<WF_INT4>, dim3(grid),
+                       dim3(256), 0, st, reinterpret_cast<const uint32_t*>(codes),
+                       static_cast<const uint16_t*>(scales), reinterpret_cast<uint4*>(out), n8, cols, g);
   } else {
     hipLaunchKernelGGL(dequant_fp8_kernel, dim3(grid), dim3(256), 0, st,
                        reinterpret_cast<const uint2*>(codes), reinterpret_cast<uint4*>(out), n8);

@@ -224,11 +224,11 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
         put(i, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
     } else {
-      const I4Scale wsc = i4scale(wsb);
+      const auto wsc = W4<WF>::scale(wsb);
       uint32_t v[4] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w};
       rot4(v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) put(i, dq_int4x8(v[i], wsc));
+      for (int i = 0; i < 4; ++i) put(i, W4<WF>::dq(v[i], wsc));
     }
     // prologue -> Bs[m][n]
 #pragma unroll

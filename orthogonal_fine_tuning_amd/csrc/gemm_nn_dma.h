@@ -74,7 +74,7 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
   using ntd::copy4;
   using ntd::lds_addr;
   using ntd::swz_x;
-  static_assert(WF == WF_INT4 || WF == WF_BF16, "weights");
+  static_assert(wf_4bit(WF) || WF == WF_BF16, "weights");
   static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD, "epilogue");
   constexpr bool W16 = WF == WF_BF16;
   constexpr int TM = BM / 64;  // 32-row tiles per wave
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
       const uint8_t* C = smem + OFF_W + (s % NST) * CS_BYTES;
       const uint4 cw = *reinterpret_cast<const uint4*>(C + dq_r * 128 + 16 * dq_q);
       const uint16_t sb = *reinterpret_cast<const uint16_t*>(C + C_BYTES + dq_r * dpr * 4 + 2 * dq_sidx);
-      const I4Scale sc = i4scale(sb);
+      const auto sc = W4<WF>::scale(sb);
       // rotate the four code words by dq_rot: output i is chunk (i + rot) % 4
       uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
       uint32_t v[4];
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 4 * dq_q + ((i + dq_rot) & 3);
-        *reinterpret_cast<uint4*>(D + 16 * (c ^ wsw(dq_r))) = dq_int4x8(w[i], sc);
+        *reinterpret_cast<uint4*>(D + 16 * (c ^ wsw(dq_r))) = W4<WF>::dq(w[i], sc);
       }
     }
   };

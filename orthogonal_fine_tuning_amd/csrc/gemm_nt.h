@@ -1,5 +1,5 @@
 // Generic forward-type dequant GEMM:  C^T[n][m] = sum_k W[n][k] A[m][k]
-// (W: packed INT4 / FP8 rows, A: token rows), bf16 MFMA 32x32x16 with fp32
+// (W: packed 4-bit / FP8 rows, A: token rows), bf16 MFMA 32x32x16 with fp32
 // accumulation, dequantisation in registers on the way into LDS.
 //
 // Row mapping:
@@ -62,9 +62,11 @@ constexpr int LDK = BK + 8;
 // buffer and issue the global loads of step s + 2.  NBUF = 1: one buffer, two
 // barriers per step; the smaller LDS footprint lets two workgroups share a
 // CU and overlap each other's dequantisation with their matrix-core work.
-template <int BM, bool AF32, bool FP8, int B, int EPI, bool GROUPED, bool OUTF32, int NBUF = 2>
+template <int BM, bool AF32, int WF, int B, int EPI, bool GROUPED, bool OUTF32, int NBUF = 2>
 __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt_kernel(NtArgs p) {
   using namespace nt;
+  constexpr bool FP8 = WF == WF_FP8;
+  static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
   static_assert(BM == 128 || BM == 256, "tile");
   static_assert(NBUF == 1 || NBUF == 2, "buffers");
   constexpr int TM = BM / 64;  // 32-token tiles per wave
@@ -181,11 +183,11 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
         dst[q] = make_uint4(lo.x, lo.y, hi.x, hi.y);
       }
     } else {
-      const I4Scale wsc = i4scale(wsb);
-      dst[0] = dq_int4x8(wr[0].x, wsc);
-      dst[1] = dq_int4x8(wr[0].y, wsc);
-      dst[2] = dq_int4x8(wr[0].z, wsc);
-      dst[3] = dq_int4x8(wr[0].w, wsc);
+      const auto wsc = W4<WF>::scale(wsb);
+      dst[0] = W4<WF>::dq(wr[0].x, wsc);
+      dst[1] = W4<WF>::dq(wr[0].y, wsc);
+      dst[2] = W4<WF>::dq(wr[0].z, wsc);
+      dst[3] = W4<WF>::dq(wr[0].w, wsc);
     }
   };
 

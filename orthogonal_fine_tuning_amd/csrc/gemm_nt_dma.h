@@ -1,6 +1,6 @@
 // Dense dequant GEMM with asynchronous global -> LDS copies (bf16 x):
 //   C^T[n][m] = sum_k W[n][k] x[m][k]
-// with W as FP8 or INT4 codes (the forward, EPI_ROT: the rotation epilogue
+// with W as FP8 or 4-bit codes (the forward, EPI_ROT: the rotation epilogue
 // of gemm_nt.h) or as bf16 (EPI_PLAIN: plain store; the backward's dX runs
 // here with W = the transposed, dequantised weight and x = the rotated
 // upstream gradient).
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   // every token of the tile (each code row is dequantised by one wave only);
   // otherwise 4 x 2 waves of 64 channels x BM / 2 tokens (with 256 tokens
   // the matrix work per dequantised operand is already large enough)
-  constexpr bool W8 = WF == WF_INT4 && BM == 128;
+  constexpr bool W8 = wf_4bit(WF) && BM == 128;
   constexpr int TN = W8 ? 1 : 2;              // 32-channel tiles per wave
   constexpr int TM = W8 ? BM / 32 : BM / 64;  // 32-token tiles per wave
   constexpr int NWN = W8 ? 8 : 4;             // waves along the channels
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   // copy source row: invalid rows copy the workgroup's first row (never stored)
   auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
   const int nk = K / KB;
-  const int kg = WF == WF_INT4 ? K / p.g : 1;  // INT4 scales per row
+  const int kg = wf_4bit(WF) ? K / p.g : 1;  // 4-bit scales per row
   const int gs = p.g == 32 ? 1 : p.g == 64 ? 0 : -1;  // INT4: log2(64 / g)
 
   // ---- copy sources: activations (dense: per-lane 32-bit offsets from the
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
       return;
     }
     uint32_t cw[TN][KB / 4];  // this lane's codes for the step (INT4: words 0..3)
-    I4Scale sc[TN];
+    typename W4<WF>::S sc[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       if constexpr (W16) {
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
         const uint32_t word = *reinterpret_cast<const uint32_t*>(W + BN * BK / 2 + rw * 4);
         // this lane's in-features 64 s + 32 g2 .. + 31 lie in group (64 s + 32 g2) / g
         const uint32_t idx = srd[tn] + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
-        sc[tn] = i4scale((uint16_t)(word >> (16 * (idx & 1))));
+        sc[tn] = W4<WF>::scale((uint16_t)(word >> (16 * (idx & 1))));
       }
     }
     // operands of MFMA group kk: weights (dequantised or read) and tokens
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
           const uint2 lo = dq_fp8x4(cw[tn][2 * kk]), hi = dq_fp8x4(cw[tn][2 * kk + 1]);
           a[tn] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         } else {
-          a[tn] = as_bf16x8(dq_int4x8(cw[tn][kk], sc[tn]));
+          a[tn] = as_bf16x8(W4<WF>::dq(cw[tn][kk], sc[tn]));
         }
       }
     };
@@ -737,11 +737,13 @@ constexpr int DEC_BN = 128, DEC_NST = 4, DEC_NTHR = 512;
 template <bool FP8> constexpr int DEC_W_HALF = FP8 ? DEC_BN * BK : DEC_BN * BK / 2 + DEC_BN * 4;
 }  // namespace ntd
 
-template <bool FP8, int B, int EPI = EPI_ROT, bool GROUPED = false, int BMD = 64>
-__global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel(NtArgs p) {
+template <int WF, int B, int EPI = EPI_ROT, bool GROUPED = false, int BMD = 64>
+__global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_dec_kernel(NtArgs p) {
   using namespace ntd;
+  constexpr bool FP8 = WF == WF_FP8;
+  static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
-  static_assert(BMD == 64 || (BMD == 16 && !FP8 && GROUPED), "16-row tiles: grouped INT4");
+  static_assert(BMD == 64 || (BMD == 16 && !FP8 && GROUPED), "16-row tiles: grouped 4-bit weights");
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   // INT4: three stages (75 KB; 16-row tiles: five, 65 KB), two workgroups
   // per CU; FP8: four stages
@@ -882,7 +884,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
     const uint8_t* X = smem + st * SB + kh * XH;
     const uint8_t* W = smem + st * SB + 2 * XH + kh * WH;
     uint32_t cw[8];
-    I4Scale sc;
+    typename W4<WF>::S sc;
     if constexpr (FP8) {
       const uint4 c0 = *reinterpret_cast<const uint4*>(W + wrd[0]);
       const uint4 c1 = *reinterpret_cast<const uint4*>(W + wrd[1]);
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
       cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
       const uint32_t word = *reinterpret_cast<const uint32_t*>(W + DEC_BN * BK / 2 + rw * 4);
       const uint32_t idx = srd + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
-      sc = i4scale((uint16_t)(word >> (16 * (idx & 1))));
+      sc = W4<WF>::scale((uint16_t)(word >> (16 * (idx & 1))));
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -902,7 +904,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, FP8 ? 1 : 2) void gemm_nt_dec_kernel
         const uint2 lo = dq_fp8x4(cw[2 * kk]), hi = dq_fp8x4(cw[2 * kk + 1]);
         a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
       } else {
-        a = as_bf16x8(dq_int4x8(cw[kk], sc));
+        a = as_bf16x8(W4<WF>::dq(cw[kk], sc));
       }
 #pragma unroll
       for (int tm = 0; tm < TMV; ++tm) {
@@ -950,8 +952,9 @@ namespace ntd {
 constexpr int D4_NST = 3;
 }  // namespace ntd
 
-template <int B, int EPI, bool GROUPED, int BMD>
+template <int B, int EPI, bool GROUPED, int BMD, int WF = WF_INT4>
 __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4_kernel(NtArgs p) {
+  static_assert(wf_4bit(WF), "4-bit weights");
   using namespace ntd;
   static_assert(BMD == 16 || BMD == 64, "tile rows");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
@@ -1075,19 +1078,19 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
     const uint4 v0 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * (c0 ^ wsw));
     const uint4 v1 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * ((c0 + 1) ^ wsw));
     const uint32_t cw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    I4Scale sc[2];
+    typename W4<WF>::S sc[2];
     if (p.g == 32) {
       const uint32_t word = *reinterpret_cast<const uint32_t*>(S + rw * 16 + 2 * c0);
-      sc[0] = i4scale((uint16_t)word);
-      sc[1] = i4scale((uint16_t)(word >> 16));
+      sc[0] = W4<WF>::scale((uint16_t)word);
+      sc[1] = W4<WF>::scale((uint16_t)(word >> 16));
     } else {
       const int gi = p.g == 64 ? c0 / 2 : kh;
-      sc[0] = i4scale(*reinterpret_cast<const uint16_t*>(S + rw * sg + 2 * gi));
+      sc[0] = W4<WF>::scale(*reinterpret_cast<const uint16_t*>(S + rw * sg + 2 * gi));
       sc[1] = sc[0];
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 a = as_bf16x8(dq_int4x8(cw[kk], sc[kk >> 2]));
+      const bf16x8 a = as_bf16x8(W4<WF>::dq(cw[kk], sc[kk >> 2]));
 #pragma unroll
       for (int tm = 0; tm < TMV; ++tm) {
         const int xr = BMD == 64 ? 32 * tm + l32 : (l32 & 15);

@@ -21,8 +21,10 @@
 
 namespace oft {
 
-template <bool AF32, bool FP8, int B, bool OUTF32, int TN = 1, int EPI = EPI_ROT>
+template <bool AF32, int WF, int B, bool OUTF32, int TN = 1, int EPI = EPI_ROT>
 __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
+  constexpr bool FP8 = WF == WF_FP8;
+  static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
   static_assert(EPI == EPI_ROT || EPI == EPI_BASE, "epilogue");
   __shared__ float red[3][TN][2][16][64];
 
@@ -103,11 +105,11 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
           a[tn][j] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
       } else {
-        const I4Scale sc = i4scale(ch.s[tn]);
-        a[tn][0] = as_bf16x8(dq_int4x8(ch.w[tn][0].x, sc));
-        a[tn][1] = as_bf16x8(dq_int4x8(ch.w[tn][0].y, sc));
-        a[tn][2] = as_bf16x8(dq_int4x8(ch.w[tn][0].z, sc));
-        a[tn][3] = as_bf16x8(dq_int4x8(ch.w[tn][0].w, sc));
+        const auto sc = W4<WF>::scale(ch.s[tn]);
+        a[tn][0] = as_bf16x8(W4<WF>::dq(ch.w[tn][0].x, sc));
+        a[tn][1] = as_bf16x8(W4<WF>::dq(ch.w[tn][0].y, sc));
+        a[tn][2] = as_bf16x8(W4<WF>::dq(ch.w[tn][0].z, sc));
+        a[tn][3] = as_bf16x8(W4<WF>::dq(ch.w[tn][0].w, sc));
       }
     }
 #pragma unroll

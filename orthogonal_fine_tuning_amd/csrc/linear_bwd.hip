@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   }
 }
 
-template <bool XF32, bool FP8, int B, int PRO>
+template <bool XF32, int WF, int B, int PRO>
 hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src, const uint8_t* wc,
                        const void* ws, const uint16_t* Rops, void* dx, char* work, hipStream_t st) {
   constexpr int BM = 128;
@@ -515,7 +515,7 @@ hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src
     p.nsplit_len = pl.nsplit_len;
     p.part = reinterpret_cast<float*>(work + pl.npart_off);
   }
-  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, FP8 ? WF_FP8 : WF_INT4, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, WF, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
   if (pl.nsplit_n > 1) {
     const size_t n4 = (size_t)a.M * a.K / 4;
     hipLaunchKernelGGL(split_reduce_kernel<XF32>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, p.part,
@@ -552,10 +552,11 @@ __global__ __launch_bounds__(256) void transpose_fp8_kernel(const uint8_t* __res
   }
 }
 
-// INT4 codes [N][K/2] + fp16 scales [N][K/g] -> bf16 [K][N] holding the
-// dequant hook's values bf16(q s); 64 x 64 tiles, natural layout in LDS,
-// each thread then pairs two rows n into 4-byte output words.
-__global__ __launch_bounds__(256) void transpose_dequant_int4_kernel(const uint8_t* __restrict__ codes,
+// 4-bit codes [N][K/2] + group scales [N][K/g] -> bf16 [K][N] holding the
+// dequant hook's values; 64 x 64 tiles, natural layout in LDS, each thread
+// then pairs two rows n into 4-byte output words.
+template <int WF>
+__global__ __launch_bounds__(256) void transpose_dequant_w4_kernel(const uint8_t* __restrict__ codes,
                                                                      const uint16_t* __restrict__ scales,
                                                                      uint16_t* __restrict__ out, int N, int K,
                                                                      int g) {
@@ -566,10 +567,10 @@ __global__ __launch_bounds__(256) void transpose_dequant_int4_kernel(const uint8
   {
     const int n = tid >> 2, q = tid & 3;  // in-features k0 + 16q .. + 15 (one scale group: g >= 32)
     const uint2 c = *reinterpret_cast<const uint2*>(codes + (size_t)(n0 + n) * (K / 2) + (k0 + 16 * q) / 2);
-    const I4Scale sc = i4scale(scales[(size_t)(n0 + n) * (K / g) + (k0 + 16 * q) / g]);
+    const auto sc = W4<WF>::scale(scales[(size_t)(n0 + n) * (K / g) + (k0 + 16 * q) / g]);
     uint4* dst = reinterpret_cast<uint4*>(&t[n * LD + 16 * q]);
-    dst[0] = dq_int4x8(c.x, sc);
-    dst[1] = dq_int4x8(c.y, sc);
+    dst[0] = W4<WF>::dq(c.x, sc);
+    dst[1] = W4<WF>::dq(c.y, sc);
   }
   __syncthreads();
   const int np = tid & 31, kq = tid >> 5;  // rows n 2np, 2np + 1; in-features 8kq .. 8kq + 7
@@ -585,15 +586,16 @@ __global__ __launch_bounds__(256) void transpose_dequant_int4_kernel(const uint8
 }
 
 // dX = dZ' . W through the transposed weight (plan.wt)
-template <bool XF32, bool FP8>
+template <bool XF32, int WF>
 hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz, const uint8_t* wc,
                         const void* ws, void* dx, char* work, hipStream_t st) {
+  constexpr bool FP8 = WF == WF_FP8;
   uint8_t* wt = reinterpret_cast<uint8_t*>(work + pl.wt_off);
   const dim3 tgrid(a.K / 64, a.N / 64);
   if constexpr (FP8)
     hipLaunchKernelGGL(transpose_fp8_kernel, tgrid, dim3(256), 0, st, wc, wt, a.N, a.K);
   else
-    hipLaunchKernelGGL(transpose_dequant_int4_kernel, tgrid, dim3(256), 0, st, wc,
+    hipLaunchKernelGGL(transpose_dequant_w4_kernel<WF>, tgrid, dim3(256), 0, st, wc,
                        static_cast<const uint16_t*>(ws), reinterpret_cast<uint16_t*>(wt), a.N, a.K, a.g);
   NtArgs p{};
   p.a = dz;
@@ -737,23 +739,29 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || dx == nullptr || a.M == 0) return err;
   if (dz != nullptr && p.wt) {
-    if (a.xf32) return a.fp8 ? launch_dx_wt<true, true>(a, p, dz, wc, ws, dx, work, st)
-                             : launch_dx_wt<true, false>(a, p, dz, wc, ws, dx, work, st);
-    return a.fp8 ? launch_dx_wt<false, true>(a, p, dz, wc, ws, dx, work, st)
-                 : launch_dx_wt<false, false>(a, p, dz, wc, ws, dx, work, st);
+#define OFT_DXW(XF, WFV) \
+  if (a.xf32 == XF && a.wf == WFV) return launch_dx_wt<XF, WFV>(a, p, dz, wc, ws, dx, work, st);
+    OFT_DXW(false, WF_INT4)
+    OFT_DXW(false, WF_FP8)
+    OFT_DXW(false, WF_FP4)
+    OFT_DXW(true, WF_INT4)
+    OFT_DXW(true, WF_FP8)
+    OFT_DXW(true, WF_FP4)
+#undef OFT_DXW
+    return hipErrorInvalidValue;
   }
-#define OFT_DX(XF, F8, BB)                                                                              \
-  if (a.xf32 == XF && a.fp8 == F8 && a.b == BB)                                                         \
-    return dz != nullptr ? launch_dx_t<XF, F8, BB, PRO_NONE>(a, p, dz, wc, ws, Rops, dx, work, st)     \
-                         : launch_dx_t<XF, F8, BB, PRO_ROT>(a, p, dy, wc, ws, Rops, dx, work, st);
-  OFT_DX(false, false, 32)
-  OFT_DX(false, false, 16)
-  OFT_DX(false, true, 32)
-  OFT_DX(false, true, 16)
-  OFT_DX(true, false, 32)
-  OFT_DX(true, false, 16)
-  OFT_DX(true, true, 32)
-  OFT_DX(true, true, 16)
+#define OFT_DX(XF, WFV, BB)                                                                             \
+  if (a.xf32 == XF && a.wf == WFV && a.b == BB)                                                         \
+    return dz != nullptr ? launch_dx_t<XF, WFV, BB, PRO_NONE>(a, p, dz, wc, ws, Rops, dx, work, st)    \
+                         : launch_dx_t<XF, WFV, BB, PRO_ROT>(a, p, dy, wc, ws, Rops, dx, work, st);
+#define OFT_DX_B(XF, WFV) OFT_DX(XF, WFV, 32) OFT_DX(XF, WFV, 16)
+  OFT_DX_B(false, WF_INT4)
+  OFT_DX_B(false, WF_FP8)
+  OFT_DX_B(false, WF_FP4)
+  OFT_DX_B(true, WF_INT4)
+  OFT_DX_B(true, WF_FP8)
+  OFT_DX_B(true, WF_FP4)
+#undef OFT_DX_B
 #undef OFT_DX
   return hipErrorInvalidValue;
 }

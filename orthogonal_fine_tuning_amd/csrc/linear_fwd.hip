@@ -24,9 +24,10 @@ constexpr int FWD_BM = 256;
 constexpr int FWD_NBUF = 1;
 
 // EPI: EPI_ROT (the adapted layer) or EPI_BASE (the frozen base alone)
-template <bool XF32, bool FP8, int B, int EPI = EPI_ROT>
+template <bool XF32, int WF, int B, int EPI = EPI_ROT>
 hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                         const uint16_t* Rops, void* y, hipStream_t st) {
+  constexpr bool FP8 = WF == WF_FP8;
   if constexpr (!XF32) {
     if (a.M <= 64) {  // few tokens: weight stream through the deep copy ring
       NtArgs p{};
@@ -42,10 +43,11 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       p.N = a.N;
       p.g = a.g;
       const dim3 grid((a.N + ntd::DEC_BN - 1) / ntd::DEC_BN, 1);
-      if (!FP8 && a.K % 256 == 0)  // INT4: whole-line weight copies on 256-wide steps
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI, false, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      if (!FP8 && a.K % 256 == 0)  // 4-bit: whole-line weight copies on 256-wide steps
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI, false, 64, FP8 ? WF_INT4 : WF>), grid, dim3(ntd::DEC_NTHR),
+                           0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<FP8, B, EPI>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<WF, B, EPI>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       return hipGetLastError();
     }
   }
@@ -64,10 +66,10 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
     p.g = a.g;
     constexpr int TN = 2;
     if (a.N % (32 * TN) == 0) {
-      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, TN, EPI>), dim3(a.N / (32 * TN), 1), dim3(256),
+      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, WF, B, XF32, TN, EPI>), dim3(a.N / (32 * TN), 1), dim3(256),
                          0, st, p);
     } else {
-      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, FP8, B, XF32, 1, EPI>), dim3(a.N / 32, 1), dim3(256), 0, st,
+      hipLaunchKernelGGL((gemm_nt_skinny_kernel<XF32, WF, B, XF32, 1, EPI>), dim3(a.N / 32, 1), dim3(256), 0, st,
                          p);
     }
     return hipGetLastError();
@@ -88,7 +90,6 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
     if (a.K % ntd::BK == 0) {
       const int nt = (a.N + ntd::BN - 1) / ntd::BN;
       const int bm = pick_token_tile(nt, a.M, num_cus(), 256);
-      constexpr int WF = FP8 ? WF_FP8 : WF_INT4;
       if (bm == 256)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI, false>), dim3(nt, (a.M + 255) / 256),
                            dim3(ntd::NTHR), 0, st, p);
@@ -105,7 +106,7 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
     }
   }
   dim3 grid((a.N + nt::BN - 1) / nt::BN, (a.M + FWD_BM - 1) / FWD_BM);
-  hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, FP8, B, EPI, false, XF32, FWD_NBUF>), grid, dim3(256), 0,
+  hipLaunchKernelGGL((gemm_nt_kernel<FWD_BM, XF32, WF, B, EPI, false, XF32, FWD_NBUF>), grid, dim3(256), 0,
                      st, p);
   return hipGetLastError();
 }
@@ -127,16 +128,16 @@ int num_cus() {
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                              const uint16_t* Rops, void* y, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-#define OFT_FWD_CASE(XF, F8, BB) \
-  if (a.xf32 == XF && a.fp8 == F8 && a.b == BB) return launch_fwd_t<XF, F8, BB>(a, x, wc, ws, Rops, y, st);
-  OFT_FWD_CASE(false, false, 32)
-  OFT_FWD_CASE(false, false, 16)
-  OFT_FWD_CASE(false, true, 32)
-  OFT_FWD_CASE(false, true, 16)
-  OFT_FWD_CASE(true, false, 32)
-  OFT_FWD_CASE(true, false, 16)
-  OFT_FWD_CASE(true, true, 32)
-  OFT_FWD_CASE(true, true, 16)
+#define OFT_FWD_CASE(XF, WFV, BB) \
+  if (a.xf32 == XF && a.wf == WFV && a.b == BB) return launch_fwd_t<XF, WFV, BB>(a, x, wc, ws, Rops, y, st);
+#define OFT_FWD_B(XF, WFV) OFT_FWD_CASE(XF, WFV, 32) OFT_FWD_CASE(XF, WFV, 16)
+  OFT_FWD_B(false, WF_INT4)
+  OFT_FWD_B(false, WF_FP8)
+  OFT_FWD_B(false, WF_FP4)
+  OFT_FWD_B(true, WF_INT4)
+  OFT_FWD_B(true, WF_FP8)
+  OFT_FWD_B(true, WF_FP4)
+#undef OFT_FWD_B
 #undef OFT_FWD_CASE
   return hipErrorInvalidValue;
 }
@@ -146,10 +147,16 @@ hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* w
 hipError_t launch_linear_fwd_base(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws, void* y,
                                   hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (a.xf32) return a.fp8 ? launch_fwd_t<true, true, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st)
-                           : launch_fwd_t<true, false, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st);
-  return a.fp8 ? launch_fwd_t<false, true, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st)
-               : launch_fwd_t<false, false, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st);
+#define OFT_BASE_CASE(XF, WFV) \
+  if (a.xf32 == XF && a.wf == WFV) return launch_fwd_t<XF, WFV, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st);
+  OFT_BASE_CASE(false, WF_INT4)
+  OFT_BASE_CASE(false, WF_FP8)
+  OFT_BASE_CASE(false, WF_FP4)
+  OFT_BASE_CASE(true, WF_INT4)
+  OFT_BASE_CASE(true, WF_FP8)
+  OFT_BASE_CASE(true, WF_FP4)
+#undef OFT_BASE_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace oft

@@ -573,7 +573,8 @@ hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRout
   return last();
 }
 
-template <int B>
+// W4F: the 4-bit format of the weights when they are not bf16
+template <int B, int W4F>
 static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                                 const MoeWs& L, hipStream_t st) {
   const long P = (long)d.T * d.k;
@@ -626,21 +627,21 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
     } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.I + ntd::DEC_BN / 2 - 1) / (ntd::DEC_BN / 2), (unsigned)L.max_tiles64);
       if (d.H % 256 == 0 && dec16)  // whole-line weight copies on 256-wide steps
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 16, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else if (d.H % 256 == 0)
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 64, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else if (dec16)
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, EPI_ROT_SWIGLU, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
                            st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     }
   }
   {
@@ -670,20 +671,20 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_INT4, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
     } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.H + ntd::DEC_BN - 1) / ntd::DEC_BN, (unsigned)L.max_tiles64);
       if (d.I % 256 == 0 && dec16)
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 16, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else if (d.I % 256 == 0)
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 64>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 64, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else if (dec16)
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, 32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<false, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     }
   }
   const size_t n8 = (size_t)d.T * d.H / 8;
@@ -699,10 +700,12 @@ hipError_t launch_moe_fwd(const MoeDims& d, const float* logits, const MoeFwdPtr
   hipError_t err = launch_moe_route(d, logits, rt, ws, L, st);
   if (err != hipSuccess) return err;
   if (d.T == 0) return hipSuccess;
-  return d.b == 32 ? moe_fwd_gemms<32>(d, q, rt, ws, L, st) : moe_fwd_gemms<16>(d, q, rt, ws, L, st);
+  if (d.wf == WF_FP4)
+    return d.b == 32 ? moe_fwd_gemms<32, WF_FP4>(d, q, rt, ws, L, st) : moe_fwd_gemms<16, WF_FP4>(d, q, rt, ws, L, st);
+  return d.b == 32 ? moe_fwd_gemms<32, WF_INT4>(d, q, rt, ws, L, st) : moe_fwd_gemms<16, WF_INT4>(d, q, rt, ws, L, st);
 }
 
-template <int B>
+template <int B, int W4F>
 static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                             const MoeWs& L, hipStream_t st) {
   const long P = (long)d.T * d.k;
@@ -748,7 +751,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
       if (w16)
         hipLaunchKernelGGL((gemm_nn_dma_kernel<WF_BF16, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nn_dma_kernel<WF_INT4, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nn_dma_kernel<W4F, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
       nkt = (d.I + nnd::BKO - 1) / nnd::BKO;
     } else {
       dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
@@ -756,7 +759,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
         hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>),
                            grid, dim3(256), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_INT4, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>),
+        hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, W4F, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>),
                            grid, dim3(256), 0, st, p);
       nkt = (d.I + nn::BKO - 1) / nn::BKO;
     }
@@ -794,7 +797,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
       hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
                          dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_INT4, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
+      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, W4F, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
                          dim3(256), 0, st, p);
     const size_t n8 = (size_t)d.T * d.H / 8;
     hipLaunchKernelGGL(moe_unpermute_sum_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dXp, d.H,
@@ -805,7 +808,9 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
 
 hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                           const MoeWs& L, hipStream_t st) {
-  return d.b == 32 ? moe_bwd_t<32>(d, q, rt, ws, L, st) : moe_bwd_t<16>(d, q, rt, ws, L, st);
+  if (d.wf == WF_FP4)
+    return d.b == 32 ? moe_bwd_t<32, WF_FP4>(d, q, rt, ws, L, st) : moe_bwd_t<16, WF_FP4>(d, q, rt, ws, L, st);
+  return d.b == 32 ? moe_bwd_t<32, WF_INT4>(d, q, rt, ws, L, st) : moe_bwd_t<16, WF_INT4>(d, q, rt, ws, L, st);
 }
 
 hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,

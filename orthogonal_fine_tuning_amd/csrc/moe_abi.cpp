@@ -18,23 +18,22 @@ int32_t validate_moe(const oft_moe_desc* d) {
   if (d->k > 16 || d->E > 1024 || d->k > d->E) return OFT_EUNSUPPORTED;
   if ((long long)d->T * d->k > (1LL << 30) || d->H > (1 << 16) || d->I > (1 << 16)) return OFT_EUNSUPPORTED;
   if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;
-  if (d->w_fmt != OFT_W_INT4 && d->w_fmt != OFT_W_BF16) return OFT_EDTYPE;
-  const bool int4 = d->w_fmt == OFT_W_INT4;
-  if (int4 && d->g != 32 && d->g != 64 && d->g != 128) return OFT_EUNSUPPORTED;
+  if (d->w_fmt != OFT_W_INT4 && d->w_fmt != OFT_W_FP4_E2M1 && d->w_fmt != OFT_W_BF16) return OFT_EDTYPE;
+  const bool w4 = d->w_fmt != OFT_W_BF16;  // INT4 or FP4: codes + group scales
+  if (w4 && d->g != 32 && d->g != 64 && d->g != 128) return OFT_EUNSUPPORTED;
   if (d->renorm != 0 && d->renorm != 1) return OFT_EINVAL;
   if (d->H % 64 != 0 || d->I % 64 != 0 || d->I % d->b != 0) return OFT_ESHAPE;
-  if (int4 && (d->H % d->g != 0 || d->I % d->g != 0)) return OFT_ESHAPE;
+  if (w4 && (d->H % d->g != 0 || d->I % d->g != 0)) return OFT_ESHAPE;
   return OFT_OK;
 }
 
 oft::MoeDims dims(const oft_moe_desc* d) {
-  const bool int4 = d->w_fmt == OFT_W_INT4;
-  return oft::MoeDims{d->T, d->E, d->k, d->H, d->I, int4 ? d->g : 64, d->b, d->chunk, d->renorm,
-                      int4 ? oft::WF_INT4 : oft::WF_BF16};
+  const int wf = d->w_fmt == OFT_W_INT4 ? oft::WF_INT4 : d->w_fmt == OFT_W_FP4_E2M1 ? oft::WF_FP4 : oft::WF_BF16;
+  return oft::MoeDims{d->T, d->E, d->k, d->H, d->I, wf != oft::WF_BF16 ? d->g : 64, d->b, d->chunk, d->renorm, wf};
 }
 
-// scales are required for INT4 weights only
-bool scales_ok(const oft_moe_desc* d, const void* p) { return d->w_fmt != OFT_W_INT4 || ptr_ok(p); }
+// scales are required for the 4-bit formats only
+bool scales_ok(const oft_moe_desc* d, const void* p) { return d->w_fmt == OFT_W_BF16 || ptr_ok(p); }
 
 int32_t routing_ok(const oft_moe_routing* rt) {
   if (rt == nullptr) return OFT_EINVAL;

@@ -80,6 +80,45 @@ __device__ __forceinline__ uint4 dq_int4x8(uint32_t w, I4Scale sc) {
   return r;
 }
 
+// FP4 group scale: the E8M0 exponent code c in the low byte of the 16-bit
+// slot stands for 2^(c - 127) (OCP Microscaling formats).  The conversion
+// instruction takes the scale from the exponent field of an fp32 operand
+// only, so c << 23 carries it exactly, c = 0 (2^-127) included.
+__device__ __forceinline__ float fp4scale(uint16_t bits) {
+  return __builtin_bit_cast(float, ((uint32_t)bits & 0xFFu) << 23);
+}
+
+// 8 E2M1 codes (low nibble first) times 2^(c - 127) -> 8 bf16
+// (v_cvt_scalef32_pk_bf16_fp4, one byte = two codes per instruction; low
+// nibble to the low half).  Exact: an E2M1 value has two significant bits,
+// so the product only leaves the bf16 range by overflow (c >= 253), which
+// gives infinity.
+__device__ __forceinline__ uint4 dq_fp4x8(uint32_t w, float s) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+  return r;
+}
+
+// The 4-bit formats behind one interface: W4<WF>::S the decoded group scale,
+// scale(bits) its decode, dq(w, s) eight codes to bf16.  INT4 is the primary
+// template so that code paths compiled but never taken for FP8 or bf16
+// weights still name a type.
+template <int WF>
+struct W4 {
+  using S = I4Scale;
+  static __device__ __forceinline__ S scale(uint16_t bits) { return i4scale(bits); }
+  static __device__ __forceinline__ uint4 dq(uint32_t w, S s) { return dq_int4x8(w, s); }
+};
+template <>
+struct W4<WF_FP4> {
+  using S = float;
+  static __device__ __forceinline__ S scale(uint16_t bits) { return fp4scale(bits); }
+  static __device__ __forceinline__ uint4 dq(uint32_t w, S s) { return dq_fp4x8(w, s); }
+};
+
 // 4 e4m3fn bytes (byte 0 first) -> 4 bf16, exact (scale 1.0).
 __device__ __forceinline__ uint2 dq_fp8x4(uint32_t w) {
   bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);

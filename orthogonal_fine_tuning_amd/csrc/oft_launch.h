@@ -44,14 +44,16 @@ inline int pick_token_tile(long col_tiles, long M, int cus, int max_bm) {
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st);
 
+// fmt: a WF_* value (numbered as the OFT_W_* formats of the C ABI)
 hipError_t launch_dequant(int fmt, int rows, int cols, int g, const uint8_t* codes,
                           const void* scales, uint16_t* out, hipStream_t st);
 
-// Dense layer.  xf32: x / y / dx are fp32 (else bf16); fp8: FP8 weights
-// (else INT4 with group g).
+// Dense layer.  xf32: x / y / dx are fp32 (else bf16); wf: the weight
+// format (the 4-bit ones with group g).
 struct DenseArgs {
   int M, K, N, g, b;
-  bool xf32, fp8;
+  bool xf32, fp8;  // fp8: wf == WF_FP8
+  int wf;          // WF_INT4, WF_FP8 or WF_FP4
 };
 
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,

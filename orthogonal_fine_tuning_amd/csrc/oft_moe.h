@@ -11,7 +11,7 @@ namespace oft {
 
 struct MoeDims {
   int T, E, k, H, I, g, b, chunk, renorm;
-  int wf;  // WF_INT4 or WF_BF16 (dequantised reference weights)
+  int wf;  // WF_INT4, WF_FP4 or WF_BF16 (dequantised reference weights)
 };
 
 // device pointers of the routing tables (mirrors oft_moe_routing)

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.oft_abi_version() == 4
+    assert lib.oft_abi_version() == 5
     for s in range(-6, 1):
         assert lib.oft_status_str(s)
     assert b"unknown" in lib.oft_status_str(-99)
@@ -55,6 +55,9 @@ def _desc(**kw):
     (dict(x_dtype=7), _lib.OFT_EDTYPE),
     (dict(w_fmt=9), _lib.OFT_EDTYPE),
     (dict(M=-1), _lib.OFT_EINVAL),
+    (dict(w_fmt=oft.OFT_W_FP4_E2M1), _lib.OFT_OK),  # FP4: the INT4 constraints
+    (dict(w_fmt=oft.OFT_W_FP4_E2M1, g=16), _lib.OFT_EUNSUPPORTED),
+    (dict(w_fmt=oft.OFT_W_FP4_E2M1, K=320, g=128), _lib.OFT_ESHAPE),
 ])
 def test_linear_validation(kw, code):
     d = _desc(**kw)
@@ -119,7 +122,7 @@ def test_cayley_and_dequant_validation():
     assert lib.cayley_build(ok, 4, 24, ok, None, None) == _lib.OFT_EUNSUPPORTED
     assert lib.cayley_build(ok, -1, 32, ok, None, None) == _lib.OFT_EINVAL
     assert lib.cayley_build(None, 0, 32, None, None, None) == _lib.OFT_OK  # empty no-op
-    assert lib.oft_dequant(3, 4, 64, 32, ok, ok, ok, None) == _lib.OFT_EDTYPE
+    assert lib.oft_dequant(9, 4, 64, 32, ok, ok, ok, None) == _lib.OFT_EDTYPE
     assert lib.oft_dequant(0, 4, 60, 32, ok, ok, ok, None) == _lib.OFT_ESHAPE
     assert lib.oft_dequant(0, 4, 64, 48, ok, ok, ok, None) == _lib.OFT_EUNSUPPORTED
     assert lib.oft_dequant(0, 4, 64, 32, ok, None, ok, None) == _lib.OFT_EINVAL
@@ -147,6 +150,8 @@ def _moe(**kw):
     (dict(w_fmt=7), _lib.OFT_EDTYPE),
     (dict(w_fmt=2, g=0), _lib.OFT_OK),  # bf16 reference weights: no group
     (dict(w_fmt=2, g=0, I=96), _lib.OFT_ESHAPE),
+    (dict(w_fmt=3), _lib.OFT_OK),  # FP4 experts
+    (dict(w_fmt=3, g=0), _lib.OFT_EUNSUPPORTED),
 ])
 def test_moe_validation(kw, code):
     d = _moe(**kw)

@@ -49,7 +49,27 @@ SMALL = {
                                    w_fmt="int4", g=32),
     "decode_int4_g64_b16": DenseConfig("decode_int4_g64_b16", M=20, K=768, segs=(96, 64), b=16,
                                        x_dtype="bf16", w_fmt="int4", g=64),
+    # FP4 base (OCP MX E2M1 + E8M0 group exponents) through every forward
+    # kernel and both dX routes: copy ring with the gemm_nn dX, copy ring
+    # with the transposed-weight dX, register prefetch (fp32 x), skinny,
+    # 256-wide-step decode, 64-wide-step decode
+    "fp4_g32_ragged": DenseConfig("fp4_g32_ragged", M=300, K=512, segs=(256, 64, 96), b=32,
+                                  x_dtype="bf16", w_fmt="fp4", g=32),
+    "fp4_g64_wide": DenseConfig("fp4_g64_wide", M=200, K=576, segs=(320, 320), b=32,
+                                x_dtype="bf16", w_fmt="fp4", g=64),
+    "fp4_f32x_b16": DenseConfig("fp4_f32x_b16", M=150, K=384, segs=(96, 96), b=16,
+                                x_dtype="f32", w_fmt="fp4", g=64),
+    "fp4_skinny_f32x": DenseConfig("fp4_skinny_f32x", M=33, K=256, segs=(64, 32), b=32,
+                                   x_dtype="f32", w_fmt="fp4", g=32),
+    "fp4_decode_g32": DenseConfig("fp4_decode_g32", M=48, K=512, segs=(160, 128), b=32, x_dtype="bf16",
+                                  w_fmt="fp4", g=32),
+    "fp4_decode_k576_b16": DenseConfig("fp4_decode_k576_b16", M=20, K=576, segs=(96, 64), b=16,
+                                       x_dtype="bf16", w_fmt="fp4", g=64),
 }
+
+
+def _wfmt(oft, name):
+    return {"int4": oft.OFT_W_INT4, "fp8": oft.OFT_W_FP8_E4M3, "fp4": oft.OFT_W_FP4_E2M1}[name]
 
 
 def _run_gpu(inp, want_bwd=True):
@@ -58,7 +78,7 @@ def _run_gpu(inp, want_bwd=True):
 
     cfg = inp["cfg"]
     xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
-    wf = oft.OFT_W_FP8_E4M3 if cfg.w_fmt == "fp8" else oft.OFT_W_INT4
+    wf = _wfmt(oft, cfg.w_fmt)
     d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
     tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
     q = dev(inp["p"])
@@ -87,7 +107,7 @@ def _run_base(inp):
 
     cfg = inp["cfg"]
     xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
-    wf = oft.OFT_W_FP8_E4M3 if cfg.w_fmt == "fp8" else oft.OFT_W_INT4
+    wf = _wfmt(oft, cfg.w_fmt)
     d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
     tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
     y = torch.full((cfg.M, cfg.N), -7, dtype=tdt, device="cuda")
@@ -100,7 +120,7 @@ def _run_base(inp):
 # prefetch FP8 and INT4 (fp32 x), skinny (fp32 x, few tokens), INT4 decode
 # on 256-wide steps (one and two token tiles), FP8 decode
 BASE_CASES = ["fp8_b32_ragged", "int4_g64_ragged_k", "fp8_b16_f32x", "int4_f32x_wide", "int4_g32_f32x_b32",
-              "decode_int4_g32", "decode_m1", "decode_split_fp8_b16"]
+              "decode_int4_g32", "decode_m1", "decode_split_fp8_b16", "fp4_g64_wide", "fp4_decode_g32"]
 
 
 @pytest.mark.parametrize("name", BASE_CASES)
@@ -162,7 +182,8 @@ def test_cayley_ops_pack_is_bf16_of_f32():
     assert np.array_equal(ops[:, 1], np.swapaxes(want, 1, 2))
 
 
-@pytest.mark.parametrize("fmt,g", [("int4", 32), ("int4", 64), ("int4", 128), ("fp8", 0)])
+@pytest.mark.parametrize("fmt,g", [("int4", 32), ("int4", 64), ("int4", 128), ("fp8", 0), ("fp4", 32),
+                                   ("fp4", 128)])
 def test_dequant_bit_exact(fmt, g):
     import torch
     import orthogonal_fine_tuning_amd as oft
@@ -175,11 +196,17 @@ def test_dequant_bit_exact(fmt, g):
         codes[(codes & 0x7F) == 0x7F] = 0
         inp["w_codes"] = codes
         ref = codec.f32_to_bf16_bits(odense.dequant_fp8_codes(codes).astype(np.float32))
+    elif fmt == "fp4":  # every exponent code 0 .. 254, the high byte of the slot set (ignored)
+        ns = rows * cols // g
+        inp["w_scales"] = ((np.arange(ns) % 255) | 0x5A00).astype(np.uint16).reshape(rows, cols // g)
+        with np.errstate(over="ignore"):
+            ref = codec.f32_to_bf16_bits(odense.dequant_fp4(inp["w_codes"], inp["w_scales"], g)
+                                         .astype(np.float32))
     else:
         ref = codec.f32_to_bf16_bits(odense.dequant_int4(inp["w_codes"], inp["w_scales"], g)
                                      .astype(np.float32))
     out = torch.empty((rows, cols), dtype=torch.int16, device="cuda")
-    wf = oft.OFT_W_FP8_E4M3 if fmt == "fp8" else oft.OFT_W_INT4
+    wf = _wfmt(oft, fmt)
     oft.oft_dequant(wf, rows, cols, g, dev(inp["w_codes"]), dev(inp["w_scales"]), out)
     torch.cuda.synchronize()
     assert np.array_equal(host(out, np.uint16), ref)

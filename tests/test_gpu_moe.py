@@ -46,7 +46,24 @@ SMALL = {
     # 9 to 63 rows per expert on average: 64-row weight-streaming tiles
     "moe_dec64_g128": MoEConfig("moe_dec64_g128", T=100, E=16, k=4, H=256, I=256, g=128, chunk=4, b=32,
                                 q_std=0.05),
+    # FP4 experts (OCP MX E2M1 + E8M0 group exponents) through each grouped
+    # kernel family: copy ring, 16- and 64-row weight streams on 256-wide
+    # steps, and on 64-wide steps (H % 256 != 0)
+    "moe_small_fp4": MoEConfig("moe_small_fp4", T=300, E=16, k=4, H=256, I=128, g=32, chunk=3, b=32,
+                               q_std=0.05, w_fmt="fp4"),
+    "moe_dense_fp4_b16_g64": MoEConfig("moe_dense_fp4_b16_g64", T=256, E=4, k=2, H=192, I=192, g=64, chunk=2,
+                                       b=16, q_std=0.05, w_fmt="fp4"),
+    "moe_decode16_fp4": MoEConfig("moe_decode16_fp4", T=40, E=32, k=4, H=512, I=256, g=32, chunk=3, b=32,
+                                  q_std=0.05, w_fmt="fp4"),
+    "moe_dec64_fp4_g128": MoEConfig("moe_dec64_fp4_g128", T=100, E=16, k=4, H=256, I=256, g=128, chunk=4,
+                                    b=32, q_std=0.05, w_fmt="fp4"),
+    "moe_decode_fp4_h192": MoEConfig("moe_decode_fp4_h192", T=24, E=16, k=3, H=192, I=192, g=64, chunk=5,
+                                     b=16, q_std=0.05, w_fmt="fp4"),
 }
+
+
+def _wfmt(oft, name):
+    return {"int4": oft.OFT_W_INT4, "fp4": oft.OFT_W_FP4_E2M1}[name]
 
 
 def _routing_tensors(T, E, k):
@@ -147,8 +164,9 @@ def _bf16_weights(inp):
     E, H, I, g = cfg.E, cfg.H, cfg.I, cfg.g
     wgu = torch.empty((E, 2 * I, H), dtype=torch.int16, device="cuda")
     wd = torch.empty((E, H, I), dtype=torch.int16, device="cuda")
-    oft.oft_dequant(oft.OFT_W_INT4, E * 2 * I, H, g, dev(inp["wgu_codes"]), dev(inp["wgu_scales"]), wgu)
-    oft.oft_dequant(oft.OFT_W_INT4, E * H, I, g, dev(inp["wd_codes"]), dev(inp["wd_scales"]), wd)
+    wf = _wfmt(oft, cfg.w_fmt)
+    oft.oft_dequant(wf, E * 2 * I, H, g, dev(inp["wgu_codes"]), dev(inp["wgu_scales"]), wgu)
+    oft.oft_dequant(wf, E * H, I, g, dev(inp["wd_codes"]), dev(inp["wd_scales"]), wd)
     return {"wgu_codes": wgu, "wgu_scales": None, "wd_codes": wd, "wd_scales": None}
 
 
@@ -159,7 +177,7 @@ def _run_moe(inp, want_bwd=True, bf16_weights=False):
     cfg = inp["cfg"]
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
     P = T * k
-    w_fmt = oft.OFT_W_BF16 if bf16_weights else oft.OFT_W_INT4
+    w_fmt = oft.OFT_W_BF16 if bf16_weights else _wfmt(oft, cfg.w_fmt)
     d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=w_fmt)
     rtt = _routing_tensors(T, E, k)
     rt = oft.moe_routing(**rtt)
