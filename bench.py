@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qkv_4b")
+    ap.add_argument("--w-fmt", choices=("int4", "fp4"), default=None,
+                    help="run a 4-bit workload with this base format (FP4: OCP MX E2M1 codes, E8M0 group "
+                         "exponents in the same layout and bytes as INT4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="MoE: skip the dense-bf16-weight reference run of the same grouped kernels")
@@ -113,7 +116,7 @@ def dense_bytes(cfg):
     """Algorithmic HBM bytes: what the method must read and write once."""
     M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
     xb = 4 if cfg.x_dtype == "f32" else 2
-    if cfg.w_fmt == "int4":
+    if cfg.w_fmt in ("int4", "fp4"):
         wbytes = N * K // 2 + N * (K // cfg.g) * 2
     else:
         wbytes = N * K + N * 4
@@ -138,7 +141,7 @@ def fwd_kernel_name(cfg):
     """The kernel oft_linear_fwd launches for this shape (one launch per call)."""
     if cfg.x_dtype == "bf16":
         if cfg.M <= 64:
-            return "gemm_nt_dec4_kernel" if cfg.w_fmt == "int4" and cfg.K % 256 == 0 else "gemm_nt_dec_kernel"
+            return "gemm_nt_dec4_kernel" if cfg.w_fmt != "fp8" and cfg.K % 256 == 0 else "gemm_nt_dec_kernel"
         return "gemm_nt_dma_kernel"
     if cfg.M <= 64 and cfg.K % 256 == 0:
         return "gemm_nt_skinny_kernel"
@@ -259,7 +262,8 @@ def run_moe(cfg, args):
 
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
     P = T * k
-    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0)
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0,
+                     w_fmt=oft.OFT_W_FP4_E2M1 if cfg.w_fmt == "fp4" else oft.OFT_W_INT4)
     i32 = dict(dtype=torch.int32, device="cuda")
     rtt = dict(topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32), perm=torch.empty(P, **i32),
@@ -333,7 +337,7 @@ def run_moe(cfg, args):
         "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "experts": E, "top_k": k, "hidden": H,
-                   "expert_intermediate": I, "weights": f"int4_g{cfg.g}", "oft_block": b, "chunk": cfg.chunk,
+                   "expert_intermediate": I, "weights": f"{cfg.w_fmt}_g{cfg.g}", "oft_block": b, "chunk": cfg.chunk,
                    "active_experts": n_active, "parallelism": "single_gpu"},
         "roofline": roofline_object((f_fwd + f_bwd) / (by_fwd + by_bwd) > RIDGE, f_fwd + f_bwd, by_fwd + by_bwd,
                                     t_fwd + t_bwd, kernel="moe fwd+bwd calls", traffic=None),
@@ -379,7 +383,8 @@ def moe_dense_reference(cfg, inp, args, bufs, t_ours):
     for name, rows, cols, out in (("wgu", E * 2 * I, H, wgu), ("wd", E * H, I, wd)):
         codes = torch.from_numpy(np.ascontiguousarray(inp[f"{name}_codes"])).to("cuda")
         scales = torch.from_numpy(np.ascontiguousarray(inp[f"{name}_scales"]).view(np.int16)).to("cuda")
-        oft.oft_dequant(oft.OFT_W_INT4, rows, cols, g, codes, scales, out)
+        oft.oft_dequant(oft.OFT_W_FP4_E2M1 if cfg.w_fmt == "fp4" else oft.OFT_W_INT4, rows, cols, g, codes,
+                        scales, out)
         del codes, scales
     nbf = oft.oft_moe_workspace_bytes(d16, oft.OFT_PASS_FWD)
     nbb = oft.oft_moe_workspace_bytes(d16, oft.OFT_PASS_BWD)
@@ -466,6 +471,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     cfg = CONFIGS[args.config]
+    if args.w_fmt is not None:
+        if cfg.w_fmt not in ("int4", "fp4"):
+            raise SystemExit(f"--w-fmt applies to 4-bit workloads; {cfg.name} has {cfg.w_fmt} weights")
+        cfg = cfg.with_(w_fmt=args.w_fmt)
     if not hasattr(cfg, "segs"):
         print(json.dumps(run_moe(cfg, args)))
         return
@@ -478,7 +487,7 @@ def main():
         return torch.from_numpy(a).to("cuda")
 
     xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
-    wf = oft.OFT_W_FP8_E4M3 if cfg.w_fmt == "fp8" else oft.OFT_W_INT4
+    wf = {"int4": oft.OFT_W_INT4, "fp8": oft.OFT_W_FP8_E4M3, "fp4": oft.OFT_W_FP4_E2M1}[cfg.w_fmt]
     d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
     tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
     q, x = dev(inp["p"]), dev(inp["x"])
@@ -541,7 +550,8 @@ def main():
     fwd_src = FWD_KERNEL_SOURCES
     sha = kernel_source_sha(fwd_src)
     roof = roofline_object(f_fwd / by_fwd > RIDGE, f_fwd, by_fwd, t_kernel, kernel=fwd_kernel_name(cfg),
-                           traffic=load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha))
+                           traffic=None if cfg.w_fmt != CONFIGS[args.config].w_fmt  # counters taken on the stock format
+                           else load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha))
     roof["kernel_timing"] = f"HIP events around {burst} back-to-back launches queued behind a spin, after the timed steps"
     roof["source_sha"] = sha
     f_base = 2 * cfg.M * cfg.N * cfg.K
@@ -556,7 +566,7 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.M, "in_features": cfg.K,
                    "out_features": cfg.N, "segments": list(cfg.segs), "oft_block": cfg.b,
-                   "weights": cfg.w_fmt + (f"_g{cfg.g}" if cfg.w_fmt == "int4" else "_e4m3"),
+                   "weights": cfg.w_fmt + (f"_g{cfg.g}" if cfg.w_fmt != "fp8" else "_e4m3"),
                    "x_dtype": cfg.x_dtype, "parallelism": "single_gpu"},
         "roofline": roof,
         "reference_policy_fwd": base_roof,
