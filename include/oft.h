@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 5
+#define OFT_ABI_VERSION 6
 
 typedef enum {
   OFT_OK = 0,
@@ -182,6 +182,40 @@ int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_
 int32_t oft_linear_fwd(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
                        const void* w_scales, const uint16_t* R_ops, void* y, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* ---- double-buffered adapter slots ----------------------------------------
+ * The pages keep a version number per adapter and stream a new version into
+ * the inactive of two slots while the active one keeps serving, then switch
+ * atomically (the Synced article's "Technical details" section; the
+ * chooseai.io page's "Five design features of the adapter-first
+ * architecture").  The caller owns the two rotation packs R_ops0 / R_ops1
+ * ([nblk, 2, b, b] bf16 each, written by cayley_build) and a device int32
+ * state[3]: [0] the active slot (0 or 1), [1] and [2] the adapter version
+ * held by slot 0 and slot 1.  Zero the state before first use (slot 0
+ * active, version 0).
+ *
+ * oft_slots_switch: after the work enqueued before it on `stream` (the
+ * Cayley build into `slot`), state[1 + slot] = version, then state[0] =
+ * slot, both device-scope release stores: a reader that sees the new slot
+ * sees its version.  Errors: OFT_EINVAL (state NULL or misaligned, slot not
+ * 0 or 1). */
+int32_t oft_slots_switch(int32_t* state, int32_t slot, int32_t version, void* stream);
+
+/* oft_linear_fwd on the active slot.  One thread first copies {active slot,
+ * its version} from state into latch (device int32[2], caller-owned), then
+ * every workgroup of the forward reads latch[0]: one call uses one slot
+ * throughout, and latch[1] names the adapter version that produced y.  The
+ * slot is read when the kernels run, not when they are enqueued, so a graph
+ * captured once follows every later switch.  The double buffer lets a build
+ * into the inactive slot and a switch overlap with forwards on the active
+ * one; a build into a slot must not overlap with a forward that latched
+ * that slot (order them with an event across streams).  Workspace: none.
+ * M == 0 still writes the latch.  Errors: as oft_linear_fwd, and
+ * OFT_EINVAL for a NULL or misaligned state, latch, R_ops0 or R_ops1. */
+int32_t oft_linear_fwd_slots(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
+                             const void* w_scales, const uint16_t* R_ops0, const uint16_t* R_ops1,
+                             const int32_t* state, int32_t* latch, void* y, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* Reference-policy forward: y = x . dequant(W0)^T, the frozen base alone
  * (R = I).  The pages' section "Five design features of the adapter-first

@@ -16,6 +16,7 @@ from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
     "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd",
+    "oft_slots_switch", "oft_linear_fwd_slots",
     "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
     "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_W_FP4_E2M1", "OFT_PASS_FWD",
     "OFT_PASS_BWD",
@@ -95,6 +96,19 @@ def oft_linear_fwd_base(desc, x, w_codes, w_scales, y, ws=None, ws_bytes=0, stre
     _lib.check(_lib.load().oft_linear_fwd_base(C.byref(desc), _ptr(x), _ptr(w_codes), _ptr(w_scales),
                                                _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
                "oft_linear_fwd_base")
+
+
+def oft_slots_switch(state, slot, version, stream=None):
+    _lib.check(_lib.load().oft_slots_switch(_ptr(state), int(slot), int(version), _stream(stream)),
+               "oft_slots_switch")
+
+
+def oft_linear_fwd_slots(desc, x, w_codes, w_scales, R_ops0, R_ops1, state, latch, y, ws=None, ws_bytes=0,
+                         stream=None):
+    _lib.check(_lib.load().oft_linear_fwd_slots(C.byref(desc), _ptr(x), _ptr(w_codes), _ptr(w_scales),
+                                                _ptr(R_ops0), _ptr(R_ops1), _ptr(state), _ptr(latch), _ptr(y),
+                                                _ptr(ws), ws_bytes, _stream(stream)),
+               "oft_linear_fwd_slots")
 
 
 def oft_linear_bwd(desc, dy, y_saved, w_codes, w_scales, R_f32, R_ops, dx=None, dq=None, ws=None,

@@ -52,6 +52,8 @@ SIGNATURES = {
     "oft_linear_workspace_bytes": (_I, [C.POINTER(oft_linear_desc), _I, C.POINTER(_SZ)]),
     "oft_linear_fwd": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oft_linear_fwd_base": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _SZ, _P]),
+    "oft_slots_switch": (_I, [_P, C.c_int32, C.c_int32, _P]),
+    "oft_linear_fwd_slots": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oft_moe_router_bwd": (_I, [C.POINTER(oft_moe_desc), _P, _P, _P, _P, _P]),
     "oft_linear_bwd": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                             _P]),

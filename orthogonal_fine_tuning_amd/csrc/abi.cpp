@@ -158,6 +158,27 @@ int32_t oft_linear_fwd_base(const oft_linear_desc* d, const void* x, const uint8
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int32_t oft_slots_switch(int32_t* state, int32_t slot, int32_t version, void* stream) {
+  if (!ptr_ok(state) || (slot != 0 && slot != 1)) return OFT_EINVAL;
+  return hip_status(oft::launch_slots_switch(state, slot, version, static_cast<hipStream_t>(stream)));
+}
+
+int32_t oft_linear_fwd_slots(const oft_linear_desc* d, const void* x, const uint8_t* w_codes,
+                             const void* w_scales, const uint16_t* R_ops0, const uint16_t* R_ops1,
+                             const int32_t* state, int32_t* latch, void* y, void* ws, size_t ws_bytes,
+                             void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const int32_t v = validate_linear(d);
+  if (v != OFT_OK) return v;
+  if (!ptr_ok(state) || !ptr_ok(latch)) return OFT_EINVAL;
+  if (d->M > 0 && (!ptr_ok(x) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(R_ops0) || !ptr_ok(R_ops1) ||
+                   !ptr_ok(y)))
+    return OFT_EINVAL;
+  return hip_status(oft::launch_linear_fwd_slots(dense_args(d), x, w_codes, w_scales, R_ops0, R_ops1, state, latch,
+                                                 y, static_cast<hipStream_t>(stream)));
+}
+
 int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void* y_saved,
                        const uint8_t* w_codes, const void* w_scales, const float* R_f32,
                        const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,

@@ -37,6 +37,10 @@ struct NtArgs {
   long wc_e, ws_e;  // per-expert strides: code bytes, scale elements
   const uint16_t* rops;
   long rops_e;      // per-expert stride of the rotation operands (elements)
+  // double-buffered adapter: when rops_sel is set, *rops_sel (the slot
+  // latched for this call) picks rops (0) or rops_alt (1) at kernel start
+  const uint16_t* rops_alt;
+  const int* rops_sel;
   void* out;
   long ldo;
   uint16_t* act;    // EPI_ROT_SWIGLU only
@@ -49,6 +53,13 @@ struct NtArgs {
   const int* perm;
   int kslots;
 };
+
+// the rotation operands of this launch (the latched slot of a
+// double-buffered adapter, else rops)
+__device__ __forceinline__ const uint16_t* nt_rops(const NtArgs& p) {
+  if (p.rops_sel == nullptr) return p.rops;
+  return *p.rops_sel == 1 ? p.rops_alt : p.rops;
+}
 
 namespace nt {
 constexpr int BN = 128;
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
     nrows = min(BM, p.M - pos0);
   }
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
-  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
   const float* ws_f = static_cast<const float*>(p.ws);
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
 

@@ -184,7 +184,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   }
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
-  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
   // channel of local weight row rw (0..255), or -1 past the layer's channels
   const int cbase = SWI ? blockIdx.x * (BN / 2) : blockIdx.x * BN;
   auto chan = [&](int rw) -> int {
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_d
   }
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
-  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
   // channel of local weight row rw (0..127), or -1 past the layer's channels
   const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
   auto chan = [&](int rw) -> int {
@@ -983,7 +983,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   }
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
-  const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
+  const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
   const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
   auto chan = [&](int rw) -> int {
     if constexpr (SWI) {

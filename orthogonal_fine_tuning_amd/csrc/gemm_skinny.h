@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
   const int kq = K / 4;
   const int kbeg = wave * kq;
   const int nchunk = kq / 64;
+  const uint16_t* const rops = nt_rops(p);
 
   // weight rows of this lane: nb0 + 32 tn + l32 (always < N: N % (32 TN) == 0)
   const float* ws_f = static_cast<const float*>(p.ws);
@@ -183,12 +184,12 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
       for (int t = 0; t < 2; ++t) {
         uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
         if constexpr (B == 32) {
-          const uint16_t* Rj = p.rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
+          const uint16_t* Rj = rops + (size_t)(nb / 32) * 2048 + l32 * 32 + 16 * t + 4 * g2;
           lo = *reinterpret_cast<const uint2*>(Rj);
           hi = *reinterpret_cast<const uint2*>(Rj + 8);
         } else {
           if ((l32 >> 4) == t) {
-            const uint16_t* Rj = p.rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
+            const uint16_t* Rj = rops + (size_t)(nb / 16 + t) * 512 + (l32 & 15) * 16 + 4 * g2;
             lo = *reinterpret_cast<const uint2*>(Rj);
             hi = *reinterpret_cast<const uint2*>(Rj + 8);
           }

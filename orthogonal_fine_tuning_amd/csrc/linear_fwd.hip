@@ -36,6 +36,8 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       p.wc = wc;
       p.ws = ws;
       p.rops = Rops;
+    p.rops_alt = a.rops_alt;
+    p.rops_sel = a.rops_sel;
       p.out = y;
       p.ldo = a.N;
       p.M = a.M;
@@ -58,6 +60,8 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
     p.wc = wc;
     p.ws = ws;
     p.rops = Rops;
+    p.rops_alt = a.rops_alt;
+    p.rops_sel = a.rops_sel;
     p.out = y;
     p.ldo = a.N;
     p.M = a.M;
@@ -80,6 +84,8 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
   p.wc = wc;
   p.ws = ws;
   p.rops = Rops;
+  p.rops_alt = a.rops_alt;
+  p.rops_sel = a.rops_sel;
   p.out = y;
   p.ldo = a.N;
   p.M = a.M;
@@ -140,6 +146,41 @@ hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* w
 #undef OFT_FWD_B
 #undef OFT_FWD_CASE
   return hipErrorInvalidValue;
+}
+
+// ---- double-buffered adapter slots ----------------------------------------
+// One thread each.  The switch stores the slot's version, then the active
+// index, both as device-scope release stores: a reader that sees the new
+// index (acquire) also sees the version.  The latch snapshots the pair for
+// one forward, whose workgroups then all read the same slot.
+__global__ __launch_bounds__(64) void slots_switch_kernel(int* state, int slot, int version) {
+  if (threadIdx.x != 0) return;
+  __hip_atomic_store(&state[1 + slot], version, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&state[0], slot, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(64) void slots_latch_kernel(const int* state, int* latch) {
+  if (threadIdx.x != 0) return;
+  const int a = __hip_atomic_load(&state[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 1 ? 1 : 0;
+  latch[0] = a;
+  latch[1] = __hip_atomic_load(&state[1 + a], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_slots_switch(int* state, int slot, int version, hipStream_t st) {
+  hipLaunchKernelGGL(slots_switch_kernel, dim3(1), dim3(64), 0, st, state, slot, version);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_fwd_slots(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
+                                   const uint16_t* R0, const uint16_t* R1, const int* state, int* latch, void* y,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(slots_latch_kernel, dim3(1), dim3(64), 0, st, state, latch);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.M == 0) return err;
+  DenseArgs s = a;
+  s.rops_alt = R1;
+  s.rops_sel = latch;
+  return launch_linear_fwd(s, x, wc, ws, R0, y, st);
 }
 
 // The frozen base alone (R = I): y = x . dequant(W0)^T, the same kernels with

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.oft_abi_version() == 5
+    assert lib.oft_abi_version() == 6
     for s in range(-6, 1):
         assert lib.oft_status_str(s)
     assert b"unknown" in lib.oft_status_str(-99)
@@ -157,6 +157,28 @@ def test_moe_validation(kw, code):
     d = _moe(**kw)
     n = C.c_size_t(0)
     assert _lib.load().oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == code
+
+
+def test_slots_validation():
+    lib = _lib.load()
+    ok = C.c_void_p(0x1000)
+    bad = C.c_void_p(0x1004)
+    assert lib.oft_slots_switch(None, 0, 1, None) == _lib.OFT_EINVAL
+    assert lib.oft_slots_switch(bad, 0, 1, None) == _lib.OFT_EINVAL
+    assert lib.oft_slots_switch(ok, 2, 1, None) == _lib.OFT_EINVAL
+    assert lib.oft_slots_switch(ok, -1, 1, None) == _lib.OFT_EINVAL
+    d = _desc()
+    args = [ok] * 8  # x, codes, scales, R_ops0, R_ops1, state, latch, y
+    for i in range(8):
+        a = list(args)
+        a[i] = None
+        assert lib.oft_linear_fwd_slots(C.byref(d), *a, None, 0, None) == _lib.OFT_EINVAL
+        a[i] = bad
+        assert lib.oft_linear_fwd_slots(C.byref(d), *a, None, 0, None) == _lib.OFT_EINVAL
+    assert lib.oft_linear_fwd_slots(C.byref(_desc(b=8)), *args, None, 0, None) == _lib.OFT_EUNSUPPORTED
+    # M == 0: only state and latch are needed
+    a = [None] * 5 + [ok, None, None]
+    assert lib.oft_linear_fwd_slots(C.byref(_desc(M=0)), *a, None, 0, None) == _lib.OFT_EINVAL
 
 
 def test_moe_router_bwd_validation():
