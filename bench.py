@@ -27,7 +27,9 @@ allocated during the timed calls beyond what existed before them) and
 dequantised to bf16 beforehand (``--no-dense-ref`` skips it), with the ratio
 of the INT4 path's time to it.  Dense workloads also report
 ``reference_policy_fwd``: the frozen base alone (``oft_linear_fwd_base``, the
-KL reference), timed the same way as ``roofline``; MoE workloads report
+KL reference), and ``slots_fwd`` (``oft_linear_fwd_slots``: the forward on
+the active slot of a double-buffered adapter, latch launch included), timed
+the same way as ``roofline``; MoE workloads report
 ``router_bwd`` (``oft_moe_router_bwd``: d_logits from the combine-weight
 gradient, outside the step) the same way.  ``phases_cold_us`` times
 fwd and bwd again, each right after evicting the last-level cache, so that
@@ -543,6 +545,13 @@ def main():
     # the reference-policy forward (frozen base alone, oft_linear_fwd_base),
     # timed the same way
     t_base = burst_seconds(stream, lambda: oft.oft_linear_fwd_base(d, x, wc, ws, y, stream=sp), burst)
+    # the forward on the active slot of a double-buffered adapter (one latch
+    # launch, then the same kernels reading the slot through it)
+    state = torch.zeros(4, dtype=torch.int32, device="cuda")
+    latch = torch.zeros(4, dtype=torch.int32, device="cuda")
+    oft.oft_slots_switch(state, 1, 1, stream=sp)
+    t_slots = burst_seconds(stream, lambda: oft.oft_linear_fwd_slots(d, x, wc, ws, Rops, Rops, state, latch, y,
+                                                                     stream=sp), burst)
     f_fwd, f_bwd = dense_flops(cfg)
     by_fwd, by_bwd = dense_bytes(cfg)
     value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
@@ -570,6 +579,9 @@ def main():
                    "x_dtype": cfg.x_dtype, "parallelism": "single_gpu"},
         "roofline": roof,
         "reference_policy_fwd": base_roof,
+        "slots_fwd": {"kernel_us": round(t_slots * 1e6, 2), "plain_fwd_us": round(t_kernel * 1e6, 2),
+                      "overhead_us": round((t_slots - t_kernel) * 1e6, 2),
+                      "timing": "latch + forward per call, same burst timing as roofline"},
         "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
                       "bwd": round(t_bwd * 1e6, 2)},
         "phase_rates": {
