@@ -190,19 +190,19 @@ int32_t oft_linear_fwd(const oft_linear_desc* d, const void* x, const uint8_t* w
  * chooseai.io page's "Five design features of the adapter-first
  * architecture").  The caller owns the two rotation packs R_ops0 / R_ops1
  * ([nblk, 2, b, b] bf16 each, written by cayley_build) and a device int32
- * state[3]: [0] the active slot (0 or 1), [1] and [2] the adapter version
- * held by slot 0 and slot 1.  Zero the state before first use (slot 0
+ * state[2]: [0] the active slot (0 or 1), [1] the adapter version it holds,
+ * kept as one 64-bit word.  Zero the state before first use (slot 0
  * active, version 0).
  *
  * oft_slots_switch: after the work enqueued before it on `stream` (the
- * Cayley build into `slot`), state[1 + slot] = version, then state[0] =
- * slot, both device-scope release stores: a reader that sees the new slot
- * sees its version.  Errors: OFT_EINVAL (state NULL or misaligned, slot not
- * 0 or 1). */
+ * Cayley build into `slot`), state = {slot, version} by one device-scope
+ * atomic 64-bit store, so a reader sees the old pair or the new one, never
+ * a mix.  Errors: OFT_EINVAL (state NULL or misaligned, slot not 0 or
+ * 1). */
 int32_t oft_slots_switch(int32_t* state, int32_t slot, int32_t version, void* stream);
 
 /* oft_linear_fwd on the active slot.  One thread first copies {active slot,
- * its version} from state into latch (device int32[2], caller-owned), then
+ * its version} from state (one atomic 64-bit load) into latch (device int32[2], caller-owned), then
  * every workgroup of the forward reads latch[0]: one call uses one slot
  * throughout, and latch[1] names the adapter version that produced y.  The
  * slot is read when the kernels run, not when they are enqueued, so a graph

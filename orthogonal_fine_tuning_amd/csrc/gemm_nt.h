@@ -38,8 +38,10 @@ struct NtArgs {
   const uint16_t* rops;
   long rops_e;      // per-expert stride of the rotation operands (elements)
   // double-buffered adapter: when rops_sel is set, *rops_sel (the slot
-  // latched for this call) picks rops (0) or rops_alt (1) at kernel start
-  const uint16_t* rops_alt;
+  // latched for this call) picks rops (0) or rops + rops_alt (1): the second
+  // pack is addressed from the first, so every operand pointer stays derived
+  // from the kernel argument
+  long rops_alt;  // elements from rops to the second pack
   const int* rops_sel;
   void* out;
   long ldo;
@@ -57,8 +59,8 @@ struct NtArgs {
 // the rotation operands of this launch (the latched slot of a
 // double-buffered adapter, else rops)
 __device__ __forceinline__ const uint16_t* nt_rops(const NtArgs& p) {
-  if (p.rops_sel == nullptr) return p.rops;
-  return *p.rops_sel == 1 ? p.rops_alt : p.rops;
+  const long off = (p.rops_sel != nullptr && *p.rops_sel == 1) ? p.rops_alt : 0;
+  return p.rops + off;
 }
 
 namespace nt {

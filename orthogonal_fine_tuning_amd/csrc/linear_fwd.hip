@@ -149,21 +149,25 @@ hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* w
 }
 
 // ---- double-buffered adapter slots ----------------------------------------
-// One thread each.  The switch stores the slot's version, then the active
-// index, both as device-scope release stores: a reader that sees the new
-// index (acquire) also sees the version.  The latch snapshots the pair for
-// one forward, whose workgroups then all read the same slot.
+// One thread each.  The state {active slot, its version} is one 64-bit word:
+// the switch stores it and the latch loads it with single device-scope
+// atomics, so a latch sees either the old pair or the new one, never a mix.
+// The rotation pack needs no fence of its own here: the Cayley build before
+// the switch has completed (and released its writes at its kernel boundary)
+// before the switch can store, and the forward kernels start after the
+// latch, with the acquire at their own kernel boundary.
 __global__ __launch_bounds__(64) void slots_switch_kernel(int* state, int slot, int version) {
   if (threadIdx.x != 0) return;
-  __hip_atomic_store(&state[1 + slot], version, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&state[0], slot, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long w = (unsigned long long)(unsigned)slot | ((unsigned long long)(unsigned)version << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(state), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(64) void slots_latch_kernel(const int* state, int* latch) {
   if (threadIdx.x != 0) return;
-  const int a = __hip_atomic_load(&state[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 1 ? 1 : 0;
-  latch[0] = a;
-  latch[1] = __hip_atomic_load(&state[1 + a], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long w =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(state), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  latch[0] = (unsigned)w == 1u ? 1 : 0;
+  latch[1] = (int)(unsigned)(w >> 32);
 }
 
 hipError_t launch_slots_switch(int* state, int slot, int version, hipStream_t st) {
@@ -178,7 +182,7 @@ hipError_t launch_linear_fwd_slots(const DenseArgs& a, const void* x, const uint
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.M == 0) return err;
   DenseArgs s = a;
-  s.rops_alt = R1;
+  s.rops_alt = R1 - R0;  // the second pack, addressed from the first (flat device address space)
   s.rops_sel = latch;
   return launch_linear_fwd(s, x, wc, ws, R0, y, st);
 }

@@ -55,15 +55,15 @@ struct DenseArgs {
   bool xf32, fp8;  // fp8: wf == WF_FP8
   int wf;          // WF_INT4, WF_FP8 or WF_FP4
   // double-buffered adapter (forward only): *rops_sel picks the rotation
-  // pack passed to the launch (0) or rops_alt (1)
-  const uint16_t* rops_alt = nullptr;
+  // pack passed to the launch (0) or the one rops_alt elements after it (1)
+  long rops_alt = 0;
   const int* rops_sel = nullptr;
 };
 
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                              const uint16_t* Rops, void* y, hipStream_t st);
-// adapter slots: state int32[3] = {active slot, version of slot 0, version
-// of slot 1}; the switch writes a slot's version, then makes it active
+// adapter slots: state int32[2] = {active slot, its version}, stored and
+// loaded as one 64-bit word
 hipError_t launch_slots_switch(int* state, int slot, int version, hipStream_t st);
 // forward on the active slot: latch int32[2] <- {active, its version}, then
 // the forward with a.rops_sel = latch over (R0, R1)
