@@ -455,8 +455,8 @@ def moe_cpu_baseline(cfg, inp, n_experts=4):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is a design note only)"}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1 "
+                                   "(sharding over several GPUs is designed, not implemented)"}))
         sys.exit(2)
 
     import numpy as np
