@@ -144,28 +144,33 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
 // dl_{idx_m} = w_m (dw_m - S) and the other experts get 0.  p and w are
 // recomputed from the logits with the arithmetic of moe_topk_kernel (a NaN
 // logit ranks as -inf there and gets no gradient here).  One wave per token.
-template <int NV>  // NV * 64 >= E: logits per lane
+// L lanes per token (a power of two, 16 .. 64; 64 / L tokens per wave), NV
+// logits per lane (L * NV >= E)
+template <int L, int NV>
 __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                              int renorm, const int* __restrict__ idx,
                                                              const float* __restrict__ dw,
                                                              float* __restrict__ dl) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  static_assert(L == 16 || L == 32 || L == 64, "lanes per token");
+  constexpr int TPW = 64 / L;
+  const int lane = threadIdx.x & 63, sl = lane % L;  // lane within the token's group
+  const int t = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW + lane / L;
+  if (t >= T) return;  // whole groups leave together: the shuffles below stay within a group
+  const int g0 = lane - sl;  // first lane of the group
   const float* row = logits + (size_t)t * E;
   // one round trip: the row, the selection and its dw are all in flight
   // before the first is used; the selected logits are read from the row's
   // registers, not loaded again
   int ej = -1;
   float dj = 0.0f;
-  if (lane < k) {
-    ej = idx[(size_t)t * k + lane];
-    dj = dw[(size_t)t * k + lane];
+  if (sl < k) {
+    ej = idx[(size_t)t * k + sl];
+    dj = dw[(size_t)t * k + sl];
   }
   float v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
+    const int e = sl + L * i;
     const float x = e < E ? row[e] : -INFINITY;
     v[i] = x != x ? -INFINITY : x;
   }
@@ -173,11 +178,11 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
 #pragma unroll
   for (int i = 1; i < NV; ++i) mx = fmaxf(mx, v[i]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  for (int off = L / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float p[NV], s = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    p[i] = lane + 64 * i < E ? __expf(v[i] - mx) : 0.0f;
+    p[i] = sl + L * i < E ? __expf(v[i] - mx) : 0.0f;
     s += p[i];
   }
   // dw of the selected experts this lane owns (0 elsewhere); an index
@@ -190,11 +195,11 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
     in[i] = false;
   }
   for (int m = 0; m < k; ++m) {
-    const int em = __builtin_amdgcn_readlane(ej, m);
-    const float dm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dj), m));
+    const int em = __shfl(ej, g0 + m);
+    const float dm = __shfl(dj, g0 + m);
 #pragma unroll
     for (int i = 0; i < NV; ++i)
-      if (em == lane + 64 * i) {
+      if (em == sl + L * i) {
         g[i] = dm;
         in[i] = true;
       }
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
     gp = fmaf(g[i], p[i], gp);
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
+  for (int off = L / 2; off >= 1; off >>= 1) {
     s += __shfl_xor(s, off);
     sel += __shfl_xor(sel, off);
     gp += __shfl_xor(gp, off);
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(256) void moe_router_bwd_kernel(const float* __rest
   float* out = dl + (size_t)t * E;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
+    const int e = sl + L * i;
     if (e < E) {
       const float q = (renorm && !in[i]) ? 0.0f : p[i] / den;
       out[e] = q * (g[i] - S);
@@ -816,23 +821,24 @@ hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutin
 hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,
                                  float* d_logits, hipStream_t st) {
   if (d.T == 0) return hipSuccess;
-  const dim3 grid((d.T + 3) / 4), block(256);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, st, logits, d.T, d.E, d.k, d.renorm, topk_idx, dw, d_logits);
+  auto go = [&](auto kern, int tpw) {  // tpw tokens per wave, four waves per workgroup
+    const int per = 4 * tpw;
+    hipLaunchKernelGGL(kern, dim3((d.T + per - 1) / per), dim3(256), 0, st, logits, d.T, d.E, d.k, d.renorm,
+                       topk_idx, dw, d_logits);
   };
-  const int nv = (d.E + 63) / 64;  // E <= 1024
-  if (nv <= 1)
-    go(moe_router_bwd_kernel<1>);
-  else if (nv <= 2)
-    go(moe_router_bwd_kernel<2>);
-  else if (nv <= 4)
-    go(moe_router_bwd_kernel<4>);
-  else if (nv <= 6)
-    go(moe_router_bwd_kernel<6>);
-  else if (nv <= 8)
-    go(moe_router_bwd_kernel<8>);
+  // E <= 1024, k <= 16 <= L
+  if (d.E <= 64)
+    go(moe_router_bwd_kernel<16, 4>, 4);
+  else if (d.E <= 128)
+    go(moe_router_bwd_kernel<16, 8>, 4);
+  else if (d.E <= 256)
+    go(moe_router_bwd_kernel<32, 8>, 2);
+  else if (d.E <= 384)
+    go(moe_router_bwd_kernel<64, 6>, 1);
+  else if (d.E <= 512)
+    go(moe_router_bwd_kernel<64, 8>, 1);
   else
-    go(moe_router_bwd_kernel<16>);
+    go(moe_router_bwd_kernel<64, 16>, 1);
   return hipGetLastError();
 }
 

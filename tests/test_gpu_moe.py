@@ -114,15 +114,28 @@ def test_routing_bit_exact_config_logits(name):
     _check_routing(cfg, logits, _run_route(cfg, logits))
 
 
+# router-only shapes for the lane-group widths the small configurations miss
+# (33 .. 64 experts: 16 lanes per token; 129 .. 256: 32; 385 .. 512 and
+# 513 .. 1024: 64 with 8 and 16 logits per lane)
+ROUTER = {
+    "router_e60": MoEConfig("router_e60", T=45, E=60, k=5, H=64, I=64, g=32, chunk=4, b=32),
+    "router_e200": MoEConfig("router_e200", T=77, E=200, k=6, H=64, I=64, g=32, chunk=4, b=32, bias_std=0.5),
+    "router_e500": MoEConfig("router_e500", T=50, E=500, k=16, H=64, I=64, g=32, chunk=4, b=32),
+    "router_e1000": MoEConfig("router_e1000", T=33, E=1000, k=16, H=64, I=64, g=32, chunk=4, b=32, bias_std=0.5),
+}
+
+
 @pytest.mark.parametrize("name,renorm", [("moe_small_b32", 0), ("moe_small_g128", 1), ("moe_decode16_b32", 1),
-                                         ("moe_30b_a3b", 0), ("moe_1t_decode", 1), ("moe_1t_train", 0)])
+                                         ("moe_30b_a3b", 0), ("moe_1t_decode", 1), ("moe_1t_train", 0),
+                                         ("router_e60", 1), ("router_e200", 0), ("router_e200", 1),
+                                         ("router_e500", 0), ("router_e1000", 1)])
 def test_router_backward(name, renorm):
     """d_logits through the softmax top-k, the selection from the GPU routing
     (bit-exact against the oracle's) and a seeded dw, against the oracle."""
     import torch
     import orthogonal_fine_tuning_amd as oft
 
-    cfg = SMALL[name] if name in SMALL else CONFIGS[name]
+    cfg = SMALL.get(name) or ROUTER.get(name) or CONFIGS[name]
     print(f"[router bwd] {name} T={cfg.T} E={cfg.E} k={cfg.k} renorm={renorm}", flush=True)
     logits = make_moe_logits(cfg, seed=0)
     got = _run_route(cfg, logits, renorm=renorm)
