@@ -182,7 +182,10 @@ hipError_t launch_linear_fwd_slots(const DenseArgs& a, const void* x, const uint
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.M == 0) return err;
   DenseArgs s = a;
-  s.rops_alt = R1 - R0;  // the second pack, addressed from the first (flat device address space)
+  // the second pack as an element offset from the first, taken on the
+  // integer addresses (both packs live in the one flat device address space
+  // and are 16-byte aligned)
+  s.rops_alt = (long)((intptr_t)R1 - (intptr_t)R0) / (long)sizeof(uint16_t);
   s.rops_sel = latch;
   return launch_linear_fwd(s, x, wc, ws, R0, y, st);
 }
