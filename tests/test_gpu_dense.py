@@ -259,10 +259,14 @@ def test_deterministic_bitwise():
 
 # the QKV layer at 3072 tokens: the forward picks 192-token tiles (128-wide
 # K steps at that tile size) and dX 128-token tiles
-FULL_EXTRA = {"qkv_3072": CONFIGS["qkv_4b"].with_(name="qkv_3072", M=3072)}
+# and the gate/up workloads on an FP4 base, as `bench.py --w-fmt fp4` times them
+FULL_EXTRA = {"qkv_3072": CONFIGS["qkv_4b"].with_(name="qkv_3072", M=3072),
+              "gateup_4b_train_fp4": CONFIGS["gateup_4b_train"].with_(name="gateup_4b_train_fp4", w_fmt="fp4"),
+              "gateup_4b_decode_fp4": CONFIGS["gateup_4b_decode"].with_(name="gateup_4b_decode_fp4", w_fmt="fp4")}
 
 
-@pytest.mark.parametrize("name", ["qkv_4b", "gateup_4b_train", "gateup_4b_decode", "qkv_3072"])
+@pytest.mark.parametrize("name", ["qkv_4b", "gateup_4b_train", "gateup_4b_decode", "qkv_3072", "gateup_4b_train_fp4",
+                                  "gateup_4b_decode_fp4"])
 def test_dense_full_size_sampled(name):
     """Full workload shapes in the launch configuration the benchmark times;
     the oracle checks sampled token rows of y and dX and sampled adapter

@@ -341,9 +341,14 @@ def _sampled_reference(inp, tokens, experts, threads=16):
     return rt, y, dx, dw, dp
 
 
-@pytest.mark.parametrize("name", ["moe_30b_a3b", "moe_1t_train", "moe_1t_decode"])
+# the MoE workloads on FP4 experts, as `bench.py --w-fmt fp4` times them
+MOE_FULL_FP4 = {n + "_fp4": CONFIGS[n].with_(name=n + "_fp4", w_fmt="fp4") for n in ("moe_30b_a3b", "moe_1t_decode")}
+
+
+@pytest.mark.parametrize("name", ["moe_30b_a3b", "moe_1t_train", "moe_1t_decode", "moe_30b_a3b_fp4",
+                                  "moe_1t_decode_fp4"])
 def test_moe_full_size_sampled(name):
-    cfg = CONFIGS[name]
+    cfg = MOE_FULL_FP4.get(name) or CONFIGS[name]
     print(f"[moe full size] {name}: generating inputs", flush=True)
     inp = make_moe(cfg, seed=0)
     print(f"[moe full size] {name}: GPU fwd+bwd", flush=True)
