@@ -20,6 +20,8 @@
 //   permute : rank of a token inside its tile and expert = popcount of the
 //             mask bits below its lane, so positions are stable (expert, then
 //             token).
+#include <utility>
+
 #include "gemm_nn.h"
 #include "gemm_nn_dma.h"
 #include "gemm_nt.h"
@@ -66,33 +68,38 @@ __device__ int block_excl_scan(int v, int* total, int* sh) {
 }
 
 // ---------------------------------------------------------------- top-k
+// L lanes per token (64 / L tokens per wave), NV logits per lane (L NV >= E).
+// Slot j: the largest logit not yet taken, ties to the lower expert id (NaN
+// ranks as -inf, so every slot finds a candidate); lane j of the group keeps
+// slot j.
+template <int L, int NV>
 __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                        int k, int renorm, int* __restrict__ idx,
                                                        float* __restrict__ wout) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  static_assert(L == 16 || L == 32 || L == 64, "lanes per token");
+  static_assert(NV <= 32, "taken mask");
+  constexpr int TPW = 64 / L;
+  const int lane = threadIdx.x & 63, sl = lane % L;
+  const int t = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW + lane / L;
+  if (t >= T) return;  // whole groups leave together: the shuffles below stay within a group
   const float* row = logits + (size_t)t * E;
-  constexpr int MAXV = 16;  // E <= 1024
-  float v[MAXV];
-  const int nv = (E + 63) / 64;
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + 64 * i;
-    const float x = (i < nv && e < E) ? row[e] : -INFINITY;
-    v[i] = x != x ? -INFINITY : x;  // NaN ranks as -inf: every slot finds a candidate
+  for (int i = 0; i < NV; ++i) {
+    const int e = sl + L * i;
+    const float x = e < E ? row[e] : -INFINITY;
+    v[i] = x != x ? -INFINITY : x;
   }
   uint32_t taken = 0;
-  float mx = 0.0f, sel_sum = 0.0f;
-  float sel_v[16];
-  int sel_e[16];
+  float mx = 0.0f, myv = 0.0f;
+  int mye = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const int e = lane + 64 * i;
-      if (i < nv && e < E && !((taken >> i) & 1u)) {
+    for (int i = 0; i < NV; ++i) {
+      const int e = sl + L * i;
+      if (e < E && !((taken >> i) & 1u)) {
         if (v[i] > bv || (v[i] == bv && e < be)) {
           bv = v[i];
           be = e;
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
       }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = L / 2; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oe = __shfl_xor(be, off);
       if (ov > bv || (ov == bv && oe < be)) {
@@ -108,31 +115,26 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
         be = oe;
       }
     }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    sel_v[j] = bv;
-    sel_e[j] = be;
+    if (be % L == sl) taken |= 1u << (be / L);
+    if (sl == j) {
+      myv = bv;
+      mye = be;
+    }
     if (j == 0) mx = bv;
   }
-  float s = 0.0f;
+  float s = 0.0f, sel = sl < k ? __expf(myv - mx) : 0.0f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + 64 * i;
-    if (i < nv && e < E) s += __expf(v[i] - mx);
+  for (int i = 0; i < NV; ++i)
+    if (sl + L * i < E) s += __expf(v[i] - mx);
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) {
+    s += __shfl_xor(s, off);
+    sel += __shfl_xor(sel, off);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  for (int j = 0; j < k; ++j) sel_sum += __expf(sel_v[j] - mx);
-  const float den = renorm ? sel_sum : s;
-  if (lane < k) {
-    float myv = 0.0f;
-    int mye = 0;
-    for (int j = 0; j < k; ++j)
-      if (j == lane) {
-        myv = sel_v[j];
-        mye = sel_e[j];
-      }
-    idx[(size_t)t * k + lane] = mye;
-    wout[(size_t)t * k + lane] = __expf(myv - mx) / den;
+  const float den = renorm ? sel : s;
+  if (sl < k) {
+    idx[(size_t)t * k + sl] = mye;
+    wout[(size_t)t * k + sl] = __expf(myv - mx) / den;
   }
 }
 
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(256) void moe_topk_kernel(const float* __restrict__
 // w_j); renormalised, w is the softmax of the selected logits alone, so
 // dl_{idx_m} = w_m (dw_m - S) and the other experts get 0.  p and w are
 // recomputed from the logits with the arithmetic of moe_topk_kernel (a NaN
-// logit ranks as -inf there and gets no gradient here).  One wave per token.
+// logit ranks as -inf there and gets no gradient here).
 // L lanes per token (a power of two, 16 .. 64; 64 / L tokens per wave), NV
 // logits per lane (L * NV >= E)
 template <int L, int NV>
@@ -555,14 +557,38 @@ MoeWs moe_ws_layout(const MoeDims& d, int pass) {
   return w;
 }
 
+// Lane-group shape of the per-token router kernels (top-k, router backward):
+// f(L, NV) with L lanes per token and NV logits per lane for E experts
+// (E <= 1024; L >= 16 >= k, so a token's k slots live on its own group).
+template <class F>
+static void router_shape(int E, F&& f) {
+  using std::integral_constant;
+  if (E <= 64)
+    f(integral_constant<int, 16>{}, integral_constant<int, 4>{});
+  else if (E <= 128)
+    f(integral_constant<int, 16>{}, integral_constant<int, 8>{});
+  else if (E <= 256)
+    f(integral_constant<int, 32>{}, integral_constant<int, 8>{});
+  else if (E <= 384)
+    f(integral_constant<int, 64>{}, integral_constant<int, 6>{});
+  else if (E <= 512)
+    f(integral_constant<int, 64>{}, integral_constant<int, 8>{});
+  else
+    f(integral_constant<int, 64>{}, integral_constant<int, 16>{});
+}
+
 hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRoutingDev& rt, char* ws,
                             const MoeWs& L, hipStream_t st) {
   const int nt64 = (d.T + 63) / 64;
   int* list = reinterpret_cast<int*>(ws + L.list);
   int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
   if (d.T > 0) {
-    hipLaunchKernelGGL(moe_topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, st, logits, d.T, d.E, d.k, d.renorm,
-                       rt.topk_idx, rt.topk_w);
+    router_shape(d.E, [&](auto l, auto nv) {
+      constexpr int Lc = decltype(l)::value, NVc = decltype(nv)::value;
+      const int per = 4 * (64 / Lc);  // tokens per workgroup
+      hipLaunchKernelGGL((moe_topk_kernel<Lc, NVc>), dim3((d.T + per - 1) / per), dim3(256), 0, st, logits, d.T,
+                         d.E, d.k, d.renorm, rt.topk_idx, rt.topk_w);
+    });
     hipLaunchKernelGGL(moe_count_kernel, dim3(nt64), dim3(64), (size_t)d.E * 8, st, rt.topk_idx, d.T, d.E, d.k,
                        reinterpret_cast<unsigned long long*>(ws + L.gmask));
   }
@@ -821,24 +847,12 @@ hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutin
 hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,
                                  float* d_logits, hipStream_t st) {
   if (d.T == 0) return hipSuccess;
-  auto go = [&](auto kern, int tpw) {  // tpw tokens per wave, four waves per workgroup
-    const int per = 4 * tpw;
-    hipLaunchKernelGGL(kern, dim3((d.T + per - 1) / per), dim3(256), 0, st, logits, d.T, d.E, d.k, d.renorm,
-                       topk_idx, dw, d_logits);
-  };
-  // E <= 1024, k <= 16 <= L
-  if (d.E <= 64)
-    go(moe_router_bwd_kernel<16, 4>, 4);
-  else if (d.E <= 128)
-    go(moe_router_bwd_kernel<16, 8>, 4);
-  else if (d.E <= 256)
-    go(moe_router_bwd_kernel<32, 8>, 2);
-  else if (d.E <= 384)
-    go(moe_router_bwd_kernel<64, 6>, 1);
-  else if (d.E <= 512)
-    go(moe_router_bwd_kernel<64, 8>, 1);
-  else
-    go(moe_router_bwd_kernel<64, 16>, 1);
+  router_shape(d.E, [&](auto l, auto nv) {
+    constexpr int Lc = decltype(l)::value, NVc = decltype(nv)::value;
+    const int per = 4 * (64 / Lc);  // tokens per workgroup
+    hipLaunchKernelGGL((moe_router_bwd_kernel<Lc, NVc>), dim3((d.T + per - 1) / per), dim3(256), 0, st, logits,
+                       d.T, d.E, d.k, d.renorm, topk_idx, dw, d_logits);
+  });
   return hipGetLastError();
 }
 

@@ -139,6 +139,7 @@ def test_router_backward(name, renorm):
     print(f"[router bwd] {name} T={cfg.T} E={cfg.E} k={cfg.k} renorm={renorm}", flush=True)
     logits = make_moe_logits(cfg, seed=0)
     got = _run_route(cfg, logits, renorm=renorm)
+    _check_routing(cfg, logits, got, renorm=bool(renorm))  # the top-k of every lane-group shape, bit-exact
     idx = got["topk_idx"][:cfg.T]
     dw = np.random.default_rng(7).standard_normal((cfg.T, cfg.k)).astype(np.float32)
     d = oft.moe_desc(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.g, cfg.b, cfg.chunk, renorm)
