@@ -297,14 +297,14 @@ def test_dense_full_size_sampled(name):
     assert max(e_y, e_dx, e_dq) <= TOL and orth <= 1e-3
 
 
-@pytest.mark.parametrize("b", [32, 16])
-def test_cayley_many_blocks(b):
-    """Many blocks, the last wave holding fewer than 64 / b of them."""
+@pytest.mark.parametrize("b,nblk", [(32, 3001), (16, 3001), (32, 37), (16, 37), (16, 1), (32, 1)])
+def test_cayley_many_blocks(b, nblk):
+    """Many blocks (one lane per row), and few (two lanes per row: the build
+    of a dense layer), the last wave holding fewer blocks than it can."""
     import torch
     import orthogonal_fine_tuning_amd as oft
     from oft_inputs import to_bf16_bits
 
-    nblk = 3001
     rng = np.random.default_rng(b)
     p = to_bf16_bits(rng.normal(0.0, 0.3, size=(nblk, b * (b - 1) // 2)).astype(np.float32))
     Rf = torch.empty((nblk, b, b), dtype=torch.float32, device="cuda")
