@@ -550,11 +550,15 @@ def main():
     state = torch.zeros(4, dtype=torch.int32, device="cuda")
     latch = torch.zeros(4, dtype=torch.int32, device="cuda")
     oft.oft_slots_switch(state, 1, 1, stream=sp)
-    t_slots = burst_seconds(stream, lambda: oft.oft_linear_fwd_slots(d, x, wc, ws, Rops, Rops, state, latch, y,
-                                                                     stream=sp), burst)
-    # the plain forward again right after, so that the comparison brackets
-    # the slot burst in time (sustained matrix-core load lowers the clock)
-    t_plain2 = burst_seconds(stream, lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp), burst)
+    # slot and plain bursts alternate three times and each side takes its
+    # median: a single burst pair is at the mercy of where it falls in the
+    # clock's response to sustained matrix-core load
+    ts, tp = [], []
+    for _ in range(3):
+        ts.append(burst_seconds(stream, lambda: oft.oft_linear_fwd_slots(d, x, wc, ws, Rops, Rops, state, latch, y,
+                                                                         stream=sp), burst))
+        tp.append(burst_seconds(stream, lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp), burst))
+    t_slots, t_plain2 = float(np.median(ts)), float(np.median(tp))
     f_fwd, f_bwd = dense_flops(cfg)
     by_fwd, by_bwd = dense_bytes(cfg)
     value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
@@ -584,8 +588,8 @@ def main():
         "reference_policy_fwd": base_roof,
         "slots_fwd": {"kernel_us": round(t_slots * 1e6, 2), "plain_fwd_us": round(t_plain2 * 1e6, 2),
                       "overhead_us": round((t_slots - t_plain2) * 1e6, 2),
-                      "timing": "latch + forward per call, same burst timing as roofline; the plain forward "
-                                "burst right after it for comparison"},
+                      "timing": "latch + forward per call, same burst timing as roofline; medians of three "
+                                "slot bursts alternating with three plain-forward bursts"},
         "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
                       "bwd": round(t_bwd * 1e6, 2)},
         "phase_rates": {
