@@ -76,8 +76,10 @@ enum { OFT_DT_BF16 = 0, OFT_DT_F32 = 1 };
 /* OFT_W_BF16: weights already dequantised to bf16 (MoE calls only; the
  * dense-weight reference that the grouped dequant GEMMs are measured
  * against: same kernels, no scales, two bytes per weight in HBM). */
-/* OFT_W_FP4_E2M1: an FP4 base (the pages' "Architectural advantages of OFT
- * over LoRA" section names one) in the OCP Microscaling form: E2M1 codes
+/* OFT_W_FP4_E2M1: an FP4 base (the chooseai.io page's "Technical
+ * principles" section lists FP4 among the frozen base precisions, and the
+ * Synced article's DeepSeek V4 Flash experiment trains a BF16 adapter on an
+ * FP4 base) in the OCP Microscaling form: E2M1 codes
  * (1 sign, 2 exponent bits with bias 1, 1 fraction bit; 0, 0.5, 1, 1.5, 2,
  * 3, 4, 6 and their negatives), two per byte, low nibble first, exactly as
  * INT4 codes; one scale slot per group of g codes along K, also as INT4, but
@@ -93,7 +95,10 @@ enum { OFT_PASS_FWD = 0, OFT_PASS_BWD = 1 };
 /* Dense OFT linear layer: x [M, K] -> y [M, N], N = sum(seg).
  * Constraints: M >= 0 (M == 0 is a no-op); K >= 64 and K % 64 == 0;
  * b in {16, 32}; 1 <= n_seg <= 8, every seg[s] > 0 and seg[s] % b == 0,
- * N % 32 == 0; INT4 and FP4: g in {32, 64, 128} and K % g == 0. */
+ * N % 32 == 0; INT4 and FP4: g in {32, 64, 128} and K % g == 0.
+ * Size range (else OFT_EUNSUPPORTED): M <= 2^22, K and N <= 2^20 and
+ * N * K < 2^31 (token tiles run along the launch grid's y dimension, and
+ * weight offsets inside the kernels are 32-bit). */
 typedef struct {
   int32_t M, K, N;
   int32_t x_dtype; /* OFT_DT_BF16 | OFT_DT_F32; y and dx use the same dtype */
@@ -116,7 +121,9 @@ typedef struct {
  * Constraints: T >= 0; 1 <= k <= 16; k <= E <= 1024; H % 64 == 0;
  * I % 64 == 0; b in {16, 32}; I % b == 0; INT4 and FP4: g in {32, 64,
  * 128}, H % g == 0, I % g == 0; chunk >= 1; renorm in {0, 1}; w_fmt one of
- * the three formats above (else OFT_EDTYPE). */
+ * the three formats above (else OFT_EDTYPE).  Size range (else
+ * OFT_EUNSUPPORTED): H and I <= 2^16, ceil(T k / 16) + E <= 65535 (the
+ * grouped work list runs along the launch grid's y dimension). */
 typedef struct {
   int32_t T, E, k, H, I, g, b;
   int32_t chunk;  /* active experts per chunk (scheduling unit)            */
@@ -204,7 +211,10 @@ int32_t oft_slots_switch(int32_t* state, int32_t slot, int32_t version, void* st
 /* oft_linear_fwd on the active slot.  One thread first copies {active slot,
  * its version} from state (one atomic 64-bit load) into latch (device int32[2], caller-owned), then
  * every workgroup of the forward reads latch[0]: one call uses one slot
- * throughout, and latch[1] names the adapter version that produced y.  The
+ * throughout, and latch[1] names the adapter version that produced y.
+ * Every call in flight needs a latch of its own: a later call on another
+ * stream (or another branch of a graph) writing the same latch while an
+ * earlier forward still reads it could switch that forward's slot midway.  The
  * slot is read when the kernels run, not when they are enqueued, so a graph
  * captured once follows every later switch.  The double buffer lets a build
  * into the inactive slot and a switch overlap with forwards on the active

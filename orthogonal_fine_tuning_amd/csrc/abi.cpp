@@ -35,7 +35,11 @@ bool w4(int f) { return f == OFT_W_INT4 || f == OFT_W_FP4_E2M1; }
 int32_t validate_linear(const oft_linear_desc* d) {
   if (d == nullptr) return OFT_EINVAL;
   if (d->M < 0 || d->K <= 0 || d->N <= 0) return OFT_EINVAL;
-  if (d->M > (1 << 24) || d->K > (1 << 20) || d->N > (1 << 20)) return OFT_EUNSUPPORTED;
+  // index range of the kernels: token tiles of 128 run along grid y (at
+  // most 65535 workgroups), and weight element / scale offsets are 32-bit
+  // (N K < 2^31 keeps N K / g fp16 scale bytes far inside as well)
+  if (d->M > (1 << 22) || d->K > (1 << 20) || d->N > (1 << 20)) return OFT_EUNSUPPORTED;
+  if ((long long)d->N * d->K >= (1LL << 31)) return OFT_EUNSUPPORTED;
   if (d->x_dtype != OFT_DT_BF16 && d->x_dtype != OFT_DT_F32) return OFT_EDTYPE;
   if (!w4(d->w_fmt) && d->w_fmt != OFT_W_FP8_E4M3) return OFT_EDTYPE;
   if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;

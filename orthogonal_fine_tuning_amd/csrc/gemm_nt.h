@@ -157,11 +157,11 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
     }
     const size_t n = (size_t)wchan;
     if constexpr (FP8) {
-      const uint8_t* src = wc + n * K + k0 + 32 * w_half;
+      const uint8_t* src = wc + (size_t)n * K + k0 + 32 * w_half;
       wr[0] = w_ok ? *reinterpret_cast<const uint4*>(src) : zero4();
       wr[1] = w_ok ? *reinterpret_cast<const uint4*>(src + 16) : zero4();
     } else {
-      const uint8_t* src = wc + n * (K / 2) + k0 / 2 + 16 * w_half;
+      const uint8_t* src = wc + (size_t)n * (K / 2) + k0 / 2 + 16 * w_half;
       wr[0] = w_ok ? *reinterpret_cast<const uint4*>(src) : zero4();
       wsb = w_ok ? ws_h[n * (K / p.g) + (k0 + 32 * w_half) / p.g] : (uint16_t)0;
     }

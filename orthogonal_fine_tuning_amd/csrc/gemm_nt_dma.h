@@ -14,7 +14,7 @@
 // stored, then act = silu(gate) * up, the up waves handing their bf16
 // outputs to the gate waves through LDS.
 //
-// Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 128, 192, 256), K
+// Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 128 or 192), K
 // steps of 64.  FP8 and bf16 weights: wave (wn, wm) = (wave % 4, wave / 4)
 // owns channels 64 wn + [0, 64) and tokens wm BM / 2 + [0, BM / 2).  INT4
 // weights on 128-token tiles: wave wn owns channels 32 wn + [0, 32) and every
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
     NtArgs p) {
   using namespace ntd;
   static_assert(KB == 64 || (KB == 128 && WF == WF_FP8 && BM <= 192 && !GROUPED), "128-wide K steps: FP8, <= 192 tokens");
-  static_assert(BM == 128 || BM == 192 || BM == 256, "tile");
+  static_assert(BM == 128 || BM == 192, "tile");
   static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
   static_assert(EPI != EPI_ROT_SWIGLU || BM == 128, "exchange buffer sized for 128-token tiles");
@@ -135,8 +135,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
   // wave layout: INT4 weights on 128-token tiles, 8 waves x 32 channels over
   // every token of the tile (each code row is dequantised by one wave only);
-  // otherwise 4 x 2 waves of 64 channels x BM / 2 tokens (with 256 tokens
-  // the matrix work per dequantised operand is already large enough)
+  // otherwise 4 x 2 waves of 64 channels x BM / 2 tokens
   constexpr bool W8 = wf_4bit(WF) && BM == 128;
   constexpr int TN = W8 ? 1 : 2;              // 32-channel tiles per wave
   constexpr int TM = W8 ? BM / 32 : BM / 64;  // 32-token tiles per wave

@@ -61,12 +61,12 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
     for (int tn = 0; tn < TN; ++tn) {
       const size_t n = (size_t)(nb0 + 32 * tn + l32);
       if constexpr (FP8) {
-        const uint8_t* src = p.wc + n * K + kk;
+        const uint8_t* src = p.wc + (size_t)n * K + kk;
         ch.w[tn][0] = *reinterpret_cast<const uint4*>(src);
         ch.w[tn][1] = *reinterpret_cast<const uint4*>(src + 16);
         ch.s[tn] = 0;
       } else {
-        ch.w[tn][0] = *reinterpret_cast<const uint4*>(p.wc + n * (K / 2) + kk / 2);
+        ch.w[tn][0] = *reinterpret_cast<const uint4*>(p.wc + (size_t)n * (K / 2) + kk / 2);
         ch.s[tn] = ws_h[n * (K / p.g) + kk / p.g];
       }
     }

@@ -611,11 +611,8 @@ hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz
   p.g = 64;
   const int ntl = (a.K + ntd::BN - 1) / ntd::BN;
   if constexpr (FP8) {
-    const int bm = pick_token_tile(ntl, a.M, num_cus(), 256);
-    if (bm == 256)
-      hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 256, EPI_PLAIN, XF32>), dim3(ntl, (a.M + 255) / 256),
-                         dim3(ntd::NTHR), 0, st, p);
-    else if (bm == 192 && a.N % 128 == 0)  // 128-wide K steps
+    const int bm = pick_token_tile(ntl, a.M, num_cus(), 192);
+    if (bm == 192 && a.N % 128 == 0)  // 128-wide K steps
       hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, 32, 192, EPI_PLAIN, XF32, false, 128>),
                          dim3(ntl, (a.M + 191) / 192), dim3(ntd::NTHR), 0, st, p);
     else if (bm == 192)

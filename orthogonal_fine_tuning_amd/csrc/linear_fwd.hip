@@ -95,11 +95,8 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
   if constexpr (!XF32) {
     if (a.K % ntd::BK == 0) {
       const int nt = (a.N + ntd::BN - 1) / ntd::BN;
-      const int bm = pick_token_tile(nt, a.M, num_cus(), 256);
-      if (bm == 256)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 256, EPI, false>), dim3(nt, (a.M + 255) / 256),
-                           dim3(ntd::NTHR), 0, st, p);
-      else if (bm == 192 && FP8 && a.K % 128 == 0)  // FP8: 128-wide K steps
+      const int bm = pick_token_tile(nt, a.M, num_cus(), 192);
+      if (bm == 192 && FP8 && a.K % 128 == 0)  // FP8: 128-wide K steps
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_FP8, B, 192, EPI, false, false, 128>),
                            dim3(nt, (a.M + 191) / 192), dim3(ntd::NTHR), 0, st, p);
       else if (bm == 192)

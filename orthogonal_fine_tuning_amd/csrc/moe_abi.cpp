@@ -16,7 +16,11 @@ int32_t validate_moe(const oft_moe_desc* d) {
   if (d == nullptr) return OFT_EINVAL;
   if (d->T < 0 || d->E <= 0 || d->k <= 0 || d->H <= 0 || d->I <= 0 || d->chunk < 1) return OFT_EINVAL;
   if (d->k > 16 || d->E > 1024 || d->k > d->E) return OFT_EUNSUPPORTED;
-  if ((long long)d->T * d->k > (1LL << 30) || d->H > (1 << 16) || d->I > (1 << 16)) return OFT_EUNSUPPORTED;
+  // the grouped work lists run along grid y (at most 65535 workgroups): the
+  // finest, 16-row tiles of the few-rows-per-expert forward, number at most
+  // ceil(T k / 16) + E
+  if (d->H > (1 << 16) || d->I > (1 << 16)) return OFT_EUNSUPPORTED;
+  if (((long long)d->T * d->k + 15) / 16 + d->E > 65535) return OFT_EUNSUPPORTED;
   if (d->b != 16 && d->b != 32) return OFT_EUNSUPPORTED;
   if (d->w_fmt != OFT_W_INT4 && d->w_fmt != OFT_W_FP4_E2M1 && d->w_fmt != OFT_W_BF16) return OFT_EDTYPE;
   const bool w4 = d->w_fmt != OFT_W_BF16;  // INT4 or FP4: codes + group scales

@@ -65,6 +65,21 @@ def test_linear_validation(kw, code):
     assert _lib.load().oft_linear_workspace_bytes(C.byref(d), 1, C.byref(n)) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=1 << 22), _lib.OFT_OK),                       # 32768 token tiles of 128 along grid y
+    (dict(M=(1 << 22) + 1), _lib.OFT_EUNSUPPORTED),
+    (dict(M=64, K=1984, segs=(1 << 20,), b=32), _lib.OFT_OK),  # N K = 2^31 - 2^26
+    (dict(M=64, K=2048, segs=(1 << 20,), b=32), _lib.OFT_EUNSUPPORTED),  # N K = 2^31: 32-bit offsets
+    (dict(M=64, K=1 << 21, segs=(128,)), _lib.OFT_EUNSUPPORTED),
+])
+def test_linear_size_range(kw, code):
+    """The descriptor's sizes stay inside the kernels' index range: the
+    launch grid's y limit for token tiles and 32-bit weight offsets."""
+    d = _desc(**kw)
+    n = C.c_size_t(0)
+    assert _lib.load().oft_linear_workspace_bytes(C.byref(d), 1, C.byref(n)) == code
+
+
 def test_linear_segment_sum_mismatch():
     d = _desc()
     d.N = 512
@@ -154,6 +169,18 @@ def _moe(**kw):
     (dict(w_fmt=3, g=0), _lib.OFT_EUNSUPPORTED),
 ])
 def test_moe_validation(kw, code):
+    d = _moe(**kw)
+    n = C.c_size_t(0)
+    assert _lib.load().oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=262076, E=16, k=4), _lib.OFT_OK),            # ceil(T k / 16) + E = 65535
+    (dict(T=262077, E=16, k=4), _lib.OFT_EUNSUPPORTED),  # 65536 work-list tiles along grid y
+    (dict(H=1 << 17), _lib.OFT_EUNSUPPORTED),
+    (dict(I=1 << 17), _lib.OFT_EUNSUPPORTED),
+])
+def test_moe_size_range(kw, code):
     d = _moe(**kw)
     n = C.c_size_t(0)
     assert _lib.load().oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == code

@@ -101,6 +101,65 @@ def test_fp8_q_zero_reproduces_base_output_exactly():
     assert np.array_equal(dense.forward(x, W, R), x @ W.T)
 
 
+def _fp8_golden():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_channel_scale.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    n = np.array([int(r[0]) for r in rows])
+    s = np.array([int(r[1], 16) for r in rows], dtype=np.uint32).view(np.float32)
+    c = np.array([int(r[2], 16) for r in rows], dtype=np.uint8)
+    v = np.array([float(r[3]) for r in rows])
+    return n, s, c, v
+
+
+def test_fp8_channel_scale_golden():
+    """The per-channel scale multiplies the decoded code of its own row (the
+    golden table: products of OCP E4M3 values and fp32 scales)."""
+    n, s, c, v = _fp8_golden()
+    rows = int(n.max()) + 1
+    scales = np.zeros(rows, dtype=np.float32)
+    scales[n] = s
+    # one code per column, on its own row, the other rows' entries zero
+    codes = np.zeros((rows, n.size), dtype=np.uint8)
+    codes[n, np.arange(n.size)] = c
+    W = dense.dequant_fp8(codes, scales)
+    got = W[n, np.arange(n.size)]
+    assert np.array_equal(got, v) and np.array_equal(np.signbit(got), np.signbit(v))
+
+
+def _fp8_source_weights(cfg, seed):
+    """The generator's fp32 weights before quantisation (same seeded stream:
+    x is drawn first, then w ~ N(0, 1))."""
+    rng = np.random.default_rng(seed)
+    rng.standard_normal((cfg.M, cfg.K), dtype=np.float32)
+    return rng.standard_normal((cfg.N, cfg.K), dtype=np.float32).astype(np.float64)
+
+
+def _fp8_reconstructs(W, w, s):
+    # e4m3fn keeps 3 fraction bits: a normal value is within 2^-4 relative
+    # of what was encoded; below 2^-6 the spacing is 2^-9, so the absolute
+    # error is at most 2^-10 (times the row scale)
+    tol = np.maximum(np.abs(w) * 2.0 ** -4, 2.0 ** -10 * s[:, None])
+    return bool(np.all(np.abs(W - w) <= tol * (1 + 1e-12)))
+
+
+def test_fp8_dequant_reconstructs_generator_weights():
+    """code * s[n] gives back the generator's w to e4m3 rounding (w / s was
+    encoded, s[n] = max_k |w[n, k]| / 448); dividing by the scale, or taking
+    it along the wrong axis, does not (planted mistakes)."""
+    cfg = CONFIGS["qkv_4b"].with_(M=8, K=192, segs=(96, 64, 32))
+    inp = make_dense(cfg, seed=3)
+    w = _fp8_source_weights(cfg, 3)
+    s = np.asarray(inp["w_scales"], dtype=np.float64)
+    assert _fp8_reconstructs(dense.dequant(inp), w, s)
+    e = dense.dequant_fp8_codes(inp["w_codes"])
+    wrong = {"divided by the scale": e / s[:, None],
+             "scale of another row": e * np.roll(s, 1)[:, None],
+             "scale along the in-features": e * np.resize(s, cfg.K)[None, :]}
+    for name, Wb in wrong.items():
+        assert not _fp8_reconstructs(Wb, w, s), name
+
+
 def test_base_forward_is_the_q_zero_layer():
     """The reference-policy layer (frozen base alone) is the adapted layer at
     Q = 0 exactly, and differs from it once the adapter has moved."""
