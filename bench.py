@@ -1,39 +1,48 @@
 #!/usr/bin/env python3
 """Benchmark of the OFT dequant-GEMM hot path on one MI355X.
 
-One step = one pass of the whole dense path over one batch: Cayley build of
-the adapter rotations, the forward (dequant GEMM + split-projection rotation
-epilogue) and the backward (dX with the rotation prologue, and dQ).  The
-default workload is the fused Q/K/V projection of a 4B-shaped model: 4096
-tokens, hidden 2560, out 6144 = 4096 + 1024 + 1024, FP8 e4m3 weights with
-per-channel scales, OFT blocks of 32.  Inputs are seeded synthetic data,
-resident in HBM before timing starts.
+A step is one pass of the whole path over one batch of a workload: the
+Cayley build of the adapter rotations, the forward and the backward (dense:
+dX and dQ; MoE: routing, grouped gate/up with the per-expert rotation,
+SwiGLU, down, combine, and dX, dQ and the combine-weight gradient dw).
+Inputs are seeded synthetic data (``oft_inputs``), resident in HBM before
+timing starts.
 
-Prints ONE JSON line (rank 0).  ``value`` is algorithmic TFLOP/s of the
-whole step (fwd 2MNK + 2MNb, bwd 2MNK + 4MNb; the Cayley build is timed but
-its flops are not counted).  ``roofline`` reports the forward GEMM kernel:
-algorithmic flops per launch over its mean duration against the bf16
-matrix peak, or, for shapes below the ridge point (312.5 flop per byte:
-the weight streams of few-token layers), algorithmic bytes per launch
-against HBM; the duration comes from HIP events on the launch stream
-around a burst of back-to-back forward launches right after the timed
-steps, queued behind a short GPU spin so that the host's cost per call
-leaves no gaps (``phases_us`` comes from events around each phase of every
-timed step and also counts the idle time an event boundary adds).
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.  MoE workloads also report ``transient_bytes`` (peak device memory
-allocated during the timed calls beyond what existed before them) and
-``dense_bf16_reference``: the same fwd + bwd calls on every expert's weights
-dequantised to bf16 beforehand (``--no-dense-ref`` skips it), with the ratio
-of the INT4 path's time to it.  Dense workloads also report
-``reference_policy_fwd``: the frozen base alone (``oft_linear_fwd_base``, the
-KL reference), and ``slots_fwd`` (``oft_linear_fwd_slots``: the forward on
-the active slot of a double-buffered adapter, latch launch included), timed
-the same way as ``roofline``; MoE workloads report
-``router_bwd`` (``oft_moe_router_bwd``: d_logits from the combine-weight
-gradient, outside the step) the same way.  ``phases_cold_us`` times
-fwd and bwd again, each right after evicting the last-level cache, so that
-the weights stream from HBM.
+By default every workload runs: the seven shapes of the OFT layer (fused
+Q/K/V of a 4B model, gate/up of a 4B model at a training token count and a
+decode batch, the tiny parity shape, a 30B-A3B MoE layer and one GPU's share
+of a ~1T MoE layer at a training token count and a decode batch).  The
+printed line is the largest single-GPU workload, the ~1T-shaped MoE layer at
+4096 tokens (``--config`` picks another, or ``all``); every workload's
+figures are under ``workloads``.
+
+Per workload:
+  * ``value``: algorithmic TFLOP/s of the whole step (dense fwd 2MNK + 2MNb,
+    bwd 2MNK + 4MNb; MoE fwd 2P.H.2I + 2P.I.H + 2P.2I.b, bwd the same GEMMs
+    + 4P.2I.b; the Cayley build is timed inside the step but its flops are
+    not counted), over the wall time of K steps bracketed by syncs;
+  * ``step_roofline``: that step against the bound of its arithmetic
+    intensity (algorithmic flop per algorithmic HBM byte): the bf16 matrix
+    peak above the ridge point (312.5 flop/B), HBM below it;
+  * ``kernels``: the library's per-step kernel times, from HIP events the
+    library records on the launch stream around each step of its work
+    (``oft_prof_*``), averaged over profiled steps run right after the timed
+    ones;
+  * ``roofline``: the dominant kernel step (the largest time per step): its
+    algorithmic flops or bytes per launch over its average duration, against
+    the matrix peak or HBM by its own intensity; ``traffic`` is the HBM
+    bytes per launch from committed rocprofv3 counter runs
+    (``profiles/traffic.json``), null when the kernel sources changed since;
+  * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample of the
+    workload (token rows for dense layers, a few experts for MoE layers);
+  * MoE: ``transient_bytes`` (device memory allocated during the timed calls
+    beyond what existed before: the library allocates nothing) and
+    ``dense_bf16_reference`` (the same calls on every expert's weights
+    dequantised to bf16 beforehand; the ratio of the 4-bit path's time to
+    it); dense: ``reference_policy_fwd`` (the frozen base alone) and
+    ``slots_fwd`` (the forward on the active slot of a double-buffered
+    adapter), timed as bursts of back-to-back launches; ``phases_cold_us``:
+    fwd and bwd again, each right after evicting the last-level cache.
 """
 from __future__ import annotations
 
@@ -51,26 +60,83 @@ METRIC = "OFT dequant-GEMM fwd+bwd TFLOP/s and HBM GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte where the two meet (312.5)
+HEADLINE = "moe_1t_train"
+ORDER = ["moe_1t_train", "qkv_4b", "gateup_4b_train", "gateup_4b_decode", "tiny_qkv", "moe_30b_a3b",
+         "moe_1t_decode"]
+SOURCES = "orthogonal_fine_tuning_amd/csrc"
 
 
-def roofline_object(mfma_bound, flops, nbytes, seconds, kernel, traffic):
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="all", help="a workload name, or 'all' (the default)")
+    ap.add_argument("--w-fmt", choices=("int4", "fp4"), default=None,
+                    help="run the 4-bit workloads with this base format (FP4: OCP MX E2M1 codes, E8M0 group "
+                         "exponents in the same layout and bytes as INT4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-ref", action="store_true",
+                    help="MoE: skip the dense-bf16-weight reference run of the same grouped kernels")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip phases_cold_us (keeps a profiler's kernel averages to the timed steps)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the reference-policy, slot and router-backward bursts")
+    ap.add_argument("--prof-steps", type=int, default=5, help="steps timed kernel by kernel after the timed ones")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="about this much oracle work per non-headline workload (3x for the headline)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (a reference "
+                         "for HBM byte counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ rooflines
+def roofline(flops, nbytes, seconds, kernel=None, traffic=None):
     """Above the ridge point: algorithmic TFLOP/s against the bf16 matrix
-    peak; below it (the weight streams of few-token shapes): algorithmic
-    GB/s against HBM."""
-    if mfma_bound:
+    peak; below it: algorithmic GB/s against HBM."""
+    mfma = nbytes == 0 or flops / nbytes > RIDGE
+    if mfma:
         achieved, peak, unit = flops / seconds / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s"
-    return {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel,
-            "kernel_us": round(seconds * 1e6, 2), "algorithmic_flops": int(flops), "algorithmic_bytes": int(nbytes)}
+    out = {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4)}
+    if kernel is not None:
+        out["traffic"] = traffic
+        out["kernel"] = kernel
+    out.update({"us": round(seconds * 1e6, 2), "algorithmic_flops": int(flops), "algorithmic_bytes": int(nbytes)})
+    return out
+
+
+def source_sha():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, SOURCES)
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(key, sha):
+    """HBM bytes per launch of a kernel step from the committed counter runs,
+    or None when the sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get("entries", {}).get(key)
+    if not ent or data.get("source_sha") != sha:
+        return None
+    return ent.get("bytes_per_launch")
 
 
 def burst_seconds(stream, launch, n=10):
     """Mean duration of one of n back-to-back launches: HIP events on the
-    launch stream around the burst.  A short GPU spin is queued first, so
-    every launch is already in the queue when the first event fires and the
-    host's cost per call adds no idle time between the kernels."""
+    launch stream around the burst, queued behind a short GPU spin so that
+    the host's cost per call adds no idle time between the kernels."""
     import torch
 
     eb = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -85,120 +151,27 @@ def burst_seconds(stream, launch, n=10):
     return eb[0].elapsed_time(eb[1]) * 1e-3 / n
 
 
-def parse():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="qkv_4b")
-    ap.add_argument("--w-fmt", choices=("int4", "fp4"), default=None,
-                    help="run a 4-bit workload with this base format (FP4: OCP MX E2M1 codes, E8M0 group "
-                         "exponents in the same layout and bytes as INT4)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense-ref", action="store_true",
-                    help="MoE: skip the dense-bf16-weight reference run of the same grouped kernels")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip phases_cold_us (keeps a profiler's kernel averages to the timed steps)")
-    ap.add_argument("--cpu-rows", type=int, default=1 << 30,
-                    help="token rows of the oracle sample for cpu_baseline")
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="run one plain device copy of this many MiB before timing (a reference "
-                         "for HBM byte counters)")
-    return ap.parse_args()
+def profile_steps(step, nsteps):
+    """Per-step kernel times from the library's own HIP events (averaged over
+    nsteps steps): {name: (milliseconds per step, launches per step)}."""
+    import torch
 
+    import orthogonal_fine_tuning_amd as oft
 
-def dense_flops(cfg):
-    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
-    fwd = 2 * M * N * K + 2 * M * N * b
-    bwd = 2 * M * N * K + 4 * M * N * b
-    return fwd, bwd
-
-
-def dense_bytes(cfg):
-    """Algorithmic HBM bytes: what the method must read and write once."""
-    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
-    xb = 4 if cfg.x_dtype == "f32" else 2
-    if cfg.w_fmt in ("int4", "fp4"):
-        wbytes = N * K // 2 + N * (K // cfg.g) * 2
-    else:
-        wbytes = N * K + N * 4
-    nblk = N // b
-    rops = nblk * 2 * b * b * 2
-    rf = nblk * b * b * 4
-    npair = b * (b - 1) // 2
-    fwd = wbytes + M * K * xb + M * N * xb + rops
-    bwd = wbytes + M * N * 2 + M * N * xb + M * K * xb + rops + rf + nblk * npair * 4
-    return fwd, bwd
-
-
-FWD_KERNEL_SOURCES = ["orthogonal_fine_tuning_amd/csrc/linear_fwd.hip",
-                      "orthogonal_fine_tuning_amd/csrc/gemm_nt.h",
-                      "orthogonal_fine_tuning_amd/csrc/gemm_nt_dma.h",
-                      "orthogonal_fine_tuning_amd/csrc/gemm_skinny.h",
-                      "orthogonal_fine_tuning_amd/csrc/oft_device.h",
-                      "orthogonal_fine_tuning_amd/csrc/oft_formats.h"]
-
-
-def fwd_kernel_name(cfg):
-    """The kernel oft_linear_fwd launches for this shape (one launch per call)."""
-    if cfg.x_dtype == "bf16":
-        if cfg.M <= 64:
-            return "gemm_nt_dec4_kernel" if cfg.w_fmt != "fp8" and cfg.K % 256 == 0 else "gemm_nt_dec_kernel"
-        return "gemm_nt_dma_kernel"
-    if cfg.M <= 64 and cfg.K % 256 == 0:
-        return "gemm_nt_skinny_kernel"
-    return "gemm_nt_kernel"
-
-
-def kernel_source_sha(paths):
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def load_traffic(kernel_key, sha):
-    """HBM traffic per launch from committed rocprofv3 counter runs, or None
-    when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        data = json.load(f)
-    ent = data.get(kernel_key)
-    if not ent or ent.get("source_sha") != sha:
-        return None
-    return ent.get("bytes_per_launch")
-
-
-def cpu_baseline(cfg, inp, rows):
-    import numpy as np
-    from oracle import dense as odense
-
+    torch.cuda.synchronize()
+    oft.prof_enable(True)
     try:
-        import threadpoolctl
-
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover - informational only
-        cores = os.cpu_count() or 1
-    ms = min(rows, cfg.M)
-    sub = dict(inp)
-    sub["cfg"] = cfg.with_(M=ms)
-    sub["x"] = inp["x"][:ms]
-    sub["dy"] = inp["dy"][:ms]
-    reps, t0 = 0, time.perf_counter()
-    while True:  # repeat the sample for at least ~10 s of CPU work
-        odense.run(sub)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 50:
-            break
-    f, b = dense_flops(sub["cfg"])
-    return {"value": reps * (f + b) / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{cfg.name}: {ms} of {cfg.M} token rows, dequant + Cayley + fwd + bwd (dX, dQ) "
-                      f"in fp64 numpy, {reps} repetitions in {dt:.1f} s"}
+        for _ in range(nsteps):
+            step()
+        torch.cuda.synchronize()
+        recs = oft.prof_records()
+    finally:
+        oft.prof_enable(False)
+    agg = {}
+    for name, ms in recs:
+        t, c = agg.get(name, (0.0, 0))
+        agg[name] = (t + ms, c + 1)
+    return {k: (t / nsteps, c / nsteps) for k, (t, c) in agg.items()}
 
 
 def cold_phases(fwd, bwd, reps=5):
@@ -230,31 +203,302 @@ def cold_phases(fwd, bwd, reps=5):
     return float(np.median(tf)), float(np.median(tb))
 
 
+def blas_threads():
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        return max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - informational only
+        return os.cpu_count() or 1
+
+
+def time_steps(step, steps, warmup, nev=4):
+    """Warm-up, then `steps` steps bracketed by syncs (wall clock), with HIP
+    events between the phases of every timed step."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e-3 for i in range(nev - 1)]
+    return wall / steps, phases
+
+
+# ------------------------------------------------------------------ dense
+def dense_flops(cfg):
+    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
+    return 2 * M * N * K + 2 * M * N * b, 2 * M * N * K + 4 * M * N * b
+
+
+def dense_bytes(cfg):
+    """Algorithmic HBM bytes: what the method must read and write once."""
+    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
+    xb = 4 if cfg.x_dtype == "f32" else 2
+    wbytes = N * K // 2 + N * (K // cfg.g) * 2 if cfg.w_fmt in ("int4", "fp4") else N * K + N * 4
+    nblk = N // b
+    rops = nblk * 2 * b * b * 2
+    rf = nblk * b * b * 4
+    dq = nblk * (b * (b - 1) // 2) * 4
+    fwd = wbytes + M * K * xb + M * N * xb + rops
+    bwd = wbytes + M * N * 2 + M * N * xb + M * K * xb + rops + rf + dq
+    return fwd, bwd, wbytes
+
+
+def dense_kernel_work(cfg):
+    """Algorithmic (flops, bytes) per launch of each kernel step."""
+    M, N, K, b = cfg.M, cfg.N, cfg.K, cfg.b
+    xb = 4 if cfg.x_dtype == "f32" else 2
+    f_fwd, _ = dense_flops(cfg)
+    b_fwd, _, wbytes = dense_bytes(cfg)
+    nblk = N // b
+    return {
+        "dense.fwd": (f_fwd, b_fwd),
+        "dense.fwd_base": (2 * M * N * K, b_fwd - nblk * 2 * b * b * 2),
+        # dX = rot^T(dY) W: the contraction, reading the weight and dZ' once
+        "dense.dx": (2 * M * N * K, wbytes + M * N * 2 + M * K * xb),
+        # dQ pass: S = dY^T Y per block and the rotated dY (2MNb each),
+        # reading dY and Y, writing dZ'
+        "dense.dq": (4 * M * N * b, M * N * 2 + M * N * xb + M * N * 2 + nblk * 2 * b * b * 2),
+        "dense.dq_final": (4 * nblk * b ** 3, nblk * b * b * 4 * 2 + nblk * (b * (b - 1) // 2) * 4),
+        "dense.transpose": (0, wbytes + K * N * (1 if cfg.w_fmt == "fp8" else 2)),
+        "dense.dx_reduce": (0, M * K * (4 + xb)),
+        "cayley": (2 * nblk * b ** 3, nblk * (b * (b - 1) // 2) * 2 + nblk * b * b * 4 + nblk * 2 * b * b * 2),
+    }
+
+
+def dense_cpu_baseline(cfg, inp, seconds):
+    """The oracle on a row sample of about `seconds` of work (one timed pass,
+    scaled from a small probe)."""
+    from oracle import dense as odense
+
+    def run_rows(m):
+        sub = dict(inp)
+        sub["cfg"] = cfg.with_(M=m)
+        sub["x"] = inp["x"][:m]
+        sub["dy"] = inp["dy"][:m]
+        t0 = time.perf_counter()
+        odense.run(sub)
+        return time.perf_counter() - t0, sub["cfg"]
+
+    m = min(cfg.M, 64)
+    dt, sc = run_rows(m)
+    if m < cfg.M and dt < seconds / 2:
+        m = int(min(cfg.M, max(m, m * seconds / max(dt, 1e-3))))
+        dt, sc = run_rows(m)
+    f, b = dense_flops(sc)
+    return {"value": (f + b) / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{cfg.name}: {m} of {cfg.M} token rows, dequant + Cayley + fwd + bwd (dX, dQ) "
+                      f"in fp64 numpy, {dt:.2f} s"}
+
+
+def run_dense(cfg, args, sha, headline):
+    import numpy as np
+    import torch
+
+    import orthogonal_fine_tuning_amd as oft
+    from oft_inputs import make_dense
+
+    inp = make_dense(cfg, seed=0)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to("cuda")
+
+    xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
+    wf = {"int4": oft.OFT_W_INT4, "fp8": oft.OFT_W_FP8_E4M3, "fp4": oft.OFT_W_FP4_E2M1}[cfg.w_fmt]
+    d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
+    tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
+    q, x = dev(inp["p"]), dev(inp["x"])
+    wc, ws = dev(inp["w_codes"]), dev(inp["w_scales"])
+    dy = dev(inp["dy"])
+    Rf = torch.empty((cfg.nblk, cfg.b, cfg.b), dtype=torch.float32, device="cuda")
+    Rops = torch.empty((cfg.nblk, 2, cfg.b, cfg.b), dtype=torch.int16, device="cuda")
+    y = torch.empty((cfg.M, cfg.N), dtype=tdt, device="cuda")
+    dx = torch.empty((cfg.M, cfg.K), dtype=tdt, device="cuda")
+    dq = torch.empty((cfg.nblk, cfg.npair), dtype=torch.float32, device="cuda")
+    nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
+    work = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def fwd():
+        oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp)
+
+    def bwd():
+        oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        oft.cayley_build(q, cfg.nblk, cfg.b, Rf, Rops, stream=sp)
+        if ev is not None:
+            ev[1].record(stream)
+        fwd()
+        if ev is not None:
+            ev[2].record(stream)
+        bwd()
+        if ev is not None:
+            ev[3].record(stream)
+
+    t_step, (t_cay, t_fwd, t_bwd) = time_steps(step, args.steps, args.warmup)
+    kern = profile_steps(step, args.prof_steps)
+    f_fwd, f_bwd = dense_flops(cfg)
+    by_fwd, by_bwd, _ = dense_bytes(cfg)
+    out = summary(cfg.name, t_step, f_fwd + f_bwd, by_fwd + by_bwd, kern, dense_kernel_work(cfg), sha,
+                  {"cayley_build": t_cay, "fwd": t_fwd, "bwd": t_bwd})
+    out["config"] = {"workload": cfg.name, "tokens": cfg.M, "in_features": cfg.K, "out_features": cfg.N,
+                     "segments": list(cfg.segs), "oft_block": cfg.b,
+                     "weights": cfg.w_fmt + (f"_g{cfg.g}" if cfg.w_fmt != "fp8" else "_e4m3"),
+                     "x_dtype": cfg.x_dtype, "parallelism": "single_gpu"}
+    out["phase_rates"] = {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
+                          "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1)}
+    if not args.no_extras:
+        burst = 10
+        t_base = burst_seconds(stream, lambda: oft.oft_linear_fwd_base(d, x, wc, ws, y, stream=sp), burst)
+        fb, bb = dense_kernel_work(cfg)["dense.fwd_base"]
+        out["reference_policy_fwd"] = roofline(fb, bb, t_base)
+        state = torch.zeros(4, dtype=torch.int32, device="cuda")
+        latch = torch.zeros(4, dtype=torch.int32, device="cuda")
+        oft.oft_slots_switch(state, 1, 1, stream=sp)
+        ts, tp = [], []
+        for _ in range(3):  # alternating bursts, medians (the clock settles under sustained load)
+            ts.append(burst_seconds(stream, lambda: oft.oft_linear_fwd_slots(d, x, wc, ws, Rops, Rops, state, latch,
+                                                                             y, stream=sp), burst))
+            tp.append(burst_seconds(stream, fwd, burst))
+        t_s, t_p = float(np.median(ts)), float(np.median(tp))
+        out["slots_fwd"] = {"us": round(t_s * 1e6, 2), "plain_fwd_us": round(t_p * 1e6, 2),
+                            "overhead_us": round((t_s - t_p) * 1e6, 2)}
+    if not args.no_cold:
+        cf, cb = cold_phases(fwd, bwd)
+        out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
+                                 "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = dense_cpu_baseline(cfg, inp, args.cpu_seconds * (3 if headline else 1))
+    del x, wc, ws, dy, Rf, Rops, y, dx, dq, work
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------------ MoE
 def moe_flops(cfg):
     P, H, I, b = cfg.T * cfg.k, cfg.H, cfg.I, cfg.b
     gemm = 2 * P * H * 2 * I + 2 * P * I * H
     return gemm + 2 * P * 2 * I * b, gemm + 4 * P * 2 * I * b
 
 
+def moe_weight_bytes(cfg):
+    """Packed bytes of one expert's gate/up and down weights (codes + scales)."""
+    H, I, g = cfg.H, cfg.I, cfg.g
+    return 2 * I * H // 2 + 2 * I * (H // g) * 2, H * I // 2 + H * (I // g) * 2
+
+
 def moe_bytes(cfg, n_active):
-    P, T, E, H, I, g, b = cfg.T * cfg.k, cfg.T, cfg.E, cfg.H, cfg.I, cfg.g, cfg.b
-    w_e = 2 * I * H // 2 + 2 * I * (H // g) * 2 + H * I // 2 + H * (I // g) * 2
+    P, T, E, H, I, b = cfg.T * cfg.k, cfg.T, cfg.E, cfg.H, cfg.I, cfg.b
+    wgu, wd = moe_weight_bytes(cfg)
     nblk = 2 * I // b
     rops = nblk * 2 * b * b * 2
-    fwd = n_active * (w_e + rops) + T * H * 2 + T * E * 4 + P * 2 * I * 2 + T * H * 2 + P * 16
-    bwd = (n_active * (w_e + rops + nblk * b * b * 4) + T * H * 2 + P * 2 * I * 2 + T * H * 2
+    fwd = n_active * (wgu + wd + rops) + T * H * 2 + T * E * 4 + P * 2 * I * 2 + T * H * 2 + P * 16
+    bwd = (n_active * (wgu + wd + rops + nblk * b * b * 4) + T * H * 2 + P * 2 * I * 2 + T * H * 2
            + E * nblk * (b * (b - 1) // 2) * 4 + P * 4 + P * 16)
     return fwd, bwd
 
 
-def run_moe(cfg, args):
+def moe_kernel_work(cfg, n_active):
+    """Algorithmic (flops, bytes) per launch of each kernel step (weights of
+    the active experts only)."""
+    P, T, E, H, I, b = cfg.T * cfg.k, cfg.T, cfg.E, cfg.H, cfg.I, cfg.b
+    wgu, wd = moe_weight_bytes(cfg)
+    nblk = 2 * I // b
+    rops = nblk * 2 * b * b * 2
+    npair = b * (b - 1) // 2
+    return {
+        "moe.route": (0, T * E * 4 + P * 4 * 5 + T * (P // T) * 4),
+        "moe.worklist": (0, E * 8),
+        # gate/up GEMM + per-expert rotation: weights, the gathered tokens
+        # (each read once), h and act written
+        "moe.gateup": (2 * P * H * 2 * I + 2 * P * 2 * I * b, n_active * (wgu + rops) + T * H * 2 + P * 2 * I * 2
+                       + P * I * 2),
+        "moe.down": (2 * P * I * H, n_active * wd + P * I * 2 + P * H * 2),
+        "moe.combine": (0, P * H * 2 + T * H * 2 + P * 8),
+        # dA = dO . W_d per pair, SwiGLU backward: weights, dy (once), h read,
+        # dH written
+        "moe.dA": (2 * P * H * I, n_active * wd + T * H * 2 + P * 2 * I * 2 * 2 + P * 4),
+        "moe.dw_reduce": (0, P * 4 * 3),
+        # S = dH^T H per block and the rotated dH (2 P 2I b each): dH and h
+        # read, dz written
+        "moe.dq": (4 * P * 2 * I * b, P * 2 * I * 2 * 3 + n_active * nblk * b * b * 6 + E * nblk * npair * 4),
+        "moe.dX": (2 * P * 2 * I * H, n_active * wgu + P * 2 * I * 2 + P * H * 2),
+        "moe.unpermute": (0, P * H * 2 + T * H * 2 + P * 4),
+        "moe.router_bwd": (0, 2 * T * E * 4 + 2 * P * 4),
+        "cayley": (2 * E * nblk * b ** 3, E * nblk * (npair * 2 + b * b * 4 + 2 * b * b * 2)),
+    }
+
+
+def moe_cpu_baseline(cfg, inp, seconds):
+    """The oracle's forward and backward of whole experts (every routed row
+    of each), as many as fit in about `seconds`."""
+    from oracle import codec, moe as omoe
+
+    idx, w = omoe.route(inp["logits"], cfg.k)
+    rt = omoe.group(idx, cfg.E, cfg.chunk)
+    rt.update(idx=idx, w=w)
+    act = [int(e) for e in rt["active"]]
+    X = codec.bf16_bits_to_f64(inp["x"])
+    dy = codec.bf16_bits_to_f64(inp["dy"])
+    wflat = w.reshape(-1)
+    done, t0 = [], time.perf_counter()
+    for e in act:  # the oracle's per-expert forward and backward, expert by expert
+        pairs = rt["perm"][rt["offsets"][e]:rt["offsets"][e + 1]]
+        Wgu, Wd, R = omoe.expert_weights(inp, e)
+        omoe.expert_forward(X[pairs // cfg.k], Wgu, Wd, R, cfg.I)
+        omoe.expert_backward(inp, e, pairs, X, dy, wflat)
+        done.append(e)
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    rows = int(sum(rt["counts"][e] for e in done))
+    H, I, b = cfg.H, cfg.I, cfg.b
+    gemm = 2 * rows * H * 2 * I + 2 * rows * I * H
+    fl = 2 * gemm + 6 * rows * 2 * I * b
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{cfg.name}: {len(done)} of {len(act)} active experts ({rows} routed rows), "
+                      f"dequant + Cayley + fwd + bwd in fp64 numpy, {dt:.2f} s"}
+
+
+def moe_inputs(cfg, cache):
+    """Seeded inputs; a workload that differs from one already drawn only in
+    its token count takes that one's weights and its first T token rows."""
+    from oft_inputs import make_moe, moe_token_rows
+
+    for other in cache.values():
+        oc = other["cfg"]
+        if (oc.E, oc.k, oc.H, oc.I, oc.g, oc.b, oc.w_fmt, oc.bias_std) == (cfg.E, cfg.k, cfg.H, cfg.I, cfg.g,
+                                                                          cfg.b, cfg.w_fmt, cfg.bias_std) \
+                and oc.T >= cfg.T:
+            return moe_token_rows(other, cfg)
+    inp = make_moe(cfg, seed=0)
+    cache[cfg.name] = inp
+    return inp
+
+
+def run_moe(cfg, args, sha, headline, cache):
     import numpy as np
     import torch
 
     import orthogonal_fine_tuning_amd as oft
-    from oft_inputs import make_moe
 
-    inp = make_moe(cfg, seed=0)
+    inp = moe_inputs(cfg, cache)
 
     def dev(a):
         a = np.ascontiguousarray(a)
@@ -264,8 +508,8 @@ def run_moe(cfg, args):
 
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
     P = T * k
-    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0,
-                     w_fmt=oft.OFT_W_FP4_E2M1 if cfg.w_fmt == "fp4" else oft.OFT_W_INT4)
+    w_fmt = oft.OFT_W_FP4_E2M1 if cfg.w_fmt == "fp4" else oft.OFT_W_INT4
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=w_fmt)
     i32 = dict(dtype=torch.int32, device="cuda")
     rtt = dict(topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32), perm=torch.empty(P, **i32),
@@ -290,82 +534,62 @@ def run_moe(cfg, args):
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
+    def fwd():
+        oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rops, rt,
+                                hs, y, wsf, nbf, stream=sp)
+
+    def bwd():
+        oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rf,
+                                Rops, dx, dq, dw, wsb, nbb, stream=sp)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         oft.cayley_build(q, nblk, b, Rf, Rops, stream=sp)
         if ev is not None:
             ev[1].record(stream)
-        oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rops, rt,
-                                hs, y, wsf, nbf, stream=sp)
+        fwd()
         if ev is not None:
             ev[2].record(stream)
-        oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], Rf,
-                                Rops, dx, dq, dw, wsb, nbb, stream=sp)
+        bwd()
         if ev is not None:
             ev[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     mem0 = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    t_step, (t_cay, t_fwd, t_bwd) = time_steps(step, args.steps, 0)
     transient = torch.cuda.max_memory_allocated() - mem0  # the library allocates nothing
     n_active = int(rtt["n_active"][0].item())
-    # the router backward (d_logits from dw through the softmax top-k), not
-    # part of the step: a burst of launches on the step's routing and dw
-    dl = torch.empty((T, E), dtype=torch.float32, device="cuda")
-    burst = 10
-    t_rb = burst_seconds(stream, lambda: oft.oft_moe_router_bwd(d, lg, rtt["topk_idx"], dw, dl, stream=sp), burst)
-    by_rb = 2 * T * E * 4 + 2 * T * k * 4  # logits in, d_logits out, idx and dw in
-    rb_roof = roofline_object(False, 0, by_rb, t_rb, kernel="moe_router_bwd_kernel", traffic=None)
-    rb_roof["kernel_timing"] = (f"HIP events around {burst} back-to-back launches queued behind a spin, "
-                                "after the timed steps")
-    del dl
-    t_cay = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    kern = profile_steps(step, args.prof_steps)
     f_fwd, f_bwd = moe_flops(cfg)
     by_fwd, by_bwd = moe_bytes(cfg, n_active)
-    value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
-    out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": T, "experts": E, "top_k": k, "hidden": H,
-                   "expert_intermediate": I, "weights": f"{cfg.w_fmt}_g{cfg.g}", "oft_block": b, "chunk": cfg.chunk,
-                   "active_experts": n_active, "parallelism": "single_gpu"},
-        "roofline": roofline_object((f_fwd + f_bwd) / (by_fwd + by_bwd) > RIDGE, f_fwd + f_bwd, by_fwd + by_bwd,
-                                    t_fwd + t_bwd, kernel="moe fwd+bwd calls", traffic=None),
-        "router_bwd": rb_roof,
-        "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
-                      "bwd": round(t_bwd * 1e6, 2)},
-        "phase_rates": {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
-                        "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
-                        "hbm_frac": round((by_fwd + by_bwd) / (t_fwd + t_bwd) / 1e9 / PEAK_HBM_GBS, 4)},
-    }
+    out = summary(cfg.name, t_step, f_fwd + f_bwd, by_fwd + by_bwd, kern, moe_kernel_work(cfg, n_active), sha,
+                  {"cayley_build": t_cay, "fwd": t_fwd, "bwd": t_bwd})
+    out["config"] = {"workload": cfg.name, "tokens": T, "experts": E, "top_k": k, "hidden": H,
+                     "expert_intermediate": I, "weights": f"{cfg.w_fmt}_g{cfg.g}", "oft_block": b,
+                     "chunk": cfg.chunk, "active_experts": n_active, "parallelism": "single_gpu"}
+    out["phase_rates"] = {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
+                          "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1)}
     out["transient_bytes"] = int(transient)
+    if not args.no_extras:
+        dl = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        t_rb = burst_seconds(stream, lambda: oft.oft_moe_router_bwd(d, lg, rtt["topk_idx"], dw, dl, stream=sp))
+        out["router_bwd"] = roofline(*moe_kernel_work(cfg, n_active)["moe.router_bwd"], t_rb)
+        del dl
     if not args.no_cold:
-        cf, cb = cold_phases(
-            lambda: oft.oft_moe_grouped_fwd(d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"],
-                                            Rops, rt, hs, y, wsf, nbf, stream=sp),
-            lambda: oft.oft_moe_grouped_bwd(d, dy, rt, hs, W["wgu_codes"], W["wgu_scales"], W["wd_codes"],
-                                            W["wd_scales"], Rf, Rops, dx, dq, dw, wsb, nbb, stream=sp))
+        cf, cb = cold_phases(fwd, bwd)
         out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
-                                 "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
-                                 "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
+                                 "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1)}
     if not args.no_dense_ref:
         del W
+        torch.cuda.empty_cache()
         out["dense_bf16_reference"] = moe_dense_reference(cfg, inp, args, dict(
             x=x, lg=lg, dy=dy, rt=rt, Rf=Rf, Rops=Rops, hs=hs, y=y, dx=dx, dq=dq, dw=dw), t_fwd + t_bwd)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = moe_cpu_baseline(cfg, inp)
+        out["cpu_baseline"] = moe_cpu_baseline(cfg, inp, args.cpu_seconds * (3 if headline else 1))
     return out
 
 
@@ -408,48 +632,42 @@ def moe_dense_reference(cfg, inp, args, bufs, t_ours):
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t_fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    _, (t_fwd, t_bwd) = time_steps(step, args.steps, args.warmup, nev=3)
     del wgu, wd, wsf, wsb
     torch.cuda.empty_cache()
     return {"fwd_us": round(t_fwd * 1e6, 2), "bwd_us": round(t_bwd * 1e6, 2),
             "weights_bytes": int(E * 3 * I * H * 2),
             "ratio": round(t_ours / (t_fwd + t_bwd), 4),
-            "note": "fwd+bwd time of the INT4 path over that of the same kernels on bf16 weights"}
+            "note": "fwd+bwd time of the 4-bit path over that of the same kernels on bf16 weights"}
 
 
-def moe_cpu_baseline(cfg, inp, n_experts=4):
-    from oracle import moe as omoe
-
-    try:
-        import threadpoolctl
-
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    idx, w = omoe.route(inp["logits"], cfg.k)
-    rt = omoe.group(idx, cfg.E, cfg.chunk)
-    rt.update(idx=idx, w=w)
-    experts = [int(e) for e in rt["active"][:n_experts]]
-    t0 = time.perf_counter()
-    omoe.forward(inp, rt, experts=experts)
-    omoe.backward(inp, rt, experts=experts)
-    dt = time.perf_counter() - t0
-    rows = int(sum(rt["counts"][e] for e in experts))
-    H, I, b = cfg.H, cfg.I, cfg.b
-    gemm = 2 * rows * H * 2 * I + 2 * rows * I * H
-    fl = 2 * gemm + 6 * rows * 2 * I * b
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{cfg.name}: experts {experts} ({rows} routed rows), dequant + Cayley + fwd + bwd "
-                      f"in fp64 numpy, {dt:.2f} s"}
+# ------------------------------------------------------------------ summary
+def summary(name, t_step, flops, nbytes, kern, work, sha, phases):
+    """The step's rate and roofline, the kernel-step table and the dominant
+    kernel step's roofline."""
+    kernels = {}
+    for kname, (ms, calls) in sorted(kern.items(), key=lambda kv: -kv[1][0]):
+        ent = {"us_per_step": round(ms * 1e3, 2), "launches_per_step": round(calls, 2)}
+        if kname in work and calls > 0:
+            f, by = work[kname]
+            per = ms * 1e-3 / calls
+            r = roofline(f, by, per)
+            ent.update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"], frac=r["frac"])
+        kernels[kname] = ent
+    dom = max(kern, key=lambda kk: kern[kk][0])
+    ms, calls = kern[dom]
+    f, by = work.get(dom, (0, 0))
+    roof = roofline(f, by, ms * 1e-3 / max(calls, 1), kernel=dom, traffic=load_traffic(f"{dom}:{name}", sha))
+    roof["timing"] = ("HIP events the library records on the launch stream around this step of its work, "
+                      "averaged over profiled steps right after the timed steps")
+    roof["source_sha"] = sha
+    return {
+        "value": round(flops / t_step / 1e12, 3), "unit": "TFLOP/s", "ms_per_step": round(t_step * 1e3, 4),
+        "roofline": roof,
+        "step_roofline": roofline(flops, nbytes, t_step),
+        "phases_us": {k: round(v * 1e6, 2) for k, v in phases.items()},
+        "kernels": kernels,
+    }
 
 
 def main():
@@ -459,12 +677,12 @@ def main():
                                    "(sharding over several GPUs is designed, not implemented)"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import orthogonal_fine_tuning_amd as oft
-    from oft_inputs import CONFIGS, make_dense
+    from oft_inputs import CONFIGS
 
+    oft._lib.load()
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -472,140 +690,37 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg = CONFIGS[args.config]
-    if args.w_fmt is not None:
-        if cfg.w_fmt not in ("int4", "fp4"):
-            raise SystemExit(f"--w-fmt applies to 4-bit workloads; {cfg.name} has {cfg.w_fmt} weights")
-        cfg = cfg.with_(w_fmt=args.w_fmt)
-    if not hasattr(cfg, "segs"):
-        print(json.dumps(run_moe(cfg, args)))
-        return
-    inp = make_dense(cfg, seed=0)
-
-    def dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            a = a.view(np.int16)
-        return torch.from_numpy(a).to("cuda")
-
-    xdt = oft.OFT_DT_F32 if cfg.x_dtype == "f32" else oft.OFT_DT_BF16
-    wf = {"int4": oft.OFT_W_INT4, "fp8": oft.OFT_W_FP8_E4M3, "fp4": oft.OFT_W_FP4_E2M1}[cfg.w_fmt]
-    d = oft.linear_desc(cfg.M, cfg.K, cfg.segs, cfg.b, xdt, wf, cfg.g)
-    tdt = torch.float32 if cfg.x_dtype == "f32" else torch.int16
-    q, x = dev(inp["p"]), dev(inp["x"])
-    wc, ws = dev(inp["w_codes"]), dev(inp["w_scales"])
-    dy = dev(inp["dy"])
-    Rf = torch.empty((cfg.nblk, cfg.b, cfg.b), dtype=torch.float32, device="cuda")
-    Rops = torch.empty((cfg.nblk, 2, cfg.b, cfg.b), dtype=torch.int16, device="cuda")
-    y = torch.empty((cfg.M, cfg.N), dtype=tdt, device="cuda")
-    dx = torch.empty((cfg.M, cfg.K), dtype=tdt, device="cuda")
-    dq = torch.empty((cfg.nblk, cfg.npair), dtype=torch.float32, device="cuda")
-    nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
-    work = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        oft.cayley_build(q, cfg.nblk, cfg.b, Rf, Rops, stream=sp)
-        if ev is not None:
-            ev[1].record(stream)
-        oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp)
-        if ev is not None:
-            ev[2].record(stream)
-        oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp)
-        if ev is not None:
-            ev[3].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    t_cay = np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_fwd = np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    t_bwd = np.mean([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
-    ms_per_step = wall / args.steps * 1e3
-
-    # Roofline kernel time: one event pair on the same stream around a burst
-    # of back-to-back forward launches (one kernel each), queued behind a
-    # spin.  The per-phase
-    # events above also count the idle time an event boundary adds on each
-    # side of the launch it brackets (about 6 us here).
-    burst = 10
-    t_kernel = burst_seconds(stream, lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp), burst)
-    # the reference-policy forward (frozen base alone, oft_linear_fwd_base),
-    # timed the same way
-    t_base = burst_seconds(stream, lambda: oft.oft_linear_fwd_base(d, x, wc, ws, y, stream=sp), burst)
-    # the forward on the active slot of a double-buffered adapter (one latch
-    # launch, then the same kernels reading the slot through it)
-    state = torch.zeros(4, dtype=torch.int32, device="cuda")
-    latch = torch.zeros(4, dtype=torch.int32, device="cuda")
-    oft.oft_slots_switch(state, 1, 1, stream=sp)
-    # slot and plain bursts alternate three times and each side takes its
-    # median: a single burst pair is at the mercy of where it falls in the
-    # clock's response to sustained matrix-core load
-    ts, tp = [], []
-    for _ in range(3):
-        ts.append(burst_seconds(stream, lambda: oft.oft_linear_fwd_slots(d, x, wc, ws, Rops, Rops, state, latch, y,
-                                                                         stream=sp), burst))
-        tp.append(burst_seconds(stream, lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp), burst))
-    t_slots, t_plain2 = float(np.median(ts)), float(np.median(tp))
-    f_fwd, f_bwd = dense_flops(cfg)
-    by_fwd, by_bwd = dense_bytes(cfg)
-    value = (f_fwd + f_bwd) / (wall / args.steps) / 1e12
-
-    fwd_src = FWD_KERNEL_SOURCES
-    sha = kernel_source_sha(fwd_src)
-    roof = roofline_object(f_fwd / by_fwd > RIDGE, f_fwd, by_fwd, t_kernel, kernel=fwd_kernel_name(cfg),
-                           traffic=None if cfg.w_fmt != CONFIGS[args.config].w_fmt  # counters taken on the stock format
-                           else load_traffic(f"{fwd_kernel_name(cfg)}:{cfg.name}", sha))
-    roof["kernel_timing"] = f"HIP events around {burst} back-to-back launches queued behind a spin, after the timed steps"
-    roof["source_sha"] = sha
-    f_base = 2 * cfg.M * cfg.N * cfg.K
-    by_base = by_fwd - cfg.nblk * 2 * cfg.b * cfg.b * 2  # no rotation operands
-    base_roof = roofline_object(f_base / by_base > RIDGE, f_base, by_base, t_base, kernel=fwd_kernel_name(cfg),
-                                traffic=None)
-
-    out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "tokens": cfg.M, "in_features": cfg.K,
-                   "out_features": cfg.N, "segments": list(cfg.segs), "oft_block": cfg.b,
-                   "weights": cfg.w_fmt + (f"_g{cfg.g}" if cfg.w_fmt != "fp8" else "_e4m3"),
-                   "x_dtype": cfg.x_dtype, "parallelism": "single_gpu"},
-        "roofline": roof,
-        "reference_policy_fwd": base_roof,
-        "slots_fwd": {"kernel_us": round(t_slots * 1e6, 2), "plain_fwd_us": round(t_plain2 * 1e6, 2),
-                      "overhead_us": round((t_slots - t_plain2) * 1e6, 2),
-                      "timing": "latch + forward per call, same burst timing as roofline; medians of three "
-                                "slot bursts alternating with three plain-forward bursts"},
-        "phases_us": {"cayley_build": round(t_cay * 1e6, 2), "fwd": round(t_fwd * 1e6, 2),
-                      "bwd": round(t_bwd * 1e6, 2)},
-        "phase_rates": {
-            "fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
-            "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1),
-            "step_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4)},
-    }
-    if not args.no_cold:
-        cf, cb = cold_phases(lambda: oft.oft_linear_fwd(d, x, wc, ws, Rops, y, stream=sp),
-                             lambda: oft.oft_linear_bwd(d, dy, y, wc, ws, Rf, Rops, dx, dq, work, nb, stream=sp))
-        out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
-                                 "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1),
-                                 "note": "fwd and bwd each right after writing 512 MiB (2x the MALL)"}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
-    print(json.dumps(out))
+    names = ORDER if args.config == "all" else [args.config]
+    head = HEADLINE if args.config == "all" else args.config
+    sha = source_sha()
+    cache = {}
+    results = {}
+    for name in names:
+        cfg = CONFIGS[name]
+        if args.w_fmt is not None and cfg.w_fmt in ("int4", "fp4"):
+            cfg = cfg.with_(w_fmt=args.w_fmt)
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        if hasattr(cfg, "segs"):
+            results[name] = run_dense(cfg, args, sha, name == head)
+        else:
+            results[name] = run_moe(cfg, args, sha, name == head, cache)
+        results[name]["bench_seconds"] = round(time.perf_counter() - t0, 1)
+        if name == "moe_1t_decode" or len(names) == 1:
+            cache.clear()
+    h = results[head]
+    line = {"metric": METRIC, "value": h["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": h["config"],
+            "roofline": h["roofline"]}
+    if "cpu_baseline" in h:
+        line["cpu_baseline"] = h["cpu_baseline"]
+    for k, v in h.items():
+        if k not in line and k != "value":
+            line[k] = v
+    if len(names) > 1:
+        line["workloads"] = {n: r for n, r in results.items() if n != head}
+    print(json.dumps(line))
 
 
 if __name__ == "__main__":

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 6
+#define OFT_ABI_VERSION 7
 
 typedef enum {
   OFT_OK = 0,
@@ -151,6 +151,23 @@ typedef struct {
 int32_t oft_abi_version(void);
 const char* oft_status_str(int32_t status); /* static string, never NULL */
 int32_t oft_last_hip_error(void);           /* hipError_t of the last OFT_EHIP */
+
+/* ---- opt-in kernel timing (measurement only) ------------------------------
+ * oft_prof_enable(1) clears the record list and starts recording: from then
+ * on every call records, per step of its work (e.g. "moe.gateup",
+ * "dense.fwd", "dense.dq"), a HIP event on its launch stream before and
+ * after the kernels of that step; oft_prof_enable(0) stops recording (the
+ * records stay readable) and is the default.  The first enable creates the
+ * event pool (2 x 1024 events of the device current then; records past 1024
+ * are dropped); recording does not allocate device memory.  oft_prof_count()
+ * returns the number of records; oft_prof_read(i, ...) waits for record i's
+ * second event and writes its name (NUL-terminated, truncated to name_len)
+ * and its duration in milliseconds.  Process-wide, serialised by a mutex;
+ * not for use during graph capture.  Errors: OFT_EINVAL (index out of
+ * range, NULL output, name_len < 1), OFT_EHIP (event creation or wait). */
+int32_t oft_prof_enable(int32_t on);
+int32_t oft_prof_count(void);
+int32_t oft_prof_read(int32_t i, char* name, int32_t name_len, float* ms);
 
 /* ---- Cayley map (adapter -> rotation) ------------------------------------
  * Per block: A = I - Q_j, R_j = (I + Q_j) A^-1 = 2 A^-1 - I, by Gauss-Jordan

@@ -40,6 +40,7 @@ __all__ = [
     "make_dense",
     "make_moe",
     "make_moe_logits",
+    "moe_token_rows",
     "to_bf16_bits",
     "to_fp16_bits",
 ]
@@ -158,8 +159,11 @@ CONFIGS = {
 # generators
 # --------------------------------------------------------------------------
 def _int4_bytes(rng: np.random.Generator, n: int) -> np.ndarray:
-    # every byte uniform over 0..255, so each nibble is uniform over [-8, 7]
-    return np.frombuffer(rng.bytes(n), dtype=np.uint8).copy()
+    """n bytes, each uniform over 0..255 (so each nibble is uniform over
+    [-8, 7]): the little-endian bytes of ceil(n / 8) raw 64-bit outputs of
+    the generator's bit stream, the first n of them."""
+    words = rng.bit_generator.random_raw((n + 7) // 8)
+    return words.view(np.uint8)[:n] if n % 8 else words.view(np.uint8)
 
 
 def _scale_slots(rng: np.random.Generator, w_fmt: str, lo: float, hi: float, shape) -> np.ndarray:
@@ -219,18 +223,12 @@ def make_moe(cfg: MoEConfig, seed: int = 0, with_dy: bool = True) -> dict:
         bias = rng.normal(0.0, cfg.bias_std, size=E).astype(np.float32)
         logits = (logits + bias[None, :]).astype(np.float32)
     out["logits"] = logits
-    wgu = np.empty((E, 2 * I, H // 2), dtype=np.uint8)
-    for e in range(E):
-        wgu[e] = _int4_bytes(rng, 2 * I * H // 2).reshape(2 * I, H // 2)
-    sgu = np.empty((E, 2 * I, H // g), dtype=np.uint16)
-    for e in range(E):
-        sgu[e] = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (2 * I, H // g))
-    wd = np.empty((E, H, I // 2), dtype=np.uint8)
-    for e in range(E):
-        wd[e] = _int4_bytes(rng, H * I // 2).reshape(H, I // 2)
-    sd = np.empty((E, H, I // g), dtype=np.uint16)
-    for e in range(E):
-        sd[e] = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (H, I // g))
+    # expert by expert within each array: one draw per array is the same
+    # stream as E consecutive per-expert draws (each a multiple of 8 bytes)
+    wgu = _int4_bytes(rng, E * 2 * I * H // 2).reshape(E, 2 * I, H // 2)
+    sgu = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (E, 2 * I, H // g))
+    wd = _int4_bytes(rng, E * H * I // 2).reshape(E, H, I // 2)
+    sd = _scale_slots(rng, cfg.w_fmt, cfg.scale_lo, cfg.scale_hi, (E, H, I // g))
     out.update(wgu_codes=wgu, wgu_scales=sgu, wd_codes=wd, wd_scales=sd)
     p = rng.normal(0.0, cfg.q_std, size=(E, cfg.nblk_e, cfg.npair)).astype(np.float32)
     out["p"] = to_bf16_bits(p)
@@ -249,3 +247,19 @@ def make_moe_logits(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
         bias = rng.normal(0.0, cfg.bias_std, size=cfg.E).astype(np.float32)
         logits = (logits + bias[None, :]).astype(np.float32)
     return logits
+
+
+def moe_token_rows(inp: dict, cfg: MoEConfig) -> dict:
+    """A problem of T = cfg.T tokens from a drawn one with at least as many:
+    the same weights, adapter and expert layout, and its first T rows of x,
+    logits and dy (each row is an independent draw of the same
+    distribution, so this is a seeded problem of the smaller shape)."""
+    src = inp["cfg"]
+    assert (src.E, src.k, src.H, src.I, src.g, src.b, src.w_fmt) == (cfg.E, cfg.k, cfg.H, cfg.I, cfg.g, cfg.b,
+                                                                     cfg.w_fmt) and cfg.T <= src.T
+    out = dict(inp)
+    out["cfg"] = cfg
+    for key in ("x", "logits", "dy"):
+        if key in inp:
+            out[key] = inp[key][:cfg.T]
+    return out

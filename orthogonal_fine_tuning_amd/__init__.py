@@ -18,6 +18,7 @@ __all__ = [
     "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd",
     "oft_slots_switch", "oft_linear_fwd_slots",
     "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
+    "prof_enable", "prof_records",
     "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_W_FP4_E2M1", "OFT_PASS_FWD",
     "OFT_PASS_BWD",
 ]
@@ -39,6 +40,24 @@ def _stream(stream):
 
 def abi_version() -> int:
     return _lib.load().oft_abi_version()
+
+
+def prof_enable(on: bool) -> None:
+    """Start (clearing the list) or stop the library's per-step kernel timing."""
+    _lib.check(_lib.load().oft_prof_enable(1 if on else 0), "oft_prof_enable")
+
+
+def prof_records():
+    """[(name, milliseconds)] of the recorded steps, in launch order (waits
+    for each record's events)."""
+    lib = _lib.load()
+    out = []
+    buf = C.create_string_buffer(64)
+    ms = C.c_float(0.0)
+    for i in range(lib.oft_prof_count()):
+        _lib.check(lib.oft_prof_read(i, buf, 64, C.byref(ms)), "oft_prof_read")
+        out.append((buf.value.decode(), float(ms.value)))
+    return out
 
 
 def linear_desc(M, K, segs, b, x_dtype=OFT_DT_BF16, w_fmt=OFT_W_INT4, g=0) -> oft_linear_desc:

@@ -45,6 +45,9 @@ _SZ = C.c_size_t
 # name -> (restype, argtypes)
 SIGNATURES = {
     "oft_abi_version": (_I, []),
+    "oft_prof_enable": (_I, [_I]),
+    "oft_prof_count": (_I, []),
+    "oft_prof_read": (_I, [_I, C.c_char_p, _I, C.POINTER(C.c_float)]),
     "oft_status_str": (C.c_char_p, [_I]),
     "oft_last_hip_error": (_I, []),
     "cayley_build": (_I, [_P, _I, _I, _P, _P, _P]),

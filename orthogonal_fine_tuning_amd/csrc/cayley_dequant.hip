@@ -16,6 +16,7 @@
 
 #include "oft_device.h"
 #include "oft_launch.h"
+#include "oft_prof.h"
 
 namespace oft {
 
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint2* __restric
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st) {
   if (nblk == 0) return hipSuccess;
+  ProfScope prof(st, "cayley");
   // few blocks (at most a few per SIMD): the serial pivot chain is the cost,
   // so two lanes per row; many blocks: throughput, one lane per row
   const bool two = nblk <= 4 * num_cus() * (b == 32 ? 1 : 2);

@@ -27,6 +27,7 @@
 #include "gemm_nn.h"
 #include "gemm_nt_dma.h"
 #include "oft_launch.h"
+#include "oft_prof.h"
 
 namespace oft {
 namespace {
@@ -515,8 +516,12 @@ hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src
     p.nsplit_len = pl.nsplit_len;
     p.part = reinterpret_cast<float*>(work + pl.npart_off);
   }
-  hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, WF, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
+  {
+    ProfScope prof(st, "dense.dx");
+    hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, WF, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
+  }
   if (pl.nsplit_n > 1) {
+    ProfScope prof(st, "dense.dx_reduce");
     const size_t n4 = (size_t)a.M * a.K / 4;
     hipLaunchKernelGGL(split_reduce_kernel<XF32>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, p.part,
                        pl.nsplit_n, n4, dx);
@@ -592,11 +597,15 @@ hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz
   constexpr bool FP8 = WF == WF_FP8;
   uint8_t* wt = reinterpret_cast<uint8_t*>(work + pl.wt_off);
   const dim3 tgrid(a.K / 64, a.N / 64);
+  {
+  ProfScope prof(st, "dense.transpose");
   if constexpr (FP8)
     hipLaunchKernelGGL(transpose_fp8_kernel, tgrid, dim3(256), 0, st, wc, wt, a.N, a.K);
   else
     hipLaunchKernelGGL(transpose_dequant_w4_kernel<WF>, tgrid, dim3(256), 0, st, wc,
                        static_cast<const uint16_t*>(ws), reinterpret_cast<uint16_t*>(wt), a.N, a.K, a.g);
+  }
+  ProfScope prof(st, "dense.dx");
   NtArgs p{};
   p.a = dz;
   p.lda = a.N;
@@ -700,6 +709,7 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
   float* part = reinterpret_cast<float*>(work);
   uint16_t* dz = (dx != nullptr && p.prerotate && a.M > 0) ? reinterpret_cast<uint16_t*>(work + p.dz_off) : nullptr;
   if ((dq != nullptr || dz != nullptr) && p.nsplit > 0) {
+    ProfScope prof(st, "dense.dq");
     dim3 grid((a.N + 63) / 64, p.nsplit);
     const float* s8 = a.fp8 ? static_cast<const float*>(ws) : nullptr;
     float* dq_part = dq != nullptr ? part : nullptr;
@@ -726,6 +736,7 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
   }
   const bool fused = dq != nullptr && p.nsplit == 1 && !a.xf32;
   if (dq != nullptr && !fused) {
+    ProfScope prof(st, "dense.dq_final");
     const int nblk = a.N / a.b;
     if (a.b == 32)
       hipLaunchKernelGGL(dq_final_kernel<32>, dim3(nblk), dim3(256), 0, st, part, p.nsplit, p.ng32, nblk, Rf, dq);

@@ -16,6 +16,7 @@
 #include "gemm_nt_dma.h"
 #include "gemm_skinny.h"
 #include "oft_launch.h"
+#include "oft_prof.h"
 
 namespace oft {
 namespace {
@@ -131,6 +132,7 @@ int num_cus() {
 hipError_t launch_linear_fwd(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                              const uint16_t* Rops, void* y, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  ProfScope prof(st, "dense.fwd");
 #define OFT_FWD_CASE(XF, WFV, BB) \
   if (a.xf32 == XF && a.wf == WFV && a.b == BB) return launch_fwd_t<XF, WFV, BB>(a, x, wc, ws, Rops, y, st);
 #define OFT_FWD_B(XF, WFV) OFT_FWD_CASE(XF, WFV, 32) OFT_FWD_CASE(XF, WFV, 16)
@@ -175,7 +177,10 @@ hipError_t launch_slots_switch(int* state, int slot, int version, hipStream_t st
 hipError_t launch_linear_fwd_slots(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws,
                                    const uint16_t* R0, const uint16_t* R1, const int* state, int* latch, void* y,
                                    hipStream_t st) {
-  hipLaunchKernelGGL(slots_latch_kernel, dim3(1), dim3(64), 0, st, state, latch);
+  {
+    ProfScope prof(st, "dense.slots_latch");
+    hipLaunchKernelGGL(slots_latch_kernel, dim3(1), dim3(64), 0, st, state, latch);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.M == 0) return err;
   DenseArgs s = a;
@@ -192,6 +197,7 @@ hipError_t launch_linear_fwd_slots(const DenseArgs& a, const void* x, const uint
 hipError_t launch_linear_fwd_base(const DenseArgs& a, const void* x, const uint8_t* wc, const void* ws, void* y,
                                   hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  ProfScope prof(st, "dense.fwd_base");
 #define OFT_BASE_CASE(XF, WFV) \
   if (a.xf32 == XF && a.wf == WFV) return launch_fwd_t<XF, WFV, 32, EPI_BASE>(a, x, wc, ws, nullptr, y, st);
   OFT_BASE_CASE(false, WF_INT4)

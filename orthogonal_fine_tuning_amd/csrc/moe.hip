@@ -27,6 +27,7 @@
 #include "gemm_nt.h"
 #include "gemm_nt_dma.h"
 #include "oft_moe.h"
+#include "oft_prof.h"
 
 namespace oft {
 namespace {
@@ -582,6 +583,7 @@ hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRout
   const int nt64 = (d.T + 63) / 64;
   int* list = reinterpret_cast<int*>(ws + L.list);
   int* ntiles = reinterpret_cast<int*>(ws + L.ntiles);
+  ProfScope prof(st, "moe.route");
   if (d.T > 0) {
     router_shape(d.E, [&](auto l, auto nv) {
       constexpr int Lc = decltype(l)::value, NVc = decltype(nv)::value;
@@ -625,10 +627,13 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
   const long wb2 = w16 ? 4 : 1;  // bytes per two weights
   int* list64 = reinterpret_cast<int*>(ws + L.list64);
   int* ntiles64 = reinterpret_cast<int*>(ws + L.ntiles64);
-  if (dec)
+  if (dec) {
+    ProfScope prof(st, "moe.worklist");
     hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, dec16 ? 16 : 64, list64,
                        ntiles64);
+  }
   {
+    ProfScope prof(st, "moe.gateup");
     NtArgs p{};
     p.a = q.x;
     p.lda = d.H;
@@ -676,6 +681,7 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     }
   }
   {
+    ProfScope prof(st, "moe.down");
     NtArgs p{};
     p.a = act;
     p.lda = d.I;
@@ -719,9 +725,11 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     }
   }
   const size_t n8 = (size_t)d.T * d.H / 8;
-  if (n8 > 0)
+  if (n8 > 0) {
+    ProfScope prof(st, "moe.combine");
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, O, d.H, d.k,
                        rt.inv_perm, rt.topk_w, n8, q.y);
+  }
   (void)P;
   return last();
 }
@@ -748,7 +756,10 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
   const int nblk_e = 2 * d.I / B;
   const bool w16 = d.wf == WF_BF16;
   const long wb2 = w16 ? 4 : 1;  // bytes per two weights
-  hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, MOE_BM, list, ntiles);
+  {
+    ProfScope prof(st, "moe.worklist");
+    hipLaunchKernelGGL(moe_worklist_kernel, dim3(1), dim3(1024), 0, st, rt.counts, d.E, MOE_BM, list, ntiles);
+  }
   if (d.T > 0) {
     NnArgs p{};
     p.src = q.dy;
@@ -778,6 +789,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     // there; with fewer rows the two-workgroups-per-CU kernel is)
     int nkt;  // column tiles = partial sums of dw per position
     if ((long)d.T * d.k >= 64L * d.E) {
+      ProfScope prof(st, "moe.dA");
       dim3 grid((d.I + nnd::BKO - 1) / nnd::BKO, (unsigned)L.max_tiles);
       if (w16)
         hipLaunchKernelGGL((gemm_nn_dma_kernel<WF_BF16, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
@@ -785,6 +797,7 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
         hipLaunchKernelGGL((gemm_nn_dma_kernel<W4F, EPI_SWIGLU_BWD, true>), grid, dim3(nnd::NTHR), 0, st, p);
       nkt = (d.I + nnd::BKO - 1) / nnd::BKO;
     } else {
+      ProfScope prof(st, "moe.dA");
       dim3 grid((d.I + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
       if (w16)
         hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_SWIGLU_BWD, true, MOE_NBUF>),
@@ -794,15 +807,21 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
                            grid, dim3(256), 0, st, p);
       nkt = (d.I + nn::BKO - 1) / nn::BKO;
     }
-    if (q.dw)
+    if (q.dw) {
+      ProfScope prof(st, "moe.dw_reduce");
       hipLaunchKernelGGL(moe_dw_reduce_kernel, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, st, dw_part, nkt, P,
                          rt.inv_perm, q.dw);
+    }
   }
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + L.dz);
-  if (q.dq || (q.dx && d.T > 0))
+  if (q.dq || (q.dx && d.T > 0)) {
+    ProfScope prof(st, "moe.dq");
     hipLaunchKernelGGL(moe_dq_kernel<B>, dim3(2 * d.I / 64, d.E), dim3(256), 0, st, dH, q.h_saved, 2 * d.I,
                        rt.offsets, q.R_f32, nblk_e, q.dq, q.R_ops, (q.dx && d.T > 0) ? dz : nullptr);
+  }
   if (q.dx && d.T > 0) {
+    {
+    ProfScope prof(st, "moe.dX");
     NnArgs p{};
     p.src = dz;
     p.lds = 2 * d.I;
@@ -830,7 +849,9 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     else
       hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, W4F, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
                          dim3(256), 0, st, p);
+    }
     const size_t n8 = (size_t)d.T * d.H / 8;
+    ProfScope prof(st, "moe.unpermute");
     hipLaunchKernelGGL(moe_unpermute_sum_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, dXp, d.H,
                        d.k, rt.inv_perm, n8, q.dx);
   }
@@ -847,6 +868,7 @@ hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutin
 hipError_t launch_moe_router_bwd(const MoeDims& d, const float* logits, const int* topk_idx, const float* dw,
                                  float* d_logits, hipStream_t st) {
   if (d.T == 0) return hipSuccess;
+  ProfScope prof(st, "moe.router_bwd");
   router_shape(d.E, [&](auto l, auto nv) {
     constexpr int Lc = decltype(l)::value, NVc = decltype(nv)::value;
     const int per = 4 * (64 / Lc);  // tokens per workgroup

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.oft_abi_version() == 6
+    assert lib.oft_abi_version() == 7
     for s in range(-6, 1):
         assert lib.oft_status_str(s)
     assert b"unknown" in lib.oft_status_str(-99)
@@ -248,3 +248,17 @@ def test_moe_bf16_weights_need_no_scales():
     # the rejection is exercised here
     assert lib.oft_moe_grouped_fwd(C.byref(_moe()), ok, ok, ok, None, ok, None, ok, C.byref(full),
                                    ok, ok, ok, ws, None) == _lib.OFT_EINVAL
+
+
+def test_prof_hook_without_gpu_work():
+    """The timing hook's bookkeeping (no GPU needed while nothing is
+    recorded): off by default, an empty list, and reads out of range
+    rejected."""
+    lib = _lib.load()
+    assert lib.oft_prof_count() == 0
+    buf = C.create_string_buffer(16)
+    ms = C.c_float(0.0)
+    assert lib.oft_prof_read(0, buf, 16, C.byref(ms)) == _lib.OFT_EINVAL
+    assert lib.oft_prof_read(-1, buf, 16, C.byref(ms)) == _lib.OFT_EINVAL
+    assert lib.oft_prof_enable(0) == _lib.OFT_OK  # stopping never touches the device
+    assert lib.oft_prof_count() == 0

@@ -2,8 +2,10 @@
 
 Routing tables must match bit for bit; outputs and gradients to
 max|a - ref| / max|ref| <= 2e-2; combine weights to 1e-5 relative.
-Full-size configurations are checked on sampled tokens (y, dX, dw) and
-sampled experts (dQ), which the oracle computes one by one.
+At full size the decode shape is compared whole; at the training shapes the
+hottest, a median and the coldest expert are compared in full (saved
+activations, dQ) and every 128-row tile of each through tokens it holds
+(y, dX, dw), which the oracle computes expert by expert.
 """
 from concurrent.futures import ThreadPoolExecutor
 
@@ -299,8 +301,11 @@ def test_moe_zero_tokens():
     assert host(out["rt"]["n_active"])[0] == 0
 
 
-# ------------------------------------------------------------ full size, sampled
-def _sampled_reference(inp, tokens, experts, threads=16):
+# ------------------------------------------------------------ full size
+def _reference_subset(inp, tokens, experts, threads=16):
+    """The oracle on a subset: y, dX and dw of the given tokens (through all
+    k experts of each), and the full saved activations h and the full dQ of
+    the given experts (over every row the expert holds)."""
     cfg = inp["cfg"]
     k = cfg.k
     idx, w = omoe.route(inp["logits"], k)
@@ -308,27 +313,37 @@ def _sampled_reference(inp, tokens, experts, threads=16):
     X = codec.bf16_bits_to_f64(inp["x"])
     dy = codec.bf16_bits_to_f64(inp["dy"])
     wflat = w.reshape(-1)
-    need = sorted(set(int(idx[t, j]) for t in tokens for j in range(k)) | set(experts))
+    tokset = set(int(t) for t in tokens)
+    need = sorted(set(int(idx[t, j]) for t in tokset for j in range(k)) | set(int(e) for e in experts))
+
+    expset = set(int(e) for e in experts)
 
     def one(e):
         pairs_all = rt["perm"][rt["offsets"][e]:rt["offsets"][e + 1]]
-        sel = [p for p in pairs_all if p // k in set(tokens)]
+        insel = np.asarray([int(p) // k in tokset for p in pairs_all], dtype=bool)
+        sel = pairs_all[insel]
         Wgu, Wd, R = omoe.expert_weights(inp, e)
         res = {}
-        if sel:
-            sel = np.asarray(sel)
+        if e in expset:  # every row of the expert: its h and its dQ
+            if pairs_all.size:
+                _, Hh, _, O = omoe.expert_forward(X[pairs_all // k], Wgu, Wd, R, cfg.I)
+                dwe, dpe, dXp = omoe.expert_backward(inp, e, pairs_all, X, dy, wflat)
+                res["h"], res["dp"] = Hh, dpe
+                if sel.size:
+                    res["tok"] = (sel, O[insel], dwe[insel], dXp[insel])
+            else:
+                res["h"] = np.zeros((0, 2 * cfg.I))
+                res["dp"] = np.zeros((cfg.nblk_e, cfg.npair))
+        elif sel.size:
             _, _, _, O = omoe.expert_forward(X[sel // k], Wgu, Wd, R, cfg.I)
             dwe, _, dXp = omoe.expert_backward(inp, e, sel, X, dy, wflat)
             res["tok"] = (sel, O, dwe, dXp)
-        if e in experts:
-            res["dp"] = omoe.expert_backward(inp, e, pairs_all, X, dy, wflat)[1] if len(pairs_all) else \
-                np.zeros((cfg.nblk_e, cfg.npair))
         return e, res
 
     with ThreadPoolExecutor(threads) as ex:
         results = dict(ex.map(one, need))
-    y = {t: np.zeros(cfg.H) for t in tokens}
-    dx = {t: np.zeros(cfg.H) for t in tokens}
+    y = {t: np.zeros(cfg.H) for t in tokset}
+    dx = {t: np.zeros(cfg.H) for t in tokset}
     dw = {}
     for e, res in results.items():
         if "tok" in res:
@@ -338,40 +353,114 @@ def _sampled_reference(inp, tokens, experts, threads=16):
                 y[t] += wflat[p] * O[r]
                 dx[t] += dXp[r]
                 dw[int(p)] = dwe[r]
+    h = {e: results[e]["h"] for e in experts}
     dp = {e: results[e]["dp"] for e in experts}
-    return rt, y, dx, dw, dp
+    return rt, y, dx, dw, h, dp
+
+
+def _tile_tokens(rt, e, k, tile=128):
+    """Tokens that put a row in every 128-row tile of expert e: the first,
+    a middle and the last row of each tile."""
+    lo, hi = int(rt["offsets"][e]), int(rt["offsets"][e + 1])
+    toks = set()
+    for t0 in range(lo, hi, tile):
+        t1 = min(hi, t0 + tile) - 1
+        for pos in (t0, (t0 + t1) // 2, t1):
+            toks.add(int(rt["perm"][pos]) // k)
+    return toks
+
+
+def _compare(name, cfg, out, rt, tokens, y, dx, dw, h, dp):
+    gy = bf16_to_f64(host(out["y"]))
+    gdx = bf16_to_f64(host(out["dx"]))
+    ghs = host(out["hs"])
+    gdw = host(out["dw"]).reshape(-1)
+    gdq = host(out["dq"])
+    tokens = sorted(tokens)
+    e_y = err(np.stack([gy[t] for t in tokens]), np.stack([y[t] for t in tokens]))
+    e_dx = err(np.stack([gdx[t] for t in tokens]), np.stack([dx[t] for t in tokens]))
+    ps = sorted(dw)
+    e_dw = err(gdw[ps], np.array([dw[p] for p in ps]))
+    e_h = max(err(bf16_to_f64(ghs[rt["offsets"][e]:rt["offsets"][e + 1]]), h[e]) for e in h if h[e].size)
+    e_dq = max(err(gdq[e], dp[e]) for e in dp if np.abs(dp[e]).max() > 0)
+    print(f"  {name}: {len(tokens)} tokens, experts {sorted(dp)}: err y={e_y:.2e} dx={e_dx:.2e} dw={e_dw:.2e} "
+          f"h={e_h:.2e} dq={e_dq:.2e}", flush=True)
+    assert max(e_y, e_dx, e_dw, e_h, e_dq) <= TOL
 
 
 # the MoE workloads on FP4 experts, as `bench.py --w-fmt fp4` times them
 MOE_FULL_FP4 = {n + "_fp4": CONFIGS[n].with_(name=n + "_fp4", w_fmt="fp4") for n in ("moe_30b_a3b", "moe_1t_decode")}
 
 
-@pytest.mark.parametrize("name", ["moe_30b_a3b", "moe_1t_train", "moe_1t_decode", "moe_30b_a3b_fp4",
-                                  "moe_1t_decode_fp4"])
-def test_moe_full_size_sampled(name):
+@pytest.mark.parametrize("name", ["moe_30b_a3b", "moe_1t_train", "moe_30b_a3b_fp4"])
+def test_moe_full_size_tiles(name):
+    """Training shapes: the hottest, a median and the coldest active expert,
+    every 128-row tile of each covered by compared tokens (y, dX, dw through
+    all their experts), and those experts' full saved activations h and
+    full dQ."""
     cfg = MOE_FULL_FP4.get(name) or CONFIGS[name]
     print(f"[moe full size] {name}: generating inputs", flush=True)
     inp = make_moe(cfg, seed=0)
     print(f"[moe full size] {name}: GPU fwd+bwd", flush=True)
     out = _run_moe(inp)
     counts = host(out["rt"]["counts"])
-    order = np.argsort(-counts, kind="stable")
-    experts = [int(order[0]), int(order[len(order) // 2])]
-    inactive = np.nonzero(counts == 0)[0]
-    tokens = [0, cfg.T // 3, cfg.T - 1]
-    print(f"[moe full size] {name}: oracle on tokens {tokens}, experts {experts}", flush=True)
-    rt, y, dx, dw, dp = _sampled_reference(inp, tokens, experts)
-    assert np.array_equal(counts, rt["counts"])
-    gy = bf16_to_f64(host(out["y"]))
-    gdx = bf16_to_f64(host(out["dx"]))
-    gdw = host(out["dw"]).reshape(-1)
+    act = np.nonzero(counts)[0]
+    order = act[np.argsort(-counts[act], kind="stable")]
+    experts = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    idx, _ = omoe.route(inp["logits"], cfg.k)
+    rtg = omoe.group(idx, cfg.E, cfg.chunk)
+    assert np.array_equal(counts, rtg["counts"])
+    tokens = set()
+    for e in experts:
+        tokens |= _tile_tokens(rtg, e, cfg.k)
+    print(f"[moe full size] {name}: oracle on {len(tokens)} tokens, experts {experts} "
+          f"(rows {[int(counts[e]) for e in experts]})", flush=True)
+    rt, y, dx, dw, h, dp = _reference_subset(inp, tokens, experts)
+    _compare(name, cfg, out, rt, tokens, y, dx, dw, h, dp)
     gdq = host(out["dq"])
-    e_y = err(np.stack([gy[t] for t in tokens]), np.stack([y[t] for t in tokens]))
-    e_dx = err(np.stack([gdx[t] for t in tokens]), np.stack([dx[t] for t in tokens]))
-    ps = sorted(dw)
-    e_dw = err(gdw[ps], np.array([dw[p] for p in ps]))
-    e_dq = max(err(gdq[e], dp[e]) for e in experts)
-    print(f"  err y={e_y:.2e} dx={e_dx:.2e} dw={e_dw:.2e} dq={e_dq:.2e} inactive={len(inactive)}", flush=True)
-    assert max(e_y, e_dx, e_dw, e_dq) <= TOL
-    for e in inactive[:8]:
+    for e in np.nonzero(counts == 0)[0]:
         assert np.all(gdq[e] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["moe_1t_decode", "moe_1t_decode_fp4"])
+def test_moe_decode_full(name):
+    """The decode shape whole: every token's y, dX and dw, every active
+    expert's saved activations and dQ, zero dQ for the inactive ones."""
+    cfg = MOE_FULL_FP4.get(name) or CONFIGS[name]
+    print(f"[moe decode full] {name}: generating inputs", flush=True)
+    inp = make_moe(cfg, seed=0)
+    print(f"[moe decode full] {name}: GPU fwd+bwd", flush=True)
+    out = _run_moe(inp)
+    counts = host(out["rt"]["counts"])
+    experts = [int(e) for e in np.nonzero(counts)[0]]
+    print(f"[moe decode full] {name}: oracle on all {cfg.T} tokens, {len(experts)} experts", flush=True)
+    rt, y, dx, dw, h, dp = _reference_subset(inp, range(cfg.T), experts)
+    assert len(dw) == cfg.T * cfg.k
+    _compare(name, cfg, out, rt, range(cfg.T), y, dx, dw, h, dp)
+    gdq = host(out["dq"])
+    for e in np.nonzero(counts == 0)[0]:
+        assert np.all(gdq[e] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["moe_small_b32", "moe_decode16_b32", "moe_30b_a3b"])
+def test_moe_chunk_size_invariance(name):
+    """The chunk size schedules the active experts; it must not change any
+    result: y, h, dX, dQ and dw bit for bit for chunk 1, the configured
+    chunk and E (one chunk), and the chunk table follows each."""
+    cfg = SMALL.get(name) or CONFIGS[name]
+    inp = make_moe(cfg, seed=2)
+    runs = {}
+    for c in sorted({1, cfg.chunk, cfg.E}):
+        print(f"[moe chunk invariance] {name}: chunk {c}", flush=True)
+        inp["cfg"] = cfg.with_(chunk=c)
+        o = _run_moe(inp)
+        rt = {kk: host(v) for kk, v in o["rt"].items()}
+        act = rt["active"][:rt["n_active"][0]]
+        want = np.full(cfg.E, -1)
+        want[act] = np.arange(act.size) // c
+        assert np.array_equal(rt["chunk_of_expert"], want)
+        runs[c] = {kk: host(o[kk]) for kk in ("y", "hs", "dx", "dq", "dw")}
+    first = runs[1]
+    for c, r in runs.items():
+        for kk in first:
+            assert np.array_equal(r[kk], first[kk]), (c, kk)
