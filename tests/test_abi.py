@@ -262,3 +262,34 @@ def test_prof_hook_without_gpu_work():
     assert lib.oft_prof_read(-1, buf, 16, C.byref(ms)) == _lib.OFT_EINVAL
     assert lib.oft_prof_enable(0) == _lib.OFT_OK  # stopping never touches the device
     assert lib.oft_prof_count() == 0
+
+
+def test_every_gpu_test_shape_passes_validation():
+    """Every dense and MoE configuration the GPU tests run is a valid
+    descriptor (checked here on the CPU, so a bad test shape never reaches
+    the GPU)."""
+    import importlib.util
+
+    from oft_inputs import CONFIGS
+
+    def mod(name):
+        spec = importlib.util.spec_from_file_location(name, os.path.join(os.path.dirname(__file__), name + ".py"))
+        m = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(m)
+        return m
+
+    lib = _lib.load()
+    dense_m, moe_m = mod("test_gpu_dense"), mod("test_gpu_moe")
+    wf = {"int4": oft.OFT_W_INT4, "fp8": oft.OFT_W_FP8_E4M3, "fp4": oft.OFT_W_FP4_E2M1}
+    dense = list(dense_m.SMALL.values()) + list(dense_m.FULL_EXTRA.values()) + \
+        [c for c in CONFIGS.values() if hasattr(c, "segs")]
+    n = C.c_size_t(0)
+    for c in dense:
+        d = oft.linear_desc(c.M, c.K, c.segs, c.b, oft.OFT_DT_F32 if c.x_dtype == "f32" else oft.OFT_DT_BF16,
+                            wf[c.w_fmt], c.g)
+        assert lib.oft_linear_workspace_bytes(C.byref(d), 1, C.byref(n)) == _lib.OFT_OK, c.name
+    moe = list(moe_m.SMALL.values()) + list(moe_m.ROUTER.values()) + list(moe_m.MOE_FULL_FP4.values()) + \
+        [c for c in CONFIGS.values() if not hasattr(c, "segs")]
+    for c in moe:
+        d = oft.moe_desc(c.T, c.E, c.k, c.H, c.I, c.g, c.b, c.chunk, 0, w_fmt=wf[c.w_fmt])
+        assert lib.oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == _lib.OFT_OK, c.name

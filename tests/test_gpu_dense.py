@@ -70,7 +70,7 @@ SMALL = {
     # and INT4 with b = 16 (gemm_nn dX)
     "fp8_8seg": DenseConfig("fp8_8seg", M=300, K=512, segs=(64, 32, 96, 32, 64, 128, 32, 64), b=32,
                             x_dtype="bf16", w_fmt="fp8"),
-    "int4_8seg_b16": DenseConfig("int4_8seg_b16", M=150, K=256, segs=(16, 48, 32, 16, 64, 16, 32, 16), b=16,
+    "int4_8seg_b16": DenseConfig("int4_8seg_b16", M=150, K=256, segs=(16, 48, 32, 16, 64, 16, 32, 32), b=16,
                                  x_dtype="bf16", w_fmt="int4", g=32, q_std=0.05),
 }
 
