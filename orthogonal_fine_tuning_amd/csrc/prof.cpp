@@ -60,7 +60,7 @@ int32_t oft_prof_enable(int32_t on) {
     }
     g_events = true;
   }
-  g_n = 0;
+  if (on) g_n = 0;  // stopping keeps the records readable
   g_on.store(on != 0, std::memory_order_relaxed);
   return OFT_OK;
 }
