@@ -267,6 +267,21 @@ int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void*
                        const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ---- reference-policy log-probabilities ------------------------------------
+ * The KL regulariser of the pages compares the trained policy with the
+ * frozen base run without the adapter (the chooseai.io page's "Five design
+ * features of the adapter-first architecture": zero extra reference model);
+ * its estimate needs both policies' log-probability of the sampled token.
+ * out[t] = log softmax(logits_actor[t])[labels[t]]
+ *        - log softmax(logits_ref[t])[labels[t]]   (natural log, fp32)
+ * logits_* fp32 [T, V] (e.g. the vocabulary projection of the adapted layers'
+ * and the oft_*_fwd_base outputs), labels int32 [T], out fp32 [T]; a label
+ * outside [0, V) gives NaN.  Deterministic (fixed-order reductions).
+ * T == 0 is a no-op.  Errors: OFT_EINVAL (T < 0, V < 1, T V >= 2^40, a NULL
+ * or misaligned pointer). */
+int32_t oft_logprob_diff(int32_t T, int32_t V, const float* logits_actor, const float* logits_ref,
+                         const int32_t* labels, float* out, void* stream);
+
 /* ---- MoE layer ------------------------------------------------------------ */
 int32_t oft_moe_workspace_bytes(const oft_moe_desc* d, int32_t pass, size_t* bytes);
 
@@ -291,6 +306,22 @@ int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const floa
                             const uint16_t* R_ops, const oft_moe_routing* rt,
                             uint16_t* h_saved, uint16_t* y, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* Reference-policy forward of the MoE layer: the frozen base alone, every
+ * expert's gate/up projection without its adapter rotation (the pages'
+ * section "Five design features of the adapter-first architecture" takes the
+ * KL reference from the frozen base, so no copy of the actor is kept).  The
+ * same routing, grouped dequant GEMMs, SwiGLU, down projection and combine
+ * as oft_moe_grouped_fwd, with the rotation epilogue left out: y is
+ * bit-identical to oft_moe_grouped_fwd's with Q = 0 (R exactly I).
+ * h_or_null, when set, receives the un-rotated gate/up output [P, 2I] in
+ * permuted order (nothing reads it back: a reference pass has no backward).
+ * Arguments otherwise as oft_moe_grouped_fwd, without R_ops; the block size
+ * b is validated but plays no part.  Errors as oft_moe_grouped_fwd. */
+int32_t oft_moe_grouped_fwd_base(const oft_moe_desc* d, const uint16_t* x, const float* logits,
+                                 const uint8_t* wgu_codes, const uint16_t* wgu_scales, const uint8_t* wd_codes,
+                                 const uint16_t* wd_scales, const oft_moe_routing* rt, uint16_t* h_or_null,
+                                 uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of <dy, y> with the routing fixed: dx [T, H] bf16 through the
  * experts, dq fp32 [E, 2I/b, b(b-1)/2] (zero for inactive experts) and

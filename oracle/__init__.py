@@ -40,4 +40,4 @@ the dequant rounding, per-expert adapters, SwiGLU, un-renormalised combine
 weights) are "parity unpinned" by the pages: they are fixed by the tests only
 as this library's stated convention.
 """
-from . import codec, dense, moe  # noqa: F401
+from . import codec, dense, moe, policy  # noqa: F401

@@ -242,6 +242,35 @@ def backward(inp: dict, rt: dict, experts=None, threads: int = 1, X=None, P=None
     return dX, dp_all, dw.reshape(T, k)
 
 
+def base_forward(inp: dict, rt: dict | None = None):
+    """The frozen base alone, the reference policy of [P2] "Five design
+    features" (no copy of the actor: the base without the adapter):
+    y[t] = sum_j w[t, j] * W_d,e . SwiGLU(W_gu,e . x[t]), e = idx[t, j], the
+    gate/up output not rotated.  Returns (y [T, H], Z [P, 2I] in permuted
+    order, rt)."""
+    cfg = inp["cfg"]
+    T, k, H, I = cfg.T, cfg.k, cfg.H, cfg.I
+    if rt is None:
+        idx, w = route(inp["logits"], k)
+        rt = group(idx, cfg.E, cfg.chunk)
+        rt.update(idx=idx, w=w)
+    X = bf16_bits_to_f64(inp["x"])
+    wflat = rt["w"].reshape(-1)
+    y = np.zeros((T, H))
+    Zs = np.zeros((T * k, 2 * I))
+    for e in rt["active"]:
+        e = int(e)
+        lo, hi = rt["offsets"][e], rt["offsets"][e + 1]
+        pairs = rt["perm"][lo:hi]
+        Wgu = dequant_fmt(cfg.w_fmt, inp["wgu_codes"][e], inp["wgu_scales"][e], cfg.g)
+        Wd = dequant_fmt(cfg.w_fmt, inp["wd_codes"][e], inp["wd_scales"][e], cfg.g)
+        Z = X[pairs // k] @ Wgu.T
+        act = silu(Z[:, :I]) * Z[:, I:]
+        Zs[lo:hi] = Z
+        np.add.at(y, pairs // k, wflat[pairs][:, None] * (act @ Wd.T))
+    return y, Zs, rt
+
+
 def bruteforce_forward(inp: dict, idx: np.ndarray, w: np.ndarray) -> np.ndarray:
     """Every token through every expert with gate w[t, j] if selected else 0.
 

@@ -15,9 +15,9 @@ from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF
 
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
-    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd",
+    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd", "oft_logprob_diff",
     "oft_slots_switch", "oft_linear_fwd_slots",
-    "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_bwd", "abi_version",
+    "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_fwd_base", "oft_moe_grouped_bwd", "abi_version",
     "prof_enable", "prof_records",
     "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_W_FP4_E2M1", "OFT_PASS_FWD",
     "OFT_PASS_BWD",
@@ -138,6 +138,12 @@ def oft_linear_bwd(desc, dy, y_saved, w_codes, w_scales, R_f32, R_ops, dx=None, 
                "oft_linear_bwd")
 
 
+def oft_logprob_diff(logits_actor, logits_ref, labels, out, stream=None):
+    T, V = logits_actor.shape
+    _lib.check(_lib.load().oft_logprob_diff(int(T), int(V), _ptr(logits_actor), _ptr(logits_ref), _ptr(labels),
+                                            _ptr(out), _stream(stream)), "oft_logprob_diff")
+
+
 def oft_moe_workspace_bytes(desc, pass_) -> int:
     n = C.c_size_t(0)
     _lib.check(_lib.load().oft_moe_workspace_bytes(C.byref(desc), pass_, C.byref(n)),
@@ -161,6 +167,13 @@ def oft_moe_grouped_fwd(desc, x, logits, wgu_codes, wgu_scales, wd_codes, wd_sca
         C.byref(desc), _ptr(x), _ptr(logits), _ptr(wgu_codes), _ptr(wgu_scales), _ptr(wd_codes),
         _ptr(wd_scales), _ptr(R_ops), C.byref(rt), _ptr(h_saved), _ptr(y), _ptr(ws), ws_bytes,
         _stream(stream)), "oft_moe_grouped_fwd")
+
+
+def oft_moe_grouped_fwd_base(desc, x, logits, wgu_codes, wgu_scales, wd_codes, wd_scales, rt, h=None, y=None,
+                             ws=None, ws_bytes=0, stream=None):
+    _lib.check(_lib.load().oft_moe_grouped_fwd_base(
+        C.byref(desc), _ptr(x), _ptr(logits), _ptr(wgu_codes), _ptr(wgu_scales), _ptr(wd_codes), _ptr(wd_scales),
+        C.byref(rt), _ptr(h), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)), "oft_moe_grouped_fwd_base")
 
 
 def oft_moe_grouped_bwd(desc, dy, rt, h_saved, wgu_codes, wgu_scales, wd_codes, wd_scales, R_f32,

@@ -60,10 +60,13 @@ SIGNATURES = {
     "oft_moe_router_bwd": (_I, [C.POINTER(oft_moe_desc), _P, _P, _P, _P, _P]),
     "oft_linear_bwd": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                             _P]),
+    "oft_logprob_diff": (_I, [_I, _I, _P, _P, _P, _P, _P]),
     "oft_moe_workspace_bytes": (_I, [C.POINTER(oft_moe_desc), _I, C.POINTER(_SZ)]),
     "oft_moe_route": (_I, [C.POINTER(oft_moe_desc), _P, C.POINTER(oft_moe_routing), _P, _SZ, _P]),
     "oft_moe_grouped_fwd": (_I, [C.POINTER(oft_moe_desc), _P, _P, _P, _P, _P, _P, _P,
                                  C.POINTER(oft_moe_routing), _P, _P, _P, _SZ, _P]),
+    "oft_moe_grouped_fwd_base": (_I, [C.POINTER(oft_moe_desc), _P, _P, _P, _P, _P, _P,
+                                      C.POINTER(oft_moe_routing), _P, _P, _P, _SZ, _P]),
     "oft_moe_grouped_bwd": (_I, [C.POINTER(oft_moe_desc), _P, C.POINTER(oft_moe_routing), _P, _P,
                                  _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }

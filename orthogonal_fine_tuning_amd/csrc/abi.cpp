@@ -183,6 +183,15 @@ int32_t oft_linear_fwd_slots(const oft_linear_desc* d, const void* x, const uint
                                                  y, static_cast<hipStream_t>(stream)));
 }
 
+int32_t oft_logprob_diff(int32_t T, int32_t V, const float* logits_actor, const float* logits_ref,
+                         const int32_t* labels, float* out, void* stream) {
+  if (T < 0 || V < 1 || (long long)T * V >= (1LL << 40)) return OFT_EINVAL;
+  if (T == 0) return OFT_OK;
+  if (!ptr_ok(logits_actor) || !ptr_ok(logits_ref) || !ptr_ok(labels) || !ptr_ok(out)) return OFT_EINVAL;
+  return hip_status(oft::launch_logprob_diff(T, V, logits_actor, logits_ref, labels, out,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void* y_saved,
                        const uint8_t* w_codes, const void* w_scales, const float* R_f32,
                        const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,

@@ -97,12 +97,10 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
   const int l32 = lane & 31, g2 = lane >> 5;
   const int wk = wave >> 1, wm = wave & 1;
   const int K = p.K, N = p.N;
-  const int k0 = blockIdx.x * BKO;
-
-  int e = 0, pos0, nrows;
+  int e = 0, pos0, nrows, cx = blockIdx.x;
   if constexpr (GROUPED) {
-    const int t = blockIdx.y;
-    if (t >= *p.ntiles) return;
+    int t;
+    if (!grouped_tile(*p.ntiles, cx, t)) return;
     e = p.tiles[2 * t];
     const int r0 = p.tiles[2 * t + 1];
     pos0 = p.offsets[e] + r0;
@@ -111,6 +109,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
     pos0 = blockIdx.y * BM;
     nrows = min(BM, p.M - pos0);
   }
+  const int k0 = cx * BKO;
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
   const uint16_t* rops = p.rops + (size_t)e * p.rops_e;
   const float* ws_f = static_cast<const float*>(p.ws);
@@ -437,7 +436,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
         const int ml = wm * (BM / 2) + tm * 32 + l32;
-        if (ml < nrows) p.dw_part[(size_t)blockIdx.x * p.P + pos0 + ml] = dwp[tm] + dwred[ml];
+        if (ml < nrows) p.dw_part[(size_t)cx * p.P + pos0 + ml] = dwp[tm] + dwred[ml];
       }
     }
   }

@@ -91,13 +91,12 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
   const int wk = wave & 3, wm = wave >> 2;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
-  const int kbase = blockIdx.x * BKO;
   const int ns = p.N / BNS;  // the host guarantees N % 64 == 0
 
-  int e = 0, pos0, nrows;
+  int e = 0, pos0, nrows, cx = blockIdx.x;
   if constexpr (GROUPED) {
-    const int t = blockIdx.y;
-    if (t >= *p.ntiles) return;
+    int t;
+    if (!grouped_tile(*p.ntiles, cx, t)) return;
     e = p.tiles[2 * t];
     pos0 = p.offsets[e] + p.tiles[2 * t + 1];
     nrows = min(BM, p.offsets[e + 1] - pos0);
@@ -105,6 +104,7 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
     pos0 = blockIdx.y * BM;
     nrows = min(BM, p.M - pos0);
   }
+  const int kbase = cx * BKO;
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
 
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
       for (int tm = 0; tm < TM; ++tm) {
         const int ml = 64 * wm + 32 * tm + l32;
         if (ml < nrows)
-          p.dw_part[(size_t)blockIdx.x * p.P + pos0 + ml] =
+          p.dw_part[(size_t)cx * p.P + pos0 + ml] =
               ((red[ml] + red[BM + ml]) + red[2 * BM + ml]) + red[3 * BM + ml];
       }
     }

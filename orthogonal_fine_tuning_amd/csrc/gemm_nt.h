@@ -18,16 +18,20 @@
 //                    matching 64 up channels [I+c, I+c+64); both are rotated
 //                    and stored, then act = silu(gate) * up (from the bf16
 //                    values just stored) is written as well;
-//   EPI_BASE       : FP8 scale, store rows (the frozen base alone, R = I).
+//   EPI_BASE       : FP8 scale, store rows (the frozen base alone, R = I);
+//   EPI_BASE_SWIGLU: EPI_ROT_SWIGLU without the rotation (the frozen base
+//                    alone); the h store is skipped when out is null.
 #pragma once
 
 #include "oft_device.h"
 
 namespace oft {
 
-enum : int { EPI_ROT = 0, EPI_PLAIN = 1, EPI_ROT_SWIGLU = 2, EPI_BASE = 3 };
+enum : int { EPI_ROT = 0, EPI_PLAIN = 1, EPI_ROT_SWIGLU = 2, EPI_BASE = 3, EPI_BASE_SWIGLU = 4 };
 // epilogues that apply the block rotation
 constexpr bool epi_rotates(int epi) { return epi == EPI_ROT || epi == EPI_ROT_SWIGLU; }
+// epilogues of the gate/up projection: gate and up channel halves, SwiGLU
+constexpr bool epi_swiglu(int epi) { return epi == EPI_ROT_SWIGLU || epi == EPI_BASE_SWIGLU; }
 
 struct NtArgs {
   const void* a;

@@ -12,7 +12,8 @@
 // EPI_ROT_SWIGLU: the 256-channel tile is 128 gate channels [c, c + 128) and
 // the matching 128 up channels [I + c, I + c + 128); both are rotated and
 // stored, then act = silu(gate) * up, the up waves handing their bf16
-// outputs to the gate waves through LDS.
+// outputs to the gate waves through LDS.  EPI_BASE_SWIGLU: the same without
+// the rotation (the frozen base alone), h stored only when out is set.
 //
 // Workgroup: 8 waves, tile 256 channels x BM tokens (BM = 128 or 192), K
 // steps of 64.  FP8 and bf16 weights: wave (wn, wm) = (wave % 4, wave / 4)
@@ -128,11 +129,11 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   static_assert(KB == 64 || (KB == 128 && WF == WF_FP8 && BM <= 192 && !GROUPED), "128-wide K steps: FP8, <= 192 tokens");
   static_assert(BM == 128 || BM == 192, "tile");
   static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
-  static_assert(EPI != EPI_ROT_SWIGLU || BM == 128, "exchange buffer sized for 128-token tiles");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || epi_swiglu(EPI) || EPI == EPI_BASE, "epilogue");
+  static_assert(!epi_swiglu(EPI) || BM == 128, "exchange buffer sized for 128-token tiles");
   constexpr bool FP8 = WF == WF_FP8;
   constexpr bool W16 = WF == WF_BF16;
-  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
+  constexpr bool SWI = epi_swiglu(EPI);
   // wave layout: INT4 weights on 128-token tiles, 8 waves x 32 channels over
   // every token of the tile (each code row is dequantised by one wave only);
   // otherwise 4 x 2 waves of 64 channels x BM / 2 tokens
@@ -170,10 +171,10 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   const int K = p.K;
 
   // ---- tile: rows (tokens / expert positions) and weight rows (channels)
-  int e = 0, pos0, nrows;
+  int e = 0, pos0, nrows, cx = blockIdx.x;
   if constexpr (GROUPED) {
-    const int t = blockIdx.y;
-    if (t >= *p.ntiles) return;
+    int t;
+    if (!grouped_tile(*p.ntiles, cx, t)) return;
     e = p.tiles[2 * t];
     pos0 = p.offsets[e] + p.tiles[2 * t + 1];
     nrows = min(BM, p.offsets[e + 1] - pos0);
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
   const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
   // channel of local weight row rw (0..255), or -1 past the layer's channels
-  const int cbase = SWI ? blockIdx.x * (BN / 2) : blockIdx.x * BN;
+  const int cbase = SWI ? cx * (BN / 2) : cx * BN;
   auto chan = [&](int rw) -> int {
     if constexpr (SWI) {
       const int c = cbase + (rw & (BN / 2 - 1));
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
           swg[tn][tm][2 * q] = lo;
           swg[tn][tm][2 * q + 1] = hi;
         }
-        if (m_ok) {
+        if (m_ok && (!SWI || p.out != nullptr)) {  // gate/up: the h store is optional
           const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
           if constexpr (OUTF32) {
             *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) =
@@ -581,7 +582,7 @@ template <bool FP8, int B, int EPI, int TM, int SMEM>
 __device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], uint8_t* smem, int wn, int kh,
                                            int lane, int nb, int nrows, int pos0, const uint16_t* rops) {
   using namespace ntd;
-  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
+  constexpr bool SWI = epi_swiglu(EPI);
   const int l32 = lane & 31, g2 = lane >> 5;
   lds_barrier_plain();
   float* red = reinterpret_cast<float*>(smem);
@@ -667,7 +668,7 @@ __device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], u
           swg[tm][2 * q] = lo;
           swg[tm][2 * q + 1] = hi;
         }
-        if (ml < nrows) {
+        if (ml < nrows && (!SWI || p.out != nullptr)) {  // gate/up: the h store is optional
           const size_t off = (size_t)(pos0 + ml) * p.ldo + nb + 8 * q + 4 * g2;
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) = make_uint2(lo, hi);
         }
@@ -741,9 +742,9 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_d
   using namespace ntd;
   constexpr bool FP8 = WF == WF_FP8;
   static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || epi_swiglu(EPI) || EPI == EPI_BASE, "epilogue");
   static_assert(BMD == 64 || (BMD == 16 && !FP8 && GROUPED), "16-row tiles: grouped 4-bit weights");
-  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
+  constexpr bool SWI = epi_swiglu(EPI);
   // INT4: three stages (75 KB; 16-row tiles: five, 65 KB), two workgroups
   // per CU; FP8: four stages
     constexpr int TM = BMD == 64 ? 2 : 1, NST = FP8 ? DEC_NST : (BMD == 16 ? 5 : DEC_NST - 1);
@@ -759,10 +760,10 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_d
   const int wn = wave & 3, kh = wave >> 2;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
-  int e = 0, pos0, nrows;
+  int e = 0, pos0, nrows, cx = blockIdx.x;
   if constexpr (GROUPED) {
-    const int t = blockIdx.y;
-    if (t >= *p.ntiles) return;
+    int t;
+    if (!grouped_tile(*p.ntiles, cx, t)) return;
     e = p.tiles[2 * t];
     pos0 = p.offsets[e] + p.tiles[2 * t + 1];
     nrows = min(BMD, p.offsets[e + 1] - pos0);
@@ -774,7 +775,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_d
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
   const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
   // channel of local weight row rw (0..127), or -1 past the layer's channels
-  const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
+  const int cbase = SWI ? cx * (DEC_BN / 2) : cx * DEC_BN;
   auto chan = [&](int rw) -> int {
     if constexpr (SWI) {
       const int c = cbase + (rw & (DEC_BN / 2 - 1));
@@ -956,8 +957,8 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   static_assert(wf_4bit(WF), "4-bit weights");
   using namespace ntd;
   static_assert(BMD == 16 || BMD == 64, "tile rows");
-  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_ROT_SWIGLU || EPI == EPI_BASE, "epilogue");
-  constexpr bool SWI = EPI == EPI_ROT_SWIGLU;
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || epi_swiglu(EPI) || EPI == EPI_BASE, "epilogue");
+  constexpr bool SWI = epi_swiglu(EPI);
   constexpr int TM = BMD == 64 ? 2 : 1, NST = D4_NST;
   constexpr int WBY = 128 * 128, SBY = 128 * 16, XBY = BMD * 512, SB = WBY + SBY + XBY;
   constexpr int XI = BMD / 16;  // activation copies per wave per step (2 rows x 512 B each)
@@ -969,10 +970,10 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   const int wn = wave & 3, kh = wave >> 2;
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
-  int e = 0, pos0, nrows;
+  int e = 0, pos0, nrows, cx = blockIdx.x;
   if constexpr (GROUPED) {
-    const int t = blockIdx.y;
-    if (t >= *p.ntiles) return;
+    int t;
+    if (!grouped_tile(*p.ntiles, cx, t)) return;
     e = p.tiles[2 * t];
     pos0 = p.offsets[e] + p.tiles[2 * t + 1];
     nrows = min(BMD, p.offsets[e + 1] - pos0);
@@ -983,7 +984,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
   const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e;
   const uint16_t* rops = nt_rops(p) + (size_t)e * p.rops_e;
-  const int cbase = SWI ? blockIdx.x * (DEC_BN / 2) : blockIdx.x * DEC_BN;
+  const int cbase = SWI ? cx * (DEC_BN / 2) : cx * DEC_BN;
   auto chan = [&](int rw) -> int {
     if constexpr (SWI) {
       const int c = cbase + (rw & (DEC_BN / 2 - 1));

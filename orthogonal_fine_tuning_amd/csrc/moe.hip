@@ -606,8 +606,10 @@ hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRout
   return last();
 }
 
-// W4F: the 4-bit format of the weights when they are not bf16
-template <int B, int W4F>
+// W4F: the 4-bit format of the weights when they are not bf16; GEPI: the
+// gate/up epilogue, EPI_ROT_SWIGLU (the adapted layer) or EPI_BASE_SWIGLU
+// (the frozen base alone: no rotation, h stored only when q.h_saved is set)
+template <int B, int W4F, int GEPI>
 static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                                 const MoeWs& L, hipStream_t st) {
   const long P = (long)d.T * d.k;
@@ -642,7 +644,7 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.wc_e = (long)2 * d.I * d.H / 2 * wb2;
     p.ws_e = w16 ? 0 : (long)2 * d.I * (d.H / d.g);
     p.rops = q.R_ops;
-    p.rops_e = (long)nblk_e * 2 * B * B;
+    p.rops_e = GEPI == EPI_ROT_SWIGLU ? (long)nblk_e * 2 * B * B : 0;
     p.out = q.h_saved;
     p.ldo = 2 * d.I;
     p.act = act;
@@ -660,24 +662,24 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     if (dma) {
       dim3 grid((d.I + ntd::BN / 2 - 1) / (ntd::BN / 2), (unsigned)L.max_tiles);
       if (w16)
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, B, MOE_BM, GEPI, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, B, MOE_BM, EPI_ROT_SWIGLU, false, true>), grid,
+        hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, B, MOE_BM, GEPI, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
     } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.I + ntd::DEC_BN / 2 - 1) / (ntd::DEC_BN / 2), (unsigned)L.max_tiles64);
       if (d.H % 256 == 0 && dec16)  // whole-line weight copies on 256-wide steps
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 16, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, GEPI, true, 16, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else if (d.H % 256 == 0)
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI_ROT_SWIGLU, true, 64, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, GEPI, true, 64, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       else if (dec16)
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, EPI_ROT_SWIGLU, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, GEPI, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
                            st, p);
       else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, EPI_ROT_SWIGLU, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, GEPI, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
     }
   }
   {
@@ -735,13 +737,18 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
 }
 
 hipError_t launch_moe_fwd(const MoeDims& d, const float* logits, const MoeFwdPtrs& q, const MoeRoutingDev& rt,
-                          char* ws, const MoeWs& L, hipStream_t st) {
+                          char* ws, const MoeWs& L, hipStream_t st, bool base) {
   hipError_t err = launch_moe_route(d, logits, rt, ws, L, st);
   if (err != hipSuccess) return err;
   if (d.T == 0) return hipSuccess;
+  if (base)  // the frozen base alone: the block size plays no part
+    return d.wf == WF_FP4 ? moe_fwd_gemms<32, WF_FP4, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st)
+                          : moe_fwd_gemms<32, WF_INT4, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st);
   if (d.wf == WF_FP4)
-    return d.b == 32 ? moe_fwd_gemms<32, WF_FP4>(d, q, rt, ws, L, st) : moe_fwd_gemms<16, WF_FP4>(d, q, rt, ws, L, st);
-  return d.b == 32 ? moe_fwd_gemms<32, WF_INT4>(d, q, rt, ws, L, st) : moe_fwd_gemms<16, WF_INT4>(d, q, rt, ws, L, st);
+    return d.b == 32 ? moe_fwd_gemms<32, WF_FP4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st)
+                     : moe_fwd_gemms<16, WF_FP4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st);
+  return d.b == 32 ? moe_fwd_gemms<32, WF_INT4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st)
+                   : moe_fwd_gemms<16, WF_INT4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st);
 }
 
 template <int B, int W4F>

@@ -118,6 +118,28 @@ int32_t oft_moe_grouped_fwd(const oft_moe_desc* d, const uint16_t* x, const floa
                                         static_cast<hipStream_t>(stream)));
 }
 
+int32_t oft_moe_grouped_fwd_base(const oft_moe_desc* d, const uint16_t* x, const float* logits,
+                                 const uint8_t* wgu_codes, const uint16_t* wgu_scales, const uint8_t* wd_codes,
+                                 const uint16_t* wd_scales, const oft_moe_routing* rt, uint16_t* h_or_null,
+                                 uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  int32_t v = validate_moe(d);
+  if (v != OFT_OK) return v;
+  if ((v = routing_ok(rt)) != OFT_OK) return v;
+  if (!opt_ok(h_or_null)) return OFT_EINVAL;
+  if (d->T > 0) {
+    const void* req[] = {x, logits, wgu_codes, wd_codes, y};
+    for (const void* p : req)
+      if (!ptr_ok(p)) return OFT_EINVAL;
+    if (!scales_ok(d, wgu_scales) || !scales_ok(d, wd_scales)) return OFT_EINVAL;
+  }
+  const oft::MoeWs L = oft::moe_ws_layout(dims(d), OFT_PASS_FWD);
+  if (!ptr_ok(ws)) return OFT_EINVAL;
+  if (ws_bytes < L.bytes) return OFT_EWORKSPACE;
+  const oft::MoeFwdPtrs q{x, wgu_codes, wgu_scales, wd_codes, wd_scales, nullptr, h_or_null, y};
+  return hip_status(oft::launch_moe_fwd(dims(d), logits, q, routing_dev(rt), static_cast<char*>(ws), L,
+                                        static_cast<hipStream_t>(stream), true));
+}
+
 int32_t oft_moe_grouped_bwd(const oft_moe_desc* d, const uint16_t* dy, const oft_moe_routing* rt,
                             const uint16_t* h_saved, const uint8_t* wgu_codes,
                             const uint16_t* wgu_scales, const uint8_t* wd_codes,

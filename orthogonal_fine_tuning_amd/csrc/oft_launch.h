@@ -97,4 +97,8 @@ hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t
                              const uint8_t* wc, const void* ws, const float* Rf, const uint16_t* Rops,
                              void* dx, float* dq, char* work, hipStream_t st);
 
+// per-token log-probability difference of two policies' logits [T, V]
+hipError_t launch_logprob_diff(int T, int V, const float* a, const float* r, const int* labels, float* out,
+                               hipStream_t st);
+
 }  // namespace oft

@@ -63,8 +63,10 @@ struct MoeBwdPtrs {
 
 hipError_t launch_moe_route(const MoeDims& d, const float* logits, const MoeRoutingDev& rt, char* ws,
                             const MoeWs& L, hipStream_t st);
+// base: the frozen base alone (gate/up without the rotation; R_ops unused,
+// h_saved optional)
 hipError_t launch_moe_fwd(const MoeDims& d, const float* logits, const MoeFwdPtrs& q,
-                          const MoeRoutingDev& rt, char* ws, const MoeWs& L, hipStream_t st);
+                          const MoeRoutingDev& rt, char* ws, const MoeWs& L, hipStream_t st, bool base = false);
 hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutingDev& rt, char* ws,
                           const MoeWs& L, hipStream_t st);
 // d_logits [T, E] from dw [T, k] through the softmax and the top-k selection

@@ -293,3 +293,24 @@ def test_every_gpu_test_shape_passes_validation():
     for c in moe:
         d = oft.moe_desc(c.T, c.E, c.k, c.H, c.I, c.g, c.b, c.chunk, 0, w_fmt=wf[c.w_fmt])
         assert lib.oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == _lib.OFT_OK, c.name
+
+
+def test_logprob_diff_and_moe_base_validation():
+    lib = _lib.load()
+    ok = C.c_void_p(0x1000)
+    bad = C.c_void_p(0x1008)
+    assert lib.oft_logprob_diff(0, 10, None, None, None, None, None) == _lib.OFT_OK  # no-op
+    assert lib.oft_logprob_diff(-1, 10, ok, ok, ok, ok, None) == _lib.OFT_EINVAL
+    assert lib.oft_logprob_diff(4, 0, ok, ok, ok, ok, None) == _lib.OFT_EINVAL
+    assert lib.oft_logprob_diff(4, 10, ok, None, ok, ok, None) == _lib.OFT_EINVAL
+    assert lib.oft_logprob_diff(4, 10, ok, ok, bad, ok, None) == _lib.OFT_EINVAL
+    d = _moe()
+    rt = oft.moe_routing(*([type("T", (), {"data_ptr": lambda self: 0x1000})()] * 9))
+    args = (ok, ok, ok, ok, ok, ok, C.byref(rt), None, ok, ok, 1 << 30, None)
+    assert lib.oft_moe_grouped_fwd_base(C.byref(_moe(b=64)), *args) == _lib.OFT_EUNSUPPORTED
+    assert lib.oft_moe_grouped_fwd_base(C.byref(d), ok, ok, ok, ok, ok, ok, C.byref(rt), bad, ok, ok, 1 << 30,
+                                        None) == _lib.OFT_EINVAL  # misaligned optional h
+    assert lib.oft_moe_grouped_fwd_base(C.byref(d), ok, ok, ok, ok, ok, ok, C.byref(rt), None, None, ok, 1 << 30,
+                                        None) == _lib.OFT_EINVAL  # y required
+    assert lib.oft_moe_grouped_fwd_base(C.byref(d), ok, ok, ok, ok, ok, ok, C.byref(rt), None, ok, ok, 16,
+                                        None) == _lib.OFT_EWORKSPACE

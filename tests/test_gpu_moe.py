@@ -464,3 +464,64 @@ def test_moe_chunk_size_invariance(name):
     for c, r in runs.items():
         for kk in first:
             assert np.array_equal(r[kk], first[kk]), (c, kk)
+
+
+# ------------------------------------------------------------ reference policy
+def _run_moe_base(inp, with_h=True):
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = inp["cfg"]
+    T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=_wfmt(oft, cfg.w_fmt))
+    rtt = _routing_tensors(T, E, k)
+    rt = oft.moe_routing(**rtt)
+    W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
+    hs = torch.full((max(T * k, 1), 2 * I), -7, dtype=torch.int16, device="cuda") if with_h else None
+    y = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
+    nbf = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
+    wsf = torch.empty(nbf, dtype=torch.uint8, device="cuda")
+    oft.oft_moe_grouped_fwd_base(d, dev(inp["x"]), dev(inp["logits"]), W["wgu_codes"], W["wgu_scales"],
+                                 W["wd_codes"], W["wd_scales"], rt, hs, y, wsf, nbf)
+    torch.cuda.synchronize()
+    return {"rt": rtt, "hs": hs, "y": y}
+
+
+BASE_MOE = ["moe_small_b32", "moe_dense_g128", "moe_decode16_b32", "moe_dec64_g128", "moe_small_fp4",
+            "moe_decode16_i128", "moe_decode_fp4_h192"]
+
+
+@pytest.mark.parametrize("name", BASE_MOE)
+def test_moe_base_forward(name):
+    """The reference-policy MoE forward (frozen base, no rotation) against the
+    oracle's plain mixture, and bit-identical to the adapted forward with
+    Q = 0 (R exactly I), h included; without an h buffer y is unchanged."""
+    cfg = SMALL[name]
+    print(f"[moe base fwd] {name}", flush=True)
+    inp = make_moe(cfg, seed=6)
+    y_ref, Z_ref, rt = omoe.base_forward(inp)
+    out = _run_moe_base(inp)
+    P = cfg.T * cfg.k
+    e_y = err(bf16_to_f64(host(out["y"])), y_ref)
+    e_h = err(bf16_to_f64(host(out["hs"])[:P]), Z_ref)
+    print(f"  err y={e_y:.2e} h={e_h:.2e}", flush=True)
+    assert max(e_y, e_h) <= TOL
+    inp0 = dict(inp)
+    inp0["p"] = np.zeros_like(inp["p"])
+    adapted = _run_moe(inp0, want_bwd=False)
+    assert np.array_equal(host(adapted["y"]), host(out["y"]))
+    assert np.array_equal(host(adapted["hs"])[:P], host(out["hs"])[:P])
+    no_h = _run_moe_base(inp, with_h=False)
+    assert np.array_equal(host(no_h["y"]), host(out["y"]))
+
+
+def test_moe_base_forward_full_size_decode():
+    cfg = CONFIGS["moe_1t_decode"]
+    print("[moe base fwd] moe_1t_decode: generating inputs", flush=True)
+    inp = make_moe(cfg, seed=0)
+    out = _run_moe_base(inp, with_h=False)
+    print("[moe base fwd] moe_1t_decode: oracle", flush=True)
+    y_ref, _, _ = omoe.base_forward(inp)
+    e_y = err(bf16_to_f64(host(out["y"])), y_ref)
+    print(f"  err y={e_y:.2e}", flush=True)
+    assert e_y <= TOL

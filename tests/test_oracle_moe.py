@@ -190,3 +190,22 @@ def test_router_backward_rows_sum_to_zero(renorm):
         mask = np.ones_like(g, dtype=bool)
         mask[np.arange(g.shape[0])[:, None], idx] = False
         assert np.all(g[mask] == 0.0)
+
+
+def test_base_forward_is_the_q_zero_layer_and_differs_otherwise():
+    """The reference-policy layer (frozen base, no rotation) equals the
+    adapted layer at Q = 0 (R = I exactly) and differs once Q moves; its
+    saved gate/up output is the un-rotated Z."""
+    cfg = MoEConfig("base", T=48, E=6, k=2, H=64, I=32, g=32, chunk=2, b=8, q_std=0.2)
+    inp = make_moe(cfg, seed=4)
+    yb, Zb, rt = moe.base_forward(inp)
+    inp0 = dict(inp)
+    inp0["p"] = np.zeros_like(inp["p"])
+    y0, H0, _ = moe.forward(inp0)
+    assert np.array_equal(yb, y0)
+    assert np.array_equal(Zb, H0)
+    y1, H1, _ = moe.forward(inp)
+    assert np.abs(y1 - yb).max() > 1e-3 * np.abs(yb).max()
+    # brute force over every expert, gate weights w or 0 (R = I: no rotation)
+    ybf = moe.bruteforce_forward(inp0, rt["idx"], rt["w"])
+    assert np.abs(yb - ybf).max() <= 1e-12 * np.abs(yb).max()
