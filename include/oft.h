@@ -267,6 +267,23 @@ int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void*
                        const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* oft_linear_bwd without a workspace, for callers that cannot allocate
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments and results as oft_linear_bwd; its scratch is a
+ * fixed device array of OFT_NOALLOC_SCRATCH_BYTES inside the library, held
+ * by every GPU the library runs on until the process ends (looked up once
+ * per device, on the first call there).  It allocates nothing and
+ * synchronises nothing.  Calls that overlap on one GPU (different streams,
+ * parallel graph branches) share the array and race: order them.  Errors:
+ * as oft_linear_bwd, and OFT_EWORKSPACE when the layer's backward needs
+ * more scratch than the array holds (oft_linear_workspace_bytes(d,
+ * OFT_PASS_BWD) > OFT_NOALLOC_SCRATCH_BYTES: e.g. the 4096-token fused QKV
+ * layer of a 4B model fits, the 8192-token gate/up layer does not). */
+#define OFT_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int32_t oft_linear_bwd_noalloc(const oft_linear_desc* d, const uint16_t* dy, const void* y_saved,
+                               const uint8_t* w_codes, const void* w_scales, const float* R_f32,
+                               const uint16_t* R_ops, void* dx_or_null, float* dq_or_null, void* stream);
+
 /* ---- reference-policy log-probabilities ------------------------------------
  * The KL regulariser of the pages compares the trained policy with the
  * frozen base run without the adapter (the chooseai.io page's "Five design

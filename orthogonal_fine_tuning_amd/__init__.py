@@ -15,7 +15,7 @@ from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF
 
 __all__ = [
     "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
-    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd", "oft_logprob_diff",
+    "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd", "oft_linear_bwd_noalloc", "oft_logprob_diff",
     "oft_slots_switch", "oft_linear_fwd_slots",
     "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_fwd_base", "oft_moe_grouped_bwd", "abi_version",
     "prof_enable", "prof_records",
@@ -136,6 +136,13 @@ def oft_linear_bwd(desc, dy, y_saved, w_codes, w_scales, R_f32, R_ops, dx=None, 
                                           _ptr(w_scales), _ptr(R_f32), _ptr(R_ops), _ptr(dx),
                                           _ptr(dq), _ptr(ws), ws_bytes, _stream(stream)),
                "oft_linear_bwd")
+
+
+def oft_linear_bwd_noalloc(desc, dy, y_saved, w_codes, w_scales, R_f32, R_ops, dx=None, dq=None, stream=None):
+    _lib.check(_lib.load().oft_linear_bwd_noalloc(C.byref(desc), _ptr(dy), _ptr(y_saved), _ptr(w_codes),
+                                                  _ptr(w_scales), _ptr(R_f32), _ptr(R_ops), _ptr(dx), _ptr(dq),
+                                                  _stream(stream)),
+               "oft_linear_bwd_noalloc")
 
 
 def oft_logprob_diff(logits_actor, logits_ref, labels, out, stream=None):

@@ -17,6 +17,7 @@ OFT_DT_BF16, OFT_DT_F32 = 0, 1
 OFT_W_INT4, OFT_W_FP8_E4M3, OFT_W_BF16, OFT_W_FP4_E2M1 = 0, 1, 2, 3
 OFT_PASS_FWD, OFT_PASS_BWD = 0, 1
 OFT_MAX_SEGMENTS = 8
+OFT_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class oft_linear_desc(C.Structure):
@@ -60,6 +61,7 @@ SIGNATURES = {
     "oft_moe_router_bwd": (_I, [C.POINTER(oft_moe_desc), _P, _P, _P, _P, _P]),
     "oft_linear_bwd": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                             _P]),
+    "oft_linear_bwd_noalloc": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "oft_logprob_diff": (_I, [_I, _I, _P, _P, _P, _P, _P]),
     "oft_moe_workspace_bytes": (_I, [C.POINTER(oft_moe_desc), _I, C.POINTER(_SZ)]),
     "oft_moe_route": (_I, [C.POINTER(oft_moe_desc), _P, C.POINTER(oft_moe_routing), _P, _SZ, _P]),

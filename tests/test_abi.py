@@ -314,3 +314,17 @@ def test_logprob_diff_and_moe_base_validation():
                                         None) == _lib.OFT_EINVAL  # y required
     assert lib.oft_moe_grouped_fwd_base(C.byref(d), ok, ok, ok, ok, ok, ok, C.byref(rt), None, ok, ok, 16,
                                         None) == _lib.OFT_EWORKSPACE
+
+
+def test_noalloc_bwd_rejects_beyond_its_scratch_without_a_gpu():
+    """The fixed-scratch backward refuses, before touching the device, a
+    layer whose backward needs more than its array holds."""
+    lib = _lib.load()
+    ok = C.c_void_p(0x1000)
+    big = _desc(M=8192, K=2560, segs=(9728, 9728), b=32, x_dtype=oft.OFT_DT_BF16, g=128)
+    n = C.c_size_t(0)
+    assert lib.oft_linear_workspace_bytes(C.byref(big), 1, C.byref(n)) == _lib.OFT_OK
+    assert n.value > _lib.OFT_NOALLOC_SCRATCH_BYTES
+    assert lib.oft_linear_bwd_noalloc(C.byref(big), ok, ok, ok, ok, ok, ok, ok, ok, None) == _lib.OFT_EWORKSPACE
+    assert lib.oft_linear_bwd_noalloc(C.byref(_desc(b=8)), ok, ok, ok, ok, ok, ok, ok, ok, None) == \
+        _lib.OFT_EUNSUPPORTED
