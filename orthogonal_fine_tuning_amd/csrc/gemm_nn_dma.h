@@ -155,10 +155,14 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
     s_dst = (uint32_t)(4 * ((wave * 64) % (64 * dpr)));
   }
 
+  // B copies of this wave that hold a row of the tile (the rest would only
+  // copy rows past its end, whose products are never stored: skipped)
+  const int vb = (16 * wave < nrows ? 1 : 0) + (16 * wave + 8 < nrows ? 1 : 0);
   auto issue_b = [&](int s) {
     const uint32_t dst = b_lds + (uint32_t)((s % NST) * B_BYTES);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if (i >= vb) break;
       if constexpr (GROUPED)
         copy16v(dst + i * 1024, bptr[i] + (size_t)s * BNS * 2);
       else
@@ -257,8 +261,10 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
     }
   };
 
-  // copies issued per wave and step: B 2, weights 4 (bf16) or 2 (codes + scales)
-  constexpr int VB = 2, VW = W16 ? 4 : 2;
+  // copies issued per wave and step: B vb (0 .. 2), weights 4 (bf16) or 2
+  // (codes + scales)
+  const int VB = vb;
+  constexpr int VW = W16 ? 4 : 2;
   auto run = [&](auto tmv_c) {
     if constexpr (W16) {
       issue_w(0);

@@ -219,6 +219,14 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
     }
   }
   const uint32_t x_lds = lds_addr(xs) + (uint32_t)((BM / 8) * wave * XROW);
+  // activation copies of this wave that hold a row of the tile (a prefix of
+  // the XI; the rest would only copy rows past the tile's end, whose
+  // products are never stored: skipped, and the wave's copy count per step
+  // drops accordingly)
+  int xc = 0;
+#pragma unroll
+  for (int i = 0; i < XI; ++i) xc += (BM / 8) * wave + (KB == 128 ? 4 : 8) * i < nrows ? 1 : 0;
+  const int vw = xc + WI;  // copies per step of this wave
 
   // weights: per-lane 32-bit offsets from the row of channel cbase
   const uint8_t* wbase = wc + (W16 ? (size_t)cbase * K * 2 : FP8 ? (size_t)cbase * K : (size_t)cbase * (K / 2));
@@ -255,6 +263,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   auto copy_one = [&](int s, int c) {
     const int st = s % NSTK;
     if (c < XI) {
+      if (c >= xc) return;
       if constexpr (GROUPED)
         copy16v(x_lds + st * XB + c * 1024, xptr[c] + (size_t)s * XROW);
       else
@@ -393,14 +402,14 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
     }
   };
 
-  // every wave runs the same copies and barriers, whatever its TMV
+  // every wave takes the same barriers, whatever its TMV
   auto run = [&](auto tmv_c) {
     issue(0);
     if (LA > 1 && nk > 1) issue(1);
     for (int s = 0; s < nk; ++s) {
       // copies of steps s + 1 .. s + LA - 1 may stay in flight
       if constexpr (LA > 1) {
-        if (s + 1 < nk) wait_copies_barrier<V>(); else wait_copies_barrier<0>();
+        wait_copies_barrier_n(s + 1 < nk ? vw : 0);
       } else {
         wait_copies_barrier<0>();
       }
