@@ -24,6 +24,7 @@
 
 #include "gemm_nn.h"
 #include "gemm_nn_dma.h"
+#include "gemm_nn_q4.h"
 #include "gemm_nt.h"
 #include "gemm_nt_dma.h"
 #include "oft_moe.h"
@@ -795,7 +796,14 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     // experts averaging at least 64 rows: the copy-ring NN kernel (faster
     // there; with fewer rows the two-workgroups-per-CU kernel is)
     int nkt;  // column tiles = partial sums of dw per position
-    if ((long)d.T * d.k >= 64L * d.E) {
+    if (W4F == WF_INT4 && !w16 && d.I % nnq::BKO == 0) {
+      // INT4: codes and scales to LDS by copies, transposed 4-bit operand
+      // reads, every code dequantised by one wave
+      ProfScope prof(st, "moe.dA");
+      dim3 grid(d.I / nnq::BKO, (unsigned)L.max_tiles);
+      hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_SWIGLU_BWD, true>), grid, dim3(nnq::NTHR), 0, st, p);
+      nkt = d.I / nnq::BKO;
+    } else if ((long)d.T * d.k >= 64L * d.E) {
       ProfScope prof(st, "moe.dA");
       dim3 grid((d.I + nnd::BKO - 1) / nnd::BKO, (unsigned)L.max_tiles);
       if (w16)
@@ -849,13 +857,18 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.offsets = rt.offsets;
     p.perm = rt.perm;
     p.kslots = 0;
-    dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
-    if (w16)
-      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
-                         dim3(256), 0, st, p);
-    else
-      hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, W4F, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
-                         dim3(256), 0, st, p);
+    if (W4F == WF_INT4 && !w16 && d.H % nnq::BKO == 0) {
+      dim3 grid(d.H / nnq::BKO, (unsigned)L.max_tiles);
+      hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_STORE, true>), grid, dim3(nnq::NTHR), 0, st, p);
+    } else {
+      dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
+      if (w16)
+        hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
+                           dim3(256), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, W4F, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
+                           dim3(256), 0, st, p);
+    }
     }
     const size_t n8 = (size_t)d.T * d.H / 8;
     ProfScope prof(st, "moe.unpermute");

@@ -260,9 +260,12 @@ def test_moe_parity_small(name):
 def test_moe_bf16_weights_small(name):
     """Dequantised bf16 weights (the dense reference the grouped dequant GEMMs
     are measured against) through the same entry points: the oracle's result;
-    where both formats run the 128-row copy-ring kernels (at least 64 rows per
-    expert on average) the contraction order is the same, so every output
-    equals the INT4 run's bit for bit."""
+    where both formats run the same 128-row copy-ring kernels (at least 64
+    rows per expert on average) the contraction order is the same, so those
+    outputs equal the INT4 run's bit for bit: the forward's always, the
+    backward's where INT4 does not take the 4-bit transpose-load NN kernel
+    (dA when I % 256 == 0, and everything behind dH: dQ, dw, dX; dX alone
+    when H % 256 == 0)."""
     cfg = SMALL[name]
     print(f"[moe bf16 weights] {name}", flush=True)
     inp = make_moe(cfg, seed=3)
@@ -279,7 +282,13 @@ def test_moe_bf16_weights_small(name):
     assert max(e_y, e_h, e_dx, e_dq, e_dw) <= TOL
     if P >= 64 * cfg.E:
         ref = _run_moe(inp)
-        for key in ("y", "hs", "dx", "dq", "dw"):
+        q4 = cfg.w_fmt == "int4"
+        same = ["y", "hs"]
+        if not (q4 and cfg.I % 256 == 0):  # dA (and dH behind dQ, dw and dX) on the same kernels
+            same += ["dq", "dw"]
+            if not (q4 and cfg.H % 256 == 0):
+                same.append("dx")
+        for key in same:
             assert np.array_equal(host(out[key]), host(ref[key])), key
 
 
