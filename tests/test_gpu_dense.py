@@ -65,6 +65,12 @@ SMALL = {
                                   w_fmt="fp4", g=32),
     "fp4_decode_k576_b16": DenseConfig("fp4_decode_k576_b16", M=20, K=576, segs=(96, 64), b=16,
                                        x_dtype="bf16", w_fmt="fp4", g=64),
+    # INT4, bf16 x, many tokens, K % 256 == 0: dX reads the codes through
+    # 4-bit transpose loads (ragged row tile, g = 32 and g = 128)
+    "int4_q4_dx_g32": DenseConfig("int4_q4_dx_g32", M=300, K=512, segs=(256, 192), b=32, x_dtype="bf16",
+                                  w_fmt="int4", g=32),
+    "int4_q4_dx_g128_b16": DenseConfig("int4_q4_dx_g128_b16", M=200, K=768, segs=(320, 128), b=16, x_dtype="bf16",
+                                       w_fmt="int4", g=128, q_std=0.05),
     # the most segments the ABI takes (8), of unequal sizes, each rotated
     # with its own blocks: copy-ring forward and transposed-weight dX (FP8),
     # and INT4 with b = 16 (gemm_nn dX)
