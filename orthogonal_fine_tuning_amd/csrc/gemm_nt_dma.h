@@ -587,26 +587,32 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
 // up outputs to the gate waves through LDS.  smem: SMEM bytes, free once
 // every wave has passed the first barrier.  nb: first channel of the wave's
 // 32 (-1 past the layer).
-template <bool FP8, int B, int EPI, int TM, int SMEM>
+template <bool FP8, int B, int EPI, int TM, int SMEM, int KP = 2>
 __device__ __forceinline__ void dec_finish(const NtArgs& p, f32x16 (&acc)[TM], uint8_t* smem, int wn, int kh,
                                            int lane, int nb, int nrows, int pos0, const uint16_t* rops) {
   using namespace ntd;
   constexpr bool SWI = epi_swiglu(EPI);
+  static_assert(KP == 2 || (KP == 4 && !SWI), "k parts");
+  static_assert((KP - 1) * 4 * TM * 16 * 64 * 4 <= SMEM, "partial-sum area");
   const int l32 = lane & 31, g2 = lane >> 5;
+  // kh: this wave's part of the in-features of a step (0 .. KP - 1); parts
+  // 1 .. KP - 1 hand their sums to part 0, which adds them in part order
   lds_barrier_plain();
   float* red = reinterpret_cast<float*>(smem);
-  if (kh == 1) {
+  if (kh > 0) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[((wn * TM + tm) * 16 + r) * 64 + lane] = acc[tm][r];
+      for (int r = 0; r < 16; ++r) red[((((kh - 1) * 4 + wn) * TM + tm) * 16 + r) * 64 + lane] = acc[tm][r];
   }
   lds_barrier_plain();
   if (kh == 0) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int j = 0; j < KP - 1; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tm][r] += red[((wn * TM + tm) * 16 + r) * 64 + lane];
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tm][r] += red[(((j * 4 + wn) * TM + tm) * 16 + r) * 64 + lane];
   }
 
   // epilogue (kh = 0 waves): FP8 channel scale, bf16, rotation (EPI_ROT*), store
@@ -1072,6 +1078,12 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
 
   const int rw = 32 * wn + l32;  // this lane's operand row
   const int wsw = (rw >> 1) & 7;
+  // activation chunk offsets of this lane (step-invariant): row xr, chunk
+  // 16 kh + 8 g2 + kk; the second 32-row tile sits 32 rows (16 KB) further
+  const int xr0 = BMD == 64 ? l32 : (l32 & 15);
+  uint32_t xo[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) xo[kk] = (uint32_t)(xr0 * 512 + 16 * ((16 * kh + 8 * g2 + kk) ^ (xr0 & 15)));
   f32x16 acc[TM];
 #pragma unroll
   for (int b = 0; b < TM; ++b)
@@ -1086,27 +1098,28 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
     const int c0 = 4 * kh + 2 * g2;  // this lane's two 16-byte chunks: in-features 32 c0 .. 32 c0 + 63
     const uint4 v0 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * (c0 ^ wsw));
     const uint4 v1 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * ((c0 + 1) ^ wsw));
+    uint32_t sw;
+    if (p.g == 32)
+      sw = *reinterpret_cast<const uint32_t*>(S + rw * 16 + 2 * c0);
+    else
+      sw = *reinterpret_cast<const uint16_t*>(S + rw * sg + 2 * (p.g == 64 ? c0 / 2 : kh));
+    // every activation operand of the step is read before the first
+    // dequantisation, so the LDS latency is paid once per step
+    bf16x8 xb[8][TMV];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int tm = 0; tm < TMV; ++tm) xb[kk][tm] = *reinterpret_cast<const bf16x8*>(X + xo[kk] + 16384 * tm);
+    __builtin_amdgcn_sched_barrier(0);
     const uint32_t cw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     typename W4<WF>::S sc[2];
-    if (p.g == 32) {
-      const uint32_t word = *reinterpret_cast<const uint32_t*>(S + rw * 16 + 2 * c0);
-      sc[0] = W4<WF>::scale((uint16_t)word);
-      sc[1] = W4<WF>::scale((uint16_t)(word >> 16));
-    } else {
-      const int gi = p.g == 64 ? c0 / 2 : kh;
-      sc[0] = W4<WF>::scale(*reinterpret_cast<const uint16_t*>(S + rw * sg + 2 * gi));
-      sc[1] = sc[0];
-    }
+    sc[0] = W4<WF>::scale((uint16_t)sw);
+    sc[1] = p.g == 32 ? W4<WF>::scale((uint16_t)(sw >> 16)) : sc[0];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const bf16x8 a = as_bf16x8(W4<WF>::dq(cw[kk], sc[kk >> 2]));
 #pragma unroll
-      for (int tm = 0; tm < TMV; ++tm) {
-        const int xr = BMD == 64 ? 32 * tm + l32 : (l32 & 15);
-        const bf16x8 b =
-            *reinterpret_cast<const bf16x8*>(X + xr * 512 + 16 * ((16 * kh + 8 * g2 + kk) ^ (xr & 15)));
-        acc[tm] = mfma32(a, b, acc[tm]);
-      }
+      for (int tm = 0; tm < TMV; ++tm) acc[tm] = mfma32(a, xb[kk][tm], acc[tm]);
     }
   };
 
@@ -1127,6 +1140,154 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
     run(std::integral_constant<int, 1>{});
 
   dec_finish<false, B, EPI, TM, NST * SB>(p, acc, smem, wn, kh, lane, chan(32 * wn), nrows, pos0, rops);
+}
+
+
+// Dense decode (M <= 64 tokens, 4-bit weights, K % 256 == 0): the same
+// stage layout, copies and channel tile (128) as gemm_nt_dec4_kernel, with
+// sixteen waves per workgroup, four per SIMD: wave (wn, kq) = (wave % 4,
+// wave / 4) multiplies channels 32 wn + [0, 32) with in-features
+// [64 kq, 64 kq + 64) of every 256-wide step (one 16-byte chunk of codes per
+// lane, four matrix steps), so each SIMD has four independent instruction
+// streams to overlap dequantisation, matrix work and LDS reads, and the
+// four parts' sums are added in part order at the end (dec_finish).  Every
+// wave issues the same copies each step (one weight, two activation, and
+// for the first two or four waves one scale copy), so the waits are
+// compile-time counts.
+template <int B, int EPI, int WF = WF_INT4>
+__global__ __launch_bounds__(1024, 1) void gemm_nt_dec16_kernel(NtArgs p) {
+  static_assert(wf_4bit(WF), "4-bit weights");
+  static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_BASE, "epilogue");
+  using namespace ntd;
+  constexpr int NST = 3, BMD = 64, TM = 2;
+  constexpr int WBY = 128 * 128, SBY = 128 * 16, XBY = BMD * 512, SB = WBY + SBY + XBY;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NST * SB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, kq = wave >> 2;
+  const int l32 = lane & 31, g2 = lane >> 5;
+  const int K = p.K;
+  const int nrows = min(BMD, p.M);
+  const uint8_t* wc = p.wc;
+  const uint16_t* ws_h = static_cast<const uint16_t*>(p.ws);
+  const uint16_t* rops = nt_rops(p);
+  const int cbase = blockIdx.x * DEC_BN;
+  auto chan = [&](int rw) -> int { return cbase + rw < p.N ? cbase + rw : -1; };
+  auto crow = [&](int rw) { const int c = chan(rw); return c >= 0 ? c - cbase : 0; };
+  const int nks = K / 256;
+  const int kg = K / p.g;
+  const int sg = 512 / p.g;  // scale bytes per row and step: 16, 8 or 4
+  const int nsw = p.g == 64 ? 4 : 2;
+
+  // copies of wave w per step: weight rows 8 w + lane / 8, chunk lane % 8
+  // (one instruction); activation rows 4 w + 2 i + lane / 32 (i = 0, 1),
+  // chunk lane % 32; scales as in gemm_nt_dec4_kernel (waves w < nsw)
+  const uint8_t* wbase = wc + (size_t)cbase * (K / 2);
+  uint32_t woff;
+  {
+    const int rw = 8 * wave + (lane >> 3);
+    woff = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 7) ^ ((rw >> 1) & 7)));
+  }
+  uint32_t soff = 0;
+  {
+    const int j = 64 * (wave < nsw ? wave : 0) + lane;
+    const int row = p.g == 64 ? (j >> 1) : j;
+    const int sub = p.g == 64 ? 4 * (j & 1) : 0;
+    soff = (uint32_t)((cbase + crow(row & 127)) * kg * 2 + sub);
+  }
+  uint32_t xoff[2];
+  const uint8_t* xbase = static_cast<const uint8_t*>(p.a);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * wave + 2 * i + (lane >> 5);
+    const int rr = r < nrows ? r : 0;
+    xoff[i] = (uint32_t)(rr * p.lda * 2 + 16 * ((lane & 31) ^ (r & 15)));
+  }
+  const uint32_t base_lds = lds_addr(smem);
+  const uint32_t w_lds = base_lds + (uint32_t)(1024 * wave);
+  const uint32_t s_lds = base_lds + (uint32_t)(WBY + (p.g == 64 ? 4 * 64 * wave : (p.g == 32 ? 16 : 4) * 64 * wave));
+  const uint32_t x_lds = base_lds + (uint32_t)(WBY + SBY + 2048 * wave);
+
+  auto issue = [&](int s, auto sc_c) {
+    constexpr bool SC = decltype(sc_c)::value;
+    const uint32_t so = (uint32_t)((s % NST) * SB);
+    copy16(w_lds + so, wbase + (size_t)s * 128, woff);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) copy16(x_lds + so + 1024 * i, xbase + (size_t)s * 512, xoff[i]);
+    if constexpr (SC) {
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(ws_h) + (size_t)s * sg;
+      if (p.g == 32)
+        copy16(s_lds + so, sb, soff);
+      else
+        copy4(s_lds + so, sb, soff);
+    }
+  };
+
+  const int rw = 32 * wn + l32;  // this lane's operand row
+  const int cq = 2 * kq + g2;    // this lane's 16-byte code chunk of the step: in-features 32 cq .. 32 cq + 31
+  const uint32_t w_rd = (uint32_t)(rw * 128 + 16 * (cq ^ ((rw >> 1) & 7)));
+  const uint32_t s_rd = (uint32_t)(WBY + (p.g == 32 ? rw * 16 + 2 * cq : rw * sg + 2 * (p.g == 64 ? kq : kq >> 1)));
+  uint32_t xo[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) xo[kk] = (uint32_t)(WBY + SBY + l32 * 512 + 16 * ((4 * cq + kk) ^ (l32 & 15)));
+  f32x16 acc[TM];
+#pragma unroll
+  for (int b = 0; b < TM; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
+
+  auto compute = [&](int s, auto tmv_c) {
+    constexpr int TMV = decltype(tmv_c)::value;
+    const uint8_t* St = smem + (s % NST) * SB;
+    const uint4 cw4 = *reinterpret_cast<const uint4*>(St + w_rd);
+    const uint16_t sbits = *reinterpret_cast<const uint16_t*>(St + s_rd);
+    // every activation operand of the step is read before the first
+    // dequantisation, so the LDS latency is paid once per step
+    bf16x8 xb[4][TMV];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int tm = 0; tm < TMV; ++tm) xb[kk][tm] = *reinterpret_cast<const bf16x8*>(St + xo[kk] + 16384 * tm);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t cw[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
+    const typename W4<WF>::S sc = W4<WF>::scale(sbits);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 a = as_bf16x8(W4<WF>::dq(cw[kk], sc));
+#pragma unroll
+      for (int tm = 0; tm < TMV; ++tm) acc[tm] = mfma32(a, xb[kk][tm], acc[tm]);
+    }
+  };
+
+  auto run = [&](auto tmv_c, auto sc_c) {
+    constexpr int PER = 3 + (decltype(sc_c)::value ? 1 : 0);  // copies per step of this wave
+    const int pre = nks < NST - 1 ? nks : NST - 1;
+    for (int s = 0; s < pre; ++s) issue(s, sc_c);
+    for (int s = 0; s < nks; ++s) {
+      // the copies of step s + 1 may stay in flight
+      if (s + 1 < nks)
+        wait_copies_barrier_n(PER);
+      else
+        wait_copies_barrier_n(0);
+      if (s + NST - 1 < nks) issue(s + NST - 1, sc_c);
+      compute(s, tmv_c);
+    }
+  };
+  if (nrows > 32) {
+    if (wave < nsw)
+      run(std::integral_constant<int, TM>{}, std::true_type{});
+    else
+      run(std::integral_constant<int, TM>{}, std::false_type{});
+  } else {
+    if (wave < nsw)
+      run(std::integral_constant<int, 1>{}, std::true_type{});
+    else
+      run(std::integral_constant<int, 1>{}, std::false_type{});
+  }
+
+  dec_finish<false, B, EPI, TM, NST * SB, 4>(p, acc, smem, wn, kq, lane, chan(32 * wn), nrows, 0, rops);
 }
 
 }  // namespace oft

@@ -46,9 +46,8 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       p.N = a.N;
       p.g = a.g;
       const dim3 grid((a.N + ntd::DEC_BN - 1) / ntd::DEC_BN, 1);
-      if (!FP8 && a.K % 256 == 0)  // 4-bit: whole-line weight copies on 256-wide steps
-        hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, EPI, false, 64, FP8 ? WF_INT4 : WF>), grid, dim3(ntd::DEC_NTHR),
-                           0, st, p);
+      if (!FP8 && a.K % 256 == 0)  // 4-bit: whole-line weight copies on 256-wide steps, 16 waves
+        hipLaunchKernelGGL((gemm_nt_dec16_kernel<B, EPI, FP8 ? WF_INT4 : WF>), grid, dim3(1024), 0, st, p);
       else
         hipLaunchKernelGGL((gemm_nt_dec_kernel<WF, B, EPI>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
       return hipGetLastError();

@@ -45,32 +45,41 @@ __device__ __forceinline__ float fp16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// INT4 group scale in the two forms the dequantisation uses: the fp16 value
-// itself and -1032 s in fp32 (exact: 11 x 8 significant bits).
+// INT4 group scale in the forms the dequantisation uses (all exact in
+// fp32: s has 11 significant bits, 1032 = 129 x 8 and 72 = 9 x 8): s and
+// -1032 s for nibbles that sit in the low mantissa bits of an fp16, s / 16
+// and -72 s for nibbles that sit four bits higher.
 struct I4Scale {
-  _Float16 s;
-  float m;
+  float s, m, s16, m16;
 };
 __device__ __forceinline__ I4Scale i4scale(uint16_t bits) {
-  const _Float16 s = __builtin_bit_cast(_Float16, bits);
-  return I4Scale{s, -1032.0f * (float)s};
+  const float s = (float)__builtin_bit_cast(_Float16, bits);
+  return I4Scale{s, -1032.0f * s, 0.0625f * s, -72.0f * s};
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // 8 INT4 nibbles (low nibble first, two's complement) times one scale -> 8
-// bf16 (as uint4), each bf16(q s) rounded once to nearest even.  Nibble n
-// becomes the fp16 value 1024 + (n ^ 8) (exponent 10, so the nibble lands in
-// the low mantissa bits: one AND/XOR per two nibbles), and one mixed
-// fp16 x fp16 + fp32 FMA gives (1024 + (n ^ 8)) s - 1032 s = q s exactly.
+// bf16 (as uint4), each bf16(q s) rounded once to nearest even.  A nibble n
+// is moved into the mantissa of an fp16 whose exponent is 10 (value 1024 +
+// mantissa) with its top bit flipped (n ^ 8 = q + 8), by one AND/XOR per two
+// nibbles: nibbles 0 and 4 (bits 0-3 of each half) give 1024 + (q + 8),
+// nibbles 1 and 5 (bits 4-7) give 1024 + 16 (q + 8) in place, and one shift
+// by 8 bits brings nibbles 2, 6, 3 and 7 to the same positions.  A mixed
+// fp16 x fp32 + fp32 FMA then yields (1024 + (q + 8)) s - 1032 s or
+// (1024 + 16 (q + 8)) s / 16 - 72 s, both q s exactly (at most 15
+// significant bits), rounded once to bf16 by the pack.
 __device__ __forceinline__ uint4 dq_int4x8(uint32_t w, I4Scale sc) {
-  const float s = (float)sc.s;
+  const uint32_t v[2] = {w, w >> 8};
   float f[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * j)) & 0x000F000Fu) ^ 0x64086408u);
-    f[j] = __builtin_fmaf((float)h[0], s, sc.m);      // nibble j
-    f[j + 4] = __builtin_fmaf((float)h[1], s, sc.m);  // nibble j + 4
+  for (int j = 0; j < 2; ++j) {
+    const f16x2 lo = __builtin_bit_cast(f16x2, (v[j] & 0x000F000Fu) ^ 0x64086408u);  // nibbles 2j, 2j + 4
+    const f16x2 hi = __builtin_bit_cast(f16x2, (v[j] & 0x00F000F0u) ^ 0x64806480u);  // nibbles 2j + 1, 2j + 5
+    f[2 * j] = __builtin_fmaf((float)lo[0], sc.s, sc.m);
+    f[2 * j + 4] = __builtin_fmaf((float)lo[1], sc.s, sc.m);
+    f[2 * j + 1] = __builtin_fmaf((float)hi[0], sc.s16, sc.m16);
+    f[2 * j + 5] = __builtin_fmaf((float)hi[1], sc.s16, sc.m16);
   }
   uint4 r;
   r.x = pack_bf16x2(f[0], f[1]);
