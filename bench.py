@@ -47,9 +47,11 @@ Per workload:
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -88,6 +90,9 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (a reference "
                          "for HBM byte counters)")
+    ap.add_argument("--pmc-summary", metavar="DIR", default=None,
+                    help="no GPU work: summarise the rocprofv3 runs under DIR/<workload>/<pass> (see "
+                         "pmc_summary) into profiles/")
     return ap.parse_args()
 
 
@@ -641,6 +646,219 @@ def moe_dense_reference(cfg, inp, args, bufs, t_ours):
             "note": "fwd+bwd time of the 4-bit path over that of the same kernels on bf16 weights"}
 
 
+# ------------------------------------------------------------------ counter summaries
+PMC_PASSES = {
+    # one rocprofv3 --pmc run each (at most 8 SQ and 4 TCC counters per run)
+    "sq": "GRBM_GUI_ACTIVE SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+          "SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU SQ_INSTS_MFMA",
+    "wait": "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS "
+            "SQ_INSTS_LDS SQ_INSTS_SALU",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+PMC_BENCH = ("python3 bench.py --config {w} --steps 2 --warmup 1 --prof-steps 1 --no-cold --no-extras "
+             "--no-dense-ref --no-cpu-baseline --calibrate-copy-mib {mib}")
+TRACE_BENCH = ("python3 bench.py --config {w} --steps 5 --warmup 1 --prof-steps 1 --no-cold --no-extras "
+               "--no-dense-ref --no-cpu-baseline")
+CLOCK_GHZ = 2.4  # nominal shader clock for the VALU-busy estimate
+
+
+def kernel_region(name):
+    """The library step (bench.py kernel-table name) a kernel belongs to, from
+    its name and template arguments; None for kernels outside the library."""
+    base = re.sub(r"^(void )?oft::(\(anonymous namespace\)::)?", "", name)
+    fam, _, targs = base.partition("<")
+    a = [t.strip() for t in targs.rstrip(">").split(",")] if targs else []
+    nt = {"gemm_nt_dma_kernel": (3, 5), "gemm_nt_dec4_kernel": (1, 2), "gemm_nt_dec_kernel": (2, 3),
+          "gemm_nt_kernel": (4, 5), "gemm_nt_dec16_kernel": (1, None), "gemm_nt_skinny_kernel": (5, None)}
+    nn = {"gemm_nn_kernel": (5, 6), "gemm_nn_dma_kernel": (1, 2), "gemm_nn_q4_kernel": (0, 1)}
+    if fam in nt:
+        ie, ig = nt[fam]
+        epi = int(a[ie]) if len(a) > ie else 0
+        grouped = ig is not None and len(a) > ig and a[ig] == "true"
+        if grouped:
+            return "moe.down" if epi == 1 else "moe.gateup"
+        return {0: "dense.fwd", 1: "dense.dx", 3: "dense.fwd_base"}.get(epi, "dense.fwd")
+    if fam in nn:
+        ie, ig = nn[fam]
+        epi = int(a[ie]) if len(a) > ie else 0
+        grouped = len(a) > ig and a[ig] == "true"
+        if grouped:
+            return "moe.dA" if epi == 1 else "moe.dX"
+        return "dense.dx"
+    for pre, reg in (("dq_dma", "dense.dq"), ("dq_partial", "dense.dq"), ("dq_final", "dense.dq_final"),
+                     ("split_reduce", "dense.dx_reduce"), ("transpose_", "dense.transpose"), ("cayley", "cayley"),
+                     ("slots_latch", "dense.slots_latch"), ("moe_dq", "moe.dq"), ("moe_combine", "moe.combine"),
+                     ("moe_unpermute", "moe.unpermute"), ("moe_worklist", "moe.worklist"),
+                     ("moe_dw_reduce", "moe.dw_reduce"), ("moe_router_bwd", "moe.router_bwd"),
+                     ("moe_", "moe.route"), ("logprob", "policy.logprob_diff")):
+        if fam.startswith(pre):
+            return reg
+    return None
+
+
+def _read_dispatches(path):
+    """rocprofv3 counter CSV -> [{name, dur_us, counter: value}] in dispatch order."""
+    disp = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(r["Dispatch_Id"], {"name": re.sub(r"\((?!anonymous).*$", "", r["Kernel_Name"])})
+            d["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [disp[k] for k in sorted(disp, key=int)]
+
+
+def _mean_by_kernel(dispatches):
+    acc = {}
+    for d in dispatches:
+        e = acc.setdefault(d["name"], {"n": 0})
+        e["n"] += 1
+        for k, v in d.items():
+            if k != "name":
+                e[k] = e.get(k, 0.0) + v
+    return {n: {k: (v / e["n"] if k != "n" else v) for k, v in e.items()} for n, e in acc.items()}
+
+
+def pmc_summary(root, copy_mib=256):
+    """Write profiles/traffic.json and profiles/pmc_<workload>.md (and
+    profiles/kernels_<workload>.md from a kernel trace) from rocprofv3 runs
+    laid out as root/<workload>/<pass>/run_counter_collection.csv (passes of
+    PMC_PASSES) and root/<workload>/trace/run_kernel_stats.csv; each pass's
+    benchmark line in root/<workload>/<pass>.json.  HBM bytes: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by what they read for the plain
+    copy of copy_mib MiB run in the same process (the copy dispatch that
+    wrote the most)."""
+    prof = os.path.join(ROOT, "profiles")
+    entries, calib, shas = {}, {}, set()
+    cmds = [f"rocprofv3 --pmc {c} -d {root}/{{w}}/{p} -o run --output-format csv -- "
+            + PMC_BENCH.format(w="{w}", mib=copy_mib) for p, c in PMC_PASSES.items()]
+    cmds.append(f"rocprofv3 --kernel-trace --stats -d {root}/{{w}}/trace -o run --output-format csv -- "
+                + TRACE_BENCH.format(w="{w}"))
+    for w in sorted(os.listdir(root)):
+        wdir = os.path.join(root, w)
+        if not os.path.isdir(wdir):
+            continue
+        per = {}
+        for p in PMC_PASSES:
+            f = os.path.join(wdir, p, "run_counter_collection.csv")
+            if os.path.exists(f):
+                per[p] = _read_dispatches(f)
+            j = os.path.join(wdir, p + ".json")
+            if os.path.exists(j):
+                with open(j) as fh:
+                    for line in fh:
+                        if line.startswith("{"):
+                            shas.add(json.loads(line)["roofline"].get("source_sha"))
+        factors = {}
+        for p, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+            copies = [d for d in per.get(p, []) if "copyBuffer" in d["name"] and ctr in d]
+            if copies:
+                c = max(copies, key=lambda d: d[ctr])
+                factors[p] = copy_mib * 1024.0 / c[ctr] if c[ctr] > 0 else None
+        calib[w] = {"copy_mib": copy_mib, "fetch_factor": factors.get("fetch"), "write_factor": factors.get("write")}
+        means = {p: _mean_by_kernel([d for d in ds if kernel_region(d["name"])]) for p, ds in per.items()}
+        names = set()
+        for m in means.values():
+            names |= set(m)
+        rows = []
+        for n in names:
+            sq, wt = means.get("sq", {}).get(n, {}), means.get("wait", {}).get(n, {})
+            fe, wr = means.get("fetch", {}).get(n, {}), means.get("write", {}).get(n, {})
+            dur = sq.get("dur_us") or wt.get("dur_us") or fe.get("dur_us") or 0.0
+            calls = max(e.get("n", 0) for e in (sq, wt, fe, wr))
+            r = {"kernel": n.replace("void ", ""), "region": kernel_region(n), "dur_us": dur, "calls": calls}
+            if sq and dur > 0:
+                r["mfma_pct"] = 100.0 * sq.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) * 1024 / (dur * 1e-6) / (PEAK_BF16_TFLOPS * 1e12)
+                r["valu_pct"] = 100.0 * sq.get("SQ_ACTIVE_INST_VALU", 0) * 4 / (1024 * dur * 1e3 * CLOCK_GHZ)
+                mf = sq.get("SQ_INSTS_MFMA", 0)
+                r["valu_per_mfma"] = sq.get("SQ_INSTS_VALU", 0) / mf if mf else None
+                lds = sq.get("SQ_ACTIVE_INST_LDS", 0)
+                r["lds_conflict_pct"] = 100.0 * sq.get("SQ_LDS_BANK_CONFLICT", 0) / lds if lds else None
+            if wt and wt.get("SQ_WAVE_CYCLES"):
+                wc = wt["SQ_WAVE_CYCLES"]
+                r["wait_pct"] = 100.0 * wt.get("SQ_WAIT_ANY", 0) / wc
+                r["issue_wait_pct"] = 100.0 * wt.get("SQ_WAIT_INST_ANY", 0) / wc
+                r["active_pct"] = 100.0 * wt.get("SQ_ACTIVE_INST_ANY", 0) / wc
+            if fe and factors.get("fetch"):
+                r["fetch_mb"] = fe.get("FETCH_SIZE", 0) * factors["fetch"] * 1024 / 1e6
+            if wr and factors.get("write"):
+                r["write_mb"] = wr.get("WRITE_SIZE", 0) * factors["write"] * 1024 / 1e6
+            rows.append(r)
+        rows.sort(key=lambda r: -r["dur_us"] * r["calls"])
+        # traffic of each library step: its kernel with the most time (one launch per step)
+        seen = set()
+        for r in rows:
+            if r["region"] in seen or "fetch_mb" not in r or "write_mb" not in r:
+                continue
+            seen.add(r["region"])
+            entries[f"{r['region']}:{w}"] = {
+                "kernel": r["kernel"], "fetch_bytes": round(r["fetch_mb"] * 1e6),
+                "write_bytes": round(r["write_mb"] * 1e6),
+                "bytes_per_launch": round((r["fetch_mb"] + r["write_mb"]) * 1e6)}
+
+        def fmt(v, d=1):
+            return "—" if v is None else f"{v:.{d}f}"
+        total = sum(r["dur_us"] * r["calls"] for r in rows) or 1.0
+        lines = [f"# rocprofv3 counters: `{w}` (Cayley build + forward + backward, one GPU)", "",
+                 "Commands (from the repository root on the MI355X box, `cd /tmp && export TMPDIR=/tmp` first; "
+                 "one run per counter set):", "", "```"]
+        lines += [c.format(w=w) for c in cmds]
+        lines += [f"python3 bench.py --pmc-summary {root}", "```", "",
+                  "Per kernel, averaged over its dispatches in the counter runs (which also cover the warm-up "
+                  "and the profiled step).  MFMA % = matrix-core busy cycles x 1024 flop per cycle per SIMD "
+                  "over the kernel's duration, against the 2.5 PFLOP/s bf16 peak (padding rows included).  "
+                  f"VALU % = VALU instruction cycles (4 per instruction) over 1024 SIMDs x duration at "
+                  f"{CLOCK_GHZ} GHz.  LDS conflict % = bank-conflict cycles over LDS-active cycles.  Wait / "
+                  "issue-wait / active = SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_ANY over wave-cycles.  "
+                  "Fetch / write: FETCH_SIZE, WRITE_SIZE per dispatch, scaled by "
+                  f"{fmt(factors.get('fetch'), 3)} / {fmt(factors.get('write'), 3)} (a plain {copy_mib} MiB "
+                  "device copy in the same process).", "",
+                  "| step | kernel | calls | µs | share | MFMA % | VALU % | VALU/MFMA | LDS conflict % | wait % | "
+                  "issue-wait % | active % | fetch MB | write MB |",
+                  "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for r in rows[:14]:
+            lines.append(
+                f"| {r['region']} | `{r['kernel']}` | {r['calls']} | {r['dur_us']:.2f} | "
+                f"{100 * r['dur_us'] * r['calls'] / total:.1f}% | {fmt(r.get('mfma_pct'))} | {fmt(r.get('valu_pct'))} | "
+                f"{fmt(r.get('valu_per_mfma'))} | {fmt(r.get('lds_conflict_pct'))} | {fmt(r.get('wait_pct'))} | "
+                f"{fmt(r.get('issue_wait_pct'))} | {fmt(r.get('active_pct'))} | {fmt(r.get('fetch_mb'), 2)} | "
+                f"{fmt(r.get('write_mb'), 2)} |")
+        with open(os.path.join(prof, f"pmc_{w}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        # kernel trace
+        st = os.path.join(wdir, "trace", "run_kernel_stats.csv")
+        if os.path.exists(st):
+            with open(st) as f:
+                recs = [r for r in csv.DictReader(f)]
+            recs = [r for r in recs if kernel_region(re.sub(r"\((?!anonymous).*$", "", r["Name"]))]
+            tot = sum(float(r["TotalDurationNs"]) for r in recs) or 1.0
+            recs.sort(key=lambda r: -float(r["TotalDurationNs"]))
+            tl = [f"# rocprofv3 kernel trace: `{w}` (5 timed steps, 1 warm-up, 1 profiled)", "", "Command (from "
+                  "the repository root on the MI355X box, `cd /tmp && export TMPDIR=/tmp` first):", "", "```",
+                  cmds[-1].format(w=w), f"python3 bench.py --pmc-summary {root}", "```", "",
+                  "Library kernels only (torch's fill and spin kernels and the host copies left out); share of "
+                  "their summed time.", "", "| step | kernel | calls | avg µs | min µs | max µs | share |",
+                  "|---|---|---:|---:|---:|---:|---:|"]
+            for r in recs[:16]:
+                nm = re.sub(r"\((?!anonymous).*$", "", r["Name"]).replace("void ", "")
+                tl.append(f"| {kernel_region(nm)} | `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                          f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |")
+            with open(os.path.join(prof, f"kernels_{w}.md"), "w") as f:
+                f.write("\n".join(tl) + "\n")
+    shas.discard(None)
+    out = {"_about": "HBM bytes per launch of each library step's main kernel, from rocprofv3 FETCH_SIZE and "
+                     "WRITE_SIZE runs of bench.py per workload, scaled by the same counters on a plain device "
+                     "copy in the same process; bench.py reports them only while source_sha matches the "
+                     "kernel sources.",
+           "source_sha": shas.pop() if len(shas) == 1 else source_sha(),
+           "commands": [c for c in cmds] + [f"python3 bench.py --pmc-summary {root}"],
+           "copy_calibration": calib, "entries": entries}
+    with open(os.path.join(prof, "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+
+
 # ------------------------------------------------------------------ summary
 def summary(name, t_step, flops, nbytes, kern, work, sha, phases):
     """The step's rate and roofline, the kernel-step table and the dominant
@@ -672,6 +890,9 @@ def summary(name, t_step, flops, nbytes, kern, work, sha, phases):
 
 def main():
     args = parse()
+    if args.pmc_summary is not None:
+        pmc_summary(args.pmc_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1 "
                                    "(sharding over several GPUs is designed, not implemented)"}))
