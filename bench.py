@@ -584,6 +584,13 @@ def run_moe(cfg, args, sha, headline, cache):
         t_rb = burst_seconds(stream, lambda: oft.oft_moe_router_bwd(d, lg, rtt["topk_idx"], dw, dl, stream=sp))
         out["router_bwd"] = roofline(*moe_kernel_work(cfg, n_active)["moe.router_bwd"], t_rb)
         del dl
+        # reference-policy forward: the frozen base alone (no rotation, no saved activations)
+        t_base = burst_seconds(stream, lambda: oft.oft_moe_grouped_fwd_base(
+            d, x, lg, W["wgu_codes"], W["wgu_scales"], W["wd_codes"], W["wd_scales"], rt, None, y, wsf, nbf,
+            stream=sp), 3)
+        rops_bytes = n_active * cfg.nblk_e * 2 * b * b * 2
+        out["reference_policy_fwd"] = roofline(2 * P * H * 2 * I + 2 * P * I * H,
+                                               by_fwd - rops_bytes - P * 2 * I * 2, t_base)
     if not args.no_cold:
         cf, cb = cold_phases(fwd, bwd)
         out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
