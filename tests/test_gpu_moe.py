@@ -33,6 +33,13 @@ SMALL = {
                                    b=16, q_std=0.05),
     "moe_dense_g128": MoEConfig("moe_dense_g128", T=300, E=4, k=2, H=384, I=256, g=128, chunk=3, b=32,
                                 bias_std=0.5),
+    # the same with H and I multiples of 256 (the transpose-load NN kernels
+    # for dA and dX): b = 16 with g = 64, and experts of about 170 rows (two
+    # 128-row tiles, ragged) with g = 32
+    "moe_w16_b16_g64": MoEConfig("moe_w16_b16_g64", T=256, E=4, k=2, H=512, I=256, g=64, chunk=2, b=16,
+                                 q_std=0.05),
+    "moe_w16_g32_ragged": MoEConfig("moe_w16_g32_ragged", T=333, E=6, k=3, H=768, I=512, g=32, chunk=4, b=32,
+                                    q_std=0.05, bias_std=0.3),
     # at most 8 rows per expert on average (16-row weight-streaming tiles);
     # the hot expert spans several of them.  H, I multiples of 256 take the
     # 256-wide-step kernels (and I = 128 the 64-wide-step one for the down
