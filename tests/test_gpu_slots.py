@@ -147,3 +147,47 @@ def test_slots_graph_replay_follows_the_switch(name):
             assert host(c["latch"])[:2].tolist() == [slot, version], (slot, version, rep)
             assert np.array_equal(host(y), _fwd_plain(c, slot)), (slot, version, rep)
         print(f"  slot {slot} version {version}: two replays match", flush=True)
+
+
+@pytest.mark.parametrize("name", ["decode_int4_g32", "fp8_b32_ragged"])
+def test_slots_two_streams_own_latches(name):
+    """Two streams, each with its own latch, run the slot forward at the
+    same time, before and after a switch published on a third stream that
+    waits for both: each call's output equals the plain forward on the slot
+    its own latch names (calls in flight never share a latch)."""
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    print(f"[slots two streams] {name}", flush=True)
+    c = _ctx(name)
+    _publish(c, 0, 0, 1)
+    _publish(c, 1, 1, 1)  # builds slot 1, publishes it ...
+    _publish(c, 0, 0, 2)  # ... then slot 0 again: active slot 0, version 2
+    torch.cuda.synchronize()
+    want = {0: _fwd_plain(c, 0), 1: _fwd_plain(c, 1)}
+    sa, sb, sw = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    latches = [torch.full((4,), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    for rnd, (slot, version) in enumerate([(0, 2), (1, 3)]):
+        if rnd == 1:
+            # the switch waits for both streams' previous calls, then both wait for it
+            ev = [torch.cuda.Event() for _ in range(2)]
+            ev[0].record(sa)
+            ev[1].record(sb)
+            sw.wait_event(ev[0])
+            sw.wait_event(ev[1])
+            oft.oft_slots_switch(c["state"], slot, version, stream=sw.cuda_stream)
+            done = torch.cuda.Event()
+            done.record(sw)
+            sa.wait_event(done)
+            sb.wait_event(done)
+        ys = []
+        for st, latch in zip((sa, sb), latches):
+            y = _out(c)
+            oft.oft_linear_fwd_slots(c["d"], c["x"], c["wc"], c["ws"], c["slots"][0], c["slots"][1], c["state"],
+                                     latch, y, stream=st.cuda_stream)
+            ys.append(y)
+        torch.cuda.synchronize()
+        for y, latch in zip(ys, latches):
+            got = host(latch)[:2].tolist()
+            assert got == [slot, version], (rnd, got)
+            assert np.array_equal(host(y), want[slot])
