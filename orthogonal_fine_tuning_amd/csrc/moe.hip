@@ -393,7 +393,24 @@ __global__ __launch_bounds__(256) void moe_dw_reduce_kernel(const float* __restr
 // the same pass writes dz = dH_blk R_j (bf16, MFMA), the rotated operand of
 // the gate/up dX GEMM, once per dH tile.
 constexpr int LDM = 64 + 8;
-__device__ __forceinline__ int msw(int n) { return ((n >> 3) & 3) << 4; }
+// dYT / YT row n keeps the row pair of rows 2 rp, 2 rp + 1 at column 2 rp ^
+// msw(n): the eight-channel group of n (bits 3..5) XORs the 8-column chunk,
+// so the 4-byte transposed stores of a wave (channels 8 c + q, pairs rp)
+// fall on 64 different banks and the 16-byte operand reads stay whole chunks.
+__device__ __forceinline__ int msw(int n) { return ((n >> 3) & 7) << 3; }
+
+// LDS of one workgroup: the transposed dH / H tiles during the row loop;
+// after it, S, then the partial sums of the second wave half (red), whose
+// space the Cayley gradient's scratch takes over once S is complete.
+template <int B>
+struct MoeDqLds {
+  static constexpr int TILE = 2 * 64 * LDM * 2;          // dYT + YT
+  static constexpr int S_BYTES = 2 * 32 * 33 * 4;         // S[2][32][33]
+  static constexpr int RED_BYTES = 2 * 64 * 17 * 4;       // red[2][64][17]
+  static constexpr int SCR_BYTES = 3 * (1024 / (B * B)) * B * (B + 4) * 4;
+  static constexpr int TAIL = S_BYTES + (RED_BYTES > SCR_BYTES ? RED_BYTES : SCR_BYTES);
+  static constexpr int BYTES = TILE > TAIL ? TILE : TAIL;
+};
 
 template <int B>
 __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict__ dH, const uint16_t* __restrict__ Hs,
@@ -401,12 +418,14 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
                                                      const float* __restrict__ Rf, int nblk_e,
                                                      float* __restrict__ dq, const uint16_t* __restrict__ Rops,
                                                      uint16_t* __restrict__ dz) {
-  __shared__ __attribute__((aligned(16))) uint16_t dYT[64 * LDM];
-  __shared__ __attribute__((aligned(16))) uint16_t YT[64 * LDM];
-  __shared__ float red[2][64][17];
-  __shared__ float S[2][32][33];
+  using Lds = MoeDqLds<B>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Lds::BYTES];
+  uint16_t* dYT = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* YT = dYT + 64 * LDM;
+  auto S = reinterpret_cast<float (*)[32][33]>(lds);
+  auto red = reinterpret_cast<float (*)[64][17]>(lds + Lds::S_BYTES);
   // scratch of the Cayley gradient: 3 G B (B + 4) floats, G = 1024 / B^2
-  __shared__ __attribute__((aligned(16))) float scr[3 * (1024 / (B * B)) * B * (B + 4)];
+  float* scr = reinterpret_cast<float*>(lds + Lds::S_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -497,6 +516,7 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
     }
   }
   if (dq == nullptr) return;
+  __syncthreads();  // the transposed tiles are dead: their space holds S and red
   if (kh == 1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[grp][lane][r] = acc[r];
