@@ -25,6 +25,7 @@
 #include "gemm_nn.h"
 #include "gemm_nn_dma.h"
 #include "gemm_nn_q4.h"
+#include "gemm_nt_hl.h"
 #include "gemm_nt.h"
 #include "gemm_nt_dma.h"
 #include "oft_moe.h"
@@ -685,6 +686,8 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       if (w16)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, B, MOE_BM, GEPI, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
+      else if (d.H % 128 == 0)  // weight stages of two K steps (half-line copies)
+        hipLaunchKernelGGL((gemm_nt_hl_kernel<W4F, B, GEPI, true>), grid, dim3(nth::NTHR), 0, st, p);
       else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, B, MOE_BM, GEPI, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
@@ -730,6 +733,8 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
       if (w16)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
+      else if (d.I % 128 == 0)  // weight stages of two K steps (half-line copies)
+        hipLaunchKernelGGL((gemm_nt_hl_kernel<W4F, 32, EPI_PLAIN, true>), grid, dim3(nth::NTHR), 0, st, p);
       else
         hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
