@@ -14,6 +14,7 @@
 // pass over HBM.
 #include "gemm_nt.h"
 #include "gemm_nt_dma.h"
+#include "gemm_nt_hl.h"
 #include "gemm_skinny.h"
 #include "oft_launch.h"
 #include "oft_prof.h"
@@ -102,9 +103,19 @@ hipError_t launch_fwd_t(const DenseArgs& a, const void* x, const uint8_t* wc, co
       else if (bm == 192)
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 192, EPI, false>), dim3(nt, (a.M + 191) / 192),
                            dim3(ntd::NTHR), 0, st, p);
-      else
-        hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI, false>), dim3(nt, (a.M + 127) / 128),
-                           dim3(ntd::NTHR), 0, st, p);
+      else {
+        bool hl = false;
+        if constexpr (wf_4bit(WF)) {
+          if (a.K % 128 == 0) {  // weight stages of two K steps (half-line copies)
+            hipLaunchKernelGGL((gemm_nt_hl_kernel<WF, B, EPI, false>), dim3(nt, (a.M + 127) / 128),
+                               dim3(nth::NTHR), 0, st, p);
+            hl = true;
+          }
+        }
+        if (!hl)
+          hipLaunchKernelGGL((gemm_nt_dma_kernel<WF, B, 128, EPI, false>), dim3(nt, (a.M + 127) / 128),
+                             dim3(ntd::NTHR), 0, st, p);
+      }
       return hipGetLastError();
     }
   }
