@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--w-fmt", choices=("int4", "fp4"), default=None,
                     help="run the 4-bit workloads with this base format (FP4: OCP MX E2M1 codes, E8M0 group "
                          "exponents in the same layout and bytes as INT4)")
+    ap.add_argument("--storage", choices=("auto", "row-major"), default="auto",
+                    help="MoE INT4 weights: 'auto' packs them once, untimed, into the tiled storage "
+                         "(OFT_W_INT4_TILED) where H and I are multiples of 256; 'row-major' keeps them as given")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="MoE: skip the dense-bf16-weight reference run of the same grouped kernels")
@@ -513,7 +516,10 @@ def run_moe(cfg, args, sha, headline, cache):
 
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
     P = T * k
-    w_fmt = oft.OFT_W_FP4_E2M1 if cfg.w_fmt == "fp4" else oft.OFT_W_INT4
+    # the frozen INT4 weights in the tiled storage (a one-time permutation at
+    # load, like the quantisation itself) where its shape constraint holds
+    tiled = args.storage == "auto" and cfg.w_fmt == "int4" and H % 256 == 0 and I % 256 == 0
+    w_fmt = oft.OFT_W_FP4_E2M1 if cfg.w_fmt == "fp4" else oft.OFT_W_INT4_TILED if tiled else oft.OFT_W_INT4
     d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=w_fmt)
     i32 = dict(dtype=torch.int32, device="cuda")
     rtt = dict(topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
@@ -526,6 +532,12 @@ def run_moe(cfg, args, sha, headline, cache):
     Rf = torch.empty((E, cfg.nblk_e, b, b), dtype=torch.float32, device="cuda")
     Rops = torch.empty((E, cfg.nblk_e, 2, b, b), dtype=torch.int16, device="cuda")
     W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
+    W_rm = None
+    if tiled:
+        W_rm, W = W, {n: torch.empty_like(t) for n, t in W.items()}
+        for c, sc, rows, cols in (("wgu_codes", "wgu_scales", 2 * I, H), ("wd_codes", "wd_scales", H, I)):
+            oft.oft_pack_int4_tiled(E, rows, cols, cfg.g, W_rm[c], W_rm[sc], W[c], W[sc])
+        torch.cuda.synchronize()
     x, lg, dy = dev(inp["x"]), dev(inp["logits"]), dev(inp["dy"])
     hs = torch.empty((P, 2 * I), dtype=torch.int16, device="cuda")
     y = torch.empty((T, H), dtype=torch.int16, device="cuda")
@@ -575,10 +587,34 @@ def run_moe(cfg, args, sha, headline, cache):
                   {"cayley_build": t_cay, "fwd": t_fwd, "bwd": t_bwd})
     out["config"] = {"workload": cfg.name, "tokens": T, "experts": E, "top_k": k, "hidden": H,
                      "expert_intermediate": I, "weights": f"{cfg.w_fmt}_g{cfg.g}", "oft_block": b,
+                     "weight_storage": "tiled" if tiled else "row-major",
                      "chunk": cfg.chunk, "active_experts": n_active, "parallelism": "single_gpu"}
     out["phase_rates"] = {"fwd_tflops": round(f_fwd / t_fwd / 1e12, 2), "bwd_tflops": round(f_bwd / t_bwd / 1e12, 2),
                           "fwd_alg_gbs": round(by_fwd / t_fwd / 1e9, 1), "bwd_alg_gbs": round(by_bwd / t_bwd / 1e9, 1)}
     out["transient_bytes"] = int(transient)
+    if W_rm is not None:
+        # the same step on the row-major storage of the same weights
+        d_rm = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=oft.OFT_W_INT4)
+        nbf_rm = oft.oft_moe_workspace_bytes(d_rm, oft.OFT_PASS_FWD)
+        nbb_rm = oft.oft_moe_workspace_bytes(d_rm, oft.OFT_PASS_BWD)
+        wsf_rm = torch.empty(nbf_rm, dtype=torch.uint8, device="cuda")
+        wsb_rm = torch.empty(nbb_rm, dtype=torch.uint8, device="cuda")
+
+        def step_rm(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            oft.cayley_build(q, nblk, b, Rf, Rops, stream=sp)
+            oft.oft_moe_grouped_fwd(d_rm, x, lg, W_rm["wgu_codes"], W_rm["wgu_scales"], W_rm["wd_codes"],
+                                    W_rm["wd_scales"], Rops, rt, hs, y, wsf_rm, nbf_rm, stream=sp)
+            oft.oft_moe_grouped_bwd(d_rm, dy, rt, hs, W_rm["wgu_codes"], W_rm["wgu_scales"], W_rm["wd_codes"],
+                                    W_rm["wd_scales"], Rf, Rops, dx, dq, dw, wsb_rm, nbb_rm, stream=sp)
+            if ev is not None:
+                ev[1].record(stream)
+
+        t_rm, _ = time_steps(step_rm, args.steps, args.warmup, nev=2)
+        out["row_major_storage"] = {"ms_per_step": round(t_rm * 1e3, 4),
+                                    "speedup_of_tiled": round(t_rm / t_step, 4)}
+        del wsf_rm, wsb_rm
     if not args.no_extras:
         dl = torch.empty((T, E), dtype=torch.float32, device="cuda")
         t_rb = burst_seconds(stream, lambda: oft.oft_moe_router_bwd(d, lg, rtt["topk_idx"], dw, dl, stream=sp))
@@ -596,7 +632,7 @@ def run_moe(cfg, args, sha, headline, cache):
         out["phases_cold_us"] = {"fwd": round(cf * 1e6, 2), "bwd": round(cb * 1e6, 2),
                                  "fwd_alg_gbs": round(by_fwd / cf / 1e9, 1), "bwd_alg_gbs": round(by_bwd / cb / 1e9, 1)}
     if not args.no_dense_ref:
-        del W
+        del W, W_rm
         torch.cuda.empty_cache()
         out["dense_bf16_reference"] = moe_dense_reference(cfg, inp, args, dict(
             x=x, lg=lg, dy=dy, rt=rt, Rf=Rf, Rops=Rops, hs=hs, y=y, dx=dx, dq=dq, dw=dw, counts=rtt["counts"]),
@@ -756,7 +792,8 @@ def kernel_region(name):
     fam, _, targs = base.partition("<")
     a = [t.strip() for t in targs.rstrip(">").split(",")] if targs else []
     nt = {"gemm_nt_dma_kernel": (3, 5), "gemm_nt_dec4_kernel": (1, 2), "gemm_nt_dec_kernel": (2, 3),
-          "gemm_nt_kernel": (4, 5), "gemm_nt_dec16_kernel": (1, None), "gemm_nt_skinny_kernel": (5, None)}
+          "gemm_nt_kernel": (4, 5), "gemm_nt_dec16_kernel": (1, None), "gemm_nt_skinny_kernel": (5, None),
+          "gemm_nt_hl_kernel": (2, 3)}
     nn = {"gemm_nn_kernel": (5, 6), "gemm_nn_dma_kernel": (1, 2), "gemm_nn_q4_kernel": (0, 1)}
     if fam in nt:
         ie, ig = nt[fam]

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OFT_ABI_VERSION 7
+#define OFT_ABI_VERSION 8
 
 typedef enum {
   OFT_OK = 0,
@@ -87,7 +87,17 @@ enum { OFT_DT_BF16 = 0, OFT_DT_F32 = 1 };
  * byte is ignored): w = e2m1(code) * 2^(c - 127).  g = 32 is the OCP MXFP4
  * block; its one-byte scales are widened to 16 bits.  c = 255 (NaN in the
  * OCP format) is not supported: its results are unspecified. */
-enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1, OFT_W_BF16 = 2, OFT_W_FP4_E2M1 = 3 };
+/* OFT_W_INT4_TILED (MoE calls only): the INT4 weights of OFT_W_INT4 (same
+ * values, same fp16 group scales: the frozen 4-bit base of the QOFT paper's
+ * "Quantized OFT" section) with each expert matrix [N, K] stored in tiles of
+ * 64 rows x 128 columns, tile (rb, kb) the (rb * K/128 + kb)-th: codes 4096
+ * bytes a tile, the tile's row r at byte 64 r (its 128 codes as in a
+ * row-major row); scales 16384/g bytes a tile, the tile's row r at byte
+ * r 256/g (its 128/g slots in column order).  The arrays have the sizes of
+ * the row-major ones; oft_pack_int4_tiled converts.  The grouped GEMMs then
+ * read each 64-row block's codes and scales for a K step as contiguous
+ * runs. */
+enum { OFT_W_INT4 = 0, OFT_W_FP8_E4M3 = 1, OFT_W_BF16 = 2, OFT_W_FP4_E2M1 = 3, OFT_W_INT4_TILED = 4 };
 enum { OFT_PASS_FWD = 0, OFT_PASS_BWD = 1 };
 
 #define OFT_MAX_SEGMENTS 8
@@ -113,23 +123,27 @@ typedef struct {
  * intermediate I.  Per expert e: gate/up weight [2I, H] (gate rows [0, I),
  * up rows [I, 2I)) with its own adapter of 2I/b blocks (gate blocks first),
  * down weight [H, I] without adapter; INT4 with group g (w_fmt =
- * OFT_W_INT4, zero), FP4 with group g (OFT_W_FP4_E2M1, the same layout with
- * E8M0 exponents in the scale slots) or, as a measurement reference, bf16
+ * OFT_W_INT4, zero, or OFT_W_INT4_TILED, the same values tiled), FP4 with
+ * group g (OFT_W_FP4_E2M1, the same layout with E8M0 exponents in the scale
+ * slots) or, as a measurement reference, bf16
  * (OFT_W_BF16: the
  * code arrays hold bf16 weights [E, 2I, H] and [E, H, I], the scale
  * pointers are ignored and may be NULL, g is not checked).
  * Constraints: T >= 0; 1 <= k <= 16; k <= E <= 1024; H % 64 == 0;
  * I % 64 == 0; b in {16, 32}; I % b == 0; INT4 and FP4: g in {32, 64,
- * 128}, H % g == 0, I % g == 0; chunk >= 1; renorm in {0, 1}; w_fmt one of
- * the three formats above (else OFT_EDTYPE).  Size range (else
- * OFT_EUNSUPPORTED): H and I <= 2^16, ceil(T k / 16) + E <= 65535 (the
- * grouped work list runs along the launch grid's y dimension). */
+ * 128}, H % g == 0, I % g == 0; OFT_W_INT4_TILED: H % 256 == 0 and
+ * I % 256 == 0 (else OFT_ESHAPE); chunk >= 1; renorm in {0, 1}; w_fmt one
+ * of the four formats above (else OFT_EDTYPE).  Size range (else
+ * OFT_EUNSUPPORTED): H and I <= 2^16, I H < 2^31 (code offsets inside an
+ * expert are 32-bit), ceil(T k / 16) + E <= 65535 (the grouped work list
+ * runs along the launch grid's y dimension). */
 typedef struct {
   int32_t T, E, k, H, I, g, b;
   int32_t chunk;  /* active experts per chunk (scheduling unit)            */
   int32_t renorm; /* 0: combine weights = softmax over all E at the chosen
                      experts; 1: renormalised over the k chosen             */
-  int32_t w_fmt;  /* OFT_W_INT4 (0), OFT_W_FP4_E2M1 or OFT_W_BF16         */
+  int32_t w_fmt;  /* OFT_W_INT4 (0), OFT_W_INT4_TILED, OFT_W_FP4_E2M1 or
+                     OFT_W_BF16                                             */
 } oft_moe_desc;
 
 /* Routing tables: device pointers, caller-allocated, written by the
@@ -192,6 +206,20 @@ int32_t cayley_build(const uint16_t* q_bf16, int32_t nblk, int32_t b, float* R_f
  * cols % 8 == 0; INT4 and FP4: g in {32, 64, 128}, cols % g == 0. */
 int32_t oft_dequant(int32_t w_fmt, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
                     const void* scales, uint16_t* out_bf16, void* stream);
+
+/* ---- tiled INT4 storage (see OFT_W_INT4_TILED) ----------------------------
+ * Writes the tiled copy of `count` row-major INT4 weights [rows, cols] (group
+ * g) stored one after another: codes [count, rows, cols/2] -> codes_tiled
+ * (same size), fp16 scales [count, rows, cols/g] -> scales_tiled (same size).
+ * A permutation of bytes (exact); the weights are frozen, so a caller packs
+ * once, e.g. at load.  Device pointers, 16-byte aligned; the outputs may not
+ * overlap the inputs.  Constraints: count, rows, cols >= 0 (a zero is a
+ * no-op); rows % 64 == 0 and cols % 128 == 0 (else OFT_ESHAPE); g in {32,
+ * 64, 128} (else OFT_EUNSUPPORTED); rows cols < 2^32 (else
+ * OFT_EUNSUPPORTED).  Errors: OFT_EINVAL (null / misaligned / overlapping
+ * pointers, negative sizes), OFT_EHIP. */
+int32_t oft_pack_int4_tiled(int32_t count, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
+                            const uint16_t* scales, uint8_t* codes_tiled, uint16_t* scales_tiled, void* stream);
 
 /* ---- dense layer ----------------------------------------------------------
  * Workspace query for `pass` (OFT_PASS_FWD / OFT_PASS_BWD); writes *bytes. */

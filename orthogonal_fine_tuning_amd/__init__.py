@@ -10,16 +10,17 @@ import ctypes as C
 
 from . import _lib
 from ._lib import (OFT_DT_BF16, OFT_DT_F32, OFT_PASS_BWD, OFT_PASS_FWD, OFT_W_BF16,
-                   OFT_W_FP4_E2M1, OFT_W_FP8_E4M3, OFT_W_INT4, OftError, oft_linear_desc, oft_moe_desc,
-                   oft_moe_routing)
+                   OFT_W_FP4_E2M1, OFT_W_FP8_E4M3, OFT_W_INT4, OFT_W_INT4_TILED, OftError, oft_linear_desc,
+                   oft_moe_desc, oft_moe_routing)
 
 __all__ = [
-    "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant",
+    "OftError", "linear_desc", "moe_desc", "moe_routing", "cayley_build", "oft_dequant", "oft_pack_int4_tiled",
     "oft_linear_workspace_bytes", "oft_linear_fwd", "oft_linear_fwd_base", "oft_linear_bwd", "oft_linear_bwd_noalloc", "oft_logprob_diff",
     "oft_slots_switch", "oft_linear_fwd_slots",
     "oft_moe_workspace_bytes", "oft_moe_route", "oft_moe_router_bwd", "oft_moe_grouped_fwd", "oft_moe_grouped_fwd_base", "oft_moe_grouped_bwd", "abi_version",
     "prof_enable", "prof_records",
-    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_W_FP4_E2M1", "OFT_PASS_FWD",
+    "OFT_DT_BF16", "OFT_DT_F32", "OFT_W_INT4", "OFT_W_FP8_E4M3", "OFT_W_BF16", "OFT_W_FP4_E2M1", "OFT_W_INT4_TILED",
+    "OFT_PASS_FWD",
     "OFT_PASS_BWD",
 ]
 
@@ -96,6 +97,11 @@ def cayley_build(q, nblk, b, R_f32, R_ops=None, stream=None):
 def oft_dequant(w_fmt, rows, cols, g, codes, scales, out, stream=None):
     _lib.check(_lib.load().oft_dequant(w_fmt, rows, cols, g, _ptr(codes), _ptr(scales), _ptr(out),
                                        _stream(stream)), "oft_dequant")
+
+
+def oft_pack_int4_tiled(count, rows, cols, g, codes, scales, codes_tiled, scales_tiled, stream=None):
+    _lib.check(_lib.load().oft_pack_int4_tiled(count, rows, cols, g, _ptr(codes), _ptr(scales), _ptr(codes_tiled),
+                                               _ptr(scales_tiled), _stream(stream)), "oft_pack_int4_tiled")
 
 
 def oft_linear_workspace_bytes(desc, pass_) -> int:

@@ -14,7 +14,7 @@ LIB_PATH = os.environ.get("OFT_LIBRARY") or os.path.join(_HERE, "liboft.so")
 OFT_OK, OFT_EINVAL, OFT_ESHAPE, OFT_EDTYPE, OFT_EUNSUPPORTED, OFT_EWORKSPACE, OFT_EHIP = (
     0, -1, -2, -3, -4, -5, -6)
 OFT_DT_BF16, OFT_DT_F32 = 0, 1
-OFT_W_INT4, OFT_W_FP8_E4M3, OFT_W_BF16, OFT_W_FP4_E2M1 = 0, 1, 2, 3
+OFT_W_INT4, OFT_W_FP8_E4M3, OFT_W_BF16, OFT_W_FP4_E2M1, OFT_W_INT4_TILED = 0, 1, 2, 3, 4
 OFT_PASS_FWD, OFT_PASS_BWD = 0, 1
 OFT_MAX_SEGMENTS = 8
 OFT_NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -53,6 +53,7 @@ SIGNATURES = {
     "oft_last_hip_error": (_I, []),
     "cayley_build": (_I, [_P, _I, _I, _P, _P, _P]),
     "oft_dequant": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
+    "oft_pack_int4_tiled": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "oft_linear_workspace_bytes": (_I, [C.POINTER(oft_linear_desc), _I, C.POINTER(_SZ)]),
     "oft_linear_fwd": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "oft_linear_fwd_base": (_I, [C.POINTER(oft_linear_desc), _P, _P, _P, _P, _P, _SZ, _P]),

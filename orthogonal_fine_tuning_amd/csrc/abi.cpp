@@ -26,7 +26,7 @@ int32_t hip_status(hipError_t e) {
 bool group_ok(int g) { return g == 32 || g == 64 || g == 128; }
 
 static_assert(oft::WF_INT4 == OFT_W_INT4 && oft::WF_FP8 == OFT_W_FP8_E4M3 && oft::WF_BF16 == OFT_W_BF16 &&
-                  oft::WF_FP4 == OFT_W_FP4_E2M1,
+                  oft::WF_FP4 == OFT_W_FP4_E2M1 && oft::WF_INT4T == OFT_W_INT4_TILED,
               "kernel weight formats are numbered as the ABI's");
 
 // the 4-bit formats: codes two per byte plus a 16-bit scale per group of g
@@ -119,6 +119,25 @@ int32_t oft_dequant(int32_t w_fmt, int32_t rows, int32_t cols, int32_t g, const 
   if (!ptr_ok(codes) || !ptr_ok(out_bf16)) return OFT_EINVAL;
   if (w4(w_fmt) && !ptr_ok(scales)) return OFT_EINVAL;
   return hip_status(oft::launch_dequant(w_fmt, rows, cols, g, codes, scales, out_bf16,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t oft_pack_int4_tiled(int32_t count, int32_t rows, int32_t cols, int32_t g, const uint8_t* codes,
+                            const uint16_t* scales, uint8_t* codes_tiled, uint16_t* scales_tiled, void* stream) {
+  if (count < 0 || rows < 0 || cols < 0) return OFT_EINVAL;
+  if (!group_ok(g)) return OFT_EUNSUPPORTED;
+  if (rows % oft::T4_ROWS != 0 || cols % oft::T4_COLS != 0) return OFT_ESHAPE;
+  const long long n = (long long)count * rows * cols;
+  if (n == 0) return OFT_OK;
+  // offsets inside one matrix are 32-bit: rows * cols / 2 code bytes < 2^31
+  if ((long long)rows * cols >= (1LL << 32)) return OFT_EUNSUPPORTED;
+  if (!ptr_ok(codes) || !ptr_ok(scales) || !ptr_ok(codes_tiled) || !ptr_ok(scales_tiled)) return OFT_EINVAL;
+  // the tiled copies may not overlap their sources
+  const auto lo = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+  const uintptr_t cb = (uintptr_t)(n / 2), sb = (uintptr_t)(n / g * 2);
+  if (lo(codes) < lo(codes_tiled) + cb && lo(codes_tiled) < lo(codes) + cb) return OFT_EINVAL;
+  if (lo(scales) < lo(scales_tiled) + sb && lo(scales_tiled) < lo(scales) + sb) return OFT_EINVAL;
+  return hip_status(oft::launch_pack_t4(count, rows, cols, g, codes, scales, codes_tiled, scales_tiled,
                                         static_cast<hipStream_t>(stream)));
 }
 

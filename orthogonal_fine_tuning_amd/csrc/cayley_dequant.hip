@@ -305,6 +305,46 @@ __global__ __launch_bounds__(256) void dequant_fp8_kernel(const uint2* __restric
   out[idx] = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Row-major 4-bit weights to the tiled storage of oft_formats.h, `count`
+// [rows, cols] matrices one after another: one thread per 16-byte piece of
+// codes (32 columns of a row, which stay together in one tile row), then one
+// per scale slot.  A permutation: every byte is copied once.
+__global__ __launch_bounds__(256) void pack_t4_codes_kernel(const uint4* __restrict__ codes,
+                                                            uint8_t* __restrict__ out, size_t n16, int rows,
+                                                            int cols) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n16) return;
+  const int per_row = cols / 32;
+  const size_t per_mat = (size_t)rows * per_row;
+  const size_t m = idx / per_mat, rem = idx % per_mat;
+  const int r = (int)(rem / per_row), c = (int)(rem % per_row);
+  *reinterpret_cast<uint4*>(out + m * per_mat * 16 + t4_code_off(r, 16 * c, cols)) = codes[idx];
+}
+
+__global__ __launch_bounds__(256) void pack_t4_scales_kernel(const uint16_t* __restrict__ scales,
+                                                             uint8_t* __restrict__ out, size_t n, int rows,
+                                                             int cols, int g) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int per_row = cols / g;
+  const size_t per_mat = (size_t)rows * per_row;
+  const size_t m = idx / per_mat, rem = idx % per_mat;
+  const int r = (int)(rem / per_row), j = (int)(rem % per_row);
+  *reinterpret_cast<uint16_t*>(out + m * per_mat * 2 + t4_scale_off(r, j, cols, g)) = scales[idx];
+}
+
+hipError_t launch_pack_t4(int count, int rows, int cols, int g, const uint8_t* codes, const uint16_t* scales,
+                          uint8_t* codes_t, uint16_t* scales_t, hipStream_t st) {
+  const size_t n16 = (size_t)count * rows * (cols / 32);
+  const size_t ns = (size_t)count * rows * (cols / g);
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_t4_codes_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(codes), codes_t, n16, rows, cols);
+  hipLaunchKernelGGL(pack_t4_scales_kernel, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, st, scales,
+                     reinterpret_cast<uint8_t*>(scales_t), ns, rows, cols, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t* Rops,
                          hipStream_t st) {
   if (nblk == 0) return hipSuccess;

@@ -82,6 +82,7 @@ template <int BM, bool OUTF32, int WF, int B, int PRO, int EPI, bool GROUPED, in
 __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nn_kernel(NnArgs p) {
   using namespace nn;
   static_assert(BM == 128 || BM == 256, "tile");
+  static_assert(!wf_tiled(WF), "row-major weights only");
   constexpr bool FP8 = WF == WF_FP8;
   constexpr bool W16 = WF == WF_BF16;  // bf16 weights: plain copies into the tile
   constexpr int TM = BM / 64;   // 32-token tiles per wave (main product)

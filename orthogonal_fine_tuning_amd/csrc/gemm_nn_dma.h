@@ -74,7 +74,7 @@ __global__ __launch_bounds__(nnd::NTHR, 1) void gemm_nn_dma_kernel(NnArgs p) {
   using ntd::copy4;
   using ntd::lds_addr;
   using ntd::swz_x;
-  static_assert(wf_4bit(WF) || WF == WF_BF16, "weights");
+  static_assert((wf_4bit(WF) && !wf_tiled(WF)) || WF == WF_BF16, "row-major weights");
   static_assert(EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD, "epilogue");
   constexpr bool W16 = WF == WF_BF16;
   constexpr int TM = BM / 64;  // 32-row tiles per wave

@@ -38,6 +38,12 @@
 // product exact in fp32, one rounding: the dequant hook's value.  In MFMA
 // kk (0..3) of a step, lane group g2 takes the contraction indices
 // 32 (kk >> 1) + 16 g2 + 8 (kk & 1) + p (p = 0..7) for both operands.
+//
+// TILED: the weight in the tiled INT4 storage of oft_formats.h.  A step's
+// 64 weight rows are one 64-row block, its 256 columns two tile columns, so
+// the codes land in the same LDS layout from two 4 KB tiles (each wave's 8
+// rows: 256 contiguous bytes per tile quarter) and the 64 scales of a wave
+// are 64 slots 256/g bytes apart in one tile (row-major: 64 rows apart).
 #pragma once
 
 #include <type_traits>
@@ -64,11 +70,6 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 __device__ __forceinline__ uint2 ds_read_tr4(const uint8_t* p) {
   const v2i v = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)p);
   return make_uint2((uint32_t)v.x, (uint32_t)v.y);
-}
-// 2 bytes per lane into the LDS dword slot of the lane (zero-extended)
-__device__ __forceinline__ void copy2(uint32_t lds, const void* base, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds), "v"(voff), "s"(base)
-               : "memory", "m0");
 }
 
 // 8 INT4 codes (low nibble first) with one fp16 scale each (sc[e]: the fp16
@@ -97,10 +98,11 @@ __device__ __forceinline__ uint4 dq_i4x8_rows(uint32_t w, const uint32_t* sc) {
 }
 }  // namespace nnq
 
-template <int EPI, bool GROUPED>
+template <int EPI, bool GROUPED, bool TILED = false>
 __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
   using namespace nnq;
   using ntd::copy16;
+  using ntd::copy2;
   using ntd::copy16v;
   using ntd::lds_addr;
   using ntd::swz_x;
@@ -154,10 +156,13 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
 
   // ---- code copy: rows n = 8 wave + lane / 8, LDS piece lane % 8 holds
   // global piece (lane % 8) ^ swz_c(n) of the row's 128 bytes
+  // (the step's rows n0 = 64 s: a whole block of the tiled layout, which
+  // starts where row n0 does in the row-major one)
   const int cn = 8 * wave + (lane >> 3);
-  const uint32_t coff = (uint32_t)(cn * (K / 2) + kbase / 2 + 16 * ((lane & 7) ^ swz_c(cn)));
+  const int cbyte = kbase / 2 + 16 * ((lane & 7) ^ swz_c(cn));
+  const uint32_t coff = TILED ? oft::t4_code_off(cn, cbyte, K) : (uint32_t)(cn * (K / 2) + cbyte);
   // scale copy: lane j -> s[n0 + j][gw]
-  const uint32_t soff = (uint32_t)((lane * kg + gw) * 2);
+  const uint32_t soff = TILED ? oft::t4_scale_off(lane, gw, K, p.g) : (uint32_t)((lane * kg + gw) * 2);
 
   const uint32_t base_lds = lds_addr(smem);
   auto issue = [&](int s) {

@@ -84,6 +84,7 @@ __global__ __launch_bounds__(256, (BM == 256 && NBUF == 2) ? 1 : 2) void gemm_nt
   using namespace nt;
   constexpr bool FP8 = WF == WF_FP8;
   static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
+  static_assert(!wf_tiled(WF), "row-major weights only");
   static_assert(BM == 128 || BM == 256, "tile");
   static_assert(NBUF == 1 || NBUF == 2, "buffers");
   constexpr int TM = BM / 64;  // 32-token tiles per wave

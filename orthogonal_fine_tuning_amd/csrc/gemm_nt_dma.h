@@ -88,6 +88,11 @@ __device__ __forceinline__ void copy4(uint32_t lds, const void* base, uint32_t v
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base)
                : "memory", "m0");
 }
+// 2 bytes per lane into the LDS dword slot of the lane (zero-extended)
+__device__ __forceinline__ void copy2(uint32_t lds, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
 // wait until at most N copies of this wave are in flight, then a workgroup
 // barrier that also retires this wave's LDS reads
 template <int N>
@@ -129,6 +134,7 @@ __global__ __launch_bounds__(ntd::NTHR, (WF != WF_BF16 && BM == 128 && KB == 64)
   static_assert(KB == 64 || (KB == 128 && WF == WF_FP8 && BM <= 192 && !GROUPED), "128-wide K steps: FP8, <= 192 tokens");
   static_assert(BM == 128 || BM == 192, "tile");
   static_assert(WF != WF_BF16 || BM == 128, "bf16 weights: three stages fit with 128-token tiles only");
+  static_assert(!wf_tiled(WF), "row-major weights only");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || epi_swiglu(EPI) || EPI == EPI_BASE, "epilogue");
   static_assert(!epi_swiglu(EPI) || BM == 128, "exchange buffer sized for 128-token tiles");
   constexpr bool FP8 = WF == WF_FP8;
@@ -757,6 +763,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_d
   using namespace ntd;
   constexpr bool FP8 = WF == WF_FP8;
   static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
+  static_assert(!wf_tiled(WF), "row-major weights only");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || epi_swiglu(EPI) || EPI == EPI_BASE, "epilogue");
   static_assert(BMD == 64 || (BMD == 16 && !FP8 && GROUPED), "16-row tiles: grouped 4-bit weights");
   constexpr bool SWI = epi_swiglu(EPI);
@@ -963,6 +970,9 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, WF == WF_FP8 ? 1 : 2) void gemm_nt_d
 //   activations  BMD rows x 512 B, chunk c of row r at c ^ (r & 15)
 // (16 consecutive rows read at one chunk hit 16 distinct 16-byte bank
 // slots in both layouts).  16-row tiles: 78 KB, two workgroups per CU.
+// Tiled INT4 storage (WF_INT4T, oft_formats.h): a step is two tile columns;
+// the codes land as above, the scales as two halves (the step's two tiles)
+// of 128 rows x 256/g bytes, copied 16 contiguous bytes a lane.
 namespace ntd {
 constexpr int D4_NST = 3;
 }  // namespace ntd
@@ -974,6 +984,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   static_assert(BMD == 16 || BMD == 64, "tile rows");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || epi_swiglu(EPI) || EPI == EPI_BASE, "epilogue");
   constexpr bool SWI = epi_swiglu(EPI);
+  constexpr bool TILED = wf_tiled(WF);
   constexpr int TM = BMD == 64 ? 2 : 1, NST = D4_NST;
   constexpr int WBY = 128 * 128, SBY = 128 * 16, XBY = BMD * 512, SB = WBY + SBY + XBY;
   constexpr int XI = BMD / 16;  // activation copies per wave per step (2 rows x 512 B each)
@@ -1012,8 +1023,9 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   const int nks = K / 256;
   const int kg = K / p.g;
   const int sg = 512 / p.g;  // scale bytes per row and step: 16, 8 or 4
-  // scale copy instructions per step: g = 64 takes four (two dwords a row)
-  const int nsw = p.g == 64 ? 4 : 2;
+  // scale copy instructions per step: g = 64 takes four (two dwords a row);
+  // tiled: 128 rows x 512/g bytes, 16 a lane (g = 32 two, else one)
+  const int nsw = TILED ? (p.g == 32 ? 2 : 1) : p.g == 64 ? 4 : 2;
 
   // copies of wave w per step:
   //   weights rows 16 w + 8 i + lane / 8 (i = 0, 1), chunk lane % 8;
@@ -1025,15 +1037,29 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rw = 16 * wave + 8 * i + (lane >> 3);
-    woff[i] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 7) ^ ((rw >> 1) & 7)));
+    const int cb = 16 * ((lane & 7) ^ ((rw >> 1) & 7));
+    // (tiled: relative to the block of cbase, a multiple of 64)
+    woff[i] = TILED ? t4_code_off(crow(rw), cb, K) : (uint32_t)(crow(rw) * (K / 2) + cb);
   }
+  constexpr int WSTEP = TILED ? 2 * T4_TILE_BYTES : 128;  // code bytes from one step to the next
   uint32_t soff = 0;
-  {
+  if constexpr (TILED) {
+    // lane L = 64 wave + lane of the scale copies: half h (the step's tile
+    // h), 64-row block j of the tile's 128 rows, 16-byte piece q of that
+    // block's 64 x 256/g contiguous bytes; its LDS bytes are 16 L, i.e.
+    // [half][row][256/g]
+    const int sr = 256 / p.g;  // bytes a row in one tile
+    const int L = 64 * wave + lane;
+    const int h = L / (8 * sr), j = (L / (4 * sr)) & 1, q = L % (4 * sr);
+    soff = t4_scale_off(crow(64 * j), 0, K, p.g) + (uint32_t)(h * (16384 / p.g) + 16 * q);
+  } else {
     const int j = 64 * wave + lane;
     const int row = p.g == 64 ? (j >> 1) : j;
     const int sub = p.g == 64 ? 4 * (j & 1) : 0;
     soff = (uint32_t)((cbase + crow(row & 127)) * kg * 2 + sub);
   }
+  const uint8_t* ws_b = reinterpret_cast<const uint8_t*>(ws_h) + (TILED ? (size_t)cbase * kg * 2 : 0);
+  const int s_step = TILED ? 2 * 16384 / p.g : sg;  // scale bytes from one step to the next
   uint32_t xoff[XI];
   const uint8_t* xptr[GROUPED ? XI : 1];
   const uint8_t* xbase = static_cast<const uint8_t*>(p.a) + (size_t)pos0 * p.lda * 2;
@@ -1050,7 +1076,8 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   }
   const uint32_t base_lds = lds_addr(smem);
   const uint32_t w_lds = base_lds + (uint32_t)(16 * wave * 128);
-  const uint32_t s_lds = base_lds + (uint32_t)(WBY + (p.g == 64 ? 4 * 64 * wave : (p.g == 32 ? 16 : 4) * 64 * wave));
+  const uint32_t s_lds = base_lds + (uint32_t)(WBY + (TILED ? 1024 * wave : p.g == 64 ? 4 * 64 * wave
+                                                                           : (p.g == 32 ? 16 : 4) * 64 * wave));
   const uint32_t x_lds = base_lds + (uint32_t)(WBY + SBY + 2 * XI * wave * 512);
   const bool scopy = wave < nsw;
   const int per = 2 + XI + (scopy ? 1 : 0);  // copies per step of this wave
@@ -1059,7 +1086,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
     const int st = s % NST;
     const uint32_t so = (uint32_t)(st * SB);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) copy16(w_lds + so + 1024 * i, wbase + (size_t)s * 128, woff[i]);
+    for (int i = 0; i < 2; ++i) copy16(w_lds + so + 1024 * i, wbase + (size_t)s * WSTEP, woff[i]);
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       if constexpr (GROUPED)
@@ -1068,11 +1095,14 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
         copy16(x_lds + so + 1024 * i, xbase + (size_t)s * 512, xoff[i]);
     }
     if (scopy) {
-      const uint8_t* sb = reinterpret_cast<const uint8_t*>(ws_h) + (size_t)s * sg;
-      if (p.g == 32)
+      const uint8_t* sb = ws_b + (size_t)s * s_step;
+      if (TILED) {
+        if (p.g != 128 || lane < 32) copy16(s_lds + so, sb, soff);
+      } else if (p.g == 32) {
         copy16(s_lds + so, sb, soff);
-      else
+      } else {
         copy4(s_lds + so, sb, soff);
+      }
     }
   };
 
@@ -1099,10 +1129,19 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
     const uint4 v0 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * (c0 ^ wsw));
     const uint4 v1 = *reinterpret_cast<const uint4*>(W + rw * 128 + 16 * ((c0 + 1) ^ wsw));
     uint32_t sw;
-    if (p.g == 32)
+    if (TILED) {
+      // half kh (in-features 128 kh + ...), this lane's slots 64 g2 / g of it
+      const int sr = 256 / p.g;
+      const uint8_t* sp = S + kh * 128 * sr + rw * sr;
+      if (p.g == 32)
+        sw = *reinterpret_cast<const uint32_t*>(sp + 4 * g2);
+      else
+        sw = *reinterpret_cast<const uint16_t*>(sp + (p.g == 64 ? 2 * g2 : 0));
+    } else if (p.g == 32) {
       sw = *reinterpret_cast<const uint32_t*>(S + rw * 16 + 2 * c0);
-    else
+    } else {
       sw = *reinterpret_cast<const uint16_t*>(S + rw * sg + 2 * (p.g == 64 ? c0 / 2 : kh));
+    }
     // every activation operand of the step is read before the first
     // dequantisation, so the LDS latency is paid once per step
     bf16x8 xb[8][TMV];
@@ -1156,7 +1195,7 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
 // compile-time counts.
 template <int B, int EPI, int WF = WF_INT4>
 __global__ __launch_bounds__(1024, 1) void gemm_nt_dec16_kernel(NtArgs p) {
-  static_assert(wf_4bit(WF), "4-bit weights");
+  static_assert(wf_4bit(WF) && !wf_tiled(WF), "row-major 4-bit weights");
   static_assert(EPI == EPI_ROT || EPI == EPI_PLAIN || EPI == EPI_BASE, "epilogue");
   using namespace ntd;
   constexpr int NST = 3, BMD = 64, TM = 2;

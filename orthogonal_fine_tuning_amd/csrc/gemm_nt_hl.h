@@ -19,6 +19,13 @@
 // weight stage, so that waiting for step s's activations leaves that
 // weight stage in flight: the weights get two steps of latency, the
 // activations (mostly L2 hits) one.
+//
+// Tiled INT4 storage (WF_INT4T, see oft_formats.h): a stage is one tile
+// column of each 64-row block, so each wave's 32 rows read 2 KB of codes and
+// 256/g bytes a row of scales, each contiguous in memory (row-major: 64-byte
+// pieces 8 KB apart and one 4-byte scale word per row and step).  The LDS
+// holds the stage's scales as the tiles do, 256/g bytes a row (4-byte slots
+// for g = 64 and 128).
 #pragma once
 
 #include "gemm_nt_dma.h"
@@ -46,8 +53,11 @@ __global__ __launch_bounds__(nth::NTHR, 2) void gemm_nt_hl_kernel(NtArgs p) {
   constexpr bool SWI = epi_swiglu(EPI);
   constexpr int BN = nth::BN, BM = nth::BM, XB = nth::XB, XROW = nth::XROW, WB = nth::WB, WCB = nth::WCB;
   constexpr int TM = BM / 32;
+  constexpr bool TILED = wf_tiled(WF);
   constexpr int XI = 2;   // activation copies per wave and step (16 rows)
-  constexpr int WC = 4;   // copies per wave and weight stage: 2 of codes, 2 of scale words
+  // copies per wave and weight stage: 2 of codes, then 2 of scale words
+  // (row-major) or 1 of the stage's scale slots (tiled)
+  constexpr int WC = TILED ? 3 : 4;
   __shared__ __attribute__((aligned(16))) uint8_t xs[2 * XB];
   __shared__ __attribute__((aligned(16))) uint8_t wsm[2 * WB];
 
@@ -110,18 +120,33 @@ __global__ __launch_bounds__(nth::NTHR, 2) void gemm_nt_hl_kernel(NtArgs p) {
   const uint32_t x_lds = lds_addr(xs) + (uint32_t)(2048 * wave);
   // weight codes: rows 32 wave + 16 i + lane / 4, 16-byte chunk lane % 4 of
   // the stage's 64 bytes
+  // (tiled: cbase is a multiple of 64, so its block starts at the same
+  // byte as its row-major row, and t4_code_off of the row relative to cbase
+  // is the offset from there)
   const uint8_t* wbase = wc + (size_t)cbase * (K / 2);
   uint32_t woff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int rw = 32 * wave + 16 * i + (lane >> 2);
-    woff[i] = (uint32_t)(crow(rw) * (K / 2) + 16 * ((lane & 3) ^ swz_w8(rw)));
+    const int cb = 16 * ((lane & 3) ^ swz_w8(rw));
+    woff[i] = TILED ? t4_code_off(crow(rw), cb, K) : (uint32_t)(crow(rw) * (K / 2) + cb);
   }
+  constexpr int WSTRIDE = TILED ? T4_TILE_BYTES : nth::WROW;  // bytes from one weight stage to the next
   const uint32_t w_lds = lds_addr(wsm) + (uint32_t)(2048 * wave);
   // scale words: lanes 0..31 copy the 4-byte word holding step s's scale(s)
   // of row 32 wave + lane
   const uint32_t sbase = (uint32_t)((cbase + crow(32 * wave + l32)) * kg);
   const uint32_t s_lds = lds_addr(wsm) + (uint32_t)(WCB + 32 * wave * 4);
+  // tiled scales: bytes a row in the LDS (8 for g = 32, else a 4-byte slot
+  // per row), the wave's copy (g = 32: lane 2 r + d takes 4-byte word d of
+  // row 32 wave + r; else lanes 0..31 one row each) and its source offset
+  // from the block of cbase, stage 0; stage u adds u * 16384 / g
+  const int srow = p.g == 32 ? 8 : 4;
+  const int s_rw = p.g == 32 ? 32 * wave + (lane >> 1) : 32 * wave + l32;
+  const uint32_t st_off = TILED ? t4_scale_off(crow(s_rw), 0, K, p.g) + (p.g == 32 ? 4u * (lane & 1) : 0u) : 0u;
+  const uint32_t st_lds = lds_addr(wsm) + (uint32_t)(WCB + 32 * wave * srow);
+  const uint32_t st_stride = (uint32_t)(16384 / p.g);
+  const uint8_t* ws_b = reinterpret_cast<const uint8_t*>(ws_h) + (size_t)cbase * kg * 2;
   auto sstep = [&](int s) { return gs >= 0 ? s << gs : s >> 1; };  // first scale of step s: 64 s / g
 
   auto issue_x = [&](int s, int c) {
@@ -137,7 +162,17 @@ __global__ __launch_bounds__(nth::NTHR, 2) void gemm_nt_hl_kernel(NtArgs p) {
   auto issue_w = [&](int u, int c) {
     const uint32_t b = (uint32_t)((u & 1) * WB);
     if (c < 2) {
-      copy16(w_lds + b + 1024 * c, wbase + (size_t)u * nth::WROW, woff[c]);
+      copy16(w_lds + b + 1024 * c, wbase + (size_t)u * WSTRIDE, woff[c]);
+    } else if constexpr (TILED) {
+      const uint8_t* src = ws_b + (size_t)u * st_stride;
+      if (p.g == 32)
+        copy4(st_lds + b, src, st_off);
+      else if (lane < 32) {
+        if (p.g == 64)
+          copy4(st_lds + b, src, st_off);
+        else
+          copy2(st_lds + b, src, st_off);
+      }
     } else {
       const int s = 2 * u + (c - 2);
       if (lane < 32) copy4(s_lds + b + (uint32_t)((c - 2) * BN * 4), ws_h, ((sbase + (uint32_t)sstep(s)) * 2u) & ~3u);
@@ -181,9 +216,15 @@ __global__ __launch_bounds__(nth::NTHR, 2) void gemm_nt_hl_kernel(NtArgs p) {
     const uint8_t* W = wsm + (u & 1) * WB;
     const uint4 c4 = *reinterpret_cast<const uint4*>(W + wrd + 16 * ((2 * t + g2) ^ wsw));
     const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
-    const uint32_t word = *reinterpret_cast<const uint32_t*>(W + WCB + t * BN * 4 + rw * 4);
-    const uint32_t idx = srd + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1);
-    const typename W4<WF>::S sc = W4<WF>::scale((uint16_t)(word >> (16 * (idx & 1))));
+    uint32_t word, half;
+    if constexpr (TILED) {
+      word = *reinterpret_cast<const uint32_t*>(W + WCB + rw * srow + (gs == 1 ? 4 * t : 0));
+      half = gs == 1 ? g2 : gs == 0 ? t : 0;
+    } else {
+      word = *reinterpret_cast<const uint32_t*>(W + WCB + t * BN * 4 + rw * 4);
+      half = (srd + (uint32_t)(gs == 1 ? 2 * s + g2 : gs == 0 ? s : s >> 1)) & 1;
+    }
+    const typename W4<WF>::S sc = W4<WF>::scale((uint16_t)(word >> (16 * half)));
     auto load_b = [&](int kk, bf16x8* b) {
 #pragma unroll
       for (int tm = 0; tm < TMV; ++tm) b[tm] = *reinterpret_cast<const bf16x8*>(X + xrd[tm] + 16 * ((xg + kk) ^ xsw));
@@ -203,7 +244,7 @@ __global__ __launch_bounds__(nth::NTHR, 2) void gemm_nt_hl_kernel(NtArgs p) {
       }
       if (kk >= 1 && nw) {
         issue_w(u + 1, kk - 1);
-        if (kk == 3) issue_w(u + 1, 3);
+        if (kk == 3 && WC > 3) issue_w(u + 1, 3);
       }
       if (kk + 1 < 4) aq[c ^ 1] = as_bf16x8(W4<WF>::dq(cw[kk + 1], sc));
     }

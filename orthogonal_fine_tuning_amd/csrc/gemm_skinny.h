@@ -25,6 +25,7 @@ template <bool AF32, int WF, int B, bool OUTF32, int TN = 1, int EPI = EPI_ROT>
 __global__ __launch_bounds__(256, 2) void gemm_nt_skinny_kernel(NtArgs p) {
   constexpr bool FP8 = WF == WF_FP8;
   static_assert(FP8 || wf_4bit(WF), "FP8 or 4-bit weights");
+  static_assert(!wf_tiled(WF), "row-major weights only");
   static_assert(EPI == EPI_ROT || EPI == EPI_BASE, "epilogue");
   __shared__ float red[3][TN][2][16][64];
 

@@ -683,27 +683,32 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.kslots = d.k;
     if (dma) {
       dim3 grid((d.I + ntd::BN / 2 - 1) / (ntd::BN / 2), (unsigned)L.max_tiles);
-      if (w16)
+      if constexpr (wf_tiled(W4F)) {  // (tiled INT4: H % 256 == 0 and I % 256 == 0)
+        hipLaunchKernelGGL((gemm_nt_hl_kernel<W4F, B, GEPI, true>), grid, dim3(nth::NTHR), 0, st, p);
+      } else if (w16) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, B, MOE_BM, GEPI, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
-      else if (d.H % 128 == 0)  // weight stages of two K steps (half-line copies)
+      } else if (d.H % 128 == 0) {  // weight stages of two K steps (half-line copies)
         hipLaunchKernelGGL((gemm_nt_hl_kernel<W4F, B, GEPI, true>), grid, dim3(nth::NTHR), 0, st, p);
-      else
+      } else {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, B, MOE_BM, GEPI, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
+      }
     } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.I + ntd::DEC_BN / 2 - 1) / (ntd::DEC_BN / 2), (unsigned)L.max_tiles64);
-      if (d.H % 256 == 0 && dec16)  // whole-line weight copies on 256-wide steps
+      if (d.H % 256 == 0 && dec16) {  // whole-line weight copies on 256-wide steps
         hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, GEPI, true, 16, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-      else if (d.H % 256 == 0)
+      } else if (d.H % 256 == 0) {
         hipLaunchKernelGGL((gemm_nt_dec4_kernel<B, GEPI, true, 64, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-      else if (dec16)
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, GEPI, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
-                           st, p);
-      else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, GEPI, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      } else if constexpr (!wf_tiled(W4F)) {
+        if (dec16)
+          hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, GEPI, true, 16>), grid, dim3(ntd::DEC_NTHR), 0,
+                             st, p);
+        else
+          hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, B, GEPI, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      }
     }
   }
   {
@@ -730,26 +735,31 @@ static hipError_t moe_fwd_gemms(const MoeDims& d, const MoeFwdPtrs& q, const Moe
     p.kslots = 0;
     if (dma) {
       dim3 grid((d.H + ntd::BN - 1) / ntd::BN, (unsigned)L.max_tiles);
-      if (w16)
+      if constexpr (wf_tiled(W4F)) {
+        hipLaunchKernelGGL((gemm_nt_hl_kernel<W4F, 32, EPI_PLAIN, true>), grid, dim3(nth::NTHR), 0, st, p);
+      } else if (w16) {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<WF_BF16, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
-      else if (d.I % 128 == 0)  // weight stages of two K steps (half-line copies)
+      } else if (d.I % 128 == 0) {  // weight stages of two K steps (half-line copies)
         hipLaunchKernelGGL((gemm_nt_hl_kernel<W4F, 32, EPI_PLAIN, true>), grid, dim3(nth::NTHR), 0, st, p);
-      else
+      } else {
         hipLaunchKernelGGL((gemm_nt_dma_kernel<W4F, 32, MOE_BM, EPI_PLAIN, false, true>), grid,
                            dim3(ntd::NTHR), 0, st, p);
+      }
     } else {
       p.tiles = list64;
       p.ntiles = ntiles64;
       dim3 grid((d.H + ntd::DEC_BN - 1) / ntd::DEC_BN, (unsigned)L.max_tiles64);
-      if (d.I % 256 == 0 && dec16)
+      if (d.I % 256 == 0 && dec16) {
         hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 16, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-      else if (d.I % 256 == 0)
+      } else if (d.I % 256 == 0) {
         hipLaunchKernelGGL((gemm_nt_dec4_kernel<32, EPI_PLAIN, true, 64, W4F>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-      else if (dec16)
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, 32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
-      else
-        hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      } else if constexpr (!wf_tiled(W4F)) {
+        if (dec16)
+          hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, 32, EPI_PLAIN, true, 16>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+        else
+          hipLaunchKernelGGL((gemm_nt_dec_kernel<W4F, 32, EPI_PLAIN, true>), grid, dim3(ntd::DEC_NTHR), 0, st, p);
+      }
     }
   }
   const size_t n8 = (size_t)d.T * d.H / 8;
@@ -768,11 +778,15 @@ hipError_t launch_moe_fwd(const MoeDims& d, const float* logits, const MoeFwdPtr
   if (err != hipSuccess) return err;
   if (d.T == 0) return hipSuccess;
   if (base)  // the frozen base alone: the block size plays no part
-    return d.wf == WF_FP4 ? moe_fwd_gemms<32, WF_FP4, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st)
-                          : moe_fwd_gemms<32, WF_INT4, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st);
+    return d.wf == WF_FP4     ? moe_fwd_gemms<32, WF_FP4, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st)
+           : d.wf == WF_INT4T ? moe_fwd_gemms<32, WF_INT4T, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st)
+                              : moe_fwd_gemms<32, WF_INT4, EPI_BASE_SWIGLU>(d, q, rt, ws, L, st);
   if (d.wf == WF_FP4)
     return d.b == 32 ? moe_fwd_gemms<32, WF_FP4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st)
                      : moe_fwd_gemms<16, WF_FP4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st);
+  if (d.wf == WF_INT4T)
+    return d.b == 32 ? moe_fwd_gemms<32, WF_INT4T, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st)
+                     : moe_fwd_gemms<16, WF_INT4T, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st);
   return d.b == 32 ? moe_fwd_gemms<32, WF_INT4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st)
                    : moe_fwd_gemms<16, WF_INT4, EPI_ROT_SWIGLU>(d, q, rt, ws, L, st);
 }
@@ -821,13 +835,15 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     // experts averaging at least 64 rows: the copy-ring NN kernel (faster
     // there; with fewer rows the two-workgroups-per-CU kernel is)
     int nkt;  // column tiles = partial sums of dw per position
-    if (W4F == WF_INT4 && !w16 && d.I % nnq::BKO == 0) {
+    if (wf_tiled(W4F) || (W4F == WF_INT4 && !w16 && d.I % nnq::BKO == 0)) {
       // INT4: codes and scales to LDS by copies, transposed 4-bit operand
       // reads, every code dequantised by one wave
       ProfScope prof(st, "moe.dA");
       dim3 grid(d.I / nnq::BKO, (unsigned)L.max_tiles);
-      hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_SWIGLU_BWD, true>), grid, dim3(nnq::NTHR), 0, st, p);
+      hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_SWIGLU_BWD, true, wf_tiled(W4F)>), grid, dim3(nnq::NTHR), 0, st, p);
       nkt = d.I / nnq::BKO;
+    } else if constexpr (wf_tiled(W4F)) {
+      nkt = 0;  // (not reached: tiled INT4 takes the branch above)
     } else if ((long)d.T * d.k >= 64L * d.E) {
       ProfScope prof(st, "moe.dA");
       dim3 grid((d.I + nnd::BKO - 1) / nnd::BKO, (unsigned)L.max_tiles);
@@ -882,10 +898,10 @@ static hipError_t moe_bwd_t(const MoeDims& d, const MoeBwdPtrs& q, const MoeRout
     p.offsets = rt.offsets;
     p.perm = rt.perm;
     p.kslots = 0;
-    if (W4F == WF_INT4 && !w16 && d.H % nnq::BKO == 0) {
+    if (wf_tiled(W4F) || (W4F == WF_INT4 && !w16 && d.H % nnq::BKO == 0)) {
       dim3 grid(d.H / nnq::BKO, (unsigned)L.max_tiles);
-      hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_STORE, true>), grid, dim3(nnq::NTHR), 0, st, p);
-    } else {
+      hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_STORE, true, wf_tiled(W4F)>), grid, dim3(nnq::NTHR), 0, st, p);
+    } else if constexpr (!wf_tiled(W4F)) {
       dim3 grid((d.H + nn::BKO - 1) / nn::BKO, (unsigned)L.max_tiles);
       if (w16)
         hipLaunchKernelGGL((gemm_nn_kernel<MOE_BM, false, WF_BF16, B, PRO_NONE, EPI_STORE, true, MOE_NBUF>), grid,
@@ -907,6 +923,8 @@ hipError_t launch_moe_bwd(const MoeDims& d, const MoeBwdPtrs& q, const MoeRoutin
                           const MoeWs& L, hipStream_t st) {
   if (d.wf == WF_FP4)
     return d.b == 32 ? moe_bwd_t<32, WF_FP4>(d, q, rt, ws, L, st) : moe_bwd_t<16, WF_FP4>(d, q, rt, ws, L, st);
+  if (d.wf == WF_INT4T)
+    return d.b == 32 ? moe_bwd_t<32, WF_INT4T>(d, q, rt, ws, L, st) : moe_bwd_t<16, WF_INT4T>(d, q, rt, ws, L, st);
   return d.b == 32 ? moe_bwd_t<32, WF_INT4>(d, q, rt, ws, L, st) : moe_bwd_t<16, WF_INT4>(d, q, rt, ws, L, st);
 }
 

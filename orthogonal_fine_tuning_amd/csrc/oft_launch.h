@@ -48,6 +48,8 @@ hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t
 // fmt: a WF_* value (numbered as the OFT_W_* formats of the C ABI)
 hipError_t launch_dequant(int fmt, int rows, int cols, int g, const uint8_t* codes,
                           const void* scales, uint16_t* out, hipStream_t st);
+hipError_t launch_pack_t4(int count, int rows, int cols, int g, const uint8_t* codes, const uint16_t* scales,
+                          uint8_t* codes_t, uint16_t* scales_t, hipStream_t st);
 
 // Dense layer.  xf32: x / y / dx are fp32 (else bf16); wf: the weight
 // format (the 4-bit ones with group g).

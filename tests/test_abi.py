@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = _lib.load()
-    assert lib.oft_abi_version() == 7
+    assert lib.oft_abi_version() == 8
     for s in range(-6, 1):
         assert lib.oft_status_str(s)
     assert b"unknown" in lib.oft_status_str(-99)
@@ -167,6 +167,10 @@ def _moe(**kw):
     (dict(w_fmt=2, g=0, I=96), _lib.OFT_ESHAPE),
     (dict(w_fmt=3), _lib.OFT_OK),  # FP4 experts
     (dict(w_fmt=3, g=0), _lib.OFT_EUNSUPPORTED),
+    (dict(w_fmt=4, H=512, I=256), _lib.OFT_OK),  # tiled INT4: H, I multiples of 256
+    (dict(w_fmt=4, H=384, I=256), _lib.OFT_ESHAPE),
+    (dict(w_fmt=4, H=512, I=128), _lib.OFT_ESHAPE),
+    (dict(w_fmt=4, H=512, I=256, g=16), _lib.OFT_EUNSUPPORTED),
 ])
 def test_moe_validation(kw, code):
     d = _moe(**kw)
@@ -179,6 +183,8 @@ def test_moe_validation(kw, code):
     (dict(T=262077, E=16, k=4), _lib.OFT_EUNSUPPORTED),  # 65536 work-list tiles along grid y
     (dict(H=1 << 17), _lib.OFT_EUNSUPPORTED),
     (dict(I=1 << 17), _lib.OFT_EUNSUPPORTED),
+    (dict(H=1 << 16, I=(1 << 15) - 64), _lib.OFT_OK),      # I H < 2^31: 32-bit code offsets in an expert
+    (dict(H=1 << 16, I=1 << 15), _lib.OFT_EUNSUPPORTED),
 ])
 def test_moe_size_range(kw, code):
     d = _moe(**kw)
@@ -293,6 +299,10 @@ def test_every_gpu_test_shape_passes_validation():
     for c in moe:
         d = oft.moe_desc(c.T, c.E, c.k, c.H, c.I, c.g, c.b, c.chunk, 0, w_fmt=wf[c.w_fmt])
         assert lib.oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == _lib.OFT_OK, c.name
+    for name in moe_m.TILED:
+        c = moe_m.SMALL[name]
+        d = oft.moe_desc(c.T, c.E, c.k, c.H, c.I, c.g, c.b, c.chunk, 0, w_fmt=oft.OFT_W_INT4_TILED)
+        assert lib.oft_moe_workspace_bytes(C.byref(d), 0, C.byref(n)) == _lib.OFT_OK, name
 
 
 def test_logprob_diff_and_moe_base_validation():
@@ -328,3 +338,21 @@ def test_noalloc_bwd_rejects_beyond_its_scratch_without_a_gpu():
     assert lib.oft_linear_bwd_noalloc(C.byref(big), ok, ok, ok, ok, ok, ok, ok, ok, None) == _lib.OFT_EWORKSPACE
     assert lib.oft_linear_bwd_noalloc(C.byref(_desc(b=8)), ok, ok, ok, ok, ok, ok, ok, ok, None) == \
         _lib.OFT_EUNSUPPORTED
+
+
+def test_pack_int4_tiled_validation():
+    """Host-side checks of oft_pack_int4_tiled (no GPU work: every call fails
+    validation, or has nothing to do)."""
+    lib = _lib.load()
+    a, b, c, d = (C.c_void_p(0x10000 * i) for i in (1, 2, 3, 4))
+    f = lib.oft_pack_int4_tiled
+    assert f(0, 64, 128, 32, None, None, None, None, None) == _lib.OFT_OK  # nothing to pack
+    assert f(1, 96, 128, 32, a, b, c, d, None) == _lib.OFT_ESHAPE    # rows % 64
+    assert f(1, 64, 192, 64, a, b, c, d, None) == _lib.OFT_ESHAPE    # cols % 128
+    assert f(1, 64, 128, 16, a, b, c, d, None) == _lib.OFT_EUNSUPPORTED
+    assert f(-1, 64, 128, 32, a, b, c, d, None) == _lib.OFT_EINVAL
+    assert f(1, 64, 128, 32, None, b, c, d, None) == _lib.OFT_EINVAL
+    assert f(1, 64, 128, 32, C.c_void_p(0x10008), b, c, d, None) == _lib.OFT_EINVAL  # misaligned
+    assert f(1, 64, 128, 32, a, b, C.c_void_p(0x10000 + 2048), d, None) == _lib.OFT_EINVAL  # codes overlap
+    assert f(1, 64, 128, 32, a, b, c, C.c_void_p(0x20000 + 256), None) == _lib.OFT_EINVAL  # scales overlap
+    assert f(1, 1 << 16, 1 << 16, 32, a, b, c, d, None) == _lib.OFT_EUNSUPPORTED  # 32-bit offsets

@@ -193,14 +193,29 @@ def _bf16_weights(inp):
     return {"wgu_codes": wgu, "wgu_scales": None, "wd_codes": wd, "wd_scales": None}
 
 
-def _run_moe(inp, want_bwd=True, bf16_weights=False):
+def _tiled_weights(inp):
+    """The experts' INT4 weights in the tiled storage (oft_pack_int4_tiled)."""
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    cfg = inp["cfg"]
+    assert cfg.w_fmt == "int4"
+    out = {}
+    for c, s, rows, cols in (("wgu_codes", "wgu_scales", 2 * cfg.I, cfg.H), ("wd_codes", "wd_scales", cfg.H, cfg.I)):
+        codes, scales = dev(inp[c]), dev(inp[s])
+        out[c], out[s] = torch.empty_like(codes), torch.empty_like(scales)
+        oft.oft_pack_int4_tiled(cfg.E, rows, cols, cfg.g, codes, scales, out[c], out[s])
+    return out
+
+
+def _run_moe(inp, want_bwd=True, bf16_weights=False, tiled=False):
     import torch
     import orthogonal_fine_tuning_amd as oft
 
     cfg = inp["cfg"]
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
     P = T * k
-    w_fmt = oft.OFT_W_BF16 if bf16_weights else _wfmt(oft, cfg.w_fmt)
+    w_fmt = oft.OFT_W_BF16 if bf16_weights else oft.OFT_W_INT4_TILED if tiled else _wfmt(oft, cfg.w_fmt)
     d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=w_fmt)
     rtt = _routing_tensors(T, E, k)
     rt = oft.moe_routing(**rtt)
@@ -210,6 +225,8 @@ def _run_moe(inp, want_bwd=True, bf16_weights=False):
     oft.cayley_build(dev(inp["p"]), nblk, b, Rf, Rops)
     if bf16_weights:
         W = _bf16_weights(inp)
+    elif tiled:
+        W = _tiled_weights(inp)
     else:
         W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
     hs = torch.empty((max(P, 1), 2 * I), dtype=torch.int16, device="cuda")
@@ -436,6 +453,23 @@ def test_moe_full_size_tiles(name):
     gdq = host(out["dq"])
     for e in np.nonzero(counts == 0)[0]:
         assert np.all(gdq[e] == 0.0)
+    _check_tiled_same(name, inp, out)
+
+
+def _check_tiled_same(name, inp, out):
+    """INT4 shapes with H and I multiples of 256: the tiled storage (as the
+    benchmark runs them) gives the row-major run's every output bit for bit
+    (the same kernels' arithmetic in the same order; only copy addresses
+    differ)."""
+    cfg = inp["cfg"]
+    if cfg.w_fmt != "int4" or cfg.H % 256 or cfg.I % 256:
+        return
+    print(f"[moe full size] {name}: tiled storage", flush=True)
+    t = _run_moe(inp, tiled=True)
+    P = cfg.T * cfg.k
+    for key in ("y", "dx", "dq", "dw"):
+        assert np.array_equal(host(t[key]), host(out[key])), key
+    assert np.array_equal(host(t["hs"])[:P], host(out["hs"])[:P])
 
 
 @pytest.mark.parametrize("name", ["moe_1t_decode", "moe_1t_decode_fp4"])
@@ -456,6 +490,7 @@ def test_moe_decode_full(name):
     gdq = host(out["dq"])
     for e in np.nonzero(counts == 0)[0]:
         assert np.all(gdq[e] == 0.0)
+    _check_tiled_same(name, inp, out)
 
 
 @pytest.mark.parametrize("name", ["moe_small_b32", "moe_decode16_b32", "moe_30b_a3b"])
@@ -483,16 +518,17 @@ def test_moe_chunk_size_invariance(name):
 
 
 # ------------------------------------------------------------ reference policy
-def _run_moe_base(inp, with_h=True):
+def _run_moe_base(inp, with_h=True, tiled=False):
     import torch
     import orthogonal_fine_tuning_amd as oft
 
     cfg = inp["cfg"]
     T, E, k, H, I, b = cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.b
-    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=_wfmt(oft, cfg.w_fmt))
+    w_fmt = oft.OFT_W_INT4_TILED if tiled else _wfmt(oft, cfg.w_fmt)
+    d = oft.moe_desc(T, E, k, H, I, cfg.g, b, cfg.chunk, 0, w_fmt=w_fmt)
     rtt = _routing_tensors(T, E, k)
     rt = oft.moe_routing(**rtt)
-    W = {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
+    W = _tiled_weights(inp) if tiled else {n: dev(inp[n]) for n in ("wgu_codes", "wgu_scales", "wd_codes", "wd_scales")}
     hs = torch.full((max(T * k, 1), 2 * I), -7, dtype=torch.int16, device="cuda") if with_h else None
     y = torch.empty((max(T, 1), H), dtype=torch.int16, device="cuda")
     nbf = oft.oft_moe_workspace_bytes(d, oft.OFT_PASS_FWD)
@@ -541,3 +577,73 @@ def test_moe_base_forward_full_size_decode():
     e_y = err(bf16_to_f64(host(out["y"])), y_ref)
     print(f"  err y={e_y:.2e}", flush=True)
     assert e_y <= TOL
+
+
+# ------------------------------------------------------------ tiled INT4 storage
+# INT4 shapes with H and I multiples of 256 (the tiled storage's constraint):
+# 128-row copy-ring tiles (g = 32, 64, 128; ragged expert tiles) and the 16-
+# and 64-row weight streams
+TILED = ["moe_w16_b16_g64", "moe_w16_g32_ragged", "moe_t4_g128", "moe_decode16_b32", "moe_decode16_b16_g64",
+         "moe_decode16_g128", "moe_dec64_g128"]
+SMALL["moe_t4_g128"] = MoEConfig("moe_t4_g128", T=300, E=4, k=2, H=512, I=512, g=128, chunk=3, b=32,
+                                 q_std=0.05, bias_std=0.5)
+
+
+@pytest.mark.parametrize("name", TILED)
+def test_moe_tiled_storage(name):
+    """The tiled storage of the same INT4 weights: every output of forward
+    and backward equals the row-major run's bit for bit (so it meets the
+    oracle as that run does; checked here too)."""
+    cfg = SMALL[name]
+    print(f"[moe tiled] {name}", flush=True)
+    inp = make_moe(cfg, seed=4)
+    inp["logits"] = inp["logits"].copy()
+    inp["logits"][:, 1] -= 100.0
+    inp["logits"][:, 2] += 3.0
+    ref = _run_moe(inp)
+    out = _run_moe(inp, tiled=True)
+    P = cfg.T * cfg.k
+    for key in ("y", "dx", "dq", "dw"):
+        assert np.array_equal(host(out[key]), host(ref[key])), key
+    assert np.array_equal(host(out["hs"])[:P], host(ref["hs"])[:P])
+    y_ref, H_ref, rt = omoe.forward(inp)
+    dX_ref, dp_ref, dw_ref = omoe.backward(inp, rt)
+    e = max(err(bf16_to_f64(host(out["y"])), y_ref), err(bf16_to_f64(host(out["dx"])), dX_ref),
+            err(host(out["dq"]), dp_ref), err(host(out["dw"]), dw_ref))
+    print(f"  bit-identical to row-major; max err vs oracle {e:.2e}", flush=True)
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("name", ["moe_w16_g32_ragged", "moe_decode16_b32"])
+def test_moe_tiled_base_forward(name):
+    """The reference-policy forward on tiled storage: the row-major run's y
+    and h bit for bit."""
+    cfg = SMALL[name]
+    inp = make_moe(cfg, seed=6)
+    ref = _run_moe_base(inp)
+    out = _run_moe_base(inp, tiled=True)
+    P = cfg.T * cfg.k
+    assert np.array_equal(host(out["y"]), host(ref["y"]))
+    assert np.array_equal(host(out["hs"])[:P], host(ref["hs"])[:P])
+
+
+@pytest.mark.parametrize("count,rows,cols,g", [(1, 64, 128, 32), (3, 192, 384, 64), (2, 128, 256, 128),
+                                               (5, 64, 512, 32)])
+def test_pack_int4_tiled_layout(count, rows, cols, g):
+    """oft_pack_int4_tiled against the storage's definition written as array
+    reshapes: [rows, cols/2] bytes -> tiles of 64 rows x 64 bytes, tile
+    column fastest; [rows, cols/g] slots -> tiles of 64 rows x 128/g slots."""
+    import torch
+    import orthogonal_fine_tuning_amd as oft
+
+    rng = np.random.default_rng(count * 1000 + rows + cols + g)
+    codes = rng.integers(0, 256, size=(count, rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 1 << 16, size=(count, rows, cols // g), dtype=np.uint16)
+    ct = torch.empty(codes.size, dtype=torch.uint8, device="cuda")
+    st = torch.empty(scales.size, dtype=torch.int16, device="cuda")
+    oft.oft_pack_int4_tiled(count, rows, cols, g, dev(codes), dev(scales.view(np.int16)), ct, st)
+    torch.cuda.synchronize()
+    want_c = codes.reshape(count, rows // 64, 64, cols // 128, 64).transpose(0, 1, 3, 2, 4).reshape(-1)
+    want_s = scales.reshape(count, rows // 64, 64, cols // 128, 128 // g).transpose(0, 1, 3, 2, 4).reshape(-1)
+    assert np.array_equal(host(ct), want_c)
+    assert np.array_equal(host(st).view(np.uint16), want_s)
