@@ -195,11 +195,13 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
 
-  // TMV (a std::integral_constant): 32-row tiles that hold rows
-  auto compute = [&](int s, auto tmv_c) {
-    constexpr int TMV = decltype(tmv_c)::value;
+  // TMV (a std::integral_constant): 32-row tiles that hold rows; ST: the
+  // ring stage of step s (s % NST), a constant so that the stage offset is
+  // the LDS reads' immediate rather than per-address arithmetic
+  auto compute = [&](auto tmv_c, auto st_c) {
+    constexpr int TMV = decltype(tmv_c)::value, ST = decltype(st_c)::value;
     if constexpr (TMV > 0) {
-      const uint8_t* S = smem + (s % NST) * STAGE;
+      const uint8_t* S = smem + ST * STAGE;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         // codes of rows 32 hf + 16 g2 + [0, 16) of the lane's column, and
@@ -228,15 +230,22 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
     }
   };
 
-  // every wave takes the same barriers, whatever its TMV
+  // every wave takes the same barriers, whatever its TMV; the step loop is
+  // unrolled by the ring depth
+  static_assert(NST == 3, "ring stages");
   auto run = [&](auto tmv_c) {
     issue(0);
     if (ns > 1) issue(1);
-    for (int s = 0; s < ns; ++s) {
+    auto one = [&](int s, auto st_c) {
       // copies of step s + 1 may stay in flight
       ntd::wait_copies_barrier_n(s + 1 < ns ? vw : 0);
       if (s + 2 < ns) issue(s + 2);
-      compute(s, tmv_c);
+      compute(tmv_c, st_c);
+    };
+    for (int s = 0; s < ns; s += NST) {
+      one(s, std::integral_constant<int, 0>{});
+      if (s + 1 < ns) one(s + 1, std::integral_constant<int, 1>{});
+      if (s + 2 < ns) one(s + 2, std::integral_constant<int, 2>{});
     }
   };
   if (nrows > 96)
