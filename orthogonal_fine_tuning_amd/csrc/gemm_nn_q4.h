@@ -232,21 +232,16 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
 
   // every wave takes the same barriers, whatever its TMV; the step loop is
   // unrolled by the ring depth
-  static_assert(NST == 3, "ring stages");
+  static_assert(NST == 3, "two steps of copies in flight");
   auto run = [&](auto tmv_c) {
     issue(0);
     if (ns > 1) issue(1);
-    auto one = [&](int s, auto st_c) {
+    ring_steps<NST>(ns, [&](int s, auto st_c) {
       // copies of step s + 1 may stay in flight
       ntd::wait_copies_barrier_n(s + 1 < ns ? vw : 0);
       if (s + 2 < ns) issue(s + 2);
       compute(tmv_c, st_c);
-    };
-    for (int s = 0; s < ns; s += NST) {
-      one(s, std::integral_constant<int, 0>{});
-      if (s + 1 < ns) one(s + 1, std::integral_constant<int, 1>{});
-      if (s + 2 < ns) one(s + 2, std::integral_constant<int, 2>{});
-    }
+    });
   };
   if (nrows > 96)
     run(std::integral_constant<int, 4>{});

@@ -1120,9 +1120,9 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
 
-  auto compute = [&](int s, auto tmv_c) {
+  auto compute = [&](auto tmv_c, auto st_c) {  // st_c: the ring stage, a constant
     constexpr int TMV = decltype(tmv_c)::value;
-    const uint8_t* W = smem + (s % NST) * SB;
+    const uint8_t* W = smem + decltype(st_c)::value * SB;
     const uint8_t* S = W + WBY;
     const uint8_t* X = S + SBY;
     const int c0 = 4 * kh + 2 * g2;  // this lane's two 16-byte chunks: in-features 32 c0 .. 32 c0 + 63
@@ -1165,13 +1165,13 @@ __global__ __launch_bounds__(ntd::DEC_NTHR, BMD == 16 ? 2 : 1) void gemm_nt_dec4
   auto run = [&](auto tmv_c) {
     const int pre = nks < NST - 1 ? nks : NST - 1;
     for (int s = 0; s < pre; ++s) issue(s);
-    for (int s = 0; s < nks; ++s) {
+    ring_steps<NST>(nks, [&](int s, auto st_c) {
       // copies of steps s + 1 .. s + NST - 2 may stay in flight
       const int ahead = min(NST - 2, nks - 1 - s);
       wait_copies_barrier_n(per * ahead);
       if (s + NST - 1 < nks) issue(s + NST - 1);
-      compute(s, tmv_c);
-    }
+      compute(tmv_c, st_c);
+    });
   };
   if (BMD == 64 && nrows > 32)
     run(std::integral_constant<int, TM>{});
@@ -1277,9 +1277,9 @@ __global__ __launch_bounds__(1024, 1) void gemm_nt_dec16_kernel(NtArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.0f;
 
-  auto compute = [&](int s, auto tmv_c) {
+  auto compute = [&](auto tmv_c, auto st_c) {  // st_c: the ring stage, a constant
     constexpr int TMV = decltype(tmv_c)::value;
-    const uint8_t* St = smem + (s % NST) * SB;
+    const uint8_t* St = smem + decltype(st_c)::value * SB;
     const uint4 cw4 = *reinterpret_cast<const uint4*>(St + w_rd);
     const uint16_t sbits = *reinterpret_cast<const uint16_t*>(St + s_rd);
     // every activation operand of the step is read before the first
@@ -1304,15 +1304,15 @@ __global__ __launch_bounds__(1024, 1) void gemm_nt_dec16_kernel(NtArgs p) {
     constexpr int PER = 3 + (decltype(sc_c)::value ? 1 : 0);  // copies per step of this wave
     const int pre = nks < NST - 1 ? nks : NST - 1;
     for (int s = 0; s < pre; ++s) issue(s, sc_c);
-    for (int s = 0; s < nks; ++s) {
+    ring_steps<NST>(nks, [&](int s, auto st_c) {
       // the copies of step s + 1 may stay in flight
       if (s + 1 < nks)
         wait_copies_barrier_n(PER);
       else
         wait_copies_barrier_n(0);
       if (s + NST - 1 < nks) issue(s + NST - 1, sc_c);
-      compute(s, tmv_c);
-    }
+      compute(tmv_c, st_c);
+    });
   };
   if (nrows > 32) {
     if (wave < nsw)

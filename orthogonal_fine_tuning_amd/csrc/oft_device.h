@@ -15,6 +15,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
+#include <utility>
+
 #include "oft_formats.h"
 
 namespace oft {
@@ -158,6 +161,18 @@ __device__ __forceinline__ bool grouped_tile(int ntiles, int& cx, int& ty) {
   ty = (int)(L / gx);
   cx = (int)(L % gx);
   return true;
+}
+
+// Steps 0 .. n-1 of a loop over an NST-deep LDS ring, unrolled by NST:
+// f(s, integral_constant<int, s % NST>), so that each step's ring stage is a
+// compile-time constant (its byte offset the LDS instructions' immediate).
+template <int NST, class F, int... I>
+__device__ __forceinline__ void ring_steps_impl(int n, F& f, std::integer_sequence<int, I...>) {
+  for (int s = 0; s < n; s += NST) ((s + I < n ? (f(s + I, std::integral_constant<int, I>{}), 0) : 0), ...);
+}
+template <int NST, class F>
+__device__ __forceinline__ void ring_steps(int n, F f) {
+  ring_steps_impl<NST>(n, f, std::make_integer_sequence<int, NST>{});
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
