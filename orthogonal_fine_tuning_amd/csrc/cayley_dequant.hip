@@ -6,12 +6,13 @@
 // as R = (I + Q)(I - Q)^-1 = 2 (I - Q)^-1 - I from the skew-symmetric Q.
 //
 // Layout of the solve: in-place Gauss-Jordan on A = I - Q with row
-// ownership.  Lane r of a b-lane group holds row r of A in registers, so a
-// wave solves 64 / b blocks at once and a block needs b, not 2b, lanes (the
-// in-place form keeps the growing inverse in the columns already
-// eliminated).  Each pivot step publishes the pivot row through LDS and
-// every lane applies one fused multiply-add per element.  No pivot search is
-// needed: the symmetric part of A is I, so every pivot is >= 1.
+// ownership (the in-place form keeps the growing inverse in the columns
+// already eliminated).  Many blocks: a block per 16-lane row of a wave, each
+// lane holding b / 16 rows of A in registers; a pivot step broadcasts the
+// pivot row from its owner lane by DPP and every lane applies one fused
+// multiply-add per element it holds.  Few blocks (a dense layer's build):
+// two lanes per row, the pivot row published through LDS.  No pivot search
+// is needed: the symmetric part of A is I, so every pivot is >= 1.
 #include <utility>
 
 #include "oft_device.h"
@@ -36,19 +37,36 @@ __device__ __forceinline__ void for_each_index(F& f, std::integer_sequence<int, 
   (f(std::integral_constant<int, S>{}), ...);
 }
 
+// value x of lane n of this lane's 16-lane row (DPP row_newbcast)
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(N >= 0 && N < 16, "row lane");
+  // (every lane's source exists, so bound_ctrl changes nothing; with it
+  // the move needs no old value)
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, true));
+}
+
+// A block per 16-lane row of the wave (four per wave): lane (sub, qd), qd =
+// lane % 16, holds rows qd + 16 t (t = 0 .. RPL - 1, RPL = B / 16) of block
+// blk0 + sub.  A pivot step broadcasts each element of the pivot row from
+// its owner lane to the row by DPP (row_newbcast) just before the
+// multiply-adds that use it, so the step loop touches no LDS and needs no
+// synchronisation; each element sees the same operations in the same order
+// as with any other row ownership.
 template <int B>
 __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__ q, int nblk,
                                                     float* __restrict__ Rf, uint16_t* __restrict__ Rops) {
-  constexpr int PER = 64 / B;  // blocks per wave
+  constexpr int LPB = 16;         // lanes per block: one DPP row
+  constexpr int RPL = B / LPB;    // rows per lane
+  constexpr int PER = 64 / LPB;   // blocks per wave
   constexpr int NP = B * (B - 1) / 2;
   constexpr int TP = B + 2;  // row pitch (bf16) of the transpose tile
   // the parameters of the wave's blocks, later the bf16 transpose of R
   constexpr int STAGE = PER * NP * 4 > PER * B * TP * 2 ? PER * NP * 4 : PER * B * TP * 2;
   __shared__ __attribute__((aligned(16))) uint8_t stage[STAGE];
-  __shared__ __attribute__((aligned(16))) float prow[PER][B];  // pivot row
 
   const int lane = threadIdx.x;
-  const int sub = lane / B, r = lane % B;
+  const int sub = lane / LPB, qd = lane % LPB;
   const int blk0 = blockIdx.x * PER;
   const int nv = min(PER, nblk - blk0);  // blocks of this wave
   const int blk = blk0 + sub;
@@ -92,78 +110,89 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
 
   // A[r][c] = delta_rc - Q[r][c], Q[r][c] = p(r, c) above the diagonal and
   // -p(c, r) below (row-major upper-triangle order of p)
-  float a[B];
+  float a[RPL][B];
   const float* qb = qs + sub * NP;
 #pragma unroll
-  for (int c = 0; c < B; ++c) {
-    const int lo = c < r ? c : r, hi = c < r ? r : c;
-    const float v = (c == r || sub >= nv) ? 0.0f : qb[lo * B - lo * (lo + 1) / 2 + (hi - lo - 1)];
-    a[c] = c == r ? 1.0f : (c > r ? -v : v);
+  for (int t = 0; t < RPL; ++t) {
+    const int r = qd + LPB * t;
+#pragma unroll
+    for (int c = 0; c < B; ++c) {
+      const int lo = c < r ? c : r, hi = c < r ? r : c;
+      const float v = (c == r || sub >= nv) ? 0.0f : qb[lo * B - lo * (lo + 1) / 2 + (hi - lo - 1)];
+      a[t][c] = c == r ? 1.0f : (c > r ? -v : v);
+    }
   }
   __syncthreads();  // stage is reused for the transpose at the end
 
   // one pivot step; the step index is a compile-time constant so that every
-  // a[] access stays a register
+  // a[][] access stays a register and the owner lane is the DPP operand
   auto step = [&](auto sc) {
     constexpr int s = decltype(sc)::value;
-    if (r == s) {
-#pragma unroll
-      for (int j = 0; j < B; j += 4)
-        *reinterpret_cast<float4*>(&prow[sub][j]) = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
-    }
-    wave_sync();
-    float pr[B];
-#pragma unroll
-    for (int j = 0; j < B; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(&prow[sub][j]);
-      pr[j] = v.x;
-      pr[j + 1] = v.y;
-      pr[j + 2] = v.z;
-      pr[j + 3] = v.w;
-    }
+    constexpr int ts = s / LPB, own = s % LPB;  // the pivot row: slot ts of lane own
+    const bool owner = qd == own;
     // 1 / pivot: hardware reciprocal and one Newton step
-    const float piv = pr[s];
+    const float piv = row_bcast<own>(a[ts][s]);
     float rp = __builtin_amdgcn_rcpf(piv);
     rp = fmaf(rp, fmaf(-piv, rp, 1.0f), rp);
     // pivot row: a_sj / p; other rows: a_rj - (a_rs / p) a_sj; column s of
-    // the inverse: 1 / p on the pivot row, -a_rs / p elsewhere
-    const float f = a[s];
-    const float g = r == s ? 1.0f - rp : f * rp;
+    // the inverse: 1 / p on the pivot row, -a_rs / p elsewhere.  Each pivot
+    // element is taken from its owner before any update of its column.
+    float g[RPL];
 #pragma unroll
-    for (int j = 0; j < B; ++j)
-      if (j != s) a[j] = fmaf(-g, pr[j], a[j]);
-    a[s] = r == s ? rp : -g;
-    wave_sync();
+    for (int t = 0; t < RPL; ++t) g[t] = (t == ts && owner) ? 1.0f - rp : a[t][s] * rp;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (j == s) continue;
+      const float pj = row_bcast<own>(a[ts][j]);
+#pragma unroll
+      for (int t = 0; t < RPL; ++t) a[t][j] = fmaf(-g[t], pj, a[t][j]);
+    }
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) a[t][s] = (t == ts && owner) ? rp : -g[t];
   };
   for_each_index(step, std::make_integer_sequence<int, B>{});
 
-  // lane r holds row r of A^-1; R = 2 A^-1 - I
+  // row r = qd + LPB t of A^-1 in a[t]; R = 2 A^-1 - I
 #pragma unroll
-  for (int j = 0; j < B; ++j) a[j] = 2.0f * a[j] - (j == r ? 1.0f : 0.0f);
+  for (int t = 0; t < RPL; ++t)
+#pragma unroll
+    for (int j = 0; j < B; ++j) a[t][j] = 2.0f * a[t][j] - (j == qd + LPB * t ? 1.0f : 0.0f);
   if (sub < nv) {
-    float4* dst = reinterpret_cast<float4*>(Rf + (size_t)blk * B * B + r * B);
 #pragma unroll
-    for (int j = 0; j < B; j += 4) dst[j / 4] = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
+    for (int t = 0; t < RPL; ++t) {
+      float4* dst = reinterpret_cast<float4*>(Rf + (size_t)blk * B * B + (qd + LPB * t) * B);
+#pragma unroll
+      for (int j = 0; j < B; j += 4) dst[j / 4] = make_float4(a[t][j], a[t][j + 1], a[t][j + 2], a[t][j + 3]);
+    }
   }
   if (Rops == nullptr) return;
-  uint32_t pk[B / 2];
+  uint32_t pk[RPL][B / 2];
 #pragma unroll
-  for (int j = 0; j < B; j += 2) pk[j / 2] = pack_bf16x2(a[j], a[j + 1]);
-  // R^T through LDS: row r of R in, column r of R (row r of R^T) out
+  for (int t = 0; t < RPL; ++t)
+#pragma unroll
+    for (int j = 0; j < B; j += 2) pk[t][j / 2] = pack_bf16x2(a[t][j], a[t][j + 1]);
+  // R^T through LDS: rows of R in, columns of R (rows of R^T) out
   uint16_t* tt = reinterpret_cast<uint16_t*>(stage) + sub * B * TP;
 #pragma unroll
-  for (int j = 0; j < B; j += 2) *reinterpret_cast<uint32_t*>(tt + r * TP + j) = pk[j / 2];
+  for (int t = 0; t < RPL; ++t)
+#pragma unroll
+    for (int j = 0; j < B; j += 2)
+      *reinterpret_cast<uint32_t*>(tt + (qd + LPB * t) * TP + j) = pk[t][j / 2];
   __syncthreads();
-  uint32_t pt[B / 2];
-#pragma unroll
-  for (int j = 0; j < B; j += 2) pt[j / 2] = (uint32_t)tt[j * TP + r] | ((uint32_t)tt[(j + 1) * TP + r] << 16);
   if (sub < nv) {
-    uint4* r0 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + r * B);  // R, row r
-    uint4* r1 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + B * B + r * B);  // R^T, row r
 #pragma unroll
-    for (int v = 0; v < B / 8; ++v) {
-      r0[v] = make_uint4(pk[4 * v], pk[4 * v + 1], pk[4 * v + 2], pk[4 * v + 3]);
-      r1[v] = make_uint4(pt[4 * v], pt[4 * v + 1], pt[4 * v + 2], pt[4 * v + 3]);
+    for (int t = 0; t < RPL; ++t) {
+      const int r = qd + LPB * t;
+      uint32_t pt[B / 2];
+#pragma unroll
+      for (int j = 0; j < B; j += 2) pt[j / 2] = (uint32_t)tt[j * TP + r] | ((uint32_t)tt[(j + 1) * TP + r] << 16);
+      uint4* r0 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + r * B);          // R, row r
+      uint4* r1 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + B * B + r * B);  // R^T, row r
+#pragma unroll
+      for (int v = 0; v < B / 8; ++v) {
+        r0[v] = make_uint4(pk[t][4 * v], pk[t][4 * v + 1], pk[t][4 * v + 2], pk[t][4 * v + 3]);
+        r1[v] = make_uint4(pt[4 * v], pt[4 * v + 1], pt[4 * v + 2], pt[4 * v + 3]);
+      }
     }
   }
 }
@@ -355,7 +384,7 @@ hipError_t launch_cayley(const uint16_t* q, int nblk, int b, float* Rf, uint16_t
   if (b == 32 && two)
     hipLaunchKernelGGL(cayley2_kernel<32>, dim3(nblk), dim3(64), 0, st, q, nblk, Rf, Rops);
   else if (b == 32)
-    hipLaunchKernelGGL(cayley_kernel<32>, dim3((nblk + 1) / 2), dim3(64), 0, st, q, nblk, Rf, Rops);
+    hipLaunchKernelGGL(cayley_kernel<32>, dim3((nblk + 3) / 4), dim3(64), 0, st, q, nblk, Rf, Rops);
   else if (two)
     hipLaunchKernelGGL(cayley2_kernel<16>, dim3((nblk + 1) / 2), dim3(64), 0, st, q, nblk, Rf, Rops);
   else
