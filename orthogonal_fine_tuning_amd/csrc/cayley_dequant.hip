@@ -60,17 +60,19 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
   constexpr int RPL = B / LPB;    // rows per lane
   constexpr int PER = 64 / LPB;   // blocks per wave
   constexpr int NP = B * (B - 1) / 2;
-  constexpr int TP = B + 2;  // row pitch (bf16) of the transpose tile
-  // the parameters of the wave's blocks, later the bf16 transpose of R
-  constexpr int STAGE = PER * NP * 4 > PER * B * TP * 2 ? PER * NP * 4 : PER * B * TP * 2;
+  // the parameters of the wave's blocks, later the outputs of BR blocks at
+  // a time: R in fp32 rows of FP floats, then R and R^T in bf16 rows of OP
+  constexpr int BR = B == 32 ? 2 : 4;
+  constexpr int FP = B + 4, OP = B + 8;  // (pitches: 16-byte rows, spread banks)
+  constexpr int S_Q = PER * NP * 4, S_F = BR * B * FP * 4, S_O = BR * 2 * B * OP * 2;
+  constexpr int STAGE = S_Q > S_F ? (S_Q > S_O ? S_Q : S_O) : (S_F > S_O ? S_F : S_O);
+  static_assert(PER % BR == 0 && (BR * B * B / 4) % 64 == 0, "store rounds");
   __shared__ __attribute__((aligned(16))) uint8_t stage[STAGE];
 
   const int lane = threadIdx.x;
   const int sub = lane / LPB, qd = lane % LPB;
   const int blk0 = blockIdx.x * PER;
   const int nv = min(PER, nblk - blk0);  // blocks of this wave
-  const int blk = blk0 + sub;
-
   // parameters: PER consecutive blocks are PER * NP contiguous bf16; every
   // load of the wave is in flight before the first is used
   float* qs = reinterpret_cast<float*>(stage);
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
       a[t][c] = c == r ? 1.0f : (c > r ? -v : v);
     }
   }
-  __syncthreads();  // stage is reused for the transpose at the end
+  __syncthreads();  // stage is reused for the outputs at the end
 
   // one pivot step; the step index is a compile-time constant so that every
   // a[][] access stays a register and the owner lane is the DPP operand
@@ -157,12 +159,31 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
   for (int t = 0; t < RPL; ++t)
 #pragma unroll
     for (int j = 0; j < B; ++j) a[t][j] = 2.0f * a[t][j] - (j == qd + LPB * t ? 1.0f : 0.0f);
-  if (sub < nv) {
+  // The outputs leave through LDS, BR blocks at a time, so that every store
+  // instruction writes 64 consecutive 16-byte pieces (a block's R, and its
+  // R | R^T pack, are contiguous; rows written straight from the lanes that
+  // hold them would be 16-byte pieces of 64 rows)
+  float* F = reinterpret_cast<float*>(stage);         // [BR][B][FP] fp32
+  uint16_t* O = reinterpret_cast<uint16_t*>(stage);   // [BR][2][B][OP] bf16: R, R^T
 #pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      float4* dst = reinterpret_cast<float4*>(Rf + (size_t)blk * B * B + (qd + LPB * t) * B);
+  for (int rd = 0; rd < PER / BR; ++rd) {
+    const int bb = sub - BR * rd;  // this lane's block in the round, if 0 <= bb < BR
+    __syncthreads();  // the stage is free (parameters read, or the last round stored)
+    if (bb >= 0 && bb < BR) {
 #pragma unroll
-      for (int j = 0; j < B; j += 4) dst[j / 4] = make_float4(a[t][j], a[t][j + 1], a[t][j + 2], a[t][j + 3]);
+      for (int t = 0; t < RPL; ++t)
+#pragma unroll
+        for (int j = 0; j < B; j += 4)
+          *reinterpret_cast<float4*>(F + (bb * B + qd + LPB * t) * FP + j) =
+              make_float4(a[t][j], a[t][j + 1], a[t][j + 2], a[t][j + 3]);
+    }
+    __syncthreads();
+#pragma unroll 2  // (the rows in registers are still live: few loads in flight)
+    for (int i = 0; i < BR * B * B / 4 / 64; ++i) {
+      const int c = lane + 64 * i, cb = c / (B * B / 4), rem = c % (B * B / 4);
+      if (BR * rd + cb < nv)
+        reinterpret_cast<float4*>(Rf + (size_t)(blk0 + BR * rd + cb) * B * B)[rem] =
+            *reinterpret_cast<const float4*>(F + (cb * B + rem / (B / 4)) * FP + 4 * (rem % (B / 4)));
     }
   }
   if (Rops == nullptr) return;
@@ -171,28 +192,44 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
   for (int t = 0; t < RPL; ++t)
 #pragma unroll
     for (int j = 0; j < B; j += 2) pk[t][j / 2] = pack_bf16x2(a[t][j], a[t][j + 1]);
-  // R^T through LDS: rows of R in, columns of R (rows of R^T) out
-  uint16_t* tt = reinterpret_cast<uint16_t*>(stage) + sub * B * TP;
 #pragma unroll
-  for (int t = 0; t < RPL; ++t)
+  for (int rd = 0; rd < PER / BR; ++rd) {
+    const int bb = sub - BR * rd;
+    const bool in = bb >= 0 && bb < BR;
+    __syncthreads();
+    // R rows in; then R^T rows (columns of R) beside them
+    if (in) {
 #pragma unroll
-    for (int j = 0; j < B; j += 2)
-      *reinterpret_cast<uint32_t*>(tt + (qd + LPB * t) * TP + j) = pk[t][j / 2];
-  __syncthreads();
-  if (sub < nv) {
+      for (int t = 0; t < RPL; ++t)
 #pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      const int r = qd + LPB * t;
-      uint32_t pt[B / 2];
+        for (int v = 0; v < B / 8; ++v)
+          *reinterpret_cast<uint4*>(O + ((bb * 2) * B + qd + LPB * t) * OP + 8 * v) =
+              make_uint4(pk[t][4 * v], pk[t][4 * v + 1], pk[t][4 * v + 2], pk[t][4 * v + 3]);
+    }
+    __syncthreads();
+    if (in) {
+      const uint16_t* Rb = O + (bb * 2) * B * OP;
 #pragma unroll
-      for (int j = 0; j < B; j += 2) pt[j / 2] = (uint32_t)tt[j * TP + r] | ((uint32_t)tt[(j + 1) * TP + r] << 16);
-      uint4* r0 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + r * B);          // R, row r
-      uint4* r1 = reinterpret_cast<uint4*>(Rops + (size_t)blk * 2 * B * B + B * B + r * B);  // R^T, row r
+      for (int t = 0; t < RPL; ++t) {
+        const int r = qd + LPB * t;
+        uint32_t pt[B / 2];
 #pragma unroll
-      for (int v = 0; v < B / 8; ++v) {
-        r0[v] = make_uint4(pk[t][4 * v], pk[t][4 * v + 1], pk[t][4 * v + 2], pk[t][4 * v + 3]);
-        r1[v] = make_uint4(pt[4 * v], pt[4 * v + 1], pt[4 * v + 2], pt[4 * v + 3]);
+        for (int j = 0; j < B; j += 2) pt[j / 2] = (uint32_t)Rb[j * OP + r] | ((uint32_t)Rb[(j + 1) * OP + r] << 16);
+#pragma unroll
+        for (int v = 0; v < B / 8; ++v)
+          *reinterpret_cast<uint4*>(O + ((bb * 2 + 1) * B + r) * OP + 8 * v) =
+              make_uint4(pt[4 * v], pt[4 * v + 1], pt[4 * v + 2], pt[4 * v + 3]);
       }
+    }
+    __syncthreads();
+    // a block's pack is 2 B B bf16 = B B / 4 pieces of 16 bytes
+#pragma unroll 2
+    for (int i = 0; i < BR * B * B / 4 / 64; ++i) {
+      const int c = lane + 64 * i, cb = c / (B * B / 4), rem = c % (B * B / 4);
+      const int m = rem / (B * B / 8), row = (rem % (B * B / 8)) / (B / 8), c16 = rem % (B / 8);
+      if (BR * rd + cb < nv)
+        reinterpret_cast<uint4*>(Rops + (size_t)(blk0 + BR * rd + cb) * 2 * B * B)[rem] =
+            *reinterpret_cast<const uint4*>(O + ((cb * 2 + m) * B + row) * OP + 8 * c16);
     }
   }
 }
