@@ -389,8 +389,9 @@ __global__ __launch_bounds__(256) void moe_dw_reduce_kernel(const float* __restr
 // ---------------------------------------------------------------- dq per expert
 // One workgroup per (64 gate/up channels, expert): S = dH_blk^T H_blk over the
 // expert's rows (64-row steps through swizzled LDS transposes, MFMA), then the
-// Cayley gradient per block in fp32 (cayley_grad_group): Gq = (R^T + I) S
-// (I + R) / 2, dp_il = Gq_il - Gq_li.  Inactive experts get zeros (S = 0).  When dz != nullptr
+// Cayley gradient per block in fp32: Gq = (R^T + I) S (I + R) / 2, dp_il =
+// Gq_il - Gq_li (b = 32: the two products on the fp32 matrix cores; b = 16:
+// cayley_grad_group).  Inactive experts get zeros (S = 0).  When dz != nullptr
 // the same pass writes dz = dH_blk R_j (bf16, MFMA), the rotated operand of
 // the gate/up dX GEMM, once per dH tile.
 constexpr int LDM = 64 + 8;
@@ -528,8 +529,52 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
     for (int r = 0; r < 16; ++r) S[grp][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = acc[r] + red[grp][lane][r];
   }
   __syncthreads();
-  // the blocks of the 64 channels, G at a time
   constexpr int GB = 1024 / (B * B), NP = B * (B - 1) / 2;
+  if constexpr (B == 32) {
+    // the two blocks' gradients on the fp32 matrix cores, wave w < 2 taking
+    // block w: T1 = S + S R (D = A B + C with A = S, B = R, C = S), then
+    // 2 Gq = T1 + R^T T1 (A = R^T, B = T1, C = T1); in step s of
+    // v_mfma_f32_32x32x2f32 lane (l32, g2) supplies A[l32][2 s + g2] and
+    // B[2 s + g2][l32], and holds D[8 (r / 4) + 4 g2 + r % 4][l32] in r
+    auto T1 = reinterpret_cast<float (*)[32][33]>(lds + Lds::S_BYTES);  // the dead partial sums' space
+    const int bk = wave;
+    const int jb0 = n0 / 32 + bk;
+    if (wave < 2 && jb0 < nblk_e) {
+      const float* Rg = Rf + ((size_t)e * nblk_e + jb0) * 1024;
+      float rk[16];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) rk[s2] = Rg[(2 * s2 + g2) * 32 + l32];
+      f32x16 t;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = S[bk][(r / 4) * 8 + 4 * g2 + (r % 4)][l32];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) t = __builtin_amdgcn_mfma_f32_32x32x2f32(S[bk][l32][2 * s2 + g2], rk[s2], t, 0, 0, 0);
+      // (LDS accesses of one wave complete in order: T1 is read back below,
+      // S is overwritten after its last read)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) T1[bk][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = t[r];
+      f32x16 g = t;
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) g = __builtin_amdgcn_mfma_f32_32x32x2f32(rk[s2], T1[bk][2 * s2 + g2][l32], g, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[bk][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = 0.5f * g[r];
+    }
+    __syncthreads();
+    // dp_il = Gq_il - Gq_li, row-major upper triangle of each block
+    for (int x = tid; x < 2 * NP; x += 256) {
+      const int b2 = x / NP, rem = x - b2 * NP;
+      if (n0 / 32 + b2 >= nblk_e) break;
+      int i = 0, r2 = rem;
+      while (r2 >= 31 - i) {
+        r2 -= 31 - i;
+        ++i;
+      }
+      const int l = i + 1 + r2;
+      dq[((size_t)e * nblk_e + n0 / 32 + b2) * NP + rem] = S[b2][i][l] - S[b2][l][i];
+    }
+    return;
+  }
+  // the blocks of the 64 channels, G at a time
 #pragma unroll
   for (int q = 0; q < 64 / (GB * B); ++q) {
     const int j0 = n0 / B + q * GB;  // first block (within the expert) of the group
