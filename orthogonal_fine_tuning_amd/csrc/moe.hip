@@ -485,11 +485,28 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
       for (int r = 0; r < 16; ++r) o[r] = 0.0f;
       o = mfma32(as_bf16x8(rtf[0]), as_bf16x8(f[0]), o);
       o = mfma32(as_bf16x8(rtf[1]), as_bf16x8(f[1]), o);
-      if (mok) {
+      // lane (l32, g2) holds channels 8 q + 4 g2 + [0, 4) of row m; the two
+      // halves of the wave exchange (v_permlane32_swap: lanes 32..63 of the
+      // first operand with lanes 0..31 of the second) so that lane g2 = 0
+      // holds channels 8 q + [0, 8) for q = 0, 2 and lane g2 = 1 for q = 1,
+      // 3: two 16-byte stores per lane, 32 contiguous bytes per row each
+      uint32_t pk[4][2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<uint2*>(dz + (size_t)m * ld + nbr + 8 * q + 4 * g2) =
-              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+      for (int q = 0; q < 4; ++q) {
+        pk[q][0] = pack_bf16x2(o[4 * q], o[4 * q + 1]);
+        pk[q][1] = pack_bf16x2(o[4 * q + 2], o[4 * q + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t lo[2], hi[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * h][w], pk[2 * h + 1][w], false, false);
+          lo[w] = sw[0];
+          hi[w] = sw[1];
+        }
+        if (mok)
+          *reinterpret_cast<uint4*>(dz + (size_t)m * ld + nbr + 8 * (2 * h + g2)) = make_uint4(lo[0], lo[1], hi[0], hi[1]);
       }
     }
     __syncthreads();
