@@ -47,8 +47,22 @@ SMALL = {
     # token tiles, ragged last channel tile; one token tile)
     "decode_int4_g32": DenseConfig("decode_int4_g32", M=48, K=512, segs=(160, 128), b=32, x_dtype="bf16",
                                    w_fmt="int4", g=32),
+    "decode_int4_k768_m48": DenseConfig("decode_int4_k768_m48", M=48, K=768, segs=(160, 128), b=32, x_dtype="bf16",
+                                        w_fmt="int4", g=32),
+    "fp4_decode_k768": DenseConfig("fp4_decode_k768", M=40, K=768, segs=(160, 128), b=32, x_dtype="bf16",
+                                   w_fmt="fp4", g=32),
     "decode_int4_g64_b16": DenseConfig("decode_int4_g64_b16", M=20, K=768, segs=(96, 64), b=16,
                                        x_dtype="bf16", w_fmt="int4", g=64),
+    # few tokens, 4-bit, more 256-wide steps: odd and even step counts,
+    # one and two token tiles, a single row, many channel tiles
+    "decode_int4_g128_m64_k1536": DenseConfig("decode_int4_g128_m64_k1536", M=64, K=1536, segs=(320, 256),
+                                              b=32, x_dtype="bf16", w_fmt="int4", g=128),
+    "decode_int4_g64_b16_m1_k1024": DenseConfig("decode_int4_g64_b16_m1_k1024", M=1, K=1024, segs=(96, 64),
+                                                b=16, x_dtype="bf16", w_fmt="int4", g=64, q_std=0.05),
+    "decode_fp4_g32_m33_k2048": DenseConfig("decode_fp4_g32_m33_k2048", M=33, K=2048, segs=(128, 64), b=32,
+                                            x_dtype="bf16", w_fmt="fp4", g=32),
+    "decode_int4_520_blocks_b16": DenseConfig("decode_int4_520_blocks_b16", M=17, K=512, segs=(9600, 7040),
+                                              b=16, x_dtype="bf16", w_fmt="int4", g=32, q_std=0.05),
     # FP4 base (OCP MX E2M1 + E8M0 group exponents) through every forward
     # kernel and both dX routes: copy ring with the gemm_nn dX, copy ring
     # with the transposed-weight dX, register prefetch (fp32 x), skinny,
@@ -130,10 +144,12 @@ def _run_base(inp):
 
 
 # one case per forward kernel: copy-ring FP8 and INT4 (bf16 x), register-
-# prefetch FP8 and INT4 (fp32 x), skinny (fp32 x, few tokens), INT4 decode
-# on 256-wide steps (one and two token tiles), FP8 decode
+# prefetch FP8 and INT4 (fp32 x), skinny (fp32 x, few tokens), 4-bit decode
+# on 256-wide steps (one and two token tiles, many channel tiles), FP8
+# decode
 BASE_CASES = ["fp8_b32_ragged", "int4_g64_ragged_k", "fp8_b16_f32x", "int4_f32x_wide", "int4_g32_f32x_b32",
-              "decode_int4_g32", "decode_m1", "decode_split_fp8_b16", "fp4_g64_wide", "fp4_decode_g32"]
+              "decode_int4_g32", "decode_m1", "decode_int4_g64_b16", "decode_split_fp8_b16", "fp4_g64_wide",
+              "fp4_decode_g32", "decode_int4_520_blocks_b16"]
 
 
 @pytest.mark.parametrize("name", BASE_CASES)
