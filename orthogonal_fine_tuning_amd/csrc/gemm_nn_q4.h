@@ -115,7 +115,11 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g2 = lane >> 5;
   const int K = p.K;
-  const int ns = p.N / BNS;
+  // contraction split (dense, few rows: nsplit_len > 0, a multiple of BNS):
+  // workgroup z covers weight rows [z nsplit_len, (z + 1) nsplit_len) and
+  // stores fp32 partials to part[z][M][K]
+  const int zlo = (!GROUPED && p.nsplit_len > 0) ? (int)blockIdx.z * p.nsplit_len : 0;
+  const int ns = (!GROUPED && p.nsplit_len > 0) ? min(p.nsplit_len, p.N - zlo) / BNS : p.N / BNS;
 
   int e = 0, pos0, nrows, cx = blockIdx.x;
   if constexpr (GROUPED) {
@@ -129,13 +133,14 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
     nrows = min(BM, p.M - pos0);
   }
   const int kbase = cx * BKO;
-  const uint8_t* wc = p.wc + (size_t)e * p.wc_e;
-  const uint8_t* ws_b = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e);
   const int kg = K / p.g;                // scales per weight row
+  const uint8_t* wc = p.wc + (size_t)e * p.wc_e + (size_t)zlo * (K / 2);
+  const uint8_t* ws_b = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.ws) + (size_t)e * p.ws_e +
+                                                         (size_t)zlo * kg);
   const int gw = (kbase + 32 * wave) / p.g;  // scale group of this wave's columns
 
   // ---- B tile copies: rows 16 wave + 8 i + lane / 8 (past the end: row 0)
-  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(p.src) + (size_t)pos0 * p.lds * 2;
+  const uint8_t* bbase = reinterpret_cast<const uint8_t*>(p.src) + ((size_t)pos0 * p.lds + zlo) * 2;
   uint32_t boff[2];
   const uint8_t* bptr[GROUPED ? 2 : 1];
 #pragma unroll
@@ -257,6 +262,7 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
   // kbase + 32 wave + 8 q + 4 g2 + [0, 4) in registers 4 q .. 4 q + 3
   const int kb = kbase + 32 * wave;
   if constexpr (EPI == EPI_STORE) {
+    const bool split = !GROUPED && p.nsplit_len > 0;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
       const int ml = 32 * tm + l32;
@@ -265,8 +271,12 @@ __global__ __launch_bounds__(nnq::NTHR, 2) void gemm_nn_q4_kernel(NnArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const size_t off = (size_t)(pos0 + ml) * p.ldo + kb + 8 * q + 4 * g2;
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
-            make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+        if (split)
+          *reinterpret_cast<float4*>(p.part + (size_t)blockIdx.z * p.M * p.ldo + off) =
+              make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        else
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
+              make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
       }
     }
   } else {

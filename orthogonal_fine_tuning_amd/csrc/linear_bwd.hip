@@ -25,6 +25,7 @@
 // stage 2 reduces the slices in a fixed order and applies the Cayley
 // gradient in fp32 with R_f32.
 #include "gemm_nn.h"
+#include "gemm_nn_q4.h"
 #include "gemm_nt_dma.h"
 #include "oft_launch.h"
 #include "oft_prof.h"
@@ -518,7 +519,19 @@ hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src
   }
   {
     ProfScope prof(st, "dense.dx");
-    hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, WF, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
+    // INT4, few tokens, split contraction: the codes stream through the
+    // copy ring of gemm_nn_q4_kernel (4-bit transpose loads, 256 output
+    // columns per workgroup), its fp32 partials into the same split sum
+    bool q4 = false;
+    if constexpr (WF == WF_INT4 && PRO == PRO_NONE) {
+      if (pl.nsplit_n > 1 && a.K % nnq::BKO == 0 && a.N % nnq::BNS == 0 && pl.nsplit_len % nnq::BNS == 0) {
+        const dim3 qgrid(a.K / nnq::BKO, (a.M + nnq::BM - 1) / nnq::BM, pl.nsplit_n);
+        hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_STORE, false, false>), qgrid, dim3(nnq::NTHR), 0, st, p);
+        q4 = true;
+      }
+    }
+    if (!q4)
+      hipLaunchKernelGGL((gemm_nn_kernel<BM, XF32, WF, B, PRO, EPI_STORE, false, NB>), grid, dim3(256), 0, st, p);
   }
   if (pl.nsplit_n > 1) {
     ProfScope prof(st, "dense.dx_reduce");
@@ -639,7 +652,12 @@ hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz
 
 }  // namespace
 
-DqPlan plan_bwd(int M, int K, int N, bool fp8) {
+// workgroups of the split-contraction INT4 dX (few tokens): fewer splits
+// mean fewer fp32 partials to write and sum; 192 was the best of 128 .. 1024
+// at 64 tokens x 2560 in-features x 19456 channels
+constexpr int Q4_SPLIT_WGS = 192;
+
+DqPlan plan_bwd(int M, int K, int N, bool fp8, bool int4) {
   DqPlan p;
   p.ng32 = N / 32;
   const int ng64 = (N + 63) / 64;
@@ -679,9 +697,13 @@ DqPlan plan_bwd(int M, int K, int N, bool fp8) {
   p.nsplit_n = 1;
   p.nsplit_len = 0;
   p.npart_off = 0;
-  const int ktiles = (K + nn::BKO - 1) / nn::BKO;
+  // (INT4 with K % 256 == 0 and N % 64 == 0 runs gemm_nn_q4_kernel: 256
+  // columns per workgroup)
+  const bool q4 = int4 && K % nnq::BKO == 0 && N % nnq::BNS == 0;
+  const int ktiles = q4 ? K / nnq::BKO : (K + nn::BKO - 1) / nn::BKO;
+  const int target = q4 ? Q4_SPLIT_WGS : 512;
   if (M > 0 && M <= 128 && p.prerotate) {
-    int want = (512 + ktiles - 1) / ktiles;
+    int want = (target + ktiles - 1) / ktiles;
     const int nsteps = (N + nn::BNS - 1) / nn::BNS;
     if (want > nsteps) want = nsteps;
     if (want > 1) {

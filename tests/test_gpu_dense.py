@@ -61,6 +61,10 @@ SMALL = {
                                                 b=16, x_dtype="bf16", w_fmt="int4", g=64, q_std=0.05),
     "decode_fp4_g32_m33_k2048": DenseConfig("decode_fp4_g32_m33_k2048", M=33, K=2048, segs=(128, 64), b=32,
                                             x_dtype="bf16", w_fmt="fp4", g=32),
+    # INT4 dX on the split-contraction transposed-code kernel (K % 256 == 0,
+    # N % 64 == 0, at most 128 tokens): a full 128-row tile, 3 column tiles
+    "decode_int4_q4_m128": DenseConfig("decode_int4_q4_m128", M=128, K=768, segs=(192, 128), b=32,
+                                       x_dtype="bf16", w_fmt="int4", g=64),
     "decode_int4_520_blocks_b16": DenseConfig("decode_int4_520_blocks_b16", M=17, K=512, segs=(9600, 7040),
                                               b=16, x_dtype="bf16", w_fmt="int4", g=32, q_std=0.05),
     # FP4 base (OCP MX E2M1 + E8M0 group exponents) through every forward
