@@ -222,21 +222,26 @@ def blas_threads():
 
 
 def time_steps(step, steps, warmup, nev=4):
-    """Warm-up, then `steps` steps bracketed by syncs (wall clock), with HIP
-    events between the phases of every timed step."""
+    """Warm-up, then `steps` steps bracketed by syncs (wall clock, nothing
+    else on the stream), then the same number of steps again with HIP events
+    between their phases for the phase split (an event record between two
+    kernels adds a few microseconds of its own, so it stays out of the timed
+    steps)."""
     import numpy as np
     import torch
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     phases = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e-3 for i in range(nev - 1)]
     return wall / steps, phases
 
