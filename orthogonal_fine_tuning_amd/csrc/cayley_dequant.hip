@@ -236,8 +236,16 @@ __global__ __launch_bounds__(64) void cayley_kernel(const uint16_t* __restrict__
 
 // The same solve with two lanes per row (lane 2r + h holds columns
 // [16h, 16h + 16) of row r): half the pivot-row reads and half the updates
-// per lane on the serial chain of b pivot steps, for builds of few blocks,
-// where that chain is the whole cost.  PER = 32 / B blocks per wave.
+// per lane on the serial chain of pivot steps, for builds of few blocks,
+// where that chain is the whole cost.  PER = 32 / B blocks per wave.  The
+// pivots are taken two at a time (a 2 x 2 block K = {s, s + 1}): the
+// in-place inversion by block pivots, P = A[K][K],
+//   A[i][j] -= A[i][K] P^-1 A[K][j],  A[i][K] = -A[i][K] P^-1   (i, j not in K)
+//   A[K][j] = P^-1 A[K][j],           A[K][K] = P^-1,
+// equals the two single pivots one after the other (and needs no row
+// exchange for the same reason: every principal block of I - Q, Q skew,
+// has a positive definite symmetric part), with b / 2 broadcasts through
+// LDS on the serial chain instead of b.
 template <int B>
 __global__ __launch_bounds__(64) void cayley2_kernel(const uint16_t* __restrict__ q, int nblk,
                                                      float* __restrict__ Rf, uint16_t* __restrict__ Rops) {
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(64) void cayley2_kernel(const uint16_t* __restrict_
   constexpr int TP = B + 2;  // row pitch (bf16) of the transpose tile
   constexpr int STAGE = PER * NP * 4 > PER * B * TP * 2 ? PER * NP * 4 : PER * B * TP * 2;
   __shared__ __attribute__((aligned(16))) uint8_t stage[STAGE];
-  __shared__ __attribute__((aligned(16))) float prow[PER][B];  // pivot row
+  __shared__ __attribute__((aligned(16))) float prow[PER][2][B];  // the two pivot rows
 
   const int lane = threadIdx.x;
   const int sub = lane / (2 * B), r = (lane / 2) % B, h = lane & 1;
@@ -283,39 +291,61 @@ __global__ __launch_bounds__(64) void cayley2_kernel(const uint16_t* __restrict_
   }
   __syncthreads();  // stage is reused for the transpose at the end
 
-  auto step = [&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    constexpr int hs = s / HB, js = s % HB;  // the lane half and slot holding column s
-    if (r == s) {
+  auto step = [&](auto tc) {
+    constexpr int s = 2 * decltype(tc)::value;  // pivot columns s, s + 1
+    constexpr int hs = s / HB, js = s % HB;     // both in lane half hs (HB is even)
+    if (r == s || r == s + 1) {
 #pragma unroll
       for (int j = 0; j < HB; j += 4)
-        *reinterpret_cast<float4*>(&prow[sub][c0 + j]) = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
+        *reinterpret_cast<float4*>(&prow[sub][r - s][c0 + j]) = make_float4(a[j], a[j + 1], a[j + 2], a[j + 3]);
     }
-    // a_rs: held by the lane of half hs of this row
-    const float mine = a[js];
-    const float other = __shfl_xor(mine, 1);
-    const float f = h == hs ? mine : other;
+    // A[r][K]: held by the lane of half hs of this row
+    const float m0 = a[js], m1 = a[js + 1];
+    const float o0 = __shfl_xor(m0, 1), o1 = __shfl_xor(m1, 1);
+    const float f0 = h == hs ? m0 : o0, f1 = h == hs ? m1 : o1;
     wave_sync();
-    float pr[HB];
+    float p0[HB], p1[HB];
 #pragma unroll
     for (int j = 0; j < HB; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(&prow[sub][c0 + j]);
-      pr[j] = v.x;
-      pr[j + 1] = v.y;
-      pr[j + 2] = v.z;
-      pr[j + 3] = v.w;
+      const float4 v = *reinterpret_cast<const float4*>(&prow[sub][0][c0 + j]);
+      const float4 w = *reinterpret_cast<const float4*>(&prow[sub][1][c0 + j]);
+      p0[j] = v.x;
+      p0[j + 1] = v.y;
+      p0[j + 2] = v.z;
+      p0[j + 3] = v.w;
+      p1[j] = w.x;
+      p1[j + 1] = w.y;
+      p1[j + 2] = w.z;
+      p1[j + 3] = w.w;
     }
-    const float piv = prow[sub][s];
-    float rp = __builtin_amdgcn_rcpf(piv);
-    rp = fmaf(rp, fmaf(-piv, rp, 1.0f), rp);
-    const float g = r == s ? 1.0f - rp : f * rp;
+    const float q00 = prow[sub][0][s], q01 = prow[sub][0][s + 1];
+    const float q10 = prow[sub][1][s], q11 = prow[sub][1][s + 1];
+    const float det = q00 * q11 - q01 * q10;
+    float rd = __builtin_amdgcn_rcpf(det);
+    rd = fmaf(rd, fmaf(-det, rd, 1.0f), rd);
+    const float i00 = q11 * rd, i01 = -q01 * rd, i10 = -q10 * rd, i11 = q00 * rd;  // P^-1
+    // one update for every row: a[j] -= u0 p0[j] + u1 p1[j], with u = A[r][K] P^-1
+    // off K, and u = e_k - P^-1[k] on pivot row s + k (whose a[j] is p_k[j])
+    const bool k0 = r == s, k1 = r == s + 1;
+    float u0 = f0 * i00 + f1 * i10, u1 = f0 * i01 + f1 * i11;
+    if (k0) {
+      u0 = 1.0f - i00;
+      u1 = -i01;
+    }
+    if (k1) {
+      u0 = -i10;
+      u1 = 1.0f - i11;
+    }
 #pragma unroll
     for (int j = 0; j < HB; ++j)
-      if (h != hs || j != js) a[j] = fmaf(-g, pr[j], a[j]);
-    if (h == hs) a[js] = r == s ? rp : -g;
+      if (h != hs || (j != js && j != js + 1)) a[j] = fmaf(-u0, p0[j], fmaf(-u1, p1[j], a[j]));
+    if (h == hs) {
+      a[js] = (k0 ? 1.0f : 0.0f) - u0;
+      a[js + 1] = (k1 ? 1.0f : 0.0f) - u1;
+    }
     wave_sync();
   };
-  for_each_index(step, std::make_integer_sequence<int, B>{});
+  for_each_index(step, std::make_integer_sequence<int, B / 2>{});
 
   // row r of A^-1 (this lane's columns); R = 2 A^-1 - I
 #pragma unroll
