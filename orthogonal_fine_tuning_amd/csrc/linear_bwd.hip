@@ -427,6 +427,50 @@ __global__ __launch_bounds__(256, 2) void dq_dma_kernel(const uint16_t* __restri
   constexpr int GB = 1024 / (B * B), NP = B * (B - 1) / 2;
   float* scratch = reinterpret_cast<float*>(&tiles[1][0][0]);  // 32 KB free past Sg
   const int nblk = N / B;
+  if constexpr (B == 32) {
+    // the two blocks at once on the fp32 matrix cores, wave w < 2 taking
+    // block w: T1 = S + S R (D = A B + C with A = S, B = R, C = S), then
+    // 2 Gq = T1 + R^T T1 (A = R^T, B = T1, C = T1); in step s of
+    // v_mfma_f32_32x32x2f32 lane (l32, g2) supplies A[l32][2 s + g2] and
+    // B[2 s + g2][l32], and holds D[8 (r / 4) + 4 g2 + r % 4][l32] in r
+    auto T1 = reinterpret_cast<float(*)[32][33]>(scratch);
+    const int jb = n0 / 32 + wave;
+    if (wave < 2 && jb < nblk) {
+      const float* Rg = Rf + (size_t)jb * 1024;
+      float rk[16];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) rk[s2] = Rg[(2 * s2 + g2) * 32 + l32];
+      f32x16 t;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[r] = Sg[wave][(r / 4) * 8 + 4 * g2 + (r % 4)][l32];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2)
+        t = __builtin_amdgcn_mfma_f32_32x32x2f32(Sg[wave][l32][2 * s2 + g2], rk[s2], t, 0, 0, 0);
+      // (LDS accesses of one wave complete in order: T1 is read back below,
+      // S is overwritten after its last read)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) T1[wave][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = t[r];
+      f32x16 gq = t;
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2)
+        gq = __builtin_amdgcn_mfma_f32_32x32x2f32(rk[s2], T1[wave][2 * s2 + g2][l32], gq, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Sg[wave][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = 0.5f * gq[r];
+    }
+    __syncthreads();
+    // dp_il = Gq_il - Gq_li: thread (block tid / 128, row i, columns
+    // 8 (tid % 4) .. + 7 above the diagonal), packed index i B - i (i + 1) / 2 + l - i - 1
+    const int b2 = tid >> 7, i = (tid & 127) >> 2, c8 = 8 * (tid & 3);
+    if (n0 / 32 + b2 < nblk) {
+      float* dst = dq + (size_t)(n0 / 32 + b2) * NP + (i * 32 - i * (i + 1) / 2 - i - 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int l = c8 + k;
+        if (l > i) dst[l] = Sg[b2][i][l] - Sg[b2][l][i];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 64 / (GB * B); ++q) {
     const int j0 = n0 / B + q * GB;  // first block of the group

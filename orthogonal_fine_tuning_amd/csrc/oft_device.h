@@ -230,20 +230,18 @@ __device__ __forceinline__ void cayley_grad_group(float* lds, const float* __res
     q.w += ri * tt.w;
   }
   // S is no longer read (its last reads precede the barrier above)
-  *reinterpret_cast<float4*>(S + r * P + c) = make_float4(0.5f * q.x, 0.5f * q.y, 0.5f * q.z, 0.5f * q.w);
+  const float gq[4] = {0.5f * q.x, 0.5f * q.y, 0.5f * q.z, 0.5f * q.w};
+  *reinterpret_cast<float4*>(S + r * P + c) = make_float4(gq[0], gq[1], gq[2], gq[3]);
   __syncthreads();
-  for (int e = tid; e < G * NP; e += 256) {
-    const int gb = e / NP;
-    if (gb >= nb) break;
-    // invert the row-major upper-triangle index
-    int i = 0, rem = e - gb * NP;
-    while (rem >= B - 1 - i) {
-      rem -= B - 1 - i;
-      ++i;
+  // dp_rl = Gq_rl - Gq_lr for this thread's entries l = c .. c + 3 above the
+  // diagonal of row r: packed index r B - r (r + 1) / 2 + l - r - 1
+  if (ok) {
+    const int base = r * B - r * (r + 1) / 2 - r - 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int l = c + k;
+      if (l > r) dqg[(size_t)g * NP + base + l] = gq[k] - S[l * P + r];
     }
-    const int l = i + 1 + rem;
-    const float* Q = lds + gb * BS;
-    dqg[e] = Q[i * P + l] - Q[l * P + i];
   }
 }
 
