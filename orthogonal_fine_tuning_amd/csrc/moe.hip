@@ -577,17 +577,17 @@ __global__ __launch_bounds__(256) void moe_dq_kernel(const uint16_t* __restrict_
       for (int r = 0; r < 16; ++r) S[bk][(r / 4) * 8 + 4 * g2 + (r % 4)][l32] = 0.5f * g[r];
     }
     __syncthreads();
-    // dp_il = Gq_il - Gq_li, row-major upper triangle of each block
-    for (int x = tid; x < 2 * NP; x += 256) {
-      const int b2 = x / NP, rem = x - b2 * NP;
-      if (n0 / 32 + b2 >= nblk_e) break;
-      int i = 0, r2 = rem;
-      while (r2 >= 31 - i) {
-        r2 -= 31 - i;
-        ++i;
+    // dp_il = Gq_il - Gq_li, row-major upper triangle of each block: thread
+    // (block tid / 128, row i, columns 8 (tid % 4) .. + 7 above the
+    // diagonal), packed index i B - i (i + 1) / 2 + l - i - 1
+    const int b2 = tid >> 7, i = (tid & 127) >> 2, c8 = 8 * (tid & 3);
+    if (n0 / 32 + b2 < nblk_e) {
+      float* dst = dq + ((size_t)e * nblk_e + n0 / 32 + b2) * NP + (i * 32 - i * (i + 1) / 2 - i - 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int l = c8 + k;
+        if (l > i) dst[l] = S[b2][i][l] - S[b2][l][i];
       }
-      const int l = i + 1 + r2;
-      dq[((size_t)e * nblk_e + n0 / 32 + b2) * NP + rem] = S[b2][i][l] - S[b2][l][i];
     }
     return;
   }
