@@ -73,21 +73,31 @@ __device__ __forceinline__ uint2 ds_read_tr4(const uint8_t* p) {
 }
 
 // 8 INT4 codes (low nibble first) with one fp16 scale each (sc[e]: the fp16
-// bits in the low half) -> 8 bf16, each bf16(q s) rounded once.  Nibble e
-// becomes the fp16 value 1024 + (nibble ^ 8); subtracting 1032 (two at a
-// time, packed fp16) gives q exactly, and one mixed fp16 x fp16 + fp32 FMA
-// with a zero addend gives q s exactly in fp32 (at most 15 significant
-// bits).  The zero addend turns a -0 product into +0, which no product of
-// the matrix cores can tell apart.
+// bits in the low half) -> 8 bf16, each bf16(q s) rounded once.  One AND/XOR
+// per two nibbles puts them in fp16 mantissas with the nibble's top bit
+// flipped (n ^ 8 = q + 8): nibbles in bits 0-3 of a half under exponent 10
+// (value 1024 + (q + 8)), nibbles in bits 4-7 under exponent 6, whose unit
+// is then the mantissa's bit 4 (value 64 + (q + 8)); so one shift by 8 bits
+// serves all eight.  Subtracting 1032 or 72 (two at a time, packed fp16,
+// exact) gives q, and one mixed fp16 x fp16 + fp32 FMA with a zero addend
+// gives q s exactly in fp32 (at most 15 significant bits).  The zero addend
+// turns a -0 product into +0, which no product of the matrix cores can tell
+// apart.
 __device__ __forceinline__ uint4 dq_i4x8_rows(uint32_t w, const uint32_t* sc) {
+  const uint32_t v[2] = {w, w >> 8};
   float f[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * j)) & 0x000F000Fu) ^ 0x64086408u);
-    const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    h = h + off;
-    f[j] = __builtin_fmaf((float)h[0], (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]), 0.0f);
-    f[j + 4] = __builtin_fmaf((float)h[1], (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j + 4]), 0.0f);
+  for (int j = 0; j < 2; ++j) {
+    f16x2 lo = __builtin_bit_cast(f16x2, (v[j] & 0x000F000Fu) ^ 0x64086408u);  // nibbles 2j, 2j + 4
+    f16x2 hi = __builtin_bit_cast(f16x2, (v[j] & 0x00F000F0u) ^ 0x54805480u);  // nibbles 2j + 1, 2j + 5
+    const f16x2 olo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const f16x2 ohi = {(_Float16)-72.0f, (_Float16)-72.0f};
+    lo = lo + olo;
+    hi = hi + ohi;
+    f[2 * j] = __builtin_fmaf((float)lo[0], (float)__builtin_bit_cast(_Float16, (uint16_t)sc[2 * j]), 0.0f);
+    f[2 * j + 4] = __builtin_fmaf((float)lo[1], (float)__builtin_bit_cast(_Float16, (uint16_t)sc[2 * j + 4]), 0.0f);
+    f[2 * j + 1] = __builtin_fmaf((float)hi[0], (float)__builtin_bit_cast(_Float16, (uint16_t)sc[2 * j + 1]), 0.0f);
+    f[2 * j + 5] = __builtin_fmaf((float)hi[1], (float)__builtin_bit_cast(_Float16, (uint16_t)sc[2 * j + 5]), 0.0f);
   }
   uint4 r;
   r.x = pack_bf16x2(f[0], f[1]);
