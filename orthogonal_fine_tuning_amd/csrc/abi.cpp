@@ -148,7 +148,8 @@ int32_t oft_linear_workspace_bytes(const oft_linear_desc* d, int32_t pass, size_
   if (pass == OFT_PASS_FWD) {
     *bytes = 0;
   } else if (pass == OFT_PASS_BWD) {
-    *bytes = oft::plan_bwd(d->M, d->K, d->N, d->w_fmt == OFT_W_FP8_E4M3, d->w_fmt == OFT_W_INT4).bytes;
+    *bytes = oft::plan_bwd(d->M, d->K, d->N, d->w_fmt == OFT_W_FP8_E4M3, d->w_fmt == OFT_W_INT4,
+                       d->x_dtype == OFT_DT_F32).bytes;
   } else {
     return OFT_EINVAL;
   }
@@ -220,7 +221,8 @@ int32_t oft_linear_bwd(const oft_linear_desc* d, const uint16_t* dy, const void*
   if (!opt_ok(dx_or_null) || !opt_ok(dq_or_null)) return OFT_EINVAL;
   const bool want_dx = dx_or_null != nullptr && d->M > 0;
   const bool want_dq = dq_or_null != nullptr;
-  const oft::DqPlan plan = oft::plan_bwd(d->M, d->K, d->N, d->w_fmt == OFT_W_FP8_E4M3, d->w_fmt == OFT_W_INT4);
+  const oft::DqPlan plan = oft::plan_bwd(d->M, d->K, d->N, d->w_fmt == OFT_W_FP8_E4M3, d->w_fmt == OFT_W_INT4,
+                       d->x_dtype == OFT_DT_F32);
   if (want_dx) {
     if (!ptr_ok(dy) || !ptr_ok(w_codes) || !ptr_ok(w_scales) || !ptr_ok(R_ops)) return OFT_EINVAL;
   }

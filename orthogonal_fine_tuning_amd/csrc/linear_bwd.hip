@@ -563,12 +563,15 @@ hipError_t launch_dx_t(const DenseArgs& a, const DqPlan& pl, const uint16_t* src
   }
   {
     ProfScope prof(st, "dense.dx");
-    // INT4, few tokens, split contraction: the codes stream through the
-    // copy ring of gemm_nn_q4_kernel (4-bit transpose loads, 256 output
-    // columns per workgroup), its fp32 partials into the same split sum
+    // INT4 on the rotated copy dZ': the codes stream through the copy ring
+    // of gemm_nn_q4_kernel (4-bit transpose loads, 256 output columns per
+    // workgroup, no transposed or dequantised copy of the weight); few
+    // tokens split the contraction, its fp32 partials into the same split
+    // sum (the unsplit kernel stores bf16 dX only)
     bool q4 = false;
     if constexpr (WF == WF_INT4 && PRO == PRO_NONE) {
-      if (pl.nsplit_n > 1 && a.K % nnq::BKO == 0 && a.N % nnq::BNS == 0 && pl.nsplit_len % nnq::BNS == 0) {
+      const bool split_ok = pl.nsplit_n > 1 && pl.nsplit_len % nnq::BNS == 0;
+      if (a.K % nnq::BKO == 0 && a.N % nnq::BNS == 0 && (split_ok || (pl.nsplit_n == 1 && !XF32))) {
         const dim3 qgrid(a.K / nnq::BKO, (a.M + nnq::BM - 1) / nnq::BM, pl.nsplit_n);
         hipLaunchKernelGGL((gemm_nn_q4_kernel<EPI_STORE, false, false>), qgrid, dim3(nnq::NTHR), 0, st, p);
         q4 = true;
@@ -701,7 +704,7 @@ hipError_t launch_dx_wt(const DenseArgs& a, const DqPlan& pl, const uint16_t* dz
 // at 64 tokens x 2560 in-features x 19456 channels
 constexpr int Q4_SPLIT_WGS = 192;
 
-DqPlan plan_bwd(int M, int K, int N, bool fp8, bool int4) {
+DqPlan plan_bwd(int M, int K, int N, bool fp8, bool int4, bool xf32) {
   DqPlan p;
   p.ng32 = N / 32;
   const int ng64 = (N + 63) / 64;
@@ -759,7 +762,9 @@ DqPlan plan_bwd(int M, int K, int N, bool fp8, bool int4) {
     }
   }
   // Wide layer, many tokens: transposed weight for gemm_nt_dma_kernel
-  p.wt = M > 0 && p.prerotate && p.nsplit_n == 1 && N % 64 == 0;
+  // (FP8 codes, or FP4 / fp32-x INT4 dequantised to bf16); INT4 with bf16 x
+  // reads its codes in place on gemm_nn_q4_kernel instead
+  p.wt = M > 0 && p.prerotate && p.nsplit_n == 1 && N % 64 == 0 && !(q4 && !xf32);
   p.wt_off = 0;
   if (p.wt) {
     p.wt_off = (end + 255) / 256 * 256;

@@ -93,7 +93,7 @@ struct DqPlan {
   size_t wt_off;       // its workspace offset ([K, N]: FP8 codes or bf16)
   size_t bytes;        // total workspace
 };
-DqPlan plan_bwd(int M, int K, int N, bool fp8, bool int4);
+DqPlan plan_bwd(int M, int K, int N, bool fp8, bool int4, bool xf32);
 
 hipError_t launch_linear_bwd(const DenseArgs& a, const DqPlan& p, const uint16_t* dy, const void* y,
                              const uint8_t* wc, const void* ws, const float* Rf, const uint16_t* Rops,

@@ -120,7 +120,9 @@ def test_linear_workspace_query():
 def test_linear_bwd_workspace_covers_its_parts(w_fmt, g, M, K, segs):
     """Host-only backward planning over edge shapes (M = 0 included): the
     query succeeds and covers the dq partials, the rotated copy of dY for
-    wide layers and, for wide layers with many tokens, the transposed weight."""
+    wide layers and, for wide layers with many tokens, the transposed weight
+    (FP8 codes; INT4 with bf16 x and K % 256 == 0 reads its codes in place,
+    so only fp32 x keeps a dequantised copy there)."""
     N = sum(segs)
     d = oft.linear_desc(M, K, segs, 32, oft.OFT_DT_BF16, w_fmt, g)
     nb = oft.oft_linear_workspace_bytes(d, oft.OFT_PASS_BWD)
@@ -128,7 +130,12 @@ def test_linear_bwd_workspace_covers_its_parts(w_fmt, g, M, K, segs):
     if K > 256 and M > 0:
         assert nb >= M * N * 2  # rotated dY
     if K > 256 and M > 128 and N % 64 == 0:
-        assert nb >= M * N * 2 + K * N * (1 if w_fmt == oft.OFT_W_FP8_E4M3 else 2)
+        if w_fmt == oft.OFT_W_INT4 and K % 256 == 0:
+            d32 = oft.linear_desc(M, K, segs, 32, oft.OFT_DT_F32, w_fmt, g)
+            nb32 = oft.oft_linear_workspace_bytes(d32, oft.OFT_PASS_BWD)
+            assert nb32 >= nb + K * N * 2  # the bf16 copy: fp32 x only
+        else:
+            assert nb >= M * N * 2 + K * N * (1 if w_fmt == oft.OFT_W_FP8_E4M3 else 2)
 
 
 def test_cayley_and_dequant_validation():
