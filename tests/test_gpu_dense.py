@@ -36,6 +36,10 @@ SMALL = {
                                  x_dtype="f32", w_fmt="fp8"),
     "int4_f32x_wide": DenseConfig("int4_f32x_wide", M=140, K=384, segs=(96, 96), b=16,
                                   x_dtype="f32", w_fmt="int4", g=64),
+    # fp32 x, INT4, K % 256 == 0: the bf16-x route reads the codes in place,
+    # fp32 dX keeps the transposed bf16 copy
+    "int4_f32x_k512_wide": DenseConfig("int4_f32x_k512_wide", M=150, K=512, segs=(64, 64), b=32,
+                                       x_dtype="f32", w_fmt="int4", g=64),
     "decode_m1": DenseConfig("decode_m1", M=1, K=256, segs=(128, 128), b=32, x_dtype="bf16",
                              w_fmt="int4", g=128),
     # few tokens, wide layer: weight-streaming forward, split-contraction dX
