@@ -524,13 +524,24 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
                                                            void* __restrict__ dx) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
-  float4 s = reinterpret_cast<const float4*>(part)[i];
-  for (int z = 1; z < nsplit; ++z) {
-    const float4 v = reinterpret_cast<const float4*>(part)[(size_t)z * n4 + i];
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+  const float4* src = reinterpret_cast<const float4*>(part) + i;
+  // eight slices' loads in flight at a time, then their sum in slice order
+  constexpr int CH = 8;
+  float4 s = src[0];
+  for (int z0 = 1; z0 < nsplit; z0 += CH) {
+    float4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (z0 + c < nsplit) v[c] = src[(size_t)(z0 + c) * n4];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (z0 + c < nsplit) {
+        s.x += v[c].x;
+        s.y += v[c].y;
+        s.z += v[c].z;
+        s.w += v[c].w;
+      }
+    }
   }
   if constexpr (XF32) {
     reinterpret_cast<float4*>(dx)[i] = s;
